@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for the KDA gated delta-rule workloads.
+
+This module is shared by the tests, the benchmark and the smoke check. It holds
+none of the method's arithmetic: only random draws, the per-token L2
+normalisation of q and k and the sigmoid / softplus squashing that the workload
+recipes prescribe for the *inputs*, and round-to-nearest-even to bfloat16.
+
+Workloads (sizes from the five benchmark configurations of this library):
+
+  tiny     B=1  H=2  T=256   d=64   fp32 I/O  C=64   gates "weak"  h0 = 0
+  prefill  B=1  H=16 T=4096  d=128  bf16 I/O  C=64   gates "main"  h0 ~ N(0, 0.02)
+  batched  B=8  H=32 T=8192  d=128  bf16 I/O  C=64   gates "weak"  h0 = 0
+  varlen   seqs 32768/16384/12288/4096 packed, H=32 d=128 bf16 C=128, gates "weak",
+           per-sequence h0 ~ N(0, 0.02)
+  decode   N=256 sequences, H=32, d=128, one bf16 token per step, gates "main",
+           h0 ~ N(0, 0.02)
+
+Gate families (log alpha is drawn per token, per head and per key channel):
+  weak:  log alpha = -0.1 * softplus(N(0,1)),  beta = sigmoid(N(0,1))
+  main:  log alpha = -softplus(N(-2,1)),       beta = sigmoid(N(0,1))
+q and k are N(0,1) vectors L2-normalised per (token, head); v ~ N(0,1).
+"N(mu, s)" means standard deviation s.
+
+Layout of every array: token-major and packed, [T_total, H, d]; gates
+[T_total, H, d_k] and [T_total, H]; states [n_seqs, H, d_k, d_v] row-major
+(row = key channel). Batched workloads are packed sequences of equal length.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seqlens: tuple          # lengths of the packed sequences
+    H: int
+    dk: int
+    dv: int
+    chunk: int
+    io: str                 # "f32" or "bf16": dtype of q, k, v and o
+    gates: str              # "weak" or "main"
+    h0: str                 # "zero" or "normal"
+    seed: int
+
+    @property
+    def T_total(self) -> int:
+        return int(sum(self.seqlens))
+
+    @property
+    def n_seqs(self) -> int:
+        return len(self.seqlens)
+
+    @property
+    def scale(self) -> float:
+        return float(self.dk) ** -0.5
+
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.seqlens)]).astype(np.int32)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", (256,), 2, 64, 64, 64, "f32", "weak", "zero", 1000),
+    "prefill": Workload("prefill", (4096,), 16, 128, 128, 64, "bf16", "main", "normal", 1001),
+    "batched": Workload("batched", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002),
+    "varlen": Workload("varlen", (32768, 16384, 12288, 4096), 32, 128, 128, 128, "bf16", "weak",
+                       "normal", 1003),
+}
+
+# Decode: N sequences x H heads, one token per step.
+DECODE = dict(name="decode", N=256, H=32, dk=128, dv=128, io="bf16", gates="main", steps=1024,
+              seed=1004)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bfloat16 (ties to even); returns fp32 values
+    that are exactly representable in bfloat16."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _unit_gaussian(rng, shape, d):
+    x = rng.standard_normal(shape + (d,), dtype=np.float32).astype(np.float64)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    return x.astype(np.float32)
+
+
+def _gates(rng, family, shape, dk):
+    if family == "weak":
+        la = -0.1 * softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64))
+    elif family == "main":
+        la = -softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64) - 2.0)
+    else:
+        raise ValueError(family)
+    beta = sigmoid(rng.standard_normal(shape, dtype=np.float32).astype(np.float64))
+    return la.astype(np.float32), beta.astype(np.float32)
+
+
+def _io(x, io):
+    return round_bf16(x) if io == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def gen_sequences(seqlens, H, dk, dv, io, gates, h0, seed):
+    """Draw one packed batch of sequences. Returns a dict of fp32 numpy arrays
+    (q, k, v rounded to bf16 when io == "bf16"), the int32 cu_seqlens, and h0
+    (None when it is zero)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q_l, k_l, v_l, la_l, b_l = [], [], [], [], []
+    for L in seqlens:  # draw sequence by sequence to bound temporary memory
+        q_l.append(_io(_unit_gaussian(rng, (L, H), dk), io))
+        k_l.append(_io(_unit_gaussian(rng, (L, H), dk), io))
+        v_l.append(_io(rng.standard_normal((L, H, dv), dtype=np.float32), io))
+        la, b = _gates(rng, gates, (L, H), dk)
+        la_l.append(la)
+        b_l.append(b)
+    out = dict(
+        q=np.concatenate(q_l), k=np.concatenate(k_l), v=np.concatenate(v_l),
+        log_alpha=np.concatenate(la_l), beta=np.concatenate(b_l),
+        cu_seqlens=np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32),
+    )
+    if h0 == "normal":
+        out["h0"] = (0.02 * rng.standard_normal((len(seqlens), H, dk, dv), dtype=np.float32)
+                     ).astype(np.float32)
+    else:
+        out["h0"] = None
+    return out
+
+
+def gen_workload(w: Workload, seed: Optional[int] = None):
+    return gen_sequences(w.seqlens, w.H, w.dk, w.dv, w.io, w.gates, w.h0,
+                         w.seed if seed is None else seed)
+
+
+def gen_decode_state(N, H, dk, dv, seed):
+    """Initial decode state h0 ~ N(0, 0.02), [N, H, dk, dv] fp32."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0xD0]))
+    return (0.02 * rng.standard_normal((N, H, dk, dv), dtype=np.float32)).astype(np.float32)
+
+
+def gen_decode_step(N, H, dk, dv, io, gates, seed, step):
+    """Inputs of decode step `step` for N sequences: q, k, v [N, H, d], log_alpha
+    [N, H, dk], beta [N, H]. Each step has its own stream (seed, step), so any
+    step can be regenerated on its own."""
+    rng = np.random.Generator(np.random.PCG64([seed, step]))
+    q = _io(_unit_gaussian(rng, (N, H), dk), io)
+    k = _io(_unit_gaussian(rng, (N, H), dk), io)
+    v = _io(rng.standard_normal((N, H, dv), dtype=np.float32), io)
+    la, b = _gates(rng, gates, (N, H), dk)
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=b)

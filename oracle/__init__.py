@@ -1,0 +1,6 @@
+"""Plain fp64 CPU oracle of the KDA gated delta rule (test infrastructure).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. The GPU library never calls it and shares no code with it.
+"""
+from .oracle import build, kda_reference, library_path  # noqa: F401

@@ -1,0 +1,95 @@
+"""ctypes wrapper and build step for the fp64 KDA oracle (test infrastructure).
+
+The oracle itself is plain C in kda_oracle.c: a token-by-token fp64 loop of
+the KDA gated delta rule. This wrapper only converts arrays to contiguous fp64
+and calls it. It is "parity pinned": tests/test_oracle_pins.py ties it to the
+worked 2x2 examples of the "ten questions" page and to closed forms, brute
+force and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_libs = {}
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile kda_oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+                               "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load(path: Optional[str] = None):
+    """Load the oracle library (or, for the mutation tests, another build of it)."""
+    path = path or _LIB
+    if path not in _libs:
+        if path == _LIB and (not os.path.exists(_LIB)
+                             or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+            build(force=True)
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        lib.kda_oracle_fwd.argtypes = [ctypes.c_int64, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       P, P, P, P, P, ctypes.c_double, ctypes.c_int, P, P, P,
+                                       ctypes.c_int]
+        lib.kda_oracle_fwd.restype = ctypes.c_int
+        _libs[path] = lib
+    return _libs[path]
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def kda_reference(q, k, v, log_alpha, beta, scale: float, h0=None, cu_seqlens=None,
+                  delta_rule: bool = True, threads: Optional[int] = None,
+                  lib: Optional[str] = None):
+    """fp64 oracle over packed sequences.
+
+    q, k [T, H, dk]; v [T, H, dv]; log_alpha [T, H, dk]; beta [T, H];
+    h0 [n_seqs, H, dk, dv] or None; cu_seqlens [n_seqs + 1] or None (one sequence).
+    Returns (o [T, H, dv], hT [n_seqs, H, dk, dv]) as fp64 arrays.
+    """
+    q, k, v, log_alpha, beta = map(_f64, (q, k, v, log_alpha, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and v.shape == (T, H, dv)
+    assert log_alpha.shape == (T, H, dk) and beta.shape == (T, H)
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], dtype=np.int64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    n_seqs = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T
+    if h0 is not None:
+        h0 = _f64(h0)
+        assert h0.shape == (n_seqs, H, dk, dv)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    hT = np.zeros((n_seqs, H, dk, dv), dtype=np.float64)
+    if threads is None:
+        threads = max(1, min(os.cpu_count() or 1, n_seqs * H))
+    rc = _load(lib).kda_oracle_fwd(n_seqs, _ptr(cu), H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(log_alpha), _ptr(beta), float(scale), int(bool(delta_rule)),
+                                _ptr(h0), _ptr(o), _ptr(hT), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_fwd failed with code {rc}")
+    return o, hT

@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of libkda on one MI355X.
+
+Headline (`value`): chunked-prefill tokens/s of the KDA gated delta rule on the
+batched prefill workload B=8, H=32, T=8192, d_k=d_v=128, chunk 64, bf16 q/k/v/o,
+fp32 gates and state (token = one (sequence, position) across all 32 heads).
+One step = one kda_chunk_fwd call over the whole batch, inputs resident in HBM.
+
+Also reported on the same line:
+  roofline      achieved algorithmic HBM bytes/s of the prefill pass vs 8 TB/s
+  decode        kda_recurrent_step on 256 sequences x 32 heads (fp32 128x128
+                states, 537 MB), tokens/s = 256 / step time, with its own roofline
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample
+                of the same prefill workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import kda_synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KDA tokens/sec (prefill chunked, decode step) at H=32,d=128; % roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_states_in):
+    """q, k, v, o in the I/O dtype, log_alpha (fp32 per key channel) and beta (fp32)
+    per token-head, plus the fp32 states read and written."""
+    per = (2 * dk + 2 * dv) * io_bytes + 4 * dk + 4
+    return token_heads * per + 4 * dk * dv * (n_states_out + n_states_in)
+
+
+def bench_prefill(args, kda, torch):
+    w = kda_synth.WORKLOADS["batched"]
+    B, T, H, dk, dv, C = len(w.seqlens), w.seqlens[0], w.H, w.dk, w.dv, w.chunk
+    log(f"[bench] generating prefill inputs B={B} T={T} H={H} d={dk}")
+    t0 = time.time()
+    x = kda_synth.gen_workload(w)
+    log(f"[bench] generated in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(x["q"]).to(dev).to(torch.bfloat16).reshape(B, T, H, dk)
+    k = torch.from_numpy(x["k"]).to(dev).to(torch.bfloat16).reshape(B, T, H, dk)
+    v = torch.from_numpy(x["v"]).to(dev).to(torch.bfloat16).reshape(B, T, H, dv)
+    la = torch.from_numpy(x["log_alpha"]).to(dev).reshape(B, T, H, dk)
+    beta = torch.from_numpy(x["beta"]).to(dev).reshape(B, T, H)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_bytes(B, T, H, dk, dv, C, 0, kda.KDA_BF16), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        kda.chunk_fwd(q, k, v, la, beta, chunk=C, o=o, hT=hT, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms = wall * 1000.0 / args.steps
+    tokens = B * T
+    token_heads = tokens * H
+    alg = prefill_algorithmic_bytes(token_heads, dk, dv, 2, B * H, 0)
+    ev_avg = float(np.mean(ev_ms))
+    achieved = alg / (ev_avg * 1e-3) / 1e9
+    log(f"[bench] prefill: wall {ms:.3f} ms/step, events avg {ev_avg:.3f} min {min(ev_ms):.3f} ms, "
+        f"{tokens / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s algorithmic")
+    res = dict(ms=ms, ev_ms=ev_avg, tokens_per_s=tokens / (ms * 1e-3), alg_bytes=alg,
+               achieved_gbs=achieved, workload=w, x=x)
+    del q, k, v, la, beta, o, hT, ws
+    return res
+
+
+def bench_decode(args, kda, torch):
+    d = kda_synth.DECODE
+    N, H, dk, dv = d["N"], d["H"], d["dk"], d["dv"]
+    bank = args.decode_bank
+    log(f"[bench] generating decode state ({N}x{H}x{dk}x{dv} fp32) and {bank} distinct steps")
+    dev = torch.device("cuda:0")
+    state = torch.from_numpy(kda_synth.gen_decode_state(N, H, dk, dv, d["seed"])).to(dev)
+    steps_in = []
+    for s in range(bank):
+        y = kda_synth.gen_decode_step(N, H, dk, dv, "bf16", "main", d["seed"], s)
+        steps_in.append(dict(
+            q=torch.from_numpy(y["q"]).to(dev).to(torch.bfloat16),
+            k=torch.from_numpy(y["k"]).to(dev).to(torch.bfloat16),
+            v=torch.from_numpy(y["v"]).to(dev).to(torch.bfloat16),
+            la=torch.from_numpy(y["log_alpha"]).to(dev), beta=torch.from_numpy(y["beta"]).to(dev)))
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        s = steps_in[i % bank]
+        kda.recurrent_step(s["q"], s["k"], s["v"], s["la"], s["beta"], state, o=o)
+
+    for i in range(8):
+        step(i)
+    torch.cuda.synchronize()
+    n = args.decode_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(n):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / n
+    nh = N * H
+    alg = nh * (2 * 4 * dk * dv + (2 * dk + 2 * dv) * 2 + 4 * dk + 4)
+    achieved = alg / (ms * 1e-3) / 1e9
+    log(f"[bench] decode: {ms * 1000:.1f} us/step (wall {wall * 1000 / n * 1000:.1f}), "
+        f"{N / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s")
+    return dict(ms=ms, tokens_per_s=N / (ms * 1e-3), alg_bytes=alg, achieved_gbs=achieved, steps=n)
+
+
+def cpu_baseline(pre, args):
+    """The fp64 oracle on a bounded sample of the prefill workload: all 32 heads
+    of `--cpu-seqs` of the 8 sequences, full length, on this host's cores."""
+    import oracle
+    x, w = pre["x"], pre["workload"]
+    n_seq = args.cpu_seqs
+    T = w.seqlens[0]
+    sl = slice(0, n_seq * T)
+    cores = len(os.sched_getaffinity(0))
+    cu = np.arange(n_seq + 1, dtype=np.int64) * T
+    sub = {n: np.ascontiguousarray(x[n][sl]) for n in ("q", "k", "v", "log_alpha", "beta")}
+    log(f"[bench] cpu baseline: oracle on {n_seq} sequences x {w.H} heads x {T} tokens, "
+        f"{cores} threads")
+    t0 = time.perf_counter()
+    oracle.kda_reference(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], w.scale,
+                         cu_seqlens=cu, threads=cores)
+    dt = time.perf_counter() - t0
+    tokens = n_seq * T
+    log(f"[bench] cpu baseline: {dt:.2f}s, {tokens / dt:.1f} tokens/s")
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_seq} of the 8 sequences (all {w.H} heads, {T} tokens each) of the "
+                      f"batched prefill workload; fp64 token-by-token recurrence, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--decode-bank", type=int, default=32)
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_48_amd as kda
+    kda.load()
+    torch.cuda.set_device(0)
+
+    pre = bench_prefill(args, kda, torch)
+    dec = None if args.no_decode else bench_decode(args, kda, torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
+
+    w = pre["workload"]
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA batched chunked prefill: B=8 sequences x T=8192 tokens, H=32 heads, "
+                               "d_k=d_v=128, chunk 64, bf16 q/k/v/o, fp32 log_alpha/beta/state",
+                   "global_batch": len(w.seqlens), "seq_len": w.seqlens[0], "heads": w.H,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(pre["achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(pre["achieved_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "chunked prefill pass (kda_prep_kernel + kda_state_kernel)",
+                     "alg_bytes_per_launch": pre["alg_bytes"], "avg_launch_ms": round(pre["ev_ms"], 4)},
+        "cpu_baseline": cpu,
+    }
+    if dec is not None:
+        line["decode"] = {"value": dec["tokens_per_s"], "unit": "tokens/s", "us_per_step": round(dec["ms"] * 1000, 2),
+                          "steps": dec["steps"], "workload": "256 sequences x 32 heads, fp32 128x128 states, bf16 token",
+                          "roofline": {"bound": "hbm", "achieved": round(dec["achieved_gbs"], 1),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(dec["achieved_gbs"] / HBM_PEAK_GBS, 4),
+                                       "alg_bytes_per_launch": dec["alg_bytes"]}}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

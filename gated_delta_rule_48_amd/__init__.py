@@ -1,0 +1,8 @@
+"""libkda: the KDA (Kimi Delta Attention) gated delta rule on AMD MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind a C ABI
+(include/kda.h, built into libkda.so in this directory); this package is the
+thin Python binding over it.
+"""
+from .binding import (KdaError, abi_version, chunk_fwd, load, recurrent_step,  # noqa: F401
+                      workspace_bytes, LIB_PATH, EXPORTS, KDA_F32, KDA_BF16)

@@ -1,0 +1,180 @@
+"""ctypes binding of libkda (include/kda.h).
+
+Argument marshalling only: shape/dtype checks, output and workspace
+allocation through torch (device memory is torch's), and the call into the C
+ABI on torch's current HIP stream. Every step of the computation runs in
+libkda's HIP kernels; there is no other code path. If libkda.so has not been
+built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
+          4: "KDA_ERR_HIP"}
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
+           "kda_chunk_fwd", "kda_recurrent_step")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libkda.so is missing at {LIB_PATH}; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = I
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.kda_chunk_fwd_workspace_bytes.restype = Z
+    lib.kda_chunk_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, I, P, P, P, Z, P]
+    lib.kda_chunk_fwd.restype = I
+    lib.kda_recurrent_step.argtypes = [I, I, I, I, I, P, P, P, P, P, F, P, P, P]
+    lib.kda_recurrent_step.restype = I
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load().kda_abi_version()
+
+
+def _io_code(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return KDA_BF16
+    if dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype, shape, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def workspace_bytes(B, T, H, dk, dv, chunk, n_seqs, io) -> int:
+    return int(load().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, n_seqs, io))
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, cu_seqlens=None,
+              chunk: int = 64, output_final_state: bool = True, o=None, hT=None, workspace=None,
+              stream=None):
+    """Chunked KDA forward (kda_chunk_fwd).
+
+    q, k [B, T, H, dk] (or packed [T, H, dk] with cu_seqlens); v [.., H, dv];
+    log_alpha [.., H, dk] fp32; beta [.., H] fp32; h0 [n_seq, H, dk, dv] fp32 or None;
+    cu_seqlens int32 [n_seqs + 1] on the device, or None. Returns (o, hT); hT is
+    None when output_final_state is False.
+    """
+    import torch
+    lib = load()
+    dev = q.device
+    io = _io_code(q.dtype)
+    if cu_seqlens is not None:
+        if q.dim() != 3:
+            raise ValueError("with cu_seqlens, q must be packed [T, H, dk]")
+        B, (T, H, dk) = 1, q.shape
+        n_seqs = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", torch.int32, (n_seqs + 1,), dev)
+        lead = (T,)
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, dk]")
+        B, T, H, dk = q.shape
+        n_seqs = B
+        lead = (B, T)
+    dv = v.shape[-1]
+    _check(q, "q", q.dtype, lead + (H, dk), dev)
+    _check(k, "k", q.dtype, lead + (H, dk), dev)
+    _check(v, "v", q.dtype, lead + (H, dv), dev)
+    _check(log_alpha, "log_alpha", torch.float32, lead + (H, dk), dev)
+    _check(beta, "beta", torch.float32, lead + (H,), dev)
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (n_seqs, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty(lead + (H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, lead + (H, dv), dev)
+    if output_final_state and hT is None:
+        hT = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    if hT is not None:
+        _check(hT, "hT", torch.float32, (n_seqs, H, dk, dv), dev)
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
+                                                 n_seqs if cu_seqlens is not None else 0, io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dk ** -0.5
+    st = lib.kda_chunk_fwd(B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                           _ptr(beta), float(scale), _ptr(h0), _ptr(cu_seqlens),
+                           n_seqs if cu_seqlens is not None else 0, _ptr(o), _ptr(hT),
+                           _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd")
+    return o, hT
+
+
+def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = None, o=None,
+                   stream=None):
+    """One decode step (kda_recurrent_step): q, k [N, H, dk]; v [N, H, dv];
+    log_alpha [N, H, dk] fp32; beta [N, H] fp32; state [N, H, dk, dv] fp32,
+    updated in place. Returns o [N, H, dv]."""
+    import torch
+    lib = load()
+    dev = q.device
+    io = _io_code(q.dtype)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(k, "k", q.dtype, (N, H, dk), dev)
+    _check(v, "v", q.dtype, (N, H, dv), dev)
+    _check(log_alpha, "log_alpha", torch.float32, (N, H, dk), dev)
+    _check(beta, "beta", torch.float32, (N, H), dev)
+    _check(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, (N, H, dv), dev)
+    if scale is None:
+        scale = dk ** -0.5
+    st = lib.kda_recurrent_step(N, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                _ptr(beta), float(scale), _ptr(state), _ptr(o), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_step")
+    return o

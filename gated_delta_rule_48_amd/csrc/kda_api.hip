@@ -1,0 +1,191 @@
+// kda_api.hip -- the C ABI of libkda (see include/kda.h): argument validation,
+// workspace layout and kernel dispatch. Host code only; it never synchronises.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.hpp"
+
+#define KDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using kda::ChunkBuffers;
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// [lo, lo + bytes) ranges overlap?
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+struct WsLayout {
+    size_t W, U, QO, KtT, Aqk, eg, choff, total;
+    int64_t n_chunks;  // upper bound on the number of chunks over all sequences
+};
+
+// Workspace layout: per-chunk buffers (chunk-major, see ChunkBuffers) and, for
+// packed variable-length input, the chunk offsets of the sequences.
+bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varlen, int io,
+               WsLayout *L) {
+    if (T <= 0) {
+        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0};
+        return true;
+    }
+    const size_t esz = io == KDA_BF16 ? 2 : 4;
+    const int64_t per_seq = ((int64_t)T + C - 1) / C;
+    L->n_chunks = varlen ? per_seq + n_seqs : (int64_t)B * per_seq;
+    const size_t nch = (size_t)L->n_chunks * (size_t)H;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    L->W = take(nch * C * dk * esz);
+    L->U = take(nch * C * dv * esz);
+    L->QO = take(nch * C * dk * esz);
+    L->KtT = take(nch * dk * C * esz);
+    L->Aqk = take(nch * C * C * esz);
+    L->eg = take(nch * dk * sizeof(float));
+    // chunk offsets [n_seqs + 1], then sequence begins and ends [n_seqs] each
+    L->choff = varlen ? take(((size_t)3 * n_seqs + 1) * sizeof(int32_t)) : 0;
+    L->total = off;
+    return true;
+}
+
+kda_status check_sizes(int B, int T, int H, int dk, int dv, int chunk, int io, bool varlen,
+                       int n_seqs) {
+    if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (B < 1 || T < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (varlen && (B != 1 || n_seqs < 1)) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 64 && chunk != 128) return KDA_ERR_UNSUPPORTED;
+    if (H > 65535) return KDA_ERR_UNSUPPORTED;  // grid y limit of the prep kernel
+    const int64_t tokens = (int64_t)B * T;
+    if (tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    const int64_t nseq = varlen ? n_seqs : B;
+    if (nseq * H * 4 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+KDA_EXPORT const char *kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported size or dtype";
+        case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case KDA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk,
+                                                int n_seqs, int io) {
+    const bool varlen = n_seqs > 0 && B == 1;
+    if (check_sizes(B, T, H, d_k, d_v, chunk, io, varlen, varlen ? n_seqs : 0) != KDA_OK) return 0;
+    WsLayout L;
+    ws_layout(B, T, H, d_k, d_v, chunk, varlen ? n_seqs : 0, varlen, io, &L);
+    return L.total;
+}
+
+KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                             const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, float scale,
+                             const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                             void *o, float *hT, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    const bool varlen = cu_seqlens != nullptr;
+    kda_status st = check_sizes(B, T, H, d_k, d_v, chunk, io, varlen, n_seqs);
+    if (st != KDA_OK) return st;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    const int nseq = varlen ? n_seqs : B;
+    const size_t tokens = (size_t)B * T;
+    const size_t esz = io == KDA_BF16 ? 2 : 4;
+    if (tokens > 0) {
+        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(log_alpha, 16) || !aligned(beta, 4))
+            return KDA_ERR_INVALID_ARG;
+        const size_t ob = tokens * H * d_v * esz;
+        if (overlaps(o, ob, q, tokens * H * d_k * esz) || overlaps(o, ob, k, tokens * H * d_k * esz) ||
+            overlaps(o, ob, v, ob) || overlaps(o, ob, log_alpha, tokens * H * d_k * 4) ||
+            overlaps(o, ob, beta, tokens * H * 4))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if ((h0 && !aligned(h0, 16)) || (hT && !aligned(hT, 16))) return KDA_ERR_INVALID_ARG;
+    if (varlen && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+
+    WsLayout L;
+    ws_layout(B, T, H, d_k, d_v, chunk, varlen ? n_seqs : 0, varlen, io, &L);
+    if (L.total > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total))
+        return KDA_ERR_WORKSPACE;
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    ChunkBuffers buf{};
+    if (L.total > 0) {
+        buf = ChunkBuffers{ws + L.W, ws + L.U, ws + L.QO, ws + L.KtT, ws + L.Aqk,
+                           reinterpret_cast<float *>(ws + L.eg)};
+    }
+
+    kda::SeqMap map{};
+    map.C = chunk;
+    map.n_seqs = nseq;
+    if (varlen && tokens > 0) {
+        int32_t *off = reinterpret_cast<int32_t *>(ws + L.choff);
+        map.varlen = 1;
+        map.chunk_off = off;
+        map.seq_begin = off + n_seqs + 1;
+        map.seq_end = off + 2 * n_seqs + 1;
+        map.seq_len = 0;
+        if (kda::launch_chunk_offsets(cu_seqlens, n_seqs, (int)tokens, chunk, off, off + n_seqs + 1,
+                                      off + 2 * n_seqs + 1, hs) != hipSuccess)
+            return KDA_ERR_HIP;
+    } else {  // B equal sequences (or no tokens at all: every sequence is empty)
+        map.varlen = 0;
+        map.seq_len = tokens > 0 ? T : 0;
+    }
+
+    const bool bf = io == KDA_BF16;
+    if (tokens > 0) {
+        kda::PrepArgs pa{q, k, v, log_alpha, beta, scale, H, map, buf};
+        if (kda::launch_prep(pa, chunk, d_k, d_v, bf, (int)L.n_chunks, hs) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
+    kda::StateArgs sa{h0, hT, o, H, map, buf};
+    if (kda::launch_state(sa, chunk, d_k, d_v, bf, nseq, hs) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+KDA_EXPORT int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,
+                                  const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta, float scale,
+                                  float *state, void *o, void *stream) {
+    if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(log_alpha, 16) || !aligned(beta, 4) || !aligned(state, 16))
+        return KDA_ERR_INVALID_ARG;
+    const size_t nh = (size_t)N * H, esz = io == KDA_BF16 ? 2 : 4;
+    if (overlaps(o, nh * d_v * esz, state, nh * d_k * d_v * 4)) return KDA_ERR_INVALID_ARG;
+    kda::DecodeArgs da{q, k, v, log_alpha, beta, scale, state, o, (int)nh};
+    if (kda::launch_decode(da, d_k, d_v, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}

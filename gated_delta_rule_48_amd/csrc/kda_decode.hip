@@ -1,0 +1,116 @@
+// kda_decode.hip -- one KDA decode step: a single token for each of N sequences.
+//
+// The step in the order of the bra-ket derivation page (mynewscn.com, the KDA
+// state-update equations at its start), in the d_k x d_v orientation:
+//
+//   S~ = Diag(alpha) S;  e = beta (v - S~^T k);  S <- S~ + k e^T;
+//   o  = scale S^T q = scale (S~^T q + (k . q) e)
+//
+// The second form of o lets one pass over the state produce both reductions
+// (S~^T k and S~^T q) before anything is written, so each state is read once
+// and written once. The step is a pure HBM read-modify-write (about one flop
+// per byte), so the kernel is built around the memory access: one workgroup per
+// (sequence, head), each thread owning 4 adjacent columns of RPT rows, 16-byte
+// loads and stores covering whole rows per wave instruction, and the column
+// sums reduced across row groups through LDS.
+
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
+    constexpr int CG = DV / 4;          // float4 column groups
+    constexpr int RG = kThreads / CG;   // row groups
+    constexpr int RPT = DK / RG;        // rows per thread
+    static_assert(RPT * RG == DK, "rows must split evenly");
+
+    __shared__ float ks[DK], qs[DK], al[DK];
+    __shared__ f32x4 red_k[RG][CG], red_q[RG][CG];
+    __shared__ float kq_part[kThreads / 64];
+
+    const int nh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const T *q = static_cast<const T *>(a.q) + (size_t)nh * DK;
+    const T *k = static_cast<const T *>(a.k) + (size_t)nh * DK;
+    const T *v = static_cast<const T *>(a.v) + (size_t)nh * DV;
+
+    float kq = 0.f;
+    if (tid < DK) {
+        const float kv = to_f32(k[tid]), qv = to_f32(q[tid]);
+        ks[tid] = kv;
+        qs[tid] = qv;
+        al[tid] = expf(a.log_alpha[(size_t)nh * DK + tid]);
+        kq = kv * qv;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
+    if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
+    __syncthreads();
+
+    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + (size_t)nh * DK * DV);
+    f32x4 sv[RPT];
+    f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int it = 0; it < RPT; ++it) {
+        const int row = it * RG + rg;
+        f32x4 x = S[row * CG + cg];
+        x *= al[row];
+        sv[it] = x;
+        rk += ks[row] * x;
+        rq += qs[row] * x;
+    }
+    red_k[rg][cg] = rk;
+    red_q[rg][cg] = rq;
+    __syncthreads();
+
+    f32x4 tk = {0.f, 0.f, 0.f, 0.f}, tq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        tk += red_k[g][cg];
+        tq += red_q[g][cg];
+    }
+    float kqs = 0.f;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) kqs += kq_part[i];
+    const float beta = a.beta[nh];
+    f32x4 e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = beta * (to_f32(v[4 * cg + i]) - tk[i]);
+    if (rg == 0) {
+        T *o = static_cast<T *>(a.o) + (size_t)nh * DV;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[4 * cg + i] = from_f32<T>(a.scale * (tq[i] + kqs * e[i]));
+    }
+#pragma unroll
+    for (int it = 0; it < RPT; ++it) {
+        const int row = it * RG + rg;
+        S[row * CG + cg] = sv[it] + ks[row] * e;
+    }
+}
+
+template <int DK, int DV, typename T>
+hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_decode_kernel<DK, DV, T>), dim3(a.NH), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_d(const DecodeArgs &a, int dk, int dv, hipStream_t st) {
+    if (dk == 64 && dv == 64) return launch_decode_t<64, 64, T>(a, st);
+    if (dk == 64 && dv == 128) return launch_decode_t<64, 128, T>(a, st);
+    if (dk == 128 && dv == 64) return launch_decode_t<128, 64, T>(a, st);
+    return launch_decode_t<128, 128, T>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, int dk, int dv, bool bf16, hipStream_t stream) {
+    return bf16 ? dispatch_d<kda::bf16>(a, dk, dv, stream) : dispatch_d<float>(a, dk, dv, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,164 @@
+// kda_device.hpp -- device-side building blocks shared by libkda's kernels
+// (gfx950, wave64). Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// ---------------------------------------------------------------- MFMA
+//
+// One 16x16 fp32 output tile, accumulated over K with the matrix cores.
+// Both operands are "K-contiguous": A is row-major [16][K] (row m at A + m*lda)
+// and B is given as its transpose, row-major [16][K] (column n of B at
+// B + n*ldb). Accumulator layout (both instructions): lane l holds
+// C[4*(l/16) + i][l%16] in element i.
+//
+//  bf16: v_mfma_f32_16x16x32_bf16, lane l supplies A[l%16][8*(l/16) .. +7] and
+//        B^T[l%16][8*(l/16) .. +7]  (one 16-byte load each).
+//  fp32: v_mfma_f32_16x16x4_f32,   lane l supplies A[l%16][l/16] and B^T[l%16][l/16].
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    typedef bf16x8 Frag;
+    static constexpr int kK = 32;   // K per instruction
+    static constexpr int kPer = 8;  // consecutive K elements per lane
+    __device__ __forceinline__ static Frag load(const bf16 *p) {
+        return *reinterpret_cast<const bf16x8 *>(p);
+    }
+    // kPer fp32 values `stride` apart, rounded to bf16 (to nearest even).
+    __device__ __forceinline__ static Frag load_f32(const float *p, int stride) {
+        Frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = static_cast<bf16>(p[i * stride]);
+        return f;
+    }
+    __device__ __forceinline__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    typedef float Frag;
+    static constexpr int kK = 4;
+    static constexpr int kPer = 1;
+    __device__ __forceinline__ static Frag load(const float *p) { return *p; }
+    __device__ __forceinline__ static Frag load_f32(const float *p, int) { return *p; }
+    __device__ __forceinline__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// acc += A[0:16, k0:k1] * (Bt[0:16, k0:k1])^T. A is row-major [16][K] (row m at
+// A + m*lda) and Bt is B transposed, row-major [16][K]; both already offset to
+// their first row. k0 and k1 are multiples of Mma<T>::kK.
+template <typename T>
+__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const T *A, int lda, const T *Bt, int ldb,
+                                        int k0, int k1) {
+    typedef Mma<T> M;
+    const int l = threadIdx.x & (kWave - 1);
+    const T *a = A + (l & 15) * lda + (l >> 4) * M::kPer;
+    const T *b = Bt + (l & 15) * ldb + (l >> 4) * M::kPer;
+    for (int k = k0; k < k1; k += M::kK) acc = M::mma(M::load(a + k), M::load(b + k), acc);
+    return acc;
+}
+
+// Same with A taken from fp32 storage (rounded to T).
+template <typename T>
+__device__ __forceinline__ f32x4 mma_nt_f32a(f32x4 acc, const float *A, int lda, const T *Bt,
+                                             int ldb, int k0, int k1) {
+    typedef Mma<T> M;
+    const int l = threadIdx.x & (kWave - 1);
+    const float *a = A + (l & 15) * lda + (l >> 4) * M::kPer;
+    const T *b = Bt + (l & 15) * ldb + (l >> 4) * M::kPer;
+    for (int k = k0; k < k1; k += M::kK) acc = M::mma(M::load_f32(a + k, 1), M::load(b + k), acc);
+    return acc;
+}
+
+// acc += A[0:16, k0:k1] * B[k0:k1, 0:16] with both in fp32 storage: A row-major
+// [16][K], B row-major [K][16] (row k at B + k*ldb), rounded to T.
+template <typename T>
+__device__ __forceinline__ f32x4 mma_nn_f32(f32x4 acc, const float *A, int lda, const float *B,
+                                            int ldb, int k0, int k1) {
+    typedef Mma<T> M;
+    const int l = threadIdx.x & (kWave - 1);
+    const float *a = A + (l & 15) * lda + (l >> 4) * M::kPer;
+    const float *b = B + (l >> 4) * M::kPer * ldb + (l & 15);
+    for (int k = k0; k < k1; k += M::kK)
+        acc = M::mma(M::load_f32(a + k, 1), M::load_f32(b + k * ldb, ldb), acc);
+    return acc;
+}
+
+__device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
+__device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
+
+// ---------------------------------------------------------------- sequences and chunks
+//
+// Sequences are packed along the token axis. Without cu_seqlens there are
+// n_seqs sequences of seq_len tokens each. With cu_seqlens, the ranges are the
+// ones kda_chunk_offsets_kernel derived from it: clamped into [0, T_total] and
+// made non-overlapping and ordered (a malformed table therefore can neither
+// move an access out of the buffers nor produce more chunks than the
+// workspace holds); chunk_off[s] is the number of chunks of all earlier
+// sequences.
+struct SeqMap {
+    const int32_t *chunk_off; // device [n_seqs + 1] when varlen
+    const int32_t *seq_begin; // device [n_seqs] when varlen
+    const int32_t *seq_end;   // device [n_seqs] when varlen
+    int varlen;
+    int n_seqs;
+    int seq_len;              // uniform length when !varlen
+    int C;
+
+    __device__ __forceinline__ void seq_range(int s, int &t_begin, int &t_end) const {
+        if (!varlen) {
+            t_begin = s * seq_len;
+            t_end = t_begin + seq_len;
+        } else {
+            t_begin = seq_begin[s];
+            t_end = seq_end[s];
+        }
+    }
+    __device__ __forceinline__ int chunks_before(int s) const {
+        return !varlen ? s * ((seq_len + C - 1) / C) : chunk_off[s];
+    }
+    __device__ __forceinline__ int total_chunks() const { return chunks_before(n_seqs); }
+    // Global chunk j -> its sequence, first token and length. False if j is past the end.
+    __device__ __forceinline__ bool locate(int j, int &s, int &t0, int &len) const {
+        if (j >= total_chunks()) return false;
+        if (!varlen) {
+            s = j / ((seq_len + C - 1) / C);
+        } else {  // last s with chunk_off[s] <= j (empty sequences share offsets)
+            int lo = 0, hi = n_seqs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (chunk_off[mid] <= j) lo = mid; else hi = mid - 1;
+            }
+            s = lo;
+        }
+        int tb, te;
+        seq_range(s, tb, te);
+        t0 = tb + (j - chunks_before(s)) * C;
+        len = min(C, te - t0);
+        return true;
+    }
+};
+
+}  // namespace kda

@@ -1,0 +1,60 @@
+// kda_internal.hpp -- launch interfaces between libkda's C ABI and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda_device.hpp"
+
+namespace kda {
+
+// Per-chunk quantities produced by the chunk-preparation kernel and consumed by
+// the state/output kernel. All are indexed chunk-major: [chunk j][head h][...],
+// where j runs over the chunks of all sequences in order.
+struct ChunkBuffers {
+    void *W;     // [C][d_k]  io dtype: T (beta k exp(g))            (WY "w")
+    void *U;     // [C][d_v]  io dtype: T (beta v)                   (WY "u", before the state term)
+    void *QO;    // [C][d_k]  io dtype: scale q exp(g)               (readout of the entering state)
+    void *KtT;   // [d_k][C]  io dtype: (k exp(gamma - g))^T         (write-back into the state)
+    void *Aqk;   // [C][C]    io dtype: scale <q_r exp(g_r - g_i), k_i>, i <= r, else 0
+    float *eg;   // [d_k]     fp32:     exp(gamma), gamma = g at the chunk's last row
+};
+
+struct PrepArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    float scale;
+    int H;
+    SeqMap map;
+    ChunkBuffers buf;
+};
+
+struct StateArgs {
+    const float *h0;
+    float *hT;
+    void *o;
+    int H;
+    SeqMap map;
+    ChunkBuffers buf;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    float scale;
+    float *state;
+    void *o;
+    int NH;  // N * H
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_chunk_offsets(const int32_t *cu, int n_seqs, int T_total, int C, int32_t *off,
+                                int32_t *tb, int32_t *te, hipStream_t stream);
+hipError_t launch_prep(const PrepArgs &a, int C, int dk, int dv, bool bf16, int n_chunks_grid,
+                       hipStream_t stream);
+hipError_t launch_state(const StateArgs &a, int C, int dk, int dv, bool bf16, int n_seqs,
+                        hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int dk, int dv, bool bf16, hipStream_t stream);
+
+}  // namespace kda

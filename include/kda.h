@@ -1,0 +1,143 @@
+/*
+ * kda.h -- C ABI of libkda: the KDA (Kimi Delta Attention) gated delta rule on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation, per (sequence, head), for t = 1..T:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T (scale * q_t),           alpha_t = exp(log_alpha_t) per key channel
+ *
+ * as written on the "ten questions" page (jokeuncle.github.io, Kimi K3 KDA math
+ * for beginners: the closing symbol-by-symbol reading of the update; Q4 for the
+ * readout o = S^T q, Q8 for Diag(alpha) acting on the rows of S), with the
+ * d_k^{-1/2} query scale of the bra-ket derivation page (mynewscn.com, the KDA
+ * state-update equations at its start). S is d_k x d_v, row i = key channel i.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a caller-owned DEVICE pointer on the current HIP
+ *    device, contiguous, 16-byte aligned. The library allocates nothing, keeps
+ *    no global mutable state, never synchronises and never prints.
+ *  - Layouts are token-major: q, k [T_total, H, d_k]; v, o [T_total, H, d_v];
+ *    log_alpha [T_total, H, d_k] fp32; beta [T_total, H] fp32; states
+ *    [n_seqs, H, d_k, d_v] fp32 row-major (row = key channel).
+ *  - `io` selects the dtype of q, k, v and o: KDA_F32 (float) or KDA_BF16
+ *    (bfloat16). Gates, states and the workspace's fp32 parts are always fp32.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it in order; the call returns before it runs.
+ *  - Supported sizes: d_k, d_v in {64, 128}; chunk in {64, 128}; H >= 1;
+ *    any T >= 0 (a ragged last chunk is handled).
+ *  - Errors: arguments are validated on the host before anything is launched;
+ *    on KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_WORKSPACE nothing is
+ *    written and nothing is enqueued. KDA_ERR_HIP reports a failed launch.
+ *    Device-side faults surface at the caller's next synchronisation. Input
+ *    VALUES are not checked: gates must be finite, and within one chunk the
+ *    summed log_alpha of each key channel must stay >= -170 (beyond that the
+ *    in-chunk decay factors are clamped and lose accuracy).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* NULL / misaligned pointer, negative or inconsistent size */
+    KDA_ERR_UNSUPPORTED = 2, /* well-formed but unsupported: d_k, d_v, chunk or dtype */
+    KDA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned (256 B) or too small */
+    KDA_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static English text for a kda_status value ("unknown status" otherwise). */
+const char *kda_status_string(int status);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for these sizes (0 when T == 0). For
+ * packed variable-length input pass B = 1, T = total tokens and n_seqs = the
+ * number of sequences; otherwise n_seqs is ignored. Returns 0 for unsupported
+ * or invalid sizes as well, so check kda_chunk_fwd's status.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk,
+                                     int n_seqs, int io);
+
+/*
+ * kda_chunk_fwd -- chunked prefill ("chunked program"): o for every token and
+ * the final state of every sequence.
+ *
+ * Method: the sequence is cut into chunks of `chunk` tokens (the essay
+ * "22,580: from GPT-2 to Kimi K3", yichencityu.github.io, section 6.2: masked
+ * attention inside a chunk, a recurrent state between chunks; section 6.3: the
+ * WY reparametrisation that solves a chunk's delta corrections with one
+ * unit-lower-triangular solve), extended with the per-channel decay of KDA
+ * (the aidehub.top summary of the same essay, Gated DeltaNet section: a write
+ * at one position read at a later one is decayed by the product of the alphas
+ * in between). Chunking is an exact refactoring of the recurrence; results
+ * differ from the token loop only by rounding.
+ *
+ * Arguments
+ *   B, T        without cu_seqlens: B sequences of T tokens each, tensors
+ *               [B, T, H, d] (the same memory as packed [B*T, H, d]).
+ *   H, d_k, d_v heads and head dims.  chunk: 64 or 128.  io: kda_dtype.
+ *   q, k, v     [B*T, H, d_k|d_k|d_v], dtype io.
+ *   log_alpha   [B*T, H, d_k] fp32, log of the per-channel decay (<= 0 normally).
+ *   beta        [B*T, H] fp32, write strength.
+ *   scale       query scale (callers normally pass d_k^{-1/2}).
+ *   h0          [n_seq, H, d_k, d_v] fp32 initial states, or NULL for zeros.
+ *               May alias hT (in-place carry).
+ *   cu_seqlens  NULL, or device int32 [n_seqs + 1] offsets of packed sequences
+ *               (then B must be 1): cu_seqlens[0] = 0, non-decreasing,
+ *               cu_seqlens[n_seqs] = T. Values outside [0, T] are clamped on
+ *               the device so that no access leaves the buffers.
+ *   n_seqs      number of packed sequences (ignored when cu_seqlens is NULL;
+ *               then n_seq = B).
+ *   o           [B*T, H, d_v] dtype io, written for every token. Must not alias
+ *               any input.
+ *   hT          [n_seq, H, d_k, d_v] fp32 final states, or NULL to skip.
+ *   workspace   device scratch of at least kda_chunk_fwd_workspace_bytes(...)
+ *               bytes, 256-byte aligned; owned by the caller, contents
+ *               undefined before and after. Two calls in flight at once need
+ *               two workspaces.
+ */
+int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                  const void *q, const void *k, const void *v,
+                  const float *log_alpha, const float *beta, float scale,
+                  const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                  void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_recurrent_step -- one decode step ("recurrent program") for N sequences:
+ * every (sequence, head) state is read once and written once, in place.
+ *
+ * Method: the step in the order of the bra-ket derivation page (mynewscn.com,
+ * the KDA state-update equations at its start), in the d_k x d_v orientation:
+ * S~ = Diag(alpha) S; e = beta (v - S~^T k); S <- S~ + k e^T;
+ * o = scale (S~^T q + (k . q) e), which equals S_t^T (scale q).
+ *
+ * Arguments
+ *   N, H, d_k, d_v, io   as above (d_k, d_v in {64, 128}).
+ *   q, k        [N, H, d_k] dtype io;  v, o [N, H, d_v] dtype io.
+ *   log_alpha   [N, H, d_k] fp32;  beta [N, H] fp32;  scale as above.
+ *   state       [N, H, d_k, d_v] fp32, updated in place. Must not alias o.
+ */
+int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,
+                       const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *beta, float scale,
+                       float *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

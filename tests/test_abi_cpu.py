@@ -1,0 +1,121 @@
+"""CPU tests of the C ABI: the library loads, exports exactly what include/kda.h
+declares, and rejects bad arguments with the documented status before anything
+is launched (every call below returns during host-side validation, so the fake
+device addresses are never touched)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_48_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+A = 0x10000  # fake, 256-byte aligned "device" addresses, never dereferenced
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+        getattr(lib, name)
+    assert {n for n in exported if n.startswith("kda_")} == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing, misaligned or too small")]:
+        assert lib.kda_status_string(code) == text
+    assert lib.kda_status_string(99) == b"unknown status"
+
+
+def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
+    per = (T + C - 1) // C
+    nch = (per + n_seqs if n_seqs else B * per) * H
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    total = 0
+    for nbytes in (nch * C * dk * esz, nch * C * dv * esz, nch * C * dk * esz, nch * dk * C * esz,
+                   nch * C * C * esz, nch * dk * 4):
+        total += r(nbytes)
+    if n_seqs:
+        total += r((3 * n_seqs + 1) * 4)
+    return total
+
+
+@pytest.mark.parametrize("args", [(8, 8192, 32, 128, 128, 64, 0, BF16), (1, 65536, 32, 128, 128, 128, 4, BF16),
+                                  (1, 256, 2, 64, 64, 64, 0, F32), (3, 77, 5, 64, 128, 128, 0, F32)])
+def test_workspace_size(lib, args):
+    B, T, H, dk, dv, C, ns, io = args
+    got = lib.kda_chunk_fwd_workspace_bytes(*args)
+    assert got == _ws_expect(B, T, H, dk, dv, C, ns, 2 if io == BF16 else 4)
+
+
+def test_workspace_size_degenerate(lib):
+    assert lib.kda_chunk_fwd_workspace_bytes(2, 0, 4, 128, 128, 64, 0, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(2, 10, 4, 96, 128, 64, 0, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(2, 10, 4, 128, 128, 32, 0, BF16) == 0
+
+
+def fwd(lib, **kw):
+    a = dict(B=2, T=100, H=4, dk=128, dv=128, chunk=64, io=BF16, q=A, k=A, v=A, la=A, beta=A,
+             scale=0.088, h0=None, cu=None, n_seqs=0, o=0x4000000, hT=None, ws=A, ws_bytes=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"],
+                             a["k"], a["v"], a["la"], a["beta"], a["scale"], a["h0"], a["cu"],
+                             a["n_seqs"], a["o"], a["hT"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED), (dict(chunk=32), UNSUPPORTED),
+    (dict(io=7), UNSUPPORTED), (dict(H=70000), UNSUPPORTED),
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(beta=None), INVALID),
+    (dict(q=A + 8), INVALID), (dict(la=A + 4), INVALID), (dict(h0=A + 4), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(o=A), INVALID),                           # o aliases the inputs
+    (dict(cu=A, n_seqs=2), INVALID),                # varlen needs B == 1
+    (dict(B=1, cu=A, n_seqs=0), INVALID),
+    (dict(cu=A + 2, B=1, n_seqs=2), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws=A + 16), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE),
+])
+def test_chunk_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def step(lib, **kw):
+    a = dict(N=4, H=2, dk=128, dv=128, io=BF16, q=A, k=A, v=A, la=A, beta=A, scale=0.088,
+             state=0x4000000, o=0x8000000, stream=None)
+    a.update(kw)
+    return lib.kda_recurrent_step(a["N"], a["H"], a["dk"], a["dv"], a["io"], a["q"], a["k"], a["v"],
+                                  a["la"], a["beta"], a["scale"], a["state"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), OK),  # nothing to do, nothing launched
+    (dict(dk=32), UNSUPPORTED), (dict(io=2), UNSUPPORTED), (dict(N=-1), INVALID), (dict(H=0), INVALID),
+    (dict(state=None), INVALID), (dict(q=A + 2), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(o=0x4000000 + 1024), INVALID),            # o inside the state
+])
+def test_recurrent_step_rejects(lib, kw, code):
+    assert step(lib, **kw) == code

@@ -1,0 +1,276 @@
+"""GPU parity of libkda (through its C ABI) against the fp64 oracle.
+
+Bar: relative L2 error of o and of hT, each over the whole tensor, <= 1e-4 on
+the fp32 path and <= 2e-2 on the bf16-input path (q, k, v, o in bf16; gates and
+states fp32). Inputs are seeded synthetic draws (kda_synth); the oracle reads
+exactly the values the GPU receives.
+"""
+import numpy as np
+import pytest
+
+import kda_synth
+import oracle
+from kda_testlib import TOL, gen, oracle_run, rel_l2, run_packed, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x, io, chunk, name, varlen=True, B=None, T=None, h0=True, tol=None):
+    tol = TOL[io] if tol is None else tol
+    say(f"[{name}] io={io} C={chunk} seqs={np.diff(x['cu_seqlens']).tolist()[:6]} "
+        f"H={x['q'].shape[1]} dk={x['q'].shape[2]} dv={x['v'].shape[2]}")
+    o, hT = run_packed(x, io, chunk, varlen=varlen, B=B, T=T, h0=h0)
+    o_ref, h_ref, _ = oracle_run(x, h0=h0)
+    eo, eh = rel_l2(o, o_ref), rel_l2(hT, h_ref)
+    say(f"[{name}] rel_l2 o={eo:.2e} hT={eh:.2e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    assert eo <= tol and eh <= tol, (eo, eh)
+    return o, hT
+
+
+def test_tiny_config():
+    """The tiny fp32 workload: B=1, H=2, T=256, d=64, C=64, weak gates, h0 = 0."""
+    w = kda_synth.WORKLOADS["tiny"]
+    x = kda_synth.gen_workload(w)
+    _check(x, "f32", w.chunk, "tiny")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_shapes(io, chunk, dk, dv):
+    """Several chunks with a ragged tail, two sequences, nonzero h0."""
+    x = gen([3 * chunk + 17, 2 * chunk], 2, dk, dv, io, seed=dk + dv + chunk)
+    _check(x, io, chunk, "shapes")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 2, 15, 63, 64, 65, 127, 129])
+def test_short_and_ragged_lengths(io, T):
+    x = gen([T, T], 3, 128, 128, io, seed=T)
+    _check(x, io, 64, f"T={T}", varlen=False, B=2, T=T)
+
+
+def test_batched_layout_equals_packed():
+    """[B, T, H, d] without cu_seqlens is the same computation as B packed
+    sequences of length T, bit for bit."""
+    x = gen([200, 200, 200], 4, 128, 128, "bf16", seed=5)
+    o1, h1 = run_packed(x, "bf16", 64, varlen=False, B=3, T=200)
+    o2, h2 = run_packed(x, "bf16", 64, varlen=True)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def test_no_h0_no_hT():
+    x = gen([150, 90], 2, 128, 128, "f32", h0="zero", seed=9)
+    o, hT = run_packed(x, "f32", 64, h0=False, hT=False)
+    assert hT is None
+    o_ref, _, _ = oracle_run(x, h0=False)
+    assert rel_l2(o, o_ref) <= TOL["f32"]
+
+
+def test_empty_input_copies_state():
+    """T = 0: no token, hT = h0 (and zeros without h0)."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    H, d = 3, 64
+    q = torch.empty((2, 0, H, d), device="cuda")
+    la = torch.empty((2, 0, H, d), device="cuda")
+    beta = torch.empty((2, 0, H), device="cuda")
+    h0 = torch.randn((2, H, d, d), device="cuda")
+    _, hT = kda.chunk_fwd(q, q, q, la, beta, h0=h0)
+    assert torch.equal(hT, h0)
+    _, hT = kda.chunk_fwd(q, q, q, la, beta)
+    assert torch.count_nonzero(hT).item() == 0
+
+
+def test_varlen_with_empty_and_tiny_sequences():
+    x = gen([0, 130, 1, 0, 64, 257], 2, 128, 128, "bf16", seed=13)
+    _check(x, "bf16", 64, "varlen-edge")
+    _check(x, "bf16", 128, "varlen-edge-C128")
+
+
+def test_varlen_equals_separate_calls():
+    """Packed sequences give exactly (bitwise) what separate calls give."""
+    x = gen([77, 300, 64], 2, 128, 128, "bf16", seed=21)
+    o, hT = run_packed(x, "bf16", 64)
+    cu = x["cu_seqlens"]
+    for s in range(3):
+        sl = slice(cu[s], cu[s + 1])
+        xs = {n: x[n][sl] for n in ("q", "k", "v", "log_alpha", "beta")}
+        xs["h0"] = x["h0"][s:s + 1]
+        xs["cu_seqlens"] = np.array([0, cu[s + 1] - cu[s]], dtype=np.int32)
+        os_, hs = run_packed(xs, "bf16", 64)
+        assert np.array_equal(o[sl], os_), s
+        assert np.array_equal(hT[s:s + 1], hs), s
+
+
+def test_chunk_size_invariance():
+    """C = 64 and C = 128 are two blockings of the same recurrence."""
+    x = gen([500], 2, 128, 128, "f32", seed=31)
+    o64, h64 = _check(x, "f32", 64, "C64")
+    o128, h128 = _check(x, "f32", 128, "C128")
+    assert rel_l2(o64, o128) <= 1e-4 and rel_l2(h64, h128) <= 1e-4
+
+
+def test_split_invariance():
+    """One call over T tokens equals two calls that carry hT -> h0."""
+    x = gen([300], 2, 128, 128, "f32", seed=41)
+    o, hT = run_packed(x, "f32", 64)
+    t1 = 130
+    a = {n: x[n][:t1] for n in ("q", "k", "v", "log_alpha", "beta")}
+    a["h0"], a["cu_seqlens"] = x["h0"], np.array([0, t1], dtype=np.int32)
+    oa, ha = run_packed(a, "f32", 64)
+    b = {n: x[n][t1:] for n in ("q", "k", "v", "log_alpha", "beta")}
+    b["h0"], b["cu_seqlens"] = ha, np.array([0, 300 - t1], dtype=np.int32)
+    ob, hb = run_packed(b, "f32", 64)
+    assert rel_l2(np.concatenate([oa, ob]), o) <= 1e-5
+    assert rel_l2(hb, hT) <= 1e-5
+
+
+def test_h0_aliases_hT():
+    import torch
+    import gated_delta_rule_48_amd as kda
+    x = gen([200], 2, 128, 128, "f32", seed=43)
+    t = to_dev(x, "f32")
+    args = [t[n] for n in ("q", "k", "v", "log_alpha", "beta")]
+    _, ref = kda.chunk_fwd(*args, h0=t["h0"], cu_seqlens=t["cu_seqlens"])
+    st = t["h0"].clone()
+    kda.chunk_fwd(*args, h0=st, hT=st, cu_seqlens=t["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(st, ref)
+
+
+@pytest.mark.parametrize("gate", ["deltanet", "gdn"])
+def test_reductions(gate):
+    """log alpha = 0 (DeltaNet) and one decay for all key channels (Gated DeltaNet)."""
+    x = gen([260], 2, 128, 128, "f32", seed=51)
+    if gate == "deltanet":
+        x["log_alpha"] = np.zeros_like(x["log_alpha"])
+    else:
+        x["log_alpha"] = np.repeat(x["log_alpha"][:, :, :1], 128, axis=2).copy()
+    _check(x, "f32", 64, gate)
+
+
+def test_beta_zero_keeps_state():
+    """beta = 0 and alpha = 1: the state is unchanged and o = scale q^T S0."""
+    x = gen([100], 2, 64, 64, "f32", seed=53)
+    x["beta"] = np.zeros_like(x["beta"])
+    x["log_alpha"] = np.zeros_like(x["log_alpha"])
+    o, hT = run_packed(x, "f32", 64)
+    assert rel_l2(hT, x["h0"]) <= 1e-6
+    _check(x, "f32", 64, "beta0")
+
+
+def test_deterministic():
+    x = gen([1000, 333], 4, 128, 128, "bf16", seed=61)
+    o1, h1 = run_packed(x, "bf16", 64)
+    o2, h2 = run_packed(x, "bf16", 64)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _decode_steps(N, H, dk, dv, io, steps, seed, sample=None):
+    """Run `steps` decode steps on the GPU; return per-step o of the sampled
+    (n, h) pairs, their final states, and the oracle's values for them."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    st0 = kda_synth.gen_decode_state(N, H, dk, dv, seed)
+    state = torch.from_numpy(st0).cuda()
+    sample = [(n, h) for n in range(N) for h in range(H)] if sample is None else sample
+    ns = np.array([p[0] for p in sample])
+    hs = np.array([p[1] for p in sample])
+    got, toks = [], []
+    for step in range(steps):
+        y = kda_synth.gen_decode_step(N, H, dk, dv, io, "main", seed, step)
+        t = to_dev(dict(y, cu_seqlens=np.zeros(1, np.int32)), io)
+        o = kda.recurrent_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], state)
+        got.append(o.float().cpu().numpy()[ns, hs])
+        toks.append({n: y[n][ns, hs] for n in ("q", "k", "v", "log_alpha", "beta")})
+    torch.cuda.synchronize()
+    st_got = state.cpu().numpy()[ns, hs]
+    # oracle: the sampled pairs as independent heads of one sequence of `steps` tokens
+    seq = {n: np.stack([tk[n] for tk in toks]) for n in toks[0]}
+    o_ref, h_ref = oracle.kda_reference(
+        seq["q"], seq["k"], seq["v"], seq["log_alpha"], seq["beta"], dk ** -0.5,
+        h0=st0[ns, hs][None])
+    return np.stack(got), st_got, o_ref, h_ref[0]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_decode_small(io, dk, dv):
+    o, st, o_ref, h_ref = _decode_steps(3, 2, dk, dv, io, 5, seed=dk + dv)
+    eo, eh = rel_l2(o, o_ref), rel_l2(st, h_ref)
+    say(f"[decode {io} {dk}x{dv}] rel_l2 o={eo:.2e} state={eh:.2e}")
+    assert eo <= TOL[io] and eh <= TOL[io]
+
+
+def test_decode_matches_chunked():
+    """T decode steps equal one chunked call over the same T tokens."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    x = gen([90], 2, 128, 128, "f32", seed=71)
+    o_c, h_c = run_packed(x, "f32", 64)
+    t = to_dev(x, "f32")
+    state = t["h0"].clone()
+    outs = []
+    for i in range(90):
+        outs.append(kda.recurrent_step(t["q"][i:i + 1], t["k"][i:i + 1], t["v"][i:i + 1],
+                                       t["log_alpha"][i:i + 1], t["beta"][i:i + 1], state))
+    torch.cuda.synchronize()
+    o_d = torch.cat(outs).cpu().numpy()
+    assert rel_l2(o_d, o_c) <= 1e-4 and rel_l2(state.cpu().numpy(), h_c) <= 1e-4
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def test_prefill_workload_full():
+    """B=1, H=16, T=4096, d=128, bf16, C=64, main gates, h0 ~ N(0, 0.02): every head."""
+    w = kda_synth.WORKLOADS["prefill"]
+    x = kda_synth.gen_workload(w)
+    _check(x, "bf16", w.chunk, "prefill-4096")
+
+
+def test_batched_workload_sampled():
+    """B=8, H=32, T=8192, bf16, C=64 (the benchmark's prefill launch): all of it on
+    the GPU, the oracle on sampled (sequence, head) pairs over their full length."""
+    w = kda_synth.WORKLOADS["batched"]
+    x = kda_synth.gen_workload(w)
+    say("[batched] generated")
+    o, hT = run_packed(x, "bf16", w.chunk, varlen=False, B=8, T=8192, h0=False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    for s, h in [(0, 0), (3, 17), (7, 31)]:
+        xs = {n: x[n] for n in ("q", "k", "v", "log_alpha", "beta", "cu_seqlens")}
+        xs["h0"] = None
+        o_ref, h_ref, idx = oracle_run(xs, heads=[h], seqs=[s], h0=False)
+        eo, eh = rel_l2(o[idx][:, [h]], o_ref), rel_l2(hT[[s]][:, [h]], h_ref)
+        say(f"[batched] seq {s} head {h}: rel_l2 o={eo:.2e} hT={eh:.2e}")
+        assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_varlen_workload_sampled():
+    """Packed 32768/16384/12288/4096 tokens, H=32, bf16, C=128, per-sequence h0:
+    all on the GPU, the oracle on two heads of every sequence."""
+    w = kda_synth.WORKLOADS["varlen"]
+    x = kda_synth.gen_workload(w)
+    say("[varlen] generated")
+    o, hT = run_packed(x, "bf16", w.chunk)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    for s in range(4):
+        for h in (s, 31 - s):
+            o_ref, h_ref, idx = oracle_run(x, heads=[h], seqs=[s])
+            eo, eh = rel_l2(o[idx][:, [h]], o_ref), rel_l2(hT[[s]][:, [h]], h_ref)
+            say(f"[varlen] seq {s} head {h}: rel_l2 o={eo:.2e} hT={eh:.2e}")
+            assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_decode_workload_sampled():
+    """256 sequences x 32 heads, d=128, bf16, main gates: 8 steps of the full
+    batch (the benchmark's decode launch), oracle on sampled (sequence, head) pairs."""
+    d = kda_synth.DECODE
+    sample = [(0, 0), (17, 5), (128, 31), (255, 16), (200, 0)]
+    o, st, o_ref, h_ref = _decode_steps(d["N"], d["H"], d["dk"], d["dv"], "bf16", 8, d["seed"], sample)
+    eo, eh = rel_l2(o, o_ref), rel_l2(st, h_ref)
+    say(f"[decode-full] rel_l2 o={eo:.2e} state={eh:.2e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]

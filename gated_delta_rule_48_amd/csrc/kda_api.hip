@@ -25,7 +25,7 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 struct WsLayout {
-    size_t W, U, QO, KtT, Aqk, eg, choff, total;
+    size_t W, U, QO, KtT, Aqk, eg, discard, choff, total;
     int64_t n_chunks;  // upper bound on the number of chunks over all sequences
 };
 
@@ -34,7 +34,7 @@ struct WsLayout {
 bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varlen, int io,
                WsLayout *L) {
     if (T <= 0) {
-        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0};
+        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         return true;
     }
     const size_t esz = io == KDA_BF16 ? 2 : 4;
@@ -53,6 +53,7 @@ bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varl
     L->KtT = take(nch * dk * C * esz);
     L->Aqk = take(nch * C * C * esz);
     L->eg = take(nch * dk * sizeof(float));
+    L->discard = take(256);  // absorbs stores of rows past a sequence's end
     // chunk offsets [n_seqs + 1], then sequence begins and ends [n_seqs] each
     L->choff = varlen ? take(((size_t)3 * n_seqs + 1) * sizeof(int32_t)) : 0;
     L->total = off;
@@ -162,7 +163,7 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
         if (kda::launch_prep(pa, chunk, d_k, d_v, bf, (int)L.n_chunks, hs) != hipSuccess)
             return KDA_ERR_HIP;
     }
-    kda::StateArgs sa{h0, hT, o, H, map, buf};
+    kda::StateArgs sa{h0, hT, o, L.total > 0 ? ws + L.discard : nullptr, H, map, buf};
     if (kda::launch_state(sa, chunk, d_k, d_v, bf, nseq, hs) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }

@@ -106,6 +106,65 @@ __device__ __forceinline__ f32x4 mma_nn_f32(f32x4 acc, const float *A, int lda, 
     return acc;
 }
 
+// ---------------------------------------------------------------- fragment-ordered tiles
+//
+// Matrix-core operands stored so that each lane's share of one instruction
+// group is 16 contiguous bytes, and the 64 lanes' shares are contiguous: one
+// wave reads a whole operand group with a single fully coalesced 1 KB access
+// (global memory) or a conflict-free ds_read_b128 (LDS).
+//
+// A group covers 16 rows x KG contraction indices. bf16 (KG = 32): lane
+// l = r + 16*(k/8) holds k % 8 = 0..7, exactly the v_mfma_f32_16x16x32_bf16
+// operand. fp32 (KG = 16): lane l = r + 16*(k%4) holds k/4 = 0..3, i.e. the
+// operands of four consecutive v_mfma_f32_16x16x4_f32 steps. Groups are stored
+// contraction-major: group (kg, row block rb) of an [R][K] matrix starts at
+// element (kg * (R/16) + rb) * 64 * EPL. The same layout serves A operands
+// ([M][K]) and transposed B operands ([N][K]).
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+    static constexpr int KG = 32, EPL = 8;
+    typedef bf16x8 Vec;
+    __device__ __forceinline__ static int lane_of(int r, int kk) { return (r & 15) + 16 * (kk >> 3); }
+    __device__ __forceinline__ static int slot_of(int kk) { return kk & 7; }
+    __device__ __forceinline__ static f32x4 mma(f32x4 acc, Vec a, Vec b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+template <> struct Frag<float> {
+    static constexpr int KG = 16, EPL = 4;
+    typedef f32x4 Vec;
+    __device__ __forceinline__ static int lane_of(int r, int kk) { return (r & 15) + 16 * (kk & 3); }
+    __device__ __forceinline__ static int slot_of(int kk) { return kk >> 2; }
+    __device__ __forceinline__ static f32x4 mma(f32x4 acc, Vec a, Vec b) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+// Element offset of (r, k) in a fragment-ordered matrix with R rows.
+template <typename T>
+__device__ __forceinline__ int frag_off(int r, int k, int R) {
+    typedef Frag<T> F;
+    const int kg = k / F::KG, kk = k % F::KG;
+    return ((kg * (R >> 4) + (r >> 4)) * 64 + F::lane_of(r, kk)) * F::EPL + F::slot_of(kk);
+}
+
+// This lane's 16-byte share of group (kg, rb) of a fragment-ordered matrix.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::Vec frag_load(const T *base, int kg, int rb, int R) {
+    const int l = threadIdx.x & 63;
+    return *reinterpret_cast<const typename Frag<T>::Vec *>(
+        base + ((kg * (R >> 4) + rb) * 64 + l) * Frag<T>::EPL);
+}
+
+// Accumulator-ordered [R][NC] matrix: 16x16 tiles row-block-major, lane l of a
+// tile holding rows 4*(l/16) + 0..3 of column l%16 contiguously (the layout of
+// a 16x16 matrix-core accumulator).
+__device__ __forceinline__ int acc_tile_off(int rb, int cb, int NC) {
+    return ((rb * (NC >> 4) + cb) * 64 + (threadIdx.x & 63)) * 4;
+}
+
 __device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
 

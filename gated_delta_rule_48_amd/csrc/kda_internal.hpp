@@ -34,6 +34,7 @@ struct StateArgs {
     const float *h0;
     float *hT;
     void *o;
+    void *discard;  // 64 io-dtype elements of workspace that absorb writes of rows past a sequence end
     int H;
     SeqMap map;
     ChunkBuffers buf;

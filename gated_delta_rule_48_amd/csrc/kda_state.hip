@@ -1,6 +1,6 @@
 // kda_state.hip -- state propagation and outputs of the chunked KDA forward.
 //
-// One workgroup (4 waves) per (sequence, head, slice of DVS value columns).
+// One workgroup (C/16 waves) per (sequence, head, slice of DVS value columns).
 // The columns of the state evolve independently (every term of the update acts
 // on S from the left or row-wise), so a head's d_v columns split over
 // workgroups without any exchange. The workgroup walks its sequence's chunks
@@ -15,59 +15,95 @@
 // This is the chunk loop of the WY algorithm in the essay "22,580: from GPT-2
 // to Kimi K3" (yichencityu.github.io, section 6.3: u = U - w S,
 // o = q S + tril(q k^T) u, S += k^T u), with KDA's per-channel decay folded
-// into W, QO, Aqk, KtT and exp(gamma). Only S (rounded to the operand type)
-// and U pass through LDS, transposed so that every matrix-core operand is
-// contiguous along the contraction.
+// into W, QO, Aqk, KtT and exp(gamma).
+//
+// The per-chunk operands are stored fragment-ordered, so each wave fetches its
+// share with fully coalesced 16-byte-per-lane loads; on the bf16 path the next
+// chunk's share is fetched while the current chunk computes. Only S (rounded
+// to the operand type) and U pass through LDS, as transposed B operands.
 
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kThreads = 256;
+template <typename T> struct Acc4;  // four io-dtype values of one accumulator lane
+template <> struct Acc4<bf16> {
+    typedef uint2 Raw;
+    __device__ __forceinline__ static float get(Raw r, int i) {
+        return static_cast<float>(reinterpret_cast<const bf16 *>(&r)[i]);
+    }
+};
+template <> struct Acc4<float> {
+    typedef f32x4 Raw;
+    __device__ __forceinline__ static float get(Raw r, int i) { return r[i]; }
+};
+
+// Store 4 consecutive contraction indices k0..k0+3 (k0 % 4 == 0) of row n of a
+// fragment-ordered matrix with R rows.
+template <typename T>
+__device__ __forceinline__ void frag_store4(T *base, int n, int k0, f32x4 v, int R) {
+    if constexpr (sizeof(T) == 2) {
+        bf16 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(v[i]);
+        *reinterpret_cast<uint2 *>(base + frag_off<T>(n, k0, R)) = *reinterpret_cast<const uint2 *>(x);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) base[frag_off<T>(n, k0 + i, R)] = v[i];
+    }
+}
 
 template <int C, int DK, int DV, int DVS, typename T>
-__global__ __launch_bounds__(kThreads) void kda_state_kernel(StateArgs a) {
-    constexpr int NSL = DV / DVS;
-    constexpr int RW = C / 4, MB = RW / 16;     // U / O rows per wave
-    constexpr int RSW = DK / 4, SB = RSW / 16;  // state rows per wave
-    constexpr int NTL = DVS / 16;               // 16-column tiles in the slice
-    constexpr int PS = DK + 8;                  // pitch of the S^T copy [DVS][DK]
-    constexpr int PU = C + 8;                   // pitch of the U^T copy [DVS][C]
-    constexpr int KK = Mma<T>::kK;
+__global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
+    typedef Frag<T> F;
+    typedef typename F::Vec V;
+    typedef typename Acc4<T>::Raw R4;
+    constexpr int NW = C / 16;
+    constexpr int NSL = DV / DVS, NTL = DVS / 16;
+    constexpr int NKG = DK / F::KG, NCG = C / F::KG;
+    constexpr int STOT = (DK / 16) * NTL;  // 16x16 state tiles of the slice
+    static_assert(STOT % NW == 0, "state tiles must split evenly over the waves");
+    constexpr int SPW = STOT / NW;                       // state tiles per wave
+    constexpr int TPB = SPW < NTL ? SPW : NTL;           // tiles per row block
+    constexpr int NSB = SPW / TPB;                       // row blocks per wave
+    constexpr bool kPrefetch = sizeof(T) == 2;
 
-    __shared__ __align__(16) T St[DVS * PS];
-    __shared__ __align__(16) T Ut[DVS * PU];
+    __shared__ __align__(16) T St[DVS * DK];  // S^T, fragment order [DVS][DK]
+    __shared__ __align__(16) T Ut[DVS * C];   // U^T, fragment order [DVS][C]
 
     const int H = a.H;
     const int sl = blockIdx.x % NSL;
     const int sh = blockIdx.x / NSL;
     const int h = sh % H, s = sh / H;
-    const int w = threadIdx.x >> 6;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int col0 = sl * DVS;
 
-    f32x4 accS[SB][NTL];
-    const float *h0 = a.h0 ? a.h0 + ((size_t)s * H + h) * DK * DV : nullptr;
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = w * RSW + sb * 16 + acc_row(i), c = col0 + nt * 16 + acc_col();
-                accS[sb][nt][i] = h0 ? h0[r * DV + c] : 0.f;
-            }
+    // state tile u of this wave: rows 16*sb(u) .., columns 16*nt(u) .. of the slice
+    auto tile_sb = [&](int sbi, int u) { return (w * SPW + sbi * TPB + u) / NTL; };
+    auto tile_nt = [&](int sbi, int u) { return (w * SPW + sbi * TPB + u) % NTL; };
 
-    auto write_state_t = [&]() {
+    f32x4 accS[NSB][TPB];
+    {
+        const float *h0 = a.h0 ? a.h0 + ((size_t)s * H + h) * DK * DV : nullptr;
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
+        for (int sbi = 0; sbi < NSB; ++sbi)
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
+            for (int u = 0; u < TPB; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = w * RSW + sb * 16 + acc_row(i), c = nt * 16 + acc_col();
-                    St[c * PS + r] = from_f32<T>(accS[sb][nt][i]);
+                    const int r = 16 * tile_sb(sbi, u) + acc_row(i);
+                    const int c = col0 + 16 * tile_nt(sbi, u) + acc_col();
+                    accS[sbi][u][i] = h0 ? h0[r * DV + c] : 0.f;
                 }
+    }
+    auto write_state_t = [&]() {
+#pragma unroll
+        for (int sbi = 0; sbi < NSB; ++sbi)
+#pragma unroll
+            for (int u = 0; u < TPB; ++u)
+                frag_store4<T>(St, 16 * tile_nt(sbi, u) + acc_col(), 16 * tile_sb(sbi, u) + acc_row(0),
+                               accS[sbi][u], DVS);
     };
     write_state_t();
     __syncthreads();
@@ -77,80 +113,125 @@ __global__ __launch_bounds__(kThreads) void kda_state_kernel(StateArgs a) {
     const int c_begin = a.map.chunks_before(s);
     const int n_c = (te - tb + C - 1) / C;
     T *o = static_cast<T *>(a.o);
+    const int kgq = (16 * w + 15) / F::KG;  // last Aqk group this wave needs
 
-    for (int ci = 0; ci < n_c; ++ci) {
-        const int t0 = tb + ci * C;
-        const int L = min(C, te - t0);
+    struct Ops {
+        V wf[NKG], qf[NKG], af[NCG], kf[NSB][NCG];
+        R4 ut[NTL];
+        f32x4 eg[NSB];
+    };
+    // Every load is unconditional (Aqk groups past the diagonal are stored as
+    // zeros) so that the number of memory operations in flight is the same on
+    // every path and the compiler can wait for exactly the group it needs.
+    auto load_ops = [&](int ci, Ops &op) {
         const size_t jh = (size_t)(c_begin + ci) * H + h;
         const T *W = static_cast<const T *>(a.buf.W) + jh * C * DK;
         const T *QO = static_cast<const T *>(a.buf.QO) + jh * C * DK;
-        const T *KtT = static_cast<const T *>(a.buf.KtT) + jh * DK * C;
         const T *Aqk = static_cast<const T *>(a.buf.Aqk) + jh * C * C;
-        const T *Ug = static_cast<const T *>(a.buf.U) + jh * C * DV + col0;
+        const T *KtT = static_cast<const T *>(a.buf.KtT) + jh * DK * C;
+        const T *Ug = static_cast<const T *>(a.buf.U) + jh * C * DV;
         const float *eg = a.buf.eg + jh * DK;
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg) {
+            op.wf[kg] = frag_load<T>(W, kg, w, C);
+            op.qf[kg] = frag_load<T>(QO, kg, w, C);
+        }
+#pragma unroll
+        for (int kg = 0; kg < NCG; ++kg) op.af[kg] = frag_load<T>(Aqk, kg, w, C);
+#pragma unroll
+        for (int sbi = 0; sbi < NSB; ++sbi) {
+            const int sb = tile_sb(sbi, 0);
+#pragma unroll
+            for (int kg = 0; kg < NCG; ++kg) op.kf[sbi][kg] = frag_load<T>(KtT, kg, sb, DK);
+            op.eg[sbi] = *reinterpret_cast<const f32x4 *>(eg + 16 * sb + 4 * (l >> 4));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt)
+            op.ut[nt] = *reinterpret_cast<const R4 *>(Ug + acc_tile_off(w, (col0 >> 4) + nt, DV));
+    };
 
-        // U = U~ - W S and the entering-state part of O
-        f32x4 accU[MB][NTL], accO[MB][NTL];
+    // One chunk: U = U~ - W S, O = QO S + Aqk U, S <- exp(gamma) S + KtT U.
+    auto chunk_step = [&](int ci, const Ops &op) {
+        const int t0 = tb + ci * C;
+        const int L = min(C, te - t0);
+        f32x4 accU[NTL], accO[NTL];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int r0 = w * RW + mb * 16;
+        for (int nt = 0; nt < NTL; ++nt) {
+            accU[nt] = accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                accU[mb][nt] = mma_nt<T>(z, W + r0 * DK, DK, St + nt * 16 * PS, PS, 0, DK);
-                accO[mb][nt] = mma_nt<T>(z, QO + r0 * DK, DK, St + nt * 16 * PS, PS, 0, DK);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + acc_row(i), c = nt * 16 + acc_col();
-                    const float u = to_f32(Ug[r * DV + c]) - accU[mb][nt][i];
-                    accU[mb][nt][i] = u;
-                    Ut[c * PU + r] = from_f32<T>(u);
-                }
+            for (int kg = 0; kg < NKG; ++kg) {
+                const V sf = frag_load<T>(St, kg, nt, DVS);
+                accU[nt] = F::mma(accU[nt], op.wf[kg], sf);
+                accO[nt] = F::mma(accO[nt], op.qf[kg], sf);
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accU[nt][i] = Acc4<T>::get(op.ut[nt], i) - accU[nt][i];
+            frag_store4<T>(Ut, 16 * nt + acc_col(), 16 * w + acc_row(0), accU[nt], DVS);
         }
         __syncthreads();  // U^T complete; every wave is done reading S^T
 
-        // O += Aqk U (Aqk is zero above the diagonal; stop at the diagonal tile)
+        // O += Aqk U (zero above the diagonal; the groups past it are skipped)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int r0 = w * RW + mb * 16;
-            const int kmax = min(C, (r0 + 16 + KK - 1) / KK * KK);
+        for (int nt = 0; nt < NTL; ++nt) {
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                accO[mb][nt] = mma_nt<T>(accO[mb][nt], Aqk + r0 * C, C, Ut + nt * 16 * PU, PU, 0, kmax);
+            for (int kg = 0; kg < NCG; ++kg)
+                if (kg <= kgq) accO[nt] = F::mma(accO[nt], op.af[kg], frag_load<T>(Ut, kg, nt, DVS));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + acc_row(i), c = col0 + nt * 16 + acc_col();
-                    if (r < L) o[((size_t)(t0 + r) * H + h) * DV + c] = from_f32<T>(accO[mb][nt][i]);
-                }
+            for (int i = 0; i < 4; ++i) {
+                // rows past the end of the sequence go to a discard slot, not through a branch
+                const int r = 16 * w + acc_row(i);
+                T *dst = r < L ? o + ((size_t)(t0 + r) * H + h) * DV + col0 + 16 * nt + acc_col()
+                               : static_cast<T *>(a.discard) + (threadIdx.x & 63);
+                *dst = from_f32<T>(accO[nt][i]);
             }
         }
 
         // S <- exp(gamma) S + KtT U
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-            const int r0 = w * RSW + sb * 16;
+        for (int sbi = 0; sbi < NSB; ++sbi)
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
+            for (int u = 0; u < TPB; ++u) {
+                accS[sbi][u] *= op.eg[sbi];
+                const int nt = tile_nt(sbi, u);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) accS[sb][nt][i] *= eg[r0 + acc_row(i)];
-                accS[sb][nt] = mma_nt<T>(accS[sb][nt], KtT + r0 * C, C, Ut + nt * 16 * PU, PU, 0, C);
+                for (int kg = 0; kg < NCG; ++kg)
+                    accS[sbi][u] = F::mma(accS[sbi][u], op.kf[sbi][kg], frag_load<T>(Ut, kg, nt, DVS));
             }
-        }
         write_state_t();
         __syncthreads();  // S^T ready for the next chunk; U^T free again
+    };
+
+    if constexpr (kPrefetch) {
+        // Two operand sets used in turn: while one chunk computes, the next
+        // chunk's operands are in flight (the last chunk re-fetches itself).
+        Ops A, B;
+        if (n_c > 0) load_ops(0, A);
+        for (int ci = 0; ci < n_c; ci += 2) {
+            load_ops(min(ci + 1, n_c - 1), B);
+            chunk_step(ci, A);
+            if (ci + 1 >= n_c) break;
+            load_ops(min(ci + 2, n_c - 1), A);
+            chunk_step(ci + 1, B);
+        }
+    } else {
+        Ops A;
+        for (int ci = 0; ci < n_c; ++ci) {
+            load_ops(ci, A);
+            chunk_step(ci, A);
+        }
     }
 
     if (a.hT) {
         float *hT = a.hT + ((size_t)s * H + h) * DK * DV;
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
+        for (int sbi = 0; sbi < NSB; ++sbi)
 #pragma unroll
-            for (int nt = 0; nt < NTL; ++nt)
+            for (int u = 0; u < TPB; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = w * RSW + sb * 16 + acc_row(i), c = col0 + nt * 16 + acc_col();
-                    hT[r * DV + c] = accS[sb][nt][i];
+                    const int r = 16 * tile_sb(sbi, u) + acc_row(i);
+                    const int c = col0 + 16 * tile_nt(sbi, u) + acc_col();
+                    hT[r * DV + c] = accS[sbi][u][i];
                 }
     }
 }
@@ -159,7 +240,7 @@ template <int C, int DK, int DV, typename T>
 hipError_t launch_state_t(const StateArgs &a, int n_seqs, hipStream_t stream) {
     constexpr int DVS = 32;
     auto kern = kda_state_kernel<C, DK, DV, DVS, T>;
-    hipLaunchKernelGGL(kern, dim3(n_seqs * a.H * (DV / DVS)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(kern, dim3(n_seqs * a.H * (DV / DVS)), dim3(4 * C), 0, stream, a);
     return hipGetLastError();
 }
 

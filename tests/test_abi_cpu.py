@@ -55,7 +55,7 @@ def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
     total = 0
     for nbytes in (nch * C * dk * esz, nch * C * dv * esz, nch * C * dk * esz, nch * dk * C * esz,
-                   nch * C * C * esz, nch * dk * 4):
+                   nch * C * C * esz, nch * dk * 4, 256):
         total += r(nbytes)
     if n_seqs:
         total += r((3 * n_seqs + 1) * 4)

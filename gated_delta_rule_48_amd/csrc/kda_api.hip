@@ -163,7 +163,7 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
         if (kda::launch_prep(pa, chunk, d_k, d_v, bf, (int)L.n_chunks, hs) != hipSuccess)
             return KDA_ERR_HIP;
     }
-    kda::StateArgs sa{h0, hT, o, L.total > 0 ? ws + L.discard : nullptr, H, map, buf};
+    kda::StateArgs sa{h0, hT, o, L.total > 0 ? ws + L.discard : nullptr, H, 0, map, buf};
     if (kda::launch_state(sa, chunk, d_k, d_v, bf, nseq, hs) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }

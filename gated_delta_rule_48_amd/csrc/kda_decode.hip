@@ -35,39 +35,50 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
     const int nh = blockIdx.x;
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
+
+    // 1. this thread's state rows first: they are the step's traffic, and
+    //    nothing below waits for them until the token is staged. Streamed once
+    //    per step (the states exceed the last-level cache), hence nontemporal.
+    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + (size_t)nh * DK * DV);
+    f32x4 sv[RPT];
+#pragma unroll
+    for (int it = 0; it < RPT; ++it) sv[it] = __builtin_nontemporal_load(&S[(it * RG + rg) * CG + cg]);
+
+    // 2. the token: k, q and alpha per key channel into LDS, k . q by reduction
     const T *q = static_cast<const T *>(a.q) + (size_t)nh * DK;
     const T *k = static_cast<const T *>(a.k) + (size_t)nh * DK;
     const T *v = static_cast<const T *>(a.v) + (size_t)nh * DV;
-
     float kq = 0.f;
     if (tid < DK) {
         const float kv = to_f32(k[tid]), qv = to_f32(q[tid]);
         ks[tid] = kv;
         qs[tid] = qv;
-        al[tid] = expf(a.log_alpha[(size_t)nh * DK + tid]);
+        al[tid] = __expf(a.log_alpha[(size_t)nh * DK + tid]);
         kq = kv * qv;
     }
+    f32x4 vv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = to_f32(v[4 * cg + i]);
+    const float beta = a.beta[nh];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
     __syncthreads();
 
-    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + (size_t)nh * DK * DV);
-    f32x4 sv[RPT];
+    // 3. decay, and the partial column sums of S~^T k and S~^T q over this thread's rows
     f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int it = 0; it < RPT; ++it) {
         const int row = it * RG + rg;
-        f32x4 x = S[row * CG + cg];
-        x *= al[row];
-        sv[it] = x;
-        rk += ks[row] * x;
-        rq += qs[row] * x;
+        sv[it] *= al[row];
+        rk += ks[row] * sv[it];
+        rq += qs[row] * sv[it];
     }
     red_k[rg][cg] = rk;
     red_q[rg][cg] = rq;
     __syncthreads();
 
+    // 4. full column sums, the error e = beta (v - S~^T k) and the output
     f32x4 tk = {0.f, 0.f, 0.f, 0.f}, tq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
@@ -77,19 +88,18 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
     float kqs = 0.f;
 #pragma unroll
     for (int i = 0; i < kThreads / 64; ++i) kqs += kq_part[i];
-    const float beta = a.beta[nh];
-    f32x4 e;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = beta * (to_f32(v[4 * cg + i]) - tk[i]);
+    const f32x4 e = beta * (vv - tk);
     if (rg == 0) {
         T *o = static_cast<T *>(a.o) + (size_t)nh * DV;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[4 * cg + i] = from_f32<T>(a.scale * (tq[i] + kqs * e[i]));
     }
+
+    // 5. write back S~ + k e^T
 #pragma unroll
     for (int it = 0; it < RPT; ++it) {
         const int row = it * RG + rg;
-        S[row * CG + cg] = sv[it] + ks[row] * e;
+        __builtin_nontemporal_store(sv[it] + ks[row] * e, &S[row * CG + cg]);
     }
 }
 

@@ -124,6 +124,8 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16> {
     static constexpr int KG = 32, EPL = 8;
     typedef bf16x8 Vec;
+    // contraction index held by lane-group hi (= lane / 16) in slot j of group kg
+    __device__ __forceinline__ static int chan(int kg, int hi, int j) { return 32 * kg + 8 * hi + j; }
     __device__ __forceinline__ static int lane_of(int r, int kk) { return (r & 15) + 16 * (kk >> 3); }
     __device__ __forceinline__ static int slot_of(int kk) { return kk & 7; }
     __device__ __forceinline__ static f32x4 mma(f32x4 acc, Vec a, Vec b) {
@@ -133,6 +135,7 @@ template <> struct Frag<bf16> {
 template <> struct Frag<float> {
     static constexpr int KG = 16, EPL = 4;
     typedef f32x4 Vec;
+    __device__ __forceinline__ static int chan(int kg, int hi, int j) { return 16 * kg + hi + 4 * j; }
     __device__ __forceinline__ static int lane_of(int r, int kk) { return (r & 15) + 16 * (kk & 3); }
     __device__ __forceinline__ static int slot_of(int kk) { return kk >> 2; }
     __device__ __forceinline__ static f32x4 mma(f32x4 acc, Vec a, Vec b) {
@@ -163,6 +166,20 @@ __device__ __forceinline__ typename Frag<T>::Vec frag_load(const T *base, int kg
 // a 16x16 matrix-core accumulator).
 __device__ __forceinline__ int acc_tile_off(int rb, int cb, int NC) {
     return ((rb * (NC >> 4) + cb) * 64 + (threadIdx.x & 63)) * 4;
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16m .. 16m+15),
+// by shifted adds; lanes shifted in from outside the row contribute zero.
+template <int D> __device__ __forceinline__ float dpp_row_shr(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x110 | D, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row16_inclusive_sum(float x) {
+    x += dpp_row_shr<1>(x);
+    x += dpp_row_shr<2>(x);
+    x += dpp_row_shr<4>(x);
+    x += dpp_row_shr<8>(x);
+    return x;
 }
 
 __device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }

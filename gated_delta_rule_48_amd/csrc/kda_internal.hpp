@@ -36,6 +36,7 @@ struct StateArgs {
     void *o;
     void *discard;  // 64 io-dtype elements of workspace that absorb writes of rows past a sequence end
     int H;
+    int xcd_group;  // set by the launcher: map a pair's d_v slices onto one XCD
     SeqMap map;
     ChunkBuffers buf;
 };

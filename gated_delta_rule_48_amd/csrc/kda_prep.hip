@@ -39,86 +39,70 @@ namespace kda {
 namespace {
 
 template <int C, int DK, int DV, typename T> struct PrepCfg {
-    static constexpr int NT = 4 * C, NW = NT / 64;
-    static constexpr int CGK = DK / 8, RPK = CGK / 4, RGK = NT / CGK;  // key-side thread tiles
-    static constexpr int CGV = DV / 8, RPV = CGV / 4;                  // value-side thread tiles
-    static constexpr int P64 = 64 + 8;  // pitch of the [C][64] Gram operand blocks
-    static constexpr int PT = C + 4;    // pitch of the fp32 [C][C] matrices
-    static constexpr size_t SMALL = (size_t)(RGK * DK + C) * 4;
-    static constexpr size_t STAGE = (size_t)C * (DK > DV ? DK : DV) * sizeof(T);
-    static constexpr size_t GRAM = (size_t)3 * C * P64 * sizeof(T);
-    static constexpr size_t MATF = (size_t)C * PT * 4;
-    static constexpr size_t OPB = (size_t)64 * C * sizeof(T);
+    typedef Frag<T> F;
+    static constexpr int NW = C / 16, NT = 64 * NW;   // wave w owns chunk rows 16w .. 16w+15
+    static constexpr int NKG = DK / F::KG, NVG = DV / F::KG;
+    static constexpr int PT = C + 4;                  // pitch of the fp32 [C][C] matrices
+    // columns of W / U~ per pass of the final product (LDS budget)
+    static constexpr int PW = (sizeof(T) == 4 && C == 128) ? 64 : 128;
     static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-    static constexpr size_t REGION = mx(mx(STAGE, GRAM), mx(2 * MATF, MATF + 2 * OPB));
+    static constexpr size_t SMALL = (size_t)(NW * DK + C) * 4;
+    static constexpr size_t MATF = (size_t)C * PT * 4;
+    static constexpr size_t GRAM = (size_t)2 * C * DK * sizeof(T);           // Km + KtT staging
+    static constexpr size_t AQK = MATF + (size_t)C * C * sizeof(T);          // Aqk staging + Am
+    static constexpr size_t SOLVE = 2 * MATF;
+    static constexpr size_t WPASS = MATF + (size_t)2 * PW * C * sizeof(T);   // Tm + B operand + W staging
+    static constexpr size_t REGION = mx(mx(GRAM, AQK), mx(SOLVE, WPASS));
     static constexpr size_t SMEM = SMALL + REGION;
 };
 
 __device__ __forceinline__ float clamp85(float x) { return fminf(fmaxf(x, -85.f), 85.f); }
-
-// Lower-triangular 16x16 tile list: tile t <-> (ti, tj), tj <= ti, row by row.
-__device__ __forceinline__ void tri_tile(int t, int &ti, int &tj) {
-    ti = 0;
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    tj = t - ti * (ti + 1) / 2;
-}
-
-template <typename T> __device__ __forceinline__ void load8(const T *p, float v[8]);
-template <> __device__ __forceinline__ void load8<bf16>(const bf16 *p, float v[8]) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(x[e]);
-}
-template <> __device__ __forceinline__ void load8<float>(const float *p, float v[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[e] = a[e];
-        v[4 + e] = b[e];
-    }
-}
-
-// Store 8 values of row r, columns c0..c0+7 (c0 % 8 == 0), of a
-// fragment-ordered matrix with R rows.
-template <typename T>
-__device__ __forceinline__ void frag_store_row8(T *base, int r, int c0, const float v[8], int R) {
-    if constexpr (sizeof(T) == 2) {
-        bf16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(v[e]);
-        *reinterpret_cast<bf16x8 *>(base + frag_off<T>(r, c0, R)) = x;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) base[frag_off<T>(r, c0 + e, R)] = v[e];
-    }
-}
-
-// Store n consecutive contraction indices k0..k0+n-1 (n = 2 or 4, k0 % n == 0)
-// of row r of a fragment-ordered matrix with R rows.
-template <typename T, int N>
-__device__ __forceinline__ void frag_store_col(T *base, int r, int k0, const float *v, int R) {
-    if constexpr (sizeof(T) == 2) {
-        bf16 x[N];
-#pragma unroll
-        for (int i = 0; i < N; ++i) x[i] = static_cast<bf16>(v[i]);
-        T *dst = base + frag_off<T>(r, k0, R);
-        if constexpr (N == 4) {
-            *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(x);
-        } else {
-            *reinterpret_cast<uint32_t *>(dst) = *reinterpret_cast<const uint32_t *>(x);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) base[frag_off<T>(r, k0 + i, R)] = v[i];
-    }
-}
 
 template <typename T, int NT>
 __device__ __forceinline__ void copy_out(T *dst, const T *src, int n) {
     typedef typename Frag<T>::Vec V;
     for (int i = threadIdx.x; i < n / Frag<T>::EPL; i += NT)
         reinterpret_cast<V *>(dst)[i] = reinterpret_cast<const V *>(src)[i];
+}
+
+// This lane's operand share of group kg of one row (the values at channels
+// Frag<T>::chan(kg, hi, 0..EPL-1)), from a row of `row` in global memory.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::Vec load_row_frag(const T *row, int kg, int hi) {
+    typedef Frag<T> F;
+    if constexpr (sizeof(T) == 2) {
+        return *reinterpret_cast<const typename F::Vec *>(row + F::chan(kg, hi, 0));
+    } else {
+        typename F::Vec v;
+#pragma unroll
+        for (int j = 0; j < F::EPL; ++j) v[j] = row[F::chan(kg, hi, j)];
+        return v;
+    }
+}
+
+// The fp32 values at the same channels (log alpha is fp32 for both dtypes).
+template <typename T>
+__device__ __forceinline__ void load_row_f32(const float *row, int kg, int hi, float *out) {
+    typedef Frag<T> F;
+    if constexpr (sizeof(T) == 2) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(row + F::chan(kg, hi, 0));
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(row + F::chan(kg, hi, 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[e] = a[e];
+            out[4 + e] = b[e];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < F::EPL; ++j) out[j] = row[F::chan(kg, hi, j)];
+    }
+}
+
+template <typename T> __device__ __forceinline__ typename Frag<T>::Vec pack_frag(const float *x) {
+    typename Frag<T>::Vec v;
+#pragma unroll
+    for (int j = 0; j < Frag<T>::EPL; ++j) v[j] = from_f32<T>(x[j]);
+    return v;
 }
 
 // A-operand fragment group kg of row block `row0` taken from an fp32 row-major
@@ -149,17 +133,25 @@ __device__ __forceinline__ typename Frag<T>::Vec a_frag_f32(const float *M, int 
 template <int C, int PT, typename T, int NT>
 __device__ void unit_lower_inverse(const float *A, float *Tm) {
     const int tid = threadIdx.x;
-    for (int e = tid; e < C * PT; e += NT) Tm[e] = 0.f;
+    for (int e = tid; e < C * PT / 4; e += NT) reinterpret_cast<f32x4 *>(Tm)[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
     if (tid < C) {
         const int base = tid & ~15, c = tid & 15;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            // row r of the diagonal block, read as four 16-byte vectors
+            float arow[16];
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(A + (base + r) * PT + base + 4 * v4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) arow[4 * v4 + e] = t[e];
+            }
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < r) acc += A[(base + r) * PT + base + i] * x[i];
+                if (i < r) acc += arow[i] * x[i];
             x[r] = (r < c) ? 0.f : (r == c ? 1.f : -acc);
         }
 #pragma unroll
@@ -257,230 +249,188 @@ template <int C, int DK, int DV, typename T>
 __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     typedef PrepCfg<C, DK, DV, T> P;
     typedef Frag<T> F;
-    constexpr int NT = P::NT, NW = P::NW, RPK = P::RPK, RPV = P::RPV;
-    constexpr int P64 = P::P64, PT = P::PT;
-    constexpr int TR = C / 16, NTILE = TR * (TR + 1) / 2, TPW = (NTILE + NW - 1) / NW;
+    typedef typename F::Vec V;
+    constexpr int NW = P::NW, NT = P::NT, NKG = P::NKG, NVG = P::NVG, PT = P::PT, PW = P::PW;
+    constexpr int EPL = F::EPL;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float *tot = reinterpret_cast<float *>(smem);  // [RGK][DK] row-group sums of log alpha
-    float *bet = tot + P::RGK * DK;                 // [C]
+    float *tot = reinterpret_cast<float *>(smem);  // [NW][DK] per-wave sums of log alpha
+    float *bet = tot + NW * DK;                     // [C] beta per chunk row
     unsigned char *R = smem + P::SMALL;
-    T *stage = reinterpret_cast<T *>(R);            // output staging (fragment order)
-    T *Kp = reinterpret_cast<T *>(R);               // [C][P64] k exp(g - m), one 64-channel block
-    T *Km = Kp + C * P64;                           // [C][P64] k exp(m - g)
-    T *Qp = Km + C * P64;                           // [C][P64] scale q exp(g - m)
-    float *Tm = reinterpret_cast<float *>(R);       // [C][PT]
-    float *Am = Tm + C * PT;                        // [C][PT]
-    T *OpB = reinterpret_cast<T *>(R + P::MATF);    // [64][C] B operand block, fragment order
-    T *Wst = reinterpret_cast<T *>(R + P::MATF + P::OPB);  // [C][64] W block, fragment order
+    T *Km = reinterpret_cast<T *>(R);                            // [C][DK] frag order: k exp(m - g)
+    T *KtS = Km + C * DK;                                        // [DK][C] frag order: KtT staging
+    T *Aqs = reinterpret_cast<T *>(R);                           // [C][C] frag order: Aqk staging
+    float *Tm = reinterpret_cast<float *>(R);                    // [C][PT]
+    float *Am = Tm + C * PT;                                     // [C][PT]
+    T *OpB = reinterpret_cast<T *>(R + P::MATF);                 // [PW][C] frag order: B operand
+    T *Wst = OpB + PW * C;                                       // [C][PW] frag order: W staging
 
     const int j = blockIdx.x, h = blockIdx.y;
     int s, t0, L;
     if (!a.map.locate(j, s, t0, L)) return;  // past the last chunk (same for the whole block)
     (void)s;
-    const int tid = threadIdx.x, w = tid >> 6;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, hi = l >> 4;
+    const int r = 16 * w + lr;  // the chunk row this lane holds
+    const bool valid = r < L;
     const int H = a.H;
+    const size_t tok = (size_t)(t0 + (valid ? r : 0)) * H + h;
     const size_t jh = (size_t)j * H + h;
-    const int rk0 = (tid / P::CGK) * RPK, ck0 = 8 * (tid % P::CGK);  // key tile: rows, channels
-    const int rv0 = (tid / P::CGV) * RPV, cv0 = 8 * (tid % P::CGV);  // value tile
+    const float scale = a.scale;
 
-    // ---- 0. the key-side global loads of this thread, before anything else
-    float kr[RPK][8], qr[RPK][8], g[RPK][8], bk[RPK];
+    // ---- 0. this lane's row of k, q and log alpha, in matrix-core operand order
+    V kr[NKG], qr[NKG];
+    float g[NKG][EPL];
+    float b = 0.f;
 #pragma unroll
-    for (int i = 0; i < RPK; ++i) {
-        const int row = rk0 + i;
-        if (row < L) {
-            const size_t o = ((size_t)(t0 + row) * H + h) * DK + ck0;
-            load8<T>(static_cast<const T *>(a.k) + o, kr[i]);
-            load8<T>(static_cast<const T *>(a.q) + o, qr[i]);
-            load8<float>(a.log_alpha + o, g[i]);
-            bk[i] = a.beta[(size_t)(t0 + row) * H + h];
+    for (int kg = 0; kg < NKG; ++kg) {
+        if (valid) {
+            kr[kg] = load_row_frag<T>(static_cast<const T *>(a.k) + tok * DK, kg, hi);
+            qr[kg] = load_row_frag<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
+            load_row_f32<T>(a.log_alpha + tok * DK, kg, hi, g[kg]);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kr[i][e] = qr[i][e] = g[i][e] = 0.f;
-            bk[i] = 0.f;
-        }
-    }
-    if (tid < C) bet[tid] = (tid < L) ? a.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-
-    // ---- 1. inclusive running sum of log alpha: within the thread's rows, then
-    //         across row groups (sums added in row-group order, so the last row's
-    //         g equals gamma exactly)
-#pragma unroll
-    for (int i = 1; i < RPK; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) g[i][e] += g[i - 1][e];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tot[(tid / P::CGK) * DK + ck0 + e] = g[RPK - 1][e];
-    __syncthreads();
-    float off[8], gam[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) off[e] = gam[e] = 0.f;
-    for (int gg = 0; gg < P::RGK; ++gg) {
-        const bool before = gg < tid / P::CGK;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = tot[gg * DK + ck0 + e];
-            if (before) off[e] += x;
-            gam[e] += x;
-        }
-    }
-
-#pragma unroll
-    for (int i = 0; i < RPK; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) g[i][e] += off[e];
-    float mid[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mid[e] = 0.5f * gam[e];
-
-    T *chunk_QO = static_cast<T *>(a.buf.QO) + jh * C * DK;
-    T *chunk_KtT = static_cast<T *>(a.buf.KtT) + jh * DK * C;
-    T *chunk_Aqk = static_cast<T *>(a.buf.Aqk) + jh * C * C;
-    T *chunk_W = static_cast<T *>(a.buf.W) + jh * C * DK;
-    T *chunk_U = static_cast<T *>(a.buf.U) + jh * C * DV;
-
-    // ---- 2. QO = scale q exp(g)  (A operand [C][DK])
-#pragma unroll
-    for (int i = 0; i < RPK; ++i) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = a.scale * qr[i][e] * __expf(g[i][e]);
-        frag_store_row8<T>(stage, rk0 + i, ck0, x, C);
-    }
-    __syncthreads();
-    copy_out<T, NT>(chunk_QO, stage, C * DK);
-    __syncthreads();
-
-    // ---- 3. KtT = (k exp(gamma - g))^T  (A operand [DK][C])
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float x[RPK];
-#pragma unroll
-        for (int i = 0; i < RPK; ++i) x[i] = kr[i][e] * __expf(gam[e] - g[i][e]);
-        frag_store_col<T, RPK>(stage, ck0 + e, rk0, x, DK);
-    }
-    __syncthreads();
-    copy_out<T, NT>(chunk_KtT, stage, DK * C);
-    __syncthreads();
-
-    // ---- 4. decayed Gram matrices, 64 key channels at a time
-    f32x4 akk[TPW], aqk[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) akk[t] = aqk[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < DK / 64; ++b) {
-        if (ck0 / 64 == b) {
-            const int cl = ck0 - 64 * b;
-#pragma unroll
-            for (int i = 0; i < RPK; ++i) {
-                float xp[8], xm[8], xq[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ep = __expf(clamp85(g[i][e] - mid[e]));
-                    const float em = __expf(clamp85(mid[e] - g[i][e]));
-                    xp[e] = kr[i][e] * ep;
-                    xm[e] = kr[i][e] * em;
-                    xq[e] = a.scale * qr[i][e] * ep;
-                }
-                T *dp = Kp + (rk0 + i) * P64 + cl, *dm = Km + (rk0 + i) * P64 + cl, *dq = Qp + (rk0 + i) * P64 + cl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    dp[e] = from_f32<T>(xp[e]);
-                    dm[e] = from_f32<T>(xm[e]);
-                    dq[e] = from_f32<T>(xq[e]);
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int tile = w + NW * t;
-            if (tile < NTILE) {
-                int ti, tj;
-                tri_tile(tile, ti, tj);
-                akk[t] = mma_nt<T>(akk[t], Kp + ti * 16 * P64, P64, Km + tj * 16 * P64, P64, 0, 64);
-                aqk[t] = mma_nt<T>(aqk[t], Qp + ti * 16 * P64, P64, Km + tj * 16 * P64, P64, 0, 64);
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- 5. A (strictly lower, rows scaled by beta) -> fp32 LDS;
-    //         Aqk (lower, diagonal included) -> memory (A operand [C][C])
-    for (int e = tid; e < C * PT; e += NT) Am[e] = 0.f;
-    for (int e = tid; e < C * C; e += NT) stage[e] = from_f32<T>(0.f);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int tile = w + NW * t;
-        if (tile < NTILE) {
-            int ti, tj;
-            tri_tile(tile, ti, tj);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ti * 16 + acc_row(i), c = tj * 16 + acc_col();
-                Am[r * PT + c] = (c < r) ? bet[r] * akk[t][i] : 0.f;
-                stage[frag_off<T>(r, c, C)] = from_f32<T>((c <= r) ? aqk[t][i] : 0.f);
+            for (int e = 0; e < EPL; ++e) {
+                kr[kg][e] = from_f32<T>(0.f);
+                qr[kg][e] = from_f32<T>(0.f);
+                g[kg][e] = 0.f;
             }
         }
     }
+    if (valid) b = a.beta[tok];
+    if (hi == 0) bet[r] = b;
+
+    // ---- 1. inclusive running sum of log alpha down the chunk: within the
+    //         wave's 16 rows by a DPP scan, then across waves through LDS (sums
+    //         taken in wave order, so the last row's g equals gamma exactly)
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            g[kg][e] = row16_inclusive_sum(g[kg][e]);
+            if (lr == 15) tot[w * DK + F::chan(kg, hi, e)] = g[kg][e];
+        }
     __syncthreads();
-    copy_out<T, NT>(chunk_Aqk, stage, C * C);
+    float gam[NKG][EPL];
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            float off = 0.f, all = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float x = tot[ww * DK + F::chan(kg, hi, e)];
+                if (ww < w) off += x;
+                all += x;
+            }
+            g[kg][e] += off;
+            gam[kg][e] = all;
+        }
+
+    // ---- 2. QO = scale q exp(g) straight to memory (this lane's fragment slot);
+    //         Gram factors: k exp(g - m), scale q exp(g - m) stay in registers,
+    //         k exp(m - g) goes to LDS for the other waves; KtT = (k exp(gamma - g))^T
+    //         is staged (transposed) in LDS
+    T *gQO = static_cast<T *>(a.buf.QO) + jh * C * DK;
+    V kp[NKG], qp[NKG];
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) {
+        float xo[EPL], xp[EPL], xq[EPL], xm[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
+            const float x = g[kg][e], m = 0.5f * gam[kg][e];
+            const float ep = __expf(clamp85(x - m)), em = __expf(clamp85(m - x));
+            xo[e] = qv * __expf(x);
+            xp[e] = kv * ep;
+            xq[e] = qv * ep;
+            xm[e] = kv * em;
+            KtS[frag_off<T>(F::chan(kg, hi, e), r, DK)] = from_f32<T>(kv * __expf(gam[kg][e] - x));
+        }
+        *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
+        kp[kg] = pack_frag<T>(xp);
+        qp[kg] = pack_frag<T>(xq);
+        *reinterpret_cast<V *>(Km + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xm);
+    }
+    __syncthreads();
+    copy_out<T, NT>(static_cast<T *>(a.buf.KtT) + jh * DK * C, KtS, DK * C);
+
+    // ---- 3. decayed Gram tiles of this wave's row block: (w, tj) for tj <= w
+    f32x4 akk[NW], aqk[NW];
+#pragma unroll
+    for (int tj = 0; tj < NW; ++tj) {
+        akk[tj] = aqk[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tj <= w) {
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg) {
+                const V bm = frag_load<T>(Km, kg, tj, C);
+                akk[tj] = F::mma(akk[tj], kp[kg], bm);
+                aqk[tj] = F::mma(aqk[tj], qp[kg], bm);
+            }
+        }
+    }
+    __syncthreads();  // Km and KtT staging are free again
+
+    // ---- 4. A (strictly lower, rows scaled by beta) -> fp32 LDS;
+    //         Aqk (lower, diagonal included; zero above) -> memory
+#pragma unroll
+    for (int tj = 0; tj < NW; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * w + acc_row(i), cc = 16 * tj + acc_col();
+            if (tj <= w) Am[rr * PT + cc] = (cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
+            Aqs[frag_off<T>(rr, cc, C)] = from_f32<T>((cc <= rr) ? aqk[tj][i] : 0.f);
+        }
+    __syncthreads();
+    copy_out<T, NT>(static_cast<T *>(a.buf.Aqk) + jh * C * C, Aqs, C * C);
     __syncthreads();
 
-    // ---- 6. T = (I + A)^{-1}, with the value rows in flight meanwhile
-    float vx[RPV][8], bv[RPV];
+    // ---- 5. T = (I + A)^{-1}, with this lane's row of v in flight meanwhile
+    V vr[NVG];
 #pragma unroll
-    for (int i = 0; i < RPV; ++i) {
-        const int row = rv0 + i;
-        if (row < L) {
-            load8<T>(static_cast<const T *>(a.v) + ((size_t)(t0 + row) * H + h) * DV + cv0, vx[i]);
-            bv[i] = a.beta[(size_t)(t0 + row) * H + h];
+    for (int kg = 0; kg < NVG; ++kg) {
+        if (valid) {
+            vr[kg] = load_row_frag<T>(static_cast<const T *>(a.v) + tok * DV, kg, hi);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vx[i][e] = 0.f;
-            bv[i] = 0.f;
+            for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
         }
     }
     unit_lower_inverse<C, PT, T, NT>(Am, Tm);
 
-    // ---- 7. W = T (beta k exp(g)) and U~ = T (beta v), 64 output columns at a time
+    // ---- 6. W = T (beta k exp(g)) and U~ = T (beta v), PW output columns per pass
+    constexpr int NCG = C / F::KG;
+    const int kgmax = ((w + 1) * 16 + F::KG - 1) / F::KG;  // T is lower triangular
+    V tf[NCG];
 #pragma unroll
-    for (int b = 0; b < DK / 64 + DV / 64; ++b) {
-        const bool isW = b < DK / 64;
-        const int cb = isW ? b : b - DK / 64;
-        if (isW && ck0 / 64 == cb) {
+    for (int kg = 0; kg < NCG; ++kg)
+        if (kg < kgmax) tf[kg] = a_frag_f32<T>(Tm, PT, 16 * w, kg);
+    T *gW = static_cast<T *>(a.buf.W) + jh * C * DK;
+    T *gU = static_cast<T *>(a.buf.U) + jh * C * DV;
+    // one pass: output columns [c0, c0 + width) of W (isW) or of U~
+    auto pass = [&](bool isW, int c0, int width) {
+        // B operand [width][C]: (beta k exp(g))^T or (beta v)^T, from this lane's row
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x[RPK];
+        for (int kg = 0; kg < (isW ? NKG : NVG); ++kg)
 #pragma unroll
-                for (int i = 0; i < RPK; ++i) x[i] = bk[i] * kr[i][e] * __expf(g[i][e]);
-                frag_store_col<T, RPK>(OpB, ck0 - 64 * cb + e, rk0, x, 64);
+            for (int e = 0; e < EPL; ++e) {
+                const int ch = F::chan(kg, hi, e);
+                if (ch >= c0 && ch < c0 + width) {
+                    const float val = isW ? b * to_f32(kr[kg][e]) * __expf(g[kg][e]) : b * to_f32(vr[kg][e]);
+                    OpB[frag_off<T>(ch - c0, r, width)] = from_f32<T>(val);
+                }
             }
-        }
-        if (!isW && cv0 / 64 == cb) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x[RPV];
-#pragma unroll
-                for (int i = 0; i < RPV; ++i) x[i] = bv[i] * vx[i][e];
-                frag_store_col<T, RPV>(OpB, cv0 - 64 * cb + e, rv0, x, 64);
-            }
-        }
         __syncthreads();
-        const int kgmax = ((w + 1) * 16 + F::KG - 1) / F::KG;  // T is lower triangular
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+        for (int tn = 0; tn < width / 16; ++tn) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kg = 0; kg < kgmax; ++kg)
-                acc = F::mma(acc, a_frag_f32<T>(Tm, PT, w * 16, kg), frag_load<T>(OpB, kg, tn, 64));
+#pragma unroll
+            for (int kg = 0; kg < NCG; ++kg)
+                if (kg < kgmax) acc = F::mma(acc, tf[kg], frag_load<T>(OpB, kg, tn, width));
             if (isW) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    Wst[frag_off<T>(w * 16 + acc_row(i), tn * 16 + acc_col(), C)] = from_f32<T>(acc[i]);
+                    Wst[frag_off<T>(16 * w + acc_row(i), 16 * tn + acc_col(), C)] = from_f32<T>(acc[i]);
             } else {
-                T *dst = chunk_U + acc_tile_off(w, (64 * cb + 16 * tn) >> 4, DV);
+                T *dst = gU + acc_tile_off(w, (c0 >> 4) + tn, DV);
                 if constexpr (sizeof(T) == 2) {
                     bf16 x[4];
 #pragma unroll
@@ -493,13 +443,20 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
         }
         __syncthreads();
         if (isW) {
-            copy_out<T, NT>(chunk_W + 64 * cb * C, Wst, C * 64);
+            copy_out<T, NT>(gW + c0 * C, Wst, C * width);
             __syncthreads();
         }
-    }
-    if (tid < DK / 8 && rk0 == 0) {
+    };
+    constexpr int PWK = DK < PW ? DK : PW, PWV = DV < PW ? DV : PW;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a.buf.eg[jh * DK + ck0 + e] = __expf(gam[e]);
+    for (int p = 0; p < DK / PWK; ++p) pass(true, p * PWK, PWK);
+#pragma unroll
+    for (int p = 0; p < DV / PWV; ++p) pass(false, p * PWV, PWV);
+    if (w == 0 && lr == 0) {
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) a.buf.eg[jh * DK + F::chan(kg, hi, e)] = __expf(gam[kg][e]);
     }
 }
 

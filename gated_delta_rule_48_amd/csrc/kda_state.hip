@@ -73,8 +73,19 @@ __global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
     __shared__ __align__(16) T Ut[DVS * C];   // U^T, fragment order [DVS][C]
 
     const int H = a.H;
-    const int sl = blockIdx.x % NSL;
-    const int sh = blockIdx.x / NSL;
+    // Workgroups are dispatched round-robin over the 8 XCDs. When the number
+    // of (sequence, head) pairs is a multiple of 8, the NSL slices of one pair
+    // get block ids 8 apart, i.e. the same XCD, so the pair's shared operands
+    // (W, QO, Aqk, KtT) are fetched into one L2 once and read there NSL times.
+    int sl, sh;
+    if (NSL > 1 && a.xcd_group) {
+        const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+        sl = idx % NSL;
+        sh = (idx / NSL) * 8 + xcd;
+    } else {
+        sl = blockIdx.x % NSL;
+        sh = blockIdx.x / NSL;
+    }
     const int h = sh % H, s = sh / H;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int col0 = sl * DVS;
@@ -236,20 +247,32 @@ __global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
     }
 }
 
-template <int C, int DK, int DV, typename T>
+template <int C, int DK, int DV, int DVS, typename T>
 hipError_t launch_state_t(const StateArgs &a, int n_seqs, hipStream_t stream) {
-    constexpr int DVS = 32;
     auto kern = kda_state_kernel<C, DK, DV, DVS, T>;
     hipLaunchKernelGGL(kern, dim3(n_seqs * a.H * (DV / DVS)), dim3(4 * C), 0, stream, a);
     return hipGetLastError();
 }
 
+// Slice width: the whole of d_v per workgroup when the (sequence, head) pairs
+// alone fill the chip (no operand is then read twice), else 32 columns so that
+// short batches still spread over the compute units.
+template <int C, int DK, int DV, typename T>
+hipError_t launch_state_w(StateArgs a, int n_seqs, hipStream_t stream) {
+    const int pairs = n_seqs * a.H;
+    a.xcd_group = (pairs % 8) == 0;
+    if constexpr (sizeof(T) == 2) {
+        if (pairs >= 256) return launch_state_t<C, DK, DV, DV, T>(a, n_seqs, stream);
+    }
+    return launch_state_t<C, DK, DV, 32, T>(a, n_seqs, stream);
+}
+
 template <int C, typename T>
 hipError_t dispatch_d(const StateArgs &a, int dk, int dv, int n, hipStream_t st) {
-    if (dk == 64 && dv == 64) return launch_state_t<C, 64, 64, T>(a, n, st);
-    if (dk == 64 && dv == 128) return launch_state_t<C, 64, 128, T>(a, n, st);
-    if (dk == 128 && dv == 64) return launch_state_t<C, 128, 64, T>(a, n, st);
-    return launch_state_t<C, 128, 128, T>(a, n, st);
+    if (dk == 64 && dv == 64) return launch_state_w<C, 64, 64, T>(a, n, st);
+    if (dk == 64 && dv == 128) return launch_state_w<C, 64, 128, T>(a, n, st);
+    if (dk == 128 && dv == 64) return launch_state_w<C, 128, 64, T>(a, n, st);
+    return launch_state_w<C, 128, 128, T>(a, n, st);
 }
 
 }  // namespace

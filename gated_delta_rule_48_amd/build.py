@@ -7,8 +7,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip"]
-HEADERS = ["kda_device.hpp", "kda_internal.hpp"]
+SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_state.hip", "kda_fused.hip", "kda_decode.hip"]
+HEADERS = ["kda_device.hpp", "kda_internal.hpp", "kda_solve.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

@@ -24,6 +24,15 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// The fused pass (one workgroup per (sequence, head), nothing staged in
+// memory) is used when the sequences have one length, the chunk is 64 and the
+// (sequence, head) pairs alone fill the chip; otherwise the split pass
+// (parallel chunk preparation, then state propagation over d_v slices).
+constexpr int kFusedMinPairs = 256;
+bool use_fused(int B, int T, int H, int C, bool varlen) {
+    return !varlen && C == 64 && T > 0 && (int64_t)B * H >= kFusedMinPairs;
+}
+
 struct WsLayout {
     size_t W, U, QO, KtT, Aqk, eg, discard, choff, total;
     int64_t n_chunks;  // upper bound on the number of chunks over all sequences
@@ -35,6 +44,11 @@ bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varl
                WsLayout *L) {
     if (T <= 0) {
         *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        return true;
+    }
+    if (use_fused(B, T, H, C, varlen)) {  // only the discard slot
+        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 256, 0};
+        L->n_chunks = 0;
         return true;
     }
     const size_t esz = io == KDA_BF16 ? 2 : 4;
@@ -133,6 +147,11 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
+    const bool bf = io == KDA_BF16;
+    if (use_fused(B, T, H, chunk, varlen)) {
+        kda::FusedArgs fa{q, k, v, log_alpha, beta, scale, h0, hT, o, ws + L.discard, H, T};
+        return kda::launch_fused(fa, d_k, d_v, bf, B, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     ChunkBuffers buf{};
     if (L.total > 0) {
         buf = ChunkBuffers{ws + L.W, ws + L.U, ws + L.QO, ws + L.KtT, ws + L.Aqk,
@@ -157,7 +176,6 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
         map.seq_len = tokens > 0 ? T : 0;
     }
 
-    const bool bf = io == KDA_BF16;
     if (tokens > 0) {
         kda::PrepArgs pa{q, k, v, log_alpha, beta, scale, H, map, buf};
         if (kda::launch_prep(pa, chunk, d_k, d_v, bf, (int)L.n_chunks, hs) != hipSuccess)

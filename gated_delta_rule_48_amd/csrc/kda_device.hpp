@@ -113,21 +113,27 @@ __device__ __forceinline__ f32x4 mma_nn_f32(f32x4 acc, const float *A, int lda, 
 // wave reads a whole operand group with a single fully coalesced 1 KB access
 // (global memory) or a conflict-free ds_read_b128 (LDS).
 //
-// A group covers 16 rows x KG contraction indices. bf16 (KG = 32): lane
-// l = r + 16*(k/8) holds k % 8 = 0..7, exactly the v_mfma_f32_16x16x32_bf16
-// operand. fp32 (KG = 16): lane l = r + 16*(k%4) holds k/4 = 0..3, i.e. the
-// operands of four consecutive v_mfma_f32_16x16x4_f32 steps. Groups are stored
-// contraction-major: group (kg, row block rb) of an [R][K] matrix starts at
-// element (kg * (R/16) + rb) * 64 * EPL. The same layout serves A operands
-// ([M][K]) and transposed B operands ([N][K]).
+// A group covers 16 rows x KG contraction indices (KG = 32 for bf16, 16 for
+// fp32), EPL = KG / 4 values per lane. Lane l = r + 16*hi holds, in slot j,
+// the contraction index
+//
+//     k = 16 * (j / 4) + 4 * hi + (j % 4)
+//
+// For bf16 that is one v_mfma_f32_16x16x32_bf16 operand; for fp32 slot j is
+// the operand of the j-th of four v_mfma_f32_16x16x4_f32 steps. The order is a
+// permutation of the natural one, applied identically to both operands of
+// every product, so it does not change any result. It is chosen because a
+// 16x16 accumulator tile holds rows 4*hi + 0..3 of column r in lane r + 16*hi:
+// the accumulator tiles of contraction indices 0..15 and 16..31 are, slot for
+// slot, the operand of the next product, with no data movement.
+//
+// Groups are stored contraction-major: group (kg, row block rb) of an [R][K]
+// matrix starts at element (kg * (R/16) + rb) * 64 * EPL. The same layout serves
+// A operands ([M][K]) and transposed B operands ([N][K]).
 template <typename T> struct Frag;
 template <> struct Frag<bf16> {
     static constexpr int KG = 32, EPL = 8;
     typedef bf16x8 Vec;
-    // contraction index held by lane-group hi (= lane / 16) in slot j of group kg
-    __device__ __forceinline__ static int chan(int kg, int hi, int j) { return 32 * kg + 8 * hi + j; }
-    __device__ __forceinline__ static int lane_of(int r, int kk) { return (r & 15) + 16 * (kk >> 3); }
-    __device__ __forceinline__ static int slot_of(int kk) { return kk & 7; }
     __device__ __forceinline__ static f32x4 mma(f32x4 acc, Vec a, Vec b) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
@@ -135,22 +141,24 @@ template <> struct Frag<bf16> {
 template <> struct Frag<float> {
     static constexpr int KG = 16, EPL = 4;
     typedef f32x4 Vec;
-    __device__ __forceinline__ static int chan(int kg, int hi, int j) { return 16 * kg + hi + 4 * j; }
-    __device__ __forceinline__ static int lane_of(int r, int kk) { return (r & 15) + 16 * (kk & 3); }
-    __device__ __forceinline__ static int slot_of(int kk) { return kk >> 2; }
     __device__ __forceinline__ static f32x4 mma(f32x4 acc, Vec a, Vec b) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
         return acc;
     }
 };
+// contraction index of slot j held by lane group hi, in group kg
+template <typename T> __device__ __forceinline__ int frag_chan(int kg, int hi, int j) {
+    return Frag<T>::KG * kg + 16 * (j >> 2) + 4 * hi + (j & 3);
+}
 
 // Element offset of (r, k) in a fragment-ordered matrix with R rows.
 template <typename T>
 __device__ __forceinline__ int frag_off(int r, int k, int R) {
     typedef Frag<T> F;
     const int kg = k / F::KG, kk = k % F::KG;
-    return ((kg * (R >> 4) + (r >> 4)) * 64 + F::lane_of(r, kk)) * F::EPL + F::slot_of(kk);
+    const int lane = (r & 15) + 16 * ((kk & 15) >> 2), slot = (kk & 3) + 4 * (kk >> 4);
+    return ((kg * (R >> 4) + (r >> 4)) * 64 + lane) * F::EPL + slot;
 }
 
 // This lane's 16-byte share of group (kg, rb) of a fragment-ordered matrix.

@@ -1,0 +1,450 @@
+// kda_fused.hip -- the whole chunked KDA forward pass of one (sequence, head)
+// in one workgroup: chunk preparation and state propagation fused, the fp32
+// d_k x d_v state resident in matrix-core accumulators for the whole sequence.
+//
+// Per chunk of C = 64 rows the workgroup computes the same quantities as the
+// split pass (kda_prep.hip then kda_state.hip) without writing any of them to
+// memory: decay prefix g and gamma, the decayed Gram matrices, T = (I + A)^{-1},
+// W = T (beta k exp(g)), U~ = T (beta v), then U = U~ - W S,
+// O = QO S + Aqk U and S <- exp(gamma) S + KtT U. The only traffic is the
+// inputs q, k, v, log_alpha, beta (read once, the next chunk's while the current
+// one computes), the outputs o, and h0 / hT.
+//
+// Wave w (of 4) owns chunk rows 16w .. 16w+15; lane l holds row 16w + l%16 with
+// the channels of contraction slot group l/16 (see the permuted fragment order
+// in kda_device.hpp). With that order, every product whose output feeds another
+// product is computed in the orientation whose accumulator tiles already are
+// the next operand (W^T = Kbe^T T^T, Aqk^T = Km Qp^T, O^T = S^T QO^T + U^T Aqk^T);
+// the three operands that need the chunk rows along the contraction (KtT,
+// (beta k exp(g))^T, (beta v)^T) are transposed by one matrix-core product with
+// an identity fragment each, which is exact.
+//
+// The method is the chunk algorithm of the essay "22,580: from GPT-2 to Kimi K3"
+// (yichencityu.github.io, section 6.3: forward-substitution T, W = T K_beta,
+// U = T V_beta, then u = U - w S, o = q S + tril(q k^T) u, S += k^T u) with the
+// per-channel cumulative decay of KDA (aidehub.top summary, Gated DeltaNet
+// section); see kda_prep.hip for the chunk identities.
+
+#include "kda_internal.hpp"
+#include "kda_solve.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kC = 64, kNW = 4, kNT = 256;
+
+template <int DK, int DV, typename T> struct FusedCfg {
+    typedef Frag<T> F;
+    static constexpr int NKG = DK / F::KG, NVG = DV / F::KG, NCG = kC / F::KG, TPG = F::KG / 16;
+    static constexpr int PT = kC + 4;                       // pitch of the fp32 [C][C] matrices
+    static constexpr int STILES = (DK / 16) * (DV / 16) / kNW;  // state tiles per wave
+    static constexpr size_t E = sizeof(T);
+    static constexpr size_t SMALL = (size_t)(kNW * DK + kC + DK) * 4;
+    static constexpr size_t KTT = (size_t)DK * kC * E;         // KtT fragments
+    static constexpr size_t MATF = (size_t)kC * PT * 4;
+    static constexpr size_t OPS = (size_t)(DK + DV) * kC * E;   // Km, then Kbe^T and (beta v)^T
+    static constexpr size_t STATE = (size_t)DV * DK * E + (size_t)DV * kC * E;  // S^T and U^T
+    static constexpr size_t REGION = (OPS + 2 * MATF) > STATE ? (OPS + 2 * MATF) : STATE;
+    static constexpr size_t SMEM = SMALL + KTT + REGION;
+};
+
+__device__ __forceinline__ float clamp85f(float x) { return fminf(fmaxf(x, -85.f), 85.f); }
+
+// Identity operand for transposing with the matrix cores: as B^T of a 16-column
+// tile t within a contraction group, lane l (column l%16) has a one in the slot
+// whose contraction index is 16 t + l%16.
+template <typename T> __device__ __forceinline__ typename Frag<T>::Vec ident_frag(int t) {
+    const int l = threadIdx.x & 63;
+    typename Frag<T>::Vec v;
+#pragma unroll
+    for (int j = 0; j < Frag<T>::EPL; ++j)
+        v[j] = from_f32<T>((frag_chan<T>(0, l >> 4, j) == 16 * t + (l & 15)) ? 1.f : 0.f);
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::Vec pack_vals(const float *x) {
+    typename Frag<T>::Vec v;
+#pragma unroll
+    for (int j = 0; j < Frag<T>::EPL; ++j) v[j] = from_f32<T>(x[j]);
+    return v;
+}
+
+// Store accumulator tile `acc` (rows 4*hi + 0..3 of one 16-row tile) as the
+// slots 4 t .. 4 t + 3 of this lane's share of group (kg, rb) of a
+// fragment-ordered matrix with R rows.
+template <typename T>
+__device__ __forceinline__ void store_acc_slots(T *base, int kg, int rb, int R, int t, f32x4 acc) {
+    const int l = threadIdx.x & 63;
+    T *dst = base + ((kg * (R >> 4) + rb) * 64 + l) * Frag<T>::EPL + 4 * t;
+    if constexpr (sizeof(T) == 2) {
+        bf16 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[i]);
+        *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(x);
+    } else {
+        *reinterpret_cast<f32x4 *>(dst) = acc;
+    }
+}
+
+// Put accumulator tile `acc` into slots 4 t .. 4 t + 3 of a register fragment.
+template <typename T>
+__device__ __forceinline__ void acc_to_slots(typename Frag<T>::Vec &v, int t, f32x4 acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[4 * t + i] = from_f32<T>(acc[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::Vec load_row_frag_f(const T *row, int kg, int hi) {
+    typename Frag<T>::Vec v;
+    if constexpr (sizeof(T) == 2) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(row + frag_chan<T>(kg, hi, 0));
+        const uint2 b = *reinterpret_cast<const uint2 *>(row + frag_chan<T>(kg, hi, 4));
+        const bf16 *pa = reinterpret_cast<const bf16 *>(&a), *pb = reinterpret_cast<const bf16 *>(&b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = pa[e];
+            v[4 + e] = pb[e];
+        }
+    } else {
+        v = *reinterpret_cast<const f32x4 *>(row + frag_chan<T>(kg, hi, 0));
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void load_row_f32_f(const float *row, int kg, int hi, float *out) {
+#pragma unroll
+    for (int r4 = 0; r4 < Frag<T>::EPL / 4; ++r4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(row + frag_chan<T>(kg, hi, 4 * r4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[4 * r4 + e] = a[e];
+    }
+}
+
+// Rows 16w + l%16 of an fp32 row-major matrix as an operand group kg (rounded to T).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::Vec row_frag_f32(const float *M, int ld, int row0, int kg) {
+    const int l = threadIdx.x & 63;
+    typename Frag<T>::Vec v;
+    const float *p = M + (row0 + (l & 15)) * ld;
+#pragma unroll
+    for (int r4 = 0; r4 < Frag<T>::EPL / 4; ++r4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p + frag_chan<T>(kg, l >> 4, 4 * r4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * r4 + e] = from_f32<T>(a[e]);
+    }
+    return v;
+}
+
+
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
+    typedef FusedCfg<DK, DV, T> P;
+    typedef Frag<T> F;
+    typedef typename F::Vec V;
+    constexpr int NKG = P::NKG, NVG = P::NVG, NCG = P::NCG, TPG = P::TPG, EPL = F::EPL, PT = P::PT;
+    constexpr int ST = P::STILES;
+    constexpr int NTN = DV / 16;  // column tiles of the state / outputs
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *tot = reinterpret_cast<float *>(smem);   // [NW][DK] per-wave sums of log alpha
+    float *bet = tot + kNW * DK;                     // [C] beta per chunk row
+    float *egam = bet + kC;                          // [DK] exp(gamma) of the chunk
+    T *KtT = reinterpret_cast<T *>(smem + P::SMALL);  // [DK][C] fragments
+    unsigned char *R = smem + P::SMALL + P::KTT;
+    T *Km = reinterpret_cast<T *>(R);                // [C][DK] fragments (Gram phase)
+    T *KbeT = reinterpret_cast<T *>(R);              // [DK][C] fragments (after the Gram)
+    T *VbT = KbeT + DK * kC;                         // [DV][C] fragments
+    float *Am = reinterpret_cast<float *>(R + P::OPS);  // [C][PT]
+    float *Tm = Am + kC * PT;                           // [C][PT]
+    T *St = reinterpret_cast<T *>(R);                // [DV][DK] fragments: S^T (state phase)
+    T *Ut = St + DV * DK;                            // [DV][C] fragments: U^T
+
+    const int H = a.H;
+    const int s = blockIdx.x / H, h = blockIdx.x % H;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, hi = l >> 4;
+    const int r = 16 * w + lr;  // chunk row held by this lane
+    const float scale = a.scale;
+    const int T_len = a.seq_len;
+    const int n_c = (T_len + kC - 1) / kC;
+    const size_t seq0 = (size_t)s * T_len;
+
+    // state tiles of this wave: t = w * ST + u -> rows (key channels) 16 tm, columns 16 tn
+    auto tile_m = [&](int u) { return (w * ST + u) / NTN; };
+    auto tile_n = [&](int u) { return (w * ST + u) % NTN; };
+    f32x4 accS[ST];
+    {
+        const float *h0 = a.h0 ? a.h0 + ((size_t)s * H + h) * DK * DV : nullptr;
+#pragma unroll
+        for (int u = 0; u < ST; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                accS[u][i] = h0 ? h0[(16 * tile_m(u) + 4 * hi + i) * DV + 16 * tile_n(u) + lr] : 0.f;
+    }
+
+    // ---- this lane's inputs of one chunk
+    V kr[NKG], qr[NKG], vr[NVG];
+    float gl[NKG][EPL];
+    float bta;
+    auto load_inputs = [&](int ci) {
+        const int t0 = ci * kC;
+        const bool valid = t0 + r < T_len;
+        const size_t tok = (seq0 + (valid ? t0 + r : 0)) * H + h;
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg) {
+            kr[kg] = load_row_frag_f<T>(static_cast<const T *>(a.k) + tok * DK, kg, hi);
+            qr[kg] = load_row_frag_f<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
+            load_row_f32_f<T>(a.log_alpha + tok * DK, kg, hi, gl[kg]);
+        }
+#pragma unroll
+        for (int kg = 0; kg < NVG; ++kg) vr[kg] = load_row_frag_f<T>(static_cast<const T *>(a.v) + tok * DV, kg, hi);
+        bta = a.beta[tok];
+        if (!valid) {  // rows past the end: zero inputs contribute nothing
+            bta = 0.f;
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    kr[kg][e] = from_f32<T>(0.f);
+                    qr[kg][e] = from_f32<T>(0.f);
+                    gl[kg][e] = 0.f;
+                }
+#pragma unroll
+            for (int kg = 0; kg < NVG; ++kg)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
+        }
+    };
+    if (n_c > 0) load_inputs(0);
+
+    const V id0 = ident_frag<T>(0), id1 = ident_frag<T>(TPG - 1);
+    T *o = static_cast<T *>(a.o);
+
+    for (int ci = 0; ci < n_c; ++ci) {
+        const int t0 = ci * kC;
+
+        // ---- 1. inclusive prefix of log alpha down the chunk (DPP row scan, then waves)
+        float g[NKG][EPL], gam[NKG][EPL];
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                g[kg][e] = row16_inclusive_sum(gl[kg][e]);
+                if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
+            }
+        if (hi == 0) bet[r] = bta;
+        __syncthreads();
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                float off = 0.f, all = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kNW; ++ww) {
+                    const float x = tot[ww * DK + frag_chan<T>(kg, hi, e)];
+                    if (ww < w) off += x;
+                    all += x;
+                }
+                g[kg][e] += off;
+                gam[kg][e] = all;
+            }
+
+        // ---- 2. elementwise: Gram factors, QO, and the rows to be transposed.
+        //      u = exp(g - m), 1/u = exp(m - g) with m = gamma / 2; exp(g) = u E,
+        //      exp(gamma - g) = E / u with E = exp(m) per channel.
+        V kp[NKG], qp[NKG], qo[NKG], kts[NKG], kbe[NKG], vb[NVG];
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg) {
+            float xp[EPL], xq[EPL], xo[EPL], xm[EPL], xt[EPL], xb[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float m = 0.5f * gam[kg][e];
+                const float E = __expf(m);
+                const float u = __expf(clamp85f(g[kg][e] - m)), ui = __expf(clamp85f(m - g[kg][e]));
+                const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
+                xp[e] = kv * u;
+                xq[e] = qv * u;
+                xm[e] = kv * ui;
+                xo[e] = xq[e] * E;
+                xt[e] = xm[e] * E;
+                xb[e] = bta * xp[e] * E;
+                if (r == 0) egam[frag_chan<T>(kg, hi, e)] = E * E;  // exp(gamma): the state's decay
+            }
+            kp[kg] = pack_vals<T>(xp);
+            qp[kg] = pack_vals<T>(xq);
+            qo[kg] = pack_vals<T>(xo);
+            kts[kg] = pack_vals<T>(xt);
+            kbe[kg] = pack_vals<T>(xb);
+            *reinterpret_cast<V *>(Km + ((kg * kNW + w) * 64 + l) * EPL) = pack_vals<T>(xm);
+        }
+#pragma unroll
+        for (int kg = 0; kg < NVG; ++kg) {
+            float xv[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) xv[e] = bta * to_f32(vr[kg][e]);
+            vb[kg] = pack_vals<T>(xv);
+        }
+        __syncthreads();  // Km complete
+        if (ci + 1 < n_c) load_inputs(ci + 1);  // next chunk's rows arrive while this one computes
+
+        // ---- 3. decayed Gram tiles of row block w: A (rows w) and Aqk^T (columns w)
+        f32x4 akk[kNW], aqt[kNW];
+#pragma unroll
+        for (int tj = 0; tj < kNW; ++tj) {
+            akk[tj] = aqt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tj <= w) {
+#pragma unroll
+                for (int kg = 0; kg < NKG; ++kg) {
+                    const V km = frag_load<T>(Km, kg, tj, kC);
+                    akk[tj] = F::mma(akk[tj], kp[kg], km);
+                    aqt[tj] = F::mma(aqt[tj], km, qp[kg]);
+                }
+            }
+        }
+        // Aqk rows of block w as operand groups: Aqk[r][i] = Aqk^T tile (i-block tj), i <= r
+        V aqf[NCG];
+#pragma unroll
+        for (int tj = 0; tj < kNW; ++tj) {
+            f32x4 x = aqt[tj];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (16 * tj + 4 * hi + i <= r) ? x[i] : 0.f;
+            acc_to_slots<T>(aqf[tj / TPG], tj % TPG, x);
+        }
+        __syncthreads();  // every wave is done reading Km (Kbe^T and Vb^T take its place)
+#pragma unroll
+        for (int tj = 0; tj < kNW; ++tj)
+            if (tj <= w) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * w + 4 * hi + i, cc = 16 * tj + lr;
+                    Am[rr * PT + cc] = (cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
+                }
+            }
+        // transposes through the matrix cores (identity operand): KtT, Kbe^T, Vb^T.
+        // Rows 16w.. of the chunk are contraction slots 4 (w % TPG) .. of group w / TPG.
+#pragma unroll
+        for (int tc = 0; tc < DK / 16; ++tc) {
+            const V id = (tc % TPG) ? id1 : id0;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            store_acc_slots<T>(KtT, w / TPG, tc, DK, w % TPG, F::mma(z, kts[tc / TPG], id));
+            store_acc_slots<T>(KbeT, w / TPG, tc, DK, w % TPG, F::mma(z, kbe[tc / TPG], id));
+        }
+#pragma unroll
+        for (int tc = 0; tc < DV / 16; ++tc) {
+            const V id = (tc % TPG) ? id1 : id0;
+            store_acc_slots<T>(VbT, w / TPG, tc, DV, w % TPG, F::mma(f32x4{0.f, 0.f, 0.f, 0.f}, vb[tc / TPG], id));
+        }
+        __syncthreads();  // A, KtT, Kbe^T, Vb^T complete
+
+        // ---- 4. T = (I + A)^{-1}
+        unit_lower_inverse<kC, PT, T, kNT>(Am, Tm);
+
+        // ---- 5. W (as W^T = Kbe^T T^T, whose tiles are W's row-block-w operand
+        //      groups) and U~ = T Vb (accumulator layout, like W S)
+        const int kgmax = (16 * w + 15) / F::KG + 1;  // T is lower triangular
+        V tf[NCG];
+#pragma unroll
+        for (int kg = 0; kg < NCG; ++kg) tf[kg] = row_frag_f32<T>(Tm, PT, 16 * w, kg);
+        V wf[NKG];
+#pragma unroll
+        for (int tm = 0; tm < DK / 16; ++tm) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kg = 0; kg < NCG; ++kg)
+                if (kg < kgmax) acc = F::mma(acc, frag_load<T>(KbeT, kg, tm, DK), tf[kg]);
+            acc_to_slots<T>(wf[tm / TPG], tm % TPG, acc);
+        }
+        f32x4 ut[NTN];
+#pragma unroll
+        for (int tn = 0; tn < NTN; ++tn) {
+            ut[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kg = 0; kg < NCG; ++kg)
+                if (kg < kgmax) ut[tn] = F::mma(ut[tn], tf[kg], frag_load<T>(VbT, kg, tn, DV));
+        }
+        __syncthreads();  // T, Kbe^T and Vb^T are no longer read
+
+        // ---- 6. state phase
+#pragma unroll
+        for (int u = 0; u < ST; ++u) store_acc_slots<T>(St, tile_m(u) / TPG, tile_n(u), DV, tile_m(u) % TPG, accS[u]);
+        __syncthreads();  // S^T complete
+        // U = U~ - W S  -> U^T (rows 16w.. of the chunk are slots of group w / TPG)
+#pragma unroll
+        for (int tn = 0; tn < NTN; ++tn) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg) acc = F::mma(acc, wf[kg], frag_load<T>(St, kg, tn, DV));
+            store_acc_slots<T>(Ut, w / TPG, tn, DV, w % TPG, ut[tn] - acc);
+        }
+        __syncthreads();  // U^T complete
+        // O^T = S^T QO^T + U^T Aqk^T: lanes hold 4 adjacent columns of row r
+#pragma unroll
+        for (int tn = 0; tn < NTN; ++tn) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg) acc = F::mma(acc, frag_load<T>(St, kg, tn, DV), qo[kg]);
+#pragma unroll
+            for (int kg = 0; kg < NCG; ++kg)
+                if (kg < kgmax) acc = F::mma(acc, frag_load<T>(Ut, kg, tn, DV), aqf[kg]);
+            T *dst = (t0 + r < T_len)
+                         ? o + ((seq0 + t0 + r) * H + h) * DV + 16 * tn + 4 * hi
+                         : static_cast<T *>(a.discard) + 4 * (l & 15);
+            if constexpr (sizeof(T) == 2) {
+                bf16 x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[i]);
+                *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(x);
+            } else {
+                *reinterpret_cast<f32x4 *>(dst) = acc;
+            }
+        }
+        // S <- exp(gamma) S + KtT U (state rows = key channels held by this lane group)
+#pragma unroll
+        for (int u = 0; u < ST; ++u) {
+            const int tm = tile_m(u), tn = tile_n(u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accS[u][i] *= egam[16 * tm + 4 * hi + i];
+#pragma unroll
+            for (int kg = 0; kg < NCG; ++kg)
+                accS[u] = F::mma(accS[u], frag_load<T>(KtT, kg, tm, DK), frag_load<T>(Ut, kg, tn, DV));
+        }
+        __syncthreads();  // S^T, U^T and KtT free for the next chunk
+    }
+
+    if (a.hT) {
+        float *hT = a.hT + ((size_t)s * H + h) * DK * DV;
+#pragma unroll
+        for (int u = 0; u < ST; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hT[(16 * tile_m(u) + 4 * hi + i) * DV + 16 * tile_n(u) + lr] = accS[u][i];
+    }
+}
+
+template <int DK, int DV, typename T>
+hipError_t launch_fused_t(const FusedArgs &a, int n_seqs, hipStream_t stream) {
+    constexpr size_t smem = FusedCfg<DK, DV, T>::SMEM;
+    static_assert(smem <= 160 * 1024, "fused LDS budget");
+    auto kern = kda_fused_kernel<DK, DV, T>;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(n_seqs * a.H), dim3(kNT), smem, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_d(const FusedArgs &a, int dk, int dv, int n, hipStream_t st) {
+    if (dk == 64 && dv == 64) return launch_fused_t<64, 64, T>(a, n, st);
+    if (dk == 64 && dv == 128) return launch_fused_t<64, 128, T>(a, n, st);
+    if (dk == 128 && dv == 64) return launch_fused_t<128, 64, T>(a, n, st);
+    return launch_fused_t<128, 128, T>(a, n, st);
+}
+
+}  // namespace
+
+hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream) {
+    return bf16 ? dispatch_d<kda::bf16>(a, dk, dv, n_seqs, stream) : dispatch_d<float>(a, dk, dv, n_seqs, stream);
+}
+
+}  // namespace kda

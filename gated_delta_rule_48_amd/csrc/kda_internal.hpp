@@ -41,6 +41,18 @@ struct StateArgs {
     ChunkBuffers buf;
 };
 
+struct FusedArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    float scale;
+    const float *h0;
+    float *hT;
+    void *o;
+    void *discard;  // absorbs stores of rows past a sequence end (256 bytes)
+    int H;
+    int seq_len;    // every sequence has seq_len tokens
+};
+
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta;
@@ -57,6 +69,7 @@ hipError_t launch_prep(const PrepArgs &a, int C, int dk, int dv, bool bf16, int 
                        hipStream_t stream);
 hipError_t launch_state(const StateArgs &a, int C, int dk, int dv, bool bf16, int n_seqs,
                         hipStream_t stream);
+hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dk, int dv, bool bf16, hipStream_t stream);
 
 }  // namespace kda

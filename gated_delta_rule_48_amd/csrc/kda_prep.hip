@@ -34,6 +34,7 @@
 // fragment-ordered layouts the state kernel reads.
 
 #include "kda_internal.hpp"
+#include "kda_solve.hpp"
 
 namespace kda {
 namespace {
@@ -66,35 +67,35 @@ __device__ __forceinline__ void copy_out(T *dst, const T *src, int n) {
 }
 
 // This lane's operand share of group kg of one row (the values at channels
-// Frag<T>::chan(kg, hi, 0..EPL-1)), from a row of `row` in global memory.
+// frag_chan<T>(kg, hi, 0..EPL-1)), from a row in global memory: runs of 4
+// consecutive channels.
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::Vec load_row_frag(const T *row, int kg, int hi) {
     typedef Frag<T> F;
+    typename F::Vec v;
     if constexpr (sizeof(T) == 2) {
-        return *reinterpret_cast<const typename F::Vec *>(row + F::chan(kg, hi, 0));
-    } else {
-        typename F::Vec v;
+        const uint2 a = *reinterpret_cast<const uint2 *>(row + frag_chan<T>(kg, hi, 0));
+        const uint2 b = *reinterpret_cast<const uint2 *>(row + frag_chan<T>(kg, hi, 4));
+        const bf16 *pa = reinterpret_cast<const bf16 *>(&a), *pb = reinterpret_cast<const bf16 *>(&b);
 #pragma unroll
-        for (int j = 0; j < F::EPL; ++j) v[j] = row[F::chan(kg, hi, j)];
-        return v;
+        for (int e = 0; e < 4; ++e) {
+            v[e] = pa[e];
+            v[4 + e] = pb[e];
+        }
+    } else {
+        v = *reinterpret_cast<const f32x4 *>(row + frag_chan<T>(kg, hi, 0));
     }
+    return v;
 }
 
 // The fp32 values at the same channels (log alpha is fp32 for both dtypes).
 template <typename T>
 __device__ __forceinline__ void load_row_f32(const float *row, int kg, int hi, float *out) {
-    typedef Frag<T> F;
-    if constexpr (sizeof(T) == 2) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(row + F::chan(kg, hi, 0));
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(row + F::chan(kg, hi, 4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            out[e] = a[e];
-            out[4 + e] = b[e];
-        }
-    } else {
+    for (int r4 = 0; r4 < Frag<T>::EPL / 4; ++r4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(row + frag_chan<T>(kg, hi, 4 * r4));
 #pragma unroll
-        for (int j = 0; j < F::EPL; ++j) out[j] = row[F::chan(kg, hi, j)];
+        for (int e = 0; e < 4; ++e) out[4 * r4 + e] = a[e];
     }
 }
 
@@ -111,138 +112,14 @@ template <typename T>
 __device__ __forceinline__ typename Frag<T>::Vec a_frag_f32(const float *M, int ld, int row0, int kg) {
     const int l = threadIdx.x & 63;
     typename Frag<T>::Vec v;
-    const float *p = M + (row0 + (l & 15)) * ld + kg * Frag<T>::KG;
-    if constexpr (sizeof(T) == 2) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(p + 8 * (l >> 4));
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 8 * (l >> 4) + 4);
+    const float *p = M + (row0 + (l & 15)) * ld;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = static_cast<bf16>(a[e]);
-            v[4 + e] = static_cast<bf16>(b[e]);
-        }
-    } else {
+    for (int r4 = 0; r4 < Frag<T>::EPL / 4; ++r4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p + frag_chan<T>(kg, l >> 4, 4 * r4));
 #pragma unroll
-        for (int s = 0; s < 4; ++s) v[s] = p[4 * s + (l >> 4)];
+        for (int e = 0; e < 4; ++e) v[4 * r4 + e] = from_f32<T>(a[e]);
     }
     return v;
-}
-
-// Tm = (I + A)^{-1} for A strictly lower triangular (C x C, fp32, pitch PT).
-// 16x16 diagonal blocks by forward substitution (one thread per column), then
-// doubling: [[T1, 0], [X, T2]] with X = -T2 A21 T1, for block sizes 16, 32, 64.
-template <int C, int PT, typename T, int NT>
-__device__ void unit_lower_inverse(const float *A, float *Tm) {
-    const int tid = threadIdx.x;
-    for (int e = tid; e < C * PT / 4; e += NT) reinterpret_cast<f32x4 *>(Tm)[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
-    if (tid < C) {
-        const int base = tid & ~15, c = tid & 15;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            // row r of the diagonal block, read as four 16-byte vectors
-            float arow[16];
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(A + (base + r) * PT + base + 4 * v4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) arow[4 * v4 + e] = t[e];
-            }
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (i < r) acc += arow[i] * x[i];
-            x[r] = (r < c) ? 0.f : (r == c ? 1.f : -acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(base + r) * PT + base + c] = x[r];
-    }
-
-    // Level n = 16 on the vector ALUs: C/32 pairs of 16x16 blocks, 256 entries each.
-    {
-        constexpr int NP = C / 32;
-        constexpr int PER = (NP * 256 + NT - 1) / NT;
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {  // Y = A21 T1, written into the X slot
-            const int e = tid + u * NT;
-            if (e < NP * 256) {
-                const int p = e >> 8, r = (e >> 4) & 15, c = e & 15;
-                const int r0 = (2 * p + 1) * 16, c0 = 2 * p * 16;
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += A[(r0 + r) * PT + c0 + m] * Tm[(c0 + m) * PT + c0 + c];
-                Tm[(r0 + r) * PT + c0 + c] = acc;
-            }
-        }
-        __syncthreads();
-        float res[PER];
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {  // X = -T2 Y
-            const int e = tid + u * NT;
-            res[u] = 0.f;
-            if (e < NP * 256) {
-                const int p = e >> 8, r = (e >> 4) & 15, c = e & 15;
-                const int r0 = (2 * p + 1) * 16, c0 = 2 * p * 16;
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += Tm[(r0 + r) * PT + r0 + m] * Tm[(r0 + m) * PT + c0 + c];
-                res[u] = -acc;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int e = tid + u * NT;
-            if (e < NP * 256) {
-                const int p = e >> 8, r = (e >> 4) & 15, c = e & 15;
-                Tm[((2 * p + 1) * 16 + r) * PT + 2 * p * 16 + c] = res[u];
-            }
-        }
-    }
-
-    // Levels n = 32, 64 on the matrix cores: (n/16)^2 output tiles per pair.
-    constexpr int NW = NT / 64;
-    const int w = tid >> 6;
-#pragma unroll
-    for (int n = 32; 2 * n <= C; n *= 2) {
-        const int NP = C / (2 * n), TPP = (n / 16) * (n / 16), NTL = NP * TPP;
-        constexpr int MAXT = (C * 64 / 512 + NW - 1) / NW;  // tiles per wave at the largest level
-        __syncthreads();
-        for (int t = w; t < NTL; t += NW) {  // Y = A21 T1 into the X slot (X is not read here)
-            const int p = t / TPP, ti = (t % TPP) / (n / 16), tj = t % (n / 16);
-            const int r0 = (2 * p + 1) * n + ti * 16, c0 = 2 * p * n + tj * 16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_nn_f32<T>(acc, A + r0 * PT + 2 * p * n, PT, Tm + (2 * p * n) * PT + c0, PT, 0, n);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Tm[(r0 + acc_row(i)) * PT + c0 + acc_col()] = acc[i];
-        }
-        __syncthreads();
-        f32x4 res[MAXT];
-#pragma unroll
-        for (int u = 0; u < MAXT; ++u) {  // X = -T2 Y
-            const int t = w + NW * u;
-            res[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (t < NTL) {
-                const int p = t / TPP, ti = (t % TPP) / (n / 16), tj = t % (n / 16);
-                const int r0 = (2 * p + 1) * n + ti * 16, c0 = 2 * p * n + tj * 16;
-                res[u] = -mma_nn_f32<T>(res[u], Tm + r0 * PT + (2 * p + 1) * n, PT,
-                                        Tm + ((2 * p + 1) * n) * PT + c0, PT, 0, n);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < MAXT; ++u) {
-            const int t = w + NW * u;
-            if (t < NTL) {
-                const int p = t / TPP, ti = (t % TPP) / (n / 16), tj = t % (n / 16);
-                const int r0 = (2 * p + 1) * n + ti * 16, c0 = 2 * p * n + tj * 16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Tm[(r0 + acc_row(i)) * PT + c0 + acc_col()] = res[u][i];
-            }
-        }
-    }
-    __syncthreads();
 }
 
 template <int C, int DK, int DV, typename T>
@@ -307,7 +184,7 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             g[kg][e] = row16_inclusive_sum(g[kg][e]);
-            if (lr == 15) tot[w * DK + F::chan(kg, hi, e)] = g[kg][e];
+            if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
         }
     __syncthreads();
     float gam[NKG][EPL];
@@ -318,7 +195,7 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             float off = 0.f, all = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                const float x = tot[ww * DK + F::chan(kg, hi, e)];
+                const float x = tot[ww * DK + frag_chan<T>(kg, hi, e)];
                 if (ww < w) off += x;
                 all += x;
             }
@@ -344,7 +221,7 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             xp[e] = kv * ep;
             xq[e] = qv * ep;
             xm[e] = kv * em;
-            KtS[frag_off<T>(F::chan(kg, hi, e), r, DK)] = from_f32<T>(kv * __expf(gam[kg][e] - x));
+            KtS[frag_off<T>(frag_chan<T>(kg, hi, e), r, DK)] = from_f32<T>(kv * __expf(gam[kg][e] - x));
         }
         *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
         kp[kg] = pack_frag<T>(xp);
@@ -413,7 +290,7 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
         for (int kg = 0; kg < (isW ? NKG : NVG); ++kg)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const int ch = F::chan(kg, hi, e);
+                const int ch = frag_chan<T>(kg, hi, e);
                 if (ch >= c0 && ch < c0 + width) {
                     const float val = isW ? b * to_f32(kr[kg][e]) * __expf(g[kg][e]) : b * to_f32(vr[kg][e]);
                     OpB[frag_off<T>(ch - c0, r, width)] = from_f32<T>(val);
@@ -456,7 +333,7 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) a.buf.eg[jh * DK + F::chan(kg, hi, e)] = __expf(gam[kg][e]);
+            for (int e = 0; e < EPL; ++e) a.buf.eg[jh * DK + frag_chan<T>(kg, hi, e)] = __expf(gam[kg][e]);
     }
 }
 

@@ -274,3 +274,31 @@ def test_decode_workload_sampled():
     eo, eh = rel_l2(o, o_ref), rel_l2(st, h_ref)
     say(f"[decode-full] rel_l2 o={eo:.2e} state={eh:.2e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- fused pass
+# Uniform batches with at least 256 (sequence, head) pairs and chunk 64 take the
+# fused pass (one workgroup per pair); the cases below have B * H = 256.
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("T", [200, 1, 64])
+def test_fused_path(io, dk, dv, T):
+    x = gen([T, T], 128, dk, dv, io, seed=7 * T + dk + dv)
+    _check(x, io, 64, f"fused T={T}", varlen=False, B=2, T=T)
+
+
+def test_fused_path_no_h0():
+    x = gen([129, 129], 128, 128, 128, "bf16", h0="zero", seed=77)
+    o, hT = run_packed(x, "bf16", 64, varlen=False, B=2, T=129, h0=False)
+    o_ref, h_ref, _ = oracle_run(x, h0=False)
+    assert rel_l2(o, o_ref) <= TOL["bf16"] and rel_l2(hT, h_ref) <= TOL["bf16"]
+
+
+def test_fused_matches_split():
+    """The same batch through the fused pass ([B, T, H, d]) and through the split
+    pass (packed with cu_seqlens): two schedules of the same arithmetic."""
+    x = gen([300, 300], 128, 128, 128, "f32", seed=79)
+    of, hf = run_packed(x, "f32", 64, varlen=False, B=2, T=300)
+    os_, hs = run_packed(x, "f32", 64, varlen=True)
+    assert rel_l2(of, os_) <= 1e-5 and rel_l2(hf, hs) <= 1e-5

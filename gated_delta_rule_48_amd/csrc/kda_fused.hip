@@ -39,13 +39,14 @@ template <int DK, int DV, typename T> struct FusedCfg {
     static constexpr int PT = kC + 4;                       // pitch of the fp32 [C][C] matrices
     static constexpr int STILES = (DK / 16) * (DV / 16) / kNW;  // state tiles per wave
     static constexpr size_t E = sizeof(T);
-    static constexpr size_t SMALL = (size_t)(kNW * DK + kC + DK) * 4;
-    static constexpr size_t KTT = (size_t)DK * kC * E;         // KtT fragments
+    // tot [NW][DK], beta [C], exp(gamma / 2) [DK], exp(gamma) [DK]
+    static constexpr size_t SMALL = (size_t)(kNW * DK + kC + 2 * DK) * 4;
+    static constexpr size_t TRN = (size_t)(2 * DK + DV) * kC * E;  // KtT, Kbe^T, Vb^T fragments
     static constexpr size_t MATF = (size_t)kC * PT * 4;
-    static constexpr size_t OPS = (size_t)(DK + DV) * kC * E;   // Km, then Kbe^T and (beta v)^T
+    static constexpr size_t PREP = (size_t)kC * DK * E + 2 * MATF;  // Km, A, T
     static constexpr size_t STATE = (size_t)DV * DK * E + (size_t)DV * kC * E;  // S^T and U^T
-    static constexpr size_t REGION = (OPS + 2 * MATF) > STATE ? (OPS + 2 * MATF) : STATE;
-    static constexpr size_t SMEM = SMALL + KTT + REGION;
+    static constexpr size_t REGION = PREP > STATE ? PREP : STATE;
+    static constexpr size_t SMEM = SMALL + TRN + REGION;
 };
 
 __device__ __forceinline__ float clamp85f(float x) { return fminf(fmaxf(x, -85.f), 85.f); }
@@ -150,14 +151,15 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     float *tot = reinterpret_cast<float *>(smem);   // [NW][DK] per-wave sums of log alpha
     float *bet = tot + kNW * DK;                     // [C] beta per chunk row
-    float *egam = bet + kC;                          // [DK] exp(gamma) of the chunk
+    float *ehalf = bet + kC;                         // [DK] exp(gamma / 2) of the chunk
+    float *egam = ehalf + DK;                        // [DK] exp(gamma) of the chunk
     T *KtT = reinterpret_cast<T *>(smem + P::SMALL);  // [DK][C] fragments
-    unsigned char *R = smem + P::SMALL + P::KTT;
-    T *Km = reinterpret_cast<T *>(R);                // [C][DK] fragments (Gram phase)
-    T *KbeT = reinterpret_cast<T *>(R);              // [DK][C] fragments (after the Gram)
+    T *KbeT = KtT + DK * kC;                         // [DK][C] fragments
     T *VbT = KbeT + DK * kC;                         // [DV][C] fragments
-    float *Am = reinterpret_cast<float *>(R + P::OPS);  // [C][PT]
-    float *Tm = Am + kC * PT;                           // [C][PT]
+    unsigned char *R = smem + P::SMALL + P::TRN;
+    T *Km = reinterpret_cast<T *>(R);                // [C][DK] fragments (Gram phase)
+    float *Am = reinterpret_cast<float *>(R + (size_t)kC * DK * sizeof(T));  // [C][PT]
+    float *Tm = Am + kC * PT;                        // [C][PT]
     T *St = reinterpret_cast<T *>(R);                // [DV][DK] fragments: S^T (state phase)
     T *Ut = St + DV * DK;                            // [DV][C] fragments: U^T
 
@@ -224,68 +226,114 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
 
-        // ---- 1. inclusive prefix of log alpha down the chunk (DPP row scan, then waves)
-        float g[NKG][EPL], gam[NKG][EPL];
+        // ---- 1. inclusive prefix of log alpha down the chunk: DPP scan over the
+        //      wave's 16 rows (step-major, so consecutive DPP operations are
+        //      independent), then the sums of earlier waves
+        float g[NKG][EPL];
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) g[kg][e] = gl[kg][e];
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) g[kg][e] += dpp_row_shr<1>(g[kg][e]);
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) g[kg][e] += dpp_row_shr<2>(g[kg][e]);
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) g[kg][e] += dpp_row_shr<4>(g[kg][e]);
 #pragma unroll
         for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                g[kg][e] = row16_inclusive_sum(gl[kg][e]);
+                g[kg][e] += dpp_row_shr<8>(g[kg][e]);
                 if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
             }
         if (hi == 0) bet[r] = bta;
         __syncthreads();
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        float m[NKG][EPL];  // gamma / 2
 #pragma unroll
         for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float off = 0.f, all = 0.f;
+            for (int r4 = 0; r4 < EPL / 4; ++r4) {
+                const int c0 = frag_chan<T>(kg, hi, 4 * r4);
+                f32x4 off = {0.f, 0.f, 0.f, 0.f}, all;
+                for (int ww = 0; ww < wu; ++ww) off += *reinterpret_cast<const f32x4 *>(tot + ww * DK + c0);
+                all = off;
+                for (int ww = wu; ww < kNW; ++ww) all += *reinterpret_cast<const f32x4 *>(tot + ww * DK + c0);
 #pragma unroll
-                for (int ww = 0; ww < kNW; ++ww) {
-                    const float x = tot[ww * DK + frag_chan<T>(kg, hi, e)];
-                    if (ww < w) off += x;
-                    all += x;
+                for (int e = 0; e < 4; ++e) {
+                    g[kg][4 * r4 + e] += off[e];
+                    m[kg][4 * r4 + e] = 0.5f * all[e];
                 }
-                g[kg][e] += off;
-                gam[kg][e] = all;
             }
+        if (tid < DK) {  // per-channel factors, once per channel
+            float all = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kNW; ++ww) all += tot[ww * DK + tid];
+            ehalf[tid] = __expf(0.5f * all);
+            egam[tid] = __expf(all);
+        }
+        __syncthreads();
 
-        // ---- 2. elementwise: Gram factors, QO, and the rows to be transposed.
-        //      u = exp(g - m), 1/u = exp(m - g) with m = gamma / 2; exp(g) = u E,
-        //      exp(gamma - g) = E / u with E = exp(m) per channel.
-        V kp[NKG], qp[NKG], qo[NKG], kts[NKG], kbe[NKG], vb[NVG];
+        // ---- 2. elementwise: u = exp(g - m) and 1/u = exp(m - g), m = gamma / 2.
+        //      Gram factors k u, scale q u (registers) and k / u (LDS, Km);
+        //      QO = scale q exp(g) = scale q u E (registers), with E = exp(m);
+        //      KtT = (k exp(gamma - g))^T = (k E / u)^T, Kbe^T = (beta k exp(g))^T and
+        //      Vb^T = (beta v)^T transposed by the matrix cores straight into LDS.
+        V kp[NKG], qp[NKG], qo[NKG];
 #pragma unroll
         for (int kg = 0; kg < NKG; ++kg) {
-            float xp[EPL], xq[EPL], xo[EPL], xm[EPL], xt[EPL], xb[EPL];
+            float xp[EPL], xq[EPL], xo[EPL], xm[EPL], xt[EPL], xb[EPL], Ev[EPL];
+#pragma unroll
+            for (int r4 = 0; r4 < EPL / 4; ++r4) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(ehalf + frag_chan<T>(kg, hi, 4 * r4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Ev[4 * r4 + e] = t[e];
+            }
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const float m = 0.5f * gam[kg][e];
-                const float E = __expf(m);
-                const float u = __expf(clamp85f(g[kg][e] - m)), ui = __expf(clamp85f(m - g[kg][e]));
+                const float u = __expf(clamp85f(g[kg][e] - m[kg][e]));
+                const float ui = __expf(clamp85f(m[kg][e] - g[kg][e]));
                 const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
                 xp[e] = kv * u;
                 xq[e] = qv * u;
                 xm[e] = kv * ui;
-                xo[e] = xq[e] * E;
-                xt[e] = xm[e] * E;
-                xb[e] = bta * xp[e] * E;
-                if (r == 0) egam[frag_chan<T>(kg, hi, e)] = E * E;  // exp(gamma): the state's decay
+                xo[e] = xq[e] * Ev[e];
+                xt[e] = xm[e] * Ev[e];
+                xb[e] = bta * xp[e] * Ev[e];
             }
             kp[kg] = pack_vals<T>(xp);
             qp[kg] = pack_vals<T>(xq);
             qo[kg] = pack_vals<T>(xo);
-            kts[kg] = pack_vals<T>(xt);
-            kbe[kg] = pack_vals<T>(xb);
             *reinterpret_cast<V *>(Km + ((kg * kNW + w) * 64 + l) * EPL) = pack_vals<T>(xm);
+            const V kts = pack_vals<T>(xt), kbe = pack_vals<T>(xb);
+            // chunk rows 16w.. are contraction slots 4 (w % TPG) .. of group w / TPG
+#pragma unroll
+            for (int t = 0; t < TPG; ++t) {
+                const V id = t ? id1 : id0;
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                store_acc_slots<T>(KtT, w / TPG, TPG * kg + t, DK, w % TPG, F::mma(z, kts, id));
+                store_acc_slots<T>(KbeT, w / TPG, TPG * kg + t, DK, w % TPG, F::mma(z, kbe, id));
+            }
         }
 #pragma unroll
         for (int kg = 0; kg < NVG; ++kg) {
             float xv[EPL];
 #pragma unroll
             for (int e = 0; e < EPL; ++e) xv[e] = bta * to_f32(vr[kg][e]);
-            vb[kg] = pack_vals<T>(xv);
+            const V vb = pack_vals<T>(xv);
+#pragma unroll
+            for (int t = 0; t < TPG; ++t)
+                store_acc_slots<T>(VbT, w / TPG, TPG * kg + t, DV, w % TPG,
+                                   F::mma(f32x4{0.f, 0.f, 0.f, 0.f}, vb, t ? id1 : id0));
         }
-        __syncthreads();  // Km complete
+        __syncthreads();  // Km, KtT, Kbe^T, Vb^T complete
         if (ci + 1 < n_c) load_inputs(ci + 1);  // next chunk's rows arrive while this one computes
 
         // ---- 3. decayed Gram tiles of row block w: A (rows w) and Aqk^T (columns w)
@@ -311,7 +359,6 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             for (int i = 0; i < 4; ++i) x[i] = (16 * tj + 4 * hi + i <= r) ? x[i] : 0.f;
             acc_to_slots<T>(aqf[tj / TPG], tj % TPG, x);
         }
-        __syncthreads();  // every wave is done reading Km (Kbe^T and Vb^T take its place)
 #pragma unroll
         for (int tj = 0; tj < kNW; ++tj)
             if (tj <= w) {
@@ -321,21 +368,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     Am[rr * PT + cc] = (cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
                 }
             }
-        // transposes through the matrix cores (identity operand): KtT, Kbe^T, Vb^T.
-        // Rows 16w.. of the chunk are contraction slots 4 (w % TPG) .. of group w / TPG.
-#pragma unroll
-        for (int tc = 0; tc < DK / 16; ++tc) {
-            const V id = (tc % TPG) ? id1 : id0;
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            store_acc_slots<T>(KtT, w / TPG, tc, DK, w % TPG, F::mma(z, kts[tc / TPG], id));
-            store_acc_slots<T>(KbeT, w / TPG, tc, DK, w % TPG, F::mma(z, kbe[tc / TPG], id));
-        }
-#pragma unroll
-        for (int tc = 0; tc < DV / 16; ++tc) {
-            const V id = (tc % TPG) ? id1 : id0;
-            store_acc_slots<T>(VbT, w / TPG, tc, DV, w % TPG, F::mma(f32x4{0.f, 0.f, 0.f, 0.f}, vb[tc / TPG], id));
-        }
-        __syncthreads();  // A, KtT, Kbe^T, Vb^T complete
+        __syncthreads();  // A complete
 
         // ---- 4. T = (I + A)^{-1}
         unit_lower_inverse<kC, PT, T, kNT>(Am, Tm);
@@ -363,7 +396,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             for (int kg = 0; kg < NCG; ++kg)
                 if (kg < kgmax) ut[tn] = F::mma(ut[tn], tf[kg], frag_load<T>(VbT, kg, tn, DV));
         }
-        __syncthreads();  // T, Kbe^T and Vb^T are no longer read
+        __syncthreads();  // T is no longer read (S^T and U^T take its place)
 
         // ---- 6. state phase
 #pragma unroll
@@ -444,7 +477,8 @@ hipError_t dispatch_d(const FusedArgs &a, int dk, int dv, int n, hipStream_t st)
 }  // namespace
 
 hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream) {
-    return bf16 ? dispatch_d<kda::bf16>(a, dk, dv, n_seqs, stream) : dispatch_d<float>(a, dk, dv, n_seqs, stream);
+    if (!bf16) return hipErrorInvalidValue;  // the fused pass is built for bf16 input only
+    return dispatch_d<kda::bf16>(a, dk, dv, n_seqs, stream);
 }
 
 }  // namespace kda

@@ -296,9 +296,13 @@ def test_fused_path_no_h0():
 
 
 def test_fused_matches_split():
-    """The same batch through the fused pass ([B, T, H, d]) and through the split
-    pass (packed with cu_seqlens): two schedules of the same arithmetic."""
-    x = gen([300, 300], 128, 128, 128, "f32", seed=79)
-    of, hf = run_packed(x, "f32", 64, varlen=False, B=2, T=300)
-    os_, hs = run_packed(x, "f32", 64, varlen=True)
-    assert rel_l2(of, os_) <= 1e-5 and rel_l2(hf, hs) <= 1e-5
+    """The same bf16 batch through the fused pass ([B, T, H, d]) and through the
+    split pass (packed with cu_seqlens): two schedules of the same arithmetic,
+    both within tolerance of the oracle and close to each other."""
+    x = gen([300, 300], 128, 128, 128, "bf16", seed=79)
+    of, hf = run_packed(x, "bf16", 64, varlen=False, B=2, T=300)
+    os_, hs = run_packed(x, "bf16", 64, varlen=True)
+    o_ref, h_ref, _ = oracle_run(x)
+    for o, hT in ((of, hf), (os_, hs)):
+        assert rel_l2(o, o_ref) <= TOL["bf16"] and rel_l2(hT, h_ref) <= TOL["bf16"]
+    assert rel_l2(of, os_) <= 1e-2 and rel_l2(hf, hs) <= 1e-2

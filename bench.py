@@ -18,8 +18,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,6 +38,65 @@ METRIC = "KDA tokens/sec (prefill chunked, decode step) at H=32,d=128; % rooflin
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Sources each prefill schedule's kernels are compiled from: a stored traffic
+# figure is used only while these files are byte-identical to when the
+# counters were taken.
+CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
+COMMON_SRC = ["kda_device.hpp", "kda_internal.hpp", "kda_solve.hpp"]
+PATHS = {
+    "fused": dict(kernel="kda_fused_kernel", sources=["kda_fused.hip"] + COMMON_SRC,
+                  traffic="kda_fused_kernel_batched_prefill_traffic.md"),
+    "split": dict(kernel="kda_prep_kernel + kda_state_kernel",
+                  sources=["kda_prep.hip", "kda_state.hip"] + COMMON_SRC,
+                  traffic="kda_split_pass_batched_prefill_traffic.md"),
+}
+
+
+def prefill_path(B, T, H, chunk, varlen, bf16):
+    """Which schedule kda_chunk_fwd runs for these sizes: the one-launch fused pass
+    (equal-length bf16 sequences, chunk 64, at least 256 (sequence, head) pairs)
+    or the split prep + state pass. Same rule as the library's dispatch."""
+    return "fused" if (not varlen and chunk == 64 and bf16 and T > 0 and B * H >= 256) else "split"
+
+
+def sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(path_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    schedule (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or
+    None when there is none or the kernel sources changed since it was taken."""
+    info = PATHS[path_key]
+    fn = os.path.join(ROOT, "profiles", info["traffic"])
+    if not os.path.exists(fn):
+        return None
+    txt = open(fn).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_h = re.search(r"sources_sha256:\s*([0-9a-f]{64})", txt)
+    if not (m_b and m_h) or m_h.group(1) != sources_digest(info["sources"]):
+        return None
+    return float(m_b.group(1))
+
+
+def copy_probe(torch, mib):
+    """A plain device copy of known size (mib MiB read, mib MiB written), launched
+    three times before the timed work, so that a counter run of this script can
+    calibrate FETCH_SIZE / WRITE_SIZE against exact byte counts."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: 3 x {mib} MiB device copy")
+    del src, dst
 
 
 def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_states_in):
@@ -88,8 +149,9 @@ def bench_prefill(args, kda, torch):
     achieved = alg / (ev_avg * 1e-3) / 1e9
     log(f"[bench] prefill: wall {ms:.3f} ms/step, events avg {ev_avg:.3f} min {min(ev_ms):.3f} ms, "
         f"{tokens / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s algorithmic")
+    path = prefill_path(B, T, H, C, False, True)
     res = dict(ms=ms, ev_ms=ev_avg, tokens_per_s=tokens / (ms * 1e-3), alg_bytes=alg,
-               achieved_gbs=achieved, workload=w, x=x)
+               achieved_gbs=achieved, workload=w, x=x, path=path)
     del q, k, v, la, beta, o, hT, ws
     return res
 
@@ -137,8 +199,8 @@ def bench_decode(args, kda, torch):
 
 
 def cpu_baseline(pre, args):
-    """The fp64 oracle on a bounded sample of the prefill workload: all 32 heads
-    of `--cpu-seqs` of the 8 sequences, full length, on this host's cores."""
+    """The fp64 oracle on the prefill workload's first `--cpu-seqs` sequences (all
+    of them by default: all heads, full length), on this host's cores."""
     import oracle
     x, w = pre["x"], pre["workload"]
     n_seq = args.cpu_seqs
@@ -156,8 +218,8 @@ def cpu_baseline(pre, args):
     tokens = n_seq * T
     log(f"[bench] cpu baseline: {dt:.2f}s, {tokens / dt:.1f} tokens/s")
     return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_seq} of the 8 sequences (all {w.H} heads, {T} tokens each) of the "
-                      f"batched prefill workload; fp64 token-by-token recurrence, {dt:.2f} s"}
+            "sample": f"{n_seq} of the {len(w.seqlens)} sequences (all {w.H} heads, {T} tokens each) of "
+                      f"the batched prefill workload; fp64 token-by-token recurrence, {dt:.2f} s"}
 
 
 def main():
@@ -167,7 +229,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--decode-bank", type=int, default=32)
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="run a device copy of MIB MiB first (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
@@ -181,6 +245,8 @@ def main():
     kda.load()
     torch.cuda.set_device(0)
 
+    if args.copy_probe > 0:
+        copy_probe(torch, args.copy_probe)
     pre = bench_prefill(args, kda, torch)
     dec = None if args.no_decode else bench_decode(args, kda, torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
@@ -205,8 +271,8 @@ def main():
                    "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(pre["achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pre["achieved_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "chunked prefill pass (kda_prep_kernel + kda_state_kernel)",
+                     "traffic": stored_traffic(pre["path"]),
+                     "kernel": PATHS[pre["path"]]["kernel"],
                      "alg_bytes_per_launch": pre["alg_bytes"], "avg_launch_ms": round(pre["ev_ms"], 4)},
         "cpu_baseline": cpu,
     }

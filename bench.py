@@ -54,11 +54,13 @@ PATHS = {
 }
 
 
-def prefill_path(B, T, H, chunk, varlen, bf16):
+def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16):
     """Which schedule kda_chunk_fwd runs for these sizes: the one-launch fused pass
-    (equal-length bf16 sequences, chunk 64, at least 256 (sequence, head) pairs)
-    or the split prep + state pass. Same rule as the library's dispatch."""
-    return "fused" if (not varlen and chunk == 64 and bf16 and T > 0 and B * H >= 256) else "split"
+    (equal-length bf16 sequences, d_k = d_v = 128, chunk 64, at least 256
+    (sequence, head) pairs) or the split prep + state pass. Same rule as the
+    library's dispatch."""
+    fused = (not varlen and chunk == 64 and bf16 and dk == dv == 128 and T > 0 and B * H >= 256)
+    return "fused" if fused else "split"
 
 
 def sources_digest(names):
@@ -149,7 +151,7 @@ def bench_prefill(args, kda, torch):
     achieved = alg / (ev_avg * 1e-3) / 1e9
     log(f"[bench] prefill: wall {ms:.3f} ms/step, events avg {ev_avg:.3f} min {min(ev_ms):.3f} ms, "
         f"{tokens / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s algorithmic")
-    path = prefill_path(B, T, H, C, False, True)
+    path = prefill_path(B, T, H, dk, dv, C, False, True)
     res = dict(ms=ms, ev_ms=ev_avg, tokens_per_s=tokens / (ms * 1e-3), alg_bytes=alg,
                achieved_gbs=achieved, workload=w, x=x, path=path)
     del q, k, v, la, beta, o, hT, ws

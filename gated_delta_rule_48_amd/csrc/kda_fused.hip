@@ -1,484 +1,527 @@
 // kda_fused.hip -- the whole chunked KDA forward pass of one (sequence, head)
-// in one workgroup: chunk preparation and state propagation fused, the fp32
-// d_k x d_v state resident in matrix-core accumulators for the whole sequence.
+// in one workgroup of 8 waves: chunk preparation and state propagation fused,
+// the fp32 128 x 128 state resident in matrix-core accumulators for the whole
+// sequence. Built for bf16 q/k/v/o, d_k = d_v = 128 and chunks of 64 rows.
 //
-// Per chunk of C = 64 rows the workgroup computes the same quantities as the
-// split pass (kda_prep.hip then kda_state.hip) without writing any of them to
-// memory: decay prefix g and gamma, the decayed Gram matrices, T = (I + A)^{-1},
+// Per chunk the workgroup computes the same quantities as the split pass
+// (kda_prep.hip then kda_state.hip) without writing any of them to memory:
+// decay prefix g and gamma, the decayed Gram matrices, T = (I + A)^{-1},
 // W = T (beta k exp(g)), U~ = T (beta v), then U = U~ - W S,
 // O = QO S + Aqk U and S <- exp(gamma) S + KtT U. The only traffic is the
 // inputs q, k, v, log_alpha, beta (read once, the next chunk's while the current
 // one computes), the outputs o, and h0 / hT.
 //
-// Wave w (of 4) owns chunk rows 16w .. 16w+15; lane l holds row 16w + l%16 with
-// the channels of contraction slot group l/16 (see the permuted fragment order
-// in kda_device.hpp). With that order, every product whose output feeds another
-// product is computed in the orientation whose accumulator tiles already are
-// the next operand (W^T = Kbe^T T^T, Aqk^T = Km Qp^T, O^T = S^T QO^T + U^T Aqk^T);
-// the three operands that need the chunk rows along the contraction (KtT,
-// (beta k exp(g))^T, (beta v)^T) are transposed by one matrix-core product with
-// an identity fragment each, which is exact.
-//
 // The method is the chunk algorithm of the essay "22,580: from GPT-2 to Kimi K3"
-// (yichencityu.github.io, section 6.3: forward-substitution T, W = T K_beta,
+// (yichencityu.github.io, section 6.3: T by forward substitution, W = T K_beta,
 // U = T V_beta, then u = U - w S, o = q S + tril(q k^T) u, S += k^T u) with the
 // per-channel cumulative decay of KDA (aidehub.top summary, Gated DeltaNet
-// section); see kda_prep.hip for the chunk identities.
+// section); kda_prep.hip states the chunk identities.
+//
+// Work split. Two waves share each SIMD, so one wave's latencies (exp, LDS,
+// matrix-core results) overlap the other's work. Wave w = rb + 4 hf:
+//   scan, elementwise  chunk rows 16 rb .. 16 rb + 15, key/value channels of
+//                      half hf (64 of 128), lane l = r + 16 hi holding row r;
+//   Gram               hf = 0: rows rb of A = beta K+ K-^T, then the inverse of
+//                      its diagonal block by forward substitution in registers
+//                      (DPP row broadcasts); hf = 1: rows rb of Aqk;
+//   solve              hf = 1, rb < 3: the off-diagonal blocks of column block rb
+//                      of T, one small matrix-core chain per column block;
+//   W, U~              rows rb, d_k (W) and d_v (U~) tiles of half hf;
+//   state              state columns 16 w .. 16 w + 15, all 128 rows.
+// Intermediates pass between phases in LDS in the permuted fragment order of
+// kda_device.hpp, in which two adjacent accumulator tiles are one operand.
 
 #include "kda_internal.hpp"
-#include "kda_solve.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kC = 64, kNW = 4, kNT = 256;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV, typename T> struct FusedCfg {
-    typedef Frag<T> F;
-    static constexpr int NKG = DK / F::KG, NVG = DV / F::KG, NCG = kC / F::KG, TPG = F::KG / 16;
-    static constexpr int PT = kC + 4;                       // pitch of the fp32 [C][C] matrices
-    static constexpr int STILES = (DK / 16) * (DV / 16) / kNW;  // state tiles per wave
-    static constexpr size_t E = sizeof(T);
-    // tot [NW][DK], beta [C], exp(gamma / 2) [DK], exp(gamma) [DK]
-    static constexpr size_t SMALL = (size_t)(kNW * DK + kC + 2 * DK) * 4;
-    static constexpr size_t TRN = (size_t)(2 * DK + DV) * kC * E;  // KtT, Kbe^T, Vb^T fragments
-    static constexpr size_t MATF = (size_t)kC * PT * 4;
-    static constexpr size_t PREP = (size_t)kC * DK * E + 2 * MATF;  // Km, A, T
-    static constexpr size_t STATE = (size_t)DV * DK * E + (size_t)DV * kC * E;  // S^T and U^T
-    static constexpr size_t REGION = PREP > STATE ? PREP : STATE;
-    static constexpr size_t SMEM = SMALL + TRN + REGION;
+constexpr int kC = 64, kDK = 128, kDV = 128, kNT = 512;
+constexpr int kPT = kC + 4;                  // pitch of the fp32 [C][C] matrix A
+constexpr float kL2E = 1.4426950408889634f;  // log2(e): exponents are kept in base 2
+constexpr float kClamp = 85.f * kL2E;        // |exponent| limit of the midpoint factors (e^85)
+
+// LDS layout (bytes). The first block is read by the state phase; the rest is
+// chunk preparation. R1 holds Km, Kp, Qp (elementwise -> Gram), then -W and U~
+// (W, U~ -> state).
+struct Lds {
+    static constexpr int QO = 0;                        // [C][DK]  bf16 fragments
+    static constexpr int KTT = QO + kC * kDK * 2;       // [DK][C]  bf16 fragments
+    static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments
+    static constexpr int EGAM = AQK + kC * kC * 2;      // [DK]     exp(gamma)
+    static constexpr int TOT = EGAM + kDK * 4;          // [4][DK]  log2-decay sum of each row block
+    static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  row-block offset minus gamma/2
+    static constexpr int EHALF = OFFM + 4 * kDK * 4;    // [DK]     exp(gamma / 2)
+    static constexpr int BET = EHALF + kDK * 4;         // [C]      beta (0 past the end)
+    static constexpr int KBET = BET + kC * 4;           // [DK][C]  (beta k exp(g))^T fragments
+    static constexpr int VBT = KBET + kDK * kC * 2;     // [DV][C]  (beta v)^T fragments
+    static constexpr int AM = VBT + kDV * kC * 2;       // [C][PT]  fp32 A (strictly lower)
+    static constexpr int TF = AM + kC * kPT * 4;        // [C][C]   T fragments
+    static constexpr int R1 = TF + kC * kC * 2;
+    static constexpr int KM = R1, KP = R1 + kC * kDK * 2, QP = R1 + 2 * kC * kDK * 2;
+    static constexpr int WN = R1, UT = R1 + kC * kDK * 2;  // -W fragments; U~ fp32 accumulator tiles
+    static constexpr int SIZE = R1 + 3 * kC * kDK * 2;
 };
+static_assert(Lds::UT + kC * kDV * 4 <= Lds::SIZE, "U~ fits in R1");
+static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
-__device__ __forceinline__ float clamp85f(float x) { return fminf(fmaxf(x, -85.f), 85.f); }
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane I of this lane's 16-lane DPP row.
+template <int I> __device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x150 + I, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = static_cast<bf16>(x[i]);
+    return r;
+}
+
+// Two accumulator tiles (contraction indices 0..15 and 16..31 of a group) as one operand.
+__device__ __forceinline__ bf16x8 tiles_to_frag(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = static_cast<bf16>(lo[i]);
+        r[4 + i] = static_cast<bf16>(hi[i]);
+    }
+    return r;
+}
 
 // Identity operand for transposing with the matrix cores: as B^T of a 16-column
 // tile t within a contraction group, lane l (column l%16) has a one in the slot
 // whose contraction index is 16 t + l%16.
-template <typename T> __device__ __forceinline__ typename Frag<T>::Vec ident_frag(int t) {
+__device__ __forceinline__ bf16x8 ident_frag(int t) {
     const int l = threadIdx.x & 63;
-    typename Frag<T>::Vec v;
+    bf16x8 v;
 #pragma unroll
-    for (int j = 0; j < Frag<T>::EPL; ++j)
-        v[j] = from_f32<T>((frag_chan<T>(0, l >> 4, j) == 16 * t + (l & 15)) ? 1.f : 0.f);
+    for (int j = 0; j < 8; ++j)
+        v[j] = static_cast<bf16>((frag_chan<bf16>(0, l >> 4, j) == 16 * t + (l & 15)) ? 1.f : 0.f);
     return v;
 }
 
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::Vec pack_vals(const float *x) {
-    typename Frag<T>::Vec v;
-#pragma unroll
-    for (int j = 0; j < Frag<T>::EPL; ++j) v[j] = from_f32<T>(x[j]);
-    return v;
-}
-
-// Store accumulator tile `acc` (rows 4*hi + 0..3 of one 16-row tile) as the
-// slots 4 t .. 4 t + 3 of this lane's share of group (kg, rb) of a
-// fragment-ordered matrix with R rows.
-template <typename T>
-__device__ __forceinline__ void store_acc_slots(T *base, int kg, int rb, int R, int t, f32x4 acc) {
+// Store accumulator tile `acc` as slots 4 t .. 4 t + 3 of this lane's share of
+// group (kg, rb) of a fragment-ordered matrix with R rows.
+__device__ __forceinline__ void store_slots(bf16 *base, int kg, int rb, int R, int t, f32x4 acc) {
     const int l = threadIdx.x & 63;
-    T *dst = base + ((kg * (R >> 4) + rb) * 64 + l) * Frag<T>::EPL + 4 * t;
-    if constexpr (sizeof(T) == 2) {
-        bf16 x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[i]);
-        *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(x);
-    } else {
-        *reinterpret_cast<f32x4 *>(dst) = acc;
-    }
+    *reinterpret_cast<bf16x4 *>(base + ((kg * (R >> 4) + rb) * 64 + l) * 8 + 4 * t) = to_bf16x4(acc);
 }
 
-// Put accumulator tile `acc` into slots 4 t .. 4 t + 3 of a register fragment.
-template <typename T>
-__device__ __forceinline__ void acc_to_slots(typename Frag<T>::Vec &v, int t, f32x4 acc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[4 * t + i] = from_f32<T>(acc[i]);
-}
-
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::Vec load_row_frag_f(const T *row, int kg, int hi) {
-    typename Frag<T>::Vec v;
-    if constexpr (sizeof(T) == 2) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(row + frag_chan<T>(kg, hi, 0));
-        const uint2 b = *reinterpret_cast<const uint2 *>(row + frag_chan<T>(kg, hi, 4));
-        const bf16 *pa = reinterpret_cast<const bf16 *>(&a), *pb = reinterpret_cast<const bf16 *>(&b);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = pa[e];
-            v[4 + e] = pb[e];
-        }
-    } else {
-        v = *reinterpret_cast<const f32x4 *>(row + frag_chan<T>(kg, hi, 0));
-    }
-    return v;
-}
-
-template <typename T>
-__device__ __forceinline__ void load_row_f32_f(const float *row, int kg, int hi, float *out) {
-#pragma unroll
-    for (int r4 = 0; r4 < Frag<T>::EPL / 4; ++r4) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(row + frag_chan<T>(kg, hi, 4 * r4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[4 * r4 + e] = a[e];
-    }
-}
-
-// Rows 16w + l%16 of an fp32 row-major matrix as an operand group kg (rounded to T).
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::Vec row_frag_f32(const float *M, int ld, int row0, int kg) {
+// This lane's slots 4 t .. 4 t + 3 (one 16 x 16 block's operand) of group (kg, rb).
+__device__ __forceinline__ bf16x4 load_slots(const bf16 *base, int kg, int rb, int R, int t) {
     const int l = threadIdx.x & 63;
-    typename Frag<T>::Vec v;
-    const float *p = M + (row0 + (l & 15)) * ld;
-#pragma unroll
-    for (int r4 = 0; r4 < Frag<T>::EPL / 4; ++r4) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(p + frag_chan<T>(kg, l >> 4, 4 * r4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * r4 + e] = from_f32<T>(a[e]);
-    }
-    return v;
+    return *reinterpret_cast<const bf16x4 *>(base + ((kg * (R >> 4) + rb) * 64 + l) * 8 + 4 * t);
 }
 
+__device__ __forceinline__ bf16x8 load_row_frag(const bf16 *row, int kg, int hi) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row + frag_chan<bf16>(kg, hi, 0));
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(row + frag_chan<bf16>(kg, hi, 4));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
-template <int DK, int DV, typename T>
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
-    typedef FusedCfg<DK, DV, T> P;
-    typedef Frag<T> F;
-    typedef typename F::Vec V;
-    constexpr int NKG = P::NKG, NVG = P::NVG, NCG = P::NCG, TPG = P::TPG, EPL = F::EPL, PT = P::PT;
-    constexpr int ST = P::STILES;
-    constexpr int NTN = DV / 16;  // column tiles of the state / outputs
-
     extern __shared__ __align__(16) unsigned char smem[];
-    float *tot = reinterpret_cast<float *>(smem);   // [NW][DK] per-wave sums of log alpha
-    float *bet = tot + kNW * DK;                     // [C] beta per chunk row
-    float *ehalf = bet + kC;                         // [DK] exp(gamma / 2) of the chunk
-    float *egam = ehalf + DK;                        // [DK] exp(gamma) of the chunk
-    T *KtT = reinterpret_cast<T *>(smem + P::SMALL);  // [DK][C] fragments
-    T *KbeT = KtT + DK * kC;                         // [DK][C] fragments
-    T *VbT = KbeT + DK * kC;                         // [DV][C] fragments
-    unsigned char *R = smem + P::SMALL + P::TRN;
-    T *Km = reinterpret_cast<T *>(R);                // [C][DK] fragments (Gram phase)
-    float *Am = reinterpret_cast<float *>(R + (size_t)kC * DK * sizeof(T));  // [C][PT]
-    float *Tm = Am + kC * PT;                        // [C][PT]
-    T *St = reinterpret_cast<T *>(R);                // [DV][DK] fragments: S^T (state phase)
-    T *Ut = St + DV * DK;                            // [DV][C] fragments: U^T
+    bf16 *QO = reinterpret_cast<bf16 *>(smem + Lds::QO);
+    bf16 *KtT = reinterpret_cast<bf16 *>(smem + Lds::KTT);
+    bf16 *Aqk = reinterpret_cast<bf16 *>(smem + Lds::AQK);
+    float *egam = reinterpret_cast<float *>(smem + Lds::EGAM);
+    float *tot = reinterpret_cast<float *>(smem + Lds::TOT);
+    float *offm = reinterpret_cast<float *>(smem + Lds::OFFM);
+    float *ehalf = reinterpret_cast<float *>(smem + Lds::EHALF);
+    float *bet = reinterpret_cast<float *>(smem + Lds::BET);
+    bf16 *KbeT = reinterpret_cast<bf16 *>(smem + Lds::KBET);
+    bf16 *VbT = reinterpret_cast<bf16 *>(smem + Lds::VBT);
+    float *Am = reinterpret_cast<float *>(smem + Lds::AM);
+    bf16 *Tf = reinterpret_cast<bf16 *>(smem + Lds::TF);
+    bf16 *Km = reinterpret_cast<bf16 *>(smem + Lds::KM);
+    bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
+    bf16 *Qp = reinterpret_cast<bf16 *>(smem + Lds::QP);
+    bf16 *Wn = reinterpret_cast<bf16 *>(smem + Lds::WN);
+    float *Ut = reinterpret_cast<float *>(smem + Lds::UT);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, hi = l >> 4;
-    const int r = 16 * w + lr;  // chunk row held by this lane
+    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, hi = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb = w & 3, hf = w >> 2;
+    const int r = 16 * rb + lr;  // chunk row held by this lane
     const float scale = a.scale;
     const int T_len = a.seq_len;
     const int n_c = (T_len + kC - 1) / kC;
     const size_t seq0 = (size_t)s * T_len;
 
-    // state tiles of this wave: t = w * ST + u -> rows (key channels) 16 tm, columns 16 tn
-    auto tile_m = [&](int u) { return (w * ST + u) / NTN; };
-    auto tile_n = [&](int u) { return (w * ST + u) % NTN; };
-    f32x4 accS[ST];
-    {
-        const float *h0 = a.h0 ? a.h0 + ((size_t)s * H + h) * DK * DV : nullptr;
+    // ---- state columns 16 w .. 16 w + 15: tile tm holds rows 16 tm + 4 hi + i of
+    //      column 16 w + lr
+    f32x4 accS[8];
+    if (a.h0) {
+        const float *h0 = a.h0 + ((size_t)s * H + h) * kDK * kDV + 16 * w + lr;
 #pragma unroll
-        for (int u = 0; u < ST; ++u)
+        for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                accS[u][i] = h0 ? h0[(16 * tile_m(u) + 4 * hi + i) * DV + 16 * tile_n(u) + lr] : 0.f;
+            for (int i = 0; i < 4; ++i) accS[tm][i] = h0[(16 * tm + 4 * hi + i) * kDV];
+    } else {
+#pragma unroll
+        for (int tm = 0; tm < 8; ++tm) accS[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- this lane's inputs of one chunk
-    V kr[NKG], qr[NKG], vr[NVG];
-    float gl[NKG][EPL];
+    // ---- this lane's inputs of one chunk: row r, channel groups 2 hf and 2 hf + 1.
+    //      The next chunk's are requested in four parts spread over the phases
+    //      (a single burst of all of them stalls the issuing waves).
+    bf16x8 kr[2], qr[2], vr[2];
+    float gl[2][8];
     float bta;
-    auto load_inputs = [&](int ci) {
-        const int t0 = ci * kC;
-        const bool valid = t0 + r < T_len;
-        const size_t tok = (seq0 + (valid ? t0 + r : 0)) * H + h;
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg) {
-            kr[kg] = load_row_frag_f<T>(static_cast<const T *>(a.k) + tok * DK, kg, hi);
-            qr[kg] = load_row_frag_f<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
-            load_row_f32_f<T>(a.log_alpha + tok * DK, kg, hi, gl[kg]);
-        }
-#pragma unroll
-        for (int kg = 0; kg < NVG; ++kg) vr[kg] = load_row_frag_f<T>(static_cast<const T *>(a.v) + tok * DV, kg, hi);
-        bta = a.beta[tok];
-        if (!valid) {  // rows past the end: zero inputs contribute nothing
-            bta = 0.f;
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    kr[kg][e] = from_f32<T>(0.f);
-                    qr[kg][e] = from_f32<T>(0.f);
-                    gl[kg][e] = 0.f;
-                }
-#pragma unroll
-            for (int kg = 0; kg < NVG; ++kg)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
-        }
+    auto tok_of = [&](int ci) {
+        // rows past the end read the last row; their beta and decay are zeroed at use
+        return (seq0 + min(ci * kC + r, T_len - 1)) * H + h;
     };
-    if (n_c > 0) load_inputs(0);
+    auto load_k = [&](int ci) {
+        const size_t tok = tok_of(ci);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) kr[x] = load_row_frag(static_cast<const bf16 *>(a.k) + tok * kDK, 2 * hf + x, hi);
+    };
+    auto load_q = [&](int ci) {
+        const size_t tok = tok_of(ci);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) qr[x] = load_row_frag(static_cast<const bf16 *>(a.q) + tok * kDK, 2 * hf + x, hi);
+    };
+    auto load_v = [&](int ci) {
+        const size_t tok = tok_of(ci);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) vr[x] = load_row_frag(static_cast<const bf16 *>(a.v) + tok * kDV, 2 * hf + x, hi);
+    };
+    auto load_g = [&](int ci) {
+        const size_t tok = tok_of(ci);
+        const float *gp = a.log_alpha + tok * kDK;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, hi, 0));
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, hi, 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gl[x][e] = g0[e];
+                gl[x][4 + e] = g1[e];
+            }
+        }
+        bta = a.beta[tok];
+    };
+    load_g(0);
+    load_k(0);
+    load_q(0);
+    load_v(0);
 
-    const V id0 = ident_frag<T>(0), id1 = ident_frag<T>(TPG - 1);
-    T *o = static_cast<T *>(a.o);
+    const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
+    bf16x4 idB;  // the 16 x 16 identity as a B operand of mma16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) idB[i] = static_cast<bf16>(4 * hi + i == lr ? 1.f : 0.f);
+    bf16 *o = static_cast<bf16 *>(a.o);
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
+        const bool valid = t0 + r < T_len;
 
-        // ---- 1. inclusive prefix of log alpha down the chunk: DPP scan over the
-        //      wave's 16 rows (step-major, so consecutive DPP operations are
-        //      independent), then the sums of earlier waves
-        float g[NKG][EPL];
+        // ---- 1. inclusive prefix of log2(alpha) down the chunk: DPP scan over the
+        //      wave's 16 rows, step-major so consecutive DPP operations are
+        //      independent; row-block sums to LDS, their prefix by one thread per channel
+        float g[2][8];
 #pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) g[kg][e] = gl[kg][e];
+            for (int e = 0; e < 8; ++e) g[x][e] = valid ? gl[x][e] * kL2E : 0.f;
+        const float bt = valid ? bta : 0.f;
 #pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) g[kg][e] += dpp_row_shr<1>(g[kg][e]);
+            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<1>(g[x][e]);
 #pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) g[kg][e] += dpp_row_shr<2>(g[kg][e]);
+            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<2>(g[x][e]);
 #pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) g[kg][e] += dpp_row_shr<4>(g[kg][e]);
+            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<4>(g[x][e]);
 #pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                g[kg][e] += dpp_row_shr<8>(g[kg][e]);
-                if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
-            }
-        if (hi == 0) bet[r] = bta;
+            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<8>(g[x][e]);
+        if (lr == 15) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e4 = 0; e4 < 2; ++e4)
+                    *reinterpret_cast<f32x4 *>(tot + rb * kDK + frag_chan<bf16>(2 * hf + x, hi, 4 * e4)) =
+                        f32x4{g[x][4 * e4], g[x][4 * e4 + 1], g[x][4 * e4 + 2], g[x][4 * e4 + 3]};
+        }
+        if (hf == 0 && hi == 0) bet[r] = bt;
         __syncthreads();
-        const int wu = __builtin_amdgcn_readfirstlane(w);
-        float m[NKG][EPL];  // gamma / 2
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-            for (int r4 = 0; r4 < EPL / 4; ++r4) {
-                const int c0 = frag_chan<T>(kg, hi, 4 * r4);
-                f32x4 off = {0.f, 0.f, 0.f, 0.f}, all;
-                for (int ww = 0; ww < wu; ++ww) off += *reinterpret_cast<const f32x4 *>(tot + ww * DK + c0);
-                all = off;
-                for (int ww = wu; ww < kNW; ++ww) all += *reinterpret_cast<const f32x4 *>(tot + ww * DK + c0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    g[kg][4 * r4 + e] += off[e];
-                    m[kg][4 * r4 + e] = 0.5f * all[e];
-                }
-            }
-        if (tid < DK) {  // per-channel factors, once per channel
-            float all = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < kNW; ++ww) all += tot[ww * DK + tid];
-            ehalf[tid] = __expf(0.5f * all);
-            egam[tid] = __expf(all);
+        if (tid < kDK) {
+            const float t0v = tot[tid], t1 = tot[kDK + tid], t2 = tot[2 * kDK + tid], t3 = tot[3 * kDK + tid];
+            const float gam = (t0v + t1) + (t2 + t3), m = 0.5f * gam;
+            offm[tid] = -m;
+            offm[kDK + tid] = t0v - m;
+            offm[2 * kDK + tid] = (t0v + t1) - m;
+            offm[3 * kDK + tid] = (t0v + t1 + t2) - m;
+            ehalf[tid] = exp2_fast(m);
+            egam[tid] = exp2_fast(gam);
         }
         __syncthreads();
 
-        // ---- 2. elementwise: u = exp(g - m) and 1/u = exp(m - g), m = gamma / 2.
-        //      Gram factors k u, scale q u (registers) and k / u (LDS, Km);
-        //      QO = scale q exp(g) = scale q u E (registers), with E = exp(m);
-        //      KtT = (k exp(gamma - g))^T = (k E / u)^T, Kbe^T = (beta k exp(g))^T and
-        //      Vb^T = (beta v)^T transposed by the matrix cores straight into LDS.
-        V kp[NKG], qp[NKG], qo[NKG];
+        // ---- 2. elementwise, with d = g - gamma/2 (clamped), u = exp(d), 1/u = exp(-d)
+        //      and E = exp(gamma/2): Gram factors Kp = k u, Qp = scale q u, Km = k / u;
+        //      QO = scale q u E; KtT = (k E / u)^T, Kbe^T = (beta k u E)^T and
+        //      Vb^T = (beta v)^T transposed by the matrix cores into LDS
+        bf16x8 kpf[2], qpf[2];
 #pragma unroll
-        for (int kg = 0; kg < NKG; ++kg) {
-            float xp[EPL], xq[EPL], xo[EPL], xm[EPL], xt[EPL], xb[EPL], Ev[EPL];
+        for (int x = 0; x < 2; ++x) {
+            const int kg = 2 * hf + x;
+            const int c0 = frag_chan<bf16>(kg, hi, 0), c4 = frag_chan<bf16>(kg, hi, 4);
+            const f32x4 om0 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c0);
+            const f32x4 om1 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c4);
+            const f32x4 E0 = *reinterpret_cast<const f32x4 *>(ehalf + c0);
+            const f32x4 E1 = *reinterpret_cast<const f32x4 *>(ehalf + c4);
+            bf16x8 km, qo, kt, kb;
 #pragma unroll
-            for (int r4 = 0; r4 < EPL / 4; ++r4) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(ehalf + frag_chan<T>(kg, hi, 4 * r4));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Ev[4 * r4 + e] = t[e];
+            for (int e = 0; e < 8; ++e) {
+                const float om = e < 4 ? om0[e] : om1[e - 4], E = e < 4 ? E0[e] : E1[e - 4];
+                const float d = __builtin_amdgcn_fmed3f(g[x][e] + om, -kClamp, kClamp);
+                const float u = exp2_fast(d), ui = exp2_fast(-d);
+                const float kv = static_cast<float>(kr[x][e]), qs = scale * static_cast<float>(qr[x][e]);
+                const float uE = u * E, xm = kv * ui;
+                kpf[x][e] = static_cast<bf16>(kv * u);
+                qpf[x][e] = static_cast<bf16>(qs * u);
+                km[e] = static_cast<bf16>(xm);
+                qo[e] = static_cast<bf16>(qs * uE);
+                kt[e] = static_cast<bf16>(xm * E);
+                kb[e] = static_cast<bf16>((bt * kv) * uE);
             }
+            const int off = ((kg * 4 + rb) * 64 + l) * 8;
+            *reinterpret_cast<bf16x8 *>(Kp + off) = kpf[x];
+            *reinterpret_cast<bf16x8 *>(Qp + off) = qpf[x];
+            *reinterpret_cast<bf16x8 *>(Km + off) = km;
+            *reinterpret_cast<bf16x8 *>(QO + off) = qo;
+            // chunk rows 16 rb .. are contraction slots 4 (rb % 2) .. of group rb / 2
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float u = __expf(clamp85f(g[kg][e] - m[kg][e]));
-                const float ui = __expf(clamp85f(m[kg][e] - g[kg][e]));
-                const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
-                xp[e] = kv * u;
-                xq[e] = qv * u;
-                xm[e] = kv * ui;
-                xo[e] = xq[e] * Ev[e];
-                xt[e] = xm[e] * Ev[e];
-                xb[e] = bta * xp[e] * Ev[e];
-            }
-            kp[kg] = pack_vals<T>(xp);
-            qp[kg] = pack_vals<T>(xq);
-            qo[kg] = pack_vals<T>(xo);
-            *reinterpret_cast<V *>(Km + ((kg * kNW + w) * 64 + l) * EPL) = pack_vals<T>(xm);
-            const V kts = pack_vals<T>(xt), kbe = pack_vals<T>(xb);
-            // chunk rows 16w.. are contraction slots 4 (w % TPG) .. of group w / TPG
-#pragma unroll
-            for (int t = 0; t < TPG; ++t) {
-                const V id = t ? id1 : id0;
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                store_acc_slots<T>(KtT, w / TPG, TPG * kg + t, DK, w % TPG, F::mma(z, kts, id));
-                store_acc_slots<T>(KbeT, w / TPG, TPG * kg + t, DK, w % TPG, F::mma(z, kbe, id));
+            for (int t = 0; t < 2; ++t) {
+                store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kt, t ? id1 : id0));
+                store_slots(KbeT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kb, t ? id1 : id0));
             }
         }
 #pragma unroll
-        for (int kg = 0; kg < NVG; ++kg) {
-            float xv[EPL];
+        for (int x = 0; x < 2; ++x) {
+            const int vg = 2 * hf + x;
+            bf16x8 vb;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) xv[e] = bta * to_f32(vr[kg][e]);
-            const V vb = pack_vals<T>(xv);
+            for (int e = 0; e < 8; ++e) vb[e] = static_cast<bf16>(bt * static_cast<float>(vr[x][e]));
 #pragma unroll
-            for (int t = 0; t < TPG; ++t)
-                store_acc_slots<T>(VbT, w / TPG, TPG * kg + t, DV, w % TPG,
-                                   F::mma(f32x4{0.f, 0.f, 0.f, 0.f}, vb, t ? id1 : id0));
+            for (int t = 0; t < 2; ++t)
+                store_slots(VbT, rb >> 1, 2 * vg + t, kDV, rb & 1, Frag<bf16>::mma(zero4, vb, t ? id1 : id0));
         }
-        __syncthreads();  // Km, KtT, Kbe^T, Vb^T complete
-        if (ci + 1 < n_c) load_inputs(ci + 1);  // next chunk's rows arrive while this one computes
+        __syncthreads();  // Kp, Qp, Km, QO, KtT, Kbe^T, Vb^T complete
+        const bool more = ci + 1 < n_c;
+        if (more) load_g(ci + 1);  // next chunk's inputs arrive while this one computes
 
-        // ---- 3. decayed Gram tiles of row block w: A (rows w) and Aqk^T (columns w)
-        f32x4 akk[kNW], aqt[kNW];
+        // ---- 3. Gram rows of block rb, contraction over all 128 channels (own half
+        //      from registers, the other half from LDS)
+        if (hf == 0) {
+            // A[r][i] = beta_r <Kp_r, Km_i>, i < r; then the inverse of its diagonal block
+            f32x4 akk[4];
 #pragma unroll
-        for (int tj = 0; tj < kNW; ++tj) {
-            akk[tj] = aqt[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tj <= w) {
+            for (int tj = 0; tj < 4; ++tj) {
+                akk[tj] = zero4;
+                if (tj <= rb) {
 #pragma unroll
-                for (int kg = 0; kg < NKG; ++kg) {
-                    const V km = frag_load<T>(Km, kg, tj, kC);
-                    akk[tj] = F::mma(akk[tj], kp[kg], km);
-                    aqt[tj] = F::mma(aqt[tj], km, qp[kg]);
+                    for (int kg = 0; kg < 4; ++kg) {
+                        const bf16x8 ka = kg < 2 ? kpf[kg] : frag_load<bf16>(Kp, kg, rb, kC);
+                        akk[tj] = Frag<bf16>::mma(akk[tj], ka, frag_load<bf16>(Km, kg, tj, kC));
+                    }
+                }
+            }
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+                if (tj <= rb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 16 * rb + 4 * hi + i, cc = 16 * tj + lr;
+                        Am[rr * kPT + cc] = (cc < rr) ? bv[i] * akk[tj][i] : 0.f;
+                    }
+                }
+            // (I + L)^{-1} of the diagonal block L = A[16rb.., 16rb..] by forward
+            // substitution: lane (r, hi) holds X[r][4 hi + j]; step i subtracts
+            // L[r][i] times row i (broadcast within the 16-lane row). The block's
+            // rows were written by this wave, and the LDS operations of one wave
+            // are performed in order.
+            float Lr[16];
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(Am + r * kPT + 16 * rb + 4 * v4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Lr[4 * v4 + e] = t[e];
+            }
+            float xs[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xs[j] = (lr == 4 * hi + j) ? 1.f : 0.f;
+#define KDA_SUBST_STEP(I) \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) xs[j] = fmaf(-Lr[I], row_bcast<I>(xs[j]), xs[j]);
+            KDA_SUBST_STEP(0) KDA_SUBST_STEP(1) KDA_SUBST_STEP(2) KDA_SUBST_STEP(3)
+            KDA_SUBST_STEP(4) KDA_SUBST_STEP(5) KDA_SUBST_STEP(6) KDA_SUBST_STEP(7)
+            KDA_SUBST_STEP(8) KDA_SUBST_STEP(9) KDA_SUBST_STEP(10) KDA_SUBST_STEP(11)
+            KDA_SUBST_STEP(12) KDA_SUBST_STEP(13) KDA_SUBST_STEP(14)
+#undef KDA_SUBST_STEP
+            // T fragments of row block rb: the diagonal block in slots 4 (rb % 2) ..,
+            // and the zero block above the diagonal for even rb
+            store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0], xs[1], xs[2], xs[3]});
+            if ((rb & 1) == 0) store_slots(Tf, rb >> 1, rb, kC, 1, zero4);
+        } else {
+            // Aqk[r][i] = <Qp_r, Km_i>, i <= r: tiles of Aqk^T = Km Qp^T are the
+            // operand slots of Aqk's rows rb
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                if (tj < 2 * ((rb >> 1) + 1)) {
+                    f32x4 acc = zero4;
+                    if (tj <= rb) {
+#pragma unroll
+                        for (int kg = 0; kg < 4; ++kg) {
+                            const bf16x8 qb = kg >= 2 ? qpf[kg - 2] : frag_load<bf16>(Qp, kg, rb, kC);
+                            acc = Frag<bf16>::mma(acc, frag_load<bf16>(Km, kg, tj, kC), qb);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] = (16 * tj + 4 * hi + i <= r) ? acc[i] : 0.f;
+                    }
+                    store_slots(Aqk, tj >> 1, rb, kC, tj & 1, acc);
                 }
             }
         }
-        // Aqk rows of block w as operand groups: Aqk[r][i] = Aqk^T tile (i-block tj), i <= r
-        V aqf[NCG];
+        __syncthreads();  // A, the diagonal blocks of T and Aqk complete
+        if (more) load_k(ci + 1);
+
+        // ---- 4. off-diagonal blocks of T, column block j = rb by wave (rb, 1):
+        //      T_ij = -D_i Y, Y = sum_{k=j}^{i-1} A_ik T_kj (D_i = T_ii). Both
+        //      orientations of each block are formed from Y: T_ij (as the B operand
+        //      of the next Y) and T_ij^T (whose tile is T_ij's A operand, stored).
+        if (hf == 1 && rb < 3) {
+            const int j = rb;
+            bf16x4 tb[3];  // B operands of T_kj, k = j .. 2
 #pragma unroll
-        for (int tj = 0; tj < kNW; ++tj) {
-            f32x4 x = aqt[tj];
+            for (int k = 0; k < 3; ++k)
+                if (k == j) tb[k] = to_bf16x4(mma16(load_slots(Tf, k >> 1, k, kC, k & 1), idB, zero4));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (16 * tj + 4 * hi + i <= r) ? x[i] : 0.f;
-            acc_to_slots<T>(aqf[tj / TPG], tj % TPG, x);
-        }
+            for (int i = 1; i < 4; ++i) {
+                if (i > j) {
+                    f32x4 y = zero4;
 #pragma unroll
-        for (int tj = 0; tj < kNW; ++tj)
-            if (tj <= w) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * w + 4 * hi + i, cc = 16 * tj + lr;
-                    Am[rr * PT + cc] = (cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
+                    for (int k = 0; k < 3; ++k)
+                        if (k >= j && k < i) {
+                            const f32x4 ar = *reinterpret_cast<const f32x4 *>(Am + (16 * i + lr) * kPT + 16 * k + 4 * hi);
+                            y = mma16(to_bf16x4(ar), tb[k], y);
+                        }
+                    const bf16x4 yb = to_bf16x4(y);
+                    const bf16x4 di = load_slots(Tf, i >> 1, i, kC, i & 1);
+                    store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, di, zero4));
+                    if (i < 3) tb[i] = to_bf16x4(-mma16(di, yb, zero4));
                 }
             }
-        __syncthreads();  // A complete
-
-        // ---- 4. T = (I + A)^{-1}
-        unit_lower_inverse<kC, PT, T, kNT>(Am, Tm);
-
-        // ---- 5. W (as W^T = Kbe^T T^T, whose tiles are W's row-block-w operand
-        //      groups) and U~ = T Vb (accumulator layout, like W S)
-        const int kgmax = (16 * w + 15) / F::KG + 1;  // T is lower triangular
-        V tf[NCG];
-#pragma unroll
-        for (int kg = 0; kg < NCG; ++kg) tf[kg] = row_frag_f32<T>(Tm, PT, 16 * w, kg);
-        V wf[NKG];
-#pragma unroll
-        for (int tm = 0; tm < DK / 16; ++tm) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kg = 0; kg < NCG; ++kg)
-                if (kg < kgmax) acc = F::mma(acc, frag_load<T>(KbeT, kg, tm, DK), tf[kg]);
-            acc_to_slots<T>(wf[tm / TPG], tm % TPG, acc);
         }
-        f32x4 ut[NTN];
-#pragma unroll
-        for (int tn = 0; tn < NTN; ++tn) {
-            ut[tn] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kg = 0; kg < NCG; ++kg)
-                if (kg < kgmax) ut[tn] = F::mma(ut[tn], tf[kg], frag_load<T>(VbT, kg, tn, DV));
-        }
-        __syncthreads();  // T is no longer read (S^T and U^T take its place)
+        __syncthreads();  // T complete
+        if (more) load_q(ci + 1);
 
-        // ---- 6. state phase
+        // ---- 5. -W (as W^T = Kbe^T T^T, whose tiles are W's operand slots) and
+        //      U~ = T Vb (accumulator tiles), rows rb, tiles of half hf
+        {
+            const bf16x8 tf0 = frag_load<bf16>(Tf, 0, rb, kC);
+            const bf16x8 tf1 = rb >= 2 ? frag_load<bf16>(Tf, 1, rb, kC) : bf16x8{};
 #pragma unroll
-        for (int u = 0; u < ST; ++u) store_acc_slots<T>(St, tile_m(u) / TPG, tile_n(u), DV, tile_m(u) % TPG, accS[u]);
-        __syncthreads();  // S^T complete
-        // U = U~ - W S  -> U^T (rows 16w.. of the chunk are slots of group w / TPG)
+            for (int u = 0; u < 4; ++u) {
+                const int tm = 4 * hf + u;
+                f32x4 acc = Frag<bf16>::mma(zero4, frag_load<bf16>(KbeT, 0, tm, kDK), tf0);
+                if (rb >= 2) acc = Frag<bf16>::mma(acc, frag_load<bf16>(KbeT, 1, tm, kDK), tf1);
+                store_slots(Wn, tm >> 1, rb, kC, tm & 1, -acc);
+            }
 #pragma unroll
-        for (int tn = 0; tn < NTN; ++tn) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg) acc = F::mma(acc, wf[kg], frag_load<T>(St, kg, tn, DV));
-            store_acc_slots<T>(Ut, w / TPG, tn, DV, w % TPG, ut[tn] - acc);
-        }
-        __syncthreads();  // U^T complete
-        // O^T = S^T QO^T + U^T Aqk^T: lanes hold 4 adjacent columns of row r
-#pragma unroll
-        for (int tn = 0; tn < NTN; ++tn) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg) acc = F::mma(acc, frag_load<T>(St, kg, tn, DV), qo[kg]);
-#pragma unroll
-            for (int kg = 0; kg < NCG; ++kg)
-                if (kg < kgmax) acc = F::mma(acc, frag_load<T>(Ut, kg, tn, DV), aqf[kg]);
-            T *dst = (t0 + r < T_len)
-                         ? o + ((seq0 + t0 + r) * H + h) * DV + 16 * tn + 4 * hi
-                         : static_cast<T *>(a.discard) + 4 * (l & 15);
-            if constexpr (sizeof(T) == 2) {
-                bf16 x[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[i]);
-                *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(x);
-            } else {
-                *reinterpret_cast<f32x4 *>(dst) = acc;
+            for (int u = 0; u < 4; ++u) {
+                const int tn = 4 * hf + u;
+                f32x4 acc = Frag<bf16>::mma(zero4, tf0, frag_load<bf16>(VbT, 0, tn, kDV));
+                if (rb >= 2) acc = Frag<bf16>::mma(acc, tf1, frag_load<bf16>(VbT, 1, tn, kDV));
+                *reinterpret_cast<f32x4 *>(Ut + acc_tile_off(rb, tn, kDV)) = acc;
             }
         }
-        // S <- exp(gamma) S + KtT U (state rows = key channels held by this lane group)
+        __syncthreads();  // -W and U~ complete
+        if (more) load_v(ci + 1);
+
+        // ---- 6. state phase (columns 16 w ..): U = U~ - W S, O = QO S + Aqk U
+        //      (stored), S <- exp(gamma) S + KtT U
+        {
+            bf16x8 sb[4];
 #pragma unroll
-        for (int u = 0; u < ST; ++u) {
-            const int tm = tile_m(u), tn = tile_n(u);
+            for (int kg = 0; kg < 4; ++kg) sb[kg] = tiles_to_frag(accS[2 * kg], accS[2 * kg + 1]);
+            f32x4 ua[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) accS[u][i] *= egam[16 * tm + 4 * hi + i];
+            for (int rr = 0; rr < 4; ++rr) ua[rr] = *reinterpret_cast<const f32x4 *>(Ut + acc_tile_off(rr, w, kDV));
 #pragma unroll
-            for (int kg = 0; kg < NCG; ++kg)
-                accS[u] = F::mma(accS[u], frag_load<T>(KtT, kg, tm, DK), frag_load<T>(Ut, kg, tn, DV));
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) ua[rr] = Frag<bf16>::mma(ua[rr], frag_load<bf16>(Wn, kg, rr, kC), sb[kg]);
+            bf16x8 ub[2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) ub[kc] = tiles_to_frag(ua[2 * kc], ua[2 * kc + 1]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                f32x4 oa = zero4;
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) oa = Frag<bf16>::mma(oa, frag_load<bf16>(QO, kg, rr, kC), sb[kg]);
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+                    if (kc <= (rr >> 1)) oa = Frag<bf16>::mma(oa, frag_load<bf16>(Aqk, kc, rr, kC), ub[kc]);
+                // transpose the tile (identity product) so that lane (r, hi) holds 4
+                // adjacent columns of chunk row 16 rr + r, stored as 8 bytes
+                const f32x4 ot = mma16(to_bf16x4(oa), idB, zero4);
+                const int row = t0 + 16 * rr + lr;
+                bf16 *dst = row < T_len ? o + ((seq0 + row) * H + h) * kDV + 16 * w + 4 * hi
+                                        : static_cast<bf16 *>(a.discard) + 4 * (l & 31);
+                *reinterpret_cast<bf16x4 *>(dst) = to_bf16x4(ot);
+            }
+#pragma unroll
+            for (int tm = 0; tm < 8; ++tm) {
+                accS[tm] *= *reinterpret_cast<const f32x4 *>(egam + 16 * tm + 4 * hi);
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) accS[tm] = Frag<bf16>::mma(accS[tm], frag_load<bf16>(KtT, kc, tm, kDK), ub[kc]);
+            }
         }
-        __syncthreads();  // S^T, U^T and KtT free for the next chunk
+        // No barrier here: before the next chunk writes anything the state phase
+        // reads (from the per-channel factors on), every wave passes its first barrier.
     }
 
     if (a.hT) {
-        float *hT = a.hT + ((size_t)s * H + h) * DK * DV;
+        float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + 16 * w + lr;
 #pragma unroll
-        for (int u = 0; u < ST; ++u)
+        for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hT[(16 * tile_m(u) + 4 * hi + i) * DV + 16 * tile_n(u) + lr] = accS[u][i];
+            for (int i = 0; i < 4; ++i) hT[(16 * tm + 4 * hi + i) * kDV] = accS[tm][i];
     }
-}
-
-template <int DK, int DV, typename T>
-hipError_t launch_fused_t(const FusedArgs &a, int n_seqs, hipStream_t stream) {
-    constexpr size_t smem = FusedCfg<DK, DV, T>::SMEM;
-    static_assert(smem <= 160 * 1024, "fused LDS budget");
-    auto kern = kda_fused_kernel<DK, DV, T>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(n_seqs * a.H), dim3(kNT), smem, stream, a);
-    return hipGetLastError();
-}
-
-template <typename T>
-hipError_t dispatch_d(const FusedArgs &a, int dk, int dv, int n, hipStream_t st) {
-    if (dk == 64 && dv == 64) return launch_fused_t<64, 64, T>(a, n, st);
-    if (dk == 64 && dv == 128) return launch_fused_t<64, 128, T>(a, n, st);
-    if (dk == 128 && dv == 64) return launch_fused_t<128, 64, T>(a, n, st);
-    return launch_fused_t<128, 128, T>(a, n, st);
 }
 
 }  // namespace
 
 hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream) {
-    if (!bf16) return hipErrorInvalidValue;  // the fused pass is built for bf16 input only
-    return dispatch_d<kda::bf16>(a, dk, dv, n_seqs, stream);
+    // the fused pass is built for bf16 input and d_k = d_v = 128 only
+    if (!bf16 || dk != kDK || dv != kDV) return hipErrorInvalidValue;
+    constexpr size_t smem = Lds::SIZE;
+    auto kern = kda_fused_kernel;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(n_seqs * a.H), dim3(kNT), smem, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace kda

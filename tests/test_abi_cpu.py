@@ -50,7 +50,8 @@ def test_version_and_status_strings(lib):
 
 
 def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
-    if n_seqs == 0 and C == 64 and B * H >= 256:  # fused pass: only the 256-byte discard slot
+    if n_seqs == 0 and C == 64 and esz == 2 and dk == dv == 128 and B * H >= 256:
+        # fused pass: only the 256-byte discard slot
         return 256
     per = (T + C - 1) // C
     nch = (per + n_seqs if n_seqs else B * per) * H

@@ -97,15 +97,33 @@ __device__ __forceinline__ bf16x8 tiles_to_frag(f32x4 lo, f32x4 hi) {
     return r;
 }
 
+// The lane index as a value the compiler cannot hoist: constants derived from it
+// are rebuilt where they are used instead of occupying registers for the whole
+// kernel.
+__device__ __forceinline__ int opaque_lane() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
 // Identity operand for transposing with the matrix cores: as B^T of a 16-column
 // tile t within a contraction group, lane l (column l%16) has a one in the slot
 // whose contraction index is 16 t + l%16.
 __device__ __forceinline__ bf16x8 ident_frag(int t) {
-    const int l = threadIdx.x & 63;
+    const int l = opaque_lane();
     bf16x8 v;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         v[j] = static_cast<bf16>((frag_chan<bf16>(0, l >> 4, j) == 16 * t + (l & 15)) ? 1.f : 0.f);
+    return v;
+}
+
+// The 16 x 16 identity as the B operand of mma16.
+__device__ __forceinline__ bf16x4 ident4() {
+    const int l = opaque_lane();
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<bf16>(4 * (l >> 4) + i == (l & 15) ? 1.f : 0.f);
     return v;
 }
 
@@ -179,28 +197,32 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16x8 kr[2], qr[2], vr[2];
     float gl[2][8];
     float bta;
-    auto tok_of = [&](int ci) {
-        // rows past the end read the last row; their beta and decay are zeroed at use
-        return (seq0 + min(ci * kC + r, T_len - 1)) * H + h;
+    // uniform base of chunk ci's first row (head h) + 32-bit lane offsets
+    auto tok0_of = [&](int ci) { return (seq0 + (size_t)ci * kC) * H + h; };
+    auto row_off = [&](int ci) {  // rows past the end read the last row; beta and decay are zeroed at use
+        return (unsigned)(min(r, T_len - 1 - ci * kC) * H);
     };
     auto load_k = [&](int ci) {
-        const size_t tok = tok_of(ci);
+        const bf16 *base = static_cast<const bf16 *>(a.k) + tok0_of(ci) * kDK;
+        const unsigned ro = row_off(ci) * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) kr[x] = load_row_frag(static_cast<const bf16 *>(a.k) + tok * kDK, 2 * hf + x, hi);
+        for (int x = 0; x < 2; ++x) kr[x] = load_row_frag(base + ro, 2 * hf + x, hi);
     };
     auto load_q = [&](int ci) {
-        const size_t tok = tok_of(ci);
+        const bf16 *base = static_cast<const bf16 *>(a.q) + tok0_of(ci) * kDK;
+        const unsigned ro = row_off(ci) * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) qr[x] = load_row_frag(static_cast<const bf16 *>(a.q) + tok * kDK, 2 * hf + x, hi);
+        for (int x = 0; x < 2; ++x) qr[x] = load_row_frag(base + ro, 2 * hf + x, hi);
     };
     auto load_v = [&](int ci) {
-        const size_t tok = tok_of(ci);
+        const bf16 *base = static_cast<const bf16 *>(a.v) + tok0_of(ci) * kDV;
+        const unsigned ro = row_off(ci) * kDV;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) vr[x] = load_row_frag(static_cast<const bf16 *>(a.v) + tok * kDV, 2 * hf + x, hi);
+        for (int x = 0; x < 2; ++x) vr[x] = load_row_frag(base + ro, 2 * hf + x, hi);
     };
     auto load_g = [&](int ci) {
-        const size_t tok = tok_of(ci);
-        const float *gp = a.log_alpha + tok * kDK;
+        const size_t t0b = tok0_of(ci);
+        const float *gp = a.log_alpha + t0b * kDK + row_off(ci) * kDK;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, hi, 0));
@@ -211,17 +233,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 gl[x][4 + e] = g1[e];
             }
         }
-        bta = a.beta[tok];
+        bta = a.beta[t0b + row_off(ci)];
     };
     load_g(0);
     load_k(0);
     load_q(0);
     load_v(0);
 
-    const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
-    bf16x4 idB;  // the 16 x 16 identity as a B operand of mma16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) idB[i] = static_cast<bf16>(4 * hi + i == lr ? 1.f : 0.f);
     bf16 *o = static_cast<bf16 *>(a.o);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -281,6 +299,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         //      QO = scale q u E; KtT = (k E / u)^T, Kbe^T = (beta k u E)^T and
         //      Vb^T = (beta v)^T transposed by the matrix cores into LDS
         bf16x8 kpf[2], qpf[2];
+        const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int kg = 2 * hf + x;
@@ -414,7 +433,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             bf16x4 tb[3];  // B operands of T_kj, k = j .. 2
 #pragma unroll
             for (int k = 0; k < 3; ++k)
-                if (k == j) tb[k] = to_bf16x4(mma16(load_slots(Tf, k >> 1, k, kC, k & 1), idB, zero4));
+                if (k == j) tb[k] = to_bf16x4(mma16(load_slots(Tf, k >> 1, k, kC, k & 1), ident4(), zero4));
 #pragma unroll
             for (int i = 1; i < 4; ++i) {
                 if (i > j) {
@@ -459,7 +478,9 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         if (more) load_v(ci + 1);
 
         // ---- 6. state phase (columns 16 w ..): U = U~ - W S, O = QO S + Aqk U
-        //      (stored), S <- exp(gamma) S + KtT U
+        //      (stored), S <- exp(gamma) S + KtT U. The shared operands come from
+        //      LDS one row block ahead of the products that use them (the
+        //      scheduling barriers keep those reads ahead of the matrix-core work).
         {
             bf16x8 sb[4];
 #pragma unroll
@@ -467,34 +488,62 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             f32x4 ua[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) ua[rr] = *reinterpret_cast<const f32x4 *>(Ut + acc_tile_off(rr, w, kDV));
+            bf16x8 fa[2][4];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
+            for (int kg = 0; kg < 4; ++kg) fa[0][kg] = frag_load<bf16>(Wn, kg, 0, kC);
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg) ua[rr] = Frag<bf16>::mma(ua[rr], frag_load<bf16>(Wn, kg, rr, kC), sb[kg]);
+            for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg)  // next: W rows rr + 1, then QO rows 0
+                    fa[(rr + 1) & 1][kg] = rr < 3 ? frag_load<bf16>(Wn, kg, rr + 1, kC) : frag_load<bf16>(QO, kg, 0, kC);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) ua[rr] = Frag<bf16>::mma(ua[rr], fa[rr & 1][kg], sb[kg]);
+            }
             bf16x8 ub[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) ub[kc] = tiles_to_frag(ua[2 * kc], ua[2 * kc + 1]);
+            bf16x8 kf[2][2];
+            bf16 *o_chunk = o + ((seq0 + t0) * H + h) * kDV + 16 * w;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                f32x4 oa = zero4;
-#pragma unroll
-                for (int kg = 0; kg < 4; ++kg) oa = Frag<bf16>::mma(oa, frag_load<bf16>(QO, kg, rr, kC), sb[kg]);
+                bf16x8 aq[2];
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
-                    if (kc <= (rr >> 1)) oa = Frag<bf16>::mma(oa, frag_load<bf16>(Aqk, kc, rr, kC), ub[kc]);
+                    if (kc <= (rr >> 1)) aq[kc] = frag_load<bf16>(Aqk, kc, rr, kC);
+                if (rr < 3) {
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = frag_load<bf16>(QO, kg, rr + 1, kC);
+                } else {
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) kf[0][kc] = frag_load<bf16>(KtT, kc, 0, kDK);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 oa = zero4;
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) oa = Frag<bf16>::mma(oa, fa[rr & 1][kg], sb[kg]);
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+                    if (kc <= (rr >> 1)) oa = Frag<bf16>::mma(oa, aq[kc], ub[kc]);
                 // transpose the tile (identity product) so that lane (r, hi) holds 4
                 // adjacent columns of chunk row 16 rr + r, stored as 8 bytes
-                const f32x4 ot = mma16(to_bf16x4(oa), idB, zero4);
-                const int row = t0 + 16 * rr + lr;
-                bf16 *dst = row < T_len ? o + ((seq0 + row) * H + h) * kDV + 16 * w + 4 * hi
-                                        : static_cast<bf16 *>(a.discard) + 4 * (l & 31);
+                const f32x4 ot = mma16(to_bf16x4(oa), ident4(), zero4);
+                bf16 *dst = t0 + 16 * rr + lr < T_len
+                                ? o_chunk + (unsigned)(((16 * rr + lr) * H) * kDV + 4 * hi)
+                                : static_cast<bf16 *>(a.discard) + 4 * (l & 31);
                 *reinterpret_cast<bf16x4 *>(dst) = to_bf16x4(ot);
             }
 #pragma unroll
             for (int tm = 0; tm < 8; ++tm) {
-                accS[tm] *= *reinterpret_cast<const f32x4 *>(egam + 16 * tm + 4 * hi);
+                if (tm < 7) {
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) accS[tm] = Frag<bf16>::mma(accS[tm], frag_load<bf16>(KtT, kc, tm, kDK), ub[kc]);
+                    for (int kc = 0; kc < 2; ++kc) kf[(tm + 1) & 1][kc] = frag_load<bf16>(KtT, kc, tm + 1, kDK);
+                }
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(egam + 16 * tm + 4 * hi);
+                __builtin_amdgcn_sched_barrier(0);
+                accS[tm] *= eg;
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) accS[tm] = Frag<bf16>::mma(accS[tm], kf[tm & 1][kc], ub[kc]);
             }
         }
         // No barrier here: before the next chunk writes anything the state phase

@@ -51,10 +51,11 @@ struct Lds {
     static constexpr int KTT = QO + kC * kDK * 2;       // [DK][C]  bf16 fragments
     static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments
     static constexpr int EGAM = AQK + kC * kC * 2;      // [DK]     exp(gamma)
-    static constexpr int TOT = EGAM + kDK * 4;          // [4][DK]  log2-decay sum of each row block
-    static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  row-block offset minus gamma/2
+    static constexpr int TOT = EGAM + kDK * 4;          // [4][DK]  log-decay sum of each row block
+    static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  (row-block offset - gamma/2) log2(e)
     static constexpr int EHALF = OFFM + 4 * kDK * 4;    // [DK]     exp(gamma / 2)
-    static constexpr int BET = EHALF + kDK * 4;         // [C]      beta (0 past the end)
+    static constexpr int EHS = EHALF + kDK * 4;         // [DK]     scale exp(gamma / 2)
+    static constexpr int BET = EHS + kDK * 4;           // [C]      beta (0 past the end)
     static constexpr int KBET = BET + kC * 4;           // [DK][C]  (beta k exp(g))^T fragments
     static constexpr int VBT = KBET + kDK * kC * 2;     // [DV][C]  (beta v)^T fragments
     static constexpr int AM = VBT + kDV * kC * 2;       // [C][PT]  fp32 A (strictly lower)
@@ -79,22 +80,27 @@ template <int I> __device__ __forceinline__ float row_bcast(float x) {
                                                                  0x150 + I, 0xf, 0xf, false));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Two floats rounded to bf16 (nearest even) in one 32-bit word.
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-    bf16x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = static_cast<bf16>(x[i]);
-    return r;
+    return __builtin_bit_cast(bf16x4, u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])});
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float *x) {
+    return __builtin_bit_cast(bf16x8, u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])});
 }
 
 // Two accumulator tiles (contraction indices 0..15 and 16..31 of a group) as one operand.
 __device__ __forceinline__ bf16x8 tiles_to_frag(f32x4 lo, f32x4 hi) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = static_cast<bf16>(lo[i]);
-        r[4 + i] = static_cast<bf16>(hi[i]);
-    }
-    return r;
+    return __builtin_bit_cast(bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])});
 }
 
 // The lane index as a value the compiler cannot hoist: constants derived from it
@@ -106,45 +112,60 @@ __device__ __forceinline__ int opaque_lane() {
     return l;
 }
 
+// The 16 x 16 identity as the B operand of mma16: lane (c, hi) has a one (bf16
+// 0x3f80) in slot c - 4 hi when that is 0..3.
+__device__ __forceinline__ unsigned long long ident4_bits() {
+    const int l = opaque_lane();
+    const unsigned d = (unsigned)((l & 15) - 4 * (l >> 4));
+    return d < 4 ? 0x3f80ull << (16 * d) : 0ull;
+}
+__device__ __forceinline__ bf16x4 ident4() { return __builtin_bit_cast(bf16x4, ident4_bits()); }
+
 // Identity operand for transposing with the matrix cores: as B^T of a 16-column
 // tile t within a contraction group, lane l (column l%16) has a one in the slot
-// whose contraction index is 16 t + l%16.
+// whose contraction index is 16 t + l%16 (slots 4 t .. 4 t + 3 hold indices
+// 16 t + 4 hi .. 16 t + 4 hi + 3).
 __device__ __forceinline__ bf16x8 ident_frag(int t) {
-    const int l = opaque_lane();
-    bf16x8 v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        v[j] = static_cast<bf16>((frag_chan<bf16>(0, l >> 4, j) == 16 * t + (l & 15)) ? 1.f : 0.f);
-    return v;
+    const unsigned long long b = ident4_bits();
+    const unsigned lo = (unsigned)b, hi = (unsigned)(b >> 32);
+    return __builtin_bit_cast(bf16x8, t ? u32x4{0u, 0u, lo, hi} : u32x4{lo, hi, 0u, 0u});
 }
 
-// The 16 x 16 identity as the B operand of mma16.
-__device__ __forceinline__ bf16x4 ident4() {
-    const int l = opaque_lane();
-    bf16x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = static_cast<bf16>(4 * (l >> 4) + i == (l & 15) ? 1.f : 0.f);
-    return v;
-}
+// The LDS helpers below take the lane index l explicitly: each phase derives it
+// afresh (opaque_lane), so the per-lane addresses live only within the phase.
 
-// Store accumulator tile `acc` as slots 4 t .. 4 t + 3 of this lane's share of
+// Store accumulator tile `acc` as slots 4 t .. 4 t + 3 of lane l's share of
 // group (kg, rb) of a fragment-ordered matrix with R rows.
-__device__ __forceinline__ void store_slots(bf16 *base, int kg, int rb, int R, int t, f32x4 acc) {
-    const int l = threadIdx.x & 63;
+__device__ __forceinline__ void store_slots(bf16 *base, int kg, int rb, int R, int t, f32x4 acc, int l) {
     *reinterpret_cast<bf16x4 *>(base + ((kg * (R >> 4) + rb) * 64 + l) * 8 + 4 * t) = to_bf16x4(acc);
 }
 
-// This lane's slots 4 t .. 4 t + 3 (one 16 x 16 block's operand) of group (kg, rb).
-__device__ __forceinline__ bf16x4 load_slots(const bf16 *base, int kg, int rb, int R, int t) {
-    const int l = threadIdx.x & 63;
+// Lane l's slots 4 t .. 4 t + 3 (one 16 x 16 block's operand) of group (kg, rb).
+__device__ __forceinline__ bf16x4 load_slots(const bf16 *base, int kg, int rb, int R, int t, int l) {
     return *reinterpret_cast<const bf16x4 *>(base + ((kg * (R >> 4) + rb) * 64 + l) * 8 + 4 * t);
 }
+
+// Lane l's 16-byte share of group (kg, rb) of a fragment-ordered matrix with R rows.
+__device__ __forceinline__ bf16x8 fld(const bf16 *base, int kg, int rb, int R, int l) {
+    return *reinterpret_cast<const bf16x8 *>(base + ((kg * (R >> 4) + rb) * 64 + l) * 8);
+}
+
+// Lane l's element offset in tile (rb, cb) of an accumulator-ordered [R][NC] matrix.
+__device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb * (NC >> 4) + cb) * 64 + l) * 4; }
 
 __device__ __forceinline__ bf16x8 load_row_frag(const bf16 *row, int kg, int hi) {
     const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row + frag_chan<bf16>(kg, hi, 0));
     const bf16x4 b = *reinterpret_cast<const bf16x4 *>(row + frag_chan<bf16>(kg, hi, 4));
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+
+// Declares this lane's index l, its row lr and lane group hi, and its chunk row r
+// (within the wave's row block rb) from opaque_lane(), for the enclosing phase.
+#define KDA_PHASE_LANE                                                   \
+    const int l = opaque_lane(), lr = l & 15, hi = l >> 4, r = 16 * rb + lr; \
+    (void)lr;                                                            \
+    (void)hi;                                                            \
+    (void)r;
 
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -155,6 +176,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     float *tot = reinterpret_cast<float *>(smem + Lds::TOT);
     float *offm = reinterpret_cast<float *>(smem + Lds::OFFM);
     float *ehalf = reinterpret_cast<float *>(smem + Lds::EHALF);
+    float *ehs = reinterpret_cast<float *>(smem + Lds::EHS);
     float *bet = reinterpret_cast<float *>(smem + Lds::BET);
     bf16 *KbeT = reinterpret_cast<bf16 *>(smem + Lds::KBET);
     bf16 *VbT = reinterpret_cast<bf16 *>(smem + Lds::VBT);
@@ -245,17 +267,19 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
-        const bool valid = t0 + r < T_len;
 
-        // ---- 1. inclusive prefix of log2(alpha) down the chunk: DPP scan over the
+        // ---- 1. inclusive prefix of log(alpha) down the chunk: DPP scan over the
         //      wave's 16 rows, step-major so consecutive DPP operations are
         //      independent; row-block sums to LDS, their prefix by one thread per channel
-        float g[2][8];
+        float g[2][8], bt;
+        {
+        KDA_PHASE_LANE
+        const bool valid = t0 + r < T_len;
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] = valid ? gl[x][e] * kL2E : 0.f;
-        const float bt = valid ? bta : 0.f;
+            for (int e = 0; e < 8; ++e) g[x][e] = valid ? gl[x][e] : 0.f;
+        bt = valid ? bta : 0.f;
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -281,24 +305,30 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                         f32x4{g[x][4 * e4], g[x][4 * e4 + 1], g[x][4 * e4 + 2], g[x][4 * e4 + 3]};
         }
         if (hf == 0 && hi == 0) bet[r] = bt;
+        }
         __syncthreads();
         if (tid < kDK) {
             const float t0v = tot[tid], t1 = tot[kDK + tid], t2 = tot[2 * kDK + tid], t3 = tot[3 * kDK + tid];
             const float gam = (t0v + t1) + (t2 + t3), m = 0.5f * gam;
-            offm[tid] = -m;
-            offm[kDK + tid] = t0v - m;
-            offm[2 * kDK + tid] = (t0v + t1) - m;
-            offm[3 * kDK + tid] = (t0v + t1 + t2) - m;
-            ehalf[tid] = exp2_fast(m);
-            egam[tid] = exp2_fast(gam);
+            offm[tid] = -m * kL2E;
+            offm[kDK + tid] = (t0v - m) * kL2E;
+            offm[2 * kDK + tid] = ((t0v + t1) - m) * kL2E;
+            offm[3 * kDK + tid] = ((t0v + t1 + t2) - m) * kL2E;
+            const float eh = exp2_fast(m * kL2E);
+            ehalf[tid] = eh;
+            ehs[tid] = scale * eh;
+            egam[tid] = exp2_fast(gam * kL2E);
         }
         __syncthreads();
 
         // ---- 2. elementwise, with d = g - gamma/2 (clamped), u = exp(d), 1/u = exp(-d)
-        //      and E = exp(gamma/2): Gram factors Kp = k u, Qp = scale q u, Km = k / u;
-        //      QO = scale q u E; KtT = (k E / u)^T, Kbe^T = (beta k u E)^T and
-        //      Vb^T = (beta v)^T transposed by the matrix cores into LDS
+        //      and E = exp(gamma/2): Gram factors Kp = k u, Qp = q u, Km = k / u (the
+        //      query scale is applied to Aqk); QO = scale q u E; KtT = (k E / u)^T,
+        //      Kbe^T = (beta k u E)^T and Vb^T = (beta v)^T transposed by the matrix
+        //      cores into LDS (beta of V applied to the transposed tiles)
         bf16x8 kpf[2], qpf[2];
+        {
+        KDA_PHASE_LANE
         const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -308,21 +338,27 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             const f32x4 om1 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c4);
             const f32x4 E0 = *reinterpret_cast<const f32x4 *>(ehalf + c0);
             const f32x4 E1 = *reinterpret_cast<const f32x4 *>(ehalf + c4);
-            bf16x8 km, qo, kt, kb;
+            const f32x4 S0 = *reinterpret_cast<const f32x4 *>(ehs + c0);
+            const f32x4 S1 = *reinterpret_cast<const f32x4 *>(ehs + c4);
+            float xp[8], xq[8], xm[8], xo[8], xt[8], xb[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float om = e < 4 ? om0[e] : om1[e - 4], E = e < 4 ? E0[e] : E1[e - 4];
-                const float d = __builtin_amdgcn_fmed3f(g[x][e] + om, -kClamp, kClamp);
+                const float Es = e < 4 ? S0[e] : S1[e - 4];
+                const float d = __builtin_amdgcn_fmed3f(fmaf(g[x][e], kL2E, om), -kClamp, kClamp);
                 const float u = exp2_fast(d), ui = exp2_fast(-d);
-                const float kv = static_cast<float>(kr[x][e]), qs = scale * static_cast<float>(qr[x][e]);
-                const float uE = u * E, xm = kv * ui;
-                kpf[x][e] = static_cast<bf16>(kv * u);
-                qpf[x][e] = static_cast<bf16>(qs * u);
-                km[e] = static_cast<bf16>(xm);
-                qo[e] = static_cast<bf16>(qs * uE);
-                kt[e] = static_cast<bf16>(xm * E);
-                kb[e] = static_cast<bf16>((bt * kv) * uE);
+                const float kv = static_cast<float>(kr[x][e]);
+                const float uE = u * E;
+                xp[e] = kv * u;
+                xq[e] = static_cast<float>(qr[x][e]) * u;
+                xm[e] = kv * ui;
+                xo[e] = xq[e] * Es;
+                xt[e] = xm[e] * E;
+                xb[e] = (bt * kv) * uE;
             }
+            kpf[x] = pack8(xp);
+            qpf[x] = pack8(xq);
+            const bf16x8 km = pack8(xm), qo = pack8(xo), kt = pack8(xt), kb = pack8(xb);
             const int off = ((kg * 4 + rb) * 64 + l) * 8;
             *reinterpret_cast<bf16x8 *>(Kp + off) = kpf[x];
             *reinterpret_cast<bf16x8 *>(Qp + off) = qpf[x];
@@ -331,19 +367,20 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             // chunk rows 16 rb .. are contraction slots 4 (rb % 2) .. of group rb / 2
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kt, t ? id1 : id0));
-                store_slots(KbeT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kb, t ? id1 : id0));
+                store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kt, t ? id1 : id0), l);
+                store_slots(KbeT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kb, t ? id1 : id0), l);
             }
         }
+        {
+            // beta of chunk rows 16 rb + 4 hi + i (the rows of the transposed tiles' slots)
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int vg = 2 * hf + x;
-            bf16x8 vb;
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vb[e] = static_cast<bf16>(bt * static_cast<float>(vr[x][e]));
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                store_slots(VbT, rb >> 1, 2 * vg + t, kDV, rb & 1, Frag<bf16>::mma(zero4, vb, t ? id1 : id0));
+                for (int t = 0; t < 2; ++t)
+                    store_slots(VbT, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1,
+                                Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0) * bv, l);
+        }
         }
         __syncthreads();  // Kp, Qp, Km, QO, KtT, Kbe^T, Vb^T complete
         const bool more = ci + 1 < n_c;
@@ -352,17 +389,25 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         // ---- 3. Gram rows of block rb, contraction over all 128 channels (own half
         //      from registers, the other half from LDS)
         if (hf == 0) {
+            KDA_PHASE_LANE
             // A[r][i] = beta_r <Kp_r, Km_i>, i < r; then the inverse of its diagonal block
+            // Km groups of column block tj + 1 are read while block tj is multiplied
+            const bf16x8 ka[4] = {kpf[0], kpf[1], fld(Kp, 2, rb, kC, l), fld(Kp, 3, rb, kC, l)};
+            bf16x8 kmb[2][4];
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) kmb[0][kg] = fld(Km, kg, 0, kC, l);
             f32x4 akk[4];
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
+                if (tj < rb) {
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) kmb[(tj + 1) & 1][kg] = fld(Km, kg, tj + 1, kC, l);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 akk[tj] = zero4;
                 if (tj <= rb) {
 #pragma unroll
-                    for (int kg = 0; kg < 4; ++kg) {
-                        const bf16x8 ka = kg < 2 ? kpf[kg] : frag_load<bf16>(Kp, kg, rb, kC);
-                        akk[tj] = Frag<bf16>::mma(akk[tj], ka, frag_load<bf16>(Km, kg, tj, kC));
-                    }
+                    for (int kg = 0; kg < 4; ++kg) akk[tj] = Frag<bf16>::mma(akk[tj], ka[kg], kmb[tj & 1][kg]);
                 }
             }
             const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
@@ -399,25 +444,32 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #undef KDA_SUBST_STEP
             // T fragments of row block rb: the diagonal block in slots 4 (rb % 2) ..,
             // and the zero block above the diagonal for even rb
-            store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0], xs[1], xs[2], xs[3]});
-            if ((rb & 1) == 0) store_slots(Tf, rb >> 1, rb, kC, 1, zero4);
+            store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0], xs[1], xs[2], xs[3]}, l);
+            if ((rb & 1) == 0) store_slots(Tf, rb >> 1, rb, kC, 1, zero4, l);
         } else {
-            // Aqk[r][i] = <Qp_r, Km_i>, i <= r: tiles of Aqk^T = Km Qp^T are the
+            KDA_PHASE_LANE
+            // Aqk[r][i] = scale <Qp_r, Km_i>, i <= r: tiles of Aqk^T = Km Qp^T are the
             // operand slots of Aqk's rows rb
+            const bf16x8 qb[4] = {fld(Qp, 0, rb, kC, l), fld(Qp, 1, rb, kC, l), qpf[0], qpf[1]};
+            bf16x8 kmb[2][4];
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) kmb[0][kg] = fld(Km, kg, 0, kC, l);
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
+                if (tj < rb) {
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) kmb[(tj + 1) & 1][kg] = fld(Km, kg, tj + 1, kC, l);
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 if (tj < 2 * ((rb >> 1) + 1)) {
                     f32x4 acc = zero4;
                     if (tj <= rb) {
 #pragma unroll
-                        for (int kg = 0; kg < 4; ++kg) {
-                            const bf16x8 qb = kg >= 2 ? qpf[kg - 2] : frag_load<bf16>(Qp, kg, rb, kC);
-                            acc = Frag<bf16>::mma(acc, frag_load<bf16>(Km, kg, tj, kC), qb);
-                        }
+                        for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, kmb[tj & 1][kg], qb[kg]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] = (16 * tj + 4 * hi + i <= r) ? acc[i] : 0.f;
+                        for (int i = 0; i < 4; ++i) acc[i] = (16 * tj + 4 * hi + i <= r) ? scale * acc[i] : 0.f;
                     }
-                    store_slots(Aqk, tj >> 1, rb, kC, tj & 1, acc);
+                    store_slots(Aqk, tj >> 1, rb, kC, tj & 1, acc, l);
                 }
             }
         }
@@ -429,11 +481,12 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         //      orientations of each block are formed from Y: T_ij (as the B operand
         //      of the next Y) and T_ij^T (whose tile is T_ij's A operand, stored).
         if (hf == 1 && rb < 3) {
+            KDA_PHASE_LANE
             const int j = rb;
             bf16x4 tb[3];  // B operands of T_kj, k = j .. 2
 #pragma unroll
             for (int k = 0; k < 3; ++k)
-                if (k == j) tb[k] = to_bf16x4(mma16(load_slots(Tf, k >> 1, k, kC, k & 1), ident4(), zero4));
+                if (k == j) tb[k] = to_bf16x4(mma16(load_slots(Tf, k >> 1, k, kC, k & 1, l), ident4(), zero4));
 #pragma unroll
             for (int i = 1; i < 4; ++i) {
                 if (i > j) {
@@ -445,8 +498,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                             y = mma16(to_bf16x4(ar), tb[k], y);
                         }
                     const bf16x4 yb = to_bf16x4(y);
-                    const bf16x4 di = load_slots(Tf, i >> 1, i, kC, i & 1);
-                    store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, di, zero4));
+                    const bf16x4 di = load_slots(Tf, i >> 1, i, kC, i & 1, l);
+                    store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, di, zero4), l);
                     if (i < 3) tb[i] = to_bf16x4(-mma16(di, yb, zero4));
                 }
             }
@@ -457,21 +510,38 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         // ---- 5. -W (as W^T = Kbe^T T^T, whose tiles are W's operand slots) and
         //      U~ = T Vb (accumulator tiles), rows rb, tiles of half hf
         {
-            const bf16x8 tf0 = frag_load<bf16>(Tf, 0, rb, kC);
-            const bf16x8 tf1 = rb >= 2 ? frag_load<bf16>(Tf, 1, rb, kC) : bf16x8{};
+            KDA_PHASE_LANE
+            // all operand groups are read first (T is lower triangular: the second
+            // contraction group only for rows 32 ..)
+            const bf16x8 tf0 = fld(Tf, 0, rb, kC, l);
+            bf16x8 tf1 = {}, kb0[4], kb1[4], vb0[4], vb1[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kb0[u] = fld(KbeT, 0, 4 * hf + u, kDK, l);
+                vb0[u] = fld(VbT, 0, 4 * hf + u, kDV, l);
+            }
+            if (rb >= 2) {
+                tf1 = fld(Tf, 1, rb, kC, l);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    kb1[u] = fld(KbeT, 1, 4 * hf + u, kDK, l);
+                    vb1[u] = fld(VbT, 1, 4 * hf + u, kDV, l);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int tm = 4 * hf + u;
-                f32x4 acc = Frag<bf16>::mma(zero4, frag_load<bf16>(KbeT, 0, tm, kDK), tf0);
-                if (rb >= 2) acc = Frag<bf16>::mma(acc, frag_load<bf16>(KbeT, 1, tm, kDK), tf1);
-                store_slots(Wn, tm >> 1, rb, kC, tm & 1, -acc);
+                f32x4 acc = Frag<bf16>::mma(zero4, kb0[u], tf0);
+                if (rb >= 2) acc = Frag<bf16>::mma(acc, kb1[u], tf1);
+                store_slots(Wn, tm >> 1, rb, kC, tm & 1, -acc, l);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int tn = 4 * hf + u;
-                f32x4 acc = Frag<bf16>::mma(zero4, tf0, frag_load<bf16>(VbT, 0, tn, kDV));
-                if (rb >= 2) acc = Frag<bf16>::mma(acc, tf1, frag_load<bf16>(VbT, 1, tn, kDV));
-                *reinterpret_cast<f32x4 *>(Ut + acc_tile_off(rb, tn, kDV)) = acc;
+                f32x4 acc = Frag<bf16>::mma(zero4, tf0, vb0[u]);
+                if (rb >= 2) acc = Frag<bf16>::mma(acc, tf1, vb1[u]);
+                *reinterpret_cast<f32x4 *>(Ut + ato(rb, tn, kDV, l)) = acc;
             }
         }
         __syncthreads();  // -W and U~ complete
@@ -482,20 +552,21 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         //      LDS one row block ahead of the products that use them (the
         //      scheduling barriers keep those reads ahead of the matrix-core work).
         {
+            KDA_PHASE_LANE
             bf16x8 sb[4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) sb[kg] = tiles_to_frag(accS[2 * kg], accS[2 * kg + 1]);
             f32x4 ua[4];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) ua[rr] = *reinterpret_cast<const f32x4 *>(Ut + acc_tile_off(rr, w, kDV));
+            for (int rr = 0; rr < 4; ++rr) ua[rr] = *reinterpret_cast<const f32x4 *>(Ut + ato(rr, w, kDV, l));
             bf16x8 fa[2][4];
 #pragma unroll
-            for (int kg = 0; kg < 4; ++kg) fa[0][kg] = frag_load<bf16>(Wn, kg, 0, kC);
+            for (int kg = 0; kg < 4; ++kg) fa[0][kg] = fld(Wn, kg, 0, kC, l);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
                 for (int kg = 0; kg < 4; ++kg)  // next: W rows rr + 1, then QO rows 0
-                    fa[(rr + 1) & 1][kg] = rr < 3 ? frag_load<bf16>(Wn, kg, rr + 1, kC) : frag_load<bf16>(QO, kg, 0, kC);
+                    fa[(rr + 1) & 1][kg] = rr < 3 ? fld(Wn, kg, rr + 1, kC, l) : fld(QO, kg, 0, kC, l);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kg = 0; kg < 4; ++kg) ua[rr] = Frag<bf16>::mma(ua[rr], fa[rr & 1][kg], sb[kg]);
@@ -510,13 +581,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 bf16x8 aq[2];
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
-                    if (kc <= (rr >> 1)) aq[kc] = frag_load<bf16>(Aqk, kc, rr, kC);
+                    if (kc <= (rr >> 1)) aq[kc] = fld(Aqk, kc, rr, kC, l);
                 if (rr < 3) {
 #pragma unroll
-                    for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = frag_load<bf16>(QO, kg, rr + 1, kC);
+                    for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = fld(QO, kg, rr + 1, kC, l);
                 } else {
 #pragma unroll
-                    for (int kc = 0; kc < 2; ++kc) kf[0][kc] = frag_load<bf16>(KtT, kc, 0, kDK);
+                    for (int kc = 0; kc < 2; ++kc) kf[0][kc] = fld(KtT, kc, 0, kDK, l);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 f32x4 oa = zero4;
@@ -537,7 +608,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             for (int tm = 0; tm < 8; ++tm) {
                 if (tm < 7) {
 #pragma unroll
-                    for (int kc = 0; kc < 2; ++kc) kf[(tm + 1) & 1][kc] = frag_load<bf16>(KtT, kc, tm + 1, kDK);
+                    for (int kc = 0; kc < 2; ++kc) kf[(tm + 1) & 1][kc] = fld(KtT, kc, tm + 1, kDK, l);
                 }
                 const f32x4 eg = *reinterpret_cast<const f32x4 *>(egam + 16 * tm + 4 * hi);
                 __builtin_amdgcn_sched_barrier(0);

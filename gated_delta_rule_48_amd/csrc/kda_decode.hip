@@ -9,17 +9,19 @@
 // The second form of o lets one pass over the state produce both reductions
 // (S~^T k and S~^T q) before anything is written, so each state is read once
 // and written once. The step is a pure HBM read-modify-write (about one flop
-// per byte), so the kernel is built around the memory access: one workgroup per
-// (sequence, head), each thread owning 4 adjacent columns of RPT rows, 16-byte
-// loads and stores covering whole rows per wave instruction, and the column
-// sums reduced across row groups through LDS.
+// per byte), so the kernel is built around the memory access: one workgroup of
+// 1024 threads per (sequence, head), each thread owning 4 adjacent columns of
+// RPT rows (4 at d = 128), 16-byte loads and stores covering whole rows per
+// wave instruction, and the column sums reduced across row groups through LDS
+// (every thread adds the partials of its column group; the LDS reads are cheap
+// next to the state traffic, and no thread waits on a serial reduction).
 
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 
 template <int DK, int DV, typename T>
 __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {

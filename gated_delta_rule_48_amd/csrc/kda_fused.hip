@@ -3,13 +3,18 @@
 // the fp32 128 x 128 state resident in matrix-core accumulators for the whole
 // sequence. Built for bf16 q/k/v/o, d_k = d_v = 128 and chunks of 64 rows.
 //
-// Per chunk the workgroup computes the same quantities as the split pass
-// (kda_prep.hip then kda_state.hip) without writing any of them to memory:
-// decay prefix g and gamma, the decayed Gram matrices, T = (I + A)^{-1},
-// W = T (beta k exp(g)), U~ = T (beta v), then U = U~ - W S,
-// O = QO S + Aqk U and S <- exp(gamma) S + KtT U. The only traffic is the
-// inputs q, k, v, log_alpha, beta (read once, the next chunk's while the current
-// one computes), the outputs o, and h0 / hT.
+// Per chunk the workgroup computes the quantities of the split pass (kda_prep.hip
+// then kda_state.hip) without writing any of them to memory: decay prefix g and
+// gamma, the decayed Gram matrices, T = (I + A)^{-1}, U~ = T (beta v), and the
+// state-side products. With m = gamma/2, E = Diag(exp(m)), Kp = k exp(g - m),
+// Qp = q exp(g - m) and Km = k exp(m - g) (the midpoint factors of the Gram
+// matrices), the chunk identities read
+//     W S      = (T Diag(beta) Kp) (E S)              (k exp(g) = Kp E)
+//     QO S     = scale Qp (E S)                      (q exp(g) = Qp E)
+//     S_next   = E (E S + Km^T U)                    (exp(gamma) = E^2)
+// so E scales the state's rows inside the state phase and every per-element
+// product is one of Kp, Qp, Km. The only traffic is the inputs q, k, v,
+// log_alpha, beta (read once, ahead of use), the outputs o, and h0 / hT.
 //
 // The method is the chunk algorithm of the essay "22,580: from GPT-2 to Kimi K3"
 // (yichencityu.github.io, section 6.3: T by forward substitution, W = T K_beta,
@@ -44,28 +49,26 @@ constexpr float kL2E = 1.4426950408889634f;  // log2(e): exponents are kept in b
 constexpr float kClamp = 85.f * kL2E;        // |exponent| limit of the midpoint factors (e^85)
 
 // LDS layout (bytes). The first block is read by the state phase; the rest is
-// chunk preparation. R1 holds Km, Kp, Qp (elementwise -> Gram), then -W and U~
-// (W, U~ -> state).
+// chunk preparation. R1 holds Km and Kp (elementwise -> Gram), then -W' and U~
+// (W', U~ -> state).
 struct Lds {
-    static constexpr int QO = 0;                        // [C][DK]  bf16 fragments
-    static constexpr int KTT = QO + kC * kDK * 2;       // [DK][C]  bf16 fragments
-    static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments
-    static constexpr int EGAM = AQK + kC * kC * 2;      // [DK]     exp(gamma)
-    static constexpr int TOT = EGAM + kDK * 4;          // [4][DK]  log-decay sum of each row block
+    static constexpr int QP = 0;                        // [C][DK]  bf16 fragments: Qp (Gram and state)
+    static constexpr int KTT = QP + kC * kDK * 2;       // [DK][C]  bf16 fragments: Km^T
+    static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments: masked scale Qp Km^T
+    static constexpr int EHALF = AQK + kC * kC * 2;     // [DK]     exp(gamma / 2)
+    static constexpr int TOT = EHALF + kDK * 4;         // [4][DK]  log-decay sum of each row block
     static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  (row-block offset - gamma/2) log2(e)
-    static constexpr int EHALF = OFFM + 4 * kDK * 4;    // [DK]     exp(gamma / 2)
-    static constexpr int EHS = EHALF + kDK * 4;         // [DK]     scale exp(gamma / 2)
-    static constexpr int BET = EHS + kDK * 4;           // [C]      beta (0 past the end)
-    static constexpr int KBET = BET + kC * 4;           // [DK][C]  (beta k exp(g))^T fragments
-    static constexpr int VBT = KBET + kDK * kC * 2;     // [DV][C]  (beta v)^T fragments
+    static constexpr int BET = OFFM + 4 * kDK * 4;      // [C]      beta (0 past the end)
+    static constexpr int KBET = BET + kC * 4;           // [DK][C]  bf16 fragments: (beta Kp)^T
+    static constexpr int VBT = KBET + kDK * kC * 2;     // [DV][C]  bf16 fragments: (beta v)^T
     static constexpr int AM = VBT + kDV * kC * 2;       // [C][PT]  fp32 A (strictly lower)
-    static constexpr int TF = AM + kC * kPT * 4;        // [C][C]   T fragments
+    static constexpr int TF = AM + kC * kPT * 4;        // [C][C]   bf16 fragments: T
     static constexpr int R1 = TF + kC * kC * 2;
-    static constexpr int KM = R1, KP = R1 + kC * kDK * 2, QP = R1 + 2 * kC * kDK * 2;
-    static constexpr int WN = R1, UT = R1 + kC * kDK * 2;  // -W fragments; U~ fp32 accumulator tiles
-    static constexpr int SIZE = R1 + 3 * kC * kDK * 2;
+    static constexpr int KM = R1, KP = R1 + kC * kDK * 2;
+    static constexpr int WN = R1, UT = R1 + kC * kDK * 2;  // -W' fragments; U~ fp32 accumulator tiles
+    static constexpr int SIZE = UT + kC * kDV * 4;
 };
-static_assert(Lds::UT + kC * kDV * 4 <= Lds::SIZE, "U~ fits in R1");
+static_assert(Lds::KP + kC * kDK * 2 <= Lds::SIZE, "Km, Kp fit in R1");
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -169,14 +172,12 @@ __device__ __forceinline__ bf16x8 load_row_frag(const bf16 *row, int kg, int hi)
 
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    bf16 *QO = reinterpret_cast<bf16 *>(smem + Lds::QO);
+    bf16 *Qp = reinterpret_cast<bf16 *>(smem + Lds::QP);
     bf16 *KtT = reinterpret_cast<bf16 *>(smem + Lds::KTT);
     bf16 *Aqk = reinterpret_cast<bf16 *>(smem + Lds::AQK);
-    float *egam = reinterpret_cast<float *>(smem + Lds::EGAM);
     float *tot = reinterpret_cast<float *>(smem + Lds::TOT);
     float *offm = reinterpret_cast<float *>(smem + Lds::OFFM);
     float *ehalf = reinterpret_cast<float *>(smem + Lds::EHALF);
-    float *ehs = reinterpret_cast<float *>(smem + Lds::EHS);
     float *bet = reinterpret_cast<float *>(smem + Lds::BET);
     bf16 *KbeT = reinterpret_cast<bf16 *>(smem + Lds::KBET);
     bf16 *VbT = reinterpret_cast<bf16 *>(smem + Lds::VBT);
@@ -184,7 +185,6 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *Tf = reinterpret_cast<bf16 *>(smem + Lds::TF);
     bf16 *Km = reinterpret_cast<bf16 *>(smem + Lds::KM);
     bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
-    bf16 *Qp = reinterpret_cast<bf16 *>(smem + Lds::QP);
     bf16 *Wn = reinterpret_cast<bf16 *>(smem + Lds::WN);
     float *Ut = reinterpret_cast<float *>(smem + Lds::UT);
 
@@ -314,75 +314,59 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             offm[kDK + tid] = (t0v - m) * kL2E;
             offm[2 * kDK + tid] = ((t0v + t1) - m) * kL2E;
             offm[3 * kDK + tid] = ((t0v + t1 + t2) - m) * kL2E;
-            const float eh = exp2_fast(m * kL2E);
-            ehalf[tid] = eh;
-            ehs[tid] = scale * eh;
-            egam[tid] = exp2_fast(gam * kL2E);
+            ehalf[tid] = exp2_fast(m * kL2E);
         }
         __syncthreads();
 
-        // ---- 2. elementwise, with d = g - gamma/2 (clamped), u = exp(d), 1/u = exp(-d)
-        //      and E = exp(gamma/2): Gram factors Kp = k u, Qp = q u, Km = k / u (the
-        //      query scale is applied to Aqk); QO = scale q u E; KtT = (k E / u)^T,
-        //      Kbe^T = (beta k u E)^T and Vb^T = (beta v)^T transposed by the matrix
-        //      cores into LDS (beta of V applied to the transposed tiles)
+        // ---- 2. elementwise, with d = g - gamma/2 (clamped), u = exp(d), 1/u = exp(-d):
+        //      Kp = k u, Qp = q u and Km = k / u (registers and LDS; the query scale is
+        //      applied to Aqk and O); Km^T, (beta Kp)^T and (beta v)^T transposed by
+        //      the matrix cores into LDS (beta applied to the transposed tiles)
         bf16x8 kpf[2], qpf[2];
         {
         KDA_PHASE_LANE
         const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
+        // beta of chunk rows 16 rb + 4 hi + i (the rows of the transposed tiles' slots)
+        const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int kg = 2 * hf + x;
             const int c0 = frag_chan<bf16>(kg, hi, 0), c4 = frag_chan<bf16>(kg, hi, 4);
             const f32x4 om0 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c0);
             const f32x4 om1 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c4);
-            const f32x4 E0 = *reinterpret_cast<const f32x4 *>(ehalf + c0);
-            const f32x4 E1 = *reinterpret_cast<const f32x4 *>(ehalf + c4);
-            const f32x4 S0 = *reinterpret_cast<const f32x4 *>(ehs + c0);
-            const f32x4 S1 = *reinterpret_cast<const f32x4 *>(ehs + c4);
-            float xp[8], xq[8], xm[8], xo[8], xt[8], xb[8];
+            float xp[8], xq[8], xm[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float om = e < 4 ? om0[e] : om1[e - 4], E = e < 4 ? E0[e] : E1[e - 4];
-                const float Es = e < 4 ? S0[e] : S1[e - 4];
+                const float om = e < 4 ? om0[e] : om1[e - 4];
                 const float d = __builtin_amdgcn_fmed3f(fmaf(g[x][e], kL2E, om), -kClamp, kClamp);
                 const float u = exp2_fast(d), ui = exp2_fast(-d);
                 const float kv = static_cast<float>(kr[x][e]);
-                const float uE = u * E;
                 xp[e] = kv * u;
                 xq[e] = static_cast<float>(qr[x][e]) * u;
                 xm[e] = kv * ui;
-                xo[e] = xq[e] * Es;
-                xt[e] = xm[e] * E;
-                xb[e] = (bt * kv) * uE;
             }
             kpf[x] = pack8(xp);
             qpf[x] = pack8(xq);
-            const bf16x8 km = pack8(xm), qo = pack8(xo), kt = pack8(xt), kb = pack8(xb);
+            const bf16x8 km = pack8(xm);
             const int off = ((kg * 4 + rb) * 64 + l) * 8;
             *reinterpret_cast<bf16x8 *>(Kp + off) = kpf[x];
             *reinterpret_cast<bf16x8 *>(Qp + off) = qpf[x];
             *reinterpret_cast<bf16x8 *>(Km + off) = km;
-            *reinterpret_cast<bf16x8 *>(QO + off) = qo;
             // chunk rows 16 rb .. are contraction slots 4 (rb % 2) .. of group rb / 2
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kt, t ? id1 : id0), l);
-                store_slots(KbeT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kb, t ? id1 : id0), l);
+                store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, km, t ? id1 : id0), l);
+                store_slots(KbeT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kpf[x], t ? id1 : id0) * bv, l);
             }
         }
-        {
-            // beta of chunk rows 16 rb + 4 hi + i (the rows of the transposed tiles' slots)
-            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    store_slots(VbT, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1,
-                                Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0) * bv, l);
+            for (int t = 0; t < 2; ++t)
+                store_slots(VbT, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1,
+                            Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0) * bv, l);
         }
-        }
-        __syncthreads();  // Kp, Qp, Km, QO, KtT, Kbe^T, Vb^T complete
+        __syncthreads();  // Kp, Qp, Km, Km^T, (beta Kp)^T, (beta v)^T complete
         const bool more = ci + 1 < n_c;
         if (more) load_g(ci + 1);  // next chunk's inputs arrive while this one computes
 
@@ -507,8 +491,9 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         __syncthreads();  // T complete
         if (more) load_q(ci + 1);
 
-        // ---- 5. -W (as W^T = Kbe^T T^T, whose tiles are W's operand slots) and
-        //      U~ = T Vb (accumulator tiles), rows rb, tiles of half hf
+        // ---- 5. -W' with W' = T Diag(beta) Kp (as W'^T = (beta Kp)^T T^T, whose tiles
+        //      are W''s operand slots) and U~ = T Vb (accumulator tiles), rows rb,
+        //      tiles of half hf
         {
             KDA_PHASE_LANE
             // all operand groups are read first (T is lower triangular: the second
@@ -544,15 +529,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 *reinterpret_cast<f32x4 *>(Ut + ato(rb, tn, kDV, l)) = acc;
             }
         }
-        __syncthreads();  // -W and U~ complete
+        __syncthreads();  // -W' and U~ complete
         if (more) load_v(ci + 1);
 
-        // ---- 6. state phase (columns 16 w ..): U = U~ - W S, O = QO S + Aqk U
-        //      (stored), S <- exp(gamma) S + KtT U. The shared operands come from
-        //      LDS one row block ahead of the products that use them (the
-        //      scheduling barriers keep those reads ahead of the matrix-core work).
+        // ---- 6. state phase (columns 16 w ..): S <- E S; U = U~ - W' S;
+        //      O = scale Qp S + Aqk U (stored); S <- E (S + Km^T U). The shared
+        //      operands come from LDS one row block ahead of the products that use
+        //      them (the scheduling barriers keep those reads ahead of the
+        //      matrix-core work).
         {
             KDA_PHASE_LANE
+#pragma unroll
+            for (int tm = 0; tm < 8; ++tm) accS[tm] *= *reinterpret_cast<const f32x4 *>(ehalf + 16 * tm + 4 * hi);
             bf16x8 sb[4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) sb[kg] = tiles_to_frag(accS[2 * kg], accS[2 * kg + 1]);
@@ -565,8 +553,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg)  // next: W rows rr + 1, then QO rows 0
-                    fa[(rr + 1) & 1][kg] = rr < 3 ? fld(Wn, kg, rr + 1, kC, l) : fld(QO, kg, 0, kC, l);
+                for (int kg = 0; kg < 4; ++kg)  // next: -W' rows rr + 1, then Qp rows 0
+                    fa[(rr + 1) & 1][kg] = rr < 3 ? fld(Wn, kg, rr + 1, kC, l) : fld(Qp, kg, 0, kC, l);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kg = 0; kg < 4; ++kg) ua[rr] = Frag<bf16>::mma(ua[rr], fa[rr & 1][kg], sb[kg]);
@@ -584,7 +572,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     if (kc <= (rr >> 1)) aq[kc] = fld(Aqk, kc, rr, kC, l);
                 if (rr < 3) {
 #pragma unroll
-                    for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = fld(QO, kg, rr + 1, kC, l);
+                    for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = fld(Qp, kg, rr + 1, kC, l);
                 } else {
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) kf[0][kc] = fld(KtT, kc, 0, kDK, l);
@@ -593,6 +581,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 f32x4 oa = zero4;
 #pragma unroll
                 for (int kg = 0; kg < 4; ++kg) oa = Frag<bf16>::mma(oa, fa[rr & 1][kg], sb[kg]);
+                oa *= scale;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
                     if (kc <= (rr >> 1)) oa = Frag<bf16>::mma(oa, aq[kc], ub[kc]);
@@ -610,11 +599,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) kf[(tm + 1) & 1][kc] = fld(KtT, kc, tm + 1, kDK, l);
                 }
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(egam + 16 * tm + 4 * hi);
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(ehalf + 16 * tm + 4 * hi);
                 __builtin_amdgcn_sched_barrier(0);
-                accS[tm] *= eg;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) accS[tm] = Frag<bf16>::mma(accS[tm], kf[tm & 1][kc], ub[kc]);
+                accS[tm] *= e4;
             }
         }
         // No barrier here: before the next chunk writes anything the state phase

@@ -79,8 +79,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Value of lane I of this lane's 16-lane DPP row.
 template <int I> __device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 0x150 + I, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + I, 0xf, 0xf, true));
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -214,48 +213,60 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     }
 
     // ---- this lane's inputs of one chunk: row r, channel groups 2 hf and 2 hf + 1.
-    //      The next chunk's are requested in four parts spread over the phases
-    //      (a single burst of all of them stalls the issuing waves).
+    //      The next chunk's are requested in four parts, each just before a
+    //      barrier: decay and beta after the scan, key rows after the elementwise
+    //      phase, query rows after the off-diagonal blocks of T and value rows
+    //      after W/U. Issuing a load stalls a wave while the CU's address units
+    //      are busy; at the end of a phase the waves arrive one or two thousand
+    //      cycles apart (the first ones would only wait at the barrier), so few
+    //      requests compete, and no phase starts with a burst of them.
     bf16x8 kr[2], qr[2], vr[2];
     float gl[2][8];
     float bta;
     // uniform base of chunk ci's first row (head h) + 32-bit lane offsets
     auto tok0_of = [&](int ci) { return (seq0 + (size_t)ci * kC) * H + h; };
-    auto row_off = [&](int ci) {  // rows past the end read the last row; beta and decay are zeroed at use
-        return (unsigned)(min(r, T_len - 1 - ci * kC) * H);
+    // Each request derives the lane's row and column group afresh (opaque_lane), so
+    // the per-lane addresses are not kept as loop-carried pointers in registers.
+    auto row_off = [&](int ci, int lane) {  // rows past the end read the last row; beta and decay are zeroed at use
+        return (unsigned)(min(16 * rb + (lane & 15), T_len - 1 - ci * kC) * H);
     };
     auto load_k = [&](int ci) {
+        const int ln = opaque_lane();
         const bf16 *base = static_cast<const bf16 *>(a.k) + tok0_of(ci) * kDK;
-        const unsigned ro = row_off(ci) * kDK;
+        const unsigned ro = row_off(ci, ln) * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) kr[x] = load_row_frag(base + ro, 2 * hf + x, hi);
+        for (int x = 0; x < 2; ++x) kr[x] = load_row_frag(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_q = [&](int ci) {
+        const int ln = opaque_lane();
         const bf16 *base = static_cast<const bf16 *>(a.q) + tok0_of(ci) * kDK;
-        const unsigned ro = row_off(ci) * kDK;
+        const unsigned ro = row_off(ci, ln) * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) qr[x] = load_row_frag(base + ro, 2 * hf + x, hi);
+        for (int x = 0; x < 2; ++x) qr[x] = load_row_frag(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_v = [&](int ci) {
+        const int ln = opaque_lane();
         const bf16 *base = static_cast<const bf16 *>(a.v) + tok0_of(ci) * kDV;
-        const unsigned ro = row_off(ci) * kDV;
+        const unsigned ro = row_off(ci, ln) * kDV;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) vr[x] = load_row_frag(base + ro, 2 * hf + x, hi);
+        for (int x = 0; x < 2; ++x) vr[x] = load_row_frag(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_g = [&](int ci) {
+        const int ln = opaque_lane();
         const size_t t0b = tok0_of(ci);
-        const float *gp = a.log_alpha + t0b * kDK + row_off(ci) * kDK;
+        const unsigned ro = row_off(ci, ln);
+        const float *gp = a.log_alpha + t0b * kDK + ro * kDK;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, hi, 0));
-            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, hi, 4));
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, ln >> 4, 0));
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, ln >> 4, 4));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 gl[x][e] = g0[e];
                 gl[x][4 + e] = g1[e];
             }
         }
-        bta = a.beta[t0b + row_off(ci)];
+        bta = a.beta[t0b + ro];
     };
     load_g(0);
     load_k(0);
@@ -267,6 +278,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
+        const bool more = ci + 1 < n_c;  // the next chunk's inputs are requested below
 
         // ---- 1. inclusive prefix of log(alpha) down the chunk: DPP scan over the
         //      wave's 16 rows, step-major so consecutive DPP operations are
@@ -306,6 +318,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         if (hf == 0 && hi == 0) bet[r] = bt;
         }
+        if (more) load_g(ci + 1);  // decay and beta of this chunk are consumed
         __syncthreads();
         if (tid < kDK) {
             const float t0v = tot[tid], t1 = tot[kDK + tid], t2 = tot[2 * kDK + tid], t3 = tot[3 * kDK + tid];
@@ -366,44 +379,28 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 store_slots(VbT, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1,
                             Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0) * bv, l);
         }
+        if (more) load_k(ci + 1);  // key rows consumed
         __syncthreads();  // Kp, Qp, Km, Km^T, (beta Kp)^T, (beta v)^T complete
-        const bool more = ci + 1 < n_c;
-        if (more) load_g(ci + 1);  // next chunk's inputs arrive while this one computes
 
         // ---- 3. Gram rows of block rb, contraction over all 128 channels (own half
         //      from registers, the other half from LDS)
         if (hf == 0) {
             KDA_PHASE_LANE
-            // A[r][i] = beta_r <Kp_r, Km_i>, i < r; then the inverse of its diagonal block
-            // Km groups of column block tj + 1 are read while block tj is multiplied
+            // the diagonal block of A[r][i] = beta_r <Kp_r, Km_i> (i < r), then the
+            // inverse of (I + that block)
             const bf16x8 ka[4] = {kpf[0], kpf[1], fld(Kp, 2, rb, kC, l), fld(Kp, 3, rb, kC, l)};
-            bf16x8 kmb[2][4];
-#pragma unroll
-            for (int kg = 0; kg < 4; ++kg) kmb[0][kg] = fld(Km, kg, 0, kC, l);
-            f32x4 akk[4];
-#pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
-                if (tj < rb) {
-#pragma unroll
-                    for (int kg = 0; kg < 4; ++kg) kmb[(tj + 1) & 1][kg] = fld(Km, kg, tj + 1, kC, l);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                akk[tj] = zero4;
-                if (tj <= rb) {
-#pragma unroll
-                    for (int kg = 0; kg < 4; ++kg) akk[tj] = Frag<bf16>::mma(akk[tj], ka[kg], kmb[tj & 1][kg]);
-                }
-            }
             const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
+            bf16x8 kmb[4];
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
-                if (tj <= rb) {
+            for (int kg = 0; kg < 4; ++kg) kmb[kg] = fld(Km, kg, rb, kC, l);
+            f32x4 acc = zero4;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = 16 * rb + 4 * hi + i, cc = 16 * tj + lr;
-                        Am[rr * kPT + cc] = (cc < rr) ? bv[i] * akk[tj][i] : 0.f;
-                    }
-                }
+            for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, ka[kg], kmb[kg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * rb + 4 * hi + i, cc = 16 * rb + lr;
+                Am[rr * kPT + cc] = (cc < rr) ? bv[i] * acc[i] : 0.f;
+            }
             // (I + L)^{-1} of the diagonal block L = A[16rb.., 16rb..] by forward
             // substitution: lane (r, hi) holds X[r][4 hi + j]; step i subtracts
             // L[r][i] times row i (broadcast within the 16-lane row). The block's
@@ -432,33 +429,52 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             if ((rb & 1) == 0) store_slots(Tf, rb >> 1, rb, kC, 1, zero4, l);
         } else {
             KDA_PHASE_LANE
-            // Aqk[r][i] = scale <Qp_r, Km_i>, i <= r: tiles of Aqk^T = Km Qp^T are the
-            // operand slots of Aqk's rows rb
-            const bf16x8 qb[4] = {fld(Qp, 0, rb, kC, l), fld(Qp, 1, rb, kC, l), qpf[0], qpf[1]};
+            // The off-diagonal blocks of A's rows rb, A[r][i] = beta_r <Kp_r, Km_i> (i < 16 rb),
+            // and Aqk[r][i] = scale <Qp_r, Km_i> (i <= r) for the rows of block rq = 3 - rb:
+            // four tiles on every wave of this half, with the diagonal blocks of A on the
+            // other half. Tiles of Aqk^T = Km Qp^T are the operand slots of Aqk's rows rq.
+            // Each Km column block is read once (the next one while the current one is
+            // multiplied) and serves both products.
+            const int rq = 3 - rb, rowq = 16 * rq + lr;
+            const int nblk = rb > rq + 1 ? rb : rq + 1;  // Km column blocks used
+            const bf16x8 qb[4] = {fld(Qp, 0, rq, kC, l), fld(Qp, 1, rq, kC, l), fld(Qp, 2, rq, kC, l),
+                                  fld(Qp, 3, rq, kC, l)};
+            bf16x8 ka[4];
+            if (rb > 0) {
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) ka[kg] = fld(Kp, kg, rb, kC, l);
+            }
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
             bf16x8 kmb[2][4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) kmb[0][kg] = fld(Km, kg, 0, kC, l);
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
-                if (tj < rb) {
+                if (tj + 1 < nblk) {
 #pragma unroll
                     for (int kg = 0; kg < 4; ++kg) kmb[(tj + 1) & 1][kg] = fld(Km, kg, tj + 1, kC, l);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (tj < 2 * ((rb >> 1) + 1)) {
+                if (tj < rb) {
                     f32x4 acc = zero4;
-                    if (tj <= rb) {
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, ka[kg], kmb[tj & 1][kg]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Am[(16 * rb + 4 * hi + i) * kPT + 16 * tj + lr] = bv[i] * acc[i];
+                }
+                if (tj < 2 * ((rq >> 1) + 1)) {
+                    f32x4 acc = zero4;
+                    if (tj <= rq) {
 #pragma unroll
                         for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, kmb[tj & 1][kg], qb[kg]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] = (16 * tj + 4 * hi + i <= r) ? scale * acc[i] : 0.f;
+                        for (int i = 0; i < 4; ++i) acc[i] = (16 * tj + 4 * hi + i <= rowq) ? scale * acc[i] : 0.f;
                     }
-                    store_slots(Aqk, tj >> 1, rb, kC, tj & 1, acc, l);
+                    store_slots(Aqk, tj >> 1, rq, kC, tj & 1, acc, l);
                 }
             }
         }
         __syncthreads();  // A, the diagonal blocks of T and Aqk complete
-        if (more) load_k(ci + 1);
 
         // ---- 4. off-diagonal blocks of T, column block j = rb by wave (rb, 1):
         //      T_ij = -D_i Y, Y = sum_{k=j}^{i-1} A_ik T_kj (D_i = T_ii). Both
@@ -488,8 +504,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 }
             }
         }
-        __syncthreads();  // T complete
+        // the next chunk's decay and key rows: the waves without a chain above (half 0
+        // and the last row block) request them at once, the others after their chain
         if (more) load_q(ci + 1);
+        __syncthreads();  // T complete
 
         // ---- 5. -W' with W' = T Diag(beta) Kp (as W'^T = (beta Kp)^T T^T, whose tiles
         //      are W''s operand slots) and U~ = T Vb (accumulator tiles), rows rb,
@@ -529,8 +547,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 *reinterpret_cast<f32x4 *>(Ut + ato(rb, tn, kDV, l)) = acc;
             }
         }
-        __syncthreads();  // -W' and U~ complete
         if (more) load_v(ci + 1);
+        __syncthreads();  // -W' and U~ complete
 
         // ---- 6. state phase (columns 16 w ..): S <- E S; U = U~ - W' S;
         //      O = scale Qp S + Aqk U (stored); S <- E (S + Km^T U). The shared
@@ -578,16 +596,17 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     for (int kc = 0; kc < 2; ++kc) kf[0][kc] = fld(KtT, kc, 0, kDK, l);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                f32x4 oa = zero4;
+                // O^T = S^T (scale Qp)^T + U^T Aqk^T: the operands of O's products with
+                // their roles swapped (A-layout(X^T) is B-layout(X)), so that the
+                // accumulator tile is O^T and lane (r, hi) holds 4 adjacent columns
+                // of chunk row 16 rr + r, stored as 8 bytes
+                f32x4 ot = zero4;
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg) oa = Frag<bf16>::mma(oa, fa[rr & 1][kg], sb[kg]);
-                oa *= scale;
+                for (int kg = 0; kg < 4; ++kg) ot = Frag<bf16>::mma(ot, sb[kg], fa[rr & 1][kg]);
+                ot *= scale;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
-                    if (kc <= (rr >> 1)) oa = Frag<bf16>::mma(oa, aq[kc], ub[kc]);
-                // transpose the tile (identity product) so that lane (r, hi) holds 4
-                // adjacent columns of chunk row 16 rr + r, stored as 8 bytes
-                const f32x4 ot = mma16(to_bf16x4(oa), ident4(), zero4);
+                    if (kc <= (rr >> 1)) ot = Frag<bf16>::mma(ot, ub[kc], aq[kc]);
                 bf16 *dst = t0 + 16 * rr + lr < T_len
                                 ? o_chunk + (unsigned)(((16 * rr + lr) * H) * kDV + 4 * hi)
                                 : static_cast<bf16 *>(a.discard) + 4 * (l & 31);

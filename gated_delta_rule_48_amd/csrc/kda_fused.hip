@@ -13,7 +13,9 @@
 //     QO S     = scale Qp (E S)                      (q exp(g) = Qp E)
 //     S_next   = E (E S + Km^T U)                    (exp(gamma) = E^2)
 // so E scales the state's rows inside the state phase and every per-element
-// product is one of Kp, Qp, Km. The only traffic is the inputs q, k, v,
+// product is one of Kp, Qp, Km. Between chunks the accumulators hold
+// Q = E S + Km^T U (S_next = E Q), and the next chunk's E S is E_next E Q: one
+// scaling of the state per chunk. The only traffic is the inputs q, k, v,
 // log_alpha, beta (read once, ahead of use), the outputs o, and h0 / hT.
 //
 // The method is the chunk algorithm of the essay "22,580: from GPT-2 to Kimi K3"
@@ -55,15 +57,16 @@ struct Lds {
     static constexpr int QP = 0;                        // [C][DK]  bf16 fragments: Qp (Gram and state)
     static constexpr int KTT = QP + kC * kDK * 2;       // [DK][C]  bf16 fragments: Km^T
     static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments: masked scale Qp Km^T
-    static constexpr int EHALF = AQK + kC * kC * 2;     // [DK]     exp(gamma / 2)
+    static constexpr int EHALF = AQK + kC * kC * 2;     // [DK]     exp((gamma_prev + gamma) / 2)
     static constexpr int TOT = EHALF + kDK * 4;         // [4][DK]  log-decay sum of each row block
     static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  (row-block offset - gamma/2) log2(e)
     static constexpr int BET = OFFM + 4 * kDK * 4;      // [C]      beta (0 past the end)
-    static constexpr int KBET = BET + kC * 4;           // [DK][C]  bf16 fragments: (beta Kp)^T
-    static constexpr int VBT = KBET + kDK * kC * 2;     // [DV][C]  bf16 fragments: (beta v)^T
-    static constexpr int AM = VBT + kDV * kC * 2;       // [C][PT]  fp32 A (strictly lower)
-    static constexpr int TF = AM + kC * kPT * 4;        // [C][C]   bf16 fragments: T
-    static constexpr int R1 = TF + kC * kC * 2;
+    static constexpr int KPT = BET + kC * 4;            // [DK][C]  bf16 fragments: Kp^T
+    static constexpr int VT = KPT + kDK * kC * 2;       // [DV][C]  bf16 fragments: v^T
+    static constexpr int AM = VT + kDV * kC * 2;        // [C][PT]  fp32 A (strictly lower)
+    static constexpr int TF = AM + kC * kPT * 4;        // [C][C]   bf16 fragments: T Diag(beta)
+    static constexpr int DG = TF + kC * kC * 2;         // [4][64]  bf16x4 per lane: diagonal blocks of T
+    static constexpr int R1 = DG + 4 * 64 * 4 * 2;
     static constexpr int KM = R1, KP = R1 + kC * kDK * 2;
     static constexpr int WN = R1, UT = R1 + kC * kDK * 2;  // -W' fragments; U~ fp32 accumulator tiles
     static constexpr int SIZE = UT + kC * kDV * 4;
@@ -114,6 +117,22 @@ __device__ __forceinline__ int opaque_lane() {
     return l;
 }
 
+// Key and value channels are held in a fixed permuted order: in registers, in LDS
+// and in the state, position p = 32 kg + 16 t + 4 hi + i of a channel group (the
+// operand slot 4 t + i of lane group hi) holds channel 32 kg + 8 hi + 4 t + i. Each
+// lane's eight slots of a group are then eight adjacent channels of the tensor,
+// one 16-byte load of a bf16 row. The contractions over channels do not depend on
+// their order; only the global loads and stores map positions to channels.
+__device__ __forceinline__ int chan_of_pos(int p) {
+    return (p & ~31) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3);
+}
+
+// Channels 32 kg + 8 hi .. + 7 of a bf16 row: the operand slots of lane group hi
+// for channel group kg.
+__device__ __forceinline__ bf16x8 load_row8(const bf16 *row, int kg, int hi) {
+    return *reinterpret_cast<const bf16x8 *>(row + 32 * kg + 8 * hi);
+}
+
 // The 16 x 16 identity as the B operand of mma16: lane (c, hi) has a one (bf16
 // 0x3f80) in slot c - 4 hi when that is 0..3.
 __device__ __forceinline__ unsigned long long ident4_bits() {
@@ -155,12 +174,6 @@ __device__ __forceinline__ bf16x8 fld(const bf16 *base, int kg, int rb, int R, i
 // Lane l's element offset in tile (rb, cb) of an accumulator-ordered [R][NC] matrix.
 __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb * (NC >> 4) + cb) * 64 + l) * 4; }
 
-__device__ __forceinline__ bf16x8 load_row_frag(const bf16 *row, int kg, int hi) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row + frag_chan<bf16>(kg, hi, 0));
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(row + frag_chan<bf16>(kg, hi, 4));
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
 // Declares this lane's index l, its row lr and lane group hi, and its chunk row r
 // (within the wave's row block rb) from opaque_lane(), for the enclosing phase.
 #define KDA_PHASE_LANE                                                   \
@@ -178,10 +191,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     float *offm = reinterpret_cast<float *>(smem + Lds::OFFM);
     float *ehalf = reinterpret_cast<float *>(smem + Lds::EHALF);
     float *bet = reinterpret_cast<float *>(smem + Lds::BET);
-    bf16 *KbeT = reinterpret_cast<bf16 *>(smem + Lds::KBET);
-    bf16 *VbT = reinterpret_cast<bf16 *>(smem + Lds::VBT);
+    bf16 *KpT = reinterpret_cast<bf16 *>(smem + Lds::KPT);
+    bf16 *Vt = reinterpret_cast<bf16 *>(smem + Lds::VT);
     float *Am = reinterpret_cast<float *>(smem + Lds::AM);
     bf16 *Tf = reinterpret_cast<bf16 *>(smem + Lds::TF);
+    bf16 *Dg = reinterpret_cast<bf16 *>(smem + Lds::DG);
     bf16 *Km = reinterpret_cast<bf16 *>(smem + Lds::KM);
     bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
     bf16 *Wn = reinterpret_cast<bf16 *>(smem + Lds::WN);
@@ -198,15 +212,15 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     const int n_c = (T_len + kC - 1) / kC;
     const size_t seq0 = (size_t)s * T_len;
 
-    // ---- state columns 16 w .. 16 w + 15: tile tm holds rows 16 tm + 4 hi + i of
-    //      column 16 w + lr
+    // ---- state columns (value positions) 16 w .. 16 w + 15: tile tm holds rows (key
+    //      positions) 16 tm + 4 hi + i of column 16 w + lr
     f32x4 accS[8];
     if (a.h0) {
-        const float *h0 = a.h0 + ((size_t)s * H + h) * kDK * kDV + 16 * w + lr;
+        const float *h0 = a.h0 + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) accS[tm][i] = h0[(16 * tm + 4 * hi + i) * kDV];
+            for (int i = 0; i < 4; ++i) accS[tm][i] = h0[chan_of_pos(16 * tm + 4 * hi + i) * kDV];
     } else {
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) accS[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -235,21 +249,21 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         const bf16 *base = static_cast<const bf16 *>(a.k) + tok0_of(ci) * kDK;
         const unsigned ro = row_off(ci, ln) * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) kr[x] = load_row_frag(base + ro, 2 * hf + x, ln >> 4);
+        for (int x = 0; x < 2; ++x) kr[x] = load_row8(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_q = [&](int ci) {
         const int ln = opaque_lane();
         const bf16 *base = static_cast<const bf16 *>(a.q) + tok0_of(ci) * kDK;
         const unsigned ro = row_off(ci, ln) * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) qr[x] = load_row_frag(base + ro, 2 * hf + x, ln >> 4);
+        for (int x = 0; x < 2; ++x) qr[x] = load_row8(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_v = [&](int ci) {
         const int ln = opaque_lane();
         const bf16 *base = static_cast<const bf16 *>(a.v) + tok0_of(ci) * kDV;
         const unsigned ro = row_off(ci, ln) * kDV;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) vr[x] = load_row_frag(base + ro, 2 * hf + x, ln >> 4);
+        for (int x = 0; x < 2; ++x) vr[x] = load_row8(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_g = [&](int ci) {
         const int ln = opaque_lane();
@@ -258,8 +272,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         const float *gp = a.log_alpha + t0b * kDK + ro * kDK;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, ln >> 4, 0));
-            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + frag_chan<bf16>(2 * hf + x, ln >> 4, 4));
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + 32 * (2 * hf + x) + 8 * (ln >> 4));
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 32 * (2 * hf + x) + 8 * (ln >> 4) + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 gl[x][e] = g0[e];
@@ -276,6 +290,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *o = static_cast<bf16 *>(a.o);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    // The accumulators carry Q = P + Km^T U of the last chunk (P = E S at its start),
+    // so that one scaling per chunk, by E_next E = Diag(exp((gamma_prev + gamma) / 2)),
+    // turns Q into the next chunk's P. m_prev is the previous chunk's gamma / 2 (zero
+    // before the first chunk), kept by the threads that form the per-channel factors.
+    float m_prev = 0.f;
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
         const bool more = ci + 1 < n_c;  // the next chunk's inputs are requested below
@@ -327,20 +346,19 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             offm[kDK + tid] = (t0v - m) * kL2E;
             offm[2 * kDK + tid] = ((t0v + t1) - m) * kL2E;
             offm[3 * kDK + tid] = ((t0v + t1 + t2) - m) * kL2E;
-            ehalf[tid] = exp2_fast(m * kL2E);
+            ehalf[tid] = exp2_fast((m + m_prev) * kL2E);
+            m_prev = m;
         }
         __syncthreads();
 
         // ---- 2. elementwise, with d = g - gamma/2 (clamped), u = exp(d), 1/u = exp(-d):
         //      Kp = k u, Qp = q u and Km = k / u (registers and LDS; the query scale is
-        //      applied to Aqk and O); Km^T, (beta Kp)^T and (beta v)^T transposed by
-        //      the matrix cores into LDS (beta applied to the transposed tiles)
+        //      applied to Aqk and O); Km^T, Kp^T and v^T transposed by the matrix cores
+        //      into LDS (beta is carried by T's columns)
         bf16x8 kpf[2], qpf[2];
         {
         KDA_PHASE_LANE
         const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
-        // beta of chunk rows 16 rb + 4 hi + i (the rows of the transposed tiles' slots)
-        const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int kg = 2 * hf + x;
@@ -369,18 +387,17 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, km, t ? id1 : id0), l);
-                store_slots(KbeT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kpf[x], t ? id1 : id0) * bv, l);
+                store_slots(KpT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kpf[x], t ? id1 : id0), l);
             }
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
-                store_slots(VbT, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1,
-                            Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0) * bv, l);
+                store_slots(Vt, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1, Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0), l);
         }
         if (more) load_k(ci + 1);  // key rows consumed
-        __syncthreads();  // Kp, Qp, Km, Km^T, (beta Kp)^T, (beta v)^T complete
+        __syncthreads();  // Kp, Qp, Km, Km^T, Kp^T, v^T complete
 
         // ---- 3. Gram rows of block rb, contraction over all 128 channels (own half
         //      from registers, the other half from LDS)
@@ -425,7 +442,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #undef KDA_SUBST_STEP
             // T fragments of row block rb: the diagonal block in slots 4 (rb % 2) ..,
             // and the zero block above the diagonal for even rb
-            store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0], xs[1], xs[2], xs[3]}, l);
+            // (the unscaled block for the off-diagonal chain; T Diag(beta) for W' and U~,
+            // beta of the block's columns 16 rb + 4 hi + j)
+            *reinterpret_cast<bf16x4 *>(Dg + (rb * 64 + l) * 4) = to_bf16x4(f32x4{xs[0], xs[1], xs[2], xs[3]});
+            store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0] * bv[0], xs[1] * bv[1], xs[2] * bv[2], xs[3] * bv[3]}, l);
             if ((rb & 1) == 0) store_slots(Tf, rb >> 1, rb, kC, 1, zero4, l);
         } else {
             KDA_PHASE_LANE
@@ -476,10 +496,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         __syncthreads();  // A, the diagonal blocks of T and Aqk complete
 
-        // ---- 4. off-diagonal blocks of T, column block j = rb by wave (rb, 1):
-        //      T_ij = -D_i Y, Y = sum_{k=j}^{i-1} A_ik T_kj (D_i = T_ii). Both
-        //      orientations of each block are formed from Y: T_ij (as the B operand
-        //      of the next Y) and T_ij^T (whose tile is T_ij's A operand, stored).
+        // ---- 4. off-diagonal blocks of T' = T Diag(beta), column block j = rb by wave
+        //      (rb, 1): T'_ij = -D_i Y, Y = sum_{k=j}^{i-1} A_ik T'_kj (D_i = T_ii, the
+        //      unscaled diagonal block; the column scaling passes through the sum).
+        //      Both orientations of each block are formed from Y: T'_ij (as the B
+        //      operand of the next Y) and T'_ij^T (whose tile is T'_ij's A operand, stored).
         if (hf == 1 && rb < 3) {
             KDA_PHASE_LANE
             const int j = rb;
@@ -498,7 +519,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                             y = mma16(to_bf16x4(ar), tb[k], y);
                         }
                     const bf16x4 yb = to_bf16x4(y);
-                    const bf16x4 di = load_slots(Tf, i >> 1, i, kC, i & 1, l);
+                    const bf16x4 di = *reinterpret_cast<const bf16x4 *>(Dg + (i * 64 + l) * 4);
                     store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, di, zero4), l);
                     if (i < 3) tb[i] = to_bf16x4(-mma16(di, yb, zero4));
                 }
@@ -509,8 +530,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         if (more) load_q(ci + 1);
         __syncthreads();  // T complete
 
-        // ---- 5. -W' with W' = T Diag(beta) Kp (as W'^T = (beta Kp)^T T^T, whose tiles
-        //      are W''s operand slots) and U~ = T Vb (accumulator tiles), rows rb,
+        // ---- 5. -W' with W' = T' Kp (as W'^T = Kp^T T'^T, whose tiles are W''s operand
+        //      slots) and U~ = T' v (accumulator tiles), T' = T Diag(beta), rows rb,
         //      tiles of half hf
         {
             KDA_PHASE_LANE
@@ -520,15 +541,15 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             bf16x8 tf1 = {}, kb0[4], kb1[4], vb0[4], vb1[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                kb0[u] = fld(KbeT, 0, 4 * hf + u, kDK, l);
-                vb0[u] = fld(VbT, 0, 4 * hf + u, kDV, l);
+                kb0[u] = fld(KpT, 0, 4 * hf + u, kDK, l);
+                vb0[u] = fld(Vt, 0, 4 * hf + u, kDV, l);
             }
             if (rb >= 2) {
                 tf1 = fld(Tf, 1, rb, kC, l);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    kb1[u] = fld(KbeT, 1, 4 * hf + u, kDK, l);
-                    vb1[u] = fld(VbT, 1, 4 * hf + u, kDV, l);
+                    kb1[u] = fld(KpT, 1, 4 * hf + u, kDK, l);
+                    vb1[u] = fld(Vt, 1, 4 * hf + u, kDV, l);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -550,8 +571,9 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         if (more) load_v(ci + 1);
         __syncthreads();  // -W' and U~ complete
 
-        // ---- 6. state phase (columns 16 w ..): S <- E S; U = U~ - W' S;
-        //      O = scale Qp S + Aqk U (stored); S <- E (S + Km^T U). The shared
+        // ---- 6. state phase (columns 16 w ..): P = E S (from the previous chunk's
+        //      Q by the factor E E_prev); U = U~ - W' P; O = scale Qp P + Aqk U
+        //      (stored); Q = P + Km^T U, so that S_next = E Q. The shared
         //      operands come from LDS one row block ahead of the products that use
         //      them (the scheduling barriers keep those reads ahead of the
         //      matrix-core work).
@@ -581,7 +603,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) ub[kc] = tiles_to_frag(ua[2 * kc], ua[2 * kc + 1]);
             bf16x8 kf[2][2];
-            bf16 *o_chunk = o + ((seq0 + t0) * H + h) * kDV + 16 * w;
+            // value positions 16 w + 4 hi + i are channels 32 (w / 2) + 8 hi + 4 (w % 2) + i
+            bf16 *o_chunk = o + ((seq0 + t0) * H + h) * kDV + 32 * (w >> 1) + 4 * (w & 1);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 bf16x8 aq[2];
@@ -608,7 +631,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 for (int kc = 0; kc < 2; ++kc)
                     if (kc <= (rr >> 1)) ot = Frag<bf16>::mma(ot, ub[kc], aq[kc]);
                 bf16 *dst = t0 + 16 * rr + lr < T_len
-                                ? o_chunk + (unsigned)(((16 * rr + lr) * H) * kDV + 4 * hi)
+                                ? o_chunk + (unsigned)(((16 * rr + lr) * H) * kDV + 8 * hi)
                                 : static_cast<bf16 *>(a.discard) + 4 * (l & 31);
                 *reinterpret_cast<bf16x4 *>(dst) = to_bf16x4(ot);
             }
@@ -618,11 +641,9 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) kf[(tm + 1) & 1][kc] = fld(KtT, kc, tm + 1, kDK, l);
                 }
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(ehalf + 16 * tm + 4 * hi);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) accS[tm] = Frag<bf16>::mma(accS[tm], kf[tm & 1][kc], ub[kc]);
-                accS[tm] *= e4;
             }
         }
         // No barrier here: before the next chunk writes anything the state phase
@@ -630,11 +651,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     }
 
     if (a.hT) {
-        float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + 16 * w + lr;
+        // S = E_last Q: the factor exp(gamma / 2) of the last chunk, once every wave has
+        // read that chunk's factors
+        __syncthreads();
+        if (tid < kDK) ehalf[tid] = exp2_fast(m_prev * kL2E);
+        __syncthreads();
+        float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
 #pragma unroll
-        for (int tm = 0; tm < 8; ++tm)
+        for (int tm = 0; tm < 8; ++tm) {
+            const f32x4 e4 = *reinterpret_cast<const f32x4 *>(ehalf + 16 * tm + 4 * hi);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hT[(16 * tm + 4 * hi + i) * kDV] = accS[tm][i];
+            for (int i = 0; i < 4; ++i) hT[chan_of_pos(16 * tm + 4 * hi + i) * kDV] = e4[i] * accS[tm][i];
+        }
     }
 }
 

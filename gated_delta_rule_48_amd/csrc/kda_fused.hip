@@ -28,13 +28,15 @@
 // matrix-core results) overlap the other's work. Wave w = rb + 4 hf:
 //   scan, elementwise  chunk rows 16 rb .. 16 rb + 15, key/value channels of
 //                      half hf (64 of 128), lane l = r + 16 hi holding row r;
-//   Gram               hf = 0: rows rb of A = beta K+ K-^T, then the inverse of
-//                      its diagonal block by forward substitution in registers
-//                      (DPP row broadcasts); hf = 1: rows rb of Aqk;
+//   Gram               hf = 0: the diagonal block rb of A = beta K+ K-^T, then the
+//                      inverse of (I + that block) by forward substitution in
+//                      registers (DPP row broadcasts); hf = 1: the off-diagonal
+//                      blocks of A's rows rb and Aqk's rows 3 - rb (four tiles);
 //   solve              hf = 1, rb < 3: the off-diagonal blocks of column block rb
-//                      of T, one small matrix-core chain per column block;
-//   W, U~              rows rb, d_k (W) and d_v (U~) tiles of half hf;
-//   state              state columns 16 w .. 16 w + 15, all 128 rows.
+//                      of T' = T Diag(beta), one small matrix-core chain each;
+//   state              state columns 16 w .. 16 w + 15, all 128 rows: U = T' (v -
+//                      Kp P) for those columns (so neither W nor U~ is formed for
+//                      the whole chunk), then O and the state update.
 // Intermediates pass between phases in LDS in the permuted fragment order of
 // kda_device.hpp, in which two adjacent accumulator tiles are one operand.
 
@@ -50,9 +52,8 @@ constexpr int kPT = kC + 4;                  // pitch of the fp32 [C][C] matrix 
 constexpr float kL2E = 1.4426950408889634f;  // log2(e): exponents are kept in base 2
 constexpr float kClamp = 85.f * kL2E;        // |exponent| limit of the midpoint factors (e^85)
 
-// LDS layout (bytes). The first block is read by the state phase; the rest is
-// chunk preparation. R1 holds Km and Kp (elementwise -> Gram), then -W' and U~
-// (W', U~ -> state).
+// LDS layout (bytes): operands written by the elementwise and Gram phases and read
+// by the later phases, in the permuted fragment order.
 struct Lds {
     static constexpr int QP = 0;                        // [C][DK]  bf16 fragments: Qp (Gram and state)
     static constexpr int KTT = QP + kC * kDK * 2;       // [DK][C]  bf16 fragments: Km^T
@@ -61,17 +62,14 @@ struct Lds {
     static constexpr int TOT = EHALF + kDK * 4;         // [4][DK]  log-decay sum of each row block
     static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  (row-block offset - gamma/2) log2(e)
     static constexpr int BET = OFFM + 4 * kDK * 4;      // [C]      beta (0 past the end)
-    static constexpr int KPT = BET + kC * 4;            // [DK][C]  bf16 fragments: Kp^T
-    static constexpr int VT = KPT + kDK * kC * 2;       // [DV][C]  bf16 fragments: v^T
+    static constexpr int VT = BET + kC * 4;             // [DV][C]  bf16 fragments: v^T
     static constexpr int AM = VT + kDV * kC * 2;        // [C][PT]  fp32 A (strictly lower)
     static constexpr int TF = AM + kC * kPT * 4;        // [C][C]   bf16 fragments: T Diag(beta)
     static constexpr int DG = TF + kC * kC * 2;         // [4][64]  bf16x4 per lane: diagonal blocks of T
-    static constexpr int R1 = DG + 4 * 64 * 4 * 2;
-    static constexpr int KM = R1, KP = R1 + kC * kDK * 2;
-    static constexpr int WN = R1, UT = R1 + kC * kDK * 2;  // -W' fragments; U~ fp32 accumulator tiles
-    static constexpr int SIZE = UT + kC * kDV * 4;
+    static constexpr int KM = DG + 4 * 64 * 4 * 2;      // [C][DK]  bf16 fragments: Km (Gram)
+    static constexpr int KP = KM + kC * kDK * 2;        // [C][DK]  bf16 fragments: Kp (Gram and state)
+    static constexpr int SIZE = KP + kC * kDK * 2;
 };
-static_assert(Lds::KP + kC * kDK * 2 <= Lds::SIZE, "Km, Kp fit in R1");
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -191,15 +189,12 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     float *offm = reinterpret_cast<float *>(smem + Lds::OFFM);
     float *ehalf = reinterpret_cast<float *>(smem + Lds::EHALF);
     float *bet = reinterpret_cast<float *>(smem + Lds::BET);
-    bf16 *KpT = reinterpret_cast<bf16 *>(smem + Lds::KPT);
     bf16 *Vt = reinterpret_cast<bf16 *>(smem + Lds::VT);
     float *Am = reinterpret_cast<float *>(smem + Lds::AM);
     bf16 *Tf = reinterpret_cast<bf16 *>(smem + Lds::TF);
     bf16 *Dg = reinterpret_cast<bf16 *>(smem + Lds::DG);
     bf16 *Km = reinterpret_cast<bf16 *>(smem + Lds::KM);
     bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
-    bf16 *Wn = reinterpret_cast<bf16 *>(smem + Lds::WN);
-    float *Ut = reinterpret_cast<float *>(smem + Lds::UT);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
@@ -227,10 +222,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     }
 
     // ---- this lane's inputs of one chunk: row r, channel groups 2 hf and 2 hf + 1.
-    //      The next chunk's are requested in four parts, each just before a
+    //      The next chunk's are requested in three parts, each just before a
     //      barrier: decay and beta after the scan, key rows after the elementwise
-    //      phase, query rows after the off-diagonal blocks of T and value rows
-    //      after W/U. Issuing a load stalls a wave while the CU's address units
+    //      phase, query and value rows after the off-diagonal blocks of T.
+    //      Issuing a load stalls a wave while the CU's address units
     //      are busy; at the end of a phase the waves arrive one or two thousand
     //      cycles apart (the first ones would only wait at the barrier), so few
     //      requests compete, and no phase starts with a burst of them.
@@ -385,10 +380,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             *reinterpret_cast<bf16x8 *>(Km + off) = km;
             // chunk rows 16 rb .. are contraction slots 4 (rb % 2) .. of group rb / 2
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < 2; ++t)
                 store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, km, t ? id1 : id0), l);
-                store_slots(KpT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, kpf[x], t ? id1 : id0), l);
-            }
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
@@ -442,7 +435,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #undef KDA_SUBST_STEP
             // T fragments of row block rb: the diagonal block in slots 4 (rb % 2) ..,
             // and the zero block above the diagonal for even rb
-            // (the unscaled block for the off-diagonal chain; T Diag(beta) for W' and U~,
+            // (the unscaled block for the off-diagonal chain; T Diag(beta) for the state phase,
             // beta of the block's columns 16 rb + 4 hi + j)
             *reinterpret_cast<bf16x4 *>(Dg + (rb * 64 + l) * 4) = to_bf16x4(f32x4{xs[0], xs[1], xs[2], xs[3]});
             store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0] * bv[0], xs[1] * bv[1], xs[2] * bv[2], xs[3] * bv[3]}, l);
@@ -525,55 +518,17 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 }
             }
         }
-        // the next chunk's decay and key rows: the waves without a chain above (half 0
+        // the next chunk's query and value rows: the waves without a chain above (half 0
         // and the last row block) request them at once, the others after their chain
-        if (more) load_q(ci + 1);
+        if (more) {
+            load_q(ci + 1);
+            load_v(ci + 1);
+        }
         __syncthreads();  // T complete
 
-        // ---- 5. -W' with W' = T' Kp (as W'^T = Kp^T T'^T, whose tiles are W''s operand
-        //      slots) and U~ = T' v (accumulator tiles), T' = T Diag(beta), rows rb,
-        //      tiles of half hf
-        {
-            KDA_PHASE_LANE
-            // all operand groups are read first (T is lower triangular: the second
-            // contraction group only for rows 32 ..)
-            const bf16x8 tf0 = fld(Tf, 0, rb, kC, l);
-            bf16x8 tf1 = {}, kb0[4], kb1[4], vb0[4], vb1[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                kb0[u] = fld(KpT, 0, 4 * hf + u, kDK, l);
-                vb0[u] = fld(Vt, 0, 4 * hf + u, kDV, l);
-            }
-            if (rb >= 2) {
-                tf1 = fld(Tf, 1, rb, kC, l);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    kb1[u] = fld(KpT, 1, 4 * hf + u, kDK, l);
-                    vb1[u] = fld(Vt, 1, 4 * hf + u, kDV, l);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int tm = 4 * hf + u;
-                f32x4 acc = Frag<bf16>::mma(zero4, kb0[u], tf0);
-                if (rb >= 2) acc = Frag<bf16>::mma(acc, kb1[u], tf1);
-                store_slots(Wn, tm >> 1, rb, kC, tm & 1, -acc, l);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int tn = 4 * hf + u;
-                f32x4 acc = Frag<bf16>::mma(zero4, tf0, vb0[u]);
-                if (rb >= 2) acc = Frag<bf16>::mma(acc, tf1, vb1[u]);
-                *reinterpret_cast<f32x4 *>(Ut + ato(rb, tn, kDV, l)) = acc;
-            }
-        }
-        if (more) load_v(ci + 1);
-        __syncthreads();  // -W' and U~ complete
-
-        // ---- 6. state phase (columns 16 w ..): P = E S (from the previous chunk's
-        //      Q by the factor E E_prev); U = U~ - W' P; O = scale Qp P + Aqk U
-        //      (stored); Q = P + Km^T U, so that S_next = E Q. The shared
+        // ---- 5. state phase (columns 16 w ..): P = (E E_prev) Q; Y = v - Kp P;
+        //      U = T' Y (that is U~ - W' P with U~ = T' v, W' = T' Kp); O = scale Qp P
+        //      + Aqk U (stored); Q = P + Km^T U, so that S_next = E Q. The shared
         //      operands come from LDS one row block ahead of the products that use
         //      them (the scheduling barriers keep those reads ahead of the
         //      matrix-core work).
@@ -584,20 +539,41 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             bf16x8 sb[4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) sb[kg] = tiles_to_frag(accS[2 * kg], accS[2 * kg + 1]);
-            f32x4 ua[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) ua[rr] = *reinterpret_cast<const f32x4 *>(Ut + ato(rr, w, kDV, l));
+            // v of the wave's columns: fragment group kc of v^T's column block w holds the
+            // accumulator tiles 2 kc and 2 kc + 1 of v (chunk rows 16 rr + 4 hi + i in
+            // slots 4 (rr % 2) + i)
+            const bf16x8 vf[2] = {fld(Vt, 0, w, kDV, l), fld(Vt, 1, w, kDV, l)};
             bf16x8 fa[2][4];
 #pragma unroll
-            for (int kg = 0; kg < 4; ++kg) fa[0][kg] = fld(Wn, kg, 0, kC, l);
+            for (int kg = 0; kg < 4; ++kg) fa[0][kg] = fld(Kp, kg, 0, kC, l);
+            bf16x8 tq[6];  // T' operand groups (rows rr, contraction group kc <= rr / 2)
+            f32x4 ya[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
+                if (rr < 3) {
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg)  // next: -W' rows rr + 1, then Qp rows 0
-                    fa[(rr + 1) & 1][kg] = rr < 3 ? fld(Wn, kg, rr + 1, kC, l) : fld(Qp, kg, 0, kC, l);
+                    for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = fld(Kp, kg, rr + 1, kC, l);
+                } else {  // next: T', then Qp rows 0
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) tq[q] = fld(Tf, 0, q, kC, l);
+                    tq[4] = fld(Tf, 1, 2, kC, l);
+                    tq[5] = fld(Tf, 1, 3, kC, l);
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) fa[0][kg] = fld(Qp, kg, 0, kC, l);
+                }
                 __builtin_amdgcn_sched_barrier(0);
+                f32x4 acc = zero4;
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg) ua[rr] = Frag<bf16>::mma(ua[rr], fa[rr & 1][kg], sb[kg]);
+                for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, fa[rr & 1][kg], sb[kg]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ya[rr][i] = static_cast<float>(vf[rr >> 1][4 * (rr & 1) + i]) - acc[i];
+            }
+            const bf16x8 yb[2] = {tiles_to_frag(ya[0], ya[1]), tiles_to_frag(ya[2], ya[3])};
+            f32x4 ua[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                ua[rr] = Frag<bf16>::mma(zero4, tq[rr], yb[0]);
+                if (rr >= 2) ua[rr] = Frag<bf16>::mma(ua[rr], tq[rr + 2], yb[1]);
             }
             bf16x8 ub[2];
 #pragma unroll

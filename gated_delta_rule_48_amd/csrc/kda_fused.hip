@@ -58,7 +58,7 @@ struct Lds {
     static constexpr int QP = 0;                        // [C][DK]  bf16 fragments: Qp (Gram and state)
     static constexpr int KTT = QP + kC * kDK * 2;       // [DK][C]  bf16 fragments: Km^T
     static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments: masked scale Qp Km^T
-    static constexpr int EHALF = AQK + kC * kC * 2;     // [DK]     exp((gamma_prev + gamma) / 2)
+    static constexpr int EHALF = AQK + kC * kC * 2;     // [DK]     exp((gamma_prev + gamma) / 2), in e_slot order
     static constexpr int TOT = EHALF + kDK * 4;         // [4][DK]  log-decay sum of each row block
     static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  (row-block offset - gamma/2) log2(e)
     static constexpr int BET = OFFM + 4 * kDK * 4;      // [C]      beta (0 past the end)
@@ -124,6 +124,12 @@ __device__ __forceinline__ int opaque_lane() {
 __device__ __forceinline__ int chan_of_pos(int p) {
     return (p & ~31) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3);
 }
+
+// Slot of key position p = 16 tm + 4 hi + i in the per-channel factor array: lane
+// group hi's 32 factors (tm = 0..7, i = 0..3) are contiguous, two per lane of its
+// 16-lane row, so that one 8-byte read per lane and row broadcasts give every
+// lane all of them.
+__device__ __forceinline__ int e_slot(int p) { return ((p >> 2) & 3) * 32 + ((p >> 4) << 2) + (p & 3); }
 
 // Channels 32 kg + 8 hi .. + 7 of a bf16 row: the operand slots of lane group hi
 // for channel group kg.
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             offm[kDK + tid] = (t0v - m) * kL2E;
             offm[2 * kDK + tid] = ((t0v + t1) - m) * kL2E;
             offm[3 * kDK + tid] = ((t0v + t1 + t2) - m) * kL2E;
-            ehalf[tid] = exp2_fast((m + m_prev) * kL2E);
+            ehalf[e_slot(tid)] = exp2_fast((m + m_prev) * kL2E);
             m_prev = m;
         }
         __syncthreads();
@@ -534,8 +540,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         //      matrix-core work).
         {
             KDA_PHASE_LANE
-#pragma unroll
-            for (int tm = 0; tm < 8; ++tm) accS[tm] *= *reinterpret_cast<const f32x4 *>(ehalf + 16 * tm + 4 * hi);
+            {
+                // P = (E E_prev) Q: lane (c, hi) needs the factors of key positions
+                // 16 tm + 4 hi + i; lane lr of the row holds those of 4 tm + i = 2 lr, 2 lr + 1
+                const f32x2 e2 = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
+#define KDA_EROW(TM)                                     \
+    accS[TM][0] *= row_bcast<2 * TM>(e2[0]);             \
+    accS[TM][1] *= row_bcast<2 * TM>(e2[1]);             \
+    accS[TM][2] *= row_bcast<2 * TM + 1>(e2[0]);         \
+    accS[TM][3] *= row_bcast<2 * TM + 1>(e2[1]);
+                KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
+#undef KDA_EROW
+            }
             bf16x8 sb[4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) sb[kg] = tiles_to_frag(accS[2 * kg], accS[2 * kg + 1]);
@@ -630,12 +646,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         // S = E_last Q: the factor exp(gamma / 2) of the last chunk, once every wave has
         // read that chunk's factors
         __syncthreads();
-        if (tid < kDK) ehalf[tid] = exp2_fast(m_prev * kL2E);
+        if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
         __syncthreads();
         float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) {
-            const f32x4 e4 = *reinterpret_cast<const f32x4 *>(ehalf + 16 * tm + 4 * hi);
+            const f32x4 e4 = {ehalf[e_slot(16 * tm + 4 * hi)], ehalf[e_slot(16 * tm + 4 * hi + 1)],
+                              ehalf[e_slot(16 * tm + 4 * hi + 2)], ehalf[e_slot(16 * tm + 4 * hi + 3)]};
 #pragma unroll
             for (int i = 0; i < 4; ++i) hT[chan_of_pos(16 * tm + 4 * hi + i) * kDV] = e4[i] * accS[tm][i];
         }

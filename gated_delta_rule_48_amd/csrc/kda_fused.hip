@@ -207,7 +207,6 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, hi = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rb = w & 3, hf = w >> 2;
-    const int r = 16 * rb + lr;  // chunk row held by this lane
     const float scale = a.scale;
     const int T_len = a.seq_len;
     const int n_c = (T_len + kC - 1) / kC;
@@ -503,24 +502,35 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         if (hf == 1 && rb < 3) {
             KDA_PHASE_LANE
             const int j = rb;
-            bf16x4 tb[3];  // B operands of T_kj, k = j .. 2
+            // every operand of the chain is read first: T'_jj, the blocks A_ik (j <= k < i)
+            // and the diagonal blocks D_i (i > j); one wait, then the dependent products
+            f32x4 ar[4][3];
+            bf16x4 dg[4];
+            const bf16x4 tjj = load_slots(Tf, j >> 1, j, kC, j & 1, l);
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                if (i > j) {
+                    dg[i] = *reinterpret_cast<const bf16x4 *>(Dg + (i * 64 + l) * 4);
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        if (k >= j && k < i)
+                            ar[i][k] = *reinterpret_cast<const f32x4 *>(Am + (16 * i + lr) * kPT + 16 * k + 4 * hi);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x4 tb[3];  // B operands of T'_kj, k = j .. 2
 #pragma unroll
             for (int k = 0; k < 3; ++k)
-                if (k == j) tb[k] = to_bf16x4(mma16(load_slots(Tf, k >> 1, k, kC, k & 1, l), ident4(), zero4));
+                if (k == j) tb[k] = to_bf16x4(mma16(tjj, ident4(), zero4));
 #pragma unroll
             for (int i = 1; i < 4; ++i) {
                 if (i > j) {
                     f32x4 y = zero4;
 #pragma unroll
                     for (int k = 0; k < 3; ++k)
-                        if (k >= j && k < i) {
-                            const f32x4 ar = *reinterpret_cast<const f32x4 *>(Am + (16 * i + lr) * kPT + 16 * k + 4 * hi);
-                            y = mma16(to_bf16x4(ar), tb[k], y);
-                        }
+                        if (k >= j && k < i) y = mma16(to_bf16x4(ar[i][k]), tb[k], y);
                     const bf16x4 yb = to_bf16x4(y);
-                    const bf16x4 di = *reinterpret_cast<const bf16x4 *>(Dg + (i * 64 + l) * 4);
-                    store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, di, zero4), l);
-                    if (i < 3) tb[i] = to_bf16x4(-mma16(di, yb, zero4));
+                    store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, dg[i], zero4), l);
+                    if (i < 3) tb[i] = to_bf16x4(-mma16(dg[i], yb, zero4));
                 }
             }
         }

@@ -101,6 +101,30 @@ def copy_probe(torch, mib):
     del src, dst
 
 
+def hbm_probe(torch):
+    """Practical streaming bandwidth on this GPU, for reference next to the 8 TB/s peak:
+    event-timed device copies and in-place multiplies of 0.5, 1 and 2 GiB (bytes read +
+    bytes written over the time), 10 repetitions after 3 warm-up ones. Logged only."""
+    for mib in (512, 1024, 2048):
+        n = mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for name, fn in (("copy", lambda: b.copy_(a)), ("in-place multiply", lambda: a.mul_(1.0001))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            log(f"[bench] hbm probe: {name} of {mib} MiB: {ms:.3f} ms, "
+                f"{2 * mib * (1 << 20) / (ms * 1e-3) / 1e9:.0f} GB/s (read + write)")
+        del a, b
+
+
 def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_states_in):
     """q, k, v, o in the I/O dtype, log_alpha (fp32 per key channel) and beta (fp32)
     per token-head, plus the fp32 states read and written."""
@@ -234,6 +258,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run a device copy of MIB MiB first (counter calibration)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="log the streaming bandwidth of device copies and in-place multiplies first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
@@ -249,6 +275,8 @@ def main():
 
     if args.copy_probe > 0:
         copy_probe(torch, args.copy_probe)
+    if args.hbm_probe:
+        hbm_probe(torch)
     pre = bench_prefill(args, kda, torch)
     dec = None if args.no_decode else bench_decode(args, kda, torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)

@@ -68,7 +68,8 @@ struct Lds {
     static constexpr int DG = TF + kC * kC * 2;         // [4][64]  bf16x4 per lane: diagonal blocks of T
     static constexpr int KM = DG + 4 * 64 * 4 * 2;      // [C][DK]  bf16 fragments: Km (Gram)
     static constexpr int KP = KM + kC * kDK * 2;        // [C][DK]  bf16 fragments: Kp (Gram and state)
-    static constexpr int SIZE = KP + kC * kDK * 2;
+    static constexpr int IDN = KP + kC * kDK * 2;       // [2][64]  bf16x8: each lane's identity operands (ident_frag)
+    static constexpr int SIZE = IDN + 2 * 64 * 16;
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
@@ -144,7 +145,6 @@ __device__ __forceinline__ unsigned long long ident4_bits() {
     const unsigned d = (unsigned)((l & 15) - 4 * (l >> 4));
     return d < 4 ? 0x3f80ull << (16 * d) : 0ull;
 }
-__device__ __forceinline__ bf16x4 ident4() { return __builtin_bit_cast(bf16x4, ident4_bits()); }
 
 // Identity operand for transposing with the matrix cores: as B^T of a 16-column
 // tile t within a contraction group, lane l (column l%16) has a one in the slot
@@ -201,6 +201,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *Dg = reinterpret_cast<bf16 *>(smem + Lds::DG);
     bf16 *Km = reinterpret_cast<bf16 *>(smem + Lds::KM);
     bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
+    bf16 *idn = reinterpret_cast<bf16 *>(smem + Lds::IDN);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
@@ -282,6 +283,12 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         bta = a.beta[t0b + ro];
     };
+    // the identity operands, formed once and read back where a transpose needs them
+    // (the first barrier of the loop precedes every read)
+    if (w == 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) *reinterpret_cast<bf16x8 *>(idn + (t * 64 + l) * 8) = ident_frag(t);
+    }
     load_g(0);
     load_k(0);
     load_q(0);
@@ -298,6 +305,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
         const bool more = ci + 1 < n_c;  // the next chunk's inputs are requested below
+        const bool full = t0 + kC <= T_len;  // no row of the chunk is past the end
 
         // ---- 1. inclusive prefix of log(alpha) down the chunk: DPP scan over the
         //      wave's 16 rows, step-major so consecutive DPP operations are
@@ -305,12 +313,19 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         float g[2][8], bt;
         {
         KDA_PHASE_LANE
-        const bool valid = t0 + r < T_len;
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] = valid ? gl[x][e] : 0.f;
-        bt = valid ? bta : 0.f;
+            for (int e = 0; e < 8; ++e) g[x][e] = gl[x][e];
+        bt = bta;
+        if (!full) {  // rows past the end: no decay, no update
+            const bool valid = t0 + r < T_len;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[x][e] = valid ? g[x][e] : 0.f;
+            bt = valid ? bt : 0.f;
+        }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -358,7 +373,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         bf16x8 kpf[2], qpf[2];
         {
         KDA_PHASE_LANE
-        const bf16x8 id0 = ident_frag(0), id1 = ident_frag(1);
+        const bf16x8 id0 = *reinterpret_cast<const bf16x8 *>(idn + l * 8);
+        const bf16x8 id1 = *reinterpret_cast<const bf16x8 *>(idn + (64 + l) * 8);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int kg = 2 * hf + x;
@@ -453,7 +469,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             // other half. Tiles of Aqk^T = Km Qp^T are the operand slots of Aqk's rows rq.
             // Each Km column block is read once (the next one while the current one is
             // multiplied) and serves both products.
-            const int rq = 3 - rb, rowq = 16 * rq + lr;
+            const int rq = 3 - rb;
             const int nblk = rb > rq + 1 ? rb : rq + 1;  // Km column blocks used
             const bf16x8 qb[4] = {fld(Qp, 0, rq, kC, l), fld(Qp, 1, rq, kC, l), fld(Qp, 2, rq, kC, l),
                                   fld(Qp, 3, rq, kC, l)};
@@ -486,7 +502,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
                         for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, kmb[tj & 1][kg], qb[kg]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] = (16 * tj + 4 * hi + i <= rowq) ? scale * acc[i] : 0.f;
+                        for (int i = 0; i < 4; ++i) acc[i] *= scale;
+                        if (tj == rq) {  // the diagonal tile: i <= r only (the others lie below it)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[i] = (4 * hi + i <= lr) ? acc[i] : 0.f;
+                        }
                     }
                     store_slots(Aqk, tj >> 1, rq, kC, tj & 1, acc, l);
                 }
@@ -520,7 +540,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             bf16x4 tb[3];  // B operands of T'_kj, k = j .. 2
 #pragma unroll
             for (int k = 0; k < 3; ++k)
-                if (k == j) tb[k] = to_bf16x4(mma16(tjj, ident4(), zero4));
+                if (k == j) tb[k] = to_bf16x4(mma16(tjj, *reinterpret_cast<const bf16x4 *>(idn + l * 8), zero4));
 #pragma unroll
             for (int i = 1; i < 4; ++i) {
                 if (i > j) {
@@ -632,9 +652,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
                     if (kc <= (rr >> 1)) ot = Frag<bf16>::mma(ot, ub[kc], aq[kc]);
-                bf16 *dst = t0 + 16 * rr + lr < T_len
-                                ? o_chunk + (unsigned)(((16 * rr + lr) * H) * kDV + 8 * hi)
-                                : static_cast<bf16 *>(a.discard) + 4 * (l & 31);
+                bf16 *dst = o_chunk + (unsigned)(((16 * rr + lr) * H) * kDV + 8 * hi);
+                if (!full && t0 + 16 * rr + lr >= T_len) dst = static_cast<bf16 *>(a.discard) + 4 * (l & 31);
                 *reinterpret_cast<bf16x4 *>(dst) = to_bf16x4(ot);
             }
 #pragma unroll

@@ -470,21 +470,20 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             // Each Km column block is read once (the next one while the current one is
             // multiplied) and serves both products.
             const int rq = 3 - rb;
-            const int nblk = rb > rq + 1 ? rb : rq + 1;  // Km column blocks used
             const bf16x8 qb[4] = {fld(Qp, 0, rq, kC, l), fld(Qp, 1, rq, kC, l), fld(Qp, 2, rq, kC, l),
                                   fld(Qp, 3, rq, kC, l)};
+            // (read unconditionally: a conditional read would be merged with an undefined
+            // value at the branch's end, which costs register copies on every path)
             bf16x8 ka[4];
-            if (rb > 0) {
 #pragma unroll
-                for (int kg = 0; kg < 4; ++kg) ka[kg] = fld(Kp, kg, rb, kC, l);
-            }
+            for (int kg = 0; kg < 4; ++kg) ka[kg] = fld(Kp, kg, rb, kC, l);
             const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
             bf16x8 kmb[2][4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) kmb[0][kg] = fld(Km, kg, 0, kC, l);
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
-                if (tj + 1 < nblk) {
+                if (tj < 3) {  // block tj + 1 (read even when unused, see ka)
 #pragma unroll
                     for (int kg = 0; kg < 4; ++kg) kmb[(tj + 1) & 1][kg] = fld(Km, kg, tj + 1, kC, l);
                 }

@@ -526,15 +526,15 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             f32x4 ar[4][3];
             bf16x4 dg[4];
             const bf16x4 tjj = load_slots(Tf, j >> 1, j, kC, j & 1, l);
+            // (all below-diagonal blocks, whichever j needs: conditional reads would be
+            // merged with undefined values at the branches' ends, at the cost of copies)
 #pragma unroll
-            for (int i = 1; i < 4; ++i)
-                if (i > j) {
-                    dg[i] = *reinterpret_cast<const bf16x4 *>(Dg + (i * 64 + l) * 4);
+            for (int i = 1; i < 4; ++i) {
+                dg[i] = *reinterpret_cast<const bf16x4 *>(Dg + (i * 64 + l) * 4);
 #pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        if (k >= j && k < i)
-                            ar[i][k] = *reinterpret_cast<const f32x4 *>(Am + (16 * i + lr) * kPT + 16 * k + 4 * hi);
-                }
+                for (int k = 0; k < 3; ++k)
+                    if (k < i) ar[i][k] = *reinterpret_cast<const f32x4 *>(Am + (16 * i + lr) * kPT + 16 * k + 4 * hi);
+            }
             __builtin_amdgcn_sched_barrier(0);
             bf16x4 tb[3];  // B operands of T'_kj, k = j .. 2
 #pragma unroll

@@ -107,9 +107,8 @@ __device__ __forceinline__ bf16x8 tiles_to_frag(f32x4 lo, f32x4 hi) {
     return __builtin_bit_cast(bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])});
 }
 
-// The lane index as a value the compiler cannot hoist: constants derived from it
-// are rebuilt where they are used instead of occupying registers for the whole
-// kernel.
+// The lane index as a value the compiler cannot hoist: addresses derived from it
+// are rebuilt where they are used instead of being kept as loop-carried values.
 __device__ __forceinline__ int opaque_lane() {
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));
@@ -156,8 +155,7 @@ __device__ __forceinline__ bf16x8 ident_frag(int t) {
     return __builtin_bit_cast(bf16x8, t ? u32x4{0u, 0u, lo, hi} : u32x4{lo, hi, 0u, 0u});
 }
 
-// The LDS helpers below take the lane index l explicitly: each phase derives it
-// afresh (opaque_lane), so the per-lane addresses live only within the phase.
+// The LDS helpers below take the lane index l explicitly (each phase declares it).
 
 // Store accumulator tile `acc` as slots 4 t .. 4 t + 3 of lane l's share of
 // group (kg, rb) of a fragment-ordered matrix with R rows.
@@ -179,11 +177,11 @@ __device__ __forceinline__ bf16x8 fld(const bf16 *base, int kg, int rb, int R, i
 __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb * (NC >> 4) + cb) * 64 + l) * 4; }
 
 // Declares this lane's index l, its row lr and lane group hi, and its chunk row r
-// (within the wave's row block rb) from opaque_lane(), for the enclosing phase.
-#define KDA_PHASE_LANE                                                   \
-    const int l = opaque_lane(), lr = l & 15, hi = l >> 4, r = 16 * rb + lr; \
-    (void)lr;                                                            \
-    (void)hi;                                                            \
+// (within the wave's row block rb), for the enclosing phase.
+#define KDA_PHASE_LANE                                                         \
+    const int l = threadIdx.x & 63, lr = l & 15, hi = l >> 4, r = 16 * rb + lr; \
+    (void)lr;                                                                  \
+    (void)hi;                                                                  \
     (void)r;
 
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {

@@ -73,6 +73,8 @@ struct Lds {
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
+template <int I> struct IntTag { static constexpr int value = I; };
+
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -534,22 +536,35 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     if (k < i) ar[i][k] = *reinterpret_cast<const f32x4 *>(Am + (16 * i + lr) * kPT + 16 * k + 4 * hi);
             }
             __builtin_amdgcn_sched_barrier(0);
-            bf16x4 tb[3];  // B operands of T'_kj, k = j .. 2
+            // Right-looking order, with the column block j as a compile-time constant (so
+            // that the accumulators stay in registers): as soon as T'_kj is known, its
+            // contribution A_ik T'_kj is added to every later row block i, so that each
+            // level waits on one product and the multiplication by D_i, not on the sum.
+            auto chain = [&](auto jt) {
+                constexpr int J = decltype(jt)::value;
+                f32x4 y[4] = {zero4, zero4, zero4, zero4};
+                {
+                    const bf16x4 tb = to_bf16x4(mma16(tjj, *reinterpret_cast<const bf16x4 *>(idn + l * 8), zero4));
 #pragma unroll
-            for (int k = 0; k < 3; ++k)
-                if (k == j) tb[k] = to_bf16x4(mma16(tjj, *reinterpret_cast<const bf16x4 *>(idn + l * 8), zero4));
-#pragma unroll
-            for (int i = 1; i < 4; ++i) {
-                if (i > j) {
-                    f32x4 y = zero4;
-#pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        if (k >= j && k < i) y = mma16(to_bf16x4(ar[i][k]), tb[k], y);
-                    const bf16x4 yb = to_bf16x4(y);
-                    store_slots(Tf, j >> 1, i, kC, j & 1, -mma16(yb, dg[i], zero4), l);
-                    if (i < 3) tb[i] = to_bf16x4(-mma16(dg[i], yb, zero4));
+                    for (int i = J + 1; i < 4; ++i) y[i] = mma16(to_bf16x4(ar[i][J]), tb, y[i]);
                 }
-            }
+#pragma unroll
+                for (int i = J + 1; i < 4; ++i) {
+                    const bf16x4 yb = to_bf16x4(y[i]);
+                    store_slots(Tf, J >> 1, i, kC, J & 1, -mma16(yb, dg[i], zero4), l);
+                    if (i < 3) {
+                        const bf16x4 tb = to_bf16x4(-mma16(dg[i], yb, zero4));
+#pragma unroll
+                        for (int i2 = i + 1; i2 < 4; ++i2) y[i2] = mma16(to_bf16x4(ar[i2][i]), tb, y[i2]);
+                    }
+                }
+            };
+            if (j == 0)
+                chain(IntTag<0>{});
+            else if (j == 1)
+                chain(IntTag<1>{});
+            else
+                chain(IntTag<2>{});
         }
         // the next chunk's query and value rows: the waves without a chain above (half 0
         // and the last row block) request them at once, the others after their chain

@@ -1,0 +1,75 @@
+"""Compile-time resource checks of the gfx950 kernels (no GPU needed).
+
+The kernels keep their working set in registers and LDS. A kernel that spills
+VGPRs or places an array in scratch (private memory) still computes the right
+values, but every scratch access is a memory round trip, and a scratch reload in
+the fused pass waits, in order, behind the outstanding prefetch loads. The fused
+pass also relies on two waves per SIMD (eight waves per workgroup). These checks
+read the compiler's own resource report for each kernel.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
+SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip"]
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def _report(src, outdir):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-c", os.path.join(CSRC, src),
+           "-o", os.path.join(outdir, src + ".o"), "-Rpass-analysis=kernel-resource-usage"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-4000:]
+    kernels, cur = {}, None
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: +(.+?) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if not m:
+            continue
+        key, _, val = m.group(1).partition(":")
+        if key == "Function Name":
+            cur = val.strip()
+            kernels[cur] = {}
+        elif cur is not None:
+            kernels[cur][key.strip()] = val.strip()
+    return kernels
+
+
+@pytest.fixture(scope="module")
+def resources():
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d, ThreadPoolExecutor(len(SOURCES)) as ex:
+        reports = list(ex.map(lambda s: _report(s, d), SOURCES))
+    out = {}
+    for r in reports:
+        out.update(r)
+    return out
+
+
+def test_every_kernel_is_reported(resources):
+    names = " ".join(resources)
+    for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_decode_kernel",
+              "kda_chunk_offsets_kernel"):
+        assert k in names, k
+
+
+def test_no_scratch_and_no_spills(resources):
+    for name, r in resources.items():
+        assert r["ScratchSize [bytes/lane]"] == "0", (name, r)
+        assert r["VGPRs Spill"] == "0", (name, r)
+        assert r["Dynamic Stack"] == "False", (name, r)
+
+
+def test_fused_kernel_runs_two_waves_per_simd(resources):
+    fused = [r for n, r in resources.items() if "kda_fused_kernel" in n]
+    assert len(fused) == 1
+    assert int(fused[0]["Occupancy [waves/SIMD]"]) >= 2, fused[0]
+    assert int(fused[0]["VGPRs"]) <= 256, fused[0]

@@ -14,8 +14,10 @@
 //     S_next   = E (E S + Km^T U)                    (exp(gamma) = E^2)
 // so E scales the state's rows inside the state phase and every per-element
 // product is one of Kp, Qp, Km. Between chunks the accumulators hold
-// Q = E S + Km^T U (S_next = E Q), and the next chunk's E S is E_next E Q: one
-// scaling of the state per chunk. The only traffic is the inputs q, k, v,
+// Q = E S + Km^T U (S_next = E Q), and the next chunk's E S is E_next (E Q): the
+// two factors are applied one after the other at the start of the next state
+// phase, since their product alone underflows fp32 long before either factor.
+// The only traffic is the inputs q, k, v,
 // log_alpha, beta (read once, ahead of use), the outputs o, and h0 / hT.
 //
 // The method is the chunk algorithm of the essay "22,580: from GPT-2 to Kimi K3"
@@ -58,8 +60,8 @@ struct Lds {
     static constexpr int QP = 0;                        // [C][DK]  bf16 fragments: Qp (Gram and state)
     static constexpr int KTT = QP + kC * kDK * 2;       // [DK][C]  bf16 fragments: Km^T
     static constexpr int AQK = KTT + kDK * kC * 2;      // [C][C]   bf16 fragments: masked scale Qp Km^T
-    static constexpr int EHALF = AQK + kC * kC * 2;     // [DK]     exp((gamma_prev + gamma) / 2), in e_slot order
-    static constexpr int TOT = EHALF + kDK * 4;         // [4][DK]  log-decay sum of each row block
+    static constexpr int EHALF = AQK + kC * kC * 2;     // [2][DK]  exp(gamma_prev / 2), exp(gamma / 2), in e_slot order
+    static constexpr int TOT = EHALF + 2 * kDK * 4;     // [4][DK]  log-decay sum of each row block
     static constexpr int OFFM = TOT + 4 * kDK * 4;      // [4][DK]  (row-block offset - gamma/2) log2(e)
     static constexpr int BET = OFFM + 4 * kDK * 4;      // [C]      beta (0 past the end)
     static constexpr int VT = BET + kC * 4;             // [DV][C]  bf16 fragments: v^T
@@ -297,10 +299,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *o = static_cast<bf16 *>(a.o);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // The accumulators carry Q = P + Km^T U of the last chunk (P = E S at its start),
-    // so that one scaling per chunk, by E_next E = Diag(exp((gamma_prev + gamma) / 2)),
-    // turns Q into the next chunk's P. m_prev is the previous chunk's gamma / 2 (zero
-    // before the first chunk), kept by the threads that form the per-channel factors.
+    // The accumulators carry Q = P + Km^T U of the last chunk (P = E S at its start);
+    // the next chunk's P is E_next (E Q), E = Diag(exp(gamma / 2)). m_prev is the
+    // previous chunk's gamma / 2 (zero before the first chunk), kept by the threads
+    // that form the per-channel factors.
     float m_prev = 0.f;
     for (int ci = 0; ci < n_c; ++ci) {
         const int t0 = ci * kC;
@@ -361,7 +363,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             offm[kDK + tid] = (t0v - m) * kL2E;
             offm[2 * kDK + tid] = ((t0v + t1) - m) * kL2E;
             offm[3 * kDK + tid] = ((t0v + t1 + t2) - m) * kL2E;
-            ehalf[e_slot(tid)] = exp2_fast((m + m_prev) * kL2E);
+            ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
+            ehalf[kDK + e_slot(tid)] = exp2_fast(m * kL2E);
             m_prev = m;
         }
         __syncthreads();
@@ -574,7 +577,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         __syncthreads();  // T complete
 
-        // ---- 5. state phase (columns 16 w ..): P = (E E_prev) Q; Y = v - Kp P;
+        // ---- 5. state phase (columns 16 w ..): P = E (E_prev Q); Y = v - Kp P;
         //      U = T' Y (that is U~ - W' P with U~ = T' v, W' = T' Kp); O = scale Qp P
         //      + Aqk U (stored); Q = P + Km^T U, so that S_next = E Q. The shared
         //      operands come from LDS one row block ahead of the products that use
@@ -583,14 +586,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         {
             KDA_PHASE_LANE
             {
-                // P = (E E_prev) Q: lane (c, hi) needs the factors of key positions
-                // 16 tm + 4 hi + i; lane lr of the row holds those of 4 tm + i = 2 lr, 2 lr + 1
-                const f32x2 e2 = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
-#define KDA_EROW(TM)                                     \
-    accS[TM][0] *= row_bcast<2 * TM>(e2[0]);             \
-    accS[TM][1] *= row_bcast<2 * TM>(e2[1]);             \
-    accS[TM][2] *= row_bcast<2 * TM + 1>(e2[0]);         \
-    accS[TM][3] *= row_bcast<2 * TM + 1>(e2[1]);
+                // P = E (E_prev Q), the two factors applied one after the other: Q can be
+                // as large as E_prev is small, and their product E E_prev alone would leave
+                // the fp32 range long before either factor does. Lane (c, hi) needs the
+                // factors of key positions 16 tm + 4 hi + i; lane lr of the row holds those
+                // of 4 tm + i = 2 lr, 2 lr + 1.
+                const f32x2 ep = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
+                const f32x2 ec = *reinterpret_cast<const f32x2 *>(ehalf + kDK + 32 * hi + 2 * lr);
+#define KDA_EROW(TM)                                                                       \
+    accS[TM][0] = accS[TM][0] * row_bcast<2 * TM>(ep[0]) * row_bcast<2 * TM>(ec[0]);         \
+    accS[TM][1] = accS[TM][1] * row_bcast<2 * TM>(ep[1]) * row_bcast<2 * TM>(ec[1]);         \
+    accS[TM][2] = accS[TM][2] * row_bcast<2 * TM + 1>(ep[0]) * row_bcast<2 * TM + 1>(ec[0]); \
+    accS[TM][3] = accS[TM][3] * row_bcast<2 * TM + 1>(ep[1]) * row_bcast<2 * TM + 1>(ec[1]);
                 KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
 #undef KDA_EROW
             }

@@ -18,6 +18,8 @@ Workloads (sizes from the five benchmark configurations of this library):
 Gate families (log alpha is drawn per token, per head and per key channel):
   weak:  log alpha = -0.1 * softplus(N(0,1)),  beta = sigmoid(N(0,1))
   main:  log alpha = -softplus(N(-2,1)),       beta = sigmoid(N(0,1))
+  strong: log alpha = -1.3 softplus(N(1,1)),   beta = sigmoid(N(0,1))   (a test family: fast
+          forgetting, chunk sums of log alpha near -110 on average, inside the >= -170 limit)
 q and k are N(0,1) vectors L2-normalised per (token, head); v ~ N(0,1).
 "N(mu, s)" means standard deviation s.
 
@@ -42,7 +44,7 @@ class Workload:
     dv: int
     chunk: int
     io: str                 # "f32" or "bf16": dtype of q, k, v and o
-    gates: str              # "weak" or "main"
+    gates: str              # "weak", "main" (or "strong" in tests)
     h0: str                 # "zero" or "normal"
     seed: int
 
@@ -103,6 +105,8 @@ def _gates(rng, family, shape, dk):
         la = -0.1 * softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64))
     elif family == "main":
         la = -softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64) - 2.0)
+    elif family == "strong":
+        la = -1.3 * softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64) + 1.0)
     else:
         raise ValueError(family)
     beta = sigmoid(rng.standard_normal(shape, dtype=np.float32).astype(np.float64))

@@ -288,6 +288,20 @@ def test_fused_path(io, dk, dv, T):
     _check(x, io, 64, f"fused T={T}", varlen=False, B=2, T=T)
 
 
+@pytest.mark.parametrize("io,path", [("f32", "split"), ("bf16", "split"), ("bf16", "fused")])
+def test_strong_decay(io, path):
+    """Fast-forgetting gates ("strong": chunk sums of log alpha near -117 on average and
+    down to about -150, inside the documented >= -170 limit). The in-chunk decay factors
+    then span up to e^(+-75) and the state factors reach e^(-75) per chunk: products of
+    such factors must be formed in an order that stays inside the fp32 range."""
+    if path == "fused":
+        x = gen([200, 200], 128, 128, 128, io, gates="strong", seed=91)
+        _check(x, io, 64, "strong fused", varlen=False, B=2, T=200)
+    else:
+        x = gen([200, 130], 8, 128, 128, io, gates="strong", seed=92)
+        _check(x, io, 64, "strong split")
+
+
 def test_fused_path_no_h0():
     x = gen([129, 129], 128, 128, 128, "bf16", h0="zero", seed=77)
     o, hT = run_packed(x, "bf16", 64, varlen=False, B=2, T=129, h0=False)

@@ -32,8 +32,13 @@
  *    written and nothing is enqueued. KDA_ERR_HIP reports a failed launch.
  *    Device-side faults surface at the caller's next synchronisation. Input
  *    VALUES are not checked: gates must be finite, and within one chunk the
- *    summed log_alpha of each key channel must stay >= -170 (beyond that the
- *    in-chunk decay factors are clamped and lose accuracy).
+ *    summed log_alpha of each key channel must stay >= -170. The chunked form
+ *    factors the in-chunk decay around the chunk's midpoint, so its factors
+ *    span e^(+-|sum|/2); past the limit they leave the fp32 range and are
+ *    clamped, and the results are wrong, not merely less accurate (relative
+ *    L2 error of o about 0.3 at sums near -220). Inside it, fast-forgetting
+ *    channels (sums near -150) keep the usual accuracy. For gates that strong
+ *    use the decode step, which forms no such factors.
  */
 #ifndef KDA_H_
 #define KDA_H_

@@ -14,9 +14,10 @@
 //     S_next   = E (E S + Km^T U)                    (exp(gamma) = E^2)
 // so E scales the state's rows inside the state phase and every per-element
 // product is one of Kp, Qp, Km. Between chunks the accumulators hold
-// Q = E S + Km^T U (S_next = E Q), and the next chunk's E S is E_next (E Q): the
-// two factors are applied one after the other at the start of the next state
-// phase, since their product alone underflows fp32 long before either factor.
+// Q = E S + Km^T U (S_next = E Q), and the next chunk's E S is E_next (E Q),
+// applied at the start of the next state phase: as one factor E_next E while
+// that stays in the normal fp32 range, else one factor after the other (the
+// product underflows long before either factor does).
 // The only traffic is the inputs q, k, v,
 // log_alpha, beta (read once, ahead of use), the outputs o, and h0 / hT.
 //
@@ -71,7 +72,8 @@ struct Lds {
     static constexpr int KM = DG + 4 * 64 * 4 * 2;      // [C][DK]  bf16 fragments: Km (Gram)
     static constexpr int KP = KM + kC * kDK * 2;        // [C][DK]  bf16 fragments: Kp (Gram and state)
     static constexpr int IDN = KP + kC * kDK * 2;       // [2][64]  bf16x8: each lane's identity operands (ident_frag)
-    static constexpr int SIZE = IDN + 2 * 64 * 16;
+    static constexpr int FLG = IDN + 2 * 64 * 16;       // [2]      int: E E_prev leaves the normal fp32 range
+    static constexpr int SIZE = FLG + 16;
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *Km = reinterpret_cast<bf16 *>(smem + Lds::KM);
     bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
     bf16 *idn = reinterpret_cast<bf16 *>(smem + Lds::IDN);
+    int *flg = reinterpret_cast<int *>(smem + Lds::FLG);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
@@ -365,6 +368,9 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             offm[3 * kDK + tid] = ((t0v + t1 + t2) - m) * kL2E;
             ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
             ehalf[kDK + e_slot(tid)] = exp2_fast(m * kL2E);
+            // whether E E_prev of some channel falls below the normal fp32 range
+            const unsigned long long tiny = __ballot((m + m_prev) * kL2E < -120.f);
+            if ((tid & 63) == 0) flg[tid >> 6] = tiny != 0ull;
             m_prev = m;
         }
         __syncthreads();
@@ -586,20 +592,31 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         {
             KDA_PHASE_LANE
             {
-                // P = E (E_prev Q), the two factors applied one after the other: Q can be
-                // as large as E_prev is small, and their product E E_prev alone would leave
-                // the fp32 range long before either factor does. Lane (c, hi) needs the
-                // factors of key positions 16 tm + 4 hi + i; lane lr of the row holds those
-                // of 4 tm + i = 2 lr, 2 lr + 1.
+                // P = E (E_prev Q). Q can be as large as E_prev is small, so where the
+                // product E E_prev leaves the normal fp32 range (fast-forgetting channels)
+                // the two factors are applied one after the other; otherwise their product
+                // is. Lane (c, hi) needs the factors of key positions 16 tm + 4 hi + i;
+                // lane lr of the row holds those of 4 tm + i = 2 lr, 2 lr + 1.
                 const f32x2 ep = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
                 const f32x2 ec = *reinterpret_cast<const f32x2 *>(ehalf + kDK + 32 * hi + 2 * lr);
+                if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
 #define KDA_EROW(TM)                                                                       \
     accS[TM][0] = accS[TM][0] * row_bcast<2 * TM>(ep[0]) * row_bcast<2 * TM>(ec[0]);         \
     accS[TM][1] = accS[TM][1] * row_bcast<2 * TM>(ep[1]) * row_bcast<2 * TM>(ec[1]);         \
     accS[TM][2] = accS[TM][2] * row_bcast<2 * TM + 1>(ep[0]) * row_bcast<2 * TM + 1>(ec[0]); \
     accS[TM][3] = accS[TM][3] * row_bcast<2 * TM + 1>(ep[1]) * row_bcast<2 * TM + 1>(ec[1]);
-                KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
+                    KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
 #undef KDA_EROW
+                } else {
+                    const f32x2 e2 = ep * ec;
+#define KDA_EROW(TM)                                     \
+    accS[TM][0] *= row_bcast<2 * TM>(e2[0]);             \
+    accS[TM][1] *= row_bcast<2 * TM>(e2[1]);             \
+    accS[TM][2] *= row_bcast<2 * TM + 1>(e2[0]);         \
+    accS[TM][3] *= row_bcast<2 * TM + 1>(e2[1]);
+                    KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
+#undef KDA_EROW
+                }
             }
             bf16x8 sb[4];
 #pragma unroll

@@ -13,7 +13,10 @@ Also reported on the same line:
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample
                 of the same prefill workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+With --workloads NAMES, further prefill workloads (the small-batch, varlen and fp32
+ones of kda_synth) are timed the same way and reported under "workloads".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,varlen,tiny]
 """
 from __future__ import annotations
 
@@ -182,6 +185,61 @@ def bench_prefill(args, kda, torch):
     return res
 
 
+def bench_workload(args, kda, torch, name):
+    """kda_chunk_fwd on another synthetic workload of kda_synth (the schedule the library
+    picks for it), event-timed like the headline: ms per call, tokens/s and algorithmic
+    GB/s against the HBM peak. Equal-length sequences are passed as [B, T, H, d], others
+    packed with cu_seqlens."""
+    w = kda_synth.WORKLOADS[name]
+    log(f"[bench] generating workload {name}: seqlens {w.seqlens}, H={w.H}, d={w.dk}, chunk {w.chunk}, {w.io}")
+    x = kda_synth.gen_workload(w)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    varlen = len(set(w.seqlens)) > 1
+    B, T = (1, sum(w.seqlens)) if varlen else (len(w.seqlens), w.seqlens[0])
+    lead = (T,) if varlen else (B, T)
+    q = torch.from_numpy(x["q"]).to(dev).to(dt).reshape(lead + (w.H, w.dk))
+    k = torch.from_numpy(x["k"]).to(dev).to(dt).reshape(lead + (w.H, w.dk))
+    v = torch.from_numpy(x["v"]).to(dev).to(dt).reshape(lead + (w.H, w.dv))
+    la = torch.from_numpy(x["log_alpha"]).to(dev).reshape(lead + (w.H, w.dk))
+    beta = torch.from_numpy(x["beta"]).to(dev).reshape(lead + (w.H,))
+    h0 = None if x["h0"] is None else torch.from_numpy(x["h0"]).to(dev)
+    cu = torch.from_numpy(x["cu_seqlens"]).to(dev) if varlen else None
+    n_seqs = len(w.seqlens)
+    o = torch.empty(lead + (w.H, w.dv), dtype=dt, device=dev)
+    hT = torch.empty((n_seqs, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    io = kda.KDA_BF16 if w.io == "bf16" else kda.KDA_F32
+    ws = torch.empty(kda.workspace_bytes(B, T, w.H, w.dk, w.dv, w.chunk, n_seqs if varlen else 0, io),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_fwd(q, k, v, la, beta, scale=w.scale, h0=h0, cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT,
+                      workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = sum(w.seqlens)
+    alg = prefill_algorithmic_bytes(tokens * w.H, w.dk, w.dv, 2 if w.io == "bf16" else 4, n_seqs * w.H,
+                                    0 if h0 is None else n_seqs * w.H)
+    achieved = alg / (ms * 1e-3) / 1e9
+    path = prefill_path(B, T, w.H, w.dk, w.dv, w.chunk, varlen, w.io == "bf16")
+    log(f"[bench] workload {name} ({path} pass): {ms:.3f} ms/call, {tokens / (ms * 1e-3):.3e} tokens/s, "
+        f"{achieved:.0f} GB/s algorithmic")
+    return {"value": tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 4), "pass": path,
+            "kernel": PATHS[path]["kernel"],
+            "workload": f"seqlens {list(w.seqlens)}, H={w.H}, d_k=d_v={w.dk}, chunk {w.chunk}, {w.io} q/k/v/o",
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
+
+
 def bench_decode(args, kda, torch):
     d = kda_synth.DECODE
     N, H, dk, dv = d["N"], d["H"], d["dk"], d["dv"]
@@ -262,6 +320,9 @@ def main():
                     help="log the streaming bandwidth of device copies and in-place multiplies first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workloads", default="", metavar="NAMES",
+                    help="comma-separated further prefill workloads to time and report (" +
+                         ", ".join(n for n in kda_synth.WORKLOADS if n != "batched") + ")")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -279,6 +340,7 @@ def main():
         hbm_probe(torch)
     pre = bench_prefill(args, kda, torch)
     dec = None if args.no_decode else bench_decode(args, kda, torch)
+    others = {n: bench_workload(args, kda, torch, n) for n in args.workloads.split(",") if n}
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
 
     w = pre["workload"]
@@ -313,6 +375,8 @@ def main():
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(dec["achieved_gbs"] / HBM_PEAK_GBS, 4),
                                        "alg_bytes_per_launch": dec["alg_bytes"]}}
+    if others:
+        line["workloads"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -28,10 +28,13 @@
 // and bf16 share that range). Entries above the diagonal would carry huge
 // factors and are dropped by selection, never by multiplying with a zero mask.
 //
-// Memory access: each thread owns 8 adjacent channels of C/(4*C/(d/8)) rows and
-// issues all of its 16-byte loads before any computation; every output goes
-// through LDS and leaves as fully coalesced 16-byte stores, in the
-// fragment-ordered layouts the state kernel reads.
+// Memory access: each thread owns one chunk row's 8 (bf16) or 4 (fp32) adjacent
+// channels per operand group and issues all of its loads before any computation.
+// The outputs leave in the fragment-ordered layouts the state kernel reads: QO as
+// row groups, KtT, Aqk and W as accumulator tiles of their transposes, which the
+// matrix cores form (a product with an identity operand, or the operands of a
+// product with their roles swapped) and which are each lane's four consecutive
+// operand slots; U~ as accumulator tiles.
 
 #include "kda_internal.hpp"
 #include "kda_solve.hpp"
@@ -43,28 +46,17 @@ template <int C, int DK, int DV, typename T> struct PrepCfg {
     typedef Frag<T> F;
     static constexpr int NW = C / 16, NT = 64 * NW;   // wave w owns chunk rows 16w .. 16w+15
     static constexpr int NKG = DK / F::KG, NVG = DV / F::KG;
-    static constexpr int PT = C + 4;                  // pitch of the fp32 [C][C] matrices
+    static constexpr int PT = C + 4;                  // pitch of the fp32 [C][C] matrix A (then T)
     // columns of W / U~ per pass of the final product (LDS budget)
     static constexpr int PW = (sizeof(T) == 4 && C == 128) ? 64 : 128;
     static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-    static constexpr size_t SMALL = (size_t)(NW * DK + C) * 4;
-    static constexpr size_t MATF = (size_t)C * PT * 4;
-    static constexpr size_t GRAM = (size_t)2 * C * DK * sizeof(T);           // Km + KtT staging
-    static constexpr size_t AQK = MATF + (size_t)C * C * sizeof(T);          // Aqk staging + Am
-    static constexpr size_t SOLVE = 2 * MATF;
-    static constexpr size_t WPASS = MATF + (size_t)2 * PW * C * sizeof(T);   // Tm + B operand + W staging
-    static constexpr size_t REGION = mx(mx(GRAM, AQK), mx(SOLVE, WPASS));
+    static constexpr size_t SMALL = (size_t)(2 * NW * DK + DK + C) * 4;  // sums, offsets, exp(gamma/2), beta
+    static constexpr size_t MATF = (size_t)C * PT * 4;                   // A, then T in place
+    static constexpr size_t KMB = (size_t)C * DK * sizeof(T);            // Km (Gram operand)
+    static constexpr size_t OPB = (size_t)PW * C * sizeof(T);            // B operand of one W / U~ pass
+    static constexpr size_t REGION = mx(mx(KMB, MATF), OPB);
     static constexpr size_t SMEM = SMALL + REGION;
 };
-
-__device__ __forceinline__ float clamp85(float x) { return fminf(fmaxf(x, -85.f), 85.f); }
-
-template <typename T, int NT>
-__device__ __forceinline__ void copy_out(T *dst, const T *src, int n) {
-    typedef typename Frag<T>::Vec V;
-    for (int i = threadIdx.x; i < n / Frag<T>::EPL; i += NT)
-        reinterpret_cast<V *>(dst)[i] = reinterpret_cast<const V *>(src)[i];
-}
 
 // This lane's operand share of group kg of one row (the values at channels
 // frag_chan<T>(kg, hi, 0..EPL-1)), from a row in global memory: runs of 4
@@ -122,25 +114,54 @@ __device__ __forceinline__ typename Frag<T>::Vec a_frag_f32(const float *M, int 
     return v;
 }
 
+// The identity of tile t of a contraction group as a B operand: lane (n, hi) has a
+// one in the slot whose contraction index is 16 t + n. The product of a row group X
+// (16 rows x KG contraction indices) with it is the 16 x 16 accumulator tile
+// X[:, 16 t .. 16 t + 15], exactly (each entry is one product with 1).
+template <typename T> __device__ __forceinline__ typename Frag<T>::Vec ident_op(int t) {
+    const int l = threadIdx.x & 63, n = l & 15, hi = l >> 4;
+    typename Frag<T>::Vec v;
+#pragma unroll
+    for (int j = 0; j < Frag<T>::EPL; ++j) v[j] = from_f32<T>(frag_chan<T>(0, hi, j) == 16 * t + n ? 1.f : 0.f);
+    return v;
+}
+
+// Accumulator tile acc (lane n + 16 hi holds its entries (4 hi + i, n)) stored
+// transposed into the fragment-ordered [R][K] matrix at base: entry (4 hi + i, n)
+// becomes row 16 rb + n, contraction index 16 kb + 4 hi + i. Those are four
+// consecutive slots of the same lane: one 8-byte (bf16) or 16-byte (fp32) store.
+template <typename T>
+__device__ __forceinline__ void store_tile_t(T *base, int R, int kb, int rb, f32x4 acc) {
+    constexpr int WPG = Frag<T>::KG / 16;
+    const int l = threadIdx.x & 63;
+    T *p = base + (((kb / WPG) * (R >> 4) + rb) * 64 + l) * Frag<T>::EPL + 4 * (kb % WPG);
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<b4 *>(p) = __builtin_convertvector(acc, b4);
+    } else {
+        *reinterpret_cast<f32x4 *>(p) = acc;
+    }
+}
+
 template <int C, int DK, int DV, typename T>
 __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     typedef PrepCfg<C, DK, DV, T> P;
     typedef Frag<T> F;
     typedef typename F::Vec V;
     constexpr int NW = P::NW, NT = P::NT, NKG = P::NKG, NVG = P::NVG, PT = P::PT, PW = P::PW;
-    constexpr int EPL = F::EPL;
+    constexpr int EPL = F::EPL, KG = F::KG, TPG = KG / 16;  // 16-column tiles per contraction group
+    constexpr float kL2E = 1.4426950408889634f;             // exponents in base 2
+    constexpr float kClamp = 85.f * kL2E;                    // |exponent| limit of the Gram factors
 
     extern __shared__ __align__(16) unsigned char smem[];
     float *tot = reinterpret_cast<float *>(smem);  // [NW][DK] per-wave sums of log alpha
-    float *bet = tot + NW * DK;                     // [C] beta per chunk row
+    float *off = tot + NW * DK;                     // [NW][DK] (sum before row block w - gamma/2) log2(e)
+    float *eh = off + NW * DK;                      // [DK] exp(gamma / 2)
+    float *bet = eh + DK;                           // [C] beta per chunk row
     unsigned char *R = smem + P::SMALL;
-    T *Km = reinterpret_cast<T *>(R);                            // [C][DK] frag order: k exp(m - g)
-    T *KtS = Km + C * DK;                                        // [DK][C] frag order: KtT staging
-    T *Aqs = reinterpret_cast<T *>(R);                           // [C][C] frag order: Aqk staging
-    float *Tm = reinterpret_cast<float *>(R);                    // [C][PT]
-    float *Am = Tm + C * PT;                                     // [C][PT]
-    T *OpB = reinterpret_cast<T *>(R + P::MATF);                 // [PW][C] frag order: B operand
-    T *Wst = OpB + PW * C;                                       // [C][PW] frag order: W staging
+    T *Km = reinterpret_cast<T *>(R);               // [C][DK] frag order: k exp(m - g)  (Gram)
+    float *Am = reinterpret_cast<float *>(R);       // [C][PT] A, then T = (I + A)^{-1} in place
+    T *OpB = reinterpret_cast<T *>(R);              // [PW][C] frag order: B operand of a W / U~ pass
 
     const int j = blockIdx.x, h = blockIdx.y;
     int s, t0, L;
@@ -153,9 +174,10 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     const size_t tok = (size_t)(t0 + (valid ? r : 0)) * H + h;
     const size_t jh = (size_t)j * H + h;
     const float scale = a.scale;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // ---- 0. this lane's row of k, q and log alpha, in matrix-core operand order
-    V kr[NKG], qr[NKG];
+    // ---- 0. this lane's row of k, q, v and log alpha, in matrix-core operand order
+    V kr[NKG], qr[NKG], vr[NVG];
     float g[NKG][EPL];
     float b = 0.f;
 #pragma unroll
@@ -173,96 +195,6 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             }
         }
     }
-    if (valid) b = a.beta[tok];
-    if (hi == 0) bet[r] = b;
-
-    // ---- 1. inclusive running sum of log alpha down the chunk: within the
-    //         wave's 16 rows by a DPP scan, then across waves through LDS (sums
-    //         taken in wave order, so the last row's g equals gamma exactly)
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            g[kg][e] = row16_inclusive_sum(g[kg][e]);
-            if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
-        }
-    __syncthreads();
-    float gam[NKG][EPL];
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float off = 0.f, all = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float x = tot[ww * DK + frag_chan<T>(kg, hi, e)];
-                if (ww < w) off += x;
-                all += x;
-            }
-            g[kg][e] += off;
-            gam[kg][e] = all;
-        }
-
-    // ---- 2. QO = scale q exp(g) straight to memory (this lane's fragment slot);
-    //         Gram factors: k exp(g - m), scale q exp(g - m) stay in registers,
-    //         k exp(m - g) goes to LDS for the other waves; KtT = (k exp(gamma - g))^T
-    //         is staged (transposed) in LDS
-    T *gQO = static_cast<T *>(a.buf.QO) + jh * C * DK;
-    V kp[NKG], qp[NKG];
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg) {
-        float xo[EPL], xp[EPL], xq[EPL], xm[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
-            const float x = g[kg][e], m = 0.5f * gam[kg][e];
-            const float ep = __expf(clamp85(x - m)), em = __expf(clamp85(m - x));
-            xo[e] = qv * __expf(x);
-            xp[e] = kv * ep;
-            xq[e] = qv * ep;
-            xm[e] = kv * em;
-            KtS[frag_off<T>(frag_chan<T>(kg, hi, e), r, DK)] = from_f32<T>(kv * __expf(gam[kg][e] - x));
-        }
-        *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
-        kp[kg] = pack_frag<T>(xp);
-        qp[kg] = pack_frag<T>(xq);
-        *reinterpret_cast<V *>(Km + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xm);
-    }
-    __syncthreads();
-    copy_out<T, NT>(static_cast<T *>(a.buf.KtT) + jh * DK * C, KtS, DK * C);
-
-    // ---- 3. decayed Gram tiles of this wave's row block: (w, tj) for tj <= w
-    f32x4 akk[NW], aqk[NW];
-#pragma unroll
-    for (int tj = 0; tj < NW; ++tj) {
-        akk[tj] = aqk[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tj <= w) {
-#pragma unroll
-            for (int kg = 0; kg < NKG; ++kg) {
-                const V bm = frag_load<T>(Km, kg, tj, C);
-                akk[tj] = F::mma(akk[tj], kp[kg], bm);
-                aqk[tj] = F::mma(aqk[tj], qp[kg], bm);
-            }
-        }
-    }
-    __syncthreads();  // Km and KtT staging are free again
-
-    // ---- 4. A (strictly lower, rows scaled by beta) -> fp32 LDS;
-    //         Aqk (lower, diagonal included; zero above) -> memory
-#pragma unroll
-    for (int tj = 0; tj < NW; ++tj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * w + acc_row(i), cc = 16 * tj + acc_col();
-            if (tj <= w) Am[rr * PT + cc] = (cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
-            Aqs[frag_off<T>(rr, cc, C)] = from_f32<T>((cc <= rr) ? aqk[tj][i] : 0.f);
-        }
-    __syncthreads();
-    copy_out<T, NT>(static_cast<T *>(a.buf.Aqk) + jh * C * C, Aqs, C * C);
-    __syncthreads();
-
-    // ---- 5. T = (I + A)^{-1}, with this lane's row of v in flight meanwhile
-    V vr[NVG];
 #pragma unroll
     for (int kg = 0; kg < NVG; ++kg) {
         if (valid) {
@@ -272,42 +204,161 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
         }
     }
-    unit_lower_inverse<C, PT, T, NT>(Am, Tm);
+    if (valid) b = a.beta[tok];
+    if (hi == 0) bet[r] = b;
+
+    // ---- 1. inclusive running sum of log alpha within the wave's 16 rows (DPP scan);
+    //         the row blocks' sums to LDS
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            g[kg][e] = row16_inclusive_sum(g[kg][e]);
+            if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
+        }
+    __syncthreads();
+
+    // ---- 2. per key channel (one thread each): each row block's offset, summed in
+    //         row-block order, less gamma / 2 (in base 2); exp(gamma / 2) to LDS and
+    //         exp(gamma) to memory
+    if (tid < DK) {
+        float pre[NW], acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            pre[ww] = acc;
+            acc += tot[ww * DK + tid];
+        }
+        const float m = 0.5f * acc;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) off[ww * DK + tid] = (pre[ww] - m) * kL2E;
+        eh[tid] = __builtin_amdgcn_exp2f(m * kL2E);
+        a.buf.eg[jh * DK + tid] = __builtin_amdgcn_exp2f(acc * kL2E);
+    }
+    __syncthreads();
+
+    // ---- 3. elementwise, with d = (g - gamma/2) log2(e) clamped, ep = 2^d, em = 2^-d
+    //         and E = exp(gamma/2): the Gram factors Kp = k ep and Qp = scale q ep
+    //         (registers) and Km = k em (LDS); QO = Qp E (memory); KtT = (Km E)^T,
+    //         transposed by the matrix cores (memory); and the rows beta Kp E of W's
+    //         operand (registers). Within the supported decay (|gamma| <= 170) no factor
+    //         is clamped, so Qp E = scale q exp(g) and Km E = k exp(gamma - g).
+    T *gQO = static_cast<T *>(a.buf.QO) + jh * C * DK;
+    T *gKtT = static_cast<T *>(a.buf.KtT) + jh * DK * C;
+    V idt[TPG];
+#pragma unroll
+    for (int t = 0; t < TPG; ++t) idt[t] = ident_op<T>(t);
+    V kp[NKG], qp[NKG], kb[NKG];
+#pragma unroll
+    for (int kg = 0; kg < NKG; ++kg) {
+        float xo[EPL], xp[EPL], xq[EPL], xm[EPL], xk[EPL], xb[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int ch = frag_chan<T>(kg, hi, e);
+            const float d = __builtin_amdgcn_fmed3f(fmaf(g[kg][e], kL2E, off[w * DK + ch]), -kClamp, kClamp);
+            const float ep = __builtin_amdgcn_exp2f(d), em = __builtin_amdgcn_exp2f(-d), E = eh[ch];
+            const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
+            xp[e] = kv * ep;
+            xq[e] = qv * ep;
+            xm[e] = kv * em;
+            xo[e] = xq[e] * E;
+            xk[e] = xm[e] * E;
+            xb[e] = b * xp[e] * E;
+        }
+        *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
+        kp[kg] = pack_frag<T>(xp);
+        qp[kg] = pack_frag<T>(xq);
+        kb[kg] = pack_frag<T>(xb);
+        *reinterpret_cast<V *>(Km + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xm);
+        const V kk = pack_frag<T>(xk);
+#pragma unroll
+        for (int t = 0; t < TPG; ++t) store_tile_t<T>(gKtT, DK, w, TPG * kg + t, F::mma(zero4, kk, idt[t]));
+    }
+    __syncthreads();  // Km complete
+
+    // ---- 4. decayed Gram tiles of this wave's row block: A's tiles (w, tj <= w), and,
+    //         with the operands' roles swapped, the tiles of Aqk^T = Km Qp^T, whose
+    //         entries are Aqk's operand slots (stored to memory, zero above the diagonal)
+    T *gAqk = static_cast<T *>(a.buf.Aqk) + jh * C * C;
+    f32x4 akk[NW];
+#pragma unroll
+    for (int tj = 0; tj < NW; ++tj) {
+        akk[tj] = zero4;
+        f32x4 aq = zero4;
+        if (tj <= w) {
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg) {
+                const V bm = frag_load<T>(Km, kg, tj, C);
+                akk[tj] = F::mma(akk[tj], kp[kg], bm);
+                aq = F::mma(aq, bm, qp[kg]);
+            }
+            if (tj == w) {  // entry (4 hi + i, lr) is Aqk[16 w + lr][16 w + 4 hi + i]: kept for i <= r
+#pragma unroll
+                for (int i = 0; i < 4; ++i) aq[i] = (4 * hi + i <= lr) ? aq[i] : 0.f;
+            }
+        }
+        store_tile_t<T>(gAqk, C, tj, w, aq);
+    }
+    __syncthreads();  // Km is no longer read: the region takes A
+    // A (strictly lower, rows scaled by beta, zero elsewhere) -> fp32 LDS
+#pragma unroll
+    for (int tj = 0; tj < NW; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * w + acc_row(i), cc = 16 * tj + acc_col();
+            Am[rr * PT + cc] = (tj <= w && cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
+        }
+    __syncthreads();
+
+    // ---- 5. T = (I + A)^{-1}, in place
+    unit_lower_inverse<C, PT, T, NT>(Am);
 
     // ---- 6. W = T (beta k exp(g)) and U~ = T (beta v), PW output columns per pass
-    constexpr int NCG = C / F::KG;
-    const int kgmax = ((w + 1) * 16 + F::KG - 1) / F::KG;  // T is lower triangular
+    constexpr int NCG = C / KG;
+    const int kgmax = ((w + 1) * 16 + KG - 1) / KG;  // T is lower triangular
     V tf[NCG];
 #pragma unroll
     for (int kg = 0; kg < NCG; ++kg)
-        if (kg < kgmax) tf[kg] = a_frag_f32<T>(Tm, PT, 16 * w, kg);
+        if (kg < kgmax) tf[kg] = a_frag_f32<T>(Am, PT, 16 * w, kg);
+    __syncthreads();  // T is in registers: the region takes the B operands
     T *gW = static_cast<T *>(a.buf.W) + jh * C * DK;
     T *gU = static_cast<T *>(a.buf.U) + jh * C * DV;
     // one pass: output columns [c0, c0 + width) of W (isW) or of U~
     auto pass = [&](bool isW, int c0, int width) {
-        // B operand [width][C]: (beta k exp(g))^T or (beta v)^T, from this lane's row
+        // B operand [width][C]: this wave's rows of beta k exp(g) (W) or beta v (U~),
+        // transposed by the matrix cores
 #pragma unroll
-        for (int kg = 0; kg < (isW ? NKG : NVG); ++kg)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const int ch = frag_chan<T>(kg, hi, e);
-                if (ch >= c0 && ch < c0 + width) {
-                    const float val = isW ? b * to_f32(kr[kg][e]) * __expf(g[kg][e]) : b * to_f32(vr[kg][e]);
-                    OpB[frag_off<T>(ch - c0, r, width)] = from_f32<T>(val);
-                }
-            }
-        __syncthreads();
-        for (int tn = 0; tn < width / 16; ++tn) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kg = 0; kg < NCG; ++kg)
-                if (kg < kgmax) acc = F::mma(acc, tf[kg], frag_load<T>(OpB, kg, tn, width));
+        for (int kg = 0; kg < (isW ? NKG : NVG); ++kg) {
+            V x;
             if (isW) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Wst[frag_off<T>(16 * w + acc_row(i), 16 * tn + acc_col(), C)] = from_f32<T>(acc[i]);
+                x = kb[kg];
             } else {
-                T *dst = gU + acc_tile_off(w, (c0 >> 4) + tn, DV);
+                float xv[EPL];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) xv[e] = b * to_f32(vr[kg][e]);
+                x = pack_frag<T>(xv);
+            }
+#pragma unroll
+            for (int t = 0; t < TPG; ++t) {
+                const int cb = TPG * kg + t;
+                if (16 * cb >= c0 && 16 * cb < c0 + width)
+                    store_tile_t<T>(OpB, width, w, cb - c0 / 16, F::mma(zero4, x, idt[t]));
+            }
+        }
+        __syncthreads();
+        for (int tc = 0; tc < width / 16; ++tc) {
+            f32x4 acc = zero4;
+            if (isW) {
+                // W^T's tile (columns c0 + 16 tc .., rows 16 w ..), from the operands with
+                // their roles swapped: its entries are W's operand slots
+#pragma unroll
+                for (int kg = 0; kg < NCG; ++kg)
+                    if (kg < kgmax) acc = F::mma(acc, frag_load<T>(OpB, kg, tc, width), tf[kg]);
+                store_tile_t<T>(gW, C, c0 / 16 + tc, w, acc);
+            } else {
+#pragma unroll
+                for (int kg = 0; kg < NCG; ++kg)
+                    if (kg < kgmax) acc = F::mma(acc, tf[kg], frag_load<T>(OpB, kg, tc, width));
+                T *dst = gU + acc_tile_off(w, (c0 >> 4) + tc, DV);
                 if constexpr (sizeof(T) == 2) {
                     bf16 x[4];
 #pragma unroll
@@ -319,22 +370,12 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             }
         }
         __syncthreads();
-        if (isW) {
-            copy_out<T, NT>(gW + c0 * C, Wst, C * width);
-            __syncthreads();
-        }
     };
     constexpr int PWK = DK < PW ? DK : PW, PWV = DV < PW ? DV : PW;
 #pragma unroll
     for (int p = 0; p < DK / PWK; ++p) pass(true, p * PWK, PWK);
 #pragma unroll
     for (int p = 0; p < DV / PWV; ++p) pass(false, p * PWV, PWV);
-    if (w == 0 && lr == 0) {
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) a.buf.eg[jh * DK + frag_chan<T>(kg, hi, e)] = __expf(gam[kg][e]);
-    }
 }
 
 template <int C, int DK, int DV, typename T>

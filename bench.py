@@ -47,12 +47,12 @@ def log(*a):
 # figure is used only while these files are byte-identical to when the
 # counters were taken.
 CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
-COMMON_SRC = ["kda_device.hpp", "kda_internal.hpp", "kda_solve.hpp"]
+COMMON_SRC = ["kda_device.hpp", "kda_internal.hpp"]  # included by every kernel source
 PATHS = {
     "fused": dict(kernel="kda_fused_kernel", sources=["kda_fused.hip"] + COMMON_SRC,
                   traffic="kda_fused_kernel_batched_prefill_traffic.md"),
     "split": dict(kernel="kda_prep_kernel + kda_state_kernel",
-                  sources=["kda_prep.hip", "kda_state.hip"] + COMMON_SRC,
+                  sources=["kda_prep.hip", "kda_state.hip", "kda_solve.hpp"] + COMMON_SRC,
                   traffic="kda_split_pass_batched_prefill_traffic.md"),
 }
 

@@ -5,4 +5,5 @@ The computation runs in hand-written HIP kernels behind a C ABI
 thin Python binding over it.
 """
 from .binding import (KdaError, abi_version, chunk_fwd, load, recurrent_step,  # noqa: F401
-                      workspace_bytes, LIB_PATH, EXPORTS, KDA_F32, KDA_BF16)
+                      workspace_bytes, LIB_PATH, EXPORTS, KDA_F32, KDA_BF16, KDA_GATE_CHANNEL,
+                      KDA_GATE_HEAD, KDA_GATE_NONE)

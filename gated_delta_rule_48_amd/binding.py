@@ -16,10 +16,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
-           "kda_chunk_fwd", "kda_recurrent_step")
+           "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_step", "kda_recurrent_step_gated")
+ABI_VERSION = 2
 
 
 class KdaError(RuntimeError):
@@ -49,8 +51,15 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_workspace_bytes.restype = Z
     lib.kda_chunk_fwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, I, P, P, P, Z, P]
     lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd_gated.argtypes = [I] + lib.kda_chunk_fwd.argtypes
+    lib.kda_chunk_fwd_gated.restype = I
     lib.kda_recurrent_step.argtypes = [I, I, I, I, I, P, P, P, P, P, F, P, P, P]
     lib.kda_recurrent_step.restype = I
+    lib.kda_recurrent_step_gated.argtypes = [I] + lib.kda_recurrent_step.argtypes
+    lib.kda_recurrent_step_gated.restype = I
+    if lib.kda_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libkda.so has ABI {lib.kda_abi_version()}, this binding expects {ABI_VERSION}; "
+                           "rebuild it")
     _lib = lib
     return lib
 
@@ -83,6 +92,19 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _gate(log_alpha, lead, H, dk, dev) -> int:
+    """The decay granularity that log_alpha's shape selects (kda_gate), after checking it:
+    [.., H, dk] one decay per key channel, [.., H] one per token and head, None no decay."""
+    import torch
+    if log_alpha is None:
+        return KDA_GATE_NONE
+    if log_alpha.dim() == len(lead) + 2:
+        _check(log_alpha, "log_alpha", torch.float32, lead + (H, dk), dev)
+        return KDA_GATE_CHANNEL
+    _check(log_alpha, "log_alpha", torch.float32, lead + (H,), dev)
+    return KDA_GATE_HEAD
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -97,10 +119,12 @@ def workspace_bytes(B, T, H, dk, dv, chunk, n_seqs, io) -> int:
 def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, cu_seqlens=None,
               chunk: int = 64, output_final_state: bool = True, o=None, hT=None, workspace=None,
               stream=None):
-    """Chunked KDA forward (kda_chunk_fwd).
+    """Chunked KDA forward (kda_chunk_fwd_gated).
 
     q, k [B, T, H, dk] (or packed [T, H, dk] with cu_seqlens); v [.., H, dv];
-    log_alpha [.., H, dk] fp32; beta [.., H] fp32; h0 [n_seq, H, dk, dv] fp32 or None;
+    log_alpha fp32 [.., H, dk] (a decay per key channel), [.., H] (one per token and
+    head, Gated DeltaNet) or None (no decay, DeltaNet); beta [.., H] fp32;
+    h0 [n_seq, H, dk, dv] fp32 or None;
     cu_seqlens int32 [n_seqs + 1] on the device, or None. Returns (o, hT); hT is
     None when output_final_state is False.
     """
@@ -125,7 +149,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, 
     _check(q, "q", q.dtype, lead + (H, dk), dev)
     _check(k, "k", q.dtype, lead + (H, dk), dev)
     _check(v, "v", q.dtype, lead + (H, dv), dev)
-    _check(log_alpha, "log_alpha", torch.float32, lead + (H, dk), dev)
+    gate = _gate(log_alpha, lead, H, dk, dev)
     _check(beta, "beta", torch.float32, lead + (H,), dev)
     if h0 is not None:
         _check(h0, "h0", torch.float32, (n_seqs, H, dk, dv), dev)
@@ -143,20 +167,20 @@ def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if scale is None:
         scale = dk ** -0.5
-    st = lib.kda_chunk_fwd(B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                           _ptr(beta), float(scale), _ptr(h0), _ptr(cu_seqlens),
-                           n_seqs if cu_seqlens is not None else 0, _ptr(o), _ptr(hT),
-                           _ptr(workspace), ws_bytes, _stream(stream))
+    st = lib.kda_chunk_fwd_gated(gate, B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                 _ptr(beta), float(scale), _ptr(h0), _ptr(cu_seqlens),
+                                 n_seqs if cu_seqlens is not None else 0, _ptr(o), _ptr(hT),
+                                 _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
-        raise KdaError(st, "kda_chunk_fwd")
+        raise KdaError(st, "kda_chunk_fwd_gated")
     return o, hT
 
 
 def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = None, o=None,
                    stream=None):
-    """One decode step (kda_recurrent_step): q, k [N, H, dk]; v [N, H, dv];
-    log_alpha [N, H, dk] fp32; beta [N, H] fp32; state [N, H, dk, dv] fp32,
-    updated in place. Returns o [N, H, dv]."""
+    """One decode step (kda_recurrent_step_gated): q, k [N, H, dk]; v [N, H, dv];
+    log_alpha fp32 [N, H, dk], [N, H] or None (as in chunk_fwd); beta [N, H] fp32;
+    state [N, H, dk, dv] fp32, updated in place. Returns o [N, H, dv]."""
     import torch
     lib = load()
     dev = q.device
@@ -165,7 +189,7 @@ def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = Non
     dv = v.shape[-1]
     _check(k, "k", q.dtype, (N, H, dk), dev)
     _check(v, "v", q.dtype, (N, H, dv), dev)
-    _check(log_alpha, "log_alpha", torch.float32, (N, H, dk), dev)
+    gate = _gate(log_alpha, (N,), H, dk, dev)
     _check(beta, "beta", torch.float32, (N, H), dev)
     _check(state, "state", torch.float32, (N, H, dk, dv), dev)
     if o is None:
@@ -173,8 +197,8 @@ def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = Non
     _check(o, "o", q.dtype, (N, H, dv), dev)
     if scale is None:
         scale = dk ** -0.5
-    st = lib.kda_recurrent_step(N, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                                _ptr(beta), float(scale), _ptr(state), _ptr(o), _stream(stream))
+    st = lib.kda_recurrent_step_gated(gate, N, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                      _ptr(beta), float(scale), _ptr(state), _ptr(o), _stream(stream))
     if st != 0:
-        raise KdaError(st, "kda_recurrent_step")
+        raise KdaError(st, "kda_recurrent_step_gated")
     return o

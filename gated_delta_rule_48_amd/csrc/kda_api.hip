@@ -9,6 +9,10 @@
 
 #define KDA_EXPORT extern "C" __attribute__((visibility("default")))
 
+static_assert(KDA_GATE_CHANNEL == kda::kGateChannel && KDA_GATE_HEAD == kda::kGateHead &&
+                  KDA_GATE_NONE == kda::kGateNone,
+              "gate kinds of the ABI and the kernels");
+
 namespace {
 
 using kda::ChunkBuffers;
@@ -115,12 +119,13 @@ KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, in
     return L.total;
 }
 
-KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
-                             const void *q, const void *k, const void *v,
-                             const float *log_alpha, const float *beta, float scale,
-                             const float *h0, const int32_t *cu_seqlens, int n_seqs,
-                             void *o, float *hT, void *workspace, size_t workspace_bytes,
-                             void *stream) {
+KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                                   const void *q, const void *k, const void *v,
+                                   const float *log_alpha, const float *beta, float scale,
+                                   const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                                   void *o, float *hT, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
     const bool varlen = cu_seqlens != nullptr;
     kda_status st = check_sizes(B, T, H, d_k, d_v, chunk, io, varlen, n_seqs);
     if (st != KDA_OK) return st;
@@ -129,16 +134,20 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     const size_t tokens = (size_t)B * T;
     const size_t esz = io == KDA_BF16 ? 2 : 4;
     if (tokens > 0) {
-        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
-        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-            !aligned(log_alpha, 16) || !aligned(beta, 4))
+        if (!q || !k || !v || !beta || !o) return KDA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4))
             return KDA_ERR_INVALID_ARG;
         const size_t ob = tokens * H * d_v * esz;
         if (overlaps(o, ob, q, tokens * H * d_k * esz) || overlaps(o, ob, k, tokens * H * d_k * esz) ||
-            overlaps(o, ob, v, ob) || overlaps(o, ob, log_alpha, tokens * H * d_k * 4) ||
-            overlaps(o, ob, beta, tokens * H * 4))
+            overlaps(o, ob, v, ob) || overlaps(o, ob, beta, tokens * H * 4))
             return KDA_ERR_INVALID_ARG;
+        if (gate != KDA_GATE_NONE) {
+            const size_t gb = tokens * H * (gate == KDA_GATE_CHANNEL ? (size_t)d_k : 1) * 4;
+            if (!log_alpha || !aligned(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4) || overlaps(o, ob, log_alpha, gb))
+                return KDA_ERR_INVALID_ARG;
+        }
     }
+    if (gate == KDA_GATE_NONE) log_alpha = nullptr;  // never read
     if ((h0 && !aligned(h0, 16)) || (hT && !aligned(hT, 16))) return KDA_ERR_INVALID_ARG;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
 
@@ -151,7 +160,7 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     char *ws = static_cast<char *>(workspace);
     const bool bf = io == KDA_BF16;
     if (use_fused(B, T, H, d_k, d_v, chunk, varlen, io)) {
-        kda::FusedArgs fa{q, k, v, log_alpha, beta, scale, h0, hT, o, ws + L.discard, H, T};
+        kda::FusedArgs fa{q, k, v, log_alpha, beta, scale, h0, hT, o, ws + L.discard, H, T, gate};
         return kda::launch_fused(fa, d_k, d_v, bf, B, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     ChunkBuffers buf{};
@@ -179,7 +188,7 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     }
 
     if (tokens > 0) {
-        kda::PrepArgs pa{q, k, v, log_alpha, beta, scale, H, map, buf};
+        kda::PrepArgs pa{q, k, v, log_alpha, beta, scale, H, gate, map, buf};
         if (kda::launch_prep(pa, chunk, d_k, d_v, bf, (int)L.n_chunks, hs) != hipSuccess)
             return KDA_ERR_HIP;
     }
@@ -188,25 +197,47 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     return KDA_OK;
 }
 
-KDA_EXPORT int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,
-                                  const void *q, const void *k, const void *v,
-                                  const float *log_alpha, const float *beta, float scale,
-                                  float *state, void *o, void *stream) {
+KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                             const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, float scale,
+                             const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                             void *o, float *hT, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    return kda_chunk_fwd_gated(KDA_GATE_CHANNEL, B, T, H, d_k, d_v, chunk, io, q, k, v, log_alpha, beta, scale,
+                               h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes, stream);
+}
+
+KDA_EXPORT int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v, int io,
+                                        const void *q, const void *k, const void *v,
+                                        const float *log_alpha, const float *beta, float scale,
+                                        float *state, void *o, void *stream) {
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
     if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H < 1) return KDA_ERR_INVALID_ARG;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(log_alpha, 16) || !aligned(beta, 4) || !aligned(state, 16))
+    if (!q || !k || !v || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4) ||
+        !aligned(state, 16))
         return KDA_ERR_INVALID_ARG;
+    if (gate != KDA_GATE_NONE && (!log_alpha || !aligned(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4)))
+        return KDA_ERR_INVALID_ARG;
+    if (gate == KDA_GATE_NONE) log_alpha = nullptr;  // never read
     const size_t nh = (size_t)N * H, esz = io == KDA_BF16 ? 2 : 4;
     if (overlaps(o, nh * d_v * esz, state, nh * d_k * d_v * 4)) return KDA_ERR_INVALID_ARG;
-    kda::DecodeArgs da{q, k, v, log_alpha, beta, scale, state, o, (int)nh};
+    kda::DecodeArgs da{q, k, v, log_alpha, beta, scale, state, o, (int)nh, gate};
     if (kda::launch_decode(da, d_k, d_v, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+KDA_EXPORT int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,
+                                  const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta, float scale,
+                                  float *state, void *o, void *stream) {
+    return kda_recurrent_step_gated(KDA_GATE_CHANNEL, N, H, d_k, d_v, io, q, k, v, log_alpha, beta, scale,
+                                    state, o, stream);
 }

@@ -55,7 +55,9 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
         const float kv = to_f32(k[tid]), qv = to_f32(q[tid]);
         ks[tid] = kv;
         qs[tid] = qv;
-        al[tid] = __expf(a.log_alpha[(size_t)nh * DK + tid]);
+        al[tid] = a.gate == kGateChannel ? __expf(a.log_alpha[(size_t)nh * DK + tid])
+                  : a.gate == kGateHead  ? __expf(a.log_alpha[nh])
+                                         : 1.f;
         kq = kv * qv;
     }
     f32x4 vv;

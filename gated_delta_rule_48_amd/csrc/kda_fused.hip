@@ -190,6 +190,7 @@ __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb 
     (void)hi;                                                                  \
     (void)r;
 
+template <int G>
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     bf16 *Qp = reinterpret_cast<bf16 *>(smem + Lds::QP);
@@ -275,16 +276,24 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         const int ln = opaque_lane();
         const size_t t0b = tok0_of(ci);
         const unsigned ro = row_off(ci, ln);
-        const float *gp = a.log_alpha + t0b * kDK + ro * kDK;
+        if constexpr (G == kGateChannel) {
+            const float *gp = a.log_alpha + t0b * kDK + ro * kDK;
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + 32 * (2 * hf + x) + 8 * (ln >> 4));
-            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 32 * (2 * hf + x) + 8 * (ln >> 4) + 4);
+            for (int x = 0; x < 2; ++x) {
+                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp + 32 * (2 * hf + x) + 8 * (ln >> 4));
+                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 32 * (2 * hf + x) + 8 * (ln >> 4) + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                gl[x][e] = g0[e];
-                gl[x][4 + e] = g1[e];
+                for (int e = 0; e < 4; ++e) {
+                    gl[x][e] = g0[e];
+                    gl[x][4 + e] = g1[e];
+                }
             }
+        } else {  // one decay for every channel of the row (log_alpha [T, H]), or none
+            const float gv = G == kGateHead ? a.log_alpha[t0b + ro] : 0.f;
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gl[x][e] = gv;
         }
         bta = a.beta[t0b + ro];
     };
@@ -730,7 +739,9 @@ hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seq
     // the fused pass is built for bf16 input and d_k = d_v = 128 only
     if (!bf16 || dk != kDK || dv != kDV) return hipErrorInvalidValue;
     constexpr size_t smem = Lds::SIZE;
-    auto kern = kda_fused_kernel;
+    auto kern = a.gate == kGateHead ? kda_fused_kernel<kGateHead>
+                : a.gate == kGateNone ? kda_fused_kernel<kGateNone>
+                                      : kda_fused_kernel<kGateChannel>;
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess) return err;

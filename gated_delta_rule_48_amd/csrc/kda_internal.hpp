@@ -9,6 +9,10 @@
 
 namespace kda {
 
+// Decay granularity of log_alpha (the kda_gate values of kda.h): one decay per key
+// channel, one per token and head, or none.
+constexpr int kGateChannel = 0, kGateHead = 1, kGateNone = 2;
+
 // Per-chunk quantities produced by the chunk-preparation kernel and consumed by
 // the state/output kernel. All are indexed chunk-major: [chunk j][head h][...],
 // where j runs over the chunks of all sequences in order.
@@ -26,6 +30,7 @@ struct PrepArgs {
     const float *log_alpha, *beta;
     float scale;
     int H;
+    int gate;  // kGateChannel: log_alpha [T, H, d_k]; kGateHead: [T, H]; kGateNone: not read
     SeqMap map;
     ChunkBuffers buf;
 };
@@ -51,6 +56,7 @@ struct FusedArgs {
     void *discard;  // absorbs stores of rows past a sequence end (256 bytes)
     int H;
     int seq_len;    // every sequence has seq_len tokens
+    int gate;       // as in PrepArgs
 };
 
 struct DecodeArgs {
@@ -59,7 +65,8 @@ struct DecodeArgs {
     float scale;
     float *state;
     void *o;
-    int NH;  // N * H
+    int NH;    // N * H
+    int gate;  // as in PrepArgs (log_alpha [N, H, d_k] or [N, H])
 };
 
 // Each returns hipSuccess or the launch error.

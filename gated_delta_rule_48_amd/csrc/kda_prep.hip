@@ -185,7 +185,13 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
         if (valid) {
             kr[kg] = load_row_frag<T>(static_cast<const T *>(a.k) + tok * DK, kg, hi);
             qr[kg] = load_row_frag<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
-            load_row_f32<T>(a.log_alpha + tok * DK, kg, hi, g[kg]);
+            if (a.gate == kGateChannel) {
+                load_row_f32<T>(a.log_alpha + tok * DK, kg, hi, g[kg]);
+            } else {  // one decay for every channel of the row, or none
+                const float x = a.gate == kGateHead ? a.log_alpha[tok] : 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) g[kg][e] = x;
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -61,6 +61,22 @@ typedef enum {
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Granularity of the decay, for the *_gated entry points. The essay "22,580:
+ * from GPT-2 to Kimi K3" (yichencityu.github.io) builds the method in steps:
+ * section 06, DeltaNet (the delta rule, no decay); section 08, Gated DeltaNet
+ * (one data-dependent decay alpha_t in (0, 1] that scales the whole previous
+ * state; alpha = 1 gives back the delta rule); section 9.1, KDA (a decay per
+ * key channel). The recurrence above covers all three: a per-head decay is
+ * the same alpha_t on every key channel, and none is alpha_t = 1.
+ */
+typedef enum {
+    KDA_GATE_CHANNEL = 0, /* log_alpha [T_total, H, d_k] fp32, 16-byte aligned (KDA) */
+    KDA_GATE_HEAD = 1,    /* log_alpha [T_total, H] fp32, 4-byte aligned: one decay per
+                             token and head (Gated DeltaNet) */
+    KDA_GATE_NONE = 2     /* no decay: log_alpha is not read and may be NULL (DeltaNet) */
+} kda_gate;
 
 /* KDA_ABI_VERSION of the built library. */
 int kda_abi_version(void);
@@ -122,6 +138,21 @@ int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
                   void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd_gated -- kda_chunk_fwd with the decay granularity `gate` (a
+ * kda_gate value; any other value is KDA_ERR_INVALID_ARG). log_alpha's shape and
+ * alignment follow kda_gate; with KDA_GATE_NONE it is not read. Every other
+ * argument, the workspace size and the error behaviour are those of
+ * kda_chunk_fwd, which is this call with KDA_GATE_CHANNEL. For a per-head decay
+ * the limit on a chunk's summed log_alpha applies to that one sum.
+ */
+int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                        const void *q, const void *k, const void *v,
+                        const float *log_alpha, const float *beta, float scale,
+                        const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                        void *o, float *hT, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
  * kda_recurrent_step -- one decode step ("recurrent program") for N sequences:
  * every (sequence, head) state is read once and written once, in place.
  *
@@ -140,6 +171,16 @@ int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,
                        const void *q, const void *k, const void *v,
                        const float *log_alpha, const float *beta, float scale,
                        float *state, void *o, void *stream);
+
+/*
+ * kda_recurrent_step_gated -- kda_recurrent_step with the decay granularity
+ * `gate`: log_alpha [N, H, d_k] (KDA_GATE_CHANNEL), [N, H] (KDA_GATE_HEAD), or not
+ * read (KDA_GATE_NONE). kda_recurrent_step is this call with KDA_GATE_CHANNEL.
+ */
+int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v, int io,
+                             const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, float scale,
+                             float *state, void *o, void *stream);
 
 #ifdef __cplusplus
 }

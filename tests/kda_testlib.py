@@ -38,21 +38,45 @@ def to_dev(x, io, dev="cuda"):
     return t
 
 
-def run_packed(x, io, chunk, varlen=True, B=None, T=None, h0=True, hT=True, dev="cuda"):
-    """Run kda_chunk_fwd on generator output. varlen=True passes cu_seqlens; else
-    the sequences must have equal length and are passed as [B, T, H, d]."""
+def gate_view(log_alpha, gate):
+    """The decays the library is given for a gate kind: all of them ("channel"),
+    channel 0's for every channel ("head": one per token and head), or none."""
+    if gate == "channel":
+        return log_alpha
+    if gate == "head":
+        return log_alpha[..., 0].contiguous()
+    return None
+
+
+def with_gate(x, gate):
+    """Generator output with its per-channel decays replaced by what a gate kind
+    means on every channel (the oracle's input): channel 0's decay broadcast
+    ("head"), or zero ("none")."""
+    y = dict(x)
+    if gate == "head":
+        y["log_alpha"] = np.repeat(x["log_alpha"][..., :1], x["log_alpha"].shape[-1], axis=-1).copy()
+    elif gate == "none":
+        y["log_alpha"] = np.zeros_like(x["log_alpha"])
+    return y
+
+
+def run_packed(x, io, chunk, varlen=True, B=None, T=None, h0=True, hT=True, dev="cuda", gate="channel"):
+    """Run kda_chunk_fwd_gated on generator output. varlen=True passes cu_seqlens; else
+    the sequences must have equal length and are passed as [B, T, H, d]. `gate`
+    selects which decays the library is given (gate_view)."""
     import torch
     import gated_delta_rule_48_amd as kda
     t = to_dev(x, io, dev)
     if varlen:
-        o, hT_ = kda.chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"],
+        o, hT_ = kda.chunk_fwd(t["q"], t["k"], t["v"], gate_view(t["log_alpha"], gate), t["beta"],
                                h0=t["h0"] if h0 else None, cu_seqlens=t["cu_seqlens"], chunk=chunk,
                                output_final_state=hT)
     else:
         Tt, H, dk = t["q"].shape
         dv = t["v"].shape[-1]
         r = lambda a, d: a.reshape(B, T, H, d)  # noqa: E731
-        o, hT_ = kda.chunk_fwd(r(t["q"], dk), r(t["k"], dk), r(t["v"], dv), r(t["log_alpha"], dk),
+        la = gate_view(r(t["log_alpha"], dk), gate)
+        o, hT_ = kda.chunk_fwd(r(t["q"], dk), r(t["k"], dk), r(t["v"], dv), la,
                                t["beta"].reshape(B, T, H), h0=t["h0"] if h0 else None, chunk=chunk,
                                output_final_state=hT)
         o = o.reshape(Tt, H, dv)

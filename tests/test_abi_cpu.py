@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing, misaligned or too small")]:
         assert lib.kda_status_string(code) == text
     assert lib.kda_status_string(99) == b"unknown status"
@@ -122,3 +122,43 @@ def step(lib, **kw):
 ])
 def test_recurrent_step_rejects(lib, kw, code):
     assert step(lib, **kw) == code
+
+
+def fwd_gated(lib, gate, **kw):
+    a = dict(B=2, T=100, H=4, dk=128, dv=128, chunk=64, io=BF16, q=A, k=A, v=A, la=A, beta=A,
+             scale=0.088, h0=None, cu=None, n_seqs=0, o=0x4000000, hT=None, ws=A, ws_bytes=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(gate, a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"],
+                                   a["k"], a["v"], a["la"], a["beta"], a["scale"], a["h0"], a["cu"],
+                                   a["n_seqs"], a["o"], a["hT"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("gate,kw,code", [
+    (3, {}, INVALID), (-1, {}, INVALID),              # not a kda_gate value
+    (0, dict(la=None), INVALID), (1, dict(la=None), INVALID),
+    (0, dict(la=A + 4), INVALID),                     # per-channel decays: 16-byte aligned
+    (1, dict(la=A + 2), INVALID),                     # per-head decays: 4-byte aligned
+    (1, dict(la=A + 4, ws=None), WORKSPACE),          # ... which A + 4 is: validation goes on to the workspace
+    (2, dict(la=None, ws=None), WORKSPACE),           # no decay: log_alpha is not needed
+    (2, dict(la=None, dk=96), UNSUPPORTED),
+])
+def test_chunk_fwd_gated_validation(lib, gate, kw, code):
+    assert fwd_gated(lib, gate, **kw) == code
+
+
+def test_chunk_fwd_is_the_per_channel_gated_call(lib):
+    for kw in (dict(dk=96), dict(la=A + 4), dict(ws=None), dict(la=None)):
+        assert fwd(lib, **kw) == fwd_gated(lib, 0, **kw)
+
+
+@pytest.mark.parametrize("gate,kw,code", [
+    (7, {}, INVALID), (0, dict(la=None), INVALID), (1, dict(la=None), INVALID), (1, dict(la=A + 2), INVALID),
+    (2, dict(la=None, dk=32), UNSUPPORTED), (2, dict(la=None, N=0), OK),
+])
+def test_recurrent_step_gated_validation(lib, gate, kw, code):
+    a = dict(N=4, H=2, dk=128, dv=128, io=BF16, q=A, k=A, v=A, la=A, beta=A, scale=0.088,
+             state=0x4000000, o=0x8000000, stream=None)
+    a.update(kw)
+    assert lib.kda_recurrent_step_gated(gate, a["N"], a["H"], a["dk"], a["dv"], a["io"], a["q"], a["k"], a["v"],
+                                        a["la"], a["beta"], a["scale"], a["state"], a["o"], a["stream"]) == code

@@ -10,16 +10,16 @@ import pytest
 
 import kda_synth
 import oracle
-from kda_testlib import TOL, gen, oracle_run, rel_l2, run_packed, say, to_dev
+from kda_testlib import TOL, gate_view, gen, oracle_run, rel_l2, run_packed, say, to_dev, with_gate
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(x, io, chunk, name, varlen=True, B=None, T=None, h0=True, tol=None):
+def _check(x, io, chunk, name, varlen=True, B=None, T=None, h0=True, tol=None, gate="channel"):
     tol = TOL[io] if tol is None else tol
-    say(f"[{name}] io={io} C={chunk} seqs={np.diff(x['cu_seqlens']).tolist()[:6]} "
+    say(f"[{name}] io={io} C={chunk} gate={gate} seqs={np.diff(x['cu_seqlens']).tolist()[:6]} "
         f"H={x['q'].shape[1]} dk={x['q'].shape[2]} dv={x['v'].shape[2]}")
-    o, hT = run_packed(x, io, chunk, varlen=varlen, B=B, T=T, h0=h0)
+    o, hT = run_packed(x, io, chunk, varlen=varlen, B=B, T=T, h0=h0, gate=gate)
     o_ref, h_ref, _ = oracle_run(x, h0=h0)
     eo, eh = rel_l2(o, o_ref), rel_l2(hT, h_ref)
     say(f"[{name}] rel_l2 o={eo:.2e} hT={eh:.2e}")
@@ -170,9 +170,11 @@ def test_deterministic():
 
 # ----------------------------------------------------------------------------- decode
 
-def _decode_steps(N, H, dk, dv, io, steps, seed, sample=None):
+def _decode_steps(N, H, dk, dv, io, steps, seed, sample=None, gate="channel"):
     """Run `steps` decode steps on the GPU; return per-step o of the sampled
-    (n, h) pairs, their final states, and the oracle's values for them."""
+    (n, h) pairs, their final states, and the oracle's values for them. `gate`
+    selects which decays the library is given (gate_view); the oracle reads what
+    they mean on every channel (with_gate)."""
     import torch
     import gated_delta_rule_48_amd as kda
     st0 = kda_synth.gen_decode_state(N, H, dk, dv, seed)
@@ -182,9 +184,9 @@ def _decode_steps(N, H, dk, dv, io, steps, seed, sample=None):
     hs = np.array([p[1] for p in sample])
     got, toks = [], []
     for step in range(steps):
-        y = kda_synth.gen_decode_step(N, H, dk, dv, io, "main", seed, step)
+        y = with_gate(kda_synth.gen_decode_step(N, H, dk, dv, io, "main", seed, step), gate)
         t = to_dev(dict(y, cu_seqlens=np.zeros(1, np.int32)), io)
-        o = kda.recurrent_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], state)
+        o = kda.recurrent_step(t["q"], t["k"], t["v"], gate_view(t["log_alpha"], gate), t["beta"], state)
         got.append(o.float().cpu().numpy()[ns, hs])
         toks.append({n: y[n][ns, hs] for n in ("q", "k", "v", "log_alpha", "beta")})
     torch.cuda.synchronize()
@@ -320,3 +322,40 @@ def test_fused_matches_split():
     for o, hT in ((of, hf), (os_, hs)):
         assert rel_l2(o, o_ref) <= TOL["bf16"] and rel_l2(hT, h_ref) <= TOL["bf16"]
     assert rel_l2(of, os_) <= 1e-2 and rel_l2(hf, hs) <= 1e-2
+
+
+# ----------------------------------------------------------------------------- gate kinds
+
+@pytest.mark.parametrize("gate", ["head", "none"])
+@pytest.mark.parametrize("io,path,chunk", [("f32", "split", 64), ("bf16", "split", 64), ("bf16", "split", 128),
+                                           ("bf16", "fused", 64)])
+def test_gate_kinds(gate, io, path, chunk):
+    """kda_chunk_fwd_gated with one decay per token and head (Gated DeltaNet) and with
+    none (DeltaNet): the oracle runs the same recurrence with that decay on every key
+    channel, or with log alpha = 0."""
+    seed = {"head": 101, "none": 102}[gate] + chunk
+    if path == "fused":
+        x = with_gate(gen([200, 200], 128, 128, 128, io, seed=seed), gate)
+        _check(x, io, chunk, f"{gate} fused", varlen=False, B=2, T=200, gate=gate)
+    else:
+        x = with_gate(gen([200, 130, 1], 4, 128, 128, io, seed=seed), gate)
+        _check(x, io, chunk, f"{gate} split", gate=gate)
+
+
+@pytest.mark.parametrize("path", ["split", "fused"])
+def test_head_gate_equals_broadcast_channel_gate(path):
+    """A per-head decay and the same decay given for every key channel: one arithmetic."""
+    x = with_gate(gen([150, 150], 128, 128, 128, "bf16", seed=111), "head")
+    kw = dict(varlen=False, B=2, T=150) if path == "fused" else dict(varlen=True)
+    oh, hh = run_packed(x, "bf16", 64, gate="head", **kw)
+    oc, hc = run_packed(x, "bf16", 64, gate="channel", **kw)
+    assert np.array_equal(oh, oc) and np.array_equal(hh, hc)
+
+
+@pytest.mark.parametrize("gate", ["head", "none"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_gate_kinds(gate, io):
+    o, st, o_ref, h_ref = _decode_steps(3, 4, 128, 128, io, 5, seed=7 + len(gate), gate=gate)
+    eo, eh = rel_l2(o, o_ref), rel_l2(st, h_ref)
+    say(f"[decode {gate} {io}] rel_l2 o={eo:.2e} state={eh:.2e}")
+    assert eo <= TOL[io] and eh <= TOL[io]

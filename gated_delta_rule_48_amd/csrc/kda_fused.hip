@@ -340,22 +340,30 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 for (int e = 0; e < 8; ++e) g[x][e] = valid ? g[x][e] : 0.f;
             bt = valid ? bt : 0.f;
         }
+        if constexpr (G == kGateChannel) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<1>(g[x][e]);
+                for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<1>(g[x][e]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<2>(g[x][e]);
+                for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<2>(g[x][e]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<4>(g[x][e]);
+                for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<4>(g[x][e]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<8>(g[x][e]);
+                for (int e = 0; e < 8; ++e) g[x][e] += dpp_row_shr<8>(g[x][e]);
+        } else if constexpr (G == kGateHead) {  // the row's one decay, for every slot
+            const float s0 = row16_inclusive_sum(g[0][0]);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[x][e] = s0;
+        }
         if (lr == 15) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -400,15 +408,31 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             const f32x4 om0 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c0);
             const f32x4 om1 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c4);
             float xp[8], xq[8], xm[8];
+            if constexpr (G == kGateChannel) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float om = e < 4 ? om0[e] : om1[e - 4];
-                const float d = __builtin_amdgcn_fmed3f(fmaf(g[x][e], kL2E, om), -kClamp, kClamp);
-                const float u = exp2_fast(d), ui = exp2_fast(-d);
-                const float kv = static_cast<float>(kr[x][e]);
-                xp[e] = kv * u;
-                xq[e] = static_cast<float>(qr[x][e]) * u;
-                xm[e] = kv * ui;
+                for (int e = 0; e < 8; ++e) {
+                    const float om = e < 4 ? om0[e] : om1[e - 4];
+                    const float d = __builtin_amdgcn_fmed3f(fmaf(g[x][e], kL2E, om), -kClamp, kClamp);
+                    const float u = exp2_fast(d), ui = exp2_fast(-d);
+                    const float kv = static_cast<float>(kr[x][e]);
+                    xp[e] = kv * u;
+                    xq[e] = static_cast<float>(qr[x][e]) * u;
+                    xm[e] = kv * ui;
+                }
+            } else {  // one factor pair for the whole row (none without decay)
+                float u = 1.f, ui = 1.f;
+                if constexpr (G == kGateHead) {
+                    const float d = __builtin_amdgcn_fmed3f(fmaf(g[0][0], kL2E, om0[0]), -kClamp, kClamp);
+                    u = exp2_fast(d);
+                    ui = exp2_fast(-d);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float kv = static_cast<float>(kr[x][e]);
+                    xp[e] = kv * u;
+                    xq[e] = static_cast<float>(qr[x][e]) * u;
+                    xm[e] = kv * ui;
+                }
             }
             kpf[x] = pack8(xp);
             qpf[x] = pack8(xq);
@@ -606,6 +630,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 // the two factors are applied one after the other; otherwise their product
                 // is. Lane (c, hi) needs the factors of key positions 16 tm + 4 hi + i;
                 // lane lr of the row holds those of 4 tm + i = 2 lr, 2 lr + 1.
+                if constexpr (G == kGateHead) {  // one factor pair for every row
+                    const float ep0 = ehalf[0], ec0 = ehalf[kDK];
+                    if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
+#pragma unroll
+                        for (int tm = 0; tm < 8; ++tm) accS[tm] = accS[tm] * ep0 * ec0;
+                    } else {
+                        const float e2 = ep0 * ec0;
+#pragma unroll
+                        for (int tm = 0; tm < 8; ++tm) accS[tm] *= e2;
+                    }
+                }
+                if constexpr (G == kGateChannel) {
                 const f32x2 ep = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
                 const f32x2 ec = *reinterpret_cast<const f32x2 *>(ehalf + kDK + 32 * hi + 2 * lr);
                 if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
@@ -626,6 +662,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
 #undef KDA_EROW
                 }
+                }  // (no decay: no factor)
             }
             bf16x8 sb[4];
 #pragma unroll

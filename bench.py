@@ -128,10 +128,30 @@ def hbm_probe(torch):
         del a, b
 
 
-def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_states_in):
-    """q, k, v, o in the I/O dtype, log_alpha (fp32 per key channel) and beta (fp32)
-    per token-head, plus the fp32 states read and written."""
-    per = (2 * dk + 2 * dv) * io_bytes + 4 * dk + 4
+def spin_up(torch, fn, seconds):
+    """Run fn back to back for about `seconds` before a leg's warm-up steps. The GPU idles
+    while a leg's inputs are generated on the host, and its clocks take tens of milliseconds
+    of load to return to their sustained level: a few warm-up steps alone leave the timed
+    steps partly on the ramp (the batched prefill measured 0.85 ms per step after 5 warm-up
+    steps, 0.75 ms after 50). Nothing here is timed or reported except its duration."""
+    if seconds <= 0:
+        return
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    log(f"[bench] spin-up: {n} calls in {time.perf_counter() - t0:.2f} s")
+
+
+def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_states_in, gate="channel"):
+    """q, k, v, o in the I/O dtype, log_alpha (fp32: per key channel, one per token and
+    head, or none) and beta (fp32) per token-head, plus the fp32 states read and written."""
+    per = (2 * dk + 2 * dv) * io_bytes + {"channel": 4 * dk, "head": 4, "none": 0}[gate] + 4
     return token_heads * per + 4 * dk * dv * (n_states_out + n_states_in)
 
 
@@ -156,6 +176,7 @@ def bench_prefill(args, kda, torch):
     def step():
         kda.chunk_fwd(q, k, v, la, beta, chunk=C, o=o, hT=hT, workspace=ws)
 
+    spin_up(torch, step, args.spin_up)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -202,6 +223,10 @@ def bench_workload(args, kda, torch, name):
     k = torch.from_numpy(x["k"]).to(dev).to(dt).reshape(lead + (w.H, w.dk))
     v = torch.from_numpy(x["v"]).to(dev).to(dt).reshape(lead + (w.H, w.dv))
     la = torch.from_numpy(x["log_alpha"]).to(dev).reshape(lead + (w.H, w.dk))
+    if w.gate == "head":    # one decay per token and head: the first key channel's draw
+        la = la[..., 0].contiguous()
+    elif w.gate == "none":  # no decay
+        la = None
     beta = torch.from_numpy(x["beta"]).to(dev).reshape(lead + (w.H,))
     h0 = None if x["h0"] is None else torch.from_numpy(x["h0"]).to(dev)
     cu = torch.from_numpy(x["cu_seqlens"]).to(dev) if varlen else None
@@ -216,6 +241,7 @@ def bench_workload(args, kda, torch, name):
         kda.chunk_fwd(q, k, v, la, beta, scale=w.scale, h0=h0, cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT,
                       workspace=ws)
 
+    spin_up(torch, step, args.spin_up)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -228,14 +254,15 @@ def bench_workload(args, kda, torch, name):
     ms = e0.elapsed_time(e1) / args.steps
     tokens = sum(w.seqlens)
     alg = prefill_algorithmic_bytes(tokens * w.H, w.dk, w.dv, 2 if w.io == "bf16" else 4, n_seqs * w.H,
-                                    0 if h0 is None else n_seqs * w.H)
+                                    0 if h0 is None else n_seqs * w.H, w.gate)
     achieved = alg / (ms * 1e-3) / 1e9
     path = prefill_path(B, T, w.H, w.dk, w.dv, w.chunk, varlen, w.io == "bf16")
     log(f"[bench] workload {name} ({path} pass): {ms:.3f} ms/call, {tokens / (ms * 1e-3):.3e} tokens/s, "
         f"{achieved:.0f} GB/s algorithmic")
     return {"value": tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 4), "pass": path,
             "kernel": PATHS[path]["kernel"],
-            "workload": f"seqlens {list(w.seqlens)}, H={w.H}, d_k=d_v={w.dk}, chunk {w.chunk}, {w.io} q/k/v/o",
+            "workload": f"seqlens {list(w.seqlens)}, H={w.H}, d_k=d_v={w.dk}, chunk {w.chunk}, {w.io} q/k/v/o, "
+                        f"decay per {'key channel' if w.gate == 'channel' else 'token and head' if w.gate == 'head' else '(none)'}",
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
 
@@ -261,6 +288,8 @@ def bench_decode(args, kda, torch):
         s = steps_in[i % bank]
         kda.recurrent_step(s["q"], s["k"], s["v"], s["la"], s["beta"], state, o=o)
 
+    it = iter(range(1 << 30))
+    spin_up(torch, lambda: step(next(it)), args.spin_up)
     for i in range(8):
         step(i)
     torch.cuda.synchronize()
@@ -311,6 +340,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spin-up", type=float, default=0.3, metavar="SECONDS",
+                    help="untimed back-to-back calls before each leg's warm-up steps (GPU clocks)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--decode-bank", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=8)

@@ -14,6 +14,8 @@ Workloads (sizes from the five benchmark configurations of this library):
            per-sequence h0 ~ N(0, 0.02)
   decode   N=256 sequences, H=32, d=128, one bf16 token per step, gates "main",
            h0 ~ N(0, 0.02)
+  batched_gdn, batched_deltanet: the batched workload with the decay given per token
+           and head (the first key channel's draw) or not at all (`gate`)
 
 Gate families (log alpha is drawn per token, per head and per key channel):
   weak:  log alpha = -0.1 * softplus(N(0,1)),  beta = sigmoid(N(0,1))
@@ -47,6 +49,7 @@ class Workload:
     gates: str              # "weak", "main" (or "strong" in tests)
     h0: str                 # "zero" or "normal"
     seed: int
+    gate: str = "channel"   # decay granularity given to the library: "channel", "head" or "none"
 
     @property
     def T_total(self) -> int:
@@ -70,6 +73,10 @@ WORKLOADS = {
     "batched": Workload("batched", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002),
     "varlen": Workload("varlen", (32768, 16384, 12288, 4096), 32, 128, 128, 128, "bf16", "weak",
                        "normal", 1003),
+    # the batched workload with one decay per token and head (Gated DeltaNet) and with none (DeltaNet)
+    "batched_gdn": Workload("batched_gdn", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002, "head"),
+    "batched_deltanet": Workload("batched_deltanet", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002,
+                                 "none"),
 }
 
 # Decode: N sequences x H heads, one token per step.

@@ -20,7 +20,8 @@ KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
-           "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_recurrent_step", "kda_recurrent_step_gated")
+           "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_preact", "kda_recurrent_step",
+           "kda_recurrent_step_gated", "kda_recurrent_step_preact")
 ABI_VERSION = 2
 
 
@@ -53,10 +54,14 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = I
     lib.kda_chunk_fwd_gated.argtypes = [I] + lib.kda_chunk_fwd.argtypes
     lib.kda_chunk_fwd_gated.restype = I
+    lib.kda_chunk_fwd_preact.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, I, P, P, P, Z, P]
+    lib.kda_chunk_fwd_preact.restype = I
     lib.kda_recurrent_step.argtypes = [I, I, I, I, I, P, P, P, P, P, F, P, P, P]
     lib.kda_recurrent_step.restype = I
     lib.kda_recurrent_step_gated.argtypes = [I] + lib.kda_recurrent_step.argtypes
     lib.kda_recurrent_step_gated.restype = I
+    lib.kda_recurrent_step_preact.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P]
+    lib.kda_recurrent_step_preact.restype = I
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libkda.so has ABI {lib.kda_abi_version()}, this binding expects {ABI_VERSION}; "
                            "rebuild it")
@@ -201,4 +206,92 @@ def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = Non
                                       _ptr(beta), float(scale), _ptr(state), _ptr(o), _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_recurrent_step_gated")
+    return o
+
+
+def chunk_fwd_preact(q, k, v, a, A_log, dt_bias, b, scale: Optional[float] = None, h0=None, cu_seqlens=None,
+                     chunk: int = 64, output_final_state: bool = True, o=None, hT=None, workspace=None,
+                     stream=None):
+    """Chunked forward with the gates formed in the kernels (kda_chunk_fwd_preact):
+    log_alpha = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b).
+
+    a [.., H, dk] in q's dtype; A_log [H] fp32; dt_bias [H, dk] fp32; b [.., H] fp32;
+    the rest as in chunk_fwd. Returns (o, hT)."""
+    import torch
+    lib = load()
+    dev = q.device
+    io = _io_code(q.dtype)
+    if cu_seqlens is not None:
+        if q.dim() != 3:
+            raise ValueError("with cu_seqlens, q must be packed [T, H, dk]")
+        B, (T, H, dk) = 1, q.shape
+        n_seqs = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", torch.int32, (n_seqs + 1,), dev)
+        lead = (T,)
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, dk]")
+        B, T, H, dk = q.shape
+        n_seqs = B
+        lead = (B, T)
+    dv = v.shape[-1]
+    _check(k, "k", q.dtype, lead + (H, dk), dev)
+    _check(v, "v", q.dtype, lead + (H, dv), dev)
+    _check(a, "a", q.dtype, lead + (H, dk), dev)
+    _check(A_log, "A_log", torch.float32, (H,), dev)
+    _check(dt_bias, "dt_bias", torch.float32, (H, dk), dev)
+    _check(b, "b", torch.float32, lead + (H,), dev)
+    if h0 is not None:
+        _check(h0, "h0", torch.float32, (n_seqs, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty(lead + (H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, lead + (H, dv), dev)
+    if output_final_state and hT is None:
+        hT = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    if hT is not None:
+        _check(hT, "hT", torch.float32, (n_seqs, H, dk, dv), dev)
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
+                                                 n_seqs if cu_seqlens is not None else 0, io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dk ** -0.5
+    st = lib.kda_chunk_fwd_preact(B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
+                                  _ptr(dt_bias), _ptr(b), float(scale), _ptr(h0), _ptr(cu_seqlens),
+                                  n_seqs if cu_seqlens is not None else 0, _ptr(o), _ptr(hT),
+                                  _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_preact")
+    return o, hT
+
+
+def recurrent_step_preact(q, k, v, a, A_log, dt_bias, b, state, scale: Optional[float] = None, o=None,
+                          stream=None):
+    """One decode step with the gates formed in the kernel (kda_recurrent_step_preact):
+    a [N, H, dk] in q's dtype; A_log [H]; dt_bias [H, dk]; b [N, H] fp32; state updated
+    in place. Returns o [N, H, dv]."""
+    import torch
+    lib = load()
+    dev = q.device
+    io = _io_code(q.dtype)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check(k, "k", q.dtype, (N, H, dk), dev)
+    _check(v, "v", q.dtype, (N, H, dv), dev)
+    _check(a, "a", q.dtype, (N, H, dk), dev)
+    _check(A_log, "A_log", torch.float32, (H,), dev)
+    _check(dt_bias, "dt_bias", torch.float32, (H, dk), dev)
+    _check(b, "b", torch.float32, (N, H), dev)
+    _check(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, (N, H, dv), dev)
+    if scale is None:
+        scale = dk ** -0.5
+    st = lib.kda_recurrent_step_preact(N, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
+                                       _ptr(dt_bias), _ptr(b), float(scale), _ptr(state), _ptr(o),
+                                       _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_step_preact")
     return o

@@ -119,13 +119,14 @@ KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, in
     return L.total;
 }
 
-KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
-                                   const void *q, const void *k, const void *v,
-                                   const float *log_alpha, const float *beta, float scale,
-                                   const float *h0, const int32_t *cu_seqlens, int n_seqs,
-                                   void *o, float *hT, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
-    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
+namespace {
+
+// kda_chunk_fwd_gated (gate = a kda_gate value) and kda_chunk_fwd_preact (gate =
+// kda::kGatePreact, pre = its pre-activations; log_alpha unused, beta = b).
+int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                   const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
+                   float scale, const float *h0, const int32_t *cu_seqlens, int n_seqs, void *o, float *hT,
+                   void *workspace, size_t workspace_bytes, void *stream) {
     const bool varlen = cu_seqlens != nullptr;
     kda_status st = check_sizes(B, T, H, d_k, d_v, chunk, io, varlen, n_seqs);
     if (st != KDA_OK) return st;
@@ -141,13 +142,18 @@ KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d
         if (overlaps(o, ob, q, tokens * H * d_k * esz) || overlaps(o, ob, k, tokens * H * d_k * esz) ||
             overlaps(o, ob, v, ob) || overlaps(o, ob, beta, tokens * H * 4))
             return KDA_ERR_INVALID_ARG;
-        if (gate != KDA_GATE_NONE) {
+        if (gate == kda::kGatePreact) {
+            if (!pre.a || !pre.A_log || !pre.dt_bias || !aligned(pre.a, 16) || !aligned(pre.A_log, 4) ||
+                !aligned(pre.dt_bias, 16) || overlaps(o, ob, pre.a, tokens * H * d_k * esz) ||
+                overlaps(o, ob, pre.A_log, (size_t)H * 4) || overlaps(o, ob, pre.dt_bias, (size_t)H * d_k * 4))
+                return KDA_ERR_INVALID_ARG;
+        } else if (gate != KDA_GATE_NONE) {
             const size_t gb = tokens * H * (gate == KDA_GATE_CHANNEL ? (size_t)d_k : 1) * 4;
             if (!log_alpha || !aligned(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4) || overlaps(o, ob, log_alpha, gb))
                 return KDA_ERR_INVALID_ARG;
         }
     }
-    if (gate == KDA_GATE_NONE) log_alpha = nullptr;  // never read
+    if (gate == KDA_GATE_NONE || gate == kda::kGatePreact) log_alpha = nullptr;  // never read
     if ((h0 && !aligned(h0, 16)) || (hT && !aligned(hT, 16))) return KDA_ERR_INVALID_ARG;
     if (varlen && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
 
@@ -160,7 +166,7 @@ KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d
     char *ws = static_cast<char *>(workspace);
     const bool bf = io == KDA_BF16;
     if (use_fused(B, T, H, d_k, d_v, chunk, varlen, io)) {
-        kda::FusedArgs fa{q, k, v, log_alpha, beta, scale, h0, hT, o, ws + L.discard, H, T, gate};
+        kda::FusedArgs fa{q, k, v, log_alpha, beta, scale, h0, hT, o, ws + L.discard, H, T, gate, pre};
         return kda::launch_fused(fa, d_k, d_v, bf, B, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     ChunkBuffers buf{};
@@ -188,13 +194,40 @@ KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d
     }
 
     if (tokens > 0) {
-        kda::PrepArgs pa{q, k, v, log_alpha, beta, scale, H, gate, map, buf};
+        kda::PrepArgs pa{q, k, v, log_alpha, beta, scale, H, gate, pre, map, buf};
         if (kda::launch_prep(pa, chunk, d_k, d_v, bf, (int)L.n_chunks, hs) != hipSuccess)
             return KDA_ERR_HIP;
     }
     kda::StateArgs sa{h0, hT, o, L.total > 0 ? ws + L.discard : nullptr, H, 0, map, buf};
     if (kda::launch_state(sa, chunk, d_k, d_v, bf, nseq, hs) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+int recurrent_step_impl(int gate, const kda::PreactArgs &pre, int N, int H, int d_k, int d_v, int io,
+                        const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, float scale, float *state, void *o, void *stream);
+
+}  // namespace
+
+KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                                   const void *q, const void *k, const void *v,
+                                   const float *log_alpha, const float *beta, float scale,
+                                   const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                                   void *o, float *hT, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
+    return chunk_fwd_impl(gate, kda::PreactArgs{}, B, T, H, d_k, d_v, chunk, io, q, k, v, log_alpha, beta, scale,
+                          h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes, stream);
+}
+
+KDA_EXPORT int kda_chunk_fwd_preact(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                                    const void *q, const void *k, const void *v,
+                                    const void *a, const float *A_log, const float *dt_bias, const float *b,
+                                    float scale, const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                                    void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_fwd_impl(kda::kGatePreact, kda::PreactArgs{a, A_log, dt_bias}, B, T, H, d_k, d_v, chunk, io, q,
+                          k, v, nullptr, b, scale, h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes,
+                          stream);
 }
 
 KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
@@ -207,11 +240,11 @@ KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, i
                                h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes, stream);
 }
 
-KDA_EXPORT int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v, int io,
-                                        const void *q, const void *k, const void *v,
-                                        const float *log_alpha, const float *beta, float scale,
-                                        float *state, void *o, void *stream) {
-    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
+namespace {
+
+int recurrent_step_impl(int gate, const kda::PreactArgs &pre, int N, int H, int d_k, int d_v, int io,
+                        const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, float scale, float *state, void *o, void *stream) {
     if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H < 1) return KDA_ERR_INVALID_ARG;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
@@ -222,16 +255,40 @@ KDA_EXPORT int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(beta, 4) ||
         !aligned(state, 16))
         return KDA_ERR_INVALID_ARG;
-    if (gate != KDA_GATE_NONE && (!log_alpha || !aligned(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4)))
+    if (gate == kda::kGatePreact) {
+        if (!pre.a || !pre.A_log || !pre.dt_bias || !aligned(pre.a, 16) || !aligned(pre.A_log, 4) ||
+            !aligned(pre.dt_bias, 16))
+            return KDA_ERR_INVALID_ARG;
+    } else if (gate != KDA_GATE_NONE && (!log_alpha || !aligned(log_alpha, gate == KDA_GATE_CHANNEL ? 16 : 4))) {
         return KDA_ERR_INVALID_ARG;
-    if (gate == KDA_GATE_NONE) log_alpha = nullptr;  // never read
+    }
+    if (gate == KDA_GATE_NONE || gate == kda::kGatePreact) log_alpha = nullptr;  // never read
     const size_t nh = (size_t)N * H, esz = io == KDA_BF16 ? 2 : 4;
     if (overlaps(o, nh * d_v * esz, state, nh * d_k * d_v * 4)) return KDA_ERR_INVALID_ARG;
-    kda::DecodeArgs da{q, k, v, log_alpha, beta, scale, state, o, (int)nh, gate};
+    kda::DecodeArgs da{q, k, v, log_alpha, beta, scale, state, o, (int)nh, gate, H, pre};
     if (kda::launch_decode(da, d_k, d_v, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v, int io,
+                                        const void *q, const void *k, const void *v,
+                                        const float *log_alpha, const float *beta, float scale,
+                                        float *state, void *o, void *stream) {
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
+    return recurrent_step_impl(gate, kda::PreactArgs{}, N, H, d_k, d_v, io, q, k, v, log_alpha, beta, scale, state,
+                               o, stream);
+}
+
+KDA_EXPORT int kda_recurrent_step_preact(int N, int H, int d_k, int d_v, int io,
+                                         const void *q, const void *k, const void *v,
+                                         const void *a, const float *A_log, const float *dt_bias, const float *b,
+                                         float scale, float *state, void *o, void *stream) {
+    return recurrent_step_impl(kda::kGatePreact, kda::PreactArgs{a, A_log, dt_bias}, N, H, d_k, d_v, io, q, k, v,
+                               nullptr, b, scale, state, o, stream);
 }
 
 KDA_EXPORT int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,

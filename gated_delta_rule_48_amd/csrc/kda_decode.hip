@@ -55,15 +55,22 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
         const float kv = to_f32(k[tid]), qv = to_f32(q[tid]);
         ks[tid] = kv;
         qs[tid] = qv;
-        al[tid] = a.gate == kGateChannel ? __expf(a.log_alpha[(size_t)nh * DK + tid])
-                  : a.gate == kGateHead  ? __expf(a.log_alpha[nh])
-                                         : 1.f;
+        if (a.gate == kGatePreact) {  // alpha = exp(-exp(A_log) softplus(a + dt_bias))
+            const int hh = nh % a.H;
+            const float x = to_f32(static_cast<const T *>(a.pre.a)[(size_t)nh * DK + tid]) +
+                            a.pre.dt_bias[(size_t)hh * DK + tid];
+            al[tid] = expf(-expf(a.pre.A_log[hh]) * softplus_f(x));
+        } else {
+            al[tid] = a.gate == kGateChannel ? __expf(a.log_alpha[(size_t)nh * DK + tid])
+                      : a.gate == kGateHead  ? __expf(a.log_alpha[nh])
+                                             : 1.f;
+        }
         kq = kv * qv;
     }
     f32x4 vv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) vv[i] = to_f32(v[4 * cg + i]);
-    const float beta = a.beta[nh];
+    const float beta = a.gate == kGatePreact ? sigmoid_f(a.beta[nh]) : a.beta[nh];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if ((tid & 63) == 0) kq_part[tid >> 6] = kq;

@@ -73,7 +73,8 @@ struct Lds {
     static constexpr int KP = KM + kC * kDK * 2;        // [C][DK]  bf16 fragments: Kp (Gram and state)
     static constexpr int IDN = KP + kC * kDK * 2;       // [2][64]  bf16x8: each lane's identity operands (ident_frag)
     static constexpr int FLG = IDN + 2 * 64 * 16;       // [2]      int: E E_prev leaves the normal fp32 range
-    static constexpr int SIZE = FLG + 16;
+    static constexpr int DTB = FLG + 16;                // [DK]     fp32: dt_bias of the head (pre-activation gates)
+    static constexpr int SIZE = DTB + kDK * 4;
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
@@ -192,6 +193,8 @@ __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb 
 
 template <int G>
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
+    // a decay per key channel, given or formed from pre-activations
+    constexpr bool kPerChannel = G == kGateChannel || G == kGatePreact;
     extern __shared__ __align__(16) unsigned char smem[];
     bf16 *Qp = reinterpret_cast<bf16 *>(smem + Lds::QP);
     bf16 *KtT = reinterpret_cast<bf16 *>(smem + Lds::KTT);
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *Kp = reinterpret_cast<bf16 *>(smem + Lds::KP);
     bf16 *idn = reinterpret_cast<bf16 *>(smem + Lds::IDN);
     int *flg = reinterpret_cast<int *>(smem + Lds::FLG);
+    float *dtb = reinterpret_cast<float *>(smem + Lds::DTB);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
@@ -243,6 +247,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     //      requests compete, and no phase starts with a burst of them.
     bf16x8 kr[2], qr[2], vr[2];
     float gl[2][8];
+    bf16x8 gar[2];  // decay pre-activations (kGatePreact)
     float bta;
     // uniform base of chunk ci's first row (head h) + 32-bit lane offsets
     auto tok0_of = [&](int ci) { return (seq0 + (size_t)ci * kC) * H + h; };
@@ -276,7 +281,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         const int ln = opaque_lane();
         const size_t t0b = tok0_of(ci);
         const unsigned ro = row_off(ci, ln);
-        if constexpr (G == kGateChannel) {
+        if constexpr (G == kGatePreact) {
+            const bf16 *ap = static_cast<const bf16 *>(a.pre.a) + t0b * kDK + ro * kDK;
+#pragma unroll
+            for (int x = 0; x < 2; ++x) gar[x] = load_row8(ap, 2 * hf + x, ln >> 4);
+        } else if constexpr (G == kGateChannel) {
             const float *gp = a.log_alpha + t0b * kDK + ro * kDK;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
@@ -297,6 +306,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         bta = a.beta[t0b + ro];
     };
+    // pre-activation gates: the head's dt_bias in LDS (read after the loop's first barrier)
+    // and its decay-rate scale exp(A_log)
+    float eA = 0.f;
+    if constexpr (G == kGatePreact) {
+        if (tid < kDK) dtb[tid] = a.pre.dt_bias[(size_t)h * kDK + tid];
+        eA = exp2_fast(a.pre.A_log[h] * kL2E);
+    }
     // the identity operands, formed once and read back where a transpose needs them
     // (the first barrier of the loop precedes every read)
     if (w == 0) {
@@ -327,11 +343,30 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         float g[2][8], bt;
         {
         KDA_PHASE_LANE
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) g[x][e] = gl[x][e];
         bt = bta;
+        if constexpr (G == kGatePreact) {
+            // log alpha = -exp(A_log) softplus(a + dt_bias) (channels 32 kg + 8 hi + e of the
+            // row), beta = sigmoid(b); softplus(x) = max(x, 0) + log(1 + e^-|x|)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int c0 = 32 * (2 * hf + x) + 8 * hi;
+                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dtb + c0);
+                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dtb + c0 + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xv = static_cast<float>(gar[x][e]) + (e < 4 ? d0[e] : d1[e - 4]);
+                    const float sp = fmaxf(xv, 0.f) +
+                                     __builtin_amdgcn_logf(1.f + exp2_fast(-fabsf(xv) * kL2E)) * (1.f / kL2E);
+                    g[x][e] = -eA * sp;
+                }
+            }
+            bt = __builtin_amdgcn_rcpf(1.f + exp2_fast(-bta * kL2E));
+        } else {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) g[x][e] = gl[x][e];
+        }
         if (!full) {  // rows past the end: no decay, no update
             const bool valid = t0 + r < T_len;
 #pragma unroll
@@ -340,7 +375,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 for (int e = 0; e < 8; ++e) g[x][e] = valid ? g[x][e] : 0.f;
             bt = valid ? bt : 0.f;
         }
-        if constexpr (G == kGateChannel) {
+        if constexpr (kPerChannel) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -408,7 +443,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             const f32x4 om0 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c0);
             const f32x4 om1 = *reinterpret_cast<const f32x4 *>(offm + rb * kDK + c4);
             float xp[8], xq[8], xm[8];
-            if constexpr (G == kGateChannel) {
+            if constexpr (kPerChannel) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float om = e < 4 ? om0[e] : om1[e - 4];
@@ -641,7 +676,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                         for (int tm = 0; tm < 8; ++tm) accS[tm] *= e2;
                     }
                 }
-                if constexpr (G == kGateChannel) {
+                if constexpr (kPerChannel) {
                 const f32x2 ep = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
                 const f32x2 ec = *reinterpret_cast<const f32x2 *>(ehalf + kDK + 32 * hi + 2 * lr);
                 if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
@@ -776,9 +811,10 @@ hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seq
     // the fused pass is built for bf16 input and d_k = d_v = 128 only
     if (!bf16 || dk != kDK || dv != kDV) return hipErrorInvalidValue;
     constexpr size_t smem = Lds::SIZE;
-    auto kern = a.gate == kGateHead ? kda_fused_kernel<kGateHead>
-                : a.gate == kGateNone ? kda_fused_kernel<kGateNone>
-                                      : kda_fused_kernel<kGateChannel>;
+    auto kern = a.gate == kGateHead    ? kda_fused_kernel<kGateHead>
+                : a.gate == kGateNone   ? kda_fused_kernel<kGateNone>
+                : a.gate == kGatePreact ? kda_fused_kernel<kGatePreact>
+                                        : kda_fused_kernel<kGateChannel>;
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess) return err;

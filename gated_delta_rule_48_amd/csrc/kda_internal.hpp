@@ -12,6 +12,20 @@ namespace kda {
 // Decay granularity of log_alpha (the kda_gate values of kda.h): one decay per key
 // channel, one per token and head, or none.
 constexpr int kGateChannel = 0, kGateHead = 1, kGateNone = 2;
+// Gates formed from pre-activations: log_alpha = -exp(A_log[h]) softplus(a + dt_bias[h, c])
+// per key channel (a in the io dtype, [T, H, d_k]) and beta = sigmoid(b).
+constexpr int kGatePreact = 3;
+
+// softplus(x) = log(1 + e^x) without overflow, and sigmoid(x) = 1 / (1 + e^-x).
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// The gate pre-activations' per-head parameters (kGatePreact only).
+struct PreactArgs {
+    const void *a;          // [T, H, d_k] io dtype
+    const float *A_log;     // [H]
+    const float *dt_bias;   // [H, d_k]
+};
 
 // Per-chunk quantities produced by the chunk-preparation kernel and consumed by
 // the state/output kernel. All are indexed chunk-major: [chunk j][head h][...],
@@ -30,7 +44,9 @@ struct PrepArgs {
     const float *log_alpha, *beta;
     float scale;
     int H;
-    int gate;  // kGateChannel: log_alpha [T, H, d_k]; kGateHead: [T, H]; kGateNone: not read
+    int gate;  // kGateChannel: log_alpha [T, H, d_k]; kGateHead: [T, H]; kGateNone: not read;
+               // kGatePreact: pre (log_alpha not read) and beta holds its pre-activation
+    PreactArgs pre;
     SeqMap map;
     ChunkBuffers buf;
 };
@@ -57,6 +73,7 @@ struct FusedArgs {
     int H;
     int seq_len;    // every sequence has seq_len tokens
     int gate;       // as in PrepArgs
+    PreactArgs pre;
 };
 
 struct DecodeArgs {
@@ -67,6 +84,8 @@ struct DecodeArgs {
     void *o;
     int NH;    // N * H
     int gate;  // as in PrepArgs (log_alpha [N, H, d_k] or [N, H])
+    int H;
+    PreactArgs pre;
 };
 
 // Each returns hipSuccess or the launch error.

@@ -187,6 +187,13 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             qr[kg] = load_row_frag<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
             if (a.gate == kGateChannel) {
                 load_row_f32<T>(a.log_alpha + tok * DK, kg, hi, g[kg]);
+            } else if (a.gate == kGatePreact) {  // -exp(A_log) softplus(a + dt_bias)
+                const V ar = load_row_frag<T>(static_cast<const T *>(a.pre.a) + tok * DK, kg, hi);
+                const float eA = expf(a.pre.A_log[h]);
+                float db[EPL];
+                load_row_f32<T>(a.pre.dt_bias + (size_t)h * DK, kg, hi, db);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) g[kg][e] = -eA * softplus_f(to_f32(ar[e]) + db[e]);
             } else {  // one decay for every channel of the row, or none
                 const float x = a.gate == kGateHead ? a.log_alpha[tok] : 0.f;
 #pragma unroll
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
         }
     }
-    if (valid) b = a.beta[tok];
+    if (valid) b = a.gate == kGatePreact ? sigmoid_f(a.beta[tok]) : a.beta[tok];
     if (hi == 0) bet[r] = b;
 
     // ---- 1. inclusive running sum of log alpha within the wave's 16 rows (DPP scan);

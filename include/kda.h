@@ -153,6 +153,33 @@ int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chu
                         void *stream);
 
 /*
+ * kda_chunk_fwd_preact -- kda_chunk_fwd with the gates formed inside the kernels
+ * from their pre-activations, as the gate line of KDA's open-source layer that
+ * the "ten questions" page quotes (jokeuncle.github.io, Kimi K3 KDA math for
+ * beginners, Q9: g = -exp(A_log) softplus(f(x) + dt_bias), alpha = e^g, and beta
+ * through a sigmoid):
+ *
+ *     log_alpha[t, h, c] = -exp(A_log[h]) * softplus(a[t, h, c] + dt_bias[h, c])
+ *     beta[t, h]         = sigmoid(b[t, h])
+ *
+ * so the decay is read in the io dtype (half the bytes of fp32 log_alpha in bf16)
+ * and no separate pass forms it. softplus(x) = log(1 + e^x), sigmoid(x) =
+ * 1 / (1 + e^-x).
+ *
+ * Arguments (others as kda_chunk_fwd; the workspace size is the same):
+ *   a        [B*T, H, d_k] dtype io, 16-byte aligned: the decay's pre-activation.
+ *   A_log    [H] fp32: per-head log of the decay rate's scale.
+ *   dt_bias  [H, d_k] fp32, 16-byte aligned: per-channel bias.
+ *   b        [B*T, H] fp32: beta's pre-activation.
+ * The limit on a chunk's summed log_alpha (>= -170) applies to the formed decay.
+ */
+int kda_chunk_fwd_preact(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                         const void *q, const void *k, const void *v,
+                         const void *a, const float *A_log, const float *dt_bias, const float *b,
+                         float scale, const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                         void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_recurrent_step -- one decode step ("recurrent program") for N sequences:
  * every (sequence, head) state is read once and written once, in place.
  *
@@ -181,6 +208,16 @@ int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v, int io,
                              const void *q, const void *k, const void *v,
                              const float *log_alpha, const float *beta, float scale,
                              float *state, void *o, void *stream);
+
+/*
+ * kda_recurrent_step_preact -- kda_recurrent_step with the gates formed from
+ * pre-activations as in kda_chunk_fwd_preact: a [N, H, d_k] dtype io, A_log [H],
+ * dt_bias [H, d_k], b [N, H] fp32.
+ */
+int kda_recurrent_step_preact(int N, int H, int d_k, int d_v, int io,
+                              const void *q, const void *k, const void *v,
+                              const void *a, const float *A_log, const float *dt_bias, const float *b,
+                              float scale, float *state, void *o, void *stream);
 
 #ifdef __cplusplus
 }

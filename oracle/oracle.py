@@ -93,3 +93,19 @@ def kda_reference(q, k, v, log_alpha, beta, scale: float, h0=None, cu_seqlens=No
     if rc != 0:
         raise RuntimeError(f"kda_oracle_fwd failed with code {rc}")
     return o, hT
+
+
+def gate_prologue(a, A_log, dt_bias, b):
+    """The gates formed from their pre-activations, in fp64, as the gate line of KDA's
+    open-source layer that the "ten questions" page quotes (Q9: g = -exp(A_log)
+    softplus(f(x) + dt_bias), alpha = e^g; beta through a sigmoid):
+
+        log_alpha[t, h, c] = -exp(A_log[h]) * softplus(a[t, h, c] + dt_bias[h, c])
+        beta[t, h]         = sigmoid(b[t, h])
+
+    softplus(x) = log(1 + e^x) (np.logaddexp(0, x)), sigmoid(x) = 1 / (1 + e^-x).
+    a [..., H, dk]; A_log [H]; dt_bias [H, dk]; b [..., H]. Returns (log_alpha, beta)."""
+    a, A_log, dt_bias, b = map(_f64, (a, A_log, dt_bias, b))
+    log_alpha = -np.exp(A_log)[:, None] * np.logaddexp(0.0, a + dt_bias)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    return log_alpha, beta

@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import kda_synth
+import oracle
 import oracle_pins as P
 
 
@@ -55,3 +56,49 @@ def test_generator_is_seeded_and_normalised():
     assert list(a["cu_seqlens"]) == [0, 33, 40]
     assert np.allclose(np.linalg.norm(a["k"], axis=-1), 1.0, atol=1e-2)  # bf16-rounded unit keys
     assert np.all(a["log_alpha"] < 0) and np.all((a["beta"] > 0) & (a["beta"] < 1))
+
+
+# ----------------------------------------------------------------------------- gate prologue
+
+def _prologue_scalar(a, A_log, dt_bias, b):
+    la, be = oracle.gate_prologue(np.array([[[a]]]), np.array([A_log]), np.array([[dt_bias]]), np.array([[b]]))
+    return float(la[0, 0, 0]), float(be[0, 0])
+
+
+def test_gate_prologue_page_values():
+    """Q9 of the ten-questions page prints the squashing functions' values: sigmoid(0) = 0.5,
+    sigmoid(4) ~ 0.98, sigmoid(-4) ~ 0.02, softplus(-5) ~ 0.007, softplus(5) ~ 5.007. With
+    A_log = 0 (a rate scale of 1) the formed log alpha is -softplus(a + dt_bias)."""
+    for bb, want in ((0.0, 0.5), (4.0, 0.98), (-4.0, 0.02)):
+        assert abs(_prologue_scalar(0.0, 0.0, 0.0, bb)[1] - want) < 0.005
+    assert abs(-_prologue_scalar(-5.0, 0.0, 0.0, 0.0)[0] - 0.007) < 0.0005
+    assert abs(-_prologue_scalar(5.0, 0.0, 0.0, 0.0)[0] - 5.007) < 0.0005
+
+
+def test_gate_prologue_closed_forms():
+    # softplus(0) = ln 2; the rate scale multiplies; dt_bias shifts the pre-activation
+    assert abs(_prologue_scalar(0.0, 0.0, 0.0, 0.0)[0] + np.log(2.0)) < 1e-15
+    assert abs(_prologue_scalar(0.0, np.log(3.0), 0.0, 0.0)[0] + 3.0 * np.log(2.0)) < 1e-14
+    assert _prologue_scalar(1.5, 0.2, -0.5, 0.0)[0] == _prologue_scalar(0.5, 0.2, 0.5, 0.0)[0]
+    # far from zero softplus is its asymptote: x for large x, e^x for very negative x
+    assert abs(_prologue_scalar(40.0, 0.0, 0.0, 0.0)[0] + 40.0) < 1e-12
+    assert abs(_prologue_scalar(-40.0, 0.0, 0.0, 0.0)[0] + np.exp(-40.0)) < 1e-30
+    # sigmoid(x) + sigmoid(-x) = 1
+    assert abs(_prologue_scalar(0.0, 0.0, 0.0, 1.7)[1] + _prologue_scalar(0.0, 0.0, 0.0, -1.7)[1] - 1.0) < 1e-15
+
+
+def test_gate_prologue_ranges_and_broadcast():
+    """alpha = e^log_alpha lies in (0, 1) and beta in (0, 1) whatever the inputs; A_log is
+    per head and dt_bias per (head, channel)."""
+    rng = np.random.default_rng(5)
+    T, H, dk = 7, 3, 4
+    a = rng.standard_normal((T, H, dk)) * 10
+    A_log = rng.standard_normal(H)
+    dt_bias = rng.standard_normal((H, dk))
+    b = rng.standard_normal((T, H)) * 10
+    la, be = oracle.gate_prologue(a, A_log, dt_bias, b)
+    assert la.shape == (T, H, dk) and be.shape == (T, H)
+    assert np.all(la < 0) and np.all(np.exp(la) > 0) and np.all((be > 0) & (be < 1))
+    for t, h, c in ((0, 0, 0), (6, 2, 3), (3, 1, 2)):
+        want = -np.exp(A_log[h]) * np.log1p(np.exp(a[t, h, c] + dt_bias[h, c]))
+        assert abs(la[t, h, c] - want) <= 1e-12 * abs(want) + 1e-300

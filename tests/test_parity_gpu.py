@@ -359,3 +359,79 @@ def test_decode_gate_kinds(gate, io):
     eo, eh = rel_l2(o, o_ref), rel_l2(st, h_ref)
     say(f"[decode {gate} {io}] rel_l2 o={eo:.2e} state={eh:.2e}")
     assert eo <= TOL[io] and eh <= TOL[io]
+
+
+# ----------------------------------------------------------------------------- gates from pre-activations
+
+def _preact_case(x, io, seed):
+    """Pre-activations for x's tokens, and x with the gates they form (fp64, oracle) in place
+    of its own: the oracle's input."""
+    T, H, dk = x["q"].shape
+    p = kda_synth.gen_preact(T, H, dk, io, seed)
+    la, be = oracle.gate_prologue(p["a"], p["A_log"], p["dt_bias"], p["b"])
+    return p, dict(x, log_alpha=la, beta=be)
+
+
+@pytest.mark.parametrize("io,path,chunk", [("f32", "split", 64), ("bf16", "split", 64), ("bf16", "split", 128),
+                                           ("f32", "split", 128), ("bf16", "fused", 64)])
+def test_preact_gates(io, path, chunk):
+    """kda_chunk_fwd_preact: log alpha = -exp(A_log) softplus(a + dt_bias) and beta =
+    sigmoid(b) formed in the kernels; the oracle runs the recurrence on the same gates
+    formed in fp64."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    if path == "fused":
+        x = gen([200, 200], 128, 128, 128, io, seed=121)
+    else:
+        x = gen([200, 130, 1], 4, 128, 128, io, seed=122 + chunk)
+    p, y = _preact_case(x, io, seed=123 + chunk)
+    say(f"[preact {path}] io={io} C={chunk}")
+    t = to_dev(x, io)
+    iod = torch.bfloat16 if io == "bf16" else torch.float32
+    a = torch.from_numpy(p["a"]).cuda().to(iod)
+    A_log, dt_bias, b = (torch.from_numpy(p[n]).cuda() for n in ("A_log", "dt_bias", "b"))
+    if path == "fused":
+        B, T = 2, 200
+        r = lambda z: z.reshape((B, T) + tuple(z.shape[1:]))  # noqa: E731
+        o, hT = kda.chunk_fwd_preact(r(t["q"]), r(t["k"]), r(t["v"]), r(a), A_log, dt_bias, r(b), h0=t["h0"],
+                                     chunk=chunk)
+        o = o.reshape(t["v"].shape)
+    else:
+        o, hT = kda.chunk_fwd_preact(t["q"], t["k"], t["v"], a, A_log, dt_bias, b, h0=t["h0"],
+                                     cu_seqlens=t["cu_seqlens"], chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, h_ref, _ = oracle_run(y)
+    eo, eh = rel_l2(o.float().cpu().numpy(), o_ref), rel_l2(hT.cpu().numpy(), h_ref)
+    say(f"[preact {path}] rel_l2 o={eo:.2e} hT={eh:.2e}")
+    assert eo <= TOL[io] and eh <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_preact_gates(io):
+    """Five decode steps of kda_recurrent_step_preact against the oracle on the same gates."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    N, H, dk, dv, steps = 3, 4, 128, 128, 5
+    st0 = kda_synth.gen_decode_state(N, H, dk, dv, 131)
+    state = torch.from_numpy(st0).cuda()
+    iod = torch.bfloat16 if io == "bf16" else torch.float32
+    got, toks = [], []
+    for step in range(steps):
+        y = kda_synth.gen_decode_step(N, H, dk, dv, io, "main", 131, step)
+        p = kda_synth.gen_preact(N, H, dk, io, 1000 + step)
+        la, be = oracle.gate_prologue(p["a"], p["A_log"], p["dt_bias"], p["b"])
+        t = to_dev(dict(y, cu_seqlens=np.zeros(1, np.int32)), io)
+        a = torch.from_numpy(p["a"]).cuda().to(iod)
+        A_log, dt_bias, b = (torch.from_numpy(p[n]).cuda() for n in ("A_log", "dt_bias", "b"))
+        o = kda.recurrent_step_preact(t["q"], t["k"], t["v"], a, A_log, dt_bias, b, state)
+        got.append(o.float().cpu().numpy())
+        toks.append(dict(q=y["q"], k=y["k"], v=y["v"], log_alpha=la, beta=be))
+    torch.cuda.synchronize()
+    # the (n, h) pairs as independent heads of one sequence of `steps` tokens
+    seq = {n: np.stack([tk[n].reshape((N * H,) + tk[n].shape[2:]) for tk in toks]) for n in toks[0]}
+    o_ref, h_ref = oracle.kda_reference(seq["q"], seq["k"], seq["v"], seq["log_alpha"], seq["beta"], dk ** -0.5,
+                                        h0=st0.reshape(1, N * H, dk, dv))
+    eo = rel_l2(np.stack(got).reshape(steps, N * H, dv), o_ref)
+    eh = rel_l2(state.cpu().numpy().reshape(N * H, dk, dv), h_ref[0])
+    say(f"[decode preact {io}] rel_l2 o={eo:.2e} state={eh:.2e}")
+    assert eo <= TOL[io] and eh <= TOL[io]

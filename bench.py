@@ -151,7 +151,9 @@ def spin_up(torch, fn, seconds):
 def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_states_in, gate="channel"):
     """q, k, v, o in the I/O dtype, log_alpha (fp32: per key channel, one per token and
     head, or none) and beta (fp32) per token-head, plus the fp32 states read and written."""
-    per = (2 * dk + 2 * dv) * io_bytes + {"channel": 4 * dk, "head": 4, "none": 0}[gate] + 4
+    # gates: log_alpha fp32 per key channel, one per token and head, none, or (preact) the
+    # decay's pre-activation in the io dtype; then beta (or its pre-activation), fp32
+    per = (2 * dk + 2 * dv) * io_bytes + {"channel": 4 * dk, "head": 4, "none": 0, "preact": io_bytes * dk}[gate] + 4
     return token_heads * per + 4 * dk * dv * (n_states_out + n_states_in)
 
 
@@ -227,6 +229,13 @@ def bench_workload(args, kda, torch, name):
         la = la[..., 0].contiguous()
     elif w.gate == "none":  # no decay
         la = None
+    pre = None
+    if w.gate == "preact":  # gates formed in the kernels from pre-activations
+        p = kda_synth.gen_preact(sum(w.seqlens), w.H, w.dk, w.io, w.seed)
+        pre = dict(a=torch.from_numpy(p["a"]).to(dev).to(dt).reshape(lead + (w.H, w.dk)),
+                   A_log=torch.from_numpy(p["A_log"]).to(dev), dt_bias=torch.from_numpy(p["dt_bias"]).to(dev),
+                   b=torch.from_numpy(p["b"]).to(dev).reshape(lead + (w.H,)))
+        la = beta = None
     beta = torch.from_numpy(x["beta"]).to(dev).reshape(lead + (w.H,))
     h0 = None if x["h0"] is None else torch.from_numpy(x["h0"]).to(dev)
     cu = torch.from_numpy(x["cu_seqlens"]).to(dev) if varlen else None
@@ -238,8 +247,12 @@ def bench_workload(args, kda, torch, name):
                      dtype=torch.uint8, device=dev)
 
     def step():
-        kda.chunk_fwd(q, k, v, la, beta, scale=w.scale, h0=h0, cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT,
-                      workspace=ws)
+        if pre is not None:
+            kda.chunk_fwd_preact(q, k, v, pre["a"], pre["A_log"], pre["dt_bias"], pre["b"], scale=w.scale, h0=h0,
+                                 cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT, workspace=ws)
+        else:
+            kda.chunk_fwd(q, k, v, la, beta, scale=w.scale, h0=h0, cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT,
+                          workspace=ws)
 
     spin_up(torch, step, args.spin_up)
     for _ in range(args.warmup):
@@ -262,7 +275,8 @@ def bench_workload(args, kda, torch, name):
     return {"value": tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 4), "pass": path,
             "kernel": PATHS[path]["kernel"],
             "workload": f"seqlens {list(w.seqlens)}, H={w.H}, d_k=d_v={w.dk}, chunk {w.chunk}, {w.io} q/k/v/o, "
-                        f"decay per {'key channel' if w.gate == 'channel' else 'token and head' if w.gate == 'head' else '(none)'}",
+                        + {"channel": "decay per key channel", "head": "decay per token and head", "none": "no decay",
+                           "preact": "gates formed in the kernel from pre-activations"}[w.gate],
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
 

@@ -16,6 +16,8 @@ Workloads (sizes from the five benchmark configurations of this library):
            h0 ~ N(0, 0.02)
   batched_gdn, batched_deltanet: the batched workload with the decay given per token
            and head (the first key channel's draw) or not at all (`gate`)
+  batched_preact: the batched workload with gate pre-activations (gen_preact) instead
+           of log alpha and beta
 
 Gate families (log alpha is drawn per token, per head and per key channel):
   weak:  log alpha = -0.1 * softplus(N(0,1)),  beta = sigmoid(N(0,1))
@@ -49,7 +51,8 @@ class Workload:
     gates: str              # "weak", "main" (or "strong" in tests)
     h0: str                 # "zero" or "normal"
     seed: int
-    gate: str = "channel"   # decay granularity given to the library: "channel", "head" or "none"
+    gate: str = "channel"   # decays given to the library: "channel", "head", "none", or "preact"
+                            # (formed in the kernels from gen_preact's pre-activations)
 
     @property
     def T_total(self) -> int:
@@ -77,6 +80,9 @@ WORKLOADS = {
     "batched_gdn": Workload("batched_gdn", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002, "head"),
     "batched_deltanet": Workload("batched_deltanet", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002,
                                  "none"),
+    # the batched workload with its gates formed in the kernels from pre-activations (gen_preact)
+    "batched_preact": Workload("batched_preact", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002,
+                               "preact"),
 }
 
 # Decode: N sequences x H heads, one token per step.

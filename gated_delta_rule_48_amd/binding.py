@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_CHANNEL, KDA_GATE_HEAD, KDA_GATE_NONE = 0, 1, 2
+KDA_PREACT_QK_NORM = 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
@@ -54,13 +55,13 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = I
     lib.kda_chunk_fwd_gated.argtypes = [I] + lib.kda_chunk_fwd.argtypes
     lib.kda_chunk_fwd_gated.restype = I
-    lib.kda_chunk_fwd_preact.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, I, P, P, P, Z, P]
+    lib.kda_chunk_fwd_preact.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, I, P, P, P, Z, P]
     lib.kda_chunk_fwd_preact.restype = I
     lib.kda_recurrent_step.argtypes = [I, I, I, I, I, P, P, P, P, P, F, P, P, P]
     lib.kda_recurrent_step.restype = I
     lib.kda_recurrent_step_gated.argtypes = [I] + lib.kda_recurrent_step.argtypes
     lib.kda_recurrent_step_gated.restype = I
-    lib.kda_recurrent_step_preact.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P]
+    lib.kda_recurrent_step_preact.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P]
     lib.kda_recurrent_step_preact.restype = I
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libkda.so has ABI {lib.kda_abi_version()}, this binding expects {ABI_VERSION}; "
@@ -211,9 +212,10 @@ def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = Non
 
 def chunk_fwd_preact(q, k, v, a, A_log, dt_bias, b, scale: Optional[float] = None, h0=None, cu_seqlens=None,
                      chunk: int = 64, output_final_state: bool = True, o=None, hT=None, workspace=None,
-                     stream=None):
+                     stream=None, qk_norm: bool = False):
     """Chunked forward with the gates formed in the kernels (kda_chunk_fwd_preact):
-    log_alpha = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b).
+    log_alpha = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b); with qk_norm,
+    q and k are given before silu and per-row L2 normalisation, which the kernels apply.
 
     a [.., H, dk] in q's dtype; A_log [H] fp32; dt_bias [H, dk] fp32; b [.., H] fp32;
     the rest as in chunk_fwd. Returns (o, hT)."""
@@ -257,7 +259,7 @@ def chunk_fwd_preact(q, k, v, a, A_log, dt_bias, b, scale: Optional[float] = Non
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if scale is None:
         scale = dk ** -0.5
-    st = lib.kda_chunk_fwd_preact(B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
+    st = lib.kda_chunk_fwd_preact(KDA_PREACT_QK_NORM if qk_norm else 0, B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
                                   _ptr(dt_bias), _ptr(b), float(scale), _ptr(h0), _ptr(cu_seqlens),
                                   n_seqs if cu_seqlens is not None else 0, _ptr(o), _ptr(hT),
                                   _ptr(workspace), ws_bytes, _stream(stream))
@@ -267,10 +269,10 @@ def chunk_fwd_preact(q, k, v, a, A_log, dt_bias, b, scale: Optional[float] = Non
 
 
 def recurrent_step_preact(q, k, v, a, A_log, dt_bias, b, state, scale: Optional[float] = None, o=None,
-                          stream=None):
+                          stream=None, qk_norm: bool = False):
     """One decode step with the gates formed in the kernel (kda_recurrent_step_preact):
-    a [N, H, dk] in q's dtype; A_log [H]; dt_bias [H, dk]; b [N, H] fp32; state updated
-    in place. Returns o [N, H, dv]."""
+    a [N, H, dk] in q's dtype; A_log [H]; dt_bias [H, dk]; b [N, H] fp32; qk_norm as in
+    chunk_fwd_preact; state updated in place. Returns o [N, H, dv]."""
     import torch
     lib = load()
     dev = q.device
@@ -289,7 +291,7 @@ def recurrent_step_preact(q, k, v, a, A_log, dt_bias, b, state, scale: Optional[
     _check(o, "o", q.dtype, (N, H, dv), dev)
     if scale is None:
         scale = dk ** -0.5
-    st = lib.kda_recurrent_step_preact(N, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
+    st = lib.kda_recurrent_step_preact(KDA_PREACT_QK_NORM if qk_norm else 0, N, H, dk, dv, io, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
                                        _ptr(dt_bias), _ptr(b), float(scale), _ptr(state), _ptr(o),
                                        _stream(stream))
     if st != 0:

@@ -220,12 +220,14 @@ KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d
                           h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes, stream);
 }
 
-KDA_EXPORT int kda_chunk_fwd_preact(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+KDA_EXPORT int kda_chunk_fwd_preact(int flags, int B, int T, int H, int d_k, int d_v, int chunk, int io,
                                     const void *q, const void *k, const void *v,
                                     const void *a, const float *A_log, const float *dt_bias, const float *b,
                                     float scale, const float *h0, const int32_t *cu_seqlens, int n_seqs,
                                     void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream) {
-    return chunk_fwd_impl(kda::kGatePreact, kda::PreactArgs{a, A_log, dt_bias}, B, T, H, d_k, d_v, chunk, io, q,
+    if (flags & ~KDA_PREACT_QK_NORM) return KDA_ERR_INVALID_ARG;
+    const kda::PreactArgs pre{a, A_log, dt_bias, (flags & KDA_PREACT_QK_NORM) ? 1 : 0};
+    return chunk_fwd_impl(kda::kGatePreact, pre, B, T, H, d_k, d_v, chunk, io, q,
                           k, v, nullptr, b, scale, h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes,
                           stream);
 }
@@ -283,11 +285,13 @@ KDA_EXPORT int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v
                                o, stream);
 }
 
-KDA_EXPORT int kda_recurrent_step_preact(int N, int H, int d_k, int d_v, int io,
+KDA_EXPORT int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
                                          const void *q, const void *k, const void *v,
                                          const void *a, const float *A_log, const float *dt_bias, const float *b,
                                          float scale, float *state, void *o, void *stream) {
-    return recurrent_step_impl(kda::kGatePreact, kda::PreactArgs{a, A_log, dt_bias}, N, H, d_k, d_v, io, q, k, v,
+    if (flags & ~KDA_PREACT_QK_NORM) return KDA_ERR_INVALID_ARG;
+    const kda::PreactArgs pre{a, A_log, dt_bias, (flags & KDA_PREACT_QK_NORM) ? 1 : 0};
+    return recurrent_step_impl(kda::kGatePreact, pre, N, H, d_k, d_v, io, q, k, v,
                                nullptr, b, scale, state, o, stream);
 }
 

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
     __shared__ float ks[DK], qs[DK], al[DK];
     __shared__ f32x4 red_k[RG][CG], red_q[RG][CG];
     __shared__ float kq_part[kThreads / 64];
+    __shared__ float ss_part[2][kThreads / 64];  // sums of squares of silu(k), silu(q) (qk_norm)
 
     const int nh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -50,9 +51,15 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
     const T *q = static_cast<const T *>(a.q) + (size_t)nh * DK;
     const T *k = static_cast<const T *>(a.k) + (size_t)nh * DK;
     const T *v = static_cast<const T *>(a.v) + (size_t)nh * DV;
-    float kq = 0.f;
+    float kq = 0.f, ssk = 0.f, ssq = 0.f;
     if (tid < DK) {
-        const float kv = to_f32(k[tid]), qv = to_f32(q[tid]);
+        float kv = to_f32(k[tid]), qv = to_f32(q[tid]);
+        if (a.pre.qk_norm) {  // silu here; the row norms are applied to the sums below
+            kv = silu_f(kv);
+            qv = silu_f(qv);
+            ssk = kv * kv;
+            ssq = qv * qv;
+        }
         ks[tid] = kv;
         qs[tid] = qv;
         if (a.gate == kGatePreact) {  // alpha = exp(-exp(A_log) softplus(a + dt_bias))
@@ -74,6 +81,17 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
     if ((tid & 63) == 0) kq_part[tid >> 6] = kq;
+    if (a.pre.qk_norm) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            ssk += __shfl_xor(ssk, off);
+            ssq += __shfl_xor(ssq, off);
+        }
+        if ((tid & 63) == 0) {
+            ss_part[0][tid >> 6] = ssk;
+            ss_part[1][tid >> 6] = ssq;
+        }
+    }
     __syncthreads();
 
     // 3. decay, and the partial column sums of S~^T k and S~^T q over this thread's rows
@@ -99,6 +117,22 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
     float kqs = 0.f;
 #pragma unroll
     for (int i = 0; i < kThreads / 64; ++i) kqs += kq_part[i];
+    // with qk_norm, k and q are silu(.) / ||silu(.)||: the sums above were taken with
+    // silu(.), and each is linear in k or q
+    float rk_inv = 1.f;
+    if (a.pre.qk_norm) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < kThreads / 64; ++i) {
+            sk += ss_part[0][i];
+            sq += ss_part[1][i];
+        }
+        rk_inv = 1.f / fmaxf(sqrtf(sk), kNormEps);
+        const float rq_inv = 1.f / fmaxf(sqrtf(sq), kNormEps);
+        tk *= rk_inv;
+        tq *= rq_inv;
+        kqs *= rk_inv * rq_inv;
+    }
     const f32x4 e = beta * (vv - tk);
     if (rg == 0) {
         T *o = static_cast<T *>(a.o) + (size_t)nh * DV;
@@ -110,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int it = 0; it < RPT; ++it) {
         const int row = it * RG + rg;
-        __builtin_nontemporal_store(sv[it] + ks[row] * e, &S[row * CG + cg]);
+        __builtin_nontemporal_store(sv[it] + (ks[row] * rk_inv) * e, &S[row * CG + cg]);
     }
 }
 

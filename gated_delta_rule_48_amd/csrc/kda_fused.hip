@@ -74,7 +74,9 @@ struct Lds {
     static constexpr int IDN = KP + kC * kDK * 2;       // [2][64]  bf16x8: each lane's identity operands (ident_frag)
     static constexpr int FLG = IDN + 2 * 64 * 16;       // [2]      int: E E_prev leaves the normal fp32 range
     static constexpr int DTB = FLG + 16;                // [DK]     fp32: dt_bias of the head (pre-activation gates)
-    static constexpr int SIZE = DTB + kDK * 4;
+    static constexpr int QKS = DTB + kDK * 4;           // [2][C][2] fp32: per half, each row's sums of squares of
+                                                        //           silu(k), silu(q) (q and k normalised here)
+    static constexpr int SIZE = QKS + 2 * kC * 2 * 4;
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
@@ -193,8 +195,12 @@ __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb 
 
 template <int G>
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
+    // G: the kda_gate kinds, kGatePreact, and kGatePreactQK (kGatePreact with q and k
+    // normalised here as well)
+    constexpr bool kPreact = G == kGatePreact || G == kGatePreactQK;
+    constexpr bool kQK = G == kGatePreactQK;
     // a decay per key channel, given or formed from pre-activations
-    constexpr bool kPerChannel = G == kGateChannel || G == kGatePreact;
+    constexpr bool kPerChannel = G == kGateChannel || kPreact;
     extern __shared__ __align__(16) unsigned char smem[];
     bf16 *Qp = reinterpret_cast<bf16 *>(smem + Lds::QP);
     bf16 *KtT = reinterpret_cast<bf16 *>(smem + Lds::KTT);
@@ -212,6 +218,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     bf16 *idn = reinterpret_cast<bf16 *>(smem + Lds::IDN);
     int *flg = reinterpret_cast<int *>(smem + Lds::FLG);
     float *dtb = reinterpret_cast<float *>(smem + Lds::DTB);
+    float *qks = reinterpret_cast<float *>(smem + Lds::QKS);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         const int ln = opaque_lane();
         const size_t t0b = tok0_of(ci);
         const unsigned ro = row_off(ci, ln);
-        if constexpr (G == kGatePreact) {
+        if constexpr (kPreact) {
             const bf16 *ap = static_cast<const bf16 *>(a.pre.a) + t0b * kDK + ro * kDK;
 #pragma unroll
             for (int x = 0; x < 2; ++x) gar[x] = load_row8(ap, 2 * hf + x, ln >> 4);
@@ -306,12 +313,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         bta = a.beta[t0b + ro];
     };
-    // pre-activation gates: the head's dt_bias in LDS (read after the loop's first barrier)
-    // and its decay-rate scale exp(A_log)
+    // pre-activation gates: the head's dt_bias in LDS, complete before the first scan reads
+    // it, and its decay-rate scale exp(A_log)
     float eA = 0.f;
-    if constexpr (G == kGatePreact) {
+    if constexpr (kPreact) {
         if (tid < kDK) dtb[tid] = a.pre.dt_bias[(size_t)h * kDK + tid];
         eA = exp2_fast(a.pre.A_log[h] * kL2E);
+        __syncthreads();
     }
     // the identity operands, formed once and read back where a transpose needs them
     // (the first barrier of the loop precedes every read)
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         {
         KDA_PHASE_LANE
         bt = bta;
-        if constexpr (G == kGatePreact) {
+        if constexpr (kPreact) {
             // log alpha = -exp(A_log) softplus(a + dt_bias) (channels 32 kg + 8 hi + e of the
             // row), beta = sigmoid(b); softplus(x) = max(x, 0) + log(1 + e^-|x|)
 #pragma unroll
@@ -361,6 +369,31 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 }
             }
             bt = __builtin_amdgcn_rcpf(1.f + exp2_fast(-bta * kL2E));
+            if constexpr (kQK) {
+                // silu of this chunk's k and q rows (kept, rounded to bf16, for the
+                // elementwise phase) and the sums of their squares over the row's 64
+                // channels of this half: lanes lr + 16 hi hold the row
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    float fk[8], fq[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float kx = static_cast<float>(kr[x][e]), qx = static_cast<float>(qr[x][e]);
+                        fk[e] = kx * __builtin_amdgcn_rcpf(1.f + exp2_fast(-kx * kL2E));
+                        fq[e] = qx * __builtin_amdgcn_rcpf(1.f + exp2_fast(-qx * kL2E));
+                        sk += fk[e] * fk[e];
+                        sq += fq[e] * fq[e];
+                    }
+                    kr[x] = pack8(fk);
+                    qr[x] = pack8(fq);
+                }
+                sk += __shfl_xor(sk, 16);
+                sk += __shfl_xor(sk, 32);
+                sq += __shfl_xor(sq, 16);
+                sq += __shfl_xor(sq, 32);
+                if (hi == 0) *reinterpret_cast<f32x2 *>(qks + (hf * kC + r) * 2) = f32x2{sk, sq};
+            }
         } else {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -411,6 +444,14 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         if (more) load_g(ci + 1);  // decay and beta of this chunk are consumed
         __syncthreads();
+        float rk = 1.f, rq = 1.f;  // inverse row norms of silu(k), silu(q) (kQK)
+        if constexpr (kQK) {
+            KDA_PHASE_LANE
+            const f32x2 s0 = *reinterpret_cast<const f32x2 *>(qks + r * 2);
+            const f32x2 s1 = *reinterpret_cast<const f32x2 *>(qks + (kC + r) * 2);
+            rk = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(s0[0] + s1[0]), kNormEps));
+            rq = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(s0[1] + s1[1]), kNormEps));
+        }
         if (tid < kDK) {
             const float t0v = tot[tid], t1 = tot[kDK + tid], t2 = tot[2 * kDK + tid], t3 = tot[3 * kDK + tid];
             const float gam = (t0v + t1) + (t2 + t3), m = 0.5f * gam;
@@ -449,9 +490,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     const float om = e < 4 ? om0[e] : om1[e - 4];
                     const float d = __builtin_amdgcn_fmed3f(fmaf(g[x][e], kL2E, om), -kClamp, kClamp);
                     const float u = exp2_fast(d), ui = exp2_fast(-d);
-                    const float kv = static_cast<float>(kr[x][e]);
+                    const float kv = kQK ? static_cast<float>(kr[x][e]) * rk : static_cast<float>(kr[x][e]);
+                    const float qv = kQK ? static_cast<float>(qr[x][e]) * rq : static_cast<float>(qr[x][e]);
                     xp[e] = kv * u;
-                    xq[e] = static_cast<float>(qr[x][e]) * u;
+                    xq[e] = qv * u;
                     xm[e] = kv * ui;
                 }
             } else {  // one factor pair for the whole row (none without decay)
@@ -813,7 +855,8 @@ hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seq
     constexpr size_t smem = Lds::SIZE;
     auto kern = a.gate == kGateHead    ? kda_fused_kernel<kGateHead>
                 : a.gate == kGateNone   ? kda_fused_kernel<kGateNone>
-                : a.gate == kGatePreact ? kda_fused_kernel<kGatePreact>
+                : a.gate == kGatePreact ? (a.pre.qk_norm ? kda_fused_kernel<kGatePreactQK>
+                                                         : kda_fused_kernel<kGatePreact>)
                                         : kda_fused_kernel<kGateChannel>;
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

@@ -15,16 +15,23 @@ constexpr int kGateChannel = 0, kGateHead = 1, kGateNone = 2;
 // Gates formed from pre-activations: log_alpha = -exp(A_log[h]) softplus(a + dt_bias[h, c])
 // per key channel (a in the io dtype, [T, H, d_k]) and beta = sigmoid(b).
 constexpr int kGatePreact = 3;
+// kGatePreact with q and k given before silu and per-row L2 normalisation (kernel
+// template argument only; the arguments carry kGatePreact and PreactArgs::qk_norm).
+constexpr int kGatePreactQK = 4;
 
 // softplus(x) = log(1 + e^x) without overflow, and sigmoid(x) = 1 / (1 + e^-x).
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+// silu(x) = x sigmoid(x); rows normalised to unit L2 length with this floor on the norm.
+__device__ __forceinline__ float silu_f(float x) { return x / (1.f + expf(-x)); }
+constexpr float kNormEps = 1e-12f;
 
 // The gate pre-activations' per-head parameters (kGatePreact only).
 struct PreactArgs {
     const void *a;          // [T, H, d_k] io dtype
     const float *A_log;     // [H]
     const float *dt_bias;   // [H, d_k]
+    int qk_norm;            // q and k are given before silu and L2 normalisation per row
 };
 
 // Per-chunk quantities produced by the chunk-preparation kernel and consumed by

@@ -217,6 +217,32 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
         }
     }
+    if (a.pre.qk_norm) {
+        // q, k = silu(.) / ||silu(.)|| over the row, whose channels lie in lanes lr + 16 hi:
+        // the sums of squares by two lane exchanges, then silu again, scaled (rows past the
+        // end are zero and stay zero)
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float x = silu_f(to_f32(kr[kg][e])), y = silu_f(to_f32(qr[kg][e]));
+                sk += x * x;
+                sq += y * y;
+            }
+        sk += __shfl_xor(sk, 16);
+        sk += __shfl_xor(sk, 32);
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        const float rk = 1.f / fmaxf(sqrtf(sk), kNormEps), rq = 1.f / fmaxf(sqrtf(sq), kNormEps);
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                kr[kg][e] = from_f32<T>(silu_f(to_f32(kr[kg][e])) * rk);
+                qr[kg][e] = from_f32<T>(silu_f(to_f32(qr[kg][e])) * rq);
+            }
+    }
     if (valid) b = a.gate == kGatePreact ? sigmoid_f(a.beta[tok]) : a.beta[tok];
     if (hi == 0) bet[r] = b;
 

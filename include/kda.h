@@ -166,6 +166,12 @@ int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chu
  * and no separate pass forms it. softplus(x) = log(1 + e^x), sigmoid(x) =
  * 1 / (1 + e^-x).
  *
+ * With KDA_PREACT_QK_NORM in `flags`, q and k are given before their activation
+ * and normalisation too, and each row is formed as the delta-rule layer of the
+ * essay "22,580: from GPT-2 to Kimi K3" (section 5.2's forward) writes it:
+ * x -> silu(x) / max(||silu(x)||_2, 1e-12) over the head dimension, silu(x) =
+ * x sigmoid(x). Other flag bits are KDA_ERR_INVALID_ARG.
+ *
  * Arguments (others as kda_chunk_fwd; the workspace size is the same):
  *   a        [B*T, H, d_k] dtype io, 16-byte aligned: the decay's pre-activation.
  *   A_log    [H] fp32: per-head log of the decay rate's scale.
@@ -173,7 +179,9 @@ int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chu
  *   b        [B*T, H] fp32: beta's pre-activation.
  * The limit on a chunk's summed log_alpha (>= -170) applies to the formed decay.
  */
-int kda_chunk_fwd_preact(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+enum { KDA_PREACT_QK_NORM = 1 };
+
+int kda_chunk_fwd_preact(int flags, int B, int T, int H, int d_k, int d_v, int chunk, int io,
                          const void *q, const void *k, const void *v,
                          const void *a, const float *A_log, const float *dt_bias, const float *b,
                          float scale, const float *h0, const int32_t *cu_seqlens, int n_seqs,
@@ -212,9 +220,9 @@ int kda_recurrent_step_gated(int gate, int N, int H, int d_k, int d_v, int io,
 /*
  * kda_recurrent_step_preact -- kda_recurrent_step with the gates formed from
  * pre-activations as in kda_chunk_fwd_preact: a [N, H, d_k] dtype io, A_log [H],
- * dt_bias [H, d_k], b [N, H] fp32.
+ * dt_bias [H, d_k], b [N, H] fp32; `flags` as there.
  */
-int kda_recurrent_step_preact(int N, int H, int d_k, int d_v, int io,
+int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
                               const void *q, const void *k, const void *v,
                               const void *a, const float *A_log, const float *dt_bias, const float *b,
                               float scale, float *state, void *o, void *stream);

@@ -171,6 +171,14 @@ def gen_preact(T_total, H, dk, io, seed):
     return dict(a=a, A_log=A_log, dt_bias=dt_bias, b=b)
 
 
+def gen_qk_preact(T_total, H, dk, io, seed):
+    """q and k before their activation and normalisation: N(0,1) [T, H, dk] each, rounded
+    to the io dtype."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0xB1]))
+    return dict(q=_io(rng.standard_normal((T_total, H, dk), dtype=np.float32), io),
+                k=_io(rng.standard_normal((T_total, H, dk), dtype=np.float32), io))
+
+
 def gen_workload(w: Workload, seed: Optional[int] = None):
     return gen_sequences(w.seqlens, w.H, w.dk, w.dv, w.io, w.gates, w.h0,
                          w.seed if seed is None else seed)

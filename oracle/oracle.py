@@ -109,3 +109,17 @@ def gate_prologue(a, A_log, dt_bias, b):
     log_alpha = -np.exp(A_log)[:, None] * np.logaddexp(0.0, a + dt_bias)
     beta = 1.0 / (1.0 + np.exp(-b))
     return log_alpha, beta
+
+
+def qk_prologue(x, eps: float = 1e-12):
+    """q or k from its pre-activation, in fp64, as the delta-rule layer of the essay
+    "22,580: from GPT-2 to Kimi K3" (section 5.2's forward: normalize(silu(.)) over the
+    head dimension, so that a key read back with itself returns its value):
+
+        silu(x) = x / (1 + e^-x),   result = silu(x) / max(||silu(x)||_2, eps)
+
+    over the last axis (eps as torch's normalize)."""
+    x = _f64(x)
+    s = x / (1.0 + np.exp(-x))
+    n = np.sqrt(np.sum(s * s, axis=-1, keepdims=True))
+    return s / np.maximum(n, eps)

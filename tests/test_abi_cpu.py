@@ -168,7 +168,7 @@ def fwd_preact(lib, **kw):
     a = dict(B=2, T=100, H=4, dk=128, dv=128, chunk=64, io=BF16, q=A, k=A, v=A, pa=A, A_log=A, dt_bias=A, b=A,
              scale=0.088, h0=None, cu=None, n_seqs=0, o=0x4000000, hT=None, ws=A, ws_bytes=1 << 40, stream=None)
     a.update(kw)
-    return lib.kda_chunk_fwd_preact(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"], a["k"],
+    return lib.kda_chunk_fwd_preact(a.get("flags", 0), a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"], a["k"],
                                     a["v"], a["pa"], a["A_log"], a["dt_bias"], a["b"], a["scale"], a["h0"], a["cu"],
                                     a["n_seqs"], a["o"], a["hT"], a["ws"], a["ws_bytes"], a["stream"])
 
@@ -178,6 +178,7 @@ def fwd_preact(lib, **kw):
     (dict(pa=A + 8), INVALID), (dict(dt_bias=A + 4), INVALID), (dict(A_log=A + 2), INVALID),
     (dict(o=A), INVALID), (dict(dk=96), UNSUPPORTED),
     (dict(A_log=A + 4, ws=None), WORKSPACE),        # A_log needs 4-byte alignment only: validation goes on
+    (dict(flags=2), INVALID), (dict(flags=1, ws=None), WORKSPACE),
 ])
 def test_chunk_fwd_preact_validation(lib, kw, code):
     assert fwd_preact(lib, **kw) == code
@@ -185,11 +186,12 @@ def test_chunk_fwd_preact_validation(lib, kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(pa=None), INVALID), (dict(A_log=None), INVALID), (dict(dt_bias=A + 4), INVALID), (dict(N=0), OK),
+    (dict(flags=4), INVALID), (dict(flags=1, N=0), OK),
 ])
 def test_recurrent_step_preact_validation(lib, kw, code):
     a = dict(N=4, H=2, dk=128, dv=128, io=BF16, q=A, k=A, v=A, pa=A, A_log=A, dt_bias=A, b=A, scale=0.088,
              state=0x4000000, o=0x8000000, stream=None)
     a.update(kw)
-    assert lib.kda_recurrent_step_preact(a["N"], a["H"], a["dk"], a["dv"], a["io"], a["q"], a["k"], a["v"], a["pa"],
+    assert lib.kda_recurrent_step_preact(a.get("flags", 0), a["N"], a["H"], a["dk"], a["dv"], a["io"], a["q"], a["k"], a["v"], a["pa"],
                                          a["A_log"], a["dt_bias"], a["b"], a["scale"], a["state"], a["o"],
                                          a["stream"]) == code

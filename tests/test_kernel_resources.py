@@ -70,7 +70,7 @@ def test_no_scratch_and_no_spills(resources):
 
 def test_fused_kernel_runs_two_waves_per_simd(resources):
     fused = [r for n, r in resources.items() if "kda_fused_kernel" in n]
-    assert len(fused) == 4  # one per gate kind: per channel, per head, none, from pre-activations
+    assert len(fused) == 5  # per channel, per head, none, from pre-activations (with q, k normalised or not)
     for r in fused:
         assert int(r["Occupancy [waves/SIMD]"]) >= 2, r
         assert int(r["VGPRs"]) <= 256, r

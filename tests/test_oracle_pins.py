@@ -102,3 +102,23 @@ def test_gate_prologue_ranges_and_broadcast():
     for t, h, c in ((0, 0, 0), (6, 2, 3), (3, 1, 2)):
         want = -np.exp(A_log[h]) * np.log1p(np.exp(a[t, h, c] + dt_bias[h, c]))
         assert abs(la[t, h, c] - want) <= 1e-12 * abs(want) + 1e-300
+
+
+def test_qk_prologue():
+    """normalize(silu(x)): unit length along the head dimension; silu(0) = 0, silu(x) ~ x
+    for large x and ~ 0 for very negative x; a zero vector stays zero (the eps floor);
+    and the page's reason for it: a key of unit length reads back exactly the value it
+    wrote (beta = 1, no decay, empty state)."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((5, 3, 16)) * 3
+    y = oracle.qk_prologue(x)
+    assert np.allclose(np.linalg.norm(y, axis=-1), 1.0, atol=1e-14)
+    big = np.array([[30.0, 40.0]])  # silu(x) = x (to e^-30): direction (0.6, 0.8)
+    assert np.allclose(oracle.qk_prologue(big), [[0.6, 0.8]], atol=1e-12)
+    mixed = np.array([[50.0, -50.0, 0.0]])  # silu = (50, ~0, 0)
+    assert np.allclose(oracle.qk_prologue(mixed), [[1.0, 0.0, 0.0]], atol=1e-12)
+    assert np.all(oracle.qk_prologue(np.zeros((2, 4))) == 0.0)
+    k = oracle.qk_prologue(rng.standard_normal((1, 1, 8)))
+    v = rng.standard_normal((1, 1, 5))
+    o, _ = oracle.kda_reference(k, k, v, np.zeros((1, 1, 8)), np.ones((1, 1)), 1.0)
+    assert np.allclose(o, v, atol=1e-14)

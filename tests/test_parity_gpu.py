@@ -372,12 +372,13 @@ def _preact_case(x, io, seed):
     return p, dict(x, log_alpha=la, beta=be)
 
 
+@pytest.mark.parametrize("qk_norm", [False, True])
 @pytest.mark.parametrize("io,path,chunk", [("f32", "split", 64), ("bf16", "split", 64), ("bf16", "split", 128),
                                            ("f32", "split", 128), ("bf16", "fused", 64)])
-def test_preact_gates(io, path, chunk):
+def test_preact_gates(io, path, chunk, qk_norm):
     """kda_chunk_fwd_preact: log alpha = -exp(A_log) softplus(a + dt_bias) and beta =
-    sigmoid(b) formed in the kernels; the oracle runs the recurrence on the same gates
-    formed in fp64."""
+    sigmoid(b) formed in the kernels, and with qk_norm q, k = silu(.) / ||silu(.)|| per
+    row too; the oracle runs the recurrence on the same gates (and q, k) formed in fp64."""
     import torch
     import gated_delta_rule_48_amd as kda
     if path == "fused":
@@ -385,7 +386,12 @@ def test_preact_gates(io, path, chunk):
     else:
         x = gen([200, 130, 1], 4, 128, 128, io, seed=122 + chunk)
     p, y = _preact_case(x, io, seed=123 + chunk)
-    say(f"[preact {path}] io={io} C={chunk}")
+    if qk_norm:
+        T, H, dk = x["q"].shape
+        r = kda_synth.gen_qk_preact(T, H, dk, io, seed=124 + chunk)
+        x = dict(x, q=r["q"], k=r["k"])
+        y = dict(y, q=oracle.qk_prologue(r["q"]), k=oracle.qk_prologue(r["k"]))
+    say(f"[preact {path}] io={io} C={chunk} qk_norm={qk_norm}")
     t = to_dev(x, io)
     iod = torch.bfloat16 if io == "bf16" else torch.float32
     a = torch.from_numpy(p["a"]).cuda().to(iod)
@@ -394,11 +400,11 @@ def test_preact_gates(io, path, chunk):
         B, T = 2, 200
         r = lambda z: z.reshape((B, T) + tuple(z.shape[1:]))  # noqa: E731
         o, hT = kda.chunk_fwd_preact(r(t["q"]), r(t["k"]), r(t["v"]), r(a), A_log, dt_bias, r(b), h0=t["h0"],
-                                     chunk=chunk)
+                                     chunk=chunk, qk_norm=qk_norm)
         o = o.reshape(t["v"].shape)
     else:
         o, hT = kda.chunk_fwd_preact(t["q"], t["k"], t["v"], a, A_log, dt_bias, b, h0=t["h0"],
-                                     cu_seqlens=t["cu_seqlens"], chunk=chunk)
+                                     cu_seqlens=t["cu_seqlens"], chunk=chunk, qk_norm=qk_norm)
     torch.cuda.synchronize()
     o_ref, h_ref, _ = oracle_run(y)
     eo, eh = rel_l2(o.float().cpu().numpy(), o_ref), rel_l2(hT.cpu().numpy(), h_ref)
@@ -406,9 +412,11 @@ def test_preact_gates(io, path, chunk):
     assert eo <= TOL[io] and eh <= TOL[io]
 
 
+@pytest.mark.parametrize("qk_norm", [False, True])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_decode_preact_gates(io):
-    """Five decode steps of kda_recurrent_step_preact against the oracle on the same gates."""
+def test_decode_preact_gates(io, qk_norm):
+    """Five decode steps of kda_recurrent_step_preact against the oracle on the same gates
+    (and, with qk_norm, the same normalised q and k)."""
     import torch
     import gated_delta_rule_48_amd as kda
     N, H, dk, dv, steps = 3, 4, 128, 128, 5
@@ -418,14 +426,20 @@ def test_decode_preact_gates(io):
     got, toks = [], []
     for step in range(steps):
         y = kda_synth.gen_decode_step(N, H, dk, dv, io, "main", 131, step)
+        qk_ref = None
+        if qk_norm:
+            r = kda_synth.gen_qk_preact(N, H, dk, io, 2000 + step)
+            y = dict(y, q=r["q"], k=r["k"])
+            qk_ref = (oracle.qk_prologue(r["q"]), oracle.qk_prologue(r["k"]))
         p = kda_synth.gen_preact(N, H, dk, io, 1000 + step)
         la, be = oracle.gate_prologue(p["a"], p["A_log"], p["dt_bias"], p["b"])
         t = to_dev(dict(y, cu_seqlens=np.zeros(1, np.int32)), io)
         a = torch.from_numpy(p["a"]).cuda().to(iod)
         A_log, dt_bias, b = (torch.from_numpy(p[n]).cuda() for n in ("A_log", "dt_bias", "b"))
-        o = kda.recurrent_step_preact(t["q"], t["k"], t["v"], a, A_log, dt_bias, b, state)
+        o = kda.recurrent_step_preact(t["q"], t["k"], t["v"], a, A_log, dt_bias, b, state, qk_norm=qk_norm)
         got.append(o.float().cpu().numpy())
-        toks.append(dict(q=y["q"], k=y["k"], v=y["v"], log_alpha=la, beta=be))
+        qv, kv = qk_ref if qk_norm else (y["q"], y["k"])
+        toks.append(dict(q=qv, k=kv, v=y["v"], log_alpha=la, beta=be))
     torch.cuda.synchronize()
     # the (n, h) pairs as independent heads of one sequence of `steps` tokens
     seq = {n: np.stack([tk[n].reshape((N * H,) + tk[n].shape[2:]) for tk in toks]) for n in toks[0]}

@@ -153,7 +153,8 @@ def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_sta
     head, or none) and beta (fp32) per token-head, plus the fp32 states read and written."""
     # gates: log_alpha fp32 per key channel, one per token and head, none, or (preact) the
     # decay's pre-activation in the io dtype; then beta (or its pre-activation), fp32
-    per = (2 * dk + 2 * dv) * io_bytes + {"channel": 4 * dk, "head": 4, "none": 0, "preact": io_bytes * dk}[gate] + 4
+    per = (2 * dk + 2 * dv) * io_bytes + {"channel": 4 * dk, "head": 4, "none": 0, "preact": io_bytes * dk,
+                                          "preact_qk": io_bytes * dk}[gate] + 4
     return token_heads * per + 4 * dk * dv * (n_states_out + n_states_in)
 
 
@@ -230,7 +231,11 @@ def bench_workload(args, kda, torch, name):
     elif w.gate == "none":  # no decay
         la = None
     pre = None
-    if w.gate == "preact":  # gates formed in the kernels from pre-activations
+    if w.gate == "preact_qk":  # q and k before silu and normalisation
+        r = kda_synth.gen_qk_preact(sum(w.seqlens), w.H, w.dk, w.io, w.seed)
+        q = torch.from_numpy(r["q"]).to(dev).to(dt).reshape(lead + (w.H, w.dk))
+        k = torch.from_numpy(r["k"]).to(dev).to(dt).reshape(lead + (w.H, w.dk))
+    if w.gate in ("preact", "preact_qk"):  # gates formed in the kernels from pre-activations
         p = kda_synth.gen_preact(sum(w.seqlens), w.H, w.dk, w.io, w.seed)
         pre = dict(a=torch.from_numpy(p["a"]).to(dev).to(dt).reshape(lead + (w.H, w.dk)),
                    A_log=torch.from_numpy(p["A_log"]).to(dev), dt_bias=torch.from_numpy(p["dt_bias"]).to(dev),
@@ -249,7 +254,8 @@ def bench_workload(args, kda, torch, name):
     def step():
         if pre is not None:
             kda.chunk_fwd_preact(q, k, v, pre["a"], pre["A_log"], pre["dt_bias"], pre["b"], scale=w.scale, h0=h0,
-                                 cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT, workspace=ws)
+                                 cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT, workspace=ws,
+                                 qk_norm=w.gate == "preact_qk")
         else:
             kda.chunk_fwd(q, k, v, la, beta, scale=w.scale, h0=h0, cu_seqlens=cu, chunk=w.chunk, o=o, hT=hT,
                           workspace=ws)
@@ -276,7 +282,8 @@ def bench_workload(args, kda, torch, name):
             "kernel": PATHS[path]["kernel"],
             "workload": f"seqlens {list(w.seqlens)}, H={w.H}, d_k=d_v={w.dk}, chunk {w.chunk}, {w.io} q/k/v/o, "
                         + {"channel": "decay per key channel", "head": "decay per token and head", "none": "no decay",
-                           "preact": "gates formed in the kernel from pre-activations"}[w.gate],
+                           "preact": "gates formed in the kernel from pre-activations",
+                           "preact_qk": "gates, and q and k (silu, L2 norm), formed in the kernel"}[w.gate],
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
 

@@ -17,7 +17,8 @@ Workloads (sizes from the five benchmark configurations of this library):
   batched_gdn, batched_deltanet: the batched workload with the decay given per token
            and head (the first key channel's draw) or not at all (`gate`)
   batched_preact: the batched workload with gate pre-activations (gen_preact) instead
-           of log alpha and beta
+           of log alpha and beta; batched_preact_qk: also q and k before silu and
+           normalisation (gen_qk_preact)
 
 Gate families (log alpha is drawn per token, per head and per key channel):
   weak:  log alpha = -0.1 * softplus(N(0,1)),  beta = sigmoid(N(0,1))
@@ -51,8 +52,9 @@ class Workload:
     gates: str              # "weak", "main" (or "strong" in tests)
     h0: str                 # "zero" or "normal"
     seed: int
-    gate: str = "channel"   # decays given to the library: "channel", "head", "none", or "preact"
-                            # (formed in the kernels from gen_preact's pre-activations)
+    gate: str = "channel"   # decays given to the library: "channel", "head", "none", "preact"
+                            # (formed in the kernels from gen_preact's pre-activations) or
+                            # "preact_qk" (q and k from gen_qk_preact too)
 
     @property
     def T_total(self) -> int:
@@ -83,6 +85,9 @@ WORKLOADS = {
     # the batched workload with its gates formed in the kernels from pre-activations (gen_preact)
     "batched_preact": Workload("batched_preact", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002,
                                "preact"),
+    # ... and q, k given before silu and per-row L2 normalisation too (gen_qk_preact)
+    "batched_preact_qk": Workload("batched_preact_qk", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero",
+                                  1002, "preact_qk"),
 }
 
 # Decode: N sequences x H heads, one token per step.

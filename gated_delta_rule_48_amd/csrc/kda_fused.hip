@@ -75,8 +75,9 @@ struct Lds {
     static constexpr int FLG = IDN + 2 * 64 * 16;       // [2]      int: E E_prev leaves the normal fp32 range
     static constexpr int DTB = FLG + 16;                // [DK]     fp32: dt_bias of the head (pre-activation gates)
     static constexpr int QKS = DTB + kDK * 4;           // [2][C][2] fp32: per half, each row's sums of squares of
-                                                        //           silu(k), silu(q) (q and k normalised here)
-    static constexpr int SIZE = QKS + 2 * kC * 2 * 4;
+                                                        //           silu(k) (scan phase), silu(q) (elementwise phase)
+    static constexpr int QNR = QKS + 2 * kC * 2 * 4;   // [C] fp32: inverse norms of the rows of silu(q)
+    static constexpr int SIZE = QNR + kC * 4;
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     int *flg = reinterpret_cast<int *>(smem + Lds::FLG);
     float *dtb = reinterpret_cast<float *>(smem + Lds::DTB);
     float *qks = reinterpret_cast<float *>(smem + Lds::QKS);
+    float *qnr = reinterpret_cast<float *>(smem + Lds::QNR);
 
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
@@ -370,29 +372,26 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             }
             bt = __builtin_amdgcn_rcpf(1.f + exp2_fast(-bta * kL2E));
             if constexpr (kQK) {
-                // silu of this chunk's k and q rows (kept, rounded to bf16, for the
-                // elementwise phase) and the sums of their squares over the row's 64
-                // channels of this half: lanes lr + 16 hi hold the row
-                float sk = 0.f, sq = 0.f;
+                // silu of this chunk's key rows (kept, rounded to bf16, for the
+                // elementwise phase) and the sum of their squares over the row's 64
+                // channels of this half: lanes lr + 16 hi hold the row. The query rows
+                // follow in the elementwise phase: their norm is only needed from the
+                // Gram phase on, and it scales rows of Aqk and of O.
+                float sk = 0.f;
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
-                    float fk[8], fq[8];
+                    float fk[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float kx = static_cast<float>(kr[x][e]), qx = static_cast<float>(qr[x][e]);
+                        const float kx = static_cast<float>(kr[x][e]);
                         fk[e] = kx * __builtin_amdgcn_rcpf(1.f + exp2_fast(-kx * kL2E));
-                        fq[e] = qx * __builtin_amdgcn_rcpf(1.f + exp2_fast(-qx * kL2E));
                         sk += fk[e] * fk[e];
-                        sq += fq[e] * fq[e];
                     }
                     kr[x] = pack8(fk);
-                    qr[x] = pack8(fq);
                 }
                 sk += __shfl_xor(sk, 16);
                 sk += __shfl_xor(sk, 32);
-                sq += __shfl_xor(sq, 16);
-                sq += __shfl_xor(sq, 32);
-                if (hi == 0) *reinterpret_cast<f32x2 *>(qks + (hf * kC + r) * 2) = f32x2{sk, sq};
+                if (hi == 0) qks[(hf * kC + r) * 2] = sk;
             }
         } else {
 #pragma unroll
@@ -444,13 +443,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         if (more) load_g(ci + 1);  // decay and beta of this chunk are consumed
         __syncthreads();
-        float rk = 1.f, rq = 1.f;  // inverse row norms of silu(k), silu(q) (kQK)
+        float rk = 1.f;  // inverse row norm of silu(k) (kQK)
         if constexpr (kQK) {
             KDA_PHASE_LANE
-            const f32x2 s0 = *reinterpret_cast<const f32x2 *>(qks + r * 2);
-            const f32x2 s1 = *reinterpret_cast<const f32x2 *>(qks + (kC + r) * 2);
-            rk = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(s0[0] + s1[0]), kNormEps));
-            rq = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(s0[1] + s1[1]), kNormEps));
+            rk = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(qks[r * 2] + qks[(kC + r) * 2]), kNormEps));
         }
         if (tid < kDK) {
             const float t0v = tot[tid], t1 = tot[kDK + tid], t2 = tot[2 * kDK + tid], t3 = tot[3 * kDK + tid];
@@ -475,6 +471,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         bf16x8 kpf[2], qpf[2];
         {
         KDA_PHASE_LANE
+        float sq = 0.f;  // sum of squares of silu(q) over the lane's channels (kQK)
         const bf16x8 id0 = *reinterpret_cast<const bf16x8 *>(idn + l * 8);
         const bf16x8 id1 = *reinterpret_cast<const bf16x8 *>(idn + (64 + l) * 8);
 #pragma unroll
@@ -491,7 +488,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                     const float d = __builtin_amdgcn_fmed3f(fmaf(g[x][e], kL2E, om), -kClamp, kClamp);
                     const float u = exp2_fast(d), ui = exp2_fast(-d);
                     const float kv = kQK ? static_cast<float>(kr[x][e]) * rk : static_cast<float>(kr[x][e]);
-                    const float qv = kQK ? static_cast<float>(qr[x][e]) * rq : static_cast<float>(qr[x][e]);
+                    float qv = static_cast<float>(qr[x][e]);
+                    if constexpr (kQK) {  // silu(q); its row norm is applied to Aqk and O
+                        qv *= __builtin_amdgcn_rcpf(1.f + exp2_fast(-qv * kL2E));
+                        sq = fmaf(qv, qv, sq);
+                    }
                     xp[e] = kv * u;
                     xq[e] = qv * u;
                     xm[e] = kv * ui;
@@ -528,6 +529,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 store_slots(Vt, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1, Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0), l);
+        if constexpr (kQK) {
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            if (hi == 0) qks[(hf * kC + r) * 2 + 1] = sq;
+        }
         }
         if (more) load_k(ci + 1);  // key rows consumed
         __syncthreads();  // Kp, Qp, Km, Km^T, Kp^T, v^T complete
@@ -597,6 +603,16 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) ka[kg] = fld(Kp, kg, rb, kC, l);
             const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
+            // Aqk's scale, times the inverse norm of silu(q)'s row 16 rq + lr (kQK; kept
+            // for the state phase's O)
+            float aqs = scale;
+            if constexpr (kQK) {
+                const int qrow = 16 * rq + lr;
+                const float n = __builtin_amdgcn_rcpf(
+                    fmaxf(__builtin_sqrtf(qks[qrow * 2 + 1] + qks[(kC + qrow) * 2 + 1]), kNormEps));
+                if (hi == 0) qnr[qrow] = n;
+                aqs *= n;
+            }
             bf16x8 kmb[2][4];
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) kmb[0][kg] = fld(Km, kg, 0, kC, l);
@@ -620,7 +636,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
                         for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, kmb[tj & 1][kg], qb[kg]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] *= scale;
+                        for (int i = 0; i < 4; ++i) acc[i] *= aqs;
                         if (tj == rq) {  // the diagonal tile: i <= r only (the others lie below it)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) acc[i] = (4 * hi + i <= lr) ? acc[i] : 0.f;
@@ -807,7 +823,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 f32x4 ot = zero4;
 #pragma unroll
                 for (int kg = 0; kg < 4; ++kg) ot = Frag<bf16>::mma(ot, sb[kg], fa[rr & 1][kg]);
-                ot *= scale;
+                ot *= kQK ? scale * qnr[16 * rr + lr] : scale;
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
                     if (kc <= (rr >> 1)) ot = Frag<bf16>::mma(ot, ub[kc], aq[kc]);

@@ -332,6 +332,48 @@ def bench_decode(args, kda, torch):
     return dict(ms=ms, tokens_per_s=N / (ms * 1e-3), alg_bytes=alg, achieved_gbs=achieved, steps=n)
 
 
+def bench_attn(args, kda, torch, name, dec):
+    """The comparator: a softmax-attention layer's decode step over a KV cache
+    (kda_attn_decode), one new token per sequence, caches drawn on the GPU."""
+    B, H, H_kv, T_max, d, io, seed = kda_synth.ATTN_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating attention workload {name}: B={B} H={H} H_kv={H_kv} T_max={T_max} d={d} {io}")
+    x = kda_synth.gen_attn_decode_device(B, H, H_kv, T_max, d, torch.bfloat16, seed, dev)
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    n_ws = kda.attn_decode_workspace_bytes(B, H, H_kv, d, T_max, kda.KDA_BF16)
+    ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.attn_decode(x["q"], x["k_cache"], x["v_cache"], o=o, workspace=ws)
+
+    spin_up(torch, step, args.spin_up)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    n = args.attn_steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / n
+    alg = B * H_kv * T_max * d * 2 * 2 + 2 * B * H * d * 2  # both caches read once; q read, o written
+    achieved = alg / (ms * 1e-3) / 1e9
+    log(f"[bench] attention decode {name}: {ms * 1000:.1f} us/step, {B / (ms * 1e-3):.3e} tokens/s, "
+        f"{achieved:.0f} GB/s")
+    out = {"value": B / (ms * 1e-3), "unit": "tokens/s", "us_per_step": round(ms * 1000, 2), "steps": n,
+           "workload": f"{B} sequences x {H} query heads ({H_kv} cached), d={d}, {T_max} cached rows each, "
+                       "bf16 caches",
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
+    if dec is not None and name == "attn_batched":  # the same 256 x 32 (sequence, head) pairs
+        out["time_vs_kda_decode"] = round(ms / dec["ms"], 2)
+    del x, o, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(pre, args):
     """The fp64 oracle on the prefill workload's first `--cpu-seqs` sequences (all
     of them by default: all heads, full length), on this host's cores."""
@@ -372,6 +414,10 @@ def main():
                     help="log the streaming bandwidth of device copies and in-place multiplies first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--attn", default="attn_batched", metavar="NAMES",
+                    help="attention-decode comparator workloads to time (" + ", ".join(kda_synth.ATTN_WORKLOADS) +
+                         "; empty for none)")
+    ap.add_argument("--attn-steps", type=int, default=50)
     ap.add_argument("--workloads", default="", metavar="NAMES",
                     help="comma-separated further prefill workloads to time and report (" +
                          ", ".join(n for n in kda_synth.WORKLOADS if n != "batched") + ")")
@@ -393,6 +439,7 @@ def main():
     pre = bench_prefill(args, kda, torch)
     dec = None if args.no_decode else bench_decode(args, kda, torch)
     others = {n: bench_workload(args, kda, torch, n) for n in args.workloads.split(",") if n}
+    attn = {n: bench_attn(args, kda, torch, n, dec) for n in args.attn.split(",") if n}
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
 
     w = pre["workload"]
@@ -427,6 +474,8 @@ def main():
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(dec["achieved_gbs"] / HBM_PEAK_GBS, 4),
                                        "alg_bytes_per_launch": dec["alg_bytes"]}}
+    if attn:
+        line["attn_decode"] = attn
     if others:
         line["workloads"] = others
     print(json.dumps(line), flush=True)

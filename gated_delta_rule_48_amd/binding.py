@@ -22,8 +22,9 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
           4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_preact", "kda_recurrent_step",
-           "kda_recurrent_step_gated", "kda_recurrent_step_preact")
-ABI_VERSION = 2
+           "kda_recurrent_step_gated", "kda_recurrent_step_preact", "kda_attn_decode_workspace_bytes",
+           "kda_attn_decode")
+ABI_VERSION = 3
 
 
 class KdaError(RuntimeError):
@@ -63,6 +64,10 @@ def load() -> ctypes.CDLL:
     lib.kda_recurrent_step_gated.restype = I
     lib.kda_recurrent_step_preact.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P]
     lib.kda_recurrent_step_preact.restype = I
+    lib.kda_attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.kda_attn_decode_workspace_bytes.restype = Z
+    lib.kda_attn_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, F, P, P, Z, P]
+    lib.kda_attn_decode.restype = I
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libkda.so has ABI {lib.kda_abi_version()}, this binding expects {ABI_VERSION}; "
                            "rebuild it")
@@ -296,4 +301,40 @@ def recurrent_step_preact(q, k, v, a, A_log, dt_bias, b, state, scale: Optional[
                                        _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_recurrent_step_preact")
+    return o
+
+
+def attn_decode_workspace_bytes(B, H, H_kv, d, T_max, io) -> int:
+    return int(load().kda_attn_decode_workspace_bytes(B, H, H_kv, d, T_max, io))
+
+
+def attn_decode(q, k_cache, v_cache, seq_lens=None, scale: Optional[float] = None, o=None, workspace=None,
+                stream=None):
+    """Softmax attention of one new token per sequence over a KV cache (kda_attn_decode):
+    q [B, H, d]; k_cache, v_cache [B, H_kv, T_max, d] in q's dtype (the new token's key and
+    value already in row seq_lens[b] - 1); seq_lens [B] int32 or None (all T_max rows).
+    Query head h reads cached head h // (H // H_kv). Returns o [B, H, d]."""
+    import torch
+    lib = load()
+    dev = q.device
+    io = _io_code(q.dtype)
+    B, H, d = q.shape
+    H_kv, T_max = k_cache.shape[1], k_cache.shape[2]
+    _check(k_cache, "k_cache", q.dtype, (B, H_kv, T_max, d), dev)
+    _check(v_cache, "v_cache", q.dtype, (B, H_kv, T_max, d), dev)
+    if seq_lens is not None:
+        _check(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if o is None:
+        o = torch.empty((B, H, d), dtype=q.dtype, device=dev)
+    _check(o, "o", q.dtype, (B, H, d), dev)
+    need = int(lib.kda_attn_decode_workspace_bytes(B, H, H_kv, d, T_max, io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = d ** -0.5
+    st = lib.kda_attn_decode(B, H, H_kv, d, T_max, io, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                             float(scale), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_attn_decode")
     return o

@@ -2,6 +2,8 @@
 // workspace layout and kernel dispatch. Host code only; it never synchronises.
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "../../include/kda.h"
@@ -301,4 +303,90 @@ KDA_EXPORT int kda_recurrent_step(int N, int H, int d_k, int d_v, int io,
                                   float *state, void *o, void *stream) {
     return kda_recurrent_step_gated(KDA_GATE_CHANNEL, N, H, d_k, d_v, io, q, k, v, log_alpha, beta, scale,
                                     state, o, stream);
+}
+
+namespace {
+
+// Splits of the attention decode's cache: enough workgroups to fill the chip
+// several times over, each over at least kAttnMinSplit rows (its fixed costs are
+// the query, one merge and one partial write), in whole iterations.
+constexpr int64_t kAttnTargetGroups = 4096;
+constexpr int64_t kAttnMinSplit = 1024;
+
+struct AttnSplit {
+    int n, len;
+};
+
+AttnSplit attn_split(int B, int H_kv, int D, int T_max) {
+    const int64_t rows = kda::attn_rows_per_iter(D);
+    if (T_max <= 0) return {1, (int)rows};
+    const int64_t units = (int64_t)B * H_kv;
+    int64_t n = (kAttnTargetGroups + units - 1) / units;
+    n = std::min<int64_t>(n, std::max<int64_t>(1, T_max / kAttnMinSplit));
+    n = std::max<int64_t>(n, 1);
+    const int64_t L = ((T_max + n - 1) / n + rows - 1) / rows * rows;
+    return {(int)((T_max + L - 1) / L), (int)L};
+}
+
+int check_attn(int B, int H, int H_kv, int d, int T_max, int io) {
+    if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || H < 1 || H_kv < 1 || T_max < 0 || H % H_kv != 0) return KDA_ERR_INVALID_ARG;
+    const int G = H / H_kv;
+    if (!supported_dim(d) || (G != 1 && G != 2 && G != 4)) return KDA_ERR_UNSUPPORTED;
+    // grid limits, and 32-bit row offsets within one cached head
+    if (B > 65535 || H_kv > 65535 || (int64_t)T_max * d > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+size_t attn_ws_bytes(int B, int H, int d, const AttnSplit &sp, size_t *ml_off) {
+    if (sp.n <= 1) {
+        *ml_off = 0;
+        return 0;
+    }
+    const size_t n = (size_t)B * H * sp.n;
+    *ml_off = round_up(n * d * sizeof(float), 256);
+    return *ml_off + round_up(n * 2 * sizeof(float), 256);
+}
+
+}  // namespace
+
+KDA_EXPORT size_t kda_attn_decode_workspace_bytes(int B, int H, int H_kv, int d, int T_max, int io) {
+    if (check_attn(B, H, H_kv, d, T_max, io) != KDA_OK || B == 0) return 0;
+    size_t ml_off;
+    return attn_ws_bytes(B, H, d, attn_split(B, H_kv, d, T_max), &ml_off);
+}
+
+KDA_EXPORT int kda_attn_decode(int B, int H, int H_kv, int d, int T_max, int io, const void *q,
+                               const void *k_cache, const void *v_cache, const int32_t *seq_lens, float scale,
+                               void *o, void *workspace, size_t workspace_bytes, void *stream) {
+    const int st = check_attn(B, H, H_kv, d, T_max, io);
+    if (st != KDA_OK) return st;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (B == 0) return KDA_OK;
+    if (!q || !o || (T_max > 0 && (!k_cache || !v_cache))) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(seq_lens, 4))
+        return KDA_ERR_INVALID_ARG;
+    const size_t esz = io == KDA_BF16 ? 2 : 4;
+    const size_t o_bytes = (size_t)B * H * d * esz, cache_bytes = (size_t)B * H_kv * T_max * d * esz;
+    if (overlaps(o, o_bytes, q, o_bytes) || overlaps(o, o_bytes, k_cache, cache_bytes) ||
+        overlaps(o, o_bytes, v_cache, cache_bytes) || overlaps(o, o_bytes, seq_lens, (size_t)B * 4))
+        return KDA_ERR_INVALID_ARG;
+    const AttnSplit sp = attn_split(B, H_kv, d, T_max);
+    size_t ml_off;
+    const size_t need = attn_ws_bytes(B, H, d, sp, &ml_off);
+    float *part_acc = nullptr, *part_ml = nullptr;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+        if (overlaps(workspace, need, o, o_bytes) || overlaps(workspace, need, q, o_bytes) ||
+            overlaps(workspace, need, k_cache, cache_bytes) || overlaps(workspace, need, v_cache, cache_bytes))
+            return KDA_ERR_INVALID_ARG;
+        part_acc = static_cast<float *>(workspace);
+        part_ml = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + ml_off);
+    }
+    const kda::AttnArgs a{q, k_cache, v_cache, seq_lens, scale, o, part_acc, part_ml,
+                          H_kv, H / H_kv, T_max, sp.len, sp.n};
+    if (kda::launch_attn_decode(a, B, d, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
 }

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -226,6 +226,50 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
                               const void *q, const void *k, const void *v,
                               const void *a, const float *A_log, const float *dt_bias, const float *b,
                               float scale, float *state, void *o, void *stream);
+
+/*
+ * Full-attention decode over a KV cache: the comparator of the decode step
+ * -----------------------------------------------------------------------
+ * The step that a softmax-attention layer takes for each new token, against
+ * which kda_recurrent_step is measured. The essay "22,580: from GPT-2 to Kimi
+ * K3" defines causal softmax attention in section 2.2 and the KV cache in
+ * section 2.3: at decode time the keys and values of all earlier positions are
+ * kept, and the new token's query is compared with every one of them. The "ten
+ * questions" page (Q10) counts the cost: the cache grows by one key and one
+ * value per token and per head, and every decode step reads all of it, while
+ * KDA keeps one d_k x d_v state per head.
+ *
+ *   o[b, h] = sum_{t < len_b} w_t v_cache[b, j, t],
+ *   w_t = exp(s_t) / sum_{t' < len_b} exp(s_t'),  s_t = scale q[b, h] . k_cache[b, j, t],
+ *   j = h / (H / H_kv)   (consecutive query heads share a cached head; H_kv = H
+ *                         is multi-head attention)
+ *
+ * Arguments
+ *   B, H, H_kv  sequences, query heads, cached heads; H % H_kv == 0 and
+ *               H / H_kv in {1, 2, 4}; B <= 65535, H_kv <= 65535.
+ *   d           head dimension, 64 or 128 (queries, keys and values).
+ *   T_max       rows allocated per cached head; T_max * d < 2^31.
+ *   io          dtype of q, the caches and o (KDA_F32 or KDA_BF16).
+ *   q           [B, H, d];  o [B, H, d] (must not overlap any input).
+ *   k_cache, v_cache  [B, H_kv, T_max, d], row t of a head = position t. The
+ *               new token's key and value are expected in the cache already
+ *               (row len_b - 1): the query attends to itself.
+ *   seq_lens    [B] int32, rows in use per sequence (len_b), or NULL for
+ *               T_max everywhere. Values are clamped to [0, T_max]; rows at
+ *               and past len_b are never read. len_b = 0 gives o = 0.
+ *   scale       the score scale (d^{-1/2} for the usual attention).
+ *   workspace   kda_attn_decode_workspace_bytes(B, H, H_kv, d, T_max, io)
+ *               bytes, 256-byte aligned (NULL allowed when that is 0): the
+ *               partial results when a cache is split over several workgroups.
+ * Scores are formed in fp32 with the usual running-maximum rescaling, so any
+ * finite scores are safe. Errors as for the other entry points.
+ */
+size_t kda_attn_decode_workspace_bytes(int B, int H, int H_kv, int d, int T_max, int io);
+
+int kda_attn_decode(int B, int H, int H_kv, int d, int T_max, int io,
+                    const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *seq_lens, float scale, void *o,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,16 @@ Gate families (log alpha is drawn per token, per head and per key channel):
 q and k are N(0,1) vectors L2-normalised per (token, head); v ~ N(0,1).
 "N(mu, s)" means standard deviation s.
 
+Attention-decode comparator (a softmax-attention layer's decode step over a KV
+cache, weighed against the KDA decode step; ATTN_WORKLOADS):
+  attn_batched  B=256 sequences, H = H_kv = 32, d=128, T_max=4096 cached rows, bf16:
+                the decode workload's 256 x 32 (sequence, head) pairs at a 4K context
+  attn_1m       B=1, H = H_kv = 32, d=128, T_max=1,048,576 (a one-million-token context)
+q ~ N(0,1), keys ~ N(0, 2^2) (scores of standard deviation 2 at scale d^-1/2, so the
+softmax is neither flat nor one-hot), values ~ N(0,1). gen_attn_decode draws them on
+the host (numpy) for the sizes an fp64 check covers; gen_attn_decode_device draws the
+full-size caches on the GPU with torch's seeded generator.
+
 Layout of every array: token-major and packed, [T_total, H, d]; gates
 [T_total, H, d_k] and [T_total, H]; states [n_seqs, H, d_k, d_v] row-major
 (row = key channel). Batched workloads are packed sequences of equal length.
@@ -182,6 +192,37 @@ def gen_qk_preact(T_total, H, dk, io, seed):
     rng = np.random.Generator(np.random.PCG64([seed, 0xB1]))
     return dict(q=_io(rng.standard_normal((T_total, H, dk), dtype=np.float32), io),
                 k=_io(rng.standard_normal((T_total, H, dk), dtype=np.float32), io))
+
+
+ATTN_WORKLOADS = {
+    # name: (B, H, H_kv, T_max, d, io, seed)
+    "attn_batched": (256, 32, 32, 4096, 128, "bf16", 1005),
+    "attn_1m": (1, 32, 32, 1 << 20, 128, "bf16", 1006),
+}
+
+
+def gen_attn_decode(B, H, H_kv, T_max, d, io, seed):
+    """q [B, H, d] ~ N(0,1), k_cache ~ N(0, 2^2) and v_cache ~ N(0,1) [B, H_kv, T_max, d],
+    rounded to the io dtype (numpy; fp32 arrays holding bf16 values for "bf16")."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0xA1]))
+    q = _io(rng.standard_normal((B, H, d), dtype=np.float32), io)
+    k = _io(2.0 * rng.standard_normal((B, H_kv, T_max, d), dtype=np.float32), io)
+    v = _io(rng.standard_normal((B, H_kv, T_max, d), dtype=np.float32), io)
+    return dict(q=q, k_cache=k, v_cache=v)
+
+
+def gen_attn_decode_device(B, H, H_kv, T_max, d, dtype, seed, device):
+    """The same distributions drawn on the GPU (torch's seeded generator), for caches too
+    large to draw on the host: q [B, H, d], k_cache, v_cache [B, H_kv, T_max, d] in dtype."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    k = torch.empty((B, H_kv, T_max, d), device=device, dtype=dtype)
+    v = torch.empty((B, H_kv, T_max, d), device=device, dtype=dtype)
+    k.normal_(0.0, 2.0, generator=g)
+    v.normal_(0.0, 1.0, generator=g)
+    return dict(q=q, k_cache=k, v_cache=v)
 
 
 def gen_workload(w: Workload, seed: Optional[int] = None):

@@ -3,4 +3,5 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package. The GPU library never calls it and shares no code with it.
 """
-from .oracle import build, gate_prologue, kda_reference, library_path, qk_prologue  # noqa: F401
+from .oracle import (attn_decode_reference, build, gate_prologue, kda_reference, library_path,  # noqa: F401
+                     qk_prologue)

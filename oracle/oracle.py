@@ -4,7 +4,9 @@ The oracle itself is plain C in kda_oracle.c: a token-by-token fp64 loop of
 the KDA gated delta rule. This wrapper only converts arrays to contiguous fp64
 and calls it. It is "parity pinned": tests/test_oracle_pins.py ties it to the
 worked 2x2 examples of the "ten questions" page and to closed forms, brute
-force and invariants.
+force and invariants. The prologue functions and the softmax-attention decode
+step (the comparator of the KDA decode step) are numpy in fp64 here, each
+pinned the same way.
 """
 from __future__ import annotations
 
@@ -123,3 +125,35 @@ def qk_prologue(x, eps: float = 1e-12):
     s = x / (1.0 + np.exp(-x))
     n = np.sqrt(np.sum(s * s, axis=-1, keepdims=True))
     return s / np.maximum(n, eps)
+
+
+def attn_decode_reference(q, k_cache, v_cache, seq_lens=None, scale: float = None):
+    """Softmax attention of one new token per sequence over a KV cache, in fp64: the
+    causal softmax attention of the essay "22,580: from GPT-2 to Kimi K3" (section 2.2)
+    for the newest position, against the keys and values kept for all positions so far
+    (its section 2.3, the KV cache). For each sequence b and query head h, with cached
+    head j = h // (H // H_kv) and len = seq_lens[b] (all T_max rows if None):
+
+        s_t = scale * q[b, h] . k_cache[b, j, t]          (t < len)
+        o[b, h] = sum_t exp(s_t) v_cache[b, j, t] / sum_t exp(s_t)
+
+    computed with the largest s_t subtracted first (the same value, without overflow).
+    An empty cache (len = 0) gives o = 0. q [B, H, d]; caches [B, H_kv, T_max, d];
+    scale defaults to d^-1/2. Returns o [B, H, d] fp64."""
+    q, K, V = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, H, d = q.shape
+    H_kv, T_max = K.shape[1], K.shape[2]
+    G = H // H_kv
+    if scale is None:
+        scale = d ** -0.5
+    o = np.zeros((B, H, d))
+    for b in range(B):
+        n = T_max if seq_lens is None else min(max(int(seq_lens[b]), 0), T_max)
+        if n == 0:
+            continue
+        for h in range(H):
+            j = h // G
+            s = scale * (K[b, j, :n] @ q[b, h])
+            w = np.exp(s - s.max())
+            o[b, h] = (w @ V[b, j, :n]) / w.sum()
+    return o

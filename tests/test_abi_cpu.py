@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing, misaligned or too small")]:
         assert lib.kda_status_string(code) == text
     assert lib.kda_status_string(99) == b"unknown status"
@@ -195,3 +195,50 @@ def test_recurrent_step_preact_validation(lib, kw, code):
     assert lib.kda_recurrent_step_preact(a.get("flags", 0), a["N"], a["H"], a["dk"], a["dv"], a["io"], a["q"], a["k"], a["v"], a["pa"],
                                          a["A_log"], a["dt_bias"], a["b"], a["scale"], a["state"], a["o"],
                                          a["stream"]) == code
+
+
+# ---- softmax-attention decode over a KV cache (kda_attn_decode)
+
+def attn(lib, **kw):
+    a = dict(B=2, H=4, H_kv=2, d=128, T_max=100, io=BF16, q=A, k=0x4000000, v=0x8000000, lens=None, scale=0.088,
+             o=0xC000000, ws=A, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_attn_decode(a["B"], a["H"], a["H_kv"], a["d"], a["T_max"], a["io"], a["q"], a["k"], a["v"],
+                               a["lens"], a["scale"], a["o"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), OK),                                       # nothing to do, nothing launched
+    (dict(B=-1), INVALID), (dict(H=0), INVALID), (dict(H_kv=0), INVALID), (dict(T_max=-1), INVALID),
+    (dict(H=6, H_kv=4), INVALID),                          # H % H_kv != 0
+    (dict(H=16, H_kv=2), UNSUPPORTED),                     # groups of 8 query heads
+    (dict(H=6, H_kv=2), UNSUPPORTED),                      # groups of 3
+    (dict(d=96), UNSUPPORTED), (dict(io=2), UNSUPPORTED),
+    (dict(B=65536, H=2, H_kv=2, T_max=1), UNSUPPORTED),    # grid limit
+    (dict(T_max=1 << 24), UNSUPPORTED),                    # T_max * d >= 2^31
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(q=A + 8), INVALID), (dict(k=0x4000000 + 4), INVALID), (dict(lens=A + 2), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(o=0x4000000 + 4096), INVALID),                   # o inside the key cache
+    (dict(o=A), INVALID),                                  # o is q
+])
+def test_attn_decode_rejects(lib, kw, code):
+    assert attn(lib, **kw) == code
+
+
+def test_attn_decode_workspace(lib):
+    ws = lib.kda_attn_decode_workspace_bytes
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # one million rows of 32 heads: 4096 / 32 = 128 splits of 8192 rows
+    assert ws(1, 32, 32, 128, 1 << 20, BF16) == r(32 * 128 * 128 * 4) + r(32 * 128 * 2 * 4)
+    # 256 x 32 heads fill the chip alone (one split each): no workspace
+    assert ws(256, 32, 32, 128, 4096, BF16) == 0
+    # short caches are not split below 1024 rows
+    assert ws(1, 4, 4, 64, 1023, F32) == 0
+    # 5000 rows of 2 x 2 cached heads (4 query heads each): 4 splits of 1280 rows
+    assert ws(2, 4, 2, 128, 5000, BF16) == r(2 * 4 * 4 * 128 * 4) + r(2 * 4 * 4 * 2 * 4)
+    assert ws(0, 4, 2, 128, 5000, BF16) == 0 and ws(2, 4, 3, 128, 5000, BF16) == 0
+    # the workspace is checked only when one is needed
+    assert attn(lib, T_max=5000, ws=None) == WORKSPACE
+    assert attn(lib, T_max=5000, ws=A + 16) == WORKSPACE
+    assert attn(lib, T_max=5000, ws_bytes=1000) == WORKSPACE

@@ -18,7 +18,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
-SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip"]
+SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip", "kda_attn.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
@@ -57,7 +57,7 @@ def resources():
 def test_every_kernel_is_reported(resources):
     names = " ".join(resources)
     for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_decode_kernel",
-              "kda_chunk_offsets_kernel"):
+              "kda_chunk_offsets_kernel", "kda_attn_decode_kernel", "kda_attn_combine_kernel"):
         assert k in names, k
 
 
@@ -74,3 +74,12 @@ def test_fused_kernel_runs_two_waves_per_simd(resources):
     for r in fused:
         assert int(r["Occupancy [waves/SIMD]"]) >= 2, r
         assert int(r["VGPRs"]) <= 256, r
+
+
+def test_attn_decode_keeps_loads_in_flight(resources):
+    # a streaming kernel: at least three waves per SIMD for every instance (2 dtypes x 2 head
+    # dimensions x 3 group sizes), so that enough cache rows are requested at once
+    attn = [r for n, r in resources.items() if "kda_attn_decode_kernel" in n]
+    assert len(attn) == 12
+    for r in attn:
+        assert int(r["Occupancy [waves/SIMD]"]) >= 3, r

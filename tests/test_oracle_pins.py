@@ -122,3 +122,80 @@ def test_qk_prologue():
     v = rng.standard_normal((1, 1, 5))
     o, _ = oracle.kda_reference(k, k, v, np.zeros((1, 1, 8)), np.ones((1, 1)), 1.0)
     assert np.allclose(o, v, atol=1e-14)
+
+
+# ---- softmax-attention decode over a KV cache (the comparator of the decode step):
+# pins of oracle.attn_decode_reference against hand-worked values and closed forms
+
+def test_attn_decode_worked_example():
+    # scores scale * q . k = 0.5 * [0, 2 ln 3] = [0, ln 3] -> weights [1/4, 3/4]
+    q = np.array([[[1.0, 0.0]]])
+    K = np.array([[[[0.0, 0.0], [2 * np.log(3.0), 7.0]]]])
+    V = np.array([[[[4.0, 0.0], [0.0, 8.0]]]])
+    o = oracle.attn_decode_reference(q, K, V, scale=0.5)
+    np.testing.assert_allclose(o, [[[1.0, 6.0]]], rtol=0, atol=1e-14)
+    # scale defaults to d^-1/2
+    o2 = oracle.attn_decode_reference(q, K * (0.5 * np.sqrt(2.0)), V)  # d = 2: scale 2^-1/2
+    np.testing.assert_allclose(o2, [[[1.0, 6.0]]], rtol=0, atol=1e-14)
+
+
+def test_attn_decode_grouped_heads_and_lengths():
+    # query head h reads cached head h // (H / H_kv); constant value rows make o that constant
+    rng = np.random.default_rng(5)
+    B, H, H_kv, T, d = 2, 4, 2, 9, 8
+    q = rng.standard_normal((B, H, d))
+    K = rng.standard_normal((B, H_kv, T, d))
+    V = np.empty((B, H_kv, T, d))
+    for b in range(B):
+        for j in range(H_kv):
+            V[b, j] = 10 * b + j + 1
+    o = oracle.attn_decode_reference(q, K, V, seq_lens=[T, 3])
+    for b in range(B):
+        for h in range(H):
+            np.testing.assert_allclose(o[b, h], 10 * b + h // 2 + 1, rtol=1e-14)
+    # rows at and past the length never matter, lengths are clamped to [0, T], none gives 0
+    K2, V2 = K.copy(), V.copy()
+    K2[1, :, 3:] = 1e3
+    V2[1, :, 3:] = 1e6
+    np.testing.assert_array_equal(oracle.attn_decode_reference(q, K2, V2, seq_lens=[T, 3]), o)
+    np.testing.assert_array_equal(oracle.attn_decode_reference(q, K, V, seq_lens=[T + 5, 3]), o)
+    z = oracle.attn_decode_reference(q, K, V, seq_lens=[0, -2])
+    np.testing.assert_array_equal(z, np.zeros((B, H, d)))
+
+
+def test_attn_decode_closed_forms():
+    rng = np.random.default_rng(6)
+    d, T = 16, 12
+    q = rng.standard_normal((1, 1, d))
+    V = rng.standard_normal((1, 1, T, d))
+    # identical keys: the mean of the value rows
+    K = np.repeat(rng.standard_normal((1, 1, 1, d)), T, axis=2)
+    np.testing.assert_allclose(oracle.attn_decode_reference(q, K, V), V.mean(axis=2), rtol=1e-12, atol=1e-14)
+    # one row: that value row
+    np.testing.assert_allclose(oracle.attn_decode_reference(q, K[:, :, :1], V[:, :, :1]), V[:, :, 0],
+                               rtol=1e-14)
+    # scores near 1000 (exp would overflow): two rows 1000 and 1000 - ln 2 -> weights 2/3, 1/3
+    e = np.zeros((1, 1, d))
+    e[0, 0, 0] = 1.0
+    K2 = np.zeros((1, 1, 2, d))
+    K2[0, 0, :, 0] = [1000.0, 1000.0 - np.log(2.0)]
+    o = oracle.attn_decode_reference(e, K2, V[:, :, :2], scale=1.0)
+    np.testing.assert_allclose(o[0, 0], (2 * V[0, 0, 0] + V[0, 0, 1]) / 3, rtol=1e-12)
+
+
+def test_attn_decode_matches_library_softmax_and_is_order_free():
+    from scipy.special import softmax
+    rng = np.random.default_rng(7)
+    B, H, H_kv, T, d = 2, 4, 1, 37, 32
+    q = rng.standard_normal((B, H, d))
+    K = rng.standard_normal((B, H_kv, T, d))
+    V = rng.standard_normal((B, H_kv, T, d))
+    o = oracle.attn_decode_reference(q, K, V, scale=0.3)
+    for b in range(B):
+        for h in range(H):
+            w = softmax(0.3 * K[b, 0] @ q[b, h])
+            np.testing.assert_allclose(o[b, h], w @ V[b, 0], rtol=1e-12, atol=1e-14)
+    # permuting the cache rows (keys and values together) leaves o unchanged
+    perm = rng.permutation(T)
+    np.testing.assert_allclose(oracle.attn_decode_reference(q, K[:, :, perm], V[:, :, perm], scale=0.3), o,
+                               rtol=1e-12, atol=1e-14)

@@ -310,7 +310,7 @@ namespace {
 // Splits of the attention decode's cache: enough workgroups to fill the chip
 // several times over, each over at least kAttnMinSplit rows (its fixed costs are
 // the query, one merge and one partial write), in whole iterations.
-constexpr int64_t kAttnTargetGroups = 4096;
+constexpr int64_t kAttnTargetGroups = kda::kAttnMaxSplits;  // so no cached head takes more splits
 constexpr int64_t kAttnMinSplit = 1024;
 
 struct AttnSplit {

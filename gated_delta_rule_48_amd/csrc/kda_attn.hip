@@ -216,24 +216,57 @@ __global__ __launch_bounds__(kAttnThreads) void kda_attn_decode_kernel(AttnArgs 
     }
 }
 
-// o[b, h] from the splits' (m, l, acc): one thread per channel.
+// o[b, h] from the splits' (m, l, acc). A workgroup takes kAttnCombineChannels
+// channels of one (sequence, query head): its threads first form the common
+// maximum and each split's weight 2^(m_s - max) (one split per thread in turn,
+// the weights kept in LDS), then sum the weighted partial vectors, every channel
+// over P interleaved groups of splits, merged through LDS. The loads of a
+// thread's splits are independent, so they overlap.
 template <int D, typename T>
-__global__ __launch_bounds__(D) void kda_attn_combine_kernel(AttnArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-    const int H = a.H_kv * a.G;
-    const size_t bh = (size_t)b * H + h;
-    const float *ml = a.part_ml + bh * a.n_splits * 2;
-    const float *pa = a.part_acc + bh * a.n_splits * D + c;
+__global__ __launch_bounds__(kAttnThreads) void kda_attn_combine_kernel(AttnArgs a) {
+    constexpr int CB = kAttnCombineChannels;
+    constexpr int P = kAttnThreads / CB;
+    __shared__ float wgt[kAttnMaxSplits];
+    __shared__ float red[2][kAttnThreads / 64];
+    __shared__ float part[P][CB];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = a.n_splits;
+    const size_t bh = (size_t)b * a.H_kv * a.G + h;
+    const float *ml = a.part_ml + bh * n * 2;
+
     float mx = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, ml[2 * s]);
+    for (int s = tid; s < n; s += kAttnThreads) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[0][wv] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     const float ref = ref_of(mx);
-    float lsum = 0.f, val = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
+    float lsum = 0.f;
+    for (int s = tid; s < n; s += kAttnThreads) {
         const float f = exp2_fast(ml[2 * s] - ref);
+        wgt[s] = f;
         lsum = fmaf(ml[2 * s + 1], f, lsum);
-        val = fmaf(pa[(size_t)s * D], f, val);
     }
-    static_cast<T *>(a.o)[bh * D + c] = from_f32<T>(lsum > 0.f ? val / lsum : 0.f);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) red[1][wv] = lsum;
+    __syncthreads();  // the weights and the partial sums are complete
+    lsum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+
+    const int c = blockIdx.z * CB + tid % CB, pg = tid / CB;
+    const float *pa = a.part_acc + bh * n * D + c;
+    float val = 0.f;
+#pragma unroll 4
+    for (int s = pg; s < n; s += P) val = fmaf(pa[(size_t)s * D], wgt[s], val);
+    part[pg][tid % CB] = val;
+    __syncthreads();
+    if (tid < CB) {
+        float v = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) v += part[p][tid];
+        static_cast<T *>(a.o)[bh * D + blockIdx.z * CB + tid] = from_f32<T>(lsum > 0.f ? v / lsum : 0.f);
+    }
 }
 
 template <int D, int G, typename T>
@@ -242,7 +275,8 @@ hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t stream) {
                        stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.n_splits == 1) return err;
-    hipLaunchKernelGGL((kda_attn_combine_kernel<D, T>), dim3(a.H_kv * G, B), dim3(D), 0, stream, a);
+    hipLaunchKernelGGL((kda_attn_combine_kernel<D, T>), dim3(a.H_kv * G, B, D / kAttnCombineChannels),
+                       dim3(kAttnThreads), 0, stream, a);
     return hipGetLastError();
 }
 

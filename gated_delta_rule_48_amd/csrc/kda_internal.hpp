@@ -102,6 +102,8 @@ struct DecodeArgs {
 // maximum and sum), and a second kernel combines them.
 constexpr int kAttnThreads = 256;       // four waves
 constexpr int kAttnRowsPerLane = 4;     // cache rows per lane group per iteration
+constexpr int kAttnMaxSplits = 4096;    // splits per cached head, at most (the combine keeps a weight each in LDS)
+constexpr int kAttnCombineChannels = 32;  // channels per combine workgroup
 __host__ __device__ constexpr int attn_rows_per_iter(int D) { return 4 * (64 / (D / 8)) * kAttnRowsPerLane; }
 
 struct AttnArgs {

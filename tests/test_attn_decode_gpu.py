@@ -59,6 +59,12 @@ def test_attn_decode_split_cache(io, d):
     assert np.all(o[2] == 0)
 
 
+def test_attn_decode_many_splits():
+    # one cached head of 300,000 rows: 261 splits of 1,152 rows (more splits than the
+    # combine kernel has threads), the last one partly filled
+    _check("many-splits", 1, 2, 1, 300000, 64, "f32", [299999], seed=41)
+
+
 def test_attn_decode_all_rows_and_empty_cache():
     import torch
     import gated_delta_rule_48_amd as kda

@@ -8,6 +8,7 @@
 
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
+#include "kda_attn.hpp"
 
 #define KDA_EXPORT extern "C" __attribute__((visibility("default")))
 

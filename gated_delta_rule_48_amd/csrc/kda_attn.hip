@@ -26,7 +26,7 @@
 // G <= 4 there are at most 8 flops per cached byte, far below the point where
 // the matrix cores would pay.
 
-#include "kda_internal.hpp"
+#include "kda_attn.hpp"
 
 namespace kda {
 namespace {

@@ -157,3 +157,41 @@ def attn_decode_reference(q, k_cache, v_cache, seq_lens=None, scale: float = Non
             w = np.exp(s - s.max())
             o[b, h] = (w @ V[b, j, :n]) / w.sum()
     return o
+
+
+def kda_backward_reference(q, k, v, log_alpha, beta, scale: float, do, dhT=None, h0=None):
+    """Gradients of the KDA recurrence, in fp64: reverse-mode differentiation (torch.autograd
+    on the CPU) of the plain token loop of the "ten questions" page's update (its closing
+    symbol-by-symbol reading) in the order of the bra-ket derivation page's state-update
+    equations, for equal-length sequences:
+
+        S~ = Diag(exp(log_alpha_t)) S;  e = beta_t (v_t - S~^T k_t);  S = S~ + k_t e^T;
+        o_t = scale S^T q_t
+
+    The pages derive no gradient; this is the derivative of that loop and nothing else.
+    q, k [B, T, H, dk]; v, do [B, T, H, dv]; log_alpha [B, T, H, dk]; beta [B, T, H];
+    h0, dhT [B, H, dk, dv] or None (zero). The differentiated loss is
+    sum(o * do) + sum(hT * dhT). Returns a dict of fp64 numpy arrays: dq, dk, dv,
+    dlog_alpha, dbeta, dh0."""
+    import torch
+    B, T, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    t64 = lambda a: torch.tensor(_f64(a), dtype=torch.float64)  # noqa: E731
+    xs = [t64(a).requires_grad_(True) for a in (q, k, v, log_alpha, beta)]
+    S0 = t64(h0) if h0 is not None else torch.zeros((B, H, dk, dv), dtype=torch.float64)
+    S0.requires_grad_(True)
+    qq, kk, vv, la, bb = xs
+    S = S0
+    outs = []
+    for t in range(T):
+        St = torch.exp(la[:, t])[..., None] * S
+        e = bb[:, t][..., None] * (vv[:, t] - torch.einsum("bhkv,bhk->bhv", St, kk[:, t]))
+        S = St + kk[:, t][..., None] * e[..., None, :]
+        outs.append(scale * torch.einsum("bhkv,bhk->bhv", S, qq[:, t]))
+    loss = (torch.stack(outs, dim=1) * t64(do)).sum() if T > 0 else torch.zeros((), dtype=torch.float64)
+    if dhT is not None:
+        loss = loss + (S * t64(dhT)).sum()
+    grads = torch.autograd.grad(loss, xs + [S0], allow_unused=True)
+    names = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0")
+    refs = xs + [S0]
+    return {n: (g if g is not None else torch.zeros_like(r)).detach().numpy() for n, g, r in zip(names, grads, refs)}

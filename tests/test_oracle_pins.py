@@ -199,3 +199,69 @@ def test_attn_decode_matches_library_softmax_and_is_order_free():
     perm = rng.permutation(T)
     np.testing.assert_allclose(oracle.attn_decode_reference(q, K[:, :, perm], V[:, :, perm], scale=0.3), o,
                                rtol=1e-12, atol=1e-14)
+
+
+# ---- gradients of the recurrence (oracle.kda_backward_reference, autograd of the token loop):
+# pinned by central differences of the independent C forward oracle and by closed forms
+
+def _loss_c(q, k, v, la, beta, scale, h0, do, dhT):
+    """sum(o * do) + sum(hT * dhT) through the C oracle, for [B=1, T, H, d] inputs (h0, dhT
+    [1, H, dk, dv])."""
+    o, hT = oracle.kda_reference(q[0], k[0], v[0], la[0], beta[0], scale, h0=h0)
+    return float((o * do[0]).sum() + (hT * dhT).sum())
+
+
+def test_backward_matches_finite_differences():
+    rng = np.random.default_rng(8)
+    B, T, H, dk, dv, scale = 1, 7, 2, 3, 2, 0.6
+    q, k = rng.standard_normal((B, T, H, dk)), rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    la = -0.5 * np.log1p(np.exp(rng.standard_normal((B, T, H, dk))))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((B, T, H))))
+    h0 = 0.3 * rng.standard_normal((B, H, dk, dv))
+    do, dhT = rng.standard_normal((B, T, H, dv)), rng.standard_normal((B, H, dk, dv))
+    g = oracle.kda_backward_reference(q, k, v, la, beta, scale, do, dhT=dhT, h0=h0)
+    args = dict(q=q, k=k, v=v, la=la, beta=beta, h0=h0)
+    names = dict(q="dq", k="dk", v="dv", la="dlog_alpha", beta="dbeta", h0="dh0")
+    eps = 1e-6
+    for n, key in names.items():
+        x = args[n]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap, am = dict(args, **{n: xp}), dict(args, **{n: xm})
+            lp = _loss_c(ap["q"], ap["k"], ap["v"], ap["la"], ap["beta"], scale, ap["h0"], do, dhT)
+            lm = _loss_c(am["q"], am["k"], am["v"], am["la"], am["beta"], scale, am["h0"], do, dhT)
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[key], fd, rtol=1e-6, atol=1e-8, err_msg=key)
+
+
+def test_backward_closed_forms():
+    rng = np.random.default_rng(9)
+    B, T, H, dk, dv, s = 1, 6, 1, 4, 3, 0.8
+    q, k = rng.standard_normal((B, T, H, dk)), rng.standard_normal((B, T, H, dk))
+    v, do = rng.standard_normal((B, T, H, dv)), rng.standard_normal((B, T, H, dv))
+    h0, dhT = rng.standard_normal((B, H, dk, dv)), rng.standard_normal((B, H, dk, dv))
+    zero_b = np.zeros((B, T, H))
+    # beta = 0, alpha = 1: S_t = h0, o_t = s h0^T q_t
+    g = oracle.kda_backward_reference(q, k, v, np.zeros((B, T, H, dk)), zero_b, s, do, dhT=dhT, h0=h0)
+    H0 = h0[0, 0]
+    for t in range(T):
+        np.testing.assert_allclose(g["dq"][0, t, 0], s * H0 @ do[0, t, 0], rtol=1e-12)
+        # dL/dS_t after step t: the later outputs' s q do^T plus dhT; the delta's residual v - h0^T k
+        dS = dhT[0, 0] + sum(s * np.outer(q[0, u, 0], do[0, u, 0]) for u in range(t, T))
+        np.testing.assert_allclose(g["dbeta"][0, t, 0], (dS.T @ k[0, t, 0]) @ (v[0, t, 0] - H0.T @ k[0, t, 0]),
+                                   rtol=1e-10)
+    np.testing.assert_allclose(g["dh0"][0, 0], dhT[0, 0] + s * sum(np.outer(q[0, t, 0], do[0, t, 0]) for t in range(T)),
+                               rtol=1e-12)
+    np.testing.assert_array_equal(g["dv"], 0)
+    np.testing.assert_array_equal(g["dk"], 0)
+    # beta = 0 with decays: S_t = Diag(exp(g_t)) h0, g_t = the prefix sum of log alpha
+    la = -0.4 * np.log1p(np.exp(rng.standard_normal((B, T, H, dk))))
+    g = oracle.kda_backward_reference(q, k, v, la, zero_b, s, do, dhT=dhT, h0=h0)
+    gt = np.cumsum(la[0, :, 0], axis=0)
+    dg = np.stack([s * q[0, t, 0] * np.exp(gt[t]) * (H0 @ do[0, t, 0]) for t in range(T)])
+    dg[-1] += np.exp(gt[-1]) * (H0 * dhT[0, 0]).sum(axis=1)
+    np.testing.assert_allclose(g["dlog_alpha"][0, :, 0], np.cumsum(dg[::-1], axis=0)[::-1], rtol=1e-10)

@@ -23,8 +23,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_preact", "kda_recurrent_step",
            "kda_recurrent_step_gated", "kda_recurrent_step_preact", "kda_attn_decode_workspace_bytes",
-           "kda_attn_decode")
-ABI_VERSION = 3
+           "kda_attn_decode", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
+ABI_VERSION = 4
 
 
 class KdaError(RuntimeError):
@@ -68,6 +68,10 @@ def load() -> ctypes.CDLL:
     lib.kda_attn_decode_workspace_bytes.restype = Z
     lib.kda_attn_decode.argtypes = [I, I, I, I, I, I, P, P, P, P, F, P, P, Z, P]
     lib.kda_attn_decode.restype = I
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.kda_chunk_bwd_workspace_bytes.restype = Z
+    lib.kda_chunk_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.kda_chunk_bwd.restype = I
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libkda.so has ABI {lib.kda_abi_version()}, this binding expects {ABI_VERSION}; "
                            "rebuild it")
@@ -338,3 +342,46 @@ def attn_decode(q, k_cache, v_cache, seq_lens=None, scale: Optional[float] = Non
     if st != 0:
         raise KdaError(st, "kda_attn_decode")
     return o
+
+
+def chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk=64, io=KDA_F32) -> int:
+    return int(load().kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, io))
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, dout, scale: Optional[float] = None, h0=None, dhT=None,
+              chunk: int = 64, workspace=None, stream=None):
+    """Backward pass of chunk_fwd (kda_chunk_bwd) for equal-length fp32 sequences: q, k
+    [B, T, H, dk]; v, dout [B, T, H, dv]; log_alpha [B, T, H, dk]; beta [B, T, H]; h0, dhT
+    [B, H, dk, dv] or None. Returns (dq, dk, dv, dlog_alpha, dbeta, dh0), dh0 None when h0
+    is None."""
+    import torch
+    lib = load()
+    dev = q.device
+    io = _io_code(q.dtype)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    f32 = torch.float32
+    _check(k, "k", q.dtype, (B, T, H, dk), dev)
+    _check(v, "v", q.dtype, (B, T, H, dv), dev)
+    _check(log_alpha, "log_alpha", f32, (B, T, H, dk), dev)
+    _check(beta, "beta", f32, (B, T, H), dev)
+    _check(dout, "dout", q.dtype, (B, T, H, dv), dev)
+    for t, n in ((h0, "h0"), (dhT, "dhT")):
+        if t is not None:
+            _check(t, n, f32, (B, H, dk, dv), dev)
+    dq, dk_, dlog_alpha = (torch.empty((B, T, H, dk), dtype=q.dtype, device=dev) for _ in range(3))
+    dv_ = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    dbeta = torch.empty((B, T, H), dtype=f32, device=dev)
+    dh0 = torch.empty((B, H, dk, dv), dtype=f32, device=dev) if h0 is not None else None
+    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dk ** -0.5
+    st = lib.kda_chunk_bwd(B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                           float(scale), _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                           _ptr(dlog_alpha), _ptr(dbeta), _ptr(dh0), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_bwd")
+    return dq, dk_, dv_, dlog_alpha, dbeta, dh0

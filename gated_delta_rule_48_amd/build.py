@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_state.hip", "kda_fused.hip", "kda_decode.hip", "kda_attn.hip"]
+SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_state.hip", "kda_fused.hip", "kda_decode.hip", "kda_attn.hip", "kda_bwd.hip"]
 HEADERS = ["kda_device.hpp", "kda_internal.hpp", "kda_solve.hpp"]
 
 HIPCC_FLAGS = [

@@ -9,6 +9,7 @@
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
 #include "kda_attn.hpp"
+#include "kda_bwd.hpp"
 
 #define KDA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -389,5 +390,85 @@ KDA_EXPORT int kda_attn_decode(int B, int H, int H_kv, int d, int T_max, int io,
                           H_kv, H / H_kv, T_max, sp.len, sp.n};
     if (kda::launch_attn_decode(a, B, d, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+namespace {
+
+struct BwdPlan {
+    size_t per_bytes, scratch_off, total;
+    int n_chunks, n_groups;
+};
+
+int check_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io, BwdPlan *p) {
+    if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (io != KDA_F32 || chunk != kda::kBwdChunk || !supported_dim(d_k) || !supported_dim(d_v))
+        return KDA_ERR_UNSUPPORTED;
+    if (B > 65535 || H > 65535 || (int64_t)B * T * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    const kda::BwdLayout L{d_k, d_v};
+    p->n_chunks = (T + chunk - 1) / chunk;
+    const int64_t units = (int64_t)B * p->n_chunks * H;
+    p->n_groups = (int)std::min<int64_t>(units, kda::kBwdMaxGroups);
+    p->per_bytes = (size_t)L.per_chunk() * sizeof(float);
+    p->scratch_off = round_up((size_t)units * p->per_bytes, 256);
+    p->total = units > 0 ? p->scratch_off + round_up((size_t)p->n_groups * L.scratch() * sizeof(float), 256) : 0;
+    return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, int io) {
+    BwdPlan p;
+    if (check_bwd(B, T, H, d_k, d_v, chunk, io, &p) != KDA_OK) return 0;
+    return p.total;
+}
+
+KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io, const void *q,
+                             const void *k, const void *v, const float *log_alpha, const float *beta, float scale,
+                             const float *h0, const void *dout, const float *dhT, void *dq, void *dk, void *dv,
+                             float *dlog_alpha, float *dbeta, float *dh0, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    BwdPlan p;
+    const int st = check_bwd(B, T, H, d_k, d_v, chunk, io, &p);
+    if (st != KDA_OK) return st;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nk = ntok * d_k * 4, nv = ntok * d_v * 4, nb = ntok * 4, ns = (size_t)B * H * d_k * d_v * 4;
+    if (ntok > 0 && (!q || !k || !v || !log_alpha || !beta || !dout || !dq || !dk || !dv || !dlog_alpha || !dbeta))
+        return KDA_ERR_INVALID_ARG;
+    const void *in16[] = {q, k, v, log_alpha, dout, h0, dhT, dq, dk, dv, dlog_alpha, dh0};
+    for (const void *x : in16)
+        if (!aligned(x, 16)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(beta, 4) || !aligned(dbeta, 4)) return KDA_ERR_INVALID_ARG;
+    // no output may overlap any argument or another output
+    const void *ins[] = {q, k, v, log_alpha, beta, h0, dout, dhT};
+    const size_t in_n[] = {nk, nk, nv, nk, nb, ns, nv, ns};
+    const void *outs[] = {dq, dk, dv, dlog_alpha, dbeta, dh0};
+    const size_t out_n[] = {nk, nk, nv, nk, nb, ns};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 8; ++j)
+            if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return KDA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return KDA_ERR_INVALID_ARG;
+    }
+    if (p.total > 0) {
+        if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+        for (int j = 0; j < 8; ++j)
+            if (overlaps(workspace, p.total, ins[j], in_n[j])) return KDA_ERR_INVALID_ARG;
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(workspace, p.total, outs[i], out_n[i])) return KDA_ERR_INVALID_ARG;
+    }
+    if (ntok == 0 && !(dh0 && B > 0)) return KDA_OK;
+    float *ws = static_cast<float *>(workspace);
+    const kda::BwdArgs a{static_cast<const float *>(q), static_cast<const float *>(k),
+                         static_cast<const float *>(v), log_alpha, beta, h0,
+                         static_cast<const float *>(dout), dhT, scale,
+                         static_cast<float *>(dq), static_cast<float *>(dk), static_cast<float *>(dv),
+                         dlog_alpha, dbeta, dh0, ws,
+                         p.total > 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + p.scratch_off)
+                                     : nullptr,
+                         B, T, H, p.n_chunks, p.n_groups};
+    if (kda::launch_chunk_bwd(a, d_k, d_v, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }

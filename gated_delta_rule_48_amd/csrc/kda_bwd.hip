@@ -1,0 +1,444 @@
+// kda_bwd.hip -- the chunked backward pass of the KDA recurrence: the gradients
+// of a loss with respect to q, k, v, log alpha, beta and the initial state, from
+// its gradients with respect to every output and to the final state.
+//
+// The pages derive no gradient. This pass is the reverse-mode derivative of the
+// chunked forward (the chunk form of the essay "22,580: from GPT-2 to Kimi K3"
+// sections 6.2-6.3 with the per-channel decay of its Gated DeltaNet section),
+// taken identity by identity. Per chunk of C rows, with the prefix
+// g = cumsum(log alpha) inside the chunk, gamma = g[C-1], m = gamma / 2, the
+// scale s and the state S at the chunk's start:
+//
+//   P = k e^(g-m),  N = k e^(m-g),  Qe = q e^(g-m),  R = k e^(gamma-g)
+//   A = strict_lower(diag(beta) P N^T),  T = (I + A)^-1
+//   Bk = diag(beta) k e^g,  Bv = diag(beta) v,  W = T Bk,  U~ = T Bv
+//   QO = s q e^g,  Aqk = s lower(Qe N^T)
+//   U = U~ - W S,  O = QO S + Aqk U,  S' = Diag(e^gamma) S + R^T U
+//
+// Given dO and dS' (the loss gradient with respect to the state at the chunk's
+// end):
+//
+//   dU = Aqk^T dO + R dS'
+//   dS = QO^T dO + Diag(e^gamma) dS' - W^T dU          (the reverse recursion)
+//   dQO = dO S^T, dAqk = lower(dO U^T), dR = U dS'^T, dW = -dU S^T
+//   dT = dU Bv^T + dW Bk^T, dBv = T^T dU, dBk = T^T dW
+//   dA = strict_lower(-T^T dT T^T)
+//   dbeta = rowsum(dBv * v) + rowsum(dBk * k e^g) + rowsum(dA * P N^T)
+//   dv = diag(beta) dBv
+//   dP = diag(beta) dA N,  dN = (diag(beta) dA)^T P + s dAqk^T Qe,  dQe = s dAqk N
+//   dq = s dQO e^g + dQe e^(g-m)
+//   dk = diag(beta) dBk e^g + dP e^(g-m) + dN e^(m-g) + dR e^(gamma-g)
+//   dg = s dQO q e^g + dQe Qe + diag(beta) dBk k e^g + dP P - dN N - dR R
+//   dgamma = colsum(dR * R) + e^gamma rowsum(dS' * S), added to dg's last row
+//   dlog_alpha = the reverse prefix sum of dg down the chunk
+//
+// (m cancels in P N^T and Qe N^T and carries no gradient.) Rows past a
+// sequence's end are zero in q, k, v, dO, beta and log alpha, which leaves every
+// quantity of the valid rows unchanged.
+//
+// Four kernels: (1) the chunk-local forward quantities T, Aqk, W, U~, R, QO and
+// e^gamma, in parallel over (chunk, head); (2) the chunk-start states, in order
+// over the chunks of each (sequence, head, 16 state columns); (3) the state
+// gradients dS', in reverse order likewise, and dh0; (4) the chunk-local
+// gradients, in parallel over (chunk, head). Everything is fp32 on the vector
+// ALUs, the chunk matrices in a per-workgroup scratch in global memory, the
+// products by a plain 4 x 4 register-tiled loop: the direct form of this pass,
+// not tuned.
+
+#include "kda_bwd.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int C = kBwdChunk;
+
+// D = alpha op(A) op(B) + beta D over the workgroup (beta = 0 overwrites D).
+// op(A) is M x K: A row-major with leading dimension lda, or stored K x M (TA).
+// op(B) is K x N: B stored K x N with leading dimension ldb, or N x K (TB).
+// M and N are multiples of 4; each thread computes 4 x 4 tiles of D, consecutive
+// threads along a row of tiles. A later call with the same M and N gives every
+// thread the same tiles, so it may accumulate into D without a barrier.
+template <bool TA, bool TB>
+__device__ void gemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                     float beta, float *D, int ldd) {
+    const int tn = N / 4, tiles = (M / 4) * tn;
+    for (int t = threadIdx.x; t < tiles; t += kBwdThreads) {
+        const int i0 = (t / tn) * 4, j0 = (t % tn) * 4;
+        float acc[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+        for (int kk = 0; kk < K; ++kk) {
+            float x[4], y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = TA ? A[kk * lda + i0 + r] : A[(i0 + r) * lda + kk];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) y[c] = TB ? B[(j0 + c) * ldb + kk] : B[kk * ldb + j0 + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(x[r], y[c], acc[r][c]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float *d = D + (i0 + r) * ldd + j0 + c;
+                *d = beta == 0.f ? alpha * acc[r][c] : fmaf(alpha, acc[r][c], beta * *d);
+            }
+    }
+}
+
+// The scratch of one workgroup of the chunk-local kernels (BwdLayout::scratch()).
+template <int DK, int DV> struct Scr {
+    float *Q, *K, *V, *dO, *G, *P, *N, *Qe, *Bk, *Bv, *U, *dU, *dQO, *dR, *dW, *dBv, *dBk, *dQe, *dP, *dN, *dG;
+    float *PN, *dAqk, *dT, *Tmp, *dA, *bet, *m, *gam;
+    __device__ explicit Scr(float *p) {
+        constexpr int ck = C * DK, cv = C * DV, cc = C * C;
+        Q = p;
+        K = Q + ck;
+        G = K + ck;
+        P = G + ck;
+        N = P + ck;
+        Qe = N + ck;
+        Bk = Qe + ck;
+        dQO = Bk + ck;
+        dR = dQO + ck;
+        dW = dR + ck;
+        dBk = dW + ck;
+        dQe = dBk + ck;
+        dP = dQe + ck;
+        dN = dP + ck;
+        dG = dN + ck;
+        V = dG + ck;  // 15 C x dk matrices, then 6 C x dv
+        dO = V + cv;
+        Bv = dO + cv;
+        U = Bv + cv;
+        dU = U + cv;
+        dBv = dU + cv;
+        PN = dBv + cv;  // then 5 C x C
+        dAqk = PN + cc;
+        dT = dAqk + cc;
+        Tmp = dT + cc;
+        dA = Tmp + cc;
+        bet = dA + cc;
+        m = bet + C;
+        gam = m + DK;
+    }
+};
+
+__device__ __forceinline__ size_t row_of(const BwdArgs &a, int b, int t, int h) {
+    return ((size_t)b * a.T + t) * a.H + h;
+}
+
+// One chunk's inputs into the scratch (rows past the end zero), beta, the prefix
+// g of log alpha, gamma and m.
+template <int DK, int DV>
+__device__ void load_chunk(const BwdArgs &a, int b, int h, int t0, int n, const Scr<DK, DV> &S, bool with_dout) {
+    const int tid = threadIdx.x;
+    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+        const int r = idx / DK, i = idx % DK;
+        const size_t off = row_of(a, b, t0 + r, h) * DK + i;
+        S.Q[idx] = r < n ? a.q[off] : 0.f;
+        S.K[idx] = r < n ? a.k[off] : 0.f;
+    }
+    for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
+        const int r = idx / DV, j = idx % DV;
+        const size_t off = row_of(a, b, t0 + r, h) * DV + j;
+        S.V[idx] = r < n ? a.v[off] : 0.f;
+        if (with_dout) S.dO[idx] = r < n ? a.dout[off] : 0.f;
+    }
+    for (int r = tid; r < C; r += kBwdThreads) S.bet[r] = r < n ? a.beta[row_of(a, b, t0 + r, h)] : 0.f;
+    for (int i = tid; i < DK; i += kBwdThreads) {
+        float g = 0.f;
+        for (int r = 0; r < C; ++r) {
+            if (r < n) g += a.log_alpha[row_of(a, b, t0 + r, h) * DK + i];
+            S.G[r * DK + i] = g;
+        }
+        S.gam[i] = g;
+        S.m[i] = 0.5f * g;
+    }
+}
+
+// P, N, Qe and Bk over C x dk, Bv over C x dv (after load_chunk and a barrier).
+template <int DK, int DV>
+__device__ void chunk_factors(const Scr<DK, DV> &S) {
+    for (int idx = threadIdx.x; idx < C * DK; idx += kBwdThreads) {
+        const int r = idx / DK, i = idx % DK;
+        const float g = S.G[idx], m = S.m[i], kv = S.K[idx];
+        S.P[idx] = kv * expf(g - m);
+        S.N[idx] = kv * expf(m - g);
+        S.Qe[idx] = S.Q[idx] * expf(g - m);
+        S.Bk[idx] = S.bet[r] * kv * expf(g);
+    }
+    for (int idx = threadIdx.x; idx < C * DV; idx += kBwdThreads) S.Bv[idx] = S.bet[idx / DV] * S.V[idx];
+}
+
+// (1) T, Aqk, W, U~, R, QO and e^gamma of every (chunk, head).
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs a) {
+    constexpr BwdLayout L{DK, DV};
+    __shared__ float sA[C][C + 1];
+    const Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
+    const int tid = threadIdx.x, total = a.B * a.n_chunks * a.H;
+    for (int ch = blockIdx.x; ch < total; ch += gridDim.x) {
+        const int h = ch % a.H, c = (ch / a.H) % a.n_chunks, b = ch / (a.H * a.n_chunks);
+        const int t0 = c * C, n = min(C, a.T - t0);
+        float *cb = a.ws + (size_t)ch * L.per_chunk();
+        load_chunk<DK, DV>(a, b, h, t0, n, S, false);
+        __syncthreads();
+        chunk_factors<DK, DV>(S);
+        for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+            const int i = idx % DK;
+            const float g = S.G[idx];
+            cb[L.oR() + idx] = S.K[idx] * expf(S.gam[i] - g);
+            cb[L.oQO() + idx] = a.scale * S.Q[idx] * expf(g);
+        }
+        for (int i = tid; i < DK; i += kBwdThreads) cb[L.oEg() + i] = expf(S.gam[i]);
+        __syncthreads();
+        gemm<false, true>(C, C, DK, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);
+        gemm<false, true>(C, C, DK, a.scale, S.Qe, DK, S.N, DK, 0.f, cb + L.oAqk(), C);
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += kBwdThreads) {
+            const int r = idx / C, i = idx % C;
+            sA[r][i] = i < r ? S.bet[r] * S.PN[idx] : 0.f;
+            if (i > r) cb[L.oAqk() + idx] = 0.f;
+        }
+        __syncthreads();
+        // T = (I + A)^-1 by forward substitution, one column per thread of the first wave
+        if (tid < C) {
+            float x[C];
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                float v = r == tid ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) v = fmaf(-sA[r][i], x[i], v);
+                x[r] = v;
+            }
+#pragma unroll
+            for (int r = 0; r < C; ++r) cb[L.oT() + r * C + tid] = x[r];
+        }
+        __syncthreads();
+        gemm<false, false>(C, DK, C, 1.f, cb + L.oT(), C, S.Bk, DK, 0.f, cb + L.oW(), DK);
+        gemm<false, false>(C, DV, C, 1.f, cb + L.oT(), C, S.Bv, DV, 0.f, cb + L.oUt(), DV);
+        __syncthreads();
+    }
+}
+
+// (2) The state at every chunk's start, for 16 columns of one (sequence, head).
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) void kda_bwd_states_kernel(BwdArgs a) {
+    constexpr BwdLayout L{DK, DV};
+    constexpr int NB = kBwdCols;
+    __shared__ float sS[DK][NB];
+    __shared__ float sU[C][NB];
+    const int j0 = blockIdx.x * NB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
+        const int i = idx / NB, j = idx % NB;
+        sS[i][j] = a.h0 ? a.h0[(((size_t)b * a.H + h) * DK + i) * DV + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < a.n_chunks; ++c) {
+        float *cb = a.ws + (((size_t)b * a.n_chunks + c) * a.H + h) * L.per_chunk();
+        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
+            const int i = idx / NB, j = idx % NB;
+            cb[L.oS() + i * DV + j0 + j] = sS[i][j];
+        }
+        for (int idx = tid; idx < C * NB; idx += kBwdThreads) {  // U = U~ - W S
+            const int r = idx / NB, j = idx % NB;
+            const float *w = cb + L.oW() + r * DK;
+            float u = cb[L.oUt() + r * DV + j0 + j];
+            for (int i = 0; i < DK; ++i) u = fmaf(-w[i], sS[i][j], u);
+            sU[r][j] = u;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {  // S' = e^gamma S + R^T U
+            const int i = idx / NB, j = idx % NB;
+            float s = cb[L.oEg() + i] * sS[i][j];
+            for (int r = 0; r < C; ++r) s = fmaf(cb[L.oR() + r * DK + i], sU[r][j], s);
+            sS[i][j] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// (3) dS' of every chunk (the gradient at its end), last chunk first, and dh0.
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArgs a) {
+    constexpr BwdLayout L{DK, DV};
+    constexpr int NB = kBwdCols;
+    __shared__ float sD[DK][NB];
+    __shared__ float sdU[C][NB];
+    __shared__ float sdO[C][NB];
+    const int j0 = blockIdx.x * NB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
+        const int i = idx / NB, j = idx % NB;
+        sD[i][j] = a.dhT ? a.dhT[(((size_t)b * a.H + h) * DK + i) * DV + j0 + j] : 0.f;
+    }
+    for (int c = a.n_chunks - 1; c >= 0; --c) {
+        const int t0 = c * C, n = min(C, a.T - t0);
+        float *cb = a.ws + (((size_t)b * a.n_chunks + c) * a.H + h) * L.per_chunk();
+        for (int idx = tid; idx < C * NB; idx += kBwdThreads) {
+            const int r = idx / NB, j = idx % NB;
+            sdO[r][j] = r < n ? a.dout[row_of(a, b, t0 + r, h) * DV + j0 + j] : 0.f;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
+            const int i = idx / NB, j = idx % NB;
+            cb[L.oDS() + i * DV + j0 + j] = sD[i][j];
+        }
+        for (int idx = tid; idx < C * NB; idx += kBwdThreads) {  // dU = Aqk^T dO + R dS'
+            const int r = idx / NB, j = idx % NB;
+            float u = 0.f;
+            for (int q = 0; q < C; ++q) u = fmaf(cb[L.oAqk() + q * C + r], sdO[q][j], u);
+            const float *rr = cb + L.oR() + r * DK;
+            for (int i = 0; i < DK; ++i) u = fmaf(rr[i], sD[i][j], u);
+            sdU[r][j] = u;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {  // dS = QO^T dO + e^gamma dS' - W^T dU
+            const int i = idx / NB, j = idx % NB;
+            float s = cb[L.oEg() + i] * sD[i][j];
+            for (int r = 0; r < C; ++r) {
+                s = fmaf(cb[L.oQO() + r * DK + i], sdO[r][j], s);
+                s = fmaf(-cb[L.oW() + r * DK + i], sdU[r][j], s);
+            }
+            sD[i][j] = s;
+        }
+        __syncthreads();
+    }
+    if (a.dh0) {
+        __syncthreads();
+        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
+            const int i = idx / NB, j = idx % NB;
+            a.dh0[(((size_t)b * a.H + h) * DK + i) * DV + j0 + j] = sD[i][j];
+        }
+    }
+}
+
+// (4) dq, dk, dv, dlog_alpha and dbeta of every (chunk, head).
+template <int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArgs a) {
+    constexpr BwdLayout L{DK, DV};
+    const Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
+    const int tid = threadIdx.x, total = a.B * a.n_chunks * a.H;
+    const float s = a.scale;
+    for (int ch = blockIdx.x; ch < total; ch += gridDim.x) {
+        const int h = ch % a.H, c = (ch / a.H) % a.n_chunks, b = ch / (a.H * a.n_chunks);
+        const int t0 = c * C, n = min(C, a.T - t0);
+        const float *cb = a.ws + (size_t)ch * L.per_chunk();
+        const float *Tm = cb + L.oT(), *Aqk = cb + L.oAqk(), *W = cb + L.oW(), *Ut = cb + L.oUt();
+        const float *Rm = cb + L.oR(), *S0 = cb + L.oS(), *dS1 = cb + L.oDS();
+        load_chunk<DK, DV>(a, b, h, t0, n, S, true);
+        __syncthreads();
+        chunk_factors<DK, DV>(S);
+        for (int idx = tid; idx < C * DV; idx += kBwdThreads) S.U[idx] = Ut[idx];
+        __syncthreads();
+        gemm<false, true>(C, C, DK, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);           // P N^T
+        gemm<false, false>(C, DV, DK, -1.f, W, DK, S0, DV, 1.f, S.U, DV);          // U = U~ - W S
+        gemm<true, false>(C, DV, C, 1.f, Aqk, C, S.dO, DV, 0.f, S.dU, DV);         // dU = Aqk^T dO
+        gemm<false, false>(C, DV, DK, 1.f, Rm, DK, dS1, DV, 1.f, S.dU, DV);        //    + R dS'
+        gemm<false, true>(C, DK, DV, 1.f, S.dO, DV, S0, DV, 0.f, S.dQO, DK);       // dQO = dO S^T
+        __syncthreads();
+        gemm<false, true>(C, C, DV, 1.f, S.dO, DV, S.U, DV, 0.f, S.dAqk, C);       // dO U^T
+        gemm<false, true>(C, DK, DV, 1.f, S.U, DV, dS1, DV, 0.f, S.dR, DK);        // dR = U dS'^T
+        gemm<false, true>(C, DK, DV, -1.f, S.dU, DV, S0, DV, 0.f, S.dW, DK);       // dW = -dU S^T
+        gemm<true, false>(C, DV, C, 1.f, Tm, C, S.dU, DV, 0.f, S.dBv, DV);         // dBv = T^T dU
+        gemm<false, true>(C, C, DV, 1.f, S.dU, DV, S.Bv, DV, 0.f, S.dT, C);        // dT = dU Bv^T
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += kBwdThreads)
+            if (idx % C > idx / C) S.dAqk[idx] = 0.f;                               // lower, diagonal included
+        gemm<false, true>(C, C, DK, 1.f, S.dW, DK, S.Bk, DK, 1.f, S.dT, C);        //    + dW Bk^T
+        gemm<true, false>(C, DK, C, 1.f, Tm, C, S.dW, DK, 0.f, S.dBk, DK);         // dBk = T^T dW
+        __syncthreads();
+        gemm<true, false>(C, C, C, 1.f, Tm, C, S.dT, C, 0.f, S.Tmp, C);            // T^T dT
+        __syncthreads();
+        gemm<false, true>(C, C, C, -1.f, S.Tmp, C, Tm, C, 0.f, S.dA, C);           // dA = -T^T dT T^T
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += kBwdThreads)
+            if (idx % C >= idx / C) S.dA[idx] = 0.f;                                // strictly lower
+        __syncthreads();
+        if (tid < C) {
+            const int r = tid;
+            float d = 0.f;
+            for (int j = 0; j < DV; ++j) d = fmaf(S.dBv[r * DV + j], S.V[r * DV + j], d);
+            for (int i = 0; i < DK; ++i) d = fmaf(S.dBk[r * DK + i], S.K[r * DK + i] * expf(S.G[r * DK + i]), d);
+            // strictly lower part only: above the diagonal P N^T can overflow (e^(g_r - g_i) with
+            // i after r), and dA is zero there
+            for (int i = 0; i < r; ++i) d = fmaf(S.dA[r * C + i], S.PN[r * C + i], d);
+            if (r < n) a.dbeta[row_of(a, b, t0 + r, h)] = d;
+        }
+        for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
+            const int r = idx / DV;
+            if (r < n) a.dv[row_of(a, b, t0 + r, h) * DV + idx % DV] = S.bet[r] * S.dBv[idx];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += kBwdThreads) S.dA[idx] *= S.bet[idx / C];  // diag(beta) dA
+        __syncthreads();
+        gemm<false, false>(C, DK, C, 1.f, S.dA, C, S.N, DK, 0.f, S.dP, DK);        // dP = diag(beta) dA N
+        gemm<true, false>(C, DK, C, 1.f, S.dA, C, S.P, DK, 0.f, S.dN, DK);         // dN = (diag(beta) dA)^T P
+        gemm<true, false>(C, DK, C, s, S.dAqk, C, S.Qe, DK, 1.f, S.dN, DK);        //    + s dAqk^T Qe
+        gemm<false, false>(C, DK, C, s, S.dAqk, C, S.N, DK, 0.f, S.dQe, DK);       // dQe = s dAqk N
+        __syncthreads();
+        for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+            const int r = idx / DK, i = idx % DK;
+            const float g = S.G[idx], m = S.m[i], kv = S.K[idx], qv = S.Q[idx], bb = S.bet[r];
+            const float eG = expf(g), eGm = expf(g - m), emG = expf(m - g), eR = expf(S.gam[i] - g);
+            const float dQO = S.dQO[idx], dQe = S.dQe[idx], dBk = S.dBk[idx], dP = S.dP[idx], dN = S.dN[idx],
+                        dR = S.dR[idx];
+            S.dG[idx] = s * dQO * qv * eG + dQe * qv * eGm + bb * dBk * kv * eG + dP * kv * eGm - dN * kv * emG -
+                        dR * kv * eR;
+            if (r < n) {
+                const size_t off = row_of(a, b, t0 + r, h) * DK + i;
+                a.dq[off] = s * dQO * eG + dQe * eGm;
+                a.dk[off] = bb * dBk * eG + dP * eGm + dN * emG + dR * eR;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < DK; i += kBwdThreads) {
+            float dgam = 0.f, ss = 0.f;
+            for (int r = 0; r < C; ++r) dgam = fmaf(S.dR[r * DK + i], S.K[r * DK + i] * expf(S.gam[i] - S.G[r * DK + i]), dgam);
+            for (int j = 0; j < DV; ++j) ss = fmaf(dS1[i * DV + j], S0[i * DV + j], ss);
+            float acc = fmaf(expf(S.gam[i]), ss, dgam);
+            for (int r = C - 1; r >= 0; --r) {
+                acc += S.dG[r * DK + i];
+                if (r < n) a.dlog_alpha[row_of(a, b, t0 + r, h) * DK + i] = acc;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+    const int total = a.B * a.n_chunks * a.H;
+    if (total > 0) {
+        hipLaunchKernelGGL((kda_bwd_chunk_fwd_kernel<DK, DV>), dim3(a.n_groups), dim3(kBwdThreads), 0, st, a);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL((kda_bwd_states_kernel<DK, DV>), dim3(DV / kBwdCols, a.H, a.B), dim3(kBwdThreads), 0, st,
+                           a);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    if (total > 0 || a.dh0) {
+        hipLaunchKernelGGL((kda_bwd_state_grads_kernel<DK, DV>), dim3(DV / kBwdCols, a.H, a.B), dim3(kBwdThreads), 0,
+                           st, a);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    if (total > 0) {
+        hipLaunchKernelGGL((kda_bwd_chunk_grads_kernel<DK, DV>), dim3(a.n_groups), dim3(kBwdThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, hipStream_t stream) {
+    if (dk == 64 && dv == 64) return launch_bwd_t<64, 64>(a, stream);
+    if (dk == 64 && dv == 128) return launch_bwd_t<64, 128>(a, stream);
+    if (dk == 128 && dv == 64) return launch_bwd_t<128, 64>(a, stream);
+    return launch_bwd_t<128, 128>(a, stream);
+}
+
+}  // namespace kda

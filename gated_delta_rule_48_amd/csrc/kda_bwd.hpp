@@ -1,0 +1,49 @@
+// kda_bwd.hpp -- launch arguments of the chunked backward pass (kda_bwd.hip),
+// shared by the kernels and the C ABI.
+#pragma once
+
+#include "kda_internal.hpp"
+
+namespace kda {
+
+constexpr int kBwdChunk = 64;     // rows per chunk
+constexpr int kBwdThreads = 256;  // four waves
+constexpr int kBwdCols = 16;      // state columns per workgroup of the sequential passes
+constexpr int kBwdMaxGroups = 1024;  // persistent workgroups of the chunk-local kernels, at most
+
+// Per (chunk, head) buffers in the workspace, fp32, in this order: T (C x C), Aqk
+// (C x C), W (C x dk), U~ (C x dv), R (C x dk), QO (C x dk), exp(gamma) (dk), the
+// state at the chunk's start (dk x dv) and the loss gradient with respect to the
+// state at its end (dk x dv).
+struct BwdLayout {
+    int dk, dv;
+    __host__ __device__ constexpr int oT() const { return 0; }
+    __host__ __device__ constexpr int oAqk() const { return kBwdChunk * kBwdChunk; }
+    __host__ __device__ constexpr int oW() const { return 2 * kBwdChunk * kBwdChunk; }
+    __host__ __device__ constexpr int oUt() const { return oW() + kBwdChunk * dk; }
+    __host__ __device__ constexpr int oR() const { return oUt() + kBwdChunk * dv; }
+    __host__ __device__ constexpr int oQO() const { return oR() + kBwdChunk * dk; }
+    __host__ __device__ constexpr int oEg() const { return oQO() + kBwdChunk * dk; }
+    __host__ __device__ constexpr int oS() const { return oEg() + dk; }
+    __host__ __device__ constexpr int oDS() const { return oS() + dk * dv; }
+    __host__ __device__ constexpr int per_chunk() const { return oDS() + dk * dv; }
+    // scratch of one workgroup of the chunk-local kernels: 15 C x dk, 6 C x dv and
+    // 5 C x C matrices, C betas and 2 dk vectors
+    __host__ __device__ constexpr int scratch() const {
+        return 15 * kBwdChunk * dk + 6 * kBwdChunk * dv + 5 * kBwdChunk * kBwdChunk + kBwdChunk + 2 * dk;
+    }
+};
+
+struct BwdArgs {
+    const float *q, *k, *v, *log_alpha, *beta, *h0, *dout, *dhT;
+    float scale;
+    float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dh0;
+    float *ws;       // B * n_chunks * H per-chunk buffers (BwdLayout)
+    float *scratch;  // n_groups * BwdLayout::scratch() floats
+    int B, T, H, n_chunks, n_groups;
+};
+
+// hipSuccess or the first launch error.
+hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, hipStream_t stream);
+
+}  // namespace kda

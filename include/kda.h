@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -226,6 +226,43 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
                               const void *q, const void *k, const void *v,
                               const void *a, const float *A_log, const float *dt_bias, const float *b,
                               float scale, float *state, void *o, void *stream);
+
+/*
+ * kda_chunk_bwd -- the backward pass of kda_chunk_fwd: the gradients of a loss
+ * with respect to q, k, v, log_alpha, beta and h0, given its gradients with
+ * respect to o (dout) and to the final state (dhT).
+ *
+ * The pages derive no gradient (the essay "22,580: from GPT-2 to Kimi K3" notes
+ * that training runs the chunked form of sections 6.2-6.3); this is the exact
+ * reverse-mode derivative of the recurrence at the top of this header, computed
+ * chunk by chunk: the chunk-local forward quantities, the chunk-start states in
+ * order, the state gradients in reverse order, then the chunk-local gradients.
+ *
+ * Arguments
+ *   B, T, H, d_k, d_v   equal-length sequences [B, T, H, d] (no cu_seqlens);
+ *               d_k, d_v in {64, 128}; B, H <= 65535.
+ *   chunk       64.   io   KDA_F32 only (other dtypes KDA_ERR_UNSUPPORTED).
+ *   q, k, v, log_alpha, beta, scale, h0   the forward call's inputs (h0 NULL =
+ *               zero initial state).
+ *   dout        [B, T, H, d_v] fp32, the gradient with respect to o.
+ *   dhT         [B, H, d_k, d_v] fp32 or NULL (zero): with respect to hT.
+ *   dq, dk      [B, T, H, d_k];  dv [B, T, H, d_v];  dlog_alpha [B, T, H, d_k];
+ *               dbeta [B, T, H]: written, fp32, none overlapping any argument.
+ *   dh0         [B, H, d_k, d_v] fp32 or NULL (not computed).
+ *   workspace   kda_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned
+ *               (about 300 KB per (chunk, head) at d = 128, plus a fixed scratch
+ *               of at most 1024 x 770 KB): the chunk-local matrices, the
+ *               chunk-start states and the state gradients.
+ * Gate values as for kda_chunk_fwd. Errors as for the other entry points.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, int io);
+
+int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                  const void *q, const void *k, const void *v,
+                  const float *log_alpha, const float *beta, float scale,
+                  const float *h0, const void *dout, const float *dhT,
+                  void *dq, void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dh0,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Full-attention decode over a KV cache: the comparator of the decode step

@@ -225,6 +225,14 @@ def gen_attn_decode_device(B, H, H_kv, T_max, d, dtype, seed, device):
     return dict(q=q, k_cache=k, v_cache=v)
 
 
+def gen_grad_outputs(B, T, H, dk, dv, seed):
+    """Loss gradients for the backward pass: dout [B, T, H, dv] and dhT [B, H, dk, dv], both
+    N(0,1) fp32."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0xB2]))
+    return dict(dout=rng.standard_normal((B, T, H, dv), dtype=np.float32),
+                dhT=rng.standard_normal((B, H, dk, dv), dtype=np.float32))
+
+
 def gen_workload(w: Workload, seed: Optional[int] = None):
     return gen_sequences(w.seqlens, w.H, w.dk, w.dv, w.io, w.gates, w.h0,
                          w.seed if seed is None else seed)

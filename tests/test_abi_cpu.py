@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing, misaligned or too small")]:
         assert lib.kda_status_string(code) == text
     assert lib.kda_status_string(99) == b"unknown status"
@@ -242,3 +242,48 @@ def test_attn_decode_workspace(lib):
     assert attn(lib, T_max=5000, ws=None) == WORKSPACE
     assert attn(lib, T_max=5000, ws=A + 16) == WORKSPACE
     assert attn(lib, T_max=5000, ws_bytes=1000) == WORKSPACE
+
+
+# ---- backward pass (kda_chunk_bwd)
+
+def bwd(lib, **kw):
+    a = dict(B=2, T=100, H=4, dk=64, dv=64, chunk=64, io=F32, q=A, k=A, v=A, la=A, beta=A, scale=0.125, h0=None,
+             dout=A, dhT=None, dq=0x4000000, dk_=0x5000000, dv_=0x6000000, dla=0x7000000, dbeta=0x8000000,
+             dh0=None, ws=0x10000000, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"], a["k"], a["v"],
+                             a["la"], a["beta"], a["scale"], a["h0"], a["dout"], a["dhT"], a["dq"], a["dk_"],
+                             a["dv_"], a["dla"], a["dbeta"], a["dh0"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), OK), (dict(T=0), OK),                      # nothing to do (no dh0 asked for)
+    (dict(B=-1), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
+    (dict(io=BF16), UNSUPPORTED), (dict(io=5), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
+    (dict(dk=96), UNSUPPORTED), (dict(B=65536, T=1, H=1), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(dout=None), INVALID), (dict(dq=None), INVALID), (dict(dbeta=None), INVALID),
+    (dict(q=A + 8), INVALID), (dict(beta=A + 2), INVALID), (dict(dh0=0x9000000 + 4), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(dq=A), INVALID),                                 # an output on an input
+    (dict(dk_=0x4000000 + 64), INVALID),                   # two outputs overlapping
+    (dict(ws=None), WORKSPACE), (dict(ws=0x10000000 + 64), WORKSPACE), (dict(ws_bytes=4096), WORKSPACE),
+    (dict(ws=A), INVALID),                                 # the workspace on an input
+])
+def test_chunk_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_chunk_bwd_workspace(lib):
+    ws = lib.kda_chunk_bwd_workspace_bytes
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    C = 64
+
+    def expect(B, T, H, dk, dv):
+        per = 2 * C * C + 3 * C * dk + C * dv + dk + 2 * dk * dv
+        scr = 15 * C * dk + 6 * C * dv + 5 * C * C + C + 2 * dk
+        units = B * ((T + C - 1) // C) * H
+        return r(units * per * 4) + r(min(units, 1024) * scr * 4) if units else 0
+
+    for args in ((2, 100, 4, 64, 64), (8, 8192, 32, 128, 128), (1, 1, 1, 64, 128), (3, 0, 2, 128, 64)):
+        assert ws(*args, 64, F32) == expect(*args), args
+    assert ws(2, 100, 4, 64, 64, 64, BF16) == 0 and ws(2, 100, 4, 64, 64, 128, F32) == 0

@@ -1,0 +1,88 @@
+"""GPU parity of the backward pass (kda_chunk_bwd, through its C ABI) against the fp64
+oracle (autograd of the token loop, itself pinned by finite differences of the C forward
+oracle).
+
+Bar: relative L2 error of every gradient (dq, dk, dv, dlog_alpha, dbeta, dh0), each over
+its whole tensor, <= 1e-4 (the library's fp32 bar). Inputs are seeded synthetic draws
+(kda_synth): the forward workload recipe, and N(0,1) loss gradients.
+"""
+import numpy as np
+import pytest
+
+import kda_synth
+import oracle
+from kda_testlib import TOL, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0")
+
+
+def _inputs(B, T, H, dk, dv, gates, seed, h0=True, dhT=True):
+    x = kda_synth.gen_sequences((T,) * B, H, dk, dv, "f32", gates, "normal" if h0 else "zero", seed)
+    shp = lambda a: a.reshape((B, T) + a.shape[1:])  # noqa: E731
+    d = {n: shp(x[n]) for n in ("q", "k", "v", "log_alpha", "beta")}
+    d["h0"] = x["h0"] if h0 else None
+    g = kda_synth.gen_grad_outputs(B, T, H, dk, dv, seed)
+    d["dout"] = g["dout"]
+    d["dhT"] = g["dhT"] if dhT else None
+    return d
+
+
+def _run(d, scale, heads=None):
+    import torch
+    import gated_delta_rule_48_amd as kda
+    t = {n: (None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()) for n, x in d.items()}
+    out = kda.chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["dout"], scale=scale, h0=t["h0"],
+                        dhT=t["dhT"])
+    torch.cuda.synchronize()
+    return {n: (None if x is None else x.cpu().numpy()) for n, x in zip(NAMES, out)}
+
+
+def _check(name, B, T, H, dk, dv, gates="main", seed=0, h0=True, dhT=True):
+    say(f"[{name}] B={B} T={T} H={H} dk={dk} dv={dv} gates={gates} h0={h0} dhT={dhT}")
+    d = _inputs(B, T, H, dk, dv, gates, seed, h0, dhT)
+    scale = dk ** -0.5
+    got = _run(d, scale)
+    ref = oracle.kda_backward_reference(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], scale, d["dout"],
+                                        dhT=d["dhT"], h0=d["h0"])
+    errs = {}
+    for n in NAMES:
+        if n == "dh0" and not h0:
+            assert got[n] is None
+            continue
+        assert np.all(np.isfinite(got[n])), n
+        errs[n] = rel_l2(got[n], ref[n])
+    say(f"[{name}] rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL["f32"], (n, e)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T", [64, 100, 200])
+def test_bwd_shapes(dk, dv, T):
+    _check("bwd", 2, T, 2, dk, dv, seed=T + dk + dv)
+
+
+def test_bwd_strong_gates_and_short_sequences():
+    _check("strong", 2, 130, 2, 128, 128, gates="strong", seed=3)
+    _check("short", 3, 1, 2, 64, 64, seed=4)
+    _check("weak", 1, 65, 3, 64, 64, gates="weak", seed=5)
+
+
+def test_bwd_without_h0_or_dhT():
+    _check("no-h0", 2, 90, 2, 64, 64, seed=6, h0=False)
+    _check("no-dhT", 2, 90, 2, 64, 64, seed=7, dhT=False)
+
+
+def test_bwd_empty_sequence():
+    # T = 0: every gradient is empty and dh0 = dhT
+    import torch
+    import gated_delta_rule_48_amd as kda
+    B, H, d = 2, 3, 64
+    z = lambda *s: torch.zeros(s, device="cuda")  # noqa: E731
+    dhT = torch.randn(B, H, d, d, device="cuda")
+    out = kda.chunk_bwd(z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H), z(B, 0, H, d),
+                        h0=torch.randn(B, H, d, d, device="cuda"), dhT=dhT)
+    torch.cuda.synchronize()
+    assert torch.equal(out[5], dhT)
+    assert all(x.numel() == 0 for x in out[:5])

@@ -18,7 +18,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
-SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip", "kda_attn.hip"]
+SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip", "kda_attn.hip", "kda_bwd.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
@@ -57,7 +57,9 @@ def resources():
 def test_every_kernel_is_reported(resources):
     names = " ".join(resources)
     for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_decode_kernel",
-              "kda_chunk_offsets_kernel", "kda_attn_decode_kernel", "kda_attn_combine_kernel"):
+              "kda_chunk_offsets_kernel", "kda_attn_decode_kernel", "kda_attn_combine_kernel",
+              "kda_bwd_chunk_fwd_kernel", "kda_bwd_states_kernel", "kda_bwd_state_grads_kernel",
+              "kda_bwd_chunk_grads_kernel"):
         assert k in names, k
 
 

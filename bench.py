@@ -374,6 +374,50 @@ def bench_attn(args, kda, torch, name, dec):
     return out
 
 
+def bench_bwd(args, kda, torch):
+    """The backward pass (kda_chunk_bwd, fp32) on the batched workload's shape: B=8, T=8192,
+    H=32, d=128, chunk 64, inputs and loss gradients drawn on the GPU (torch's seeded generator)."""
+    B, T, H, d = 8, 8192, 32, 128
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating backward inputs: B={B} T={T} H={H} d={d} fp32")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+    rn = lambda *s: torch.randn(s, generator=g, device=dev)  # noqa: E731
+    q = torch.nn.functional.normalize(rn(B, T, H, d), dim=-1)
+    k = torch.nn.functional.normalize(rn(B, T, H, d), dim=-1)
+    v, dout = rn(B, T, H, d), rn(B, T, H, d)
+    la = -0.1 * torch.nn.functional.softplus(rn(B, T, H, d))
+    beta = torch.sigmoid(rn(B, T, H))
+    dhT = rn(B, H, d, d)
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(B, T, H, d, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_bwd(q, k, v, la, beta, dout, dhT=dhT, workspace=ws)
+
+    spin_up(torch, step, args.spin_up)
+    step()
+    torch.cuda.synchronize()
+    n = args.bwd_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    # algorithmic bytes: q, k, v, log alpha, dout read and dq, dk, dv, dlog alpha written (fp32, d each),
+    # beta and dbeta, dhT read
+    alg = B * T * H * (9 * d * 4 + 2 * 4) + B * H * d * d * 4
+    achieved = alg / (ms * 1e-3) / 1e9
+    log(f"[bench] backward: {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s algorithmic")
+    del q, k, v, dout, la, beta, dhT, ws
+    torch.cuda.empty_cache()
+    return {"value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 3), "steps": n,
+            "workload": f"backward of the batched prefill: B={B} x T={T}, H={H}, d_k=d_v={d}, chunk 64, fp32",
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
+
+
 def cpu_baseline(pre, args):
     """The fp64 oracle on the prefill workload's first `--cpu-seqs` sequences (all
     of them by default: all heads, full length), on this host's cores."""
@@ -418,6 +462,8 @@ def main():
                     help="attention-decode comparator workloads to time (" + ", ".join(kda_synth.ATTN_WORKLOADS) +
                          "; empty for none)")
     ap.add_argument("--attn-steps", type=int, default=50)
+    ap.add_argument("--bwd", action="store_true", help="also time the backward pass (fp32) on the batched shape")
+    ap.add_argument("--bwd-steps", type=int, default=3)
     ap.add_argument("--workloads", default="", metavar="NAMES",
                     help="comma-separated further prefill workloads to time and report (" +
                          ", ".join(n for n in kda_synth.WORKLOADS if n != "batched") + ")")
@@ -440,6 +486,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, kda, torch)
     others = {n: bench_workload(args, kda, torch, n) for n in args.workloads.split(",") if n}
     attn = {n: bench_attn(args, kda, torch, n, dec) for n in args.attn.split(",") if n}
+    bwd = bench_bwd(args, kda, torch) if args.bwd else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
 
     w = pre["workload"]
@@ -476,6 +523,8 @@ def main():
                                        "alg_bytes_per_launch": dec["alg_bytes"]}}
     if attn:
         line["attn_decode"] = attn
+    if bwd is not None:
+        line["backward"] = bwd
     if others:
         line["workloads"] = others
     print(json.dumps(line), flush=True)

@@ -40,10 +40,10 @@
 // e^gamma, in parallel over (chunk, head); (2) the chunk-start states, in order
 // over the chunks of each (sequence, head, 16 state columns); (3) the state
 // gradients dS', in reverse order likewise, and dh0; (4) the chunk-local
-// gradients, in parallel over (chunk, head). Everything is fp32 on the vector
-// ALUs, the chunk matrices in a per-workgroup scratch in global memory, the
-// products by a plain 4 x 4 register-tiled loop: the direct form of this pass,
-// not tuned.
+// gradients, in parallel over (chunk, head). Everything is fp32, the chunk
+// matrices in a per-workgroup scratch in global memory, the products on the
+// matrix cores in fp32 with their operands read straight from that memory: the
+// direct form of this pass, not tuned further.
 
 #include "kda_bwd.hpp"
 
@@ -52,41 +52,69 @@ namespace {
 
 constexpr int C = kBwdChunk;
 
-// D = alpha op(A) op(B) + beta D over the workgroup (beta = 0 overwrites D).
-// op(A) is M x K: A row-major with leading dimension lda, or stored K x M (TA).
-// op(B) is K x N: B stored K x N with leading dimension ldb, or N x K (TB).
-// M and N are multiples of 4; each thread computes 4 x 4 tiles of D, consecutive
-// threads along a row of tiles. A later call with the same M and N gives every
-// thread the same tiles, so it may accumulate into D without a barrier.
-template <bool TA, bool TB>
-__device__ void gemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-                     float beta, float *D, int ldd) {
-    const int tn = N / 4, tiles = (M / 4) * tn;
-    for (int t = threadIdx.x; t < tiles; t += kBwdThreads) {
-        const int i0 = (t / tn) * 4, j0 = (t % tn) * 4;
-        float acc[4][4];
+// Staging buffers of gemm in LDS: a C x 16 slab of op(A) and a 16 x 128 slab of
+// op(B) (rows padded against bank conflicts).
+constexpr int kSlab = 16;
+struct Stage {
+    float a[C][kSlab + 1];
+    float b[kSlab][128 + 4];
+};
+
+// D = alpha op(A) op(B) + beta D over the workgroup (beta = 0 overwrites D);
+// every thread of the workgroup calls it. op(A) is C x K: A row-major with leading
+// dimension lda, or stored K x C (TA). op(B) is K x N: B stored K x N with leading
+// dimension ldb, or N x K (TB). N is 64 or 128 and K a multiple of 16. The
+// operands pass through LDS in slabs of 16 contraction indices, read once from
+// memory; each wave computes 16 x 16 tiles of D on the matrix cores
+// (v_mfma_f32_16x16x4_f32: lane l supplies op(A)[l%16][k + l/16] and
+// op(B)[k + l/16][l%16] and holds D[4 (l/16) + i][l%16]). A later call with the
+// same N gives every lane the same elements of D, so it may accumulate into D
+// without a barrier of its own.
+template <bool TA, bool TB, int N, int K>
+__device__ void gemm(Stage &st, float alpha, const float *A, int lda, const float *B, int ldb, float beta, float *D,
+                     int ldd) {
+    static_assert((N == 64 || N == 128) && K % kSlab == 0, "gemm shape");
+    constexpr int M = C, tn = N / 16, tiles = (M / 16) * tn, kMaxTiles = tiles / (kBwdThreads / 64);
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, r = l & 15, kq = l >> 4;
+    f32x4 acc[kMaxTiles];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-        for (int kk = 0; kk < K; ++kk) {
-            float x[4], y[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = TA ? A[kk * lda + i0 + r] : A[(i0 + r) * lda + kk];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) y[c] = TB ? B[(j0 + c) * ldb + kk] : B[kk * ldb + j0 + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(x[r], y[c], acc[r][c]);
+    for (int q = 0; q < kMaxTiles; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += kSlab) {
+        for (int idx = tid; idx < M * kSlab; idx += kBwdThreads) {
+            const int m = TA ? idx % M : idx / kSlab, kk = TA ? idx / M : idx % kSlab;
+            st.a[m][kk] = TA ? A[(k0 + kk) * lda + m] : A[m * lda + k0 + kk];
         }
+        for (int idx = tid; idx < kSlab * N; idx += kBwdThreads) {
+            const int n = TB ? idx / kSlab : idx % N, kk = TB ? idx % kSlab : idx / N;
+            st.b[kk][n] = TB ? B[n * ldb + k0 + kk] : B[(k0 + kk) * ldb + n];
+        }
+        __syncthreads();
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int q = 0; q < kMaxTiles; ++q) {
+            const int t = w + 4 * q;
+            {
+                const int i0 = (t / tn) * 16, j0 = (t % tn) * 16;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float *d = D + (i0 + r) * ldd + j0 + c;
-                *d = beta == 0.f ? alpha * acc[r][c] : fmaf(alpha, acc[r][c], beta * *d);
+                for (int kk = 0; kk < kSlab; kk += 4)
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.a[i0 + r][kk + kq], st.b[kk + kq][j0 + r],
+                                                                  acc[q], 0, 0, 0);
             }
+            // one tile's operands in flight at a time (keeps the register count down)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxTiles; ++q) {
+        const int t = w + 4 * q;
+        {
+            const int i0 = (t / tn) * 16, j0 = (t % tn) * 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float *d = D + (i0 + 4 * kq + i) * ldd + j0 + r;
+                *d = beta == 0.f ? alpha * acc[q][i] : fmaf(alpha, acc[q][i], beta * *d);
+            }
+        }
     }
 }
 
@@ -180,6 +208,7 @@ template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     __shared__ float sA[C][C + 1];
+    __shared__ Stage st;
     const Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
     const int tid = threadIdx.x, total = a.B * a.n_chunks * a.H;
     for (int ch = blockIdx.x; ch < total; ch += gridDim.x) {
@@ -197,8 +226,8 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
         }
         for (int i = tid; i < DK; i += kBwdThreads) cb[L.oEg() + i] = expf(S.gam[i]);
         __syncthreads();
-        gemm<false, true>(C, C, DK, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);
-        gemm<false, true>(C, C, DK, a.scale, S.Qe, DK, S.N, DK, 0.f, cb + L.oAqk(), C);
+        gemm<false, true, C, DK>(st, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);
+        gemm<false, true, C, DK>(st, a.scale, S.Qe, DK, S.N, DK, 0.f, cb + L.oAqk(), C);
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads) {
             const int r = idx / C, i = idx % C;
@@ -220,8 +249,8 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
             for (int r = 0; r < C; ++r) cb[L.oT() + r * C + tid] = x[r];
         }
         __syncthreads();
-        gemm<false, false>(C, DK, C, 1.f, cb + L.oT(), C, S.Bk, DK, 0.f, cb + L.oW(), DK);
-        gemm<false, false>(C, DV, C, 1.f, cb + L.oT(), C, S.Bv, DV, 0.f, cb + L.oUt(), DV);
+        gemm<false, false, DK, C>(st, 1.f, cb + L.oT(), C, S.Bk, DK, 0.f, cb + L.oW(), DK);
+        gemm<false, false, DV, C>(st, 1.f, cb + L.oT(), C, S.Bv, DV, 0.f, cb + L.oUt(), DV);
         __syncthreads();
     }
 }
@@ -321,6 +350,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArg
 template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
+    __shared__ Stage st;
     const Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
     const int tid = threadIdx.x, total = a.B * a.n_chunks * a.H;
     const float s = a.scale;
@@ -335,26 +365,26 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         chunk_factors<DK, DV>(S);
         for (int idx = tid; idx < C * DV; idx += kBwdThreads) S.U[idx] = Ut[idx];
         __syncthreads();
-        gemm<false, true>(C, C, DK, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);           // P N^T
-        gemm<false, false>(C, DV, DK, -1.f, W, DK, S0, DV, 1.f, S.U, DV);          // U = U~ - W S
-        gemm<true, false>(C, DV, C, 1.f, Aqk, C, S.dO, DV, 0.f, S.dU, DV);         // dU = Aqk^T dO
-        gemm<false, false>(C, DV, DK, 1.f, Rm, DK, dS1, DV, 1.f, S.dU, DV);        //    + R dS'
-        gemm<false, true>(C, DK, DV, 1.f, S.dO, DV, S0, DV, 0.f, S.dQO, DK);       // dQO = dO S^T
+        gemm<false, true, C, DK>(st, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);           // P N^T
+        gemm<false, false, DV, DK>(st, -1.f, W, DK, S0, DV, 1.f, S.U, DV);          // U = U~ - W S
+        gemm<true, false, DV, C>(st, 1.f, Aqk, C, S.dO, DV, 0.f, S.dU, DV);         // dU = Aqk^T dO
+        gemm<false, false, DV, DK>(st, 1.f, Rm, DK, dS1, DV, 1.f, S.dU, DV);        //    + R dS'
+        gemm<false, true, DK, DV>(st, 1.f, S.dO, DV, S0, DV, 0.f, S.dQO, DK);       // dQO = dO S^T
         __syncthreads();
-        gemm<false, true>(C, C, DV, 1.f, S.dO, DV, S.U, DV, 0.f, S.dAqk, C);       // dO U^T
-        gemm<false, true>(C, DK, DV, 1.f, S.U, DV, dS1, DV, 0.f, S.dR, DK);        // dR = U dS'^T
-        gemm<false, true>(C, DK, DV, -1.f, S.dU, DV, S0, DV, 0.f, S.dW, DK);       // dW = -dU S^T
-        gemm<true, false>(C, DV, C, 1.f, Tm, C, S.dU, DV, 0.f, S.dBv, DV);         // dBv = T^T dU
-        gemm<false, true>(C, C, DV, 1.f, S.dU, DV, S.Bv, DV, 0.f, S.dT, C);        // dT = dU Bv^T
+        gemm<false, true, C, DV>(st, 1.f, S.dO, DV, S.U, DV, 0.f, S.dAqk, C);       // dO U^T
+        gemm<false, true, DK, DV>(st, 1.f, S.U, DV, dS1, DV, 0.f, S.dR, DK);        // dR = U dS'^T
+        gemm<false, true, DK, DV>(st, -1.f, S.dU, DV, S0, DV, 0.f, S.dW, DK);       // dW = -dU S^T
+        gemm<true, false, DV, C>(st, 1.f, Tm, C, S.dU, DV, 0.f, S.dBv, DV);         // dBv = T^T dU
+        gemm<false, true, C, DV>(st, 1.f, S.dU, DV, S.Bv, DV, 0.f, S.dT, C);        // dT = dU Bv^T
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads)
             if (idx % C > idx / C) S.dAqk[idx] = 0.f;                               // lower, diagonal included
-        gemm<false, true>(C, C, DK, 1.f, S.dW, DK, S.Bk, DK, 1.f, S.dT, C);        //    + dW Bk^T
-        gemm<true, false>(C, DK, C, 1.f, Tm, C, S.dW, DK, 0.f, S.dBk, DK);         // dBk = T^T dW
+        gemm<false, true, C, DK>(st, 1.f, S.dW, DK, S.Bk, DK, 1.f, S.dT, C);        //    + dW Bk^T
+        gemm<true, false, DK, C>(st, 1.f, Tm, C, S.dW, DK, 0.f, S.dBk, DK);         // dBk = T^T dW
         __syncthreads();
-        gemm<true, false>(C, C, C, 1.f, Tm, C, S.dT, C, 0.f, S.Tmp, C);            // T^T dT
+        gemm<true, false, C, C>(st, 1.f, Tm, C, S.dT, C, 0.f, S.Tmp, C);            // T^T dT
         __syncthreads();
-        gemm<false, true>(C, C, C, -1.f, S.Tmp, C, Tm, C, 0.f, S.dA, C);           // dA = -T^T dT T^T
+        gemm<false, true, C, C>(st, -1.f, S.Tmp, C, Tm, C, 0.f, S.dA, C);           // dA = -T^T dT T^T
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads)
             if (idx % C >= idx / C) S.dA[idx] = 0.f;                                // strictly lower
@@ -376,10 +406,10 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads) S.dA[idx] *= S.bet[idx / C];  // diag(beta) dA
         __syncthreads();
-        gemm<false, false>(C, DK, C, 1.f, S.dA, C, S.N, DK, 0.f, S.dP, DK);        // dP = diag(beta) dA N
-        gemm<true, false>(C, DK, C, 1.f, S.dA, C, S.P, DK, 0.f, S.dN, DK);         // dN = (diag(beta) dA)^T P
-        gemm<true, false>(C, DK, C, s, S.dAqk, C, S.Qe, DK, 1.f, S.dN, DK);        //    + s dAqk^T Qe
-        gemm<false, false>(C, DK, C, s, S.dAqk, C, S.N, DK, 0.f, S.dQe, DK);       // dQe = s dAqk N
+        gemm<false, false, DK, C>(st, 1.f, S.dA, C, S.N, DK, 0.f, S.dP, DK);        // dP = diag(beta) dA N
+        gemm<true, false, DK, C>(st, 1.f, S.dA, C, S.P, DK, 0.f, S.dN, DK);         // dN = (diag(beta) dA)^T P
+        gemm<true, false, DK, C>(st, s, S.dAqk, C, S.Qe, DK, 1.f, S.dN, DK);        //    + s dAqk^T Qe
+        gemm<false, false, DK, C>(st, s, S.dAqk, C, S.N, DK, 0.f, S.dQe, DK);       // dQe = s dAqk N
         __syncthreads();
         for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
             const int r = idx / DK, i = idx % DK;

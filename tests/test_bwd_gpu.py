@@ -86,3 +86,30 @@ def test_bwd_empty_sequence():
     torch.cuda.synchronize()
     assert torch.equal(out[5], dhT)
     assert all(x.numel() == 0 for x in out[:5])
+
+
+def test_bwd_full_size_sampled():
+    """The backward at the batched workload's shape (B=8, T=8192, H=32, d=128, fp32, weak
+    gates, as `bench.py --bwd` times it): the whole batch on the GPU, the oracle on two
+    sampled (sequence, head) pairs over their full length."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    w = kda_synth.WORKLOADS["batched"]
+    B, T, H, d = len(w.seqlens), w.seqlens[0], w.H, w.dk
+    say(f"[bwd-full] B={B} T={T} H={H} d={d} fp32 gates={w.gates}")
+    x = kda_synth.gen_sequences(w.seqlens, H, d, d, "f32", w.gates, "zero", w.seed)
+    gr = kda_synth.gen_grad_outputs(B, T, H, d, d, w.seed)
+    t = {n: torch.from_numpy(x[n].reshape((B, T) + x[n].shape[1:])).cuda()
+         for n in ("q", "k", "v", "log_alpha", "beta")}
+    dout, dhT = torch.from_numpy(gr["dout"]).cuda(), torch.from_numpy(gr["dhT"]).cuda()
+    out = kda.chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], dout, scale=d ** -0.5, dhT=dhT)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = lambda a: a[b:b + 1, :, h:h + 1].cpu().numpy()  # noqa: E731
+        ref = oracle.kda_backward_reference(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["log_alpha"]),
+                                            sl(t["beta"]), d ** -0.5, gr["dout"][b:b + 1, :, h:h + 1],
+                                            dhT=gr["dhT"][b:b + 1, h:h + 1])
+        errs = {n: rel_l2(sl(out[i]), ref[n]) for i, n in enumerate(NAMES[:5])}
+        say(f"[bwd-full] (b={b}, h={h}) rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL["f32"], (n, e)

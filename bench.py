@@ -374,6 +374,23 @@ def bench_attn(args, kda, torch, name, dec):
     return out
 
 
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix (and vector) peak
+
+
+def bwd_algorithmic_flops(B, T, H, dk, dv, C=64):
+    """Flops of the backward pass's products per call (2 per multiply-add), each counted once:
+    the chunk-local forward (P N^T, Qe N^T, T Bk, T Bv), the state recursion (W S, R^T U), the
+    state-gradient recursion (Aqk^T dO, R dS', QO^T dO, W^T dU) and the chunk-local gradients
+    (dO S^T, dO U^T, U dS'^T, dU S^T, T^T dU, dU Bv^T, dW Bk^T, T^T dW, T^T dT, (T^T dT) T^T,
+    dA N, dA^T P, dAqk^T Qe, dAqk N). Elementwise work and the triangular solve are not counted."""
+    macs = (2 * C * C * dk + C * dk * C + C * dv * C            # chunk-local forward
+            + C * dv * dk + dk * dv * C                         # states
+            + C * dv * C + C * dv * dk + dk * dv * C + dk * dv * C  # state gradients
+            + 3 * C * dk * dv + C * C * dv + C * dv * C + C * C * dv + C * C * dk + C * dk * C
+            + 2 * C * C * C + 4 * C * dk * C)                   # chunk-local gradients
+    return 2 * macs * B * ((T + C - 1) // C) * H
+
+
 def bench_bwd(args, kda, torch):
     """The backward pass (kda_chunk_bwd, fp32) on the batched workload's shape: B=8, T=8192,
     H=32, d=128, chunk 64, inputs and loss gradients drawn on the GPU (torch's seeded generator)."""
@@ -405,17 +422,19 @@ def bench_bwd(args, kda, torch):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    # algorithmic bytes: q, k, v, log alpha, dout read and dq, dk, dv, dlog alpha written (fp32, d each),
-    # beta and dbeta, dhT read
-    alg = B * T * H * (9 * d * 4 + 2 * 4) + B * H * d * d * 4
-    achieved = alg / (ms * 1e-3) / 1e9
-    log(f"[bench] backward: {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s algorithmic")
+    # bound: the products, in fp32 on the matrix cores (the inputs and gradients themselves are
+    # 9.7 GB, 1.2 ms of HBM time at 8 TB/s)
+    flops = bwd_algorithmic_flops(B, T, H, d, d)
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] backward: {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, {achieved:.1f} TFLOP/s "
+        "algorithmic (fp32)")
     del q, k, v, dout, la, beta, dhT, ws
     torch.cuda.empty_cache()
     return {"value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 3), "steps": n,
             "workload": f"backward of the batched prefill: B={B} x T={T}, H={H}, d_k=d_v={d}, chunk 64, fp32",
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MATRIX_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / FP32_MATRIX_PEAK_TFLOPS, 4),
+                         "alg_flops_per_call": flops}}
 
 
 def cpu_baseline(pre, args):

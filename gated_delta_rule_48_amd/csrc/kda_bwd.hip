@@ -52,108 +52,110 @@ namespace {
 
 constexpr int C = kBwdChunk;
 
-// Staging buffers of gemm in LDS: a C x 16 slab of op(A) and a 16 x 128 slab of
-// op(B) (rows padded against bank conflicts).
-constexpr int kSlab = 16;
+// Staging buffers of gemm in LDS: all of op(A) (C x K) and op(B) (K x N), K and N
+// up to 128 (rows padded against bank conflicts).
+constexpr int kMaxK = 128;
 struct Stage {
-    float a[C][kSlab + 1];
-    float b[kSlab][128 + 4];
+    float a[C][kMaxK + 1];
+    float b[kMaxK][128 + 4];
 };
 
 // D = alpha op(A) op(B) + beta D over the workgroup (beta = 0 overwrites D);
 // every thread of the workgroup calls it. op(A) is C x K: A row-major with leading
 // dimension lda, or stored K x C (TA). op(B) is K x N: B stored K x N with leading
-// dimension ldb, or N x K (TB). N is 64 or 128 and K a multiple of 16. The
-// operands pass through LDS in slabs of 16 contraction indices, read once from
-// memory; each wave computes 16 x 16 tiles of D on the matrix cores
-// (v_mfma_f32_16x16x4_f32: lane l supplies op(A)[l%16][k + l/16] and
-// op(B)[k + l/16][l%16] and holds D[4 (l/16) + i][l%16]). A later call with the
-// same N gives every lane the same elements of D, so it may accumulate into D
-// without a barrier of its own.
+// dimension ldb, or N x K (TB). N is 64 or 128, K 64 or 128. Both operands are
+// first copied whole into LDS (all loads in flight at once), then each wave
+// computes 16 x 16 tiles of D on the matrix cores (v_mfma_f32_16x16x4_f32: lane l
+// supplies op(A)[l%16][k + l/16] and op(B)[k + l/16][l%16] and holds
+// D[4 (l/16) + i][l%16]). A later call with the same N gives every lane the same
+// elements of D, so it may accumulate into D without a barrier of its own.
 template <bool TA, bool TB, int N, int K>
 __device__ void gemm(Stage &st, float alpha, const float *A, int lda, const float *B, int ldb, float beta, float *D,
                      int ldd) {
-    static_assert((N == 64 || N == 128) && K % kSlab == 0, "gemm shape");
+    static_assert((N == 64 || N == 128) && (K == 64 || K == 128), "gemm shape");
     constexpr int M = C, tn = N / 16, tiles = (M / 16) * tn, kMaxTiles = tiles / (kBwdThreads / 64);
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, r = l & 15, kq = l >> 4;
-    f32x4 acc[kMaxTiles];
+    // op(A) into st.a[m][k], four consecutive elements of A per load
+    for (int idx = tid; idx < M * K / 4; idx += kBwdThreads) {
+        if (TA) {  // A row kk holds op(A)[.][kk]
+            const int kk = idx / (M / 4), m = 4 * (idx % (M / 4));
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(A + kk * lda + m);
 #pragma unroll
-    for (int q = 0; q < kMaxTiles; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += kSlab) {
-        for (int idx = tid; idx < M * kSlab; idx += kBwdThreads) {
-            const int m = TA ? idx % M : idx / kSlab, kk = TA ? idx / M : idx % kSlab;
-            st.a[m][kk] = TA ? A[(k0 + kk) * lda + m] : A[m * lda + k0 + kk];
-        }
-        for (int idx = tid; idx < kSlab * N; idx += kBwdThreads) {
-            const int n = TB ? idx / kSlab : idx % N, kk = TB ? idx % kSlab : idx / N;
-            st.b[kk][n] = TB ? B[n * ldb + k0 + kk] : B[(k0 + kk) * ldb + n];
-        }
-        __syncthreads();
+            for (int e = 0; e < 4; ++e) st.a[m + e][kk] = v[e];
+        } else {
+            const int m = idx / (K / 4), kk = 4 * (idx % (K / 4));
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(A + m * lda + kk);
 #pragma unroll
-        for (int q = 0; q < kMaxTiles; ++q) {
-            const int t = w + 4 * q;
-            {
-                const int i0 = (t / tn) * 16, j0 = (t % tn) * 16;
-#pragma unroll
-                for (int kk = 0; kk < kSlab; kk += 4)
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.a[i0 + r][kk + kq], st.b[kk + kq][j0 + r],
-                                                                  acc[q], 0, 0, 0);
-            }
-            // one tile's operands in flight at a time (keeps the register count down)
-            __builtin_amdgcn_sched_barrier(0);
+            for (int e = 0; e < 4; ++e) st.a[m][kk + e] = v[e];
         }
-        __syncthreads();
     }
+    __builtin_amdgcn_sched_barrier(0);  // op(A)'s loads before op(B)'s: fewer registers in flight
+    // op(B) into st.b[k][n]
+    for (int idx = tid; idx < K * N / 4; idx += kBwdThreads) {
+        if (TB) {  // B row n holds op(B)[.][n]
+            const int n = idx / (K / 4), kk = 4 * (idx % (K / 4));
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(B + n * ldb + kk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.b[kk + e][n] = v[e];
+        } else {
+            const int kk = idx / (N / 4), n = 4 * (idx % (N / 4));
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(B + kk * ldb + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.b[kk][n + e] = v[e];
+        }
+    }
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < kMaxTiles; ++q) {
-        const int t = w + 4 * q;
-        {
-            const int i0 = (t / tn) * 16, j0 = (t % tn) * 16;
+        const int t = w + 4 * q, i0 = (t / tn) * 16, j0 = (t % tn) * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int k = 0; k < K; k += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.a[i0 + r][k + kq], st.b[k + kq][j0 + r], acc, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float *d = D + (i0 + 4 * kq + i) * ldd + j0 + r;
-                *d = beta == 0.f ? alpha * acc[q][i] : fmaf(alpha, acc[q][i], beta * *d);
-            }
+        for (int i = 0; i < 4; ++i) {
+            float *d = D + (i0 + 4 * kq + i) * ldd + j0 + r;
+            *d = beta == 0.f ? alpha * acc[i] : fmaf(alpha, acc[i], beta * *d);
         }
     }
+    __syncthreads();  // the staging buffers are free again
 }
 
-// The scratch of one workgroup of the chunk-local kernels (BwdLayout::scratch()).
+// The scratch of one workgroup of the chunk-local kernels (BwdLayout::scratch()):
+// 15 C x dk, 6 C x dv and 5 C x C matrices at fixed offsets from one base (so that
+// only the base stays in registers). The prefix g (later its gradient), gamma, m and
+// beta are kept in LDS instead (the members G, gam, m, bet).
 template <int DK, int DV> struct Scr {
-    float *Q, *K, *V, *dO, *G, *P, *N, *Qe, *Bk, *Bv, *U, *dU, *dQO, *dR, *dW, *dBv, *dBk, *dQe, *dP, *dN, *dG;
-    float *PN, *dAqk, *dT, *Tmp, *dA, *bet, *m, *gam;
-    __device__ explicit Scr(float *p) {
-        constexpr int ck = C * DK, cv = C * DV, cc = C * C;
-        Q = p;
-        K = Q + ck;
-        G = K + ck;
-        P = G + ck;
-        N = P + ck;
-        Qe = N + ck;
-        Bk = Qe + ck;
-        dQO = Bk + ck;
-        dR = dQO + ck;
-        dW = dR + ck;
-        dBk = dW + ck;
-        dQe = dBk + ck;
-        dP = dQe + ck;
-        dN = dP + ck;
-        dG = dN + ck;
-        V = dG + ck;  // 15 C x dk matrices, then 6 C x dv
-        dO = V + cv;
-        Bv = dO + cv;
-        U = Bv + cv;
-        dU = U + cv;
-        dBv = dU + cv;
-        PN = dBv + cv;  // then 5 C x C
-        dAqk = PN + cc;
-        dT = dAqk + cc;
-        Tmp = dT + cc;
-        dA = Tmp + cc;
-        bet = dA + cc;
-        m = bet + C;
-        gam = m + DK;
-    }
+    static constexpr int ck = C * DK, cv = C * DV, cc = C * C;
+    float *base;
+    float *G, *m, *gam, *bet;
+    __device__ explicit Scr(float *p) : base(p), G(nullptr), m(nullptr), gam(nullptr), bet(nullptr) {}
+    __device__ __forceinline__ float *Q() const { return base + 0 * ck; }
+    __device__ __forceinline__ float *K() const { return base + 1 * ck; }
+    __device__ __forceinline__ float *Gs() const { return base + 2 * ck; }
+    __device__ __forceinline__ float *P() const { return base + 3 * ck; }
+    __device__ __forceinline__ float *N() const { return base + 4 * ck; }
+    __device__ __forceinline__ float *Qe() const { return base + 5 * ck; }
+    __device__ __forceinline__ float *Bk() const { return base + 6 * ck; }
+    __device__ __forceinline__ float *dQO() const { return base + 7 * ck; }
+    __device__ __forceinline__ float *dR() const { return base + 8 * ck; }
+    __device__ __forceinline__ float *dW() const { return base + 9 * ck; }
+    __device__ __forceinline__ float *dBk() const { return base + 10 * ck; }
+    __device__ __forceinline__ float *dQe() const { return base + 11 * ck; }
+    __device__ __forceinline__ float *dP() const { return base + 12 * ck; }
+    __device__ __forceinline__ float *dN() const { return base + 13 * ck; }
+    __device__ __forceinline__ float *dG() const { return base + 14 * ck; }
+    __device__ __forceinline__ float *V() const { return base + 15 * ck + 0 * cv; }
+    __device__ __forceinline__ float *dO() const { return base + 15 * ck + 1 * cv; }
+    __device__ __forceinline__ float *Bv() const { return base + 15 * ck + 2 * cv; }
+    __device__ __forceinline__ float *U() const { return base + 15 * ck + 3 * cv; }
+    __device__ __forceinline__ float *dU() const { return base + 15 * ck + 4 * cv; }
+    __device__ __forceinline__ float *dBv() const { return base + 15 * ck + 5 * cv; }
+    __device__ __forceinline__ float *PN() const { return base + 15 * ck + 6 * cv + 0 * cc; }
+    __device__ __forceinline__ float *dAqk() const { return base + 15 * ck + 6 * cv + 1 * cc; }
+    __device__ __forceinline__ float *dT() const { return base + 15 * ck + 6 * cv + 2 * cc; }
+    __device__ __forceinline__ float *Tmp() const { return base + 15 * ck + 6 * cv + 3 * cc; }
+    __device__ __forceinline__ float *dA() const { return base + 15 * ck + 6 * cv + 4 * cc; }
 };
 
 __device__ __forceinline__ size_t row_of(const BwdArgs &a, int b, int t, int h) {
@@ -161,27 +163,32 @@ __device__ __forceinline__ size_t row_of(const BwdArgs &a, int b, int t, int h) 
 }
 
 // One chunk's inputs into the scratch (rows past the end zero), beta, the prefix
-// g of log alpha, gamma and m.
+// g of log alpha, gamma and m (these four in LDS). Every thread calls it.
 template <int DK, int DV>
 __device__ void load_chunk(const BwdArgs &a, int b, int h, int t0, int n, const Scr<DK, DV> &S, bool with_dout) {
     const int tid = threadIdx.x;
     for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
         const int r = idx / DK, i = idx % DK;
         const size_t off = row_of(a, b, t0 + r, h) * DK + i;
-        S.Q[idx] = r < n ? a.q[off] : 0.f;
-        S.K[idx] = r < n ? a.k[off] : 0.f;
+        S.Q()[idx] = r < n ? a.q[off] : 0.f;
+        S.K()[idx] = r < n ? a.k[off] : 0.f;
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int r = idx / DV, j = idx % DV;
         const size_t off = row_of(a, b, t0 + r, h) * DV + j;
-        S.V[idx] = r < n ? a.v[off] : 0.f;
-        if (with_dout) S.dO[idx] = r < n ? a.dout[off] : 0.f;
+        S.V()[idx] = r < n ? a.v[off] : 0.f;
+        if (with_dout) S.dO()[idx] = r < n ? a.dout[off] : 0.f;
     }
     for (int r = tid; r < C; r += kBwdThreads) S.bet[r] = r < n ? a.beta[row_of(a, b, t0 + r, h)] : 0.f;
-    for (int i = tid; i < DK; i += kBwdThreads) {
+    for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
+        const int r = idx / DK;
+        S.G[idx] = r < n ? a.log_alpha[row_of(a, b, t0 + r, h) * DK + idx % DK] : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < DK; i += kBwdThreads) {  // the prefix down each channel (G is in LDS)
         float g = 0.f;
         for (int r = 0; r < C; ++r) {
-            if (r < n) g += a.log_alpha[row_of(a, b, t0 + r, h) * DK + i];
+            g += S.G[r * DK + i];
             S.G[r * DK + i] = g;
         }
         S.gam[i] = g;
@@ -189,18 +196,25 @@ __device__ void load_chunk(const BwdArgs &a, int b, int h, int t0, int n, const 
     }
 }
 
+// Sum over the 64 lanes of a wave, left in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
 // P, N, Qe and Bk over C x dk, Bv over C x dv (after load_chunk and a barrier).
 template <int DK, int DV>
 __device__ void chunk_factors(const Scr<DK, DV> &S) {
     for (int idx = threadIdx.x; idx < C * DK; idx += kBwdThreads) {
         const int r = idx / DK, i = idx % DK;
-        const float g = S.G[idx], m = S.m[i], kv = S.K[idx];
-        S.P[idx] = kv * expf(g - m);
-        S.N[idx] = kv * expf(m - g);
-        S.Qe[idx] = S.Q[idx] * expf(g - m);
-        S.Bk[idx] = S.bet[r] * kv * expf(g);
+        const float g = S.G[idx], m = S.m[i], kv = S.K()[idx];
+        S.P()[idx] = kv * expf(g - m);
+        S.N()[idx] = kv * expf(m - g);
+        S.Qe()[idx] = S.Q()[idx] * expf(g - m);
+        S.Bk()[idx] = S.bet[r] * kv * expf(g);
     }
-    for (int idx = threadIdx.x; idx < C * DV; idx += kBwdThreads) S.Bv[idx] = S.bet[idx / DV] * S.V[idx];
+    for (int idx = threadIdx.x; idx < C * DV; idx += kBwdThreads) S.Bv()[idx] = S.bet[idx / DV] * S.V()[idx];
 }
 
 // (1) T, Aqk, W, U~, R, QO and e^gamma of every (chunk, head).
@@ -209,7 +223,12 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
     constexpr BwdLayout L{DK, DV};
     __shared__ float sA[C][C + 1];
     __shared__ Stage st;
-    const Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
+    __shared__ float lg[C * DK], lm[DK], lgam[DK], lbet[C];
+    Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
+    S.G = lg;  // the prefix, gamma, m and beta live in LDS
+    S.m = lm;
+    S.gam = lgam;
+    S.bet = lbet;
     const int tid = threadIdx.x, total = a.B * a.n_chunks * a.H;
     for (int ch = blockIdx.x; ch < total; ch += gridDim.x) {
         const int h = ch % a.H, c = (ch / a.H) % a.n_chunks, b = ch / (a.H * a.n_chunks);
@@ -221,17 +240,17 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
         for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
             const int i = idx % DK;
             const float g = S.G[idx];
-            cb[L.oR() + idx] = S.K[idx] * expf(S.gam[i] - g);
-            cb[L.oQO() + idx] = a.scale * S.Q[idx] * expf(g);
+            cb[L.oR() + idx] = S.K()[idx] * expf(S.gam[i] - g);
+            cb[L.oQO() + idx] = a.scale * S.Q()[idx] * expf(g);
         }
         for (int i = tid; i < DK; i += kBwdThreads) cb[L.oEg() + i] = expf(S.gam[i]);
         __syncthreads();
-        gemm<false, true, C, DK>(st, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);
-        gemm<false, true, C, DK>(st, a.scale, S.Qe, DK, S.N, DK, 0.f, cb + L.oAqk(), C);
+        gemm<false, true, C, DK>(st, 1.f, S.P(), DK, S.N(), DK, 0.f, S.PN(), C);
+        gemm<false, true, C, DK>(st, a.scale, S.Qe(), DK, S.N(), DK, 0.f, cb + L.oAqk(), C);
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads) {
             const int r = idx / C, i = idx % C;
-            sA[r][i] = i < r ? S.bet[r] * S.PN[idx] : 0.f;
+            sA[r][i] = i < r ? S.bet[r] * S.PN()[idx] : 0.f;
             if (i > r) cb[L.oAqk() + idx] = 0.f;
         }
         __syncthreads();
@@ -249,8 +268,8 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
             for (int r = 0; r < C; ++r) cb[L.oT() + r * C + tid] = x[r];
         }
         __syncthreads();
-        gemm<false, false, DK, C>(st, 1.f, cb + L.oT(), C, S.Bk, DK, 0.f, cb + L.oW(), DK);
-        gemm<false, false, DV, C>(st, 1.f, cb + L.oT(), C, S.Bv, DV, 0.f, cb + L.oUt(), DV);
+        gemm<false, false, DK, C>(st, 1.f, cb + L.oT(), C, S.Bk(), DK, 0.f, cb + L.oW(), DK);
+        gemm<false, false, DV, C>(st, 1.f, cb + L.oT(), C, S.Bv(), DV, 0.f, cb + L.oUt(), DV);
         __syncthreads();
     }
 }
@@ -351,7 +370,14 @@ template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     __shared__ Stage st;
-    const Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
+    __shared__ float lg[C * DK], lm[DK], lgam[DK], lbet[C];
+    // row sums for dbeta, column sums for dgamma (dR R and dS' S), by LDS atomics
+    __shared__ float lbacc[C], lgacc[DK], lsacc[DK];
+    Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
+    S.G = lg;  // the prefix (later its gradient), gamma, m and beta live in LDS
+    S.m = lm;
+    S.gam = lgam;
+    S.bet = lbet;
     const int tid = threadIdx.x, total = a.B * a.n_chunks * a.H;
     const float s = a.scale;
     for (int ch = blockIdx.x; ch < total; ch += gridDim.x) {
@@ -360,79 +386,100 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         const float *cb = a.ws + (size_t)ch * L.per_chunk();
         const float *Tm = cb + L.oT(), *Aqk = cb + L.oAqk(), *W = cb + L.oW(), *Ut = cb + L.oUt();
         const float *Rm = cb + L.oR(), *S0 = cb + L.oS(), *dS1 = cb + L.oDS();
+        for (int i = tid; i < C; i += kBwdThreads) lbacc[i] = 0.f;
+        for (int i = tid; i < DK; i += kBwdThreads) {
+            lgacc[i] = 0.f;
+            lsacc[i] = 0.f;
+        }
         load_chunk<DK, DV>(a, b, h, t0, n, S, true);
         __syncthreads();
         chunk_factors<DK, DV>(S);
-        for (int idx = tid; idx < C * DV; idx += kBwdThreads) S.U[idx] = Ut[idx];
+        for (int idx = tid; idx < C * DV; idx += kBwdThreads) S.U()[idx] = Ut[idx];
         __syncthreads();
-        gemm<false, true, C, DK>(st, 1.f, S.P, DK, S.N, DK, 0.f, S.PN, C);           // P N^T
-        gemm<false, false, DV, DK>(st, -1.f, W, DK, S0, DV, 1.f, S.U, DV);          // U = U~ - W S
-        gemm<true, false, DV, C>(st, 1.f, Aqk, C, S.dO, DV, 0.f, S.dU, DV);         // dU = Aqk^T dO
-        gemm<false, false, DV, DK>(st, 1.f, Rm, DK, dS1, DV, 1.f, S.dU, DV);        //    + R dS'
-        gemm<false, true, DK, DV>(st, 1.f, S.dO, DV, S0, DV, 0.f, S.dQO, DK);       // dQO = dO S^T
+        gemm<false, true, C, DK>(st, 1.f, S.P(), DK, S.N(), DK, 0.f, S.PN(), C);           // P N^T
+        gemm<false, false, DV, DK>(st, -1.f, W, DK, S0, DV, 1.f, S.U(), DV);          // U = U~ - W S
+        gemm<true, false, DV, C>(st, 1.f, Aqk, C, S.dO(), DV, 0.f, S.dU(), DV);         // dU = Aqk^T dO
+        gemm<false, false, DV, DK>(st, 1.f, Rm, DK, dS1, DV, 1.f, S.dU(), DV);        //    + R dS'
+        gemm<false, true, DK, DV>(st, 1.f, S.dO(), DV, S0, DV, 0.f, S.dQO(), DK);       // dQO = dO S^T
         __syncthreads();
-        gemm<false, true, C, DV>(st, 1.f, S.dO, DV, S.U, DV, 0.f, S.dAqk, C);       // dO U^T
-        gemm<false, true, DK, DV>(st, 1.f, S.U, DV, dS1, DV, 0.f, S.dR, DK);        // dR = U dS'^T
-        gemm<false, true, DK, DV>(st, -1.f, S.dU, DV, S0, DV, 0.f, S.dW, DK);       // dW = -dU S^T
-        gemm<true, false, DV, C>(st, 1.f, Tm, C, S.dU, DV, 0.f, S.dBv, DV);         // dBv = T^T dU
-        gemm<false, true, C, DV>(st, 1.f, S.dU, DV, S.Bv, DV, 0.f, S.dT, C);        // dT = dU Bv^T
-        __syncthreads();
-        for (int idx = tid; idx < C * C; idx += kBwdThreads)
-            if (idx % C > idx / C) S.dAqk[idx] = 0.f;                               // lower, diagonal included
-        gemm<false, true, C, DK>(st, 1.f, S.dW, DK, S.Bk, DK, 1.f, S.dT, C);        //    + dW Bk^T
-        gemm<true, false, DK, C>(st, 1.f, Tm, C, S.dW, DK, 0.f, S.dBk, DK);         // dBk = T^T dW
-        __syncthreads();
-        gemm<true, false, C, C>(st, 1.f, Tm, C, S.dT, C, 0.f, S.Tmp, C);            // T^T dT
-        __syncthreads();
-        gemm<false, true, C, C>(st, -1.f, S.Tmp, C, Tm, C, 0.f, S.dA, C);           // dA = -T^T dT T^T
+        gemm<false, true, C, DV>(st, 1.f, S.dO(), DV, S.U(), DV, 0.f, S.dAqk(), C);       // dO U^T
+        gemm<false, true, DK, DV>(st, 1.f, S.U(), DV, dS1, DV, 0.f, S.dR(), DK);        // dR = U dS'^T
+        gemm<false, true, DK, DV>(st, -1.f, S.dU(), DV, S0, DV, 0.f, S.dW(), DK);       // dW = -dU S^T
+        gemm<true, false, DV, C>(st, 1.f, Tm, C, S.dU(), DV, 0.f, S.dBv(), DV);         // dBv = T^T dU
+        gemm<false, true, C, DV>(st, 1.f, S.dU(), DV, S.Bv(), DV, 0.f, S.dT(), C);        // dT = dU Bv^T
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads)
-            if (idx % C >= idx / C) S.dA[idx] = 0.f;                                // strictly lower
+            if (idx % C > idx / C) S.dAqk()[idx] = 0.f;                               // lower, diagonal included
+        gemm<false, true, C, DK>(st, 1.f, S.dW(), DK, S.Bk(), DK, 1.f, S.dT(), C);        //    + dW Bk^T
+        gemm<true, false, DK, C>(st, 1.f, Tm, C, S.dW(), DK, 0.f, S.dBk(), DK);         // dBk = T^T dW
         __syncthreads();
-        if (tid < C) {
-            const int r = tid;
-            float d = 0.f;
-            for (int j = 0; j < DV; ++j) d = fmaf(S.dBv[r * DV + j], S.V[r * DV + j], d);
-            for (int i = 0; i < DK; ++i) d = fmaf(S.dBk[r * DK + i], S.K[r * DK + i] * expf(S.G[r * DK + i]), d);
-            // strictly lower part only: above the diagonal P N^T can overflow (e^(g_r - g_i) with
-            // i after r), and dA is zero there
-            for (int i = 0; i < r; ++i) d = fmaf(S.dA[r * C + i], S.PN[r * C + i], d);
-            if (r < n) a.dbeta[row_of(a, b, t0 + r, h)] = d;
+        gemm<true, false, C, C>(st, 1.f, Tm, C, S.dT(), C, 0.f, S.Tmp(), C);            // T^T dT
+        __syncthreads();
+        gemm<false, true, C, C>(st, -1.f, S.Tmp(), C, Tm, C, 0.f, S.dA(), C);           // dA = -T^T dT T^T
+        __syncthreads();
+        // dA strictly lower; dbeta's third term, rowsum(dA * P N^T), over the strictly lower
+        // part only (above the diagonal P N^T can overflow, e^(g_r - g_i) with i after r).
+        // A wave covers one row per step here and in the two loops below.
+        #pragma unroll 2
+        for (int idx = tid; idx < C * C; idx += kBwdThreads) {
+            const int r = idx / C, i = idx % C;
+            float d = S.dA()[idx], t = 0.f;
+            if (i >= r)
+                S.dA()[idx] = 0.f;
+            else
+                t = d * S.PN()[idx];
+            t = wave_sum(t);
+            if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
         }
-        for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
+        __syncthreads();
+        #pragma unroll 2
+        for (int idx = tid; idx < C * DV; idx += kBwdThreads) {  // dv, and dbeta's rowsum(dBv * v)
             const int r = idx / DV;
-            if (r < n) a.dv[row_of(a, b, t0 + r, h) * DV + idx % DV] = S.bet[r] * S.dBv[idx];
+            const float dbv = S.dBv()[idx];
+            if (r < n) a.dv[row_of(a, b, t0 + r, h) * DV + idx % DV] = S.bet[r] * dbv;
+            const float t = wave_sum(dbv * S.V()[idx]);
+            if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
         }
+        for (int idx = tid; idx < C * C; idx += kBwdThreads) S.dA()[idx] *= S.bet[idx / C];  // diag(beta) dA
         __syncthreads();
-        for (int idx = tid; idx < C * C; idx += kBwdThreads) S.dA[idx] *= S.bet[idx / C];  // diag(beta) dA
+        gemm<false, false, DK, C>(st, 1.f, S.dA(), C, S.N(), DK, 0.f, S.dP(), DK);        // dP = diag(beta) dA N
+        gemm<true, false, DK, C>(st, 1.f, S.dA(), C, S.P(), DK, 0.f, S.dN(), DK);         // dN = (diag(beta) dA)^T P
+        gemm<true, false, DK, C>(st, s, S.dAqk(), C, S.Qe(), DK, 1.f, S.dN(), DK);        //    + s dAqk^T Qe
+        gemm<false, false, DK, C>(st, s, S.dAqk(), C, S.N(), DK, 0.f, S.dQe(), DK);       // dQe = s dAqk N
         __syncthreads();
-        gemm<false, false, DK, C>(st, 1.f, S.dA, C, S.N, DK, 0.f, S.dP, DK);        // dP = diag(beta) dA N
-        gemm<true, false, DK, C>(st, 1.f, S.dA, C, S.P, DK, 0.f, S.dN, DK);         // dN = (diag(beta) dA)^T P
-        gemm<true, false, DK, C>(st, s, S.dAqk, C, S.Qe, DK, 1.f, S.dN, DK);        //    + s dAqk^T Qe
-        gemm<false, false, DK, C>(st, s, S.dAqk, C, S.N, DK, 0.f, S.dQe, DK);       // dQe = s dAqk N
-        __syncthreads();
+        // dq, dk; dg into LDS in place of g; dbeta's rowsum(dBk * k e^g); this thread's
+        // share of colsum(dR * R) (its channel is fixed: 256 is a multiple of dk)
+        float dgr = 0.f;
+        #pragma unroll 2
         for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
             const int r = idx / DK, i = idx % DK;
-            const float g = S.G[idx], m = S.m[i], kv = S.K[idx], qv = S.Q[idx], bb = S.bet[r];
+            const float g = S.G[idx], m = S.m[i], kv = S.K()[idx], qv = S.Q()[idx], bb = S.bet[r];
             const float eG = expf(g), eGm = expf(g - m), emG = expf(m - g), eR = expf(S.gam[i] - g);
-            const float dQO = S.dQO[idx], dQe = S.dQe[idx], dBk = S.dBk[idx], dP = S.dP[idx], dN = S.dN[idx],
-                        dR = S.dR[idx];
-            S.dG[idx] = s * dQO * qv * eG + dQe * qv * eGm + bb * dBk * kv * eG + dP * kv * eGm - dN * kv * emG -
-                        dR * kv * eR;
+            const float dQO = S.dQO()[idx], dQe = S.dQe()[idx], dBk = S.dBk()[idx], dP = S.dP()[idx], dN = S.dN()[idx],
+                        dR = S.dR()[idx];
+            S.G[idx] = s * dQO * qv * eG + dQe * qv * eGm + bb * dBk * kv * eG + dP * kv * eGm - dN * kv * emG -
+                       dR * kv * eR;
+            dgr = fmaf(dR, kv * eR, dgr);
             if (r < n) {
                 const size_t off = row_of(a, b, t0 + r, h) * DK + i;
                 a.dq[off] = s * dQO * eG + dQe * eGm;
                 a.dk[off] = bb * dBk * eG + dP * eGm + dN * emG + dR * eR;
             }
+            const float t = wave_sum(dBk * kv * eG);
+            if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
+        }
+        atomicAdd(&lgacc[tid % DK], dgr);
+        #pragma unroll 2
+        for (int idx = tid; idx < DK * DV; idx += kBwdThreads) {  // rowsum(dS' * S), a wave per row
+            const float t = wave_sum(dS1[idx] * S0[idx]);
+            if ((tid & 63) == 0) atomicAdd(&lsacc[idx / DV], t);
         }
         __syncthreads();
-        for (int i = tid; i < DK; i += kBwdThreads) {
-            float dgam = 0.f, ss = 0.f;
-            for (int r = 0; r < C; ++r) dgam = fmaf(S.dR[r * DK + i], S.K[r * DK + i] * expf(S.gam[i] - S.G[r * DK + i]), dgam);
-            for (int j = 0; j < DV; ++j) ss = fmaf(dS1[i * DV + j], S0[i * DV + j], ss);
-            float acc = fmaf(expf(S.gam[i]), ss, dgam);
+        for (int r = tid; r < n; r += kBwdThreads) a.dbeta[row_of(a, b, t0 + r, h)] = lbacc[r];
+        for (int i = tid; i < DK; i += kBwdThreads) {  // dgamma, then the reverse prefix of dg
+            float acc = fmaf(expf(S.gam[i]), lsacc[i], lgacc[i]);
             for (int r = C - 1; r >= 0; --r) {
-                acc += S.dG[r * DK + i];
+                acc += S.G[r * DK + i];
                 if (r < n) a.dlog_alpha[row_of(a, b, t0 + r, h) * DK + i] = acc;
             }
         }

@@ -1,0 +1,66 @@
+"""GPU parity at full size for the further prefill workloads that `bench.py --workloads`
+times (Gated DeltaNet, DeltaNet, gates from pre-activations, and q/k from
+pre-activations): the whole batch (B=8, T=8192, H=32, d=128, bf16, chunk 64: the fused
+pass) through the C ABI, the fp64 oracle on sampled (sequence, head) pairs over their
+full length. The inputs come from the same kda_synth generators as the bench's; the
+oracle forms the gates and q, k with oracle.gate_prologue and oracle.qk_prologue.
+
+Bar: relative L2 error of o and of hT for each sampled pair <= 2e-2 (bf16 I/O).
+"""
+import numpy as np
+import pytest
+
+import kda_synth
+import oracle
+from kda_testlib import TOL, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["batched_gdn", "batched_deltanet", "batched_preact", "batched_preact_qk"])
+def test_further_workload_sampled(name):
+    import torch
+    import gated_delta_rule_48_amd as kda
+    w = kda_synth.WORKLOADS[name]
+    B, T, H, d = len(w.seqlens), w.seqlens[0], w.H, w.dk
+    say(f"[{name}] B={B} T={T} H={H} d={d} {w.io} chunk {w.chunk} gate={w.gate}")
+    x = kda_synth.gen_workload(w)
+    if w.gate == "preact_qk":
+        r = kda_synth.gen_qk_preact(B * T, H, d, w.io, w.seed)
+        x["q"], x["k"] = r["q"], r["k"]
+    p = kda_synth.gen_preact(B * T, H, d, w.io, w.seed) if w.gate.startswith("preact") else None
+    dev = torch.device("cuda:0")
+    bf = lambda a, *s: torch.from_numpy(a).to(dev).to(torch.bfloat16).reshape((B, T) + s)  # noqa: E731
+    q, k, v = bf(x["q"], H, d), bf(x["k"], H, d), bf(x["v"], H, d)
+    if p is not None:
+        o, hT = kda.chunk_fwd_preact(q, k, v, bf(p["a"], H, d), torch.from_numpy(p["A_log"]).to(dev),
+                                     torch.from_numpy(p["dt_bias"]).to(dev),
+                                     torch.from_numpy(p["b"]).to(dev).reshape(B, T, H), scale=w.scale,
+                                     chunk=w.chunk, qk_norm=w.gate == "preact_qk")
+    else:
+        la = torch.from_numpy(x["log_alpha"]).to(dev).reshape(B, T, H, d)
+        la = la[..., 0].contiguous() if w.gate == "head" else None
+        o, hT = kda.chunk_fwd(q, k, v, la, torch.from_numpy(x["beta"]).to(dev).reshape(B, T, H), scale=w.scale,
+                              chunk=w.chunk)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().reshape(B * T, H, d)
+    hT = hT.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    for s, h in [(0, 0), (5, 23)]:
+        rows = slice(s * T, (s + 1) * T)
+        one = lambda a: a[rows, h:h + 1]  # noqa: E731
+        qs, ks = one(x["q"]), one(x["k"])
+        if p is not None:
+            la_s, beta_s = oracle.gate_prologue(one(p["a"]), p["A_log"][h:h + 1], p["dt_bias"][h:h + 1], one(p["b"]))
+            if w.gate == "preact_qk":
+                qs, ks = oracle.qk_prologue(qs), oracle.qk_prologue(ks)
+        else:
+            beta_s = one(x["beta"])
+            if w.gate == "head":
+                la_s = np.repeat(one(x["log_alpha"])[..., :1], d, axis=-1)
+            else:
+                la_s = np.zeros((T, 1, d))
+        o_ref, h_ref = oracle.kda_reference(qs, ks, one(x["v"]), la_s, beta_s, w.scale)
+        eo, eh = rel_l2(o[rows, h:h + 1], o_ref), rel_l2(hT[s:s + 1, h:h + 1], h_ref)
+        say(f"[{name}] seq {s} head {h}: rel_l2 o={eo:.2e} hT={eh:.2e}")
+        assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)

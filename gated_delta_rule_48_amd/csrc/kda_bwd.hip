@@ -36,7 +36,7 @@
 // sequence's end are zero in q, k, v, dO, beta and log alpha, which leaves every
 // quantity of the valid rows unchanged.
 //
-// Four kernels: (1) the chunk-local forward quantities T, Aqk, W, U~, R, QO and
+// Four kernels: (1) the chunk-local forward quantities T, Aqk^T, W, U~, R, QO and
 // e^gamma, in parallel over (chunk, head); (2) the chunk-start states, in order
 // over the chunks of each (sequence, head, 16 state columns); (3) the state
 // gradients dS', in reverse order likewise, and dh0; (4) the chunk-local
@@ -217,7 +217,7 @@ __device__ void chunk_factors(const Scr<DK, DV> &S) {
     for (int idx = threadIdx.x; idx < C * DV; idx += kBwdThreads) S.Bv()[idx] = S.bet[idx / DV] * S.V()[idx];
 }
 
-// (1) T, Aqk, W, U~, R, QO and e^gamma of every (chunk, head).
+// (1) T, Aqk^T, W, U~, R, QO and e^gamma of every (chunk, head).
 template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
@@ -246,12 +246,12 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
         for (int i = tid; i < DK; i += kBwdThreads) cb[L.oEg() + i] = expf(S.gam[i]);
         __syncthreads();
         gemm<false, true, C, DK>(st, 1.f, S.P(), DK, S.N(), DK, 0.f, S.PN(), C);
-        gemm<false, true, C, DK>(st, a.scale, S.Qe(), DK, S.N(), DK, 0.f, cb + L.oAqk(), C);
+        gemm<false, true, C, DK>(st, a.scale, S.N(), DK, S.Qe(), DK, 0.f, cb + L.oAqk(), C);  // Aqk^T
         __syncthreads();
         for (int idx = tid; idx < C * C; idx += kBwdThreads) {
             const int r = idx / C, i = idx % C;
             sA[r][i] = i < r ? S.bet[r] * S.PN()[idx] : 0.f;
-            if (i > r) cb[L.oAqk() + idx] = 0.f;
+            if (r > i) cb[L.oAqk() + idx] = 0.f;  // Aqk^T: zero below the diagonal
         }
         __syncthreads();
         // T = (I + A)^-1 by forward substitution, one column per thread of the first wave
@@ -275,12 +275,14 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
 }
 
 // (2) The state at every chunk's start, for 16 columns of one (sequence, head).
+// Each thread computes four adjacent outputs, the chunk matrices read as float4
+// rows of the workspace, the state and U from LDS.
 template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_states_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     constexpr int NB = kBwdCols;
-    __shared__ float sS[DK][NB];
-    __shared__ float sU[C][NB];
+    __shared__ __align__(16) float sS[DK][NB];
+    __shared__ __align__(16) float sU[C][NB];
     const int j0 = blockIdx.x * NB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
         const int i = idx / NB, j = idx % NB;
@@ -293,32 +295,39 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_states_kernel(BwdArgs a) 
             const int i = idx / NB, j = idx % NB;
             cb[L.oS() + i * DV + j0 + j] = sS[i][j];
         }
-        for (int idx = tid; idx < C * NB; idx += kBwdThreads) {  // U = U~ - W S
-            const int r = idx / NB, j = idx % NB;
-            const float *w = cb + L.oW() + r * DK;
-            float u = cb[L.oUt() + r * DV + j0 + j];
-            for (int i = 0; i < DK; ++i) u = fmaf(-w[i], sS[i][j], u);
-            sU[r][j] = u;
+        for (int it = tid; it < C * NB / 4; it += kBwdThreads) {  // U[r][4 jg ..] = U~ - W S
+            const int r = it / (NB / 4), jc = 4 * (it % (NB / 4));
+            f32x4 u = *reinterpret_cast<const f32x4 *>(cb + L.oUt() + r * DV + j0 + jc);
+            const f32x4 *w4 = reinterpret_cast<const f32x4 *>(cb + L.oW() + r * DK);
+            for (int i4 = 0; i4 < DK / 4; ++i4) {
+                const f32x4 w = w4[i4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u -= w[e] * *reinterpret_cast<const f32x4 *>(&sS[4 * i4 + e][jc]);
+            }
+            *reinterpret_cast<f32x4 *>(&sU[r][jc]) = u;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {  // S' = e^gamma S + R^T U
-            const int i = idx / NB, j = idx % NB;
-            float s = cb[L.oEg() + i] * sS[i][j];
-            for (int r = 0; r < C; ++r) s = fmaf(cb[L.oR() + r * DK + i], sU[r][j], s);
-            sS[i][j] = s;
+        for (int it = tid; it < DK / 4 * NB; it += kBwdThreads) {  // S'[4 ig ..][j] = e^gamma S + R^T U
+            const int i0 = 4 * (it / NB), j = it % NB;
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(cb + L.oEg() + i0);
+            f32x4 sv = {eg[0] * sS[i0][j], eg[1] * sS[i0 + 1][j], eg[2] * sS[i0 + 2][j], eg[3] * sS[i0 + 3][j]};
+            for (int r = 0; r < C; ++r) sv += *reinterpret_cast<const f32x4 *>(cb + L.oR() + r * DK + i0) * sU[r][j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sS[i0 + e][j] = sv[e];
         }
         __syncthreads();
     }
 }
 
-// (3) dS' of every chunk (the gradient at its end), last chunk first, and dh0.
+// (3) dS' of every chunk (the gradient at its end), last chunk first, and dh0;
+// arranged as kernel (2), with Aqk stored transposed.
 template <int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     constexpr int NB = kBwdCols;
-    __shared__ float sD[DK][NB];
-    __shared__ float sdU[C][NB];
-    __shared__ float sdO[C][NB];
+    __shared__ __align__(16) float sD[DK][NB];
+    __shared__ __align__(16) float sdU[C][NB];
+    __shared__ __align__(16) float sdO[C][NB];
     const int j0 = blockIdx.x * NB, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
         const int i = idx / NB, j = idx % NB;
@@ -336,23 +345,34 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArg
             const int i = idx / NB, j = idx % NB;
             cb[L.oDS() + i * DV + j0 + j] = sD[i][j];
         }
-        for (int idx = tid; idx < C * NB; idx += kBwdThreads) {  // dU = Aqk^T dO + R dS'
-            const int r = idx / NB, j = idx % NB;
-            float u = 0.f;
-            for (int q = 0; q < C; ++q) u = fmaf(cb[L.oAqk() + q * C + r], sdO[q][j], u);
-            const float *rr = cb + L.oR() + r * DK;
-            for (int i = 0; i < DK; ++i) u = fmaf(rr[i], sD[i][j], u);
-            sdU[r][j] = u;
+        for (int it = tid; it < C * NB / 4; it += kBwdThreads) {  // dU[r][4 jg ..] = Aqk^T dO + R dS'
+            const int r = it / (NB / 4), jc = 4 * (it % (NB / 4));
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 *a4 = reinterpret_cast<const f32x4 *>(cb + L.oAqk() + r * C);
+            for (int q4 = 0; q4 < C / 4; ++q4) {
+                const f32x4 x = a4[q4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u += x[e] * *reinterpret_cast<const f32x4 *>(&sdO[4 * q4 + e][jc]);
+            }
+            const f32x4 *r4 = reinterpret_cast<const f32x4 *>(cb + L.oR() + r * DK);
+            for (int i4 = 0; i4 < DK / 4; ++i4) {
+                const f32x4 x = r4[i4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) u += x[e] * *reinterpret_cast<const f32x4 *>(&sD[4 * i4 + e][jc]);
+            }
+            *reinterpret_cast<f32x4 *>(&sdU[r][jc]) = u;
         }
         __syncthreads();
-        for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {  // dS = QO^T dO + e^gamma dS' - W^T dU
-            const int i = idx / NB, j = idx % NB;
-            float s = cb[L.oEg() + i] * sD[i][j];
+        for (int it = tid; it < DK / 4 * NB; it += kBwdThreads) {  // dS = QO^T dO + e^gamma dS' - W^T dU
+            const int i0 = 4 * (it / NB), j = it % NB;
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(cb + L.oEg() + i0);
+            f32x4 sv = {eg[0] * sD[i0][j], eg[1] * sD[i0 + 1][j], eg[2] * sD[i0 + 2][j], eg[3] * sD[i0 + 3][j]};
             for (int r = 0; r < C; ++r) {
-                s = fmaf(cb[L.oQO() + r * DK + i], sdO[r][j], s);
-                s = fmaf(-cb[L.oW() + r * DK + i], sdU[r][j], s);
+                sv += *reinterpret_cast<const f32x4 *>(cb + L.oQO() + r * DK + i0) * sdO[r][j];
+                sv -= *reinterpret_cast<const f32x4 *>(cb + L.oW() + r * DK + i0) * sdU[r][j];
             }
-            sD[i][j] = s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sD[i0 + e][j] = sv[e];
         }
         __syncthreads();
     }
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         const int h = ch % a.H, c = (ch / a.H) % a.n_chunks, b = ch / (a.H * a.n_chunks);
         const int t0 = c * C, n = min(C, a.T - t0);
         const float *cb = a.ws + (size_t)ch * L.per_chunk();
-        const float *Tm = cb + L.oT(), *Aqk = cb + L.oAqk(), *W = cb + L.oW(), *Ut = cb + L.oUt();
+        const float *Tm = cb + L.oT(), *AqkT = cb + L.oAqk(), *W = cb + L.oW(), *Ut = cb + L.oUt();
         const float *Rm = cb + L.oR(), *S0 = cb + L.oS(), *dS1 = cb + L.oDS();
         for (int i = tid; i < C; i += kBwdThreads) lbacc[i] = 0.f;
         for (int i = tid; i < DK; i += kBwdThreads) {
@@ -398,7 +418,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         __syncthreads();
         gemm<false, true, C, DK>(st, 1.f, S.P(), DK, S.N(), DK, 0.f, S.PN(), C);           // P N^T
         gemm<false, false, DV, DK>(st, -1.f, W, DK, S0, DV, 1.f, S.U(), DV);          // U = U~ - W S
-        gemm<true, false, DV, C>(st, 1.f, Aqk, C, S.dO(), DV, 0.f, S.dU(), DV);         // dU = Aqk^T dO
+        gemm<false, false, DV, C>(st, 1.f, AqkT, C, S.dO(), DV, 0.f, S.dU(), DV);       // dU = Aqk^T dO
         gemm<false, false, DV, DK>(st, 1.f, Rm, DK, dS1, DV, 1.f, S.dU(), DV);        //    + R dS'
         gemm<false, true, DK, DV>(st, 1.f, S.dO(), DV, S0, DV, 0.f, S.dQO(), DK);       // dQO = dO S^T
         __syncthreads();

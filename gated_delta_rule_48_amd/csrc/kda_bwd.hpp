@@ -11,7 +11,7 @@ constexpr int kBwdThreads = 256;  // four waves
 constexpr int kBwdCols = 16;      // state columns per workgroup of the sequential passes
 constexpr int kBwdMaxGroups = 1024;  // persistent workgroups of the chunk-local kernels, at most
 
-// Per (chunk, head) buffers in the workspace, fp32, in this order: T (C x C), Aqk
+// Per (chunk, head) buffers in the workspace, fp32, in this order: T (C x C), Aqk^T
 // (C x C), W (C x dk), U~ (C x dv), R (C x dk), QO (C x dk), exp(gamma) (dk), the
 // state at the chunk's start (dk x dv) and the loss gradient with respect to the
 // state at its end (dk x dv).

@@ -57,12 +57,12 @@ PATHS = {
 }
 
 
-def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16):
+def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16, n_seqs=0):
     """Which schedule kda_chunk_fwd runs for these sizes: the one-launch fused pass
-    (equal-length bf16 sequences, d_k = d_v = 128, chunk 64, at least 256
-    (sequence, head) pairs) or the split prep + state pass. Same rule as the
-    library's dispatch."""
-    fused = (not varlen and chunk == 64 and bf16 and dk == dv == 128 and T > 0 and B * H >= 256)
+    (bf16, d_k = d_v = 128, chunk 64, at least 256 (sequence, head) pairs, equal-length
+    or packed sequences) or the split prep + state pass. Same rule as the library's
+    dispatch."""
+    fused = (chunk == 64 and bf16 and dk == dv == 128 and T > 0 and (n_seqs if varlen else B) * H >= 256)
     return "fused" if fused else "split"
 
 
@@ -275,7 +275,7 @@ def bench_workload(args, kda, torch, name):
     alg = prefill_algorithmic_bytes(tokens * w.H, w.dk, w.dv, 2 if w.io == "bf16" else 4, n_seqs * w.H,
                                     0 if h0 is None else n_seqs * w.H, w.gate)
     achieved = alg / (ms * 1e-3) / 1e9
-    path = prefill_path(B, T, w.H, w.dk, w.dv, w.chunk, varlen, w.io == "bf16")
+    path = prefill_path(B, T, w.H, w.dk, w.dv, w.chunk, varlen, w.io == "bf16", len(w.seqlens))
     log(f"[bench] workload {name} ({path} pass): {ms:.3f} ms/call, {tokens / (ms * 1e-3):.3e} tokens/s, "
         f"{achieved:.0f} GB/s algorithmic")
     return {"value": tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 4), "pass": path,

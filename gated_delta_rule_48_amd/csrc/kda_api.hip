@@ -33,14 +33,15 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 // The fused pass (one workgroup per (sequence, head), nothing staged in
-// memory) is used for bf16 input with d_k = d_v = 128 when the sequences have
-// one length, the chunk is 64 and the (sequence, head) pairs alone fill the
-// chip; otherwise the split pass (parallel chunk preparation, then state
-// propagation over d_v slices).
+// memory) is used for bf16 input with d_k = d_v = 128 and chunk 64 when the
+// (sequence, head) pairs alone fill the chip, for equal-length and for packed
+// sequences; otherwise the split pass (parallel chunk preparation, then state
+// propagation over d_v slices). With packed sequences the longest one sets the
+// fused pass's time, as it does the split pass's state propagation.
 constexpr int kFusedMinPairs = 256;
-bool use_fused(int B, int T, int H, int dk, int dv, int C, bool varlen, int io) {
-    return !varlen && C == 64 && io == KDA_BF16 && dk == 128 && dv == 128 && T > 0 &&
-           (int64_t)B * H >= kFusedMinPairs;
+bool use_fused(int B, int T, int H, int dk, int dv, int C, bool varlen, int io, int n_seqs) {
+    return C == 64 && io == KDA_BF16 && dk == 128 && dv == 128 && T > 0 &&
+           (int64_t)(varlen ? n_seqs : B) * H >= kFusedMinPairs;
 }
 
 struct WsLayout {
@@ -56,7 +57,7 @@ bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varl
         *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         return true;
     }
-    if (use_fused(B, T, H, dk, dv, C, varlen, io)) {  // only the discard slot
+    if (use_fused(B, T, H, dk, dv, C, varlen, io, n_seqs)) {  // only the discard slot
         *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 256, 0};
         L->n_chunks = 0;
         return true;
@@ -169,9 +170,10 @@ int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, in
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
     const bool bf = io == KDA_BF16;
-    if (use_fused(B, T, H, d_k, d_v, chunk, varlen, io)) {
-        kda::FusedArgs fa{q, k, v, log_alpha, beta, scale, h0, hT, o, ws + L.discard, H, T, gate, pre};
-        return kda::launch_fused(fa, d_k, d_v, bf, B, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (use_fused(B, T, H, d_k, d_v, chunk, varlen, io, n_seqs)) {
+        kda::FusedArgs fa{q,  k,     v,  log_alpha, beta, scale, h0, hT,   o, ws + L.discard, H,
+                          T,  varlen ? cu_seqlens : nullptr, (int)tokens, gate, pre};
+        return kda::launch_fused(fa, d_k, d_v, bf, nseq, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     ChunkBuffers buf{};
     if (L.total > 0) {

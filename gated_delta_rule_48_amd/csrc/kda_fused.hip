@@ -228,9 +228,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rb = w & 3, hf = w >> 2;
     const float scale = a.scale;
-    const int T_len = a.seq_len;
+    // this sequence's tokens: seq_len each, or packed at the (clamped) offsets cu_seqlens
+    int T_len = a.seq_len;
+    size_t seq0 = (size_t)s * T_len;
+    if (a.cu_seqlens) {
+        const int b0 = min(max(a.cu_seqlens[s], 0), a.T_total);
+        const int b1 = min(max(a.cu_seqlens[s + 1], b0), a.T_total);
+        T_len = b1 - b0;
+        // an empty sequence runs no chunk; its first chunk's loads (issued before the
+        // loop) then read row 0 of the batch, which exists, and are never used
+        seq0 = T_len > 0 ? (size_t)b0 : 0;
+    }
     const int n_c = (T_len + kC - 1) / kC;
-    const size_t seq0 = (size_t)s * T_len;
 
     // ---- state columns (value positions) 16 w .. 16 w + 15: tile tm holds rows (key
     //      positions) 16 tm + 4 hi + i of column 16 w + lr
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     // Each request derives the lane's row and column group afresh (opaque_lane), so
     // the per-lane addresses are not kept as loop-carried pointers in registers.
     auto row_off = [&](int ci, int lane) {  // rows past the end read the last row; beta and decay are zeroed at use
-        return (unsigned)(min(16 * rb + (lane & 15), T_len - 1 - ci * kC) * H);
+        return (unsigned)(max(min(16 * rb + (lane & 15), T_len - 1 - ci * kC), 0) * H);
     };
     auto load_k = [&](int ci) {
         const int ln = opaque_lane();

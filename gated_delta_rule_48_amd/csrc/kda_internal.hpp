@@ -78,7 +78,9 @@ struct FusedArgs {
     void *o;
     void *discard;  // absorbs stores of rows past a sequence end (256 bytes)
     int H;
-    int seq_len;    // every sequence has seq_len tokens
+    int seq_len;    // every sequence has seq_len tokens (cu_seqlens null), or
+    const int32_t *cu_seqlens;  // [n_seqs + 1] offsets of packed sequences (clamped to [0, T_total], monotone)
+    int T_total;
     int gate;       // as in PrepArgs
     PreactArgs pre;
 };

@@ -16,6 +16,8 @@ Workloads (sizes from the five benchmark configurations of this library):
            h0 ~ N(0, 0.02)
   batched_gdn, batched_deltanet: the batched workload with the decay given per token
            and head (the first key channel's draw) or not at all (`gate`)
+  varlen_many: 16 packed sequences of mixed lengths (1 to 8192, 65,536 tokens), H=32, d=128,
+           bf16, chunk 64, per-sequence h0 ~ N(0, 0.02)
   batched_preact: the batched workload with gate pre-activations (gen_preact) instead
            of log alpha and beta; batched_preact_qk: also q and k before silu and
            normalisation (gen_qk_preact)
@@ -95,6 +97,9 @@ WORKLOADS = {
     # the batched workload with its gates formed in the kernels from pre-activations (gen_preact)
     "batched_preact": Workload("batched_preact", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero", 1002,
                                "preact"),
+    # 16 packed sequences of mixed lengths (65,536 tokens, 512 (sequence, head) pairs: the fused pass)
+    "varlen_many": Workload("varlen_many", (8192, 2048, 6144, 4096, 4096, 1000, 7192, 4096, 3000, 5192, 4096, 4096,
+                                            2048, 6144, 1, 4095), 32, 128, 128, 64, "bf16", "weak", "normal", 1008),
     # ... and q, k given before silu and per-row L2 normalisation too (gen_qk_preact)
     "batched_preact_qk": Workload("batched_preact_qk", (8192,) * 8, 32, 128, 128, 64, "bf16", "weak", "zero",
                                   1002, "preact_qk"),

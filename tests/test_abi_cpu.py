@@ -50,8 +50,8 @@ def test_version_and_status_strings(lib):
 
 
 def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
-    if n_seqs == 0 and C == 64 and esz == 2 and dk == dv == 128 and B * H >= 256:
-        # fused pass: only the 256-byte discard slot
+    if C == 64 and esz == 2 and dk == dv == 128 and T > 0 and (n_seqs if n_seqs else B) * H >= 256:
+        # fused pass (equal-length or packed sequences): only the 256-byte discard slot
         return 256
     per = (T + C - 1) // C
     nch = (per + n_seqs if n_seqs else B * per) * H
@@ -66,6 +66,7 @@ def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
 
 
 @pytest.mark.parametrize("args", [(8, 8192, 32, 128, 128, 64, 0, BF16), (1, 65536, 32, 128, 128, 128, 4, BF16),
+                                  (1, 65536, 32, 128, 128, 64, 16, BF16), (1, 65536, 32, 128, 128, 64, 4, BF16),
                                   (1, 256, 2, 64, 64, 64, 0, F32), (3, 77, 5, 64, 128, 128, 0, F32)])
 def test_workspace_size(lib, args):
     B, T, H, dk, dv, C, ns, io = args

@@ -48,6 +48,8 @@ def test_pass_rule_matches_the_library():
     assert bench.prefill_path(8, 8192, 32, 128, 128, 64, False, True) == "fused"
     assert bench.prefill_path(1, 4096, 16, 128, 128, 64, False, True) == "split"      # 16 pairs
     assert bench.prefill_path(1, 65536, 32, 128, 128, 128, True, True) == "split"     # varlen, chunk 128
+    assert bench.prefill_path(1, 65536, 32, 128, 128, 64, True, True, 4) == "split"   # varlen, 128 pairs
+    assert bench.prefill_path(1, 65536, 32, 128, 128, 64, True, True, 16) == "fused"  # varlen, 512 pairs
     assert bench.prefill_path(8, 8192, 32, 128, 128, 64, False, False) == "split"     # fp32
     assert bench.prefill_path(8, 8192, 32, 64, 64, 64, False, True) == "split"        # d = 64
 

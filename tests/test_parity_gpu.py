@@ -449,3 +449,19 @@ def test_decode_preact_gates(io, qk_norm):
     eh = rel_l2(state.cpu().numpy().reshape(N * H, dk, dv), h_ref[0])
     say(f"[decode preact {io}] rel_l2 o={eo:.2e} state={eh:.2e}")
     assert eo <= TOL[io] and eh <= TOL[io]
+
+
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+def test_fused_packed_sequences(gate):
+    """Packed sequences through the fused pass (bf16, d = 128, chunk 64, n_seqs x H >= 256):
+    empty, one-token, ragged and chunk-aligned sequences, with per-sequence h0."""
+    x = gen((0, 1, 63, 64, 65, 130, 0, 200), 32, 128, 128, "bf16", "main", "normal", seed=71)
+    _check(with_gate(x, gate), "bf16", 64, f"fused-packed-{gate}", varlen=True, gate=gate)
+
+
+def test_fused_packed_workload():
+    """varlen_many: 16 packed sequences of mixed lengths (1 to 8192, 65,536 tokens), H=32,
+    the whole batch against the oracle."""
+    w = kda_synth.WORKLOADS["varlen_many"]
+    x = kda_synth.gen_workload(w)
+    _check(x, "bf16", w.chunk, "varlen_many", varlen=True)

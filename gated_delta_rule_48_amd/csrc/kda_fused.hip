@@ -240,6 +240,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         seq0 = T_len > 0 ? (size_t)b0 : 0;
     }
     const int n_c = (T_len + kC - 1) / kC;
+    const int T_ld = max(T_len, 1);  // the rows the loads may touch (row 0 for an empty sequence)
 
     // ---- state columns (value positions) 16 w .. 16 w + 15: tile tm holds rows (key
     //      positions) 16 tm + 4 hi + i of column 16 w + lr
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     // Each request derives the lane's row and column group afresh (opaque_lane), so
     // the per-lane addresses are not kept as loop-carried pointers in registers.
     auto row_off = [&](int ci, int lane) {  // rows past the end read the last row; beta and decay are zeroed at use
-        return (unsigned)(max(min(16 * rb + (lane & 15), T_len - 1 - ci * kC), 0) * H);
+        return (unsigned)(min(16 * rb + (lane & 15), T_ld - 1 - ci * kC) * H);
     };
     auto load_k = [&](int ci) {
         const int ln = opaque_lane();

@@ -391,18 +391,21 @@ def bwd_algorithmic_flops(B, T, H, dk, dv, C=64):
     return 2 * macs * B * ((T + C - 1) // C) * H
 
 
-def bench_bwd(args, kda, torch):
-    """The backward pass (kda_chunk_bwd, fp32) on the batched workload's shape: B=8, T=8192,
-    H=32, d=128, chunk 64, inputs and loss gradients drawn on the GPU (torch's seeded generator)."""
+def bench_bwd(args, kda, torch, io="f32"):
+    """The backward pass (kda_chunk_bwd) on the batched workload's shape: B=8, T=8192, H=32,
+    d=128, chunk 64, q, k, v and the output gradient in `io` (fp32 arithmetic either way),
+    inputs and loss gradients drawn on the GPU (torch's seeded generator)."""
     B, T, H, d = 8, 8192, 32, 128
     dev = torch.device("cuda:0")
-    log(f"[bench] generating backward inputs: B={B} T={T} H={H} d={d} fp32")
+    log(f"[bench] generating backward inputs: B={B} T={T} H={H} d={d} {io}")
     g = torch.Generator(device=dev)
     g.manual_seed(1007)
     rn = lambda *s: torch.randn(s, generator=g, device=dev)  # noqa: E731
     q = torch.nn.functional.normalize(rn(B, T, H, d), dim=-1)
     k = torch.nn.functional.normalize(rn(B, T, H, d), dim=-1)
     v, dout = rn(B, T, H, d), rn(B, T, H, d)
+    if io == "bf16":
+        q, k, v, dout = (x.to(torch.bfloat16) for x in (q, k, v, dout))
     la = -0.1 * torch.nn.functional.softplus(rn(B, T, H, d))
     beta = torch.sigmoid(rn(B, T, H))
     dhT = rn(B, H, d, d)
@@ -426,12 +429,12 @@ def bench_bwd(args, kda, torch):
     # 9.7 GB, 1.2 ms of HBM time at 8 TB/s)
     flops = bwd_algorithmic_flops(B, T, H, d, d)
     achieved = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] backward: {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, {achieved:.1f} TFLOP/s "
-        "algorithmic (fp32)")
+    log(f"[bench] backward ({io} I/O): {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, {achieved:.1f} "
+        "TFLOP/s algorithmic (fp32 products)")
     del q, k, v, dout, la, beta, dhT, ws
     torch.cuda.empty_cache()
     return {"value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 3), "steps": n,
-            "workload": f"backward of the batched prefill: B={B} x T={T}, H={H}, d_k=d_v={d}, chunk 64, fp32",
+            "workload": f"backward of the batched prefill: B={B} x T={T}, H={H}, d_k=d_v={d}, chunk 64, {io} I/O",
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MATRIX_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / FP32_MATRIX_PEAK_TFLOPS, 4),
                          "alg_flops_per_call": flops}}
@@ -481,7 +484,8 @@ def main():
                     help="attention-decode comparator workloads to time (" + ", ".join(kda_synth.ATTN_WORKLOADS) +
                          "; empty for none)")
     ap.add_argument("--attn-steps", type=int, default=50)
-    ap.add_argument("--bwd", action="store_true", help="also time the backward pass (fp32) on the batched shape")
+    ap.add_argument("--bwd", action="store_true",
+                    help="also time the backward pass on the batched shape (fp32 and bf16 I/O)")
     ap.add_argument("--bwd-steps", type=int, default=3)
     ap.add_argument("--workloads", default="", metavar="NAMES",
                     help="comma-separated further prefill workloads to time and report (" +
@@ -505,7 +509,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, kda, torch)
     others = {n: bench_workload(args, kda, torch, n) for n in args.workloads.split(",") if n}
     attn = {n: bench_attn(args, kda, torch, n, dec) for n in args.attn.split(",") if n}
-    bwd = bench_bwd(args, kda, torch) if args.bwd else None
+    bwd = {io: bench_bwd(args, kda, torch, io) for io in ("f32", "bf16")} if args.bwd else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
 
     w = pre["workload"]
@@ -543,7 +547,8 @@ def main():
     if attn:
         line["attn_decode"] = attn
     if bwd is not None:
-        line["backward"] = bwd
+        line["backward"] = bwd["f32"]
+        line["backward_bf16_io"] = bwd["bf16"]
     if others:
         line["workloads"] = others
     print(json.dumps(line), flush=True)

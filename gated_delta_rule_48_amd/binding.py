@@ -350,10 +350,10 @@ def chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk=64, io=KDA_F32) -> int:
 
 def chunk_bwd(q, k, v, log_alpha, beta, dout, scale: Optional[float] = None, h0=None, dhT=None,
               chunk: int = 64, workspace=None, stream=None):
-    """Backward pass of chunk_fwd (kda_chunk_bwd) for equal-length fp32 sequences: q, k
-    [B, T, H, dk]; v, dout [B, T, H, dv]; log_alpha [B, T, H, dk]; beta [B, T, H]; h0, dhT
-    [B, H, dk, dv] or None. Returns (dq, dk, dv, dlog_alpha, dbeta, dh0), dh0 None when h0
-    is None."""
+    """Backward pass of chunk_fwd (kda_chunk_bwd) for equal-length sequences: q, k
+    [B, T, H, dk]; v, dout [B, T, H, dv] (fp32 or bf16); log_alpha [B, T, H, dk]; beta
+    [B, T, H]; h0, dhT [B, H, dk, dv] or None (fp32). Returns (dq, dk, dv in q's dtype,
+    dlog_alpha, dbeta, dh0 in fp32), dh0 None when h0 is None."""
     import torch
     lib = load()
     dev = q.device
@@ -369,7 +369,8 @@ def chunk_bwd(q, k, v, log_alpha, beta, dout, scale: Optional[float] = None, h0=
     for t, n in ((h0, "h0"), (dhT, "dhT")):
         if t is not None:
             _check(t, n, f32, (B, H, dk, dv), dev)
-    dq, dk_, dlog_alpha = (torch.empty((B, T, H, dk), dtype=q.dtype, device=dev) for _ in range(3))
+    dq, dk_ = (torch.empty((B, T, H, dk), dtype=q.dtype, device=dev) for _ in range(2))
+    dlog_alpha = torch.empty((B, T, H, dk), dtype=f32, device=dev)
     dv_ = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
     dbeta = torch.empty((B, T, H), dtype=f32, device=dev)
     dh0 = torch.empty((B, H, dk, dv), dtype=f32, device=dev) if h0 is not None else None

@@ -405,8 +405,7 @@ struct BwdPlan {
 int check_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io, BwdPlan *p) {
     if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 1) return KDA_ERR_INVALID_ARG;
-    if (io != KDA_F32 || chunk != kda::kBwdChunk || !supported_dim(d_k) || !supported_dim(d_v))
-        return KDA_ERR_UNSUPPORTED;
+    if (chunk != kda::kBwdChunk || !supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
     if (B > 65535 || H > 65535 || (int64_t)B * T * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     const kda::BwdLayout L{d_k, d_v};
     p->n_chunks = (T + chunk - 1) / chunk;
@@ -435,8 +434,9 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     const int st = check_bwd(B, T, H, d_k, d_v, chunk, io, &p);
     if (st != KDA_OK) return st;
     if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
-    const size_t ntok = (size_t)B * T * H;
-    const size_t nk = ntok * d_k * 4, nv = ntok * d_v * 4, nb = ntok * 4, ns = (size_t)B * H * d_k * d_v * 4;
+    const size_t ntok = (size_t)B * T * H, esz = io == KDA_BF16 ? 2 : 4;
+    const size_t nk = ntok * d_k * esz, nv = ntok * d_v * esz, nb = ntok * 4, ns = (size_t)B * H * d_k * d_v * 4;
+    const size_t nla = ntok * d_k * 4;  // log_alpha and dlog_alpha are fp32
     if (ntok > 0 && (!q || !k || !v || !log_alpha || !beta || !dout || !dq || !dk || !dv || !dlog_alpha || !dbeta))
         return KDA_ERR_INVALID_ARG;
     const void *in16[] = {q, k, v, log_alpha, dout, h0, dhT, dq, dk, dv, dlog_alpha, dh0};
@@ -445,9 +445,9 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     if (!aligned(beta, 4) || !aligned(dbeta, 4)) return KDA_ERR_INVALID_ARG;
     // no output may overlap any argument or another output
     const void *ins[] = {q, k, v, log_alpha, beta, h0, dout, dhT};
-    const size_t in_n[] = {nk, nk, nv, nk, nb, ns, nv, ns};
+    const size_t in_n[] = {nk, nk, nv, nla, nb, ns, nv, ns};
     const void *outs[] = {dq, dk, dv, dlog_alpha, dbeta, dh0};
-    const size_t out_n[] = {nk, nk, nv, nk, nb, ns};
+    const size_t out_n[] = {nk, nk, nv, nla, nb, ns};
     for (int i = 0; i < 6; ++i) {
         for (int j = 0; j < 8; ++j)
             if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return KDA_ERR_INVALID_ARG;
@@ -463,14 +463,12 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     }
     if (ntok == 0 && !(dh0 && B > 0)) return KDA_OK;
     float *ws = static_cast<float *>(workspace);
-    const kda::BwdArgs a{static_cast<const float *>(q), static_cast<const float *>(k),
-                         static_cast<const float *>(v), log_alpha, beta, h0,
-                         static_cast<const float *>(dout), dhT, scale,
-                         static_cast<float *>(dq), static_cast<float *>(dk), static_cast<float *>(dv),
-                         dlog_alpha, dbeta, dh0, ws,
+    const kda::BwdArgs a{q,  k,  v,  log_alpha, beta,       h0,    dout, dhT, scale,
+                         dq, dk, dv, dlog_alpha, dbeta, dh0, ws,
                          p.total > 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + p.scratch_off)
                                      : nullptr,
                          B, T, H, p.n_chunks, p.n_groups};
-    if (kda::launch_chunk_bwd(a, d_k, d_v, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chunk_bwd(a, d_k, d_v, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERR_HIP;
     return KDA_OK;
 }

@@ -40,7 +40,8 @@
 // e^gamma, in parallel over (chunk, head); (2) the chunk-start states, in order
 // over the chunks of each (sequence, head, 16 state columns); (3) the state
 // gradients dS', in reverse order likewise, and dh0; (4) the chunk-local
-// gradients, in parallel over (chunk, head). Everything is fp32, the chunk
+// gradients, in parallel over (chunk, head). q, k, v, dout and dq, dk, dv are fp32
+// or bf16; everything else, and all arithmetic, is fp32, the chunk
 // matrices in a per-workgroup scratch in global memory, the products on the
 // matrix cores in fp32 with their operands read straight from that memory: the
 // direct form of this pass, not tuned further.
@@ -164,20 +165,20 @@ __device__ __forceinline__ size_t row_of(const BwdArgs &a, int b, int t, int h) 
 
 // One chunk's inputs into the scratch (rows past the end zero), beta, the prefix
 // g of log alpha, gamma and m (these four in LDS). Every thread calls it.
-template <int DK, int DV>
+template <typename T, int DK, int DV>
 __device__ void load_chunk(const BwdArgs &a, int b, int h, int t0, int n, const Scr<DK, DV> &S, bool with_dout) {
     const int tid = threadIdx.x;
     for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
         const int r = idx / DK, i = idx % DK;
         const size_t off = row_of(a, b, t0 + r, h) * DK + i;
-        S.Q()[idx] = r < n ? a.q[off] : 0.f;
-        S.K()[idx] = r < n ? a.k[off] : 0.f;
+        S.Q()[idx] = r < n ? to_f32(static_cast<const T *>(a.q)[off]) : 0.f;
+        S.K()[idx] = r < n ? to_f32(static_cast<const T *>(a.k)[off]) : 0.f;
     }
     for (int idx = tid; idx < C * DV; idx += kBwdThreads) {
         const int r = idx / DV, j = idx % DV;
         const size_t off = row_of(a, b, t0 + r, h) * DV + j;
-        S.V()[idx] = r < n ? a.v[off] : 0.f;
-        if (with_dout) S.dO()[idx] = r < n ? a.dout[off] : 0.f;
+        S.V()[idx] = r < n ? to_f32(static_cast<const T *>(a.v)[off]) : 0.f;
+        if (with_dout) S.dO()[idx] = r < n ? to_f32(static_cast<const T *>(a.dout)[off]) : 0.f;
     }
     for (int r = tid; r < C; r += kBwdThreads) S.bet[r] = r < n ? a.beta[row_of(a, b, t0 + r, h)] : 0.f;
     for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
@@ -218,7 +219,7 @@ __device__ void chunk_factors(const Scr<DK, DV> &S) {
 }
 
 // (1) T, Aqk^T, W, U~, R, QO and e^gamma of every (chunk, head).
-template <int DK, int DV>
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     __shared__ float sA[C][C + 1];
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
         const int h = ch % a.H, c = (ch / a.H) % a.n_chunks, b = ch / (a.H * a.n_chunks);
         const int t0 = c * C, n = min(C, a.T - t0);
         float *cb = a.ws + (size_t)ch * L.per_chunk();
-        load_chunk<DK, DV>(a, b, h, t0, n, S, false);
+        load_chunk<T, DK, DV>(a, b, h, t0, n, S, false);
         __syncthreads();
         chunk_factors<DK, DV>(S);
         for (int idx = tid; idx < C * DK; idx += kBwdThreads) {
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_states_kernel(BwdArgs a) 
 
 // (3) dS' of every chunk (the gradient at its end), last chunk first, and dh0;
 // arranged as kernel (2), with Aqk stored transposed.
-template <int DK, int DV>
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     constexpr int NB = kBwdCols;
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArg
         float *cb = a.ws + (((size_t)b * a.n_chunks + c) * a.H + h) * L.per_chunk();
         for (int idx = tid; idx < C * NB; idx += kBwdThreads) {
             const int r = idx / NB, j = idx % NB;
-            sdO[r][j] = r < n ? a.dout[row_of(a, b, t0 + r, h) * DV + j0 + j] : 0.f;
+            sdO[r][j] = r < n ? to_f32(static_cast<const T *>(a.dout)[row_of(a, b, t0 + r, h) * DV + j0 + j]) : 0.f;
         }
         __syncthreads();
         for (int idx = tid; idx < DK * NB; idx += kBwdThreads) {
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_state_grads_kernel(BwdArg
 }
 
 // (4) dq, dk, dv, dlog_alpha and dbeta of every (chunk, head).
-template <int DK, int DV>
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArgs a) {
     constexpr BwdLayout L{DK, DV};
     __shared__ Stage st;
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
             lgacc[i] = 0.f;
             lsacc[i] = 0.f;
         }
-        load_chunk<DK, DV>(a, b, h, t0, n, S, true);
+        load_chunk<T, DK, DV>(a, b, h, t0, n, S, true);
         __syncthreads();
         chunk_factors<DK, DV>(S);
         for (int idx = tid; idx < C * DV; idx += kBwdThreads) S.U()[idx] = Ut[idx];
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         for (int idx = tid; idx < C * DV; idx += kBwdThreads) {  // dv, and dbeta's rowsum(dBv * v)
             const int r = idx / DV;
             const float dbv = S.dBv()[idx];
-            if (r < n) a.dv[row_of(a, b, t0 + r, h) * DV + idx % DV] = S.bet[r] * dbv;
+            if (r < n) static_cast<T *>(a.dv)[row_of(a, b, t0 + r, h) * DV + idx % DV] = from_f32<T>(S.bet[r] * dbv);
             const float t = wave_sum(dbv * S.V()[idx]);
             if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
         }
@@ -482,8 +483,8 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
             dgr = fmaf(dR, kv * eR, dgr);
             if (r < n) {
                 const size_t off = row_of(a, b, t0 + r, h) * DK + i;
-                a.dq[off] = s * dQO * eG + dQe * eGm;
-                a.dk[off] = bb * dBk * eG + dP * eGm + dN * emG + dR * eR;
+                static_cast<T *>(a.dq)[off] = from_f32<T>(s * dQO * eG + dQe * eGm);
+                static_cast<T *>(a.dk)[off] = from_f32<T>(bb * dBk * eG + dP * eGm + dN * emG + dR * eR);
             }
             const float t = wave_sum(dBk * kv * eG);
             if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
@@ -507,35 +508,40 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
     }
 }
 
-template <int DK, int DV>
+template <typename T, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const int total = a.B * a.n_chunks * a.H;
     if (total > 0) {
-        hipLaunchKernelGGL((kda_bwd_chunk_fwd_kernel<DK, DV>), dim3(a.n_groups), dim3(kBwdThreads), 0, st, a);
+        hipLaunchKernelGGL((kda_bwd_chunk_fwd_kernel<T, DK, DV>), dim3(a.n_groups), dim3(kBwdThreads), 0, st, a);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL((kda_bwd_states_kernel<DK, DV>), dim3(DV / kBwdCols, a.H, a.B), dim3(kBwdThreads), 0, st,
                            a);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (total > 0 || a.dh0) {
-        hipLaunchKernelGGL((kda_bwd_state_grads_kernel<DK, DV>), dim3(DV / kBwdCols, a.H, a.B), dim3(kBwdThreads), 0,
+        hipLaunchKernelGGL((kda_bwd_state_grads_kernel<T, DK, DV>), dim3(DV / kBwdCols, a.H, a.B), dim3(kBwdThreads), 0,
                            st, a);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     if (total > 0) {
-        hipLaunchKernelGGL((kda_bwd_chunk_grads_kernel<DK, DV>), dim3(a.n_groups), dim3(kBwdThreads), 0, st, a);
+        hipLaunchKernelGGL((kda_bwd_chunk_grads_kernel<T, DK, DV>), dim3(a.n_groups), dim3(kBwdThreads), 0, st, a);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
+template <typename T>
+hipError_t dispatch_bwd(const BwdArgs &a, int dk, int dv, hipStream_t stream) {
+    if (dk == 64 && dv == 64) return launch_bwd_t<T, 64, 64>(a, stream);
+    if (dk == 64 && dv == 128) return launch_bwd_t<T, 64, 128>(a, stream);
+    if (dk == 128 && dv == 64) return launch_bwd_t<T, 128, 64>(a, stream);
+    return launch_bwd_t<T, 128, 128>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, hipStream_t stream) {
-    if (dk == 64 && dv == 64) return launch_bwd_t<64, 64>(a, stream);
-    if (dk == 64 && dv == 128) return launch_bwd_t<64, 128>(a, stream);
-    if (dk == 128 && dv == 64) return launch_bwd_t<128, 64>(a, stream);
-    return launch_bwd_t<128, 128>(a, stream);
+hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, bool is_bf16, hipStream_t stream) {
+    return is_bf16 ? dispatch_bwd<bf16>(a, dk, dv, stream) : dispatch_bwd<float>(a, dk, dv, stream);
 }
 
 }  // namespace kda

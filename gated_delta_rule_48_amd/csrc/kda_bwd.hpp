@@ -35,15 +35,19 @@ struct BwdLayout {
 };
 
 struct BwdArgs {
-    const float *q, *k, *v, *log_alpha, *beta, *h0, *dout, *dhT;
+    const void *q, *k, *v;  // io dtype (fp32 or bf16), as dout and dq, dk, dv
+    const float *log_alpha, *beta, *h0;
+    const void *dout;
+    const float *dhT;
     float scale;
-    float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dh0;
+    void *dq, *dk, *dv;
+    float *dlog_alpha, *dbeta, *dh0;
     float *ws;       // B * n_chunks * H per-chunk buffers (BwdLayout)
     float *scratch;  // n_groups * BwdLayout::scratch() floats
     int B, T, H, n_chunks, n_groups;
 };
 
 // hipSuccess or the first launch error.
-hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, hipStream_t stream);
+hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, bool bf16, hipStream_t stream);
 
 }  // namespace kda

@@ -241,13 +241,14 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  * Arguments
  *   B, T, H, d_k, d_v   equal-length sequences [B, T, H, d] (no cu_seqlens);
  *               d_k, d_v in {64, 128}; B, H <= 65535.
- *   chunk       64.   io   KDA_F32 only (other dtypes KDA_ERR_UNSUPPORTED).
+ *   chunk       64.   io   dtype of q, k, v, dout and dq, dk, dv (KDA_F32 or KDA_BF16);
+ *               all arithmetic is fp32.
  *   q, k, v, log_alpha, beta, scale, h0   the forward call's inputs (h0 NULL =
  *               zero initial state).
- *   dout        [B, T, H, d_v] fp32, the gradient with respect to o.
+ *   dout        [B, T, H, d_v] dtype io, the gradient with respect to o.
  *   dhT         [B, H, d_k, d_v] fp32 or NULL (zero): with respect to hT.
- *   dq, dk      [B, T, H, d_k];  dv [B, T, H, d_v];  dlog_alpha [B, T, H, d_k];
- *               dbeta [B, T, H]: written, fp32, none overlapping any argument.
+ *   dq, dk      [B, T, H, d_k], dv [B, T, H, d_v]: dtype io;  dlog_alpha [B, T, H, d_k]
+ *               and dbeta [B, T, H]: fp32. Written, none overlapping any argument.
  *   dh0         [B, H, d_k, d_v] fp32 or NULL (not computed).
  *   workspace   kda_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned
  *               (about 300 KB per (chunk, head) at d = 128, plus a fixed scratch

@@ -260,7 +260,8 @@ def bwd(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), OK), (dict(T=0), OK),                      # nothing to do (no dh0 asked for)
     (dict(B=-1), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
-    (dict(io=BF16), UNSUPPORTED), (dict(io=5), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
+    (dict(io=BF16, ws=None), WORKSPACE),                   # bf16 is served: validation goes on
+    (dict(io=5), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
     (dict(dk=96), UNSUPPORTED), (dict(B=65536, T=1, H=1), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(dout=None), INVALID), (dict(dq=None), INVALID), (dict(dbeta=None), INVALID),
     (dict(q=A + 8), INVALID), (dict(beta=A + 2), INVALID), (dict(dh0=0x9000000 + 4), INVALID),
@@ -287,4 +288,5 @@ def test_chunk_bwd_workspace(lib):
 
     for args in ((2, 100, 4, 64, 64), (8, 8192, 32, 128, 128), (1, 1, 1, 64, 128), (3, 0, 2, 128, 64)):
         assert ws(*args, 64, F32) == expect(*args), args
-    assert ws(2, 100, 4, 64, 64, 64, BF16) == 0 and ws(2, 100, 4, 64, 64, 128, F32) == 0
+    assert ws(2, 100, 4, 64, 64, 64, BF16) == expect(2, 100, 4, 64, 64)  # fp32 buffers whatever the io dtype
+    assert ws(2, 100, 4, 64, 64, 128, F32) == 0

@@ -197,6 +197,11 @@ __device__ void load_chunk(const BwdArgs &a, int b, int h, int t0, int n, const 
     }
 }
 
+// x from the lane that a quad permutation (DPP) selects.
+template <int CTRL> __device__ __forceinline__ float quad_swap(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
 // Sum over the 64 lanes of a wave, left in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -255,18 +260,27 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_fwd_kernel(BwdArgs 
             if (r > i) cb[L.oAqk() + idx] = 0.f;  // Aqk^T: zero below the diagonal
         }
         __syncthreads();
-        // T = (I + A)^-1 by forward substitution, one column per thread of the first wave
-        if (tid < C) {
-            float x[C];
+        // T = (I + A)^-1 by forward substitution: column j on the four lanes of quad j, lane q
+        // holding x_i for i = q mod 4 and summing those terms; the quad's partial sums meet by
+        // two DPP swaps, so each step waits on one product and two exchanges
+        {
+            const int j = tid >> 2, q = tid & 3;
+            float x[C / 4];  // zero until solved: a zero coefficient may meet it before then
+#pragma unroll
+            for (int m = 0; m < C / 4; ++m) x[m] = 0.f;
 #pragma unroll
             for (int r = 0; r < C; ++r) {
-                float v = r == tid ? 1.f : 0.f;
+                float part = 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) v = fmaf(-sA[r][i], x[i], v);
-                x[r] = v;
+                for (int m = 0; m < C / 4; ++m)
+                    if (4 * m < r) part = fmaf(4 * m + q < r ? sA[r][4 * m + q] : 0.f, x[m], part);
+                part += quad_swap<0xB1>(part);  // quad_perm [1, 0, 3, 2]
+                part += quad_swap<0x4E>(part);  // quad_perm [2, 3, 0, 1]
+                const float xr = (r == j ? 1.f : 0.f) - part;
+                if ((r & 3) == q) x[r >> 2] = xr;
             }
 #pragma unroll
-            for (int r = 0; r < C; ++r) cb[L.oT() + r * C + tid] = x[r];
+            for (int m = 0; m < C / 4; ++m) cb[L.oT() + (4 * m + q) * C + j] = x[m];
         }
         __syncthreads();
         gemm<false, false, DK, C>(st, 1.f, cb + L.oT(), C, S.Bk(), DK, 0.f, cb + L.oW(), DK);

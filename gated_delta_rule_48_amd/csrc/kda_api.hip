@@ -336,7 +336,7 @@ int check_attn(int B, int H, int H_kv, int d, int T_max, int io) {
     if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (B < 0 || H < 1 || H_kv < 1 || T_max < 0 || H % H_kv != 0) return KDA_ERR_INVALID_ARG;
     const int G = H / H_kv;
-    if (!supported_dim(d) || (G != 1 && G != 2 && G != 4)) return KDA_ERR_UNSUPPORTED;
+    if (!supported_dim(d) || (G != 1 && G != 2 && G != 4 && G != 8)) return KDA_ERR_UNSUPPORTED;
     // grid limits, and 32-bit row offsets within one cached head
     if (B > 65535 || H_kv > 65535 || (int64_t)T_max * d > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;

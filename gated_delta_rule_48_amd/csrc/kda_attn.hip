@@ -23,7 +23,7 @@
 // maximum, sum and weighted value sum, in base 2 with log2(e) folded into the
 // query); the groups are merged by lane exchanges, the waves through LDS, and
 // the splits by a second kernel. The dot products stay on the vector ALUs: at
-// G <= 4 there are at most 8 flops per cached byte, far below the point where
+// G <= 8 there are at most 8 flops per cached byte (bf16), below the point where
 // the matrix cores would pay.
 
 #include "kda_attn.hpp"
@@ -284,7 +284,8 @@ template <int D, typename T>
 hipError_t dispatch_g(const AttnArgs &a, int B, hipStream_t st) {
     if (a.G == 1) return launch_attn_t<D, 1, T>(a, B, st);
     if (a.G == 2) return launch_attn_t<D, 2, T>(a, B, st);
-    return launch_attn_t<D, 4, T>(a, B, st);
+    if (a.G == 4) return launch_attn_t<D, 4, T>(a, B, st);
+    return launch_attn_t<D, 8, T>(a, B, st);
 }
 
 }  // namespace

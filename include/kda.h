@@ -284,7 +284,7 @@ int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
  *
  * Arguments
  *   B, H, H_kv  sequences, query heads, cached heads; H % H_kv == 0 and
- *               H / H_kv in {1, 2, 4}; B <= 65535, H_kv <= 65535.
+ *               H / H_kv in {1, 2, 4, 8}; B <= 65535, H_kv <= 65535.
  *   d           head dimension, 64 or 128 (queries, keys and values).
  *   T_max       rows allocated per cached head; T_max * d < 2^31.
  *   io          dtype of q, the caches and o (KDA_F32 or KDA_BF16).

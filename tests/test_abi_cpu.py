@@ -212,7 +212,7 @@ def attn(lib, **kw):
     (dict(B=0), OK),                                       # nothing to do, nothing launched
     (dict(B=-1), INVALID), (dict(H=0), INVALID), (dict(H_kv=0), INVALID), (dict(T_max=-1), INVALID),
     (dict(H=6, H_kv=4), INVALID),                          # H % H_kv != 0
-    (dict(H=16, H_kv=2), UNSUPPORTED),                     # groups of 8 query heads
+    (dict(H=32, H_kv=2), UNSUPPORTED),                     # groups of 16 query heads
     (dict(H=6, H_kv=2), UNSUPPORTED),                      # groups of 3
     (dict(d=96), UNSUPPORTED), (dict(io=2), UNSUPPORTED),
     (dict(B=65536, H=2, H_kv=2, T_max=1), UNSUPPORTED),    # grid limit

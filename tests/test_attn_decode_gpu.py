@@ -44,7 +44,7 @@ def _check(name, B, H, H_kv, T_max, d, io, seq_lens, seed, scale=None):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("G", [1, 2, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_attn_decode_ragged_lengths(io, d, G):
     # one split per (sequence, cached head); lengths that end mid-iteration, a single row
     _check("ragged", 3, 2 * G, 2, 300, d, io, [300, 1, 173], seed=11 + G)

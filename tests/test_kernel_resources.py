@@ -84,9 +84,10 @@ def test_fused_kernel_runs_two_waves_per_simd(resources):
 
 
 def test_attn_decode_keeps_loads_in_flight(resources):
-    # a streaming kernel: at least three waves per SIMD for every instance (2 dtypes x 2 head
-    # dimensions x 3 group sizes), so that enough cache rows are requested at once
-    attn = [r for n, r in resources.items() if "kda_attn_decode_kernel" in n]
-    assert len(attn) == 12
-    for r in attn:
-        assert int(r["Occupancy [waves/SIMD]"]) >= 3, r
+    # a streaming kernel: at least three waves per SIMD for the instances of 1, 2 and 4 query
+    # heads per cached head (2 dtypes x 2 head dimensions), so that enough cache rows are
+    # requested at once; groups of 8 hold 64 query values and 64 sums per lane, at least two
+    attn = {n: r for n, r in resources.items() if "kda_attn_decode_kernel" in n}
+    assert len(attn) == 16
+    for n, r in attn.items():
+        assert int(r["Occupancy [waves/SIMD]"]) >= (2 if "ELi8E" in n else 3), (n, r)

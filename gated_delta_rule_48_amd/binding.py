@@ -97,6 +97,8 @@ def _ptr(t) -> Optional[int]:
 
 
 def _check(t, name, dtype, shape, device):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} is on {t.device}: libkda's kernels read device memory only")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
@@ -200,8 +202,11 @@ def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = Non
     lib = load()
     dev = q.device
     io = _io_code(q.dtype)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _check(q, "q", q.dtype, (N, H, dk), dev)
     _check(k, "k", q.dtype, (N, H, dk), dev)
     _check(v, "v", q.dtype, (N, H, dv), dev)
     gate = _gate(log_alpha, (N,), H, dk, dev)
@@ -246,6 +251,7 @@ def chunk_fwd_preact(q, k, v, a, A_log, dt_bias, b, scale: Optional[float] = Non
         n_seqs = B
         lead = (B, T)
     dv = v.shape[-1]
+    _check(q, "q", q.dtype, lead + (H, dk), dev)
     _check(k, "k", q.dtype, lead + (H, dk), dev)
     _check(v, "v", q.dtype, lead + (H, dv), dev)
     _check(a, "a", q.dtype, lead + (H, dk), dev)
@@ -286,8 +292,11 @@ def recurrent_step_preact(q, k, v, a, A_log, dt_bias, b, state, scale: Optional[
     lib = load()
     dev = q.device
     io = _io_code(q.dtype)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
     N, H, dk = q.shape
     dv = v.shape[-1]
+    _check(q, "q", q.dtype, (N, H, dk), dev)
     _check(k, "k", q.dtype, (N, H, dk), dev)
     _check(v, "v", q.dtype, (N, H, dv), dev)
     _check(a, "a", q.dtype, (N, H, dk), dev)
@@ -322,8 +331,11 @@ def attn_decode(q, k_cache, v_cache, seq_lens=None, scale: Optional[float] = Non
     lib = load()
     dev = q.device
     io = _io_code(q.dtype)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H, d] and the caches [B, H_kv, T_max, d]")
     B, H, d = q.shape
     H_kv, T_max = k_cache.shape[1], k_cache.shape[2]
+    _check(q, "q", q.dtype, (B, H, d), dev)
     _check(k_cache, "k_cache", q.dtype, (B, H_kv, T_max, d), dev)
     _check(v_cache, "v_cache", q.dtype, (B, H_kv, T_max, d), dev)
     if seq_lens is not None:
@@ -358,9 +370,12 @@ def chunk_bwd(q, k, v, log_alpha, beta, dout, scale: Optional[float] = None, h0=
     lib = load()
     dev = q.device
     io = _io_code(q.dtype)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     f32 = torch.float32
+    _check(q, "q", q.dtype, (B, T, H, dk), dev)
     _check(k, "k", q.dtype, (B, T, H, dk), dev)
     _check(v, "v", q.dtype, (B, T, H, dv), dev)
     _check(log_alpha, "log_alpha", f32, (B, T, H, dk), dev)

@@ -176,6 +176,32 @@ def gen_sequences(seqlens, H, dk, dv, io, gates, h0, seed):
     return out
 
 
+def gen_key_repeats(seqlens, H, dk, dv, io, kind, seed, gates="weak"):
+    """A batch of gen_sequences with keys that collide inside a chunk and beta = 1 (the
+    regime where the delta rule overwrites what a key stored). kind "repeat": every
+    token's key is one of three fixed unit vectors of its head, drawn at random per
+    token (exact repeats, also after rounding); kind "near": every key is its head's
+    fixed unit vector plus a random direction of length 0.1, normalised (cosine
+    about 0.99 between any two keys of a head)."""
+    x = gen_sequences(seqlens, H, dk, dv, io, gates, "normal", seed)
+    rng = np.random.Generator(np.random.PCG64([seed, 0xC3]))
+    T = int(sum(seqlens))
+    if kind == "repeat":
+        pool = _unit_gaussian(rng, (3, H), dk)                   # [3, H, dk]
+        pick = rng.integers(0, 3, size=(T, H))
+        k = pool[pick, np.arange(H)[None, :]]
+    elif kind == "near":
+        base = _unit_gaussian(rng, (H,), dk).astype(np.float64)  # [H, dk]
+        u = _unit_gaussian(rng, (T, H), dk).astype(np.float64)
+        k = base[None] + 0.1 * u
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    else:
+        raise ValueError(kind)
+    x["k"] = _io(k.astype(np.float32), io)
+    x["beta"] = np.ones((T, H), dtype=np.float32)
+    return x
+
+
 def gen_preact(T_total, H, dk, io, seed):
     """Gate pre-activations for the kernels that form the gates themselves: a ~ N(0,1)
     [T, H, dk] (rounded to the io dtype), A_log = log U(1, 16) per head, dt_bias =
@@ -236,6 +262,24 @@ def gen_grad_outputs(B, T, H, dk, dv, seed):
     rng = np.random.Generator(np.random.PCG64([seed, 0xB2]))
     return dict(dout=rng.standard_normal((B, T, H, dv), dtype=np.float32),
                 dhT=rng.standard_normal((B, H, dk, dv), dtype=np.float32))
+
+
+def gen_decode_step_device(N, H, dk, dv, dtype, seed, step, device):
+    """Inputs of decode step `step` drawn on the GPU with torch's seeded generator (seed
+    mixed with the step): the decode recipe with "main" gates. q, k [N, H, dk] N(0,1)
+    L2-normalised per (sequence, head), v [N, H, dv] N(0,1), all in dtype; log_alpha
+    [N, H, dk] = -softplus(N(-2, 1)) and beta [N, H] = sigmoid(N(0, 1)) in fp32. For long
+    runs over the full batch, where drawing every step on the host would dominate."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(step))
+    rn = lambda *s: torch.randn(s, generator=g, device=device, dtype=torch.float32)  # noqa: E731
+    q = torch.nn.functional.normalize(rn(N, H, dk), dim=-1).to(dtype)
+    k = torch.nn.functional.normalize(rn(N, H, dk), dim=-1).to(dtype)
+    v = rn(N, H, dv).to(dtype)
+    la = -torch.nn.functional.softplus(rn(N, H, dk) - 2.0)
+    beta = torch.sigmoid(rn(N, H))
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta)
 
 
 def gen_workload(w: Workload, seed: Optional[int] = None):

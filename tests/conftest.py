@@ -18,3 +18,16 @@ def ref():
     """The fp64 oracle (built on first use)."""
     import oracle
     return oracle.kda_reference
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The parity line of every GPU comparison (whole-tensor, worst head, worst row), so
+    that they appear in the log of a quiet run too."""
+    try:
+        from kda_testlib import PARITY_LOG
+    except ImportError:
+        return
+    if PARITY_LOG:
+        terminalreporter.section("parity: whole tensor, worst (sequence, head), worst row")
+        for line in PARITY_LOG:
+            terminalreporter.write_line(line)

@@ -52,10 +52,12 @@ def test_attn_decode_ragged_lengths(io, d, G):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_attn_decode_split_cache(io, d):
+@pytest.mark.parametrize("G", [1, 8])
+def test_attn_decode_split_cache(io, d, G):
     # 5000 rows over 4 splits of 1280: a sequence ending inside the second split (the
-    # others empty), and one with no rows at all (o = 0)
-    o, _ = _check("splits", 3, 4, 2, 5000, d, io, [5000, 2049, 0], seed=21, scale=0.11)
+    # others empty), and one with no rows at all (o = 0); groups of 1 and of 8 query heads
+    # per cached head (the split partials and the combine kernel at H = 8 H_kv)
+    o, _ = _check("splits", 3, 2 * G, 2, 5000, d, io, [5000, 2049, 0], seed=21 + G, scale=0.11)
     assert np.all(o[2] == 0)
 
 

@@ -23,8 +23,9 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_preact", "kda_recurrent_step",
            "kda_recurrent_step_gated", "kda_recurrent_step_preact", "kda_attn_decode_workspace_bytes",
-           "kda_attn_decode", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
-ABI_VERSION = 4
+           "kda_attn_decode", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_noalloc")
+ABI_VERSION = 5
+NOALLOC_MAX_WORKSPACE = 32 << 20  # KDA_NOALLOC_MAX_WORKSPACE
 
 
 class KdaError(RuntimeError):
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_bwd_workspace_bytes.restype = Z
     lib.kda_chunk_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.kda_chunk_bwd.restype = I
+    lib.kda_chunk_fwd_noalloc.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, I, P, P, P]
+    lib.kda_chunk_fwd_noalloc.restype = I
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libkda.so has ABI {lib.kda_abi_version()}, this binding expects {ABI_VERSION}; "
                            "rebuild it")
@@ -133,18 +136,8 @@ def workspace_bytes(B, T, H, dk, dv, chunk, n_seqs, io) -> int:
     return int(load().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, n_seqs, io))
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, cu_seqlens=None,
-              chunk: int = 64, output_final_state: bool = True, o=None, hT=None, workspace=None,
-              stream=None):
-    """Chunked KDA forward (kda_chunk_fwd_gated).
-
-    q, k [B, T, H, dk] (or packed [T, H, dk] with cu_seqlens); v [.., H, dv];
-    log_alpha fp32 [.., H, dk] (a decay per key channel), [.., H] (one per token and
-    head, Gated DeltaNet) or None (no decay, DeltaNet); beta [.., H] fp32;
-    h0 [n_seq, H, dk, dv] fp32 or None;
-    cu_seqlens int32 [n_seqs + 1] on the device, or None. Returns (o, hT); hT is
-    None when output_final_state is False.
-    """
+def _chunk_fwd_call(noalloc, q, k, v, log_alpha, beta, scale, h0, cu_seqlens, chunk, output_final_state, o, hT,
+                    workspace, stream):
     import torch
     lib = load()
     dev = q.device
@@ -177,20 +170,51 @@ def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, 
         hT = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
     if hT is not None:
         _check(hT, "hT", torch.float32, (n_seqs, H, dk, dv), dev)
-    need = int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk,
-                                                 n_seqs if cu_seqlens is not None else 0, io))
+    if scale is None:
+        scale = dk ** -0.5
+    ns_arg = n_seqs if cu_seqlens is not None else 0
+    if noalloc:
+        st = lib.kda_chunk_fwd_noalloc(gate, B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(log_alpha), _ptr(beta), float(scale), _ptr(h0), _ptr(cu_seqlens),
+                                       ns_arg, _ptr(o), _ptr(hT), _stream(stream))
+        if st != 0:
+            raise KdaError(st, "kda_chunk_fwd_noalloc")
+        return o, hT
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, ns_arg, io))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if scale is None:
-        scale = dk ** -0.5
     st = lib.kda_chunk_fwd_gated(gate, B, T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                                 _ptr(beta), float(scale), _ptr(h0), _ptr(cu_seqlens),
-                                 n_seqs if cu_seqlens is not None else 0, _ptr(o), _ptr(hT),
+                                 _ptr(beta), float(scale), _ptr(h0), _ptr(cu_seqlens), ns_arg, _ptr(o), _ptr(hT),
                                  _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_gated")
     return o, hT
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, cu_seqlens=None,
+              chunk: int = 64, output_final_state: bool = True, o=None, hT=None, workspace=None,
+              stream=None):
+    """Chunked KDA forward (kda_chunk_fwd_gated).
+
+    q, k [B, T, H, dk] (or packed [T, H, dk] with cu_seqlens); v [.., H, dv];
+    log_alpha fp32 [.., H, dk] (a decay per key channel), [.., H] (one per token and
+    head, Gated DeltaNet) or None (no decay, DeltaNet); beta [.., H] fp32;
+    h0 [n_seq, H, dk, dv] fp32 or None;
+    cu_seqlens int32 [n_seqs + 1] on the device, or None. Returns (o, hT); hT is
+    None when output_final_state is False.
+    """
+    return _chunk_fwd_call(False, q, k, v, log_alpha, beta, scale, h0, cu_seqlens, chunk, output_final_state, o,
+                           hT, workspace, stream)
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, scale: Optional[float] = None, h0=None, cu_seqlens=None,
+                      chunk: int = 64, output_final_state: bool = True, o=None, hT=None, stream=None):
+    """chunk_fwd through kda_chunk_fwd_noalloc: the library's own fixed workspace (at most
+    NOALLOC_MAX_WORKSPACE bytes; calls overlapping on one GPU race). Pass o (and hT) to
+    allocate nothing; otherwise they are allocated here as in chunk_fwd."""
+    return _chunk_fwd_call(True, q, k, v, log_alpha, beta, scale, h0, cu_seqlens, chunk, output_final_state, o,
+                           hT, None, stream)
 
 
 def recurrent_step(q, k, v, log_alpha, beta, state, scale: Optional[float] = None, o=None,

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/kda.h"
@@ -124,14 +125,54 @@ KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, in
     return L.total;
 }
 
+// ---------------------------------------------------------------- the workspace of kda_chunk_fwd_noalloc
+//
+// A fixed device array that takes the place of the caller's workspace. Each GPU the
+// library runs on holds its own copy until the process ends. In host code `scratch`
+// names a host-side stand-in, not the array's device address, so host code never
+// uses it directly: the address is looked up once per device (with that device
+// current) and kept in scratch_dev; kernels receive that pointer. Calls on one GPU
+// share the array, so calls that overlap in time on one GPU race (the workspace of
+// kda_chunk_fwd is caller-owned instead). Nothing in the chunked passes' workspace
+// has to start at zero: every byte a kernel reads was written earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call per device).
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
 namespace {
 
 // kda_chunk_fwd_gated (gate = a kda_gate value) and kda_chunk_fwd_preact (gate =
-// kda::kGatePreact, pre = its pre-activations; log_alpha unused, beta = b).
+// kda::kGatePreact, pre = its pre-activations; log_alpha unused, beta = b). With
+// use_scratch (kda_chunk_fwd_noalloc) the workspace is the device array `scratch`,
+// looked up once every argument has been validated.
 int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, int d_k, int d_v, int chunk, int io,
                    const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
                    float scale, const float *h0, const int32_t *cu_seqlens, int n_seqs, void *o, float *hT,
-                   void *workspace, size_t workspace_bytes, void *stream) {
+                   void *workspace, size_t workspace_bytes, void *stream, bool use_scratch = false) {
     const bool varlen = cu_seqlens != nullptr;
     kda_status st = check_sizes(B, T, H, d_k, d_v, chunk, io, varlen, n_seqs);
     if (st != KDA_OK) return st;
@@ -164,6 +205,15 @@ int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, in
 
     WsLayout L;
     ws_layout(B, T, H, d_k, d_v, chunk, varlen ? n_seqs : 0, varlen, io, &L);
+    if (use_scratch) {
+        if (L.total > KDA_NOALLOC_MAX_WORKSPACE) return KDA_ERR_WORKSPACE;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (L.total > 0) {
+            if (scratch_address(&workspace) != hipSuccess) return KDA_ERR_HIP;
+            workspace_bytes = KDA_NOALLOC_MAX_WORKSPACE;
+        }
+    }
     if (L.total > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total))
         return KDA_ERR_WORKSPACE;
 
@@ -215,6 +265,7 @@ int recurrent_step_impl(int gate, const kda::PreactArgs &pre, int N, int H, int 
 
 }  // namespace
 
+
 KDA_EXPORT int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
                                    const void *q, const void *k, const void *v,
                                    const float *log_alpha, const float *beta, float scale,
@@ -236,6 +287,16 @@ KDA_EXPORT int kda_chunk_fwd_preact(int flags, int B, int T, int H, int d_k, int
     return chunk_fwd_impl(kda::kGatePreact, pre, B, T, H, d_k, d_v, chunk, io, q,
                           k, v, nullptr, b, scale, h0, cu_seqlens, n_seqs, o, hT, workspace, workspace_bytes,
                           stream);
+}
+
+KDA_EXPORT int kda_chunk_fwd_noalloc(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                                     const void *q, const void *k, const void *v,
+                                     const float *log_alpha, const float *beta, float scale,
+                                     const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                                     void *o, float *hT, void *stream) {
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE) return KDA_ERR_INVALID_ARG;
+    return chunk_fwd_impl(gate, kda::PreactArgs{}, B, T, H, d_k, d_v, chunk, io, q, k, v, log_alpha, beta, scale,
+                          h0, cu_seqlens, n_seqs, o, hT, nullptr, 0, stream, true);
 }
 
 KDA_EXPORT int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,

@@ -16,8 +16,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor argument is a caller-owned DEVICE pointer on the current HIP
- *    device, contiguous, 16-byte aligned. The library allocates nothing, keeps
- *    no global mutable state, never synchronises and never prints.
+ *    device, contiguous, 16-byte aligned. The library allocates nothing, never
+ *    synchronises and never prints. Its only global state belongs to
+ *    kda_chunk_fwd_noalloc: a fixed device array per GPU and its address.
  *  - Layouts are token-major: q, k [T_total, H, d_k]; v, o [T_total, H, d_v];
  *    log_alpha [T_total, H, d_k] fp32; beta [T_total, H] fp32; states
  *    [n_seqs, H, d_k, d_v] fp32 row-major (row = key channel).
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
     KDA_OK = 0,
@@ -151,6 +152,34 @@ int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chu
                         const float *h0, const int32_t *cu_seqlens, int n_seqs,
                         void *o, float *hT, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd_gated without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The library allocates nothing here either: the
+ * workspace is a fixed device array of KDA_NOALLOC_MAX_WORKSPACE bytes inside the
+ * library, one per GPU, held until the process ends.
+ *
+ * Arguments, results and errors are those of kda_chunk_fwd_gated. In addition, sizes whose
+ * workspace (kda_chunk_fwd_workspace_bytes) exceeds KDA_NOALLOC_MAX_WORKSPACE are
+ * rejected with KDA_ERR_WORKSPACE before anything is enqueued; that covers every call of
+ * the one-launch pass (bf16, d_k = d_v = 128, chunk 64, at least 256 (sequence, head)
+ * pairs, whose workspace is 256 bytes) and split-pass calls of up to about 25,000 to
+ * 30,000 token-heads at d = 128. The first call on a device looks up the array's device address
+ * (KDA_ERR_HIP if that fails).
+ *
+ * All calls on one GPU share the array: calls whose work overlaps in time on one GPU
+ * (other streams, other host threads) race and give undefined results. Calls in order on
+ * one stream are safe. The array keeps the last call's contents; no call reads what an
+ * earlier one left.
+ */
+#define KDA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+
+int kda_chunk_fwd_noalloc(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
+                          const void *q, const void *k, const void *v,
+                          const float *log_alpha, const float *beta, float scale,
+                          const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                          void *o, float *hT, void *stream);
 
 /*
  * kda_chunk_fwd_preact -- kda_chunk_fwd with the gates formed inside the kernels

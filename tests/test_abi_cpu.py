@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing, misaligned or too small")]:
         assert lib.kda_status_string(code) == text
     assert lib.kda_status_string(99) == b"unknown status"
@@ -146,6 +146,35 @@ def fwd_gated(lib, gate, **kw):
 ])
 def test_chunk_fwd_gated_validation(lib, gate, kw, code):
     assert fwd_gated(lib, gate, **kw) == code
+
+
+def fwd_noalloc(lib, gate=0, **kw):
+    a = dict(B=2, T=100, H=4, dk=128, dv=128, chunk=64, io=BF16, q=A, k=A, v=A, la=A, beta=A,
+             scale=0.088, h0=None, cu=None, n_seqs=0, o=0x4000000, hT=None, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_noalloc(gate, a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"],
+                                     a["k"], a["v"], a["la"], a["beta"], a["scale"], a["h0"], a["cu"],
+                                     a["n_seqs"], a["o"], a["hT"], a["stream"])
+
+
+@pytest.mark.parametrize("gate,kw,code", [
+    (3, {}, INVALID), (0, dict(dk=96), UNSUPPORTED), (0, dict(q=None), INVALID), (0, dict(o=A), INVALID),
+    (0, dict(la=A + 4), INVALID), (2, dict(la=None, chunk=32), UNSUPPORTED), (0, dict(scale=float("nan")), INVALID),
+    # split-pass sizes whose workspace exceeds the library's fixed array (32 MiB)
+    (0, dict(B=1, T=8192, H=16, o=1 << 36), WORKSPACE), (0, dict(B=1, T=100000, H=4, io=F32, o=1 << 36), WORKSPACE),
+])
+def test_chunk_fwd_noalloc_validation(lib, gate, kw, code):
+    """Everything is checked before the fixed workspace's address is looked up (which would
+    need a GPU): these calls return during validation."""
+    assert fwd_noalloc(lib, gate, **kw) == code
+
+
+def test_noalloc_limit_matches_header(lib):
+    text = open(HEADER).read()
+    assert "#define KDA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)" in text
+    assert kda.binding.NOALLOC_MAX_WORKSPACE == 32 << 20
+    # the one-launch pass needs only its 256-byte discard slot, at any length
+    assert lib.kda_chunk_fwd_workspace_bytes(8, 1 << 20, 32, 128, 128, 64, 0, BF16) == 256
 
 
 def test_chunk_fwd_is_the_per_channel_gated_call(lib):

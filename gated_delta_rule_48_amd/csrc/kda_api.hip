@@ -46,7 +46,7 @@ bool use_fused(int B, int T, int H, int dk, int dv, int C, bool varlen, int io, 
 }
 
 struct WsLayout {
-    size_t W, U, QO, KtT, Aqk, eg, discard, choff, total;
+    size_t W, U, QO, KtT, Aqk, eg, strong, discard, choff, total;
     int64_t n_chunks;  // upper bound on the number of chunks over all sequences
 };
 
@@ -55,11 +55,13 @@ struct WsLayout {
 bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varlen, int io,
                WsLayout *L) {
     if (T <= 0) {
-        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         return true;
     }
-    if (use_fused(B, T, H, dk, dv, C, varlen, io, n_seqs)) {  // only the discard slot
-        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 256, 0};
+    if (use_fused(B, T, H, dk, dv, C, varlen, io, n_seqs)) {
+        // the discard slot, and one byte per (sequence, head): left to the strong-decay instance
+        *L = WsLayout{0, 0, 0, 0, 0, 0, 256, 0, 0, 0, 0};
+        L->total = 256 + round_up((size_t)(varlen ? n_seqs : B) * H, 256);
         L->n_chunks = 0;
         return true;
     }
@@ -79,6 +81,7 @@ bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varl
     L->KtT = take(nch * dk * C * esz);
     L->Aqk = take(nch * C * C * esz);
     L->eg = take(nch * dk * sizeof(float));
+    L->strong = take(nch);  // one byte per (chunk, head)
     L->discard = take(256);  // absorbs stores of rows past a sequence's end
     // chunk offsets [n_seqs + 1], then sequence begins and ends [n_seqs] each
     L->choff = varlen ? take(((size_t)3 * n_seqs + 1) * sizeof(int32_t)) : 0;
@@ -222,13 +225,14 @@ int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, in
     const bool bf = io == KDA_BF16;
     if (use_fused(B, T, H, d_k, d_v, chunk, varlen, io, n_seqs)) {
         kda::FusedArgs fa{q,  k,     v,  log_alpha, beta, scale, h0, hT,   o, ws + L.discard, H,
-                          T,  varlen ? cu_seqlens : nullptr, (int)tokens, gate, pre};
+                          T,  varlen ? cu_seqlens : nullptr, (int)tokens, gate, pre,
+                          reinterpret_cast<uint8_t *>(ws + L.strong)};
         return kda::launch_fused(fa, d_k, d_v, bf, nseq, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     ChunkBuffers buf{};
     if (L.total > 0) {
         buf = ChunkBuffers{ws + L.W, ws + L.U, ws + L.QO, ws + L.KtT, ws + L.Aqk,
-                           reinterpret_cast<float *>(ws + L.eg)};
+                           reinterpret_cast<float *>(ws + L.eg), reinterpret_cast<uint8_t *>(ws + L.strong)};
     }
 
     kda::SeqMap map{};

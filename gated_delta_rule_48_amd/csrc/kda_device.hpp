@@ -182,6 +182,21 @@ template <int D> __device__ __forceinline__ float dpp_row_shr(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                  0x110 | D, 0xf, 0xf, true));
 }
+template <int D> __device__ __forceinline__ float dpp_row_shl(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 0x100 | D, 0xf, 0xf, true));
+}
+// Sum over the later lanes of each 16-lane DPP row (lanes i + 1 .. 15 for lane i): the
+// exclusive suffix sum, formed from the values themselves (not as a difference of
+// prefix sums, which would cancel where the prefixes are large).
+__device__ __forceinline__ float row16_exclusive_suffix_sum(float x) {
+    x = dpp_row_shl<1>(x);
+    x += dpp_row_shl<1>(x);
+    x += dpp_row_shl<2>(x);
+    x += dpp_row_shl<4>(x);
+    x += dpp_row_shl<8>(x);
+    return x;
+}
 __device__ __forceinline__ float row16_inclusive_sum(float x) {
     x += dpp_row_shr<1>(x);
     x += dpp_row_shr<2>(x);
@@ -189,6 +204,92 @@ __device__ __forceinline__ float row16_inclusive_sum(float x) {
     x += dpp_row_shr<8>(x);
     return x;
 }
+
+// Value of lane I of this lane's 16-lane DPP row (row_newbcast).
+template <int I> __device__ __forceinline__ float dpp_row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + I, 0xf, 0xf, true));
+}
+
+// ---------------------------------------------------------------- strong decay: diagonal Gram tiles pair by pair
+//
+// Inside one 16-row block of a chunk, the decayed Gram entries
+//     A[r][i]   = sum_c k[r][c] k[i][c] e^(g[r][c] - g[i][c])        (i < r)
+//     Aqk[r][i] = sum_c q[r][c] k[i][c] e^(g[r][c] - g[i][c])        (i <= r)
+// (g: the running sum of log alpha, which does not increase with r) carry a factor
+// in (0, 1] for every pair that counts. When the block's decay spans more than the
+// fp32 range, no factorisation e^(g[r] - m) e^(m - g[i]) with one reference m keeps
+// both factors finite, so these entries are formed one pair at a time, each factor
+// from its own exponent. Lane (r, hi) of the calling wave holds N channels of row r
+// (the same channels in every lane of its group hi): kf, qf (q times the query scale)
+// and g, the prefix local to the block (its offset cancels in g[r] - g[i]).
+// diag_pairs_accum adds this lane's share to a[i] (A[r][i]) and aq[i] (Aqk[r][i]) for
+// the 16 rows i of the block; diag_pairs_reduce then sums the four lane groups, so that
+// every lane of row r holds the totals. Entries with i > r (and a's entry i = r) are
+// finite values to be discarded.
+template <int I, int N>
+__device__ __forceinline__ void diag_pair_sums(const float *kf, const float *qf, const float *g, float *a, float *aq) {
+    constexpr float kL2E = 1.4426950408889634f;
+    float sa = a[I], sq = aq[I];
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        const float ki = dpp_row_bcast<I>(kf[c]);
+        const float gi = dpp_row_bcast<I>(g[c]);
+        const float kd = ki * __builtin_amdgcn_exp2f(fminf((g[c] - gi) * kL2E, 0.f));
+        sa = fmaf(kf[c], kd, sa);
+        sq = fmaf(qf[c], kd, sq);
+    }
+    a[I] = sa;
+    aq[I] = sq;
+    // one column i at a time: interleaving the sixteen keeps all their broadcasts live
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int N>
+__device__ __forceinline__ void diag_pairs_accum(const float *kf, const float *qf, const float *g, float *a, float *aq) {
+    diag_pair_sums<0, N>(kf, qf, g, a, aq);
+    diag_pair_sums<1, N>(kf, qf, g, a, aq);
+    diag_pair_sums<2, N>(kf, qf, g, a, aq);
+    diag_pair_sums<3, N>(kf, qf, g, a, aq);
+    diag_pair_sums<4, N>(kf, qf, g, a, aq);
+    diag_pair_sums<5, N>(kf, qf, g, a, aq);
+    diag_pair_sums<6, N>(kf, qf, g, a, aq);
+    diag_pair_sums<7, N>(kf, qf, g, a, aq);
+    diag_pair_sums<8, N>(kf, qf, g, a, aq);
+    diag_pair_sums<9, N>(kf, qf, g, a, aq);
+    diag_pair_sums<10, N>(kf, qf, g, a, aq);
+    diag_pair_sums<11, N>(kf, qf, g, a, aq);
+    diag_pair_sums<12, N>(kf, qf, g, a, aq);
+    diag_pair_sums<13, N>(kf, qf, g, a, aq);
+    diag_pair_sums<14, N>(kf, qf, g, a, aq);
+    diag_pair_sums<15, N>(kf, qf, g, a, aq);
+}
+
+__device__ __forceinline__ void diag_pairs_reduce(float *a, float *aq) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        a[i] += __shfl_xor(a[i], 16);
+        a[i] += __shfl_xor(a[i], 32);
+        aq[i] += __shfl_xor(aq[i], 16);
+        aq[i] += __shfl_xor(aq[i], 32);
+    }
+}
+
+// x[4 hi .. 4 hi + 3] for the lane group hi (0..3), by selects among values held in
+// registers (every index is a constant, so the array never needs a memory copy).
+__device__ __forceinline__ f32x4 group4(const float *x, int hi) {
+    const f32x4 v0 = {x[0], x[1], x[2], x[3]}, v1 = {x[4], x[5], x[6], x[7]};
+    const f32x4 v2 = {x[8], x[9], x[10], x[11]}, v3 = {x[12], x[13], x[14], x[15]};
+    f32x4 v = v0;
+    v = hi == 1 ? v1 : v;
+    v = hi == 2 ? v2 : v;
+    v = hi == 3 ? v3 : v;
+    return v;
+}
+
+// Chunks whose summed log alpha falls below -kStrongDecay on some key channel take the
+// pair-by-pair path above (the midpoint factors 2^(+-|gamma|/2) of the usual path stay
+// within the fp32 range, e^(+-85), only above -170).
+constexpr float kStrongDecay = 160.f;
 
 __device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }

@@ -72,12 +72,17 @@ struct Lds {
     static constexpr int KM = DG + 4 * 64 * 4 * 2;      // [C][DK]  bf16 fragments: Km (Gram)
     static constexpr int KP = KM + kC * kDK * 2;        // [C][DK]  bf16 fragments: Kp (Gram and state)
     static constexpr int IDN = KP + kC * kDK * 2;       // [2][64]  bf16x8: each lane's identity operands (ident_frag)
-    static constexpr int FLG = IDN + 2 * 64 * 16;       // [2]      int: E E_prev leaves the normal fp32 range
+    static constexpr int FLG = IDN + 2 * 64 * 16;       // [4]      int: E E_prev leaves the normal fp32 range (0, 1);
+                                                        //          some channel decays strongly (2, 3)
     static constexpr int DTB = FLG + 16;                // [DK]     fp32: dt_bias of the head (pre-activation gates)
     static constexpr int QKS = DTB + kDK * 4;           // [2][C][2] fp32: per half, each row's sums of squares of
                                                         //           silu(k) (scan phase), silu(q) (elementwise phase)
     static constexpr int QNR = QKS + 2 * kC * 2 * 4;   // [C] fp32: inverse norms of the rows of silu(q)
-    static constexpr int SIZE = QNR + kC * 4;
+    // strong-decay instance only:
+    static constexpr int GPRE = QNR + kC * 4;          // [5][DK] fp32: log2 decay before row block 0..3, gamma
+    static constexpr int EGAM = GPRE + 5 * kDK * 4;    // [DK] fp32 (e_slot order): exp(gamma)
+    static constexpr int SAQ = EGAM + kDK * 4;         // [10][256] fp32: half 1's partial Aqk tiles (rb, tj <= rb)
+    static constexpr int SIZE = SAQ + 10 * 256 * 4;
 };
 static_assert(Lds::SIZE <= 160 * 1024, "fused LDS budget");
 
@@ -194,7 +199,13 @@ __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb 
     (void)hi;                                                                  \
     (void)r;
 
-template <int G>
+// kStrong = false: the usual instance. Where a chunk's decay sums below -kStrongDecay on
+// some channel (the midpoint factors of the usual path would leave the fp32 range), it
+// records the (sequence, head) in a.redo and stops. kStrong = true: runs after it, on the
+// recorded pairs only, from the start of the sequence, with every exponent <= 0: the
+// state-side factors taken from the chunk's start, the Gram tiles left of the diagonal
+// from the end of their column block, the diagonal tiles pair by pair.
+template <int G, bool kStrong>
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     // G: the kda_gate kinds, kGatePreact, and kGatePreactQK (kGatePreact with q and k
     // normalised here as well)
@@ -221,7 +232,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     float *dtb = reinterpret_cast<float *>(smem + Lds::DTB);
     float *qks = reinterpret_cast<float *>(smem + Lds::QKS);
     float *qnr = reinterpret_cast<float *>(smem + Lds::QNR);
+    float *gpre = reinterpret_cast<float *>(smem + Lds::GPRE);
+    float *egam = reinterpret_cast<float *>(smem + Lds::EGAM);
+    float *saq = reinterpret_cast<float *>(smem + Lds::SAQ);
 
+    if constexpr (kStrong) {
+        if (a.redo[blockIdx.x] == 0) return;  // the usual instance finished this pair
+    }
     const int H = a.H;
     const int s = blockIdx.x / H, h = blockIdx.x % H;
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, hi = l >> 4;
@@ -469,17 +486,112 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             ehalf[kDK + e_slot(tid)] = exp2_fast(m * kL2E);
             // whether E E_prev of some channel falls below the normal fp32 range
             const unsigned long long tiny = __ballot((m + m_prev) * kL2E < -120.f);
-            if ((tid & 63) == 0) flg[tid >> 6] = tiny != 0ull;
+            // whether some channel decays past the midpoint factors' range
+            const unsigned long long strong = __ballot(gam < -kStrongDecay);
+            if ((tid & 63) == 0) {
+                flg[tid >> 6] = tiny != 0ull;
+                flg[2 + (tid >> 6)] = strong != 0ull;
+            }
             m_prev = m;
+            if constexpr (kStrong) {  // block prefixes and gamma in log2 units; exp(gamma)
+                gpre[tid] = 0.f;
+                gpre[kDK + tid] = t0v * kL2E;
+                gpre[2 * kDK + tid] = (t0v + t1) * kL2E;
+                gpre[3 * kDK + tid] = (t0v + t1 + t2) * kL2E;
+                gpre[4 * kDK + tid] = gam * kL2E;
+                egam[e_slot(tid)] = exp2_fast(gam * kL2E);
+            }
         }
         __syncthreads();
+        if constexpr (!kStrong) {
+            // a chunk of strong decay: the pair is left to the strong instance
+            if (__builtin_amdgcn_readfirstlane(flg[2] | flg[3]) != 0) {
+                if (tid == 0) a.redo[blockIdx.x] = 1;
+                return;
+            }
+        }
 
         // ---- 2. elementwise, with d = g - gamma/2 (clamped), u = exp(d), 1/u = exp(-d):
         //      Kp = k u, Qp = q u and Km = k / u (registers and LDS; the query scale is
         //      applied to Aqk and O); Km^T, Kp^T and v^T transposed by the matrix cores
         //      into LDS (beta is carried by T's columns)
         bf16x8 kpf[2], qpf[2];
-        {
+        // strong instance: the diagonal Gram tiles' sums over this half's channels (row r,
+        // columns 16 rb + 4 hi + i)
+        f32x4 sad4, saq4;
+        if constexpr (kStrong) {
+        KDA_PHASE_LANE
+        float sq = 0.f;
+        float skf[2][8], sqf[2][8], sad[16], saqd[16];
+        const bf16x8 id0 = *reinterpret_cast<const bf16x8 *>(idn + l * 8);
+        const bf16x8 id1 = *reinterpret_cast<const bf16x8 *>(idn + (64 + l) * 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sad[i] = saqd[i] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float qv = static_cast<float>(qr[x][e]);
+                if constexpr (kQK) {  // silu(q); its row norm is applied to Aqk and O
+                    qv *= __builtin_amdgcn_rcpf(1.f + exp2_fast(-qv * kL2E));
+                    sq = fmaf(qv, qv, sq);
+                }
+                skf[x][e] = kQK ? static_cast<float>(kr[x][e]) * rk : static_cast<float>(kr[x][e]);
+                sqf[x][e] = qv;
+            }
+            diag_pairs_accum<8>(skf[x], sqf[x], g[x], sad, saqd);
+        }
+        diag_pairs_reduce(sad, saqd);
+        sad4 = group4(sad, hi);
+        saq4 = group4(saqd, hi);
+        // state-side operands from the chunk's start: Kp = k 2^ga, Qp = q 2^ga, Km^T =
+        // (k 2^(gamma - ga))^T; the Gram's column operand of this block from its end, in Km:
+        // k 2^(b - ga), b the decay up to the block's last row (every factor <= 1)
+        // (LDS positions from an opaque lane index, so that they are not hoisted out of the
+        // chunk loop and kept live across it)
+        const int ho = opaque_lane() >> 4;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int kg = 2 * hf + x;
+            float xp[8], xq[8], xm[8], xc[8];
+            const int c0 = frag_chan<bf16>(kg, ho, 0), c4 = frag_chan<bf16>(kg, ho, 4);
+            const f32x4 gp[2] = {*reinterpret_cast<const f32x4 *>(gpre + rb * kDK + c0),
+                                 *reinterpret_cast<const f32x4 *>(gpre + rb * kDK + c4)};
+            const f32x4 gg[2] = {*reinterpret_cast<const f32x4 *>(gpre + 4 * kDK + c0),
+                                 *reinterpret_cast<const f32x4 *>(gpre + 4 * kDK + c4)};
+            const f32x4 tb[2] = {*reinterpret_cast<const f32x4 *>(tot + rb * kDK + c0),
+                                 *reinterpret_cast<const f32x4 *>(tot + rb * kDK + c4)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float gl = g[x][e] * kL2E, ga = gl + gp[e >> 2][e & 3];
+                const float u = exp2_fast(ga), um = exp2_fast(gg[e >> 2][e & 3] - ga);
+                xp[e] = skf[x][e] * u;
+                xq[e] = sqf[x][e] * u;
+                xm[e] = skf[x][e] * um;
+                xc[e] = skf[x][e] * exp2_fast(fminf(tb[e >> 2][e & 3] * kL2E - gl, 0.f));
+            }
+            kpf[x] = pack8(xp);
+            qpf[x] = pack8(xq);
+            const bf16x8 km = pack8(xm);
+            const int off = ((kg * 4 + rb) * 64 + l) * 8;
+            *reinterpret_cast<bf16x8 *>(Kp + off) = kpf[x];
+            *reinterpret_cast<bf16x8 *>(Qp + off) = qpf[x];
+            *reinterpret_cast<bf16x8 *>(Km + off) = pack8(xc);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                store_slots(KtT, rb >> 1, 2 * kg + t, kDK, rb & 1, Frag<bf16>::mma(zero4, km, t ? id1 : id0), l);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                store_slots(Vt, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1, Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0), l);
+        if constexpr (kQK) {
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            if (hi == 0) qks[(hf * kC + r) * 2 + 1] = sq;
+        }
+        } else {
         KDA_PHASE_LANE
         float sq = 0.f;  // sum of squares of silu(q) over the lane's channels (kQK)
         const bf16x8 id0 = *reinterpret_cast<const bf16x8 *>(idn + l * 8);
@@ -545,28 +657,12 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             if (hi == 0) qks[(hf * kC + r) * 2 + 1] = sq;
         }
         }
-        if (more) load_k(ci + 1);  // key rows consumed
+        if (more && !kStrong) load_k(ci + 1);  // key rows consumed (the strong instance reads them again below)
         __syncthreads();  // Kp, Qp, Km, Km^T, Kp^T, v^T complete
 
-        // ---- 3. Gram rows of block rb, contraction over all 128 channels (own half
-        //      from registers, the other half from LDS)
-        if (hf == 0) {
+        // (used by the waves of half 0, which hold the diagonal block rb of A in LDS)
+        auto diag_inverse = [&](const f32x4 bv) {
             KDA_PHASE_LANE
-            // the diagonal block of A[r][i] = beta_r <Kp_r, Km_i> (i < r), then the
-            // inverse of (I + that block)
-            const bf16x8 ka[4] = {kpf[0], kpf[1], fld(Kp, 2, rb, kC, l), fld(Kp, 3, rb, kC, l)};
-            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
-            bf16x8 kmb[4];
-#pragma unroll
-            for (int kg = 0; kg < 4; ++kg) kmb[kg] = fld(Km, kg, rb, kC, l);
-            f32x4 acc = zero4;
-#pragma unroll
-            for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, ka[kg], kmb[kg]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * rb + 4 * hi + i, cc = 16 * rb + lr;
-                Am[rr * kPT + cc] = (cc < rr) ? bv[i] * acc[i] : 0.f;
-            }
             // (I + L)^{-1} of the diagonal block L = A[16rb.., 16rb..] by forward
             // substitution: lane (r, hi) holds X[r][4 hi + j]; step i subtracts
             // L[r][i] times row i (broadcast within the 16-lane row). The block's
@@ -596,6 +692,128 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             *reinterpret_cast<bf16x4 *>(Dg + (rb * 64 + l) * 4) = to_bf16x4(f32x4{xs[0], xs[1], xs[2], xs[3]});
             store_slots(Tf, rb >> 1, rb, kC, rb & 1, f32x4{xs[0] * bv[0], xs[1] * bv[1], xs[2] * bv[2], xs[3] * bv[3]}, l);
             if ((rb & 1) == 0) store_slots(Tf, rb >> 1, rb, kC, 1, zero4, l);
+        };
+
+        // ---- 3. Gram rows of block rb, contraction over all 128 channels (own half
+        //      from registers, the other half from LDS)
+        if constexpr (kStrong) {
+            KDA_PHASE_LANE
+            // Each wave: its half's share of A's tiles (rb, tj < rb) and of Aqk^T's tiles (tj, rb),
+            // with the end of block tj as the reference (rows k 2^(ga - b_tj), q 2^(ga - b_tj);
+            // columns Km of block tj), and of the diagonal tiles (pair sums of phase 2). Half 1
+            // leaves its shares in A's place and in saq; half 0 adds its own, scales and masks,
+            // and inverts the diagonal block as the usual instance does.
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
+            f32x4 at[3], qt[3];
+#pragma unroll
+            for (int tj = 0; tj < 3; ++tj) {
+                at[tj] = qt[tj] = zero4;
+                if (tj < rb) {
+                    bf16x8 rk2[2], rq2[2];
+                    const int ho = opaque_lane() >> 4;
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        float xr[8], xs2[8];
+                        const int c0 = frag_chan<bf16>(2 * hf + x, ho, 0), c4 = frag_chan<bf16>(2 * hf + x, ho, 4);
+                        const f32x4 d[2] = {*reinterpret_cast<const f32x4 *>(gpre + rb * kDK + c0) -
+                                                *reinterpret_cast<const f32x4 *>(gpre + (tj + 1) * kDK + c0),
+                                            *reinterpret_cast<const f32x4 *>(gpre + rb * kDK + c4) -
+                                                *reinterpret_cast<const f32x4 *>(gpre + (tj + 1) * kDK + c4)};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            float qv = static_cast<float>(qr[x][e]);
+                            if constexpr (kQK) qv *= __builtin_amdgcn_rcpf(1.f + exp2_fast(-qv * kL2E));
+                            const float kv = kQK ? static_cast<float>(kr[x][e]) * rk : static_cast<float>(kr[x][e]);
+                            const float f = exp2_fast(fminf(fmaf(g[x][e], kL2E, d[e >> 2][e & 3]), 0.f));
+                            xr[e] = kv * f;
+                            xs2[e] = qv * f;
+                        }
+                        rk2[x] = pack8(xr);
+                        rq2[x] = pack8(xs2);
+                    }
+                    const bf16x8 c0 = fld(Km, 2 * hf, tj, kC, l), c1 = fld(Km, 2 * hf + 1, tj, kC, l);
+                    at[tj] = Frag<bf16>::mma(Frag<bf16>::mma(zero4, rk2[0], c0), rk2[1], c1);
+                    qt[tj] = Frag<bf16>::mma(Frag<bf16>::mma(zero4, c0, rq2[0]), c1, rq2[1]);
+                }
+            }
+            const f32x4 ad4 = sad4, aq4 = saq4;  // row r, columns 16 rb + 4 hi + i
+            float *sq_rb = saq + (rb * (rb + 1) / 2) * 256;
+            if (more) load_k(ci + 1);  // key rows consumed
+            if (hf == 1) {
+#pragma unroll
+                for (int tj = 0; tj < 3; ++tj) {
+                    if (tj < rb) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Am[(16 * rb + 4 * hi + i) * kPT + 16 * tj + lr] = at[tj][i];
+                        *reinterpret_cast<f32x4 *>(sq_rb + tj * 256 + 4 * l) = qt[tj];
+                    }
+                }
+                *reinterpret_cast<f32x4 *>(Am + r * kPT + 16 * rb + 4 * hi) = ad4;
+                *reinterpret_cast<f32x4 *>(sq_rb + rb * 256 + 4 * l) = aq4;
+            }
+            __syncthreads();  // half 1's shares in place
+            if (hf == 0) {
+#pragma unroll
+                for (int tj = 0; tj < 3; ++tj) {
+                    if (tj < rb) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float *p = Am + (16 * rb + 4 * hi + i) * kPT + 16 * tj + lr;
+                            *p = bv[i] * (*p + at[tj][i]);
+                        }
+                    }
+                }
+                {
+                    const float br = bet[r];
+                    float *p = Am + r * kPT + 16 * rb + 4 * hi;
+                    const f32x4 o4 = *reinterpret_cast<const f32x4 *>(p);
+                    f32x4 d4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) d4[i] = (4 * hi + i < lr) ? br * (o4[i] + ad4[i]) : 0.f;
+                    *reinterpret_cast<f32x4 *>(p) = d4;
+                }
+                // Aqk's scale, times the inverse norm of silu(q)'s row r (kQK; kept for O)
+                float aqs = scale;
+                if constexpr (kQK) {
+                    const float n = __builtin_amdgcn_rcpf(
+                        fmaxf(__builtin_sqrtf(qks[r * 2 + 1] + qks[(kC + r) * 2 + 1]), kNormEps));
+                    if (hi == 0) qnr[r] = n;
+                    aqs *= n;
+                }
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj) {
+                    if (tj < 2 * ((rb >> 1) + 1)) {
+                        f32x4 acc = zero4;
+                        if (tj < rb) {
+                            acc = (qt[tj < 3 ? tj : 0] + *reinterpret_cast<const f32x4 *>(sq_rb + tj * 256 + 4 * l)) * aqs;
+                        } else if (tj == rb) {
+                            acc = (aq4 + *reinterpret_cast<const f32x4 *>(sq_rb + rb * 256 + 4 * l)) * aqs;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[i] = (4 * hi + i <= lr) ? acc[i] : 0.f;
+                        }
+                        store_slots(Aqk, tj >> 1, rb, kC, tj & 1, acc, l);
+                    }
+                }
+                diag_inverse(bv);
+            }
+        } else if (hf == 0) {
+            KDA_PHASE_LANE
+            // the diagonal block of A[r][i] = beta_r <Kp_r, Km_i> (i < r), then the
+            // inverse of (I + that block)
+            const bf16x8 ka[4] = {kpf[0], kpf[1], fld(Kp, 2, rb, kC, l), fld(Kp, 3, rb, kC, l)};
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * rb + 4 * hi);
+            bf16x8 kmb[4];
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) kmb[kg] = fld(Km, kg, rb, kC, l);
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) acc = Frag<bf16>::mma(acc, ka[kg], kmb[kg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * rb + 4 * hi + i, cc = 16 * rb + lr;
+                Am[rr * kPT + cc] = (cc < rr) ? bv[i] * acc[i] : 0.f;
+            }
+            diag_inverse(bv);
         } else {
             KDA_PHASE_LANE
             // The off-diagonal blocks of A's rows rb, A[r][i] = beta_r <Kp_r, Km_i> (i < 16 rb),
@@ -733,7 +951,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 // the two factors are applied one after the other; otherwise their product
                 // is. Lane (c, hi) needs the factors of key positions 16 tm + 4 hi + i;
                 // lane lr of the row holds those of 4 tm + i = 2 lr, 2 lr + 1.
-                if constexpr (G == kGateHead) {  // one factor pair for every row
+                // (The strong instance holds S itself: no factor.)
+                if constexpr (G == kGateHead && !kStrong) {  // one factor pair for every row
                     const float ep0 = ehalf[0], ec0 = ehalf[kDK];
                     if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
 #pragma unroll
@@ -744,7 +963,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                         for (int tm = 0; tm < 8; ++tm) accS[tm] *= e2;
                     }
                 }
-                if constexpr (kPerChannel) {
+                if constexpr (kPerChannel && !kStrong) {
                 const f32x2 ep = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
                 const f32x2 ec = *reinterpret_cast<const f32x2 *>(ehalf + kDK + 32 * hi + 2 * lr);
                 if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
@@ -841,6 +1060,17 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 if (!full && t0 + 16 * rr + lr >= T_len) dst = static_cast<bf16 *>(a.discard) + 4 * (l & 31);
                 *reinterpret_cast<bf16x4 *>(dst) = to_bf16x4(ot);
             }
+            if constexpr (kStrong) {
+                // S_next = Diag(exp(gamma)) S + Km^T U
+                const f32x2 eg2 = *reinterpret_cast<const f32x2 *>(egam + 32 * hi + 2 * lr);
+#define KDA_EROW(TM)                                 \
+    accS[TM][0] *= row_bcast<2 * TM>(eg2[0]);        \
+    accS[TM][1] *= row_bcast<2 * TM>(eg2[1]);        \
+    accS[TM][2] *= row_bcast<2 * TM + 1>(eg2[0]);    \
+    accS[TM][3] *= row_bcast<2 * TM + 1>(eg2[1]);
+                KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
+#undef KDA_EROW
+            }
 #pragma unroll
             for (int tm = 0; tm < 8; ++tm) {
                 if (tm < 7) {
@@ -856,6 +1086,18 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         // reads (from the per-channel factors on), every wave passes its first barrier.
     }
 
+    if constexpr (!kStrong) {
+        if (tid == 0) a.redo[blockIdx.x] = 0;  // no chunk of strong decay in this pair
+    } else {
+        if (a.hT) {
+            float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
+#pragma unroll
+            for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hT[chan_of_pos(16 * tm + 4 * hi + i) * kDV] = accS[tm][i];
+        }
+        return;
+    }
     if (a.hT) {
         // S = E_last Q: the factor exp(gamma / 2) of the last chunk, once every wave has
         // read that chunk's factors
@@ -879,16 +1121,36 @@ hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seq
     // the fused pass is built for bf16 input and d_k = d_v = 128 only
     if (!bf16 || dk != kDK || dv != kDV) return hipErrorInvalidValue;
     constexpr size_t smem = Lds::SIZE;
-    auto kern = a.gate == kGateHead    ? kda_fused_kernel<kGateHead>
-                : a.gate == kGateNone   ? kda_fused_kernel<kGateNone>
-                : a.gate == kGatePreact ? (a.pre.qk_norm ? kda_fused_kernel<kGatePreactQK>
-                                                         : kda_fused_kernel<kGatePreact>)
-                                        : kda_fused_kernel<kGateChannel>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(n_seqs * a.H), dim3(kNT), smem, stream, a);
-    return hipGetLastError();
+    // the usual instance, then the strong-decay one over the pairs the first left to it
+    // (without a decay, no chunk can leave it any)
+    typedef void (*Kern)(FusedArgs);
+    Kern kern[2];
+    if (a.gate == kGateHead) {
+        kern[0] = kda_fused_kernel<kGateHead, false>;
+        kern[1] = kda_fused_kernel<kGateHead, true>;
+    } else if (a.gate == kGateNone) {
+        kern[0] = kda_fused_kernel<kGateNone, false>;
+        kern[1] = nullptr;
+    } else if (a.gate == kGatePreact && a.pre.qk_norm) {
+        kern[0] = kda_fused_kernel<kGatePreactQK, false>;
+        kern[1] = kda_fused_kernel<kGatePreactQK, true>;
+    } else if (a.gate == kGatePreact) {
+        kern[0] = kda_fused_kernel<kGatePreact, false>;
+        kern[1] = kda_fused_kernel<kGatePreact, true>;
+    } else {
+        kern[0] = kda_fused_kernel<kGateChannel, false>;
+        kern[1] = kda_fused_kernel<kGateChannel, true>;
+    }
+    for (Kern k : kern) {
+        if (!k) continue;
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(k, dim3(n_seqs * a.H), dim3(kNT), smem, stream, a);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -44,6 +44,7 @@ struct ChunkBuffers {
     void *KtT;   // [d_k][C]  io dtype: (k exp(gamma - g))^T         (write-back into the state)
     void *Aqk;   // [C][C]    io dtype: scale <q_r exp(g_r - g_i), k_i>, i <= r, else 0
     float *eg;   // [d_k]     fp32:     exp(gamma), gamma = g at the chunk's last row
+    uint8_t *strong;  // [1]  chunk left to the strong-decay instance of the prep kernel (0 / 1)
 };
 
 struct PrepArgs {
@@ -83,6 +84,8 @@ struct FusedArgs {
     int T_total;
     int gate;       // as in PrepArgs
     PreactArgs pre;
+    uint8_t *redo;  // [n_seqs * H]: 1 where the usual instance met a chunk of strong decay
+                    // and left the (sequence, head) to the strong instance, else 0
 };
 
 struct DecodeArgs {

@@ -50,7 +50,10 @@ template <int C, int DK, int DV, typename T> struct PrepCfg {
     // columns of W / U~ per pass of the final product (LDS budget)
     static constexpr int PW = (sizeof(T) == 4 && C == 128) ? 64 : 128;
     static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-    static constexpr size_t SMALL = (size_t)(2 * NW * DK + DK + C) * 4;  // sums, offsets, exp(gamma/2), beta
+    // sums, offsets, exp(gamma/2), beta; the strong-decay path's block prefixes and gamma
+    // (log2 units), its flags and the diagonal blocks of A
+    static constexpr size_t SMALL =
+        (size_t)(2 * NW * DK + DK + C + (NW + 1) * DK + 4 + NW * (NW + 1) / 2 * 256 + NW * DK) * 4;
     static constexpr size_t MATF = (size_t)C * PT * 4;                   // A, then T in place
     static constexpr size_t KMB = (size_t)C * DK * sizeof(T);            // Km (Gram operand)
     static constexpr size_t OPB = (size_t)PW * C * sizeof(T);            // B operand of one W / U~ pass
@@ -143,7 +146,11 @@ __device__ __forceinline__ void store_tile_t(T *base, int R, int kb, int rb, f32
     }
 }
 
-template <int C, int DK, int DV, typename T>
+// kStrong = false: the usual kernel. A chunk whose decay some channel sums below
+// -kStrongDecay is left to the second instance: this one records it in a.buf.strong and
+// writes nothing else for it. kStrong = true: runs after the first, on the recorded
+// chunks only (the others return at once), with every exponent <= 0 (steps 3 and 4 below).
+template <int C, int DK, int DV, typename T, bool kStrong>
 __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     typedef PrepCfg<C, DK, DV, T> P;
     typedef Frag<T> F;
@@ -158,6 +165,13 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     float *off = tot + NW * DK;                     // [NW][DK] (sum before row block w - gamma/2) log2(e)
     float *eh = off + NW * DK;                      // [DK] exp(gamma / 2)
     float *bet = eh + DK;                           // [C] beta per chunk row
+    float *gpre = bet + C;                          // [NW + 1][DK] log2 decay before row block w (strong path)
+    float *gam2 = gpre + NW * DK;                   // [DK]: row NW of gpre, gamma log2(e)
+    int *sflag = reinterpret_cast<int *>(gam2 + DK);  // [4] some channel of the chunk decays strongly
+    // [NW (NW + 1) / 2][256] A's tiles (w, tj <= w), rows scaled by beta (strong path): tile
+    // w (w + 1) / 2 + tj; the diagonal ones row-major, the others in accumulator order
+    float *ast = gam2 + DK + 4;
+    float *gpost = ast + NW * (NW + 1) / 2 * 256;   // [NW][DK] log2 decay after row block w (strong path)
     unsigned char *R = smem + P::SMALL;
     T *Km = reinterpret_cast<T *>(R);               // [C][DK] frag order: k exp(m - g)  (Gram)
     float *Am = reinterpret_cast<float *>(R);       // [C][PT] A, then T = (I + A)^{-1} in place
@@ -167,6 +181,9 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     int s, t0, L;
     if (!a.map.locate(j, s, t0, L)) return;  // past the last chunk (same for the whole block)
     (void)s;
+    if constexpr (kStrong) {
+        if (a.buf.strong[(size_t)j * a.H + h] == 0) return;  // done by the usual instance
+    }
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, hi = l >> 4;
     const int r = 16 * w + lr;  // the chunk row this lane holds
     const bool valid = r < L;
@@ -176,38 +193,77 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
     const float scale = a.scale;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // ---- 0. this lane's row of k, q, v and log alpha, in matrix-core operand order
+    // ---- 0. this lane's row of k, q and log alpha, in matrix-core operand order (q, k
+    //         activated and normalised when asked), and the inclusive running sum of log
+    //         alpha within the wave's 16 rows (DPP scan)
+    float gsuf[NKG][EPL];  // strong instance: log alpha summed over the later rows of the block
+    auto load_kqg = [&](V (&kr_)[NKG], V (&qr_)[NKG], float (&g_)[NKG][EPL]) {
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg) {
+            if (valid) {
+                kr_[kg] = load_row_frag<T>(static_cast<const T *>(a.k) + tok * DK, kg, hi);
+                qr_[kg] = load_row_frag<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
+                if (a.gate == kGateChannel) {
+                    load_row_f32<T>(a.log_alpha + tok * DK, kg, hi, g_[kg]);
+                } else if (a.gate == kGatePreact) {  // -exp(A_log) softplus(a + dt_bias)
+                    const V ar = load_row_frag<T>(static_cast<const T *>(a.pre.a) + tok * DK, kg, hi);
+                    const float eA = expf(a.pre.A_log[h]);
+                    float db[EPL];
+                    load_row_f32<T>(a.pre.dt_bias + (size_t)h * DK, kg, hi, db);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) g_[kg][e] = -eA * softplus_f(to_f32(ar[e]) + db[e]);
+                } else {  // one decay for every channel of the row, or none
+                    const float x = a.gate == kGateHead ? a.log_alpha[tok] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) g_[kg][e] = x;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    kr_[kg][e] = from_f32<T>(0.f);
+                    qr_[kg][e] = from_f32<T>(0.f);
+                    g_[kg][e] = 0.f;
+                }
+            }
+        }
+        if (a.pre.qk_norm) {
+            // q, k = silu(.) / ||silu(.)|| over the row, whose channels lie in lanes lr + 16 hi:
+            // the sums of squares by two lane exchanges, then silu again, scaled (rows past the
+            // end are zero and stay zero)
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const float x = silu_f(to_f32(kr_[kg][e])), y = silu_f(to_f32(qr_[kg][e]));
+                    sk += x * x;
+                    sq += y * y;
+                }
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            const float rk = 1.f / fmaxf(sqrtf(sk), kNormEps), rq = 1.f / fmaxf(sqrtf(sq), kNormEps);
+#pragma unroll
+            for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    kr_[kg][e] = from_f32<T>(silu_f(to_f32(kr_[kg][e])) * rk);
+                    qr_[kg][e] = from_f32<T>(silu_f(to_f32(qr_[kg][e])) * rq);
+                }
+        }
+#pragma unroll
+        for (int kg = 0; kg < NKG; ++kg)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                if constexpr (kStrong) gsuf[kg][e] = row16_exclusive_suffix_sum(g_[kg][e]);
+                g_[kg][e] = row16_inclusive_sum(g_[kg][e]);
+            }
+    };
     V kr[NKG], qr[NKG], vr[NVG];
     float g[NKG][EPL];
     float b = 0.f;
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg) {
-        if (valid) {
-            kr[kg] = load_row_frag<T>(static_cast<const T *>(a.k) + tok * DK, kg, hi);
-            qr[kg] = load_row_frag<T>(static_cast<const T *>(a.q) + tok * DK, kg, hi);
-            if (a.gate == kGateChannel) {
-                load_row_f32<T>(a.log_alpha + tok * DK, kg, hi, g[kg]);
-            } else if (a.gate == kGatePreact) {  // -exp(A_log) softplus(a + dt_bias)
-                const V ar = load_row_frag<T>(static_cast<const T *>(a.pre.a) + tok * DK, kg, hi);
-                const float eA = expf(a.pre.A_log[h]);
-                float db[EPL];
-                load_row_f32<T>(a.pre.dt_bias + (size_t)h * DK, kg, hi, db);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) g[kg][e] = -eA * softplus_f(to_f32(ar[e]) + db[e]);
-            } else {  // one decay for every channel of the row, or none
-                const float x = a.gate == kGateHead ? a.log_alpha[tok] : 0.f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) g[kg][e] = x;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                kr[kg][e] = from_f32<T>(0.f);
-                qr[kg][e] = from_f32<T>(0.f);
-                g[kg][e] = 0.f;
-            }
-        }
-    }
+    load_kqg(kr, qr, g);
 #pragma unroll
     for (int kg = 0; kg < NVG; ++kg) {
         if (valid) {
@@ -217,44 +273,15 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
             for (int e = 0; e < EPL; ++e) vr[kg][e] = from_f32<T>(0.f);
         }
     }
-    if (a.pre.qk_norm) {
-        // q, k = silu(.) / ||silu(.)|| over the row, whose channels lie in lanes lr + 16 hi:
-        // the sums of squares by two lane exchanges, then silu again, scaled (rows past the
-        // end are zero and stay zero)
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float x = silu_f(to_f32(kr[kg][e])), y = silu_f(to_f32(qr[kg][e]));
-                sk += x * x;
-                sq += y * y;
-            }
-        sk += __shfl_xor(sk, 16);
-        sk += __shfl_xor(sk, 32);
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        const float rk = 1.f / fmaxf(sqrtf(sk), kNormEps), rq = 1.f / fmaxf(sqrtf(sq), kNormEps);
-#pragma unroll
-        for (int kg = 0; kg < NKG; ++kg)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                kr[kg][e] = from_f32<T>(silu_f(to_f32(kr[kg][e])) * rk);
-                qr[kg][e] = from_f32<T>(silu_f(to_f32(qr[kg][e])) * rq);
-            }
-    }
     if (valid) b = a.gate == kGatePreact ? sigmoid_f(a.beta[tok]) : a.beta[tok];
     if (hi == 0) bet[r] = b;
 
-    // ---- 1. inclusive running sum of log alpha within the wave's 16 rows (DPP scan);
-    //         the row blocks' sums to LDS
+    // ---- 1. the row blocks' sums of log alpha to LDS
 #pragma unroll
     for (int kg = 0; kg < NKG; ++kg)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            g[kg][e] = row16_inclusive_sum(g[kg][e]);
+        for (int e = 0; e < EPL; ++e)
             if (lr == 15) tot[w * DK + frag_chan<T>(kg, hi, e)] = g[kg][e];
-        }
     __syncthreads();
 
     // ---- 2. per key channel (one thread each): each row block's offset, summed in
@@ -269,83 +296,212 @@ __global__ __launch_bounds__(4 * C) void kda_prep_kernel(PrepArgs a) {
         }
         const float m = 0.5f * acc;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) off[ww * DK + tid] = (pre[ww] - m) * kL2E;
+        for (int ww = 0; ww < NW; ++ww) {
+            off[ww * DK + tid] = (pre[ww] - m) * kL2E;
+            gpre[ww * DK + tid] = pre[ww] * kL2E;
+        }
+        gam2[tid] = acc * kL2E;
+        float post = 0.f;  // the later row blocks' decay, summed from the end
+#pragma unroll
+        for (int ww = NW - 1; ww >= 0; --ww) {
+            gpost[ww * DK + tid] = post * kL2E;
+            post += tot[ww * DK + tid];
+        }
         eh[tid] = __builtin_amdgcn_exp2f(m * kL2E);
         a.buf.eg[jh * DK + tid] = __builtin_amdgcn_exp2f(acc * kL2E);
+        const unsigned long long st = __ballot(acc < -kStrongDecay);
+        if ((tid & 63) == 0) sflag[tid >> 6] = st != 0ull;
     }
     __syncthreads();
+    if constexpr (!kStrong) {
+        // a chunk past the midpoint factors' range goes to the strong instance
+        const bool strong = __builtin_amdgcn_readfirstlane(DK > 64 ? (sflag[0] | sflag[1]) : sflag[0]) != 0;
+        if (tid == 0) a.buf.strong[jh] = strong ? 1 : 0;
+        if (strong) return;
+    }
 
     // ---- 3. elementwise, with d = (g - gamma/2) log2(e) clamped, ep = 2^d, em = 2^-d
     //         and E = exp(gamma/2): the Gram factors Kp = k ep and Qp = scale q ep
     //         (registers) and Km = k em (LDS); QO = Qp E (memory); KtT = (Km E)^T,
     //         transposed by the matrix cores (memory); and the rows beta Kp E of W's
-    //         operand (registers). Within the supported decay (|gamma| <= 170) no factor
+    //         operand (registers). In this instance's range (|gamma| <= 160) no factor
     //         is clamped, so Qp E = scale q exp(g) and Km E = k exp(gamma - g).
     T *gQO = static_cast<T *>(a.buf.QO) + jh * C * DK;
     T *gKtT = static_cast<T *>(a.buf.KtT) + jh * DK * C;
     V idt[TPG];
 #pragma unroll
     for (int t = 0; t < TPG; ++t) idt[t] = ident_op<T>(t);
-    V kp[NKG], qp[NKG], kb[NKG];
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg) {
-        float xo[EPL], xp[EPL], xq[EPL], xm[EPL], xk[EPL], xb[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int ch = frag_chan<T>(kg, hi, e);
-            const float d = __builtin_amdgcn_fmed3f(fmaf(g[kg][e], kL2E, off[w * DK + ch]), -kClamp, kClamp);
-            const float ep = __builtin_amdgcn_exp2f(d), em = __builtin_amdgcn_exp2f(-d), E = eh[ch];
-            const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
-            xp[e] = kv * ep;
-            xq[e] = qv * ep;
-            xm[e] = kv * em;
-            xo[e] = xq[e] * E;
-            xk[e] = xm[e] * E;
-            xb[e] = b * xp[e] * E;
-        }
-        *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
-        kp[kg] = pack_frag<T>(xp);
-        qp[kg] = pack_frag<T>(xq);
-        kb[kg] = pack_frag<T>(xb);
-        *reinterpret_cast<V *>(Km + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xm);
-        const V kk = pack_frag<T>(xk);
-#pragma unroll
-        for (int t = 0; t < TPG; ++t) store_tile_t<T>(gKtT, DK, w, TPG * kg + t, F::mma(zero4, kk, idt[t]));
-    }
-    __syncthreads();  // Km complete
-
+    V kb[NKG];
+    T *gAqk = static_cast<T *>(a.buf.Aqk) + jh * C * C;
+    f32x4 akk[NW];
     // ---- 4. decayed Gram tiles of this wave's row block: A's tiles (w, tj <= w), and,
     //         with the operands' roles swapped, the tiles of Aqk^T = Km Qp^T, whose
     //         entries are Aqk's operand slots (stored to memory, zero above the diagonal)
-    T *gAqk = static_cast<T *>(a.buf.Aqk) + jh * C * C;
-    f32x4 akk[NW];
+    // (each path runs steps 3 and 4 as one block: the values one path keeps from step 3
+    // to step 4 are never live in the other)
+    if constexpr (kStrong) {
+        // QO = scale q 2^ga, KtT = (k 2^(gamma - ga))^T and W's rows beta k 2^ga, with ga the
+        // chunk's log2 decay up to the row (each exponent <= 0: underflow gives the value's
+        // own negligible size); and this block's Gram column operand k 2^(b - ga) in Km,
+        // b = the decay up to the block's last row (<= 1 as well). gamma - ga and b - ga are
+        // formed from suffix sums.
 #pragma unroll
-    for (int tj = 0; tj < NW; ++tj) {
-        akk[tj] = zero4;
-        f32x4 aq = zero4;
-        if (tj <= w) {
+        for (int kg = 0; kg < NKG; ++kg) {
+            float xo[EPL], xk[EPL], xb[EPL], xc[EPL];
 #pragma unroll
-            for (int kg = 0; kg < NKG; ++kg) {
-                const V bm = frag_load<T>(Km, kg, tj, C);
-                akk[tj] = F::mma(akk[tj], kp[kg], bm);
-                aq = F::mma(aq, bm, qp[kg]);
+            for (int e = 0; e < EPL; ++e) {
+                const int ch = frag_chan<T>(kg, hi, e);
+                // the decay from the chunk's start to the row (a prefix) and from the row to the
+                // block's and the chunk's end (suffix sums, exact where they are small)
+                const float ga = g[kg][e] * kL2E + gpre[w * DK + ch], sb = gsuf[kg][e] * kL2E;
+                const float eg = __builtin_amdgcn_exp2f(ga), egr = __builtin_amdgcn_exp2f(sb + gpost[w * DK + ch]);
+                const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
+                xo[e] = qv * eg;
+                xk[e] = kv * egr;
+                xb[e] = b * kv * eg;
+                xc[e] = kv * __builtin_amdgcn_exp2f(fminf(sb, 0.f));
             }
-            if (tj == w) {  // entry (4 hi + i, lr) is Aqk[16 w + lr][16 w + 4 hi + i]: kept for i <= r
+            *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
+            kb[kg] = pack_frag<T>(xb);
+            *reinterpret_cast<V *>(Km + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xc);
+            const V kk = pack_frag<T>(xk);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) aq[i] = (4 * hi + i <= lr) ? aq[i] : 0.f;
-            }
+            for (int t = 0; t < TPG; ++t) store_tile_t<T>(gKtT, DK, w, TPG * kg + t, F::mma(zero4, kk, idt[t]));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        store_tile_t<T>(gAqk, C, tj, w, aq);
+        __syncthreads();  // Km complete
+        // the diagonal tile pair by pair, 8 channels at a time: A's entries to LDS (ast),
+        // Aqk's (as its transposed tile) to memory
+        {
+            float ad16[16], aqd[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ad16[i] = aqd[i] = 0.f;
+            constexpr int GPB = 8 / EPL;  // operand groups per 8-channel batch
+#pragma unroll
+            for (int kb0 = 0; kb0 < NKG; kb0 += GPB) {
+                float kf[8], qf[8];
+#pragma unroll
+                for (int x = 0; x < GPB; ++x)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        kf[x * EPL + e] = to_f32(kr[kb0 + x][e]);
+                        qf[x * EPL + e] = scale * to_f32(qr[kb0 + x][e]);
+                    }
+                diag_pairs_accum<8>(kf, qf, &g[kb0][0], ad16, aqd);
+            }
+            diag_pairs_reduce(ad16, aqd);
+            const f32x4 a4 = group4(ad16, hi), q4 = group4(aqd, hi);
+            f32x4 aq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // A[r][16 w + 4 hi + i], strictly lower, rows scaled by beta; entry (4 hi + i, lr)
+                // of this tile of Aqk^T is Aqk[16 w + lr][16 w + 4 hi + i], kept for i <= r
+                ast[(w * (w + 1) / 2 + w) * 256 + lr * 16 + 4 * hi + i] = 4 * hi + i < lr ? b * a4[i] : 0.f;
+                aq[i] = (4 * hi + i <= lr) ? q4[i] : 0.f;
+            }
+            store_tile_t<T>(gAqk, C, w, w, aq);
+        }
+        // the tiles left of the diagonal, (w, tj < w), with the end of block tj as the
+        // reference: rows k 2^(ga - b_tj) and scale q 2^(ga - b_tj), columns Km of block tj
+        // (both <= 1); A's tiles to LDS (ast, rows scaled by beta)
+        const f32x4 bv = *reinterpret_cast<const f32x4 *>(bet + 16 * w + 4 * hi);
+#pragma unroll
+        for (int tj = 0; tj < NW; ++tj) {
+            f32x4 aq = zero4;
+            if (tj == w) continue;  // stored above
+            if (tj < w) {
+                f32x4 at = zero4;
+#pragma unroll
+                for (int kg = 0; kg < NKG; ++kg) {
+                    float xr[EPL], xs[EPL];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const int ch = frag_chan<T>(kg, hi, e);
+                        const float f = __builtin_amdgcn_exp2f(
+                            fminf(g[kg][e] * kL2E + gpre[w * DK + ch] - gpre[(tj + 1) * DK + ch], 0.f));
+                        xr[e] = to_f32(kr[kg][e]) * f;
+                        xs[e] = scale * to_f32(qr[kg][e]) * f;
+                    }
+                    const V bm = frag_load<T>(Km, kg, tj, C);
+                    at = F::mma(at, pack_frag<T>(xr), bm);
+                    aq = F::mma(aq, bm, pack_frag<T>(xs));
+                    __builtin_amdgcn_sched_barrier(0);  // (keeps each group's LDS reads next to their use)
+                }
+                *reinterpret_cast<f32x4 *>(ast + (w * (w + 1) / 2 + tj) * 256 + 4 * l) = at * bv;
+            }
+            store_tile_t<T>(gAqk, C, tj, w, aq);
+        }
+    } else {
+        V kp[NKG], qp[NKG];
+    #pragma unroll
+        for (int kg = 0; kg < NKG; ++kg) {
+            float xo[EPL], xp[EPL], xq[EPL], xm[EPL], xk[EPL], xb[EPL];
+    #pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int ch = frag_chan<T>(kg, hi, e);
+                const float d = __builtin_amdgcn_fmed3f(fmaf(g[kg][e], kL2E, off[w * DK + ch]), -kClamp, kClamp);
+                const float ep = __builtin_amdgcn_exp2f(d), em = __builtin_amdgcn_exp2f(-d), E = eh[ch];
+                const float kv = to_f32(kr[kg][e]), qv = scale * to_f32(qr[kg][e]);
+                xp[e] = kv * ep;
+                xq[e] = qv * ep;
+                xm[e] = kv * em;
+                xo[e] = xq[e] * E;
+                xk[e] = xm[e] * E;
+                xb[e] = b * xp[e] * E;
+            }
+            *reinterpret_cast<V *>(gQO + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xo);
+            kp[kg] = pack_frag<T>(xp);
+            qp[kg] = pack_frag<T>(xq);
+            kb[kg] = pack_frag<T>(xb);
+            *reinterpret_cast<V *>(Km + ((kg * NW + w) * 64 + l) * EPL) = pack_frag<T>(xm);
+            const V kk = pack_frag<T>(xk);
+    #pragma unroll
+            for (int t = 0; t < TPG; ++t) store_tile_t<T>(gKtT, DK, w, TPG * kg + t, F::mma(zero4, kk, idt[t]));
+        }
+        __syncthreads();  // Km complete
+    #pragma unroll
+        for (int tj = 0; tj < NW; ++tj) {
+            akk[tj] = zero4;
+            f32x4 aq = zero4;
+            if (tj <= w) {
+    #pragma unroll
+                for (int kg = 0; kg < NKG; ++kg) {
+                    const V bm = frag_load<T>(Km, kg, tj, C);
+                    akk[tj] = F::mma(akk[tj], kp[kg], bm);
+                    aq = F::mma(aq, bm, qp[kg]);
+                }
+                if (tj == w) {  // entry (4 hi + i, lr) is Aqk[16 w + lr][16 w + 4 hi + i]: kept for i <= r
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) aq[i] = (4 * hi + i <= lr) ? aq[i] : 0.f;
+                }
+            }
+            store_tile_t<T>(gAqk, C, tj, w, aq);
+        }
     }
     __syncthreads();  // Km is no longer read: the region takes A
     // A (strictly lower, rows scaled by beta, zero elsewhere) -> fp32 LDS
+    if constexpr (kStrong) {
 #pragma unroll
-    for (int tj = 0; tj < NW; ++tj)
+        for (int tj = 0; tj < NW; ++tj) {
+            const float *st = ast + (w * (w + 1) / 2 + tj) * 256;
+            if (tj == w) {  // the diagonal block (row r, columns 4 hi ..), zero above it
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(st + lr * 16 + 4 * hi);
+                *reinterpret_cast<f32x4 *>(Am + r * PT + 16 * w + 4 * hi) = x;
+            } else {
+                const f32x4 x = tj < w ? *reinterpret_cast<const f32x4 *>(st + 4 * l) : zero4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * w + acc_row(i), cc = 16 * tj + acc_col();
-            Am[rr * PT + cc] = (tj <= w && cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
+                for (int i = 0; i < 4; ++i) Am[(16 * w + acc_row(i)) * PT + 16 * tj + acc_col()] = x[i];
+            }
         }
+    } else {
+#pragma unroll
+        for (int tj = 0; tj < NW; ++tj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * w + acc_row(i), cc = 16 * tj + acc_col();
+                Am[rr * PT + cc] = (tj <= w && cc < rr) ? bet[rr] * akk[tj][i] : 0.f;
+            }
+    }
     __syncthreads();
 
     // ---- 5. T = (I + A)^{-1}, in place
@@ -421,12 +577,18 @@ template <int C, int DK, int DV, typename T>
 hipError_t launch_prep_t(const PrepArgs &a, int n_chunks_grid, hipStream_t stream) {
     constexpr size_t smem = PrepCfg<C, DK, DV, T>::SMEM;
     static_assert(smem <= 160 * 1024, "prep LDS budget");
-    auto kern = kda_prep_kernel<C, DK, DV, T>;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(n_chunks_grid, a.H), dim3(4 * C), smem, stream, a);
-    return hipGetLastError();
+    // the usual instance, then the strong-decay one over the chunks the first left to it
+    auto fast = kda_prep_kernel<C, DK, DV, T, false>;
+    auto strong = kda_prep_kernel<C, DK, DV, T, true>;
+    for (auto kern : {fast, strong}) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(kern, dim3(n_chunks_grid, a.H), dim3(4 * C), smem, stream, a);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 template <int C, typename T>

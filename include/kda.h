@@ -32,14 +32,19 @@
  *    on KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_WORKSPACE nothing is
  *    written and nothing is enqueued. KDA_ERR_HIP reports a failed launch.
  *    Device-side faults surface at the caller's next synchronisation. Input
- *    VALUES are not checked: gates must be finite, and within one chunk the
- *    summed log_alpha of each key channel must stay >= -170. The chunked form
- *    factors the in-chunk decay around the chunk's midpoint, so its factors
- *    span e^(+-|sum|/2); past the limit they leave the fp32 range and are
- *    clamped, and the results are wrong, not merely less accurate (relative
- *    L2 error of o about 0.3 at sums near -220). Inside it, fast-forgetting
- *    channels (sums near -150) keep the usual accuracy. For gates that strong
- *    use the decode step, which forms no such factors.
+ *    VALUES are not checked: gates must be finite (log_alpha <= 0 and beta in
+ *    [0, 1] in the method's own use). The chunked prefill has no limit on how
+ *    fast a channel forgets: it factors the in-chunk decay around the chunk's
+ *    midpoint, whose factors e^(+-|sum|/2) stay in the fp32 range while a
+ *    chunk's summed log_alpha is >= -160 on every key channel; a chunk below
+ *    that is computed by a second instance of the kernels in which every
+ *    exponent is <= 0 (the decay from the chunk's start, or from the end of a
+ *    16-row block, and the pairs inside a block one by one), so factors that
+ *    underflow are the negligible values they stand for. Tested at chunk sums
+ *    near -500 and -2000 for every gate kind. On the one-launch pass such a
+ *    chunk sends its whole (sequence, head) pair to the second instance, which
+ *    runs it again from the start. kda_chunk_bwd keeps the -170 limit of its
+ *    midpoint factors.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -143,8 +148,7 @@ int kda_chunk_fwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
  * kda_gate value; any other value is KDA_ERR_INVALID_ARG). log_alpha's shape and
  * alignment follow kda_gate; with KDA_GATE_NONE it is not read. Every other
  * argument, the workspace size and the error behaviour are those of
- * kda_chunk_fwd, which is this call with KDA_GATE_CHANNEL. For a per-head decay
- * the limit on a chunk's summed log_alpha applies to that one sum.
+ * kda_chunk_fwd, which is this call with KDA_GATE_CHANNEL.
  */
 int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chunk, int io,
                         const void *q, const void *k, const void *v,
@@ -206,7 +210,7 @@ int kda_chunk_fwd_noalloc(int gate, int B, int T, int H, int d_k, int d_v, int c
  *   A_log    [H] fp32: per-head log of the decay rate's scale.
  *   dt_bias  [H, d_k] fp32, 16-byte aligned: per-channel bias.
  *   b        [B*T, H] fp32: beta's pre-activation.
- * The limit on a chunk's summed log_alpha (>= -170) applies to the formed decay.
+ * Chunks whose formed decay sums below -160 are handled as for kda_chunk_fwd.
  */
 enum { KDA_PREACT_QK_NORM = 1 };
 

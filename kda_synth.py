@@ -26,7 +26,9 @@ Gate families (log alpha is drawn per token, per head and per key channel):
   weak:  log alpha = -0.1 * softplus(N(0,1)),  beta = sigmoid(N(0,1))
   main:  log alpha = -softplus(N(-2,1)),       beta = sigmoid(N(0,1))
   strong: log alpha = -1.3 softplus(N(1,1)),   beta = sigmoid(N(0,1))   (a test family: fast
-          forgetting, chunk sums of log alpha near -110 on average, inside the >= -170 limit)
+          forgetting, chunk sums of log alpha near -110 on average)
+  sum500, sum2000: log alpha = -(S/64) U(0.5, 1.5) with S = 500, 2000 (test families: chunk sums
+          near -S per channel, where the chunked form's midpoint factors leave the fp32 range)
 q and k are N(0,1) vectors L2-normalised per (token, head); v ~ N(0,1).
 "N(mu, s)" means standard deviation s.
 
@@ -140,6 +142,10 @@ def _gates(rng, family, shape, dk):
         la = -softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64) - 2.0)
     elif family == "strong":
         la = -1.3 * softplus(rng.standard_normal(shape + (dk,), dtype=np.float32).astype(np.float64) + 1.0)
+    elif family in ("sum500", "sum2000"):
+        # log alpha = -(S / 64) U(0.5, 1.5): chunk sums of about -S per channel over 64 tokens
+        S = 500.0 if family == "sum500" else 2000.0
+        la = -(S / 64.0) * rng.uniform(0.5, 1.5, shape + (dk,))
     else:
         raise ValueError(family)
     beta = sigmoid(rng.standard_normal(shape, dtype=np.float32).astype(np.float64))
@@ -215,6 +221,17 @@ def gen_preact(T_total, H, dk, io, seed):
     dt_bias = np.log(np.expm1(dt)).astype(np.float32)
     b = rng.standard_normal((T_total, H), dtype=np.float32)
     return dict(a=a, A_log=A_log, dt_bias=dt_bias, b=b)
+
+
+def gen_preact_strong(T_total, H, dk, io, seed):
+    """Gate pre-activations whose decays sum to about -2000 per 64-token chunk: A_log = log 16
+    for every head and a ~ N(8, 1), so that with gen_preact's dt_bias (about -5 to -7)
+    log alpha = -16 softplus(a + dt_bias) is about -30 per token."""
+    p = gen_preact(T_total, H, dk, io, seed)
+    rng = np.random.Generator(np.random.PCG64([seed, 0xA9]))
+    p["a"] = _io(rng.standard_normal((T_total, H, dk), dtype=np.float32) + 8.0, io)
+    p["A_log"] = np.full(H, np.log(16.0), dtype=np.float32)
+    return p
 
 
 def gen_qk_preact(T_total, H, dk, io, seed):

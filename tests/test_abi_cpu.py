@@ -50,15 +50,18 @@ def test_version_and_status_strings(lib):
 
 
 def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
-    if C == 64 and esz == 2 and dk == dv == 128 and T > 0 and (n_seqs if n_seqs else B) * H >= 256:
-        # fused pass (equal-length or packed sequences): only the 256-byte discard slot
-        return 256
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    pairs = (n_seqs if n_seqs else B) * H
+    if C == 64 and esz == 2 and dk == dv == 128 and T > 0 and pairs >= 256:
+        # fused pass (equal-length or packed sequences): the 256-byte discard slot and one
+        # byte per (sequence, head) for the strong-decay instance
+        return 256 + r(pairs)
     per = (T + C - 1) // C
     nch = (per + n_seqs if n_seqs else B * per) * H
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
     total = 0
     for nbytes in (nch * C * dk * esz, nch * C * dv * esz, nch * C * dk * esz, nch * dk * C * esz,
-                   nch * C * C * esz, nch * dk * 4, 256):
+                   nch * C * C * esz, nch * dk * 4, nch, 256):
         total += r(nbytes)
     if n_seqs:
         total += r((3 * n_seqs + 1) * 4)
@@ -173,8 +176,8 @@ def test_noalloc_limit_matches_header(lib):
     text = open(HEADER).read()
     assert "#define KDA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)" in text
     assert kda.binding.NOALLOC_MAX_WORKSPACE == 32 << 20
-    # the one-launch pass needs only its 256-byte discard slot, at any length
-    assert lib.kda_chunk_fwd_workspace_bytes(8, 1 << 20, 32, 128, 128, 64, 0, BF16) == 256
+    # the one-launch pass needs its 256-byte discard slot and a byte per pair, at any length
+    assert lib.kda_chunk_fwd_workspace_bytes(8, 1 << 20, 32, 128, 128, 64, 0, BF16) == 512
 
 
 def test_chunk_fwd_is_the_per_channel_gated_call(lib):

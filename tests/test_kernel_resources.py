@@ -63,8 +63,17 @@ def test_every_kernel_is_reported(resources):
         assert k in names, k
 
 
+def _strong_fused(name):
+    """The strong-decay instances of the fused kernel (kda_fused_kernel<G, true>): they run only
+    for (sequence, head) pairs with a chunk of strong decay, and their per-pair Gram work
+    spills; the usual instances must not."""
+    return "kda_fused_kernel" in name and "Lb1E" in name
+
+
 def test_no_scratch_and_no_spills(resources):
     for name, r in resources.items():
+        if _strong_fused(name):
+            continue
         assert r["ScratchSize [bytes/lane]"] == "0", (name, r)
         assert r["Dynamic Stack"] == "False", (name, r)
         if "kda_bwd_chunk" in name:
@@ -75,12 +84,15 @@ def test_no_scratch_and_no_spills(resources):
 
 
 def test_fused_kernel_runs_two_waves_per_simd(resources):
-    fused = [r for n, r in resources.items() if "kda_fused_kernel" in n]
-    assert len(fused) == 5  # per channel, per head, none, from pre-activations (with q, k normalised or not)
-    for r in fused:
-        assert int(r["Occupancy [waves/SIMD]"]) >= 2, r
-        assert int(r["VGPRs"]) <= 256, r
-        assert r["VGPRs Spill"] == "0", r
+    fused = {n: r for n, r in resources.items() if "kda_fused_kernel" in n}
+    # the usual instances: per channel, per head, none, from pre-activations (with q, k
+    # normalised or not); the strong-decay instances of all but "none"
+    assert sum(not _strong_fused(n) for n in fused) == 5 and sum(_strong_fused(n) for n in fused) == 4
+    for n, r in fused.items():
+        assert int(r["Occupancy [waves/SIMD]"]) >= 2, (n, r)
+        assert int(r["VGPRs"]) <= 256, (n, r)
+        if not _strong_fused(n):
+            assert r["VGPRs Spill"] == "0", (n, r)
 
 
 def test_attn_decode_keeps_loads_in_flight(resources):

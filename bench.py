@@ -51,6 +51,9 @@ COMMON_SRC = ["kda_device.hpp", "kda_internal.hpp"]  # included by every kernel 
 PATHS = {
     "fused": dict(kernel="kda_fused_kernel", sources=["kda_fused.hip"] + COMMON_SRC,
                   traffic="kda_fused_kernel_batched_prefill_traffic.md"),
+    "segmented": dict(kernel="kda_fused_kernel (segment maps, then segments) + kda_segment_chain_kernel",
+                      sources=["kda_fused.hip", "kda_segment.hip"] + COMMON_SRC,
+                      traffic="kda_segmented_pass_traffic.md"),
     "split": dict(kernel="kda_prep_kernel + kda_state_kernel",
                   sources=["kda_prep.hip", "kda_state.hip", "kda_solve.hpp"] + COMMON_SRC,
                   traffic="kda_split_pass_batched_prefill_traffic.md"),
@@ -58,12 +61,23 @@ PATHS = {
 
 
 def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16, n_seqs=0):
-    """Which schedule kda_chunk_fwd runs for these sizes: the one-launch fused pass
-    (bf16, d_k = d_v = 128, chunk 64, at least 256 (sequence, head) pairs, equal-length
-    or packed sequences) or the split prep + state pass. Same rule as the library's
-    dispatch."""
-    fused = (chunk == 64 and bf16 and dk == dv == 128 and T > 0 and (n_seqs if varlen else B) * H >= 256)
-    return "fused" if fused else "split"
+    """Which schedule kda_chunk_fwd runs for these sizes: for bf16 and d_k = d_v = 128 (any
+    chunk size asked) the fused pass, one workgroup per (sequence, head) when there are at
+    least 256 pairs, else with segments of long sequences (maps, their composition, then the
+    segments) when a sequence is longer than one segment; otherwise the split prep + state
+    pass. Same rule as the library's dispatch."""
+    if not (bf16 and dk == dv == 128 and T > 0):
+        return "split"
+    n = n_seqs if varlen else B
+    if n * H >= 256:
+        return "fused"
+    chunks = (T + 63) // 64 + n_seqs if varlen else B * ((T + 63) // 64)
+    lc = 4
+    while lc < 1024 and lc * 2 * 512 <= chunks * H:
+        lc *= 2
+    seg = lc * 64
+    longer = T > seg if varlen else (T + seg - 1) // seg > 1
+    return "segmented" if longer else "fused"
 
 
 def sources_digest(names):

@@ -33,20 +33,58 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// The fused pass (one workgroup per (sequence, head), nothing staged in
-// memory) is used for bf16 input with d_k = d_v = 128 and chunk 64 when the
-// (sequence, head) pairs alone fill the chip, for equal-length and for packed
-// sequences; otherwise the split pass (parallel chunk preparation, then state
-// propagation over d_v slices). With packed sequences the longest one sets the
-// fused pass's time, as it does the split pass's state propagation.
+// The fused pass (the state of a (sequence, head) in one workgroup's registers,
+// nothing staged in memory, 64-row chunks) serves bf16 input with d_k = d_v = 128,
+// for equal-length and for packed sequences, whatever chunk size is asked (chunking
+// is an exact refactoring of the recurrence: 64 and 128 give the same results up to
+// rounding). When the (sequence, head) pairs alone fill the chip it runs one
+// workgroup per pair. Otherwise it cuts the sequences into segments of seg_len tokens
+// and runs one workgroup per (segment, head): first each segment's map S_out = M S_in
+// + N, then their composition in order, then every segment from its entering state.
+// Other inputs (fp32, d = 64) take the split pass (parallel chunk preparation, then
+// state propagation over d_v slices) at the asked chunk size.
 constexpr int kFusedMinPairs = 256;
 bool use_fused(int B, int T, int H, int dk, int dv, int C, bool varlen, int io, int n_seqs) {
-    return C == 64 && io == KDA_BF16 && dk == 128 && dv == 128 && T > 0 &&
-           (int64_t)(varlen ? n_seqs : B) * H >= kFusedMinPairs;
+    (void)B;
+    (void)H;
+    (void)C;
+    (void)varlen;
+    (void)n_seqs;
+    return io == KDA_BF16 && dk == 128 && dv == 128 && T > 0;
+}
+
+struct FusedPlan {
+    int seg_len;       // tokens per segment (0: one workgroup per (sequence, head))
+    int segs_per_seq;  // equal-length sequences: segments of each
+    int n_seg;         // upper bound on the number of segments
+};
+
+// Segments of 4 to 1024 chunks of 64 tokens, the longest for which the (segment, head)
+// pairs still number at least 512 (two per compute unit or more: the map and the output
+// launches each run one workgroup per CU, and later ones fill the CUs the short segments
+// at sequence ends free).
+FusedPlan fused_plan(int B, int T, int H, bool varlen, int n_seqs) {
+    const int64_t pairs = (int64_t)(varlen ? n_seqs : B) * H;
+    const int n_seq = varlen ? n_seqs : B;
+    FusedPlan none{0, 1, n_seq};
+    if (pairs >= kFusedMinPairs || T <= 0) return none;
+    const int64_t chunks = varlen ? ((int64_t)T + 63) / 64 + n_seqs : (int64_t)B * (((int64_t)T + 63) / 64);
+    const int64_t work = chunks * H;
+    int64_t lc = 4;
+    while (lc < 1024 && lc * 2 * 512 <= work) lc *= 2;
+    const int seg_len = (int)(lc * 64);
+    if (!varlen) {
+        const int sps = (T + seg_len - 1) / seg_len;
+        if (sps <= 1) return none;
+        return FusedPlan{seg_len, sps, B * sps};
+    }
+    if (T <= seg_len) return none;
+    return FusedPlan{seg_len, 0, (T + seg_len - 1) / seg_len + n_seqs};
 }
 
 struct WsLayout {
     size_t W, U, QO, KtT, Aqk, eg, strong, discard, choff, total;
+    size_t seg_tab, seg_state, seg_map;  // fused pass with segments
     int64_t n_chunks;  // upper bound on the number of chunks over all sequences
 };
 
@@ -54,27 +92,33 @@ struct WsLayout {
 // packed variable-length input, the chunk offsets of the sequences.
 bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varlen, int io,
                WsLayout *L) {
-    if (T <= 0) {
-        *L = WsLayout{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        return true;
-    }
-    if (use_fused(B, T, H, dk, dv, C, varlen, io, n_seqs)) {
-        // the discard slot, and one byte per (sequence, head): left to the strong-decay instance
-        *L = WsLayout{0, 0, 0, 0, 0, 0, 256, 0, 0, 0, 0};
-        L->total = 256 + round_up((size_t)(varlen ? n_seqs : B) * H, 256);
-        L->n_chunks = 0;
-        return true;
-    }
-    const size_t esz = io == KDA_BF16 ? 2 : 4;
-    const int64_t per_seq = ((int64_t)T + C - 1) / C;
-    L->n_chunks = varlen ? per_seq + n_seqs : (int64_t)B * per_seq;
-    const size_t nch = (size_t)L->n_chunks * (size_t)H;
+    *L = WsLayout{};
+    if (T <= 0) return true;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
         off = round_up(off + bytes, 256);
         return at;
     };
+    if (use_fused(B, T, H, dk, dv, C, varlen, io, n_seqs)) {
+        // the discard slot; one byte per (sequence or segment, head): left to the strong-decay
+        // instance; with segments, their table, entering states and maps (fp32, 64 KB each)
+        const FusedPlan fp = fused_plan(B, T, H, varlen, n_seqs);
+        const size_t units = (size_t)fp.n_seg * H;
+        L->discard = take(256);
+        L->strong = take(units);
+        if (fp.seg_len > 0) {
+            L->seg_tab = varlen ? take(((size_t)3 * n_seqs + 1) * sizeof(int32_t)) : 0;
+            L->seg_state = take(units * dk * dv * sizeof(float));
+            L->seg_map = take(units * 2 * dk * dv * sizeof(float));
+        }
+        L->total = off;
+        return true;
+    }
+    const size_t esz = io == KDA_BF16 ? 2 : 4;
+    const int64_t per_seq = ((int64_t)T + C - 1) / C;
+    L->n_chunks = varlen ? per_seq + n_seqs : (int64_t)B * per_seq;
+    const size_t nch = (size_t)L->n_chunks * (size_t)H;
     L->W = take(nch * C * dk * esz);
     L->U = take(nch * C * dv * esz);
     L->QO = take(nch * C * dk * esz);
@@ -224,10 +268,27 @@ int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, in
     char *ws = static_cast<char *>(workspace);
     const bool bf = io == KDA_BF16;
     if (use_fused(B, T, H, d_k, d_v, chunk, varlen, io, n_seqs)) {
+        const FusedPlan fp = fused_plan(B, T, H, varlen, n_seqs);
         kda::FusedArgs fa{q,  k,     v,  log_alpha, beta, scale, h0, hT,   o, ws + L.discard, H,
                           T,  varlen ? cu_seqlens : nullptr, (int)tokens, gate, pre,
                           reinterpret_cast<uint8_t *>(ws + L.strong)};
-        return kda::launch_fused(fa, d_k, d_v, bf, nseq, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        fa.seg_len = fp.seg_len;
+        fa.n_seqs = nseq;
+        fa.segs_per_seq = fp.segs_per_seq;
+        if (fp.seg_len > 0) {
+            fa.seg_state = reinterpret_cast<float *>(ws + L.seg_state);
+            fa.seg_map = reinterpret_cast<float *>(ws + L.seg_map);
+            if (varlen) {
+                int32_t *tab = reinterpret_cast<int32_t *>(ws + L.seg_tab);
+                fa.seg_off = tab;
+                fa.seg_tb = tab + n_seqs + 1;
+                fa.seg_te = tab + 2 * n_seqs + 1;
+                if (kda::launch_chunk_offsets(cu_seqlens, n_seqs, (int)tokens, fp.seg_len, tab, tab + n_seqs + 1,
+                                              tab + 2 * n_seqs + 1, hs, 1) != hipSuccess)
+                    return KDA_ERR_HIP;
+            }
+        }
+        return kda::launch_fused(fa, d_k, d_v, bf, nseq, fp.n_seg, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     ChunkBuffers buf{};
     if (L.total > 0) {

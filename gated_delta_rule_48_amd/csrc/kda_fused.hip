@@ -199,14 +199,24 @@ __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb 
     (void)hi;                                                                  \
     (void)r;
 
-// kStrong = false: the usual instance. Where a chunk's decay sums below -kStrongDecay on
-// some channel (the midpoint factors of the usual path would leave the fp32 range), it
-// records the (sequence, head) in a.redo and stops. kStrong = true: runs after it, on the
-// recorded pairs only, from the start of the sequence, with every exponent <= 0: the
-// state-side factors taken from the chunk's start, the Gram tiles left of the diagonal
-// from the end of their column block, the diagonal tiles pair by pair.
-template <int G, bool kStrong>
+// Instances (kMode):
+//   kUsual  the usual pass. Where a chunk's decay sums below -kStrongDecay on some channel
+//           (the midpoint factors would leave the fp32 range), it records the (sequence,
+//           head) in a.redo and stops.
+//   kStrongPass  runs after it, on the recorded pairs only, from the start of the
+//           sequence, with every exponent <= 0: the state-side factors taken from the
+//           chunk's start, the Gram tiles left of the diagonal from the end of their column
+//           block, the diagonal tiles pair by pair.
+//   kMap    for a segment of a long sequence: its map S_out = M S_in + N, with M (d_k x d_k)
+//           carried from I and N from h0 (first segment) or zero through the segment's
+//           chunks as a second state, no outputs. A segment with a chunk of strong decay
+//           stops; its pair is run again by the strong instance.
+constexpr int kUsual = 0, kStrongPass = 1, kMap = 2;
+
+template <int G, int kMode>
 __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
+    constexpr bool kStrong = kMode == kStrongPass;
+    constexpr bool kMapMode = kMode == kMap;
     // G: the kda_gate kinds, kGatePreact, and kGatePreactQK (kGatePreact with q and k
     // normalised here as well)
     constexpr bool kPreact = G == kGatePreact || G == kGatePreactQK;
@@ -236,19 +246,61 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     float *egam = reinterpret_cast<float *>(smem + Lds::EGAM);
     float *saq = reinterpret_cast<float *>(smem + Lds::SAQ);
 
-    if constexpr (kStrong) {
-        if (a.redo[blockIdx.x] == 0) return;  // the usual instance finished this pair
-    }
     const int H = a.H;
-    const int s = blockIdx.x / H, h = blockIdx.x % H;
+    int s = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    // segments of this sequence: before this workgroup's and in all (1, 1 without segments)
+    int seg_p = 0, seg_n = 1;
+    if (a.seg_len > 0 && !kStrong) {  // (the strong instance runs whole pairs: one workgroup each)
+        // the workgroup runs segment gi (of all sequences): find its sequence
+        const int gi = blockIdx.x / H;
+        if (a.cu_seqlens) {
+            if (gi >= a.seg_off[a.n_seqs]) return;  // past the last segment
+            int lo = 0, hi2 = a.n_seqs - 1;  // last s with seg_off[s] <= gi (empty sequences have one)
+            while (lo < hi2) {
+                const int mid = (lo + hi2 + 1) >> 1;
+                if (a.seg_off[mid] <= gi) lo = mid; else hi2 = mid - 1;
+            }
+            s = lo;
+            seg_p = gi - a.seg_off[s];
+            seg_n = a.seg_off[s + 1] - a.seg_off[s];
+        } else {
+            s = gi / a.segs_per_seq;
+            if (s >= a.n_seqs) return;
+            seg_p = gi - s * a.segs_per_seq;
+            seg_n = a.segs_per_seq;
+        }
+    }
+    if constexpr (kStrong) {
+        // the usual instance finished this pair unless it flagged it (or one of its segments)
+        bool any = false;
+        if (a.seg_len > 0) {
+            const int g0 = a.cu_seqlens ? a.seg_off[s] : s * a.segs_per_seq;
+            const int gn = a.cu_seqlens ? a.seg_off[s + 1] : g0 + a.segs_per_seq;
+            for (int gi = g0; gi < gn; ++gi) any |= a.redo[(size_t)gi * H + h] != 0;
+        } else {
+            any = a.redo[blockIdx.x] != 0;
+        }
+        if (!any) return;
+    }
+    if constexpr (kMapMode) {
+        if (seg_p >= seg_n - 1) return;  // the last segment's map is not needed
+    }
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, hi = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rb = w & 3, hf = w >> 2;
     const float scale = a.scale;
     // this sequence's tokens: seq_len each, or packed at the (clamped) offsets cu_seqlens
+    // (with segments, the segment's part of them)
     int T_len = a.seq_len;
     size_t seq0 = (size_t)s * T_len;
-    if (a.cu_seqlens) {
+    if (a.seg_len > 0 && !kStrong) {
+        const int tb = a.cu_seqlens ? a.seg_tb[s] : s * a.seq_len;
+        const int te = a.cu_seqlens ? a.seg_te[s] : tb + a.seq_len;
+        const int t_beg = min(tb + seg_p * a.seg_len, te);
+        T_len = min(a.seg_len, te - t_beg);
+        seq0 = T_len > 0 ? (size_t)t_beg : 0;
+    } else if (a.cu_seqlens) {
         const int b0 = min(max(a.cu_seqlens[s], 0), a.T_total);
         const int b1 = min(max(a.cu_seqlens[s + 1], b0), a.T_total);
         T_len = b1 - b0;
@@ -256,14 +308,23 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         // loop) then read row 0 of the batch, which exists, and are never used
         seq0 = T_len > 0 ? (size_t)b0 : 0;
     }
+    // the state this workgroup starts from: h0 of the sequence (its first segment), or the
+    // state entering the segment; it writes hT only if it runs the sequence's end
+    const float *h0src = nullptr;
+    if (seg_p == 0 || kStrong) {
+        h0src = a.h0 ? a.h0 + ((size_t)s * H + h) * kDK * kDV : nullptr;
+    } else if constexpr (!kMapMode) {
+        h0src = a.seg_state + (size_t)blockIdx.x * kDK * kDV;
+    }
+    const bool writes_hT = a.hT && (kStrong || seg_p == seg_n - 1);
     const int n_c = (T_len + kC - 1) / kC;
     const int T_ld = max(T_len, 1);  // the rows the loads may touch (row 0 for an empty sequence)
 
     // ---- state columns (value positions) 16 w .. 16 w + 15: tile tm holds rows (key
     //      positions) 16 tm + 4 hi + i of column 16 w + lr
     f32x4 accS[8];
-    if (a.h0) {
-        const float *h0 = a.h0 + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
+    if (h0src) {
+        const float *h0 = h0src + chan_of_pos(16 * w + lr);
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
@@ -271,6 +332,14 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     } else {
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) accS[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // map instance: M, from the identity (rows and columns are key positions)
+    f32x4 accM[8];
+    if constexpr (kMapMode) {
+#pragma unroll
+        for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accM[tm][i] = (16 * tm + 4 * hi + i == 16 * w + lr) ? 1.f : 0.f;
     }
 
     // ---- this lane's inputs of one chunk: row r, channel groups 2 hf and 2 hf + 1.
@@ -300,6 +369,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         for (int x = 0; x < 2; ++x) kr[x] = load_row8(base + ro, 2 * hf + x, ln >> 4);
     };
     auto load_q = [&](int ci) {
+        if constexpr (kMapMode) return;  // (no outputs: q is not read)
         const int ln = opaque_lane();
         const bf16 *base = static_cast<const bf16 *>(a.q) + tok0_of(ci) * kDK;
         const unsigned ro = row_off(ci, ln) * kDK;
@@ -504,9 +574,10 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         __syncthreads();
         if constexpr (!kStrong) {
-            // a chunk of strong decay: the pair is left to the strong instance
+            // a chunk of strong decay: the pair is left to the strong instance (a segment's
+            // map is then not needed: the workgroup that runs the segment records it)
             if (__builtin_amdgcn_readfirstlane(flg[2] | flg[3]) != 0) {
-                if (tid == 0) a.redo[blockIdx.x] = 1;
+                if (!kMapMode && tid == 0) a.redo[blockIdx.x] = 1;
                 return;
             }
         }
@@ -635,11 +706,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 }
             }
             kpf[x] = pack8(xp);
-            qpf[x] = pack8(xq);
             const bf16x8 km = pack8(xm);
             const int off = ((kg * 4 + rb) * 64 + l) * 8;
             *reinterpret_cast<bf16x8 *>(Kp + off) = kpf[x];
-            *reinterpret_cast<bf16x8 *>(Qp + off) = qpf[x];
+            if constexpr (!kMapMode) {  // (the map instance has no outputs)
+                qpf[x] = pack8(xq);
+                *reinterpret_cast<bf16x8 *>(Qp + off) = qpf[x];
+            }
             *reinterpret_cast<bf16x8 *>(Km + off) = km;
             // chunk rows 16 rb .. are contraction slots 4 (rb % 2) .. of group rb / 2
 #pragma unroll
@@ -651,7 +724,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
                 store_slots(Vt, rb >> 1, 2 * (2 * hf + x) + t, kDV, rb & 1, Frag<bf16>::mma(zero4, vr[x], t ? id1 : id0), l);
-        if constexpr (kQK) {
+        if constexpr (kQK && !kMapMode) {
             sq += __shfl_xor(sq, 16);
             sq += __shfl_xor(sq, 32);
             if (hi == 0) qks[(hf * kC + r) * 2 + 1] = sq;
@@ -823,8 +896,11 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             // Each Km column block is read once (the next one while the current one is
             // multiplied) and serves both products.
             const int rq = 3 - rb;
-            const bf16x8 qb[4] = {fld(Qp, 0, rq, kC, l), fld(Qp, 1, rq, kC, l), fld(Qp, 2, rq, kC, l),
-                                  fld(Qp, 3, rq, kC, l)};
+            bf16x8 qb[4];
+            if constexpr (!kMapMode) {  // (the map instance forms no Aqk)
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) qb[kg] = fld(Qp, kg, rq, kC, l);
+            }
             // (read unconditionally: a conditional read would be merged with an undefined
             // value at the branch's end, which costs register copies on every path)
             bf16x8 ka[4];
@@ -834,7 +910,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             // Aqk's scale, times the inverse norm of silu(q)'s row 16 rq + lr (kQK; kept
             // for the state phase's O)
             float aqs = scale;
-            if constexpr (kQK) {
+            if constexpr (kQK && !kMapMode) {
                 const int qrow = 16 * rq + lr;
                 const float n = __builtin_amdgcn_rcpf(
                     fmaxf(__builtin_sqrtf(qks[qrow * 2 + 1] + qks[(kC + qrow) * 2 + 1]), kNormEps));
@@ -858,7 +934,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) Am[(16 * rb + 4 * hi + i) * kPT + 16 * tj + lr] = bv[i] * acc[i];
                 }
-                if (tj < 2 * ((rq >> 1) + 1)) {
+                if (!kMapMode && tj < 2 * ((rq >> 1) + 1)) {
                     f32x4 acc = zero4;
                     if (tj <= rq) {
 #pragma unroll
@@ -943,7 +1019,102 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         //      operands come from LDS one row block ahead of the products that use
         //      them (the scheduling barriers keep those reads ahead of the
         //      matrix-core work).
-        {
+        if constexpr (kMapMode) {
+            // The map instance: the same update for N (accS, with v) and for M (accM, whose
+            // "values" are zero: Y = -Kp P), no outputs.
+            KDA_PHASE_LANE
+            auto scale_rows = [&](f32x4 (&acc)[8]) {  // P = E (E_prev Q), as below
+                if constexpr (G == kGateHead) {
+                    const float ep0 = ehalf[0], ec0 = ehalf[kDK];
+                    if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
+#pragma unroll
+                        for (int tm = 0; tm < 8; ++tm) acc[tm] = acc[tm] * ep0 * ec0;
+                    } else {
+#pragma unroll
+                        for (int tm = 0; tm < 8; ++tm) acc[tm] *= ep0 * ec0;
+                    }
+                }
+                if constexpr (kPerChannel) {
+                    const f32x2 ep = *reinterpret_cast<const f32x2 *>(ehalf + 32 * hi + 2 * lr);
+                    const f32x2 ec = *reinterpret_cast<const f32x2 *>(ehalf + kDK + 32 * hi + 2 * lr);
+                    if (__builtin_amdgcn_readfirstlane(flg[0] | flg[1]) != 0) {
+#define KDA_EROW(TM)                                                                     \
+    acc[TM][0] = acc[TM][0] * row_bcast<2 * TM>(ep[0]) * row_bcast<2 * TM>(ec[0]);         \
+    acc[TM][1] = acc[TM][1] * row_bcast<2 * TM>(ep[1]) * row_bcast<2 * TM>(ec[1]);         \
+    acc[TM][2] = acc[TM][2] * row_bcast<2 * TM + 1>(ep[0]) * row_bcast<2 * TM + 1>(ec[0]); \
+    acc[TM][3] = acc[TM][3] * row_bcast<2 * TM + 1>(ep[1]) * row_bcast<2 * TM + 1>(ec[1]);
+                        KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
+#undef KDA_EROW
+                    } else {
+                        const f32x2 e2 = ep * ec;
+#define KDA_EROW(TM)                                   \
+    acc[TM][0] *= row_bcast<2 * TM>(e2[0]);            \
+    acc[TM][1] *= row_bcast<2 * TM>(e2[1]);            \
+    acc[TM][2] *= row_bcast<2 * TM + 1>(e2[0]);        \
+    acc[TM][3] *= row_bcast<2 * TM + 1>(e2[1]);
+                        KDA_EROW(0) KDA_EROW(1) KDA_EROW(2) KDA_EROW(3) KDA_EROW(4) KDA_EROW(5) KDA_EROW(6) KDA_EROW(7)
+#undef KDA_EROW
+                    }
+                }
+            };
+            auto advance = [&](f32x4 (&acc)[8], bool with_v) {  // Y = v - Kp P; U = T' Y; Q = P + Km^T U
+                bf16x8 sb[4];
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) sb[kg] = tiles_to_frag(acc[2 * kg], acc[2 * kg + 1]);
+                const bf16x8 vf[2] = {fld(Vt, 0, w, kDV, l), fld(Vt, 1, w, kDV, l)};
+                bf16x8 fa[2][4];
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg) fa[0][kg] = fld(Kp, kg, 0, kC, l);
+                bf16x8 tq[6];
+                f32x4 ya[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    if (rr < 3) {
+#pragma unroll
+                        for (int kg = 0; kg < 4; ++kg) fa[(rr + 1) & 1][kg] = fld(Kp, kg, rr + 1, kC, l);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) tq[q] = fld(Tf, 0, q, kC, l);
+                        tq[4] = fld(Tf, 1, 2, kC, l);
+                        tq[5] = fld(Tf, 1, 3, kC, l);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    f32x4 pk = zero4;
+#pragma unroll
+                    for (int kg = 0; kg < 4; ++kg) pk = Frag<bf16>::mma(pk, fa[rr & 1][kg], sb[kg]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ya[rr][i] = (with_v ? static_cast<float>(vf[rr >> 1][4 * (rr & 1) + i]) : 0.f) - pk[i];
+                }
+                const bf16x8 yb[2] = {tiles_to_frag(ya[0], ya[1]), tiles_to_frag(ya[2], ya[3])};
+                f32x4 ua[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    ua[rr] = Frag<bf16>::mma(zero4, tq[rr], yb[0]);
+                    if (rr >= 2) ua[rr] = Frag<bf16>::mma(ua[rr], tq[rr + 2], yb[1]);
+                }
+                bf16x8 ub[2];
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) ub[kc] = tiles_to_frag(ua[2 * kc], ua[2 * kc + 1]);
+                bf16x8 kf[2][2];
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) kf[0][kc] = fld(KtT, kc, 0, kDK, l);
+#pragma unroll
+                for (int tm = 0; tm < 8; ++tm) {
+                    if (tm < 7) {
+#pragma unroll
+                        for (int kc = 0; kc < 2; ++kc) kf[(tm + 1) & 1][kc] = fld(KtT, kc, tm + 1, kDK, l);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) acc[tm] = Frag<bf16>::mma(acc[tm], kf[tm & 1][kc], ub[kc]);
+                }
+            };
+            scale_rows(accS);
+            scale_rows(accM);
+            advance(accS, true);
+            advance(accM, false);
+        } else {
             KDA_PHASE_LANE
             {
                 // P = E (E_prev Q). Q can be as large as E_prev is small, so where the
@@ -1086,7 +1257,26 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         // reads (from the per-channel factors on), every wave passes its first barrier.
     }
 
-    if constexpr (!kStrong) {
+    if constexpr (kMapMode) {
+        // M = E_last Q_M and N = E_last Q_N: the factor exp(gamma / 2) of the last chunk,
+        // once every wave has read that chunk's factors
+        __syncthreads();
+        if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
+        __syncthreads();
+        float *mp = a.seg_map + (size_t)blockIdx.x * 2 * kDK * kDV;
+        const int cc = chan_of_pos(16 * w + lr);
+#pragma unroll
+        for (int tm = 0; tm < 8; ++tm) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = 16 * tm + 4 * hi + i;
+                const float e = ehalf[e_slot(p)];
+                mp[chan_of_pos(p) * kDK + cc] = e * accM[tm][i];
+                mp[kDK * kDK + chan_of_pos(p) * kDV + cc] = e * accS[tm][i];
+            }
+        }
+        return;
+    } else if constexpr (!kStrong) {
         if (tid == 0) a.redo[blockIdx.x] = 0;  // no chunk of strong decay in this pair
     } else {
         if (a.hT) {
@@ -1098,7 +1288,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         return;
     }
-    if (a.hT) {
+    if (writes_hT) {
         // S = E_last Q: the factor exp(gamma / 2) of the last chunk, once every wave has
         // read that chunk's factors
         __syncthreads();
@@ -1117,39 +1307,55 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
 
 }  // namespace
 
-hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream) {
+hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, int n_seg_grid,
+                        hipStream_t stream) {
     // the fused pass is built for bf16 input and d_k = d_v = 128 only
     if (!bf16 || dk != kDK || dv != kDV) return hipErrorInvalidValue;
     constexpr size_t smem = Lds::SIZE;
-    // the usual instance, then the strong-decay one over the pairs the first left to it
-    // (without a decay, no chunk can leave it any)
+    // Without segments: the usual instance over the (sequence, head) pairs, then the strong
+    // one over the pairs the first left to it. With segments: the maps of the segments, their
+    // composition, the usual instance over the (segment, head) pairs, then the strong one over
+    // the (sequence, head) pairs any of whose segments was left to it. (Without a decay, no
+    // chunk can leave anything to the strong instance.)
     typedef void (*Kern)(FusedArgs);
-    Kern kern[2];
+    Kern usual, strong, map;
     if (a.gate == kGateHead) {
-        kern[0] = kda_fused_kernel<kGateHead, false>;
-        kern[1] = kda_fused_kernel<kGateHead, true>;
+        usual = kda_fused_kernel<kGateHead, kUsual>;
+        strong = kda_fused_kernel<kGateHead, kStrongPass>;
+        map = kda_fused_kernel<kGateHead, kMap>;
     } else if (a.gate == kGateNone) {
-        kern[0] = kda_fused_kernel<kGateNone, false>;
-        kern[1] = nullptr;
+        usual = kda_fused_kernel<kGateNone, kUsual>;
+        strong = nullptr;
+        map = kda_fused_kernel<kGateNone, kMap>;
     } else if (a.gate == kGatePreact && a.pre.qk_norm) {
-        kern[0] = kda_fused_kernel<kGatePreactQK, false>;
-        kern[1] = kda_fused_kernel<kGatePreactQK, true>;
+        usual = kda_fused_kernel<kGatePreactQK, kUsual>;
+        strong = kda_fused_kernel<kGatePreactQK, kStrongPass>;
+        map = kda_fused_kernel<kGatePreactQK, kMap>;
     } else if (a.gate == kGatePreact) {
-        kern[0] = kda_fused_kernel<kGatePreact, false>;
-        kern[1] = kda_fused_kernel<kGatePreact, true>;
+        usual = kda_fused_kernel<kGatePreact, kUsual>;
+        strong = kda_fused_kernel<kGatePreact, kStrongPass>;
+        map = kda_fused_kernel<kGatePreact, kMap>;
     } else {
-        kern[0] = kda_fused_kernel<kGateChannel, false>;
-        kern[1] = kda_fused_kernel<kGateChannel, true>;
+        usual = kda_fused_kernel<kGateChannel, kUsual>;
+        strong = kda_fused_kernel<kGateChannel, kStrongPass>;
+        map = kda_fused_kernel<kGateChannel, kMap>;
     }
-    for (Kern k : kern) {
-        if (!k) continue;
+    auto go = [&](Kern k, int grid) {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(k, dim3(n_seqs * a.H), dim3(kNT), smem, stream, a);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(k, dim3(grid), dim3(kNT), smem, stream, a);
+        return hipGetLastError();
+    };
+    hipError_t err;
+    if (a.seg_len > 0) {
+        if ((err = go(map, n_seg_grid * a.H)) != hipSuccess) return err;
+        if ((err = launch_segment_chain(a, stream)) != hipSuccess) return err;
+        if ((err = go(usual, n_seg_grid * a.H)) != hipSuccess) return err;
+    } else {
+        if ((err = go(usual, n_seqs * a.H)) != hipSuccess) return err;
     }
+    if (strong && (err = go(strong, n_seqs * a.H)) != hipSuccess) return err;
     return hipSuccess;
 }
 

@@ -84,9 +84,23 @@ struct FusedArgs {
     int T_total;
     int gate;       // as in PrepArgs
     PreactArgs pre;
-    uint8_t *redo;  // [n_seqs * H]: 1 where the usual instance met a chunk of strong decay
-                    // and left the (sequence, head) to the strong instance, else 0
+    uint8_t *redo;  // [n_seqs * H] (or [n_seg * H] with segments): 1 where the usual instance met
+                    // a chunk of strong decay and left the (sequence, head) to the strong instance
+    // Segments: each sequence cut into runs of seg_len tokens (a multiple of 64), one
+    // workgroup per (segment, head); seg_len = 0: one workgroup per (sequence, head).
+    int seg_len;
+    int n_seqs;
+    int segs_per_seq;          // equal-length sequences: segments of each
+    const int32_t *seg_off;    // packed sequences: [n_seqs + 1] segments before each sequence,
+    const int32_t *seg_tb;     // then each sequence's clamped begin and end ([n_seqs] each)
+    const int32_t *seg_te;
+    float *seg_state;          // [n_seg, H, d_k, d_v] fp32: the state entering each segment (p > 0)
+    float *seg_map;            // [n_seg, H, 2, d_k, d_k | d_v] fp32: M and N of each segment (S_out = M S_in + N)
 };
+
+// The composition of segment maps: per (sequence, head, 16 value columns), in order,
+// S_in(1) = N(0) (segment 0's map starts from h0) and S_in(p + 1) = M(p) S_in(p) + N(p).
+hipError_t launch_segment_chain(const FusedArgs &a, hipStream_t stream);
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -101,13 +115,16 @@ struct DecodeArgs {
 };
 
 // Each returns hipSuccess or the launch error.
+// min_one: count at least one chunk (segment) for an empty sequence
 hipError_t launch_chunk_offsets(const int32_t *cu, int n_seqs, int T_total, int C, int32_t *off,
-                                int32_t *tb, int32_t *te, hipStream_t stream);
+                                int32_t *tb, int32_t *te, hipStream_t stream, int min_one = 0);
 hipError_t launch_prep(const PrepArgs &a, int C, int dk, int dv, bool bf16, int n_chunks_grid,
                        hipStream_t stream);
 hipError_t launch_state(const StateArgs &a, int C, int dk, int dv, bool bf16, int n_seqs,
                         hipStream_t stream);
-hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream);
+// n_seg_grid: with segments (a.seg_len > 0), an upper bound on the number of segments
+hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, int n_seg_grid,
+                        hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dk, int dv, bool bf16, hipStream_t stream);
 
 }  // namespace kda

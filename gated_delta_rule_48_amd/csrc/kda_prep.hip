@@ -602,10 +602,10 @@ hipError_t dispatch_d(const PrepArgs &a, int dk, int dv, int n, hipStream_t st) 
 // Sequence ranges and chunk offsets of packed sequences. Sequence s spans
 // [tb, te) with tb = clamp(cu[s], end of sequence s-1, T) and te = clamp(cu[s+1],
 // tb, T): ordered, non-overlapping and inside the token range whatever the table
-// holds. off[s] = sum_{s' < s} ceil((te - tb) / C) <= ceil(T / C) + n_seqs.
+// holds. off[s] = sum_{s' < s} ceil((te - tb) / C) (at least min_one each) <= ceil(T / C) + n_seqs.
 // One thread; the loop is over sequences only.
 __global__ void kda_chunk_offsets_kernel(const int32_t *cu, int n_seqs, int T_total, int C,
-                                         int32_t *off, int32_t *tb_out, int32_t *te_out) {
+                                         int32_t *off, int32_t *tb_out, int32_t *te_out, int min_one) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     int acc = 0, prev_end = 0;
     for (int s = 0; s < n_seqs; ++s) {
@@ -614,7 +614,7 @@ __global__ void kda_chunk_offsets_kernel(const int32_t *cu, int n_seqs, int T_to
         off[s] = acc;
         tb_out[s] = tb;
         te_out[s] = te;
-        acc += (te - tb + C - 1) / C;
+        acc += max((te - tb + C - 1) / C, min_one);
         prev_end = te;
     }
     off[n_seqs] = acc;
@@ -623,9 +623,9 @@ __global__ void kda_chunk_offsets_kernel(const int32_t *cu, int n_seqs, int T_to
 }  // namespace
 
 hipError_t launch_chunk_offsets(const int32_t *cu, int n_seqs, int T_total, int C, int32_t *off,
-                                int32_t *tb, int32_t *te, hipStream_t stream) {
+                                int32_t *tb, int32_t *te, hipStream_t stream, int min_one) {
     hipLaunchKernelGGL(kda_chunk_offsets_kernel, dim3(1), dim3(64), 0, stream, cu, n_seqs, T_total,
-                       C, off, tb, te);
+                       C, off, tb, te, min_one);
     return hipGetLastError();
 }
 

@@ -41,10 +41,10 @@
  *    exponent is <= 0 (the decay from the chunk's start, or from the end of a
  *    16-row block, and the pairs inside a block one by one), so factors that
  *    underflow are the negligible values they stand for. Tested at chunk sums
- *    near -500 and -2000 for every gate kind. On the one-launch pass such a
- *    chunk sends its whole (sequence, head) pair to the second instance, which
- *    runs it again from the start. kda_chunk_bwd keeps the -170 limit of its
- *    midpoint factors.
+ *    near -500 and -2000 for every gate kind. On the fused pass (bf16,
+ *    d_k = d_v = 128) such a chunk sends its whole (sequence, head) pair to the
+ *    second instance, which runs it again from the start, one workgroup per
+ *    pair. kda_chunk_bwd keeps the -170 limit of its midpoint factors.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -116,7 +116,14 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int 
  * Arguments
  *   B, T        without cu_seqlens: B sequences of T tokens each, tensors
  *               [B, T, H, d] (the same memory as packed [B*T, H, d]).
- *   H, d_k, d_v heads and head dims.  chunk: 64 or 128.  io: kda_dtype.
+ *   H, d_k, d_v heads and head dims.  io: kda_dtype.
+ *   chunk       64 or 128: rows per chunk of the split pass (fp32, or d = 64).
+ *               The fused pass (bf16, d_k = d_v = 128) works in chunks of 64
+ *               rows for either value; since chunking is exact, only rounding
+ *               differs. With fewer than 256 (sequence, head) pairs the fused
+ *               pass cuts long sequences into segments: the affine map each
+ *               segment applies to its entering state, the maps composed in
+ *               order, then every segment again from its own entering state.
  *   q, k, v     [B*T, H, d_k|d_k|d_v], dtype io.
  *   log_alpha   [B*T, H, d_k] fp32, log of the per-channel decay (<= 0 normally).
  *   beta        [B*T, H] fp32, write strength.
@@ -166,11 +173,12 @@ int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chu
  *
  * Arguments, results and errors are those of kda_chunk_fwd_gated. In addition, sizes whose
  * workspace (kda_chunk_fwd_workspace_bytes) exceeds KDA_NOALLOC_MAX_WORKSPACE are
- * rejected with KDA_ERR_WORKSPACE before anything is enqueued; that covers every call of
- * the one-launch pass (bf16, d_k = d_v = 128, chunk 64, at least 256 (sequence, head)
- * pairs, whose workspace is 256 bytes) and split-pass calls of up to about 25,000 to
- * 30,000 token-heads at d = 128. The first call on a device looks up the array's device address
- * (KDA_ERR_HIP if that fails).
+ * rejected with KDA_ERR_WORKSPACE before anything is enqueued. The fused pass (bf16,
+ * d_k = d_v = 128) with at least 256 (sequence, head) pairs needs 256 bytes plus one per
+ * pair, so all such calls fit; with fewer pairs it cuts long sequences into segments and
+ * needs 192 KB per (segment, head), which fits up to about 170 of them; split-pass calls
+ * (fp32 or d = 64) fit up to about 25,000 to 30,000 token-heads at d = 128. The first call
+ * on a device looks up the array's device address (KDA_ERR_HIP if that fails).
  *
  * All calls on one GPU share the array: calls whose work overlaps in time on one GPU
  * (other streams, other host threads) race and give undefined results. Calls in order on

@@ -51,11 +51,37 @@ def test_version_and_status_strings(lib):
 
 def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    pairs = (n_seqs if n_seqs else B) * H
-    if C == 64 and esz == 2 and dk == dv == 128 and T > 0 and pairs >= 256:
-        # fused pass (equal-length or packed sequences): the 256-byte discard slot and one
-        # byte per (sequence, head) for the strong-decay instance
-        return 256 + r(pairs)
+    n_seq = n_seqs if n_seqs else B
+    pairs = n_seq * H
+    if esz == 2 and dk == dv == 128 and T > 0:
+        # fused pass (equal-length or packed sequences, any chunk size asked): the 256-byte
+        # discard slot and one byte per (sequence or segment, head) for the strong-decay
+        # instance; below 256 pairs, segments of lc chunks of 64 tokens with their table,
+        # entering states and maps
+        seg_len, n_seg = 0, n_seq
+        if pairs < 256:
+            chunks = (T + 63) // 64 + n_seqs if n_seqs else B * ((T + 63) // 64)
+            lc = 4
+            while lc < 1024 and lc * 2 * 512 <= chunks * H:
+                lc *= 2
+            seg_len = lc * 64
+            if n_seqs:
+                if T <= seg_len:
+                    seg_len = 0
+                else:
+                    n_seg = (T + seg_len - 1) // seg_len + n_seqs
+            else:
+                sps = (T + seg_len - 1) // seg_len
+                if sps <= 1:
+                    seg_len = 0
+                else:
+                    n_seg = B * sps
+        total = 256 + r(n_seg * H)
+        if seg_len:
+            if n_seqs:
+                total += r((3 * n_seqs + 1) * 4)
+            total += r(n_seg * H * dk * dv * 4) + r(n_seg * H * 2 * dk * dv * 4)
+        return total
     per = (T + C - 1) // C
     nch = (per + n_seqs if n_seqs else B * per) * H
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
@@ -104,7 +130,7 @@ def fwd(lib, **kw):
     (dict(cu=A, n_seqs=2), INVALID),                # varlen needs B == 1
     (dict(B=1, cu=A, n_seqs=0), INVALID),
     (dict(cu=A + 2, B=1, n_seqs=2), INVALID),
-    (dict(ws=None), WORKSPACE), (dict(ws=A + 16), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE),
+    (dict(ws=None), WORKSPACE), (dict(ws=A + 16), WORKSPACE), (dict(ws_bytes=300), WORKSPACE),
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code

@@ -36,22 +36,32 @@ def test_digest_covers_the_compiled_sources():
     bench = _bench()
     fused = _local_includes("kda_fused.hip")
     assert set(bench.PATHS["fused"]["sources"]) == fused
+    assert set(bench.PATHS["segmented"]["sources"]) == fused | _local_includes("kda_segment.hip")
     split = _local_includes("kda_prep.hip") | _local_includes("kda_state.hip")
     assert set(bench.PATHS["split"]["sources"]) == split
 
 
 def test_pass_rule_matches_the_library():
-    # the library's rule, read from its source: varlen off, chunk 64, bf16, d_k = d_v = 128, B*H >= 256
+    # the library's rule, read from its source and its workspace sizes: bf16 and d_k = d_v = 128
+    # take the fused pass (any chunk size asked), with segments below 256 (sequence, head)
+    # pairs when a sequence is longer than a segment
     src = open(os.path.join(CSRC, "kda_api.hip")).read()
     assert "kFusedMinPairs = 256" in src
     bench = _bench()
     assert bench.prefill_path(8, 8192, 32, 128, 128, 64, False, True) == "fused"
-    assert bench.prefill_path(1, 4096, 16, 128, 128, 64, False, True) == "split"      # 16 pairs
-    assert bench.prefill_path(1, 65536, 32, 128, 128, 128, True, True) == "split"     # varlen, chunk 128
-    assert bench.prefill_path(1, 65536, 32, 128, 128, 64, True, True, 4) == "split"   # varlen, 128 pairs
-    assert bench.prefill_path(1, 65536, 32, 128, 128, 64, True, True, 16) == "fused"  # varlen, 512 pairs
-    assert bench.prefill_path(8, 8192, 32, 128, 128, 64, False, False) == "split"     # fp32
-    assert bench.prefill_path(8, 8192, 32, 64, 64, 64, False, True) == "split"        # d = 64
+    assert bench.prefill_path(1, 4096, 16, 128, 128, 64, False, True) == "segmented"    # 16 pairs
+    assert bench.prefill_path(1, 65536, 32, 128, 128, 128, True, True, 4) == "segmented"  # varlen, 128 pairs
+    assert bench.prefill_path(1, 65536, 32, 128, 128, 64, True, True, 16) == "fused"     # varlen, 512 pairs
+    assert bench.prefill_path(1, 200, 4, 128, 128, 64, False, True) == "fused"          # one segment: no maps
+    assert bench.prefill_path(8, 8192, 32, 128, 128, 64, False, False) == "split"       # fp32
+    assert bench.prefill_path(8, 8192, 32, 64, 64, 64, False, True) == "split"          # d = 64
+    # the workspace says the same: 256 bytes of discard slot and one byte per unit on the
+    # fused pass, more than 64 KB per segment with segments, per chunk on the split pass
+    import gated_delta_rule_48_amd as kda
+    ws = lambda *a: kda.workspace_bytes(*a)  # noqa: E731
+    assert ws(8, 8192, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512
+    assert ws(1, 200, 4, 128, 128, 64, 0, kda.KDA_BF16) == 512
+    assert ws(1, 4096, 16, 128, 128, 64, 0, kda.KDA_BF16) > 16 * 16 * 3 * 65536
 
 
 def test_more_than_one_gpu_is_refused():

@@ -18,7 +18,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
-SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_decode.hip", "kda_attn.hip", "kda_bwd.hip"]
+SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_segment.hip", "kda_decode.hip", "kda_attn.hip",
+           "kda_bwd.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
@@ -56,7 +57,7 @@ def resources():
 
 def test_every_kernel_is_reported(resources):
     names = " ".join(resources)
-    for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_decode_kernel",
+    for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_segment_chain_kernel", "kda_decode_kernel",
               "kda_chunk_offsets_kernel", "kda_attn_decode_kernel", "kda_attn_combine_kernel",
               "kda_bwd_chunk_fwd_kernel", "kda_bwd_states_kernel", "kda_bwd_state_grads_kernel",
               "kda_bwd_chunk_grads_kernel"):
@@ -64,10 +65,10 @@ def test_every_kernel_is_reported(resources):
 
 
 def _strong_fused(name):
-    """The strong-decay instances of the fused kernel (kda_fused_kernel<G, true>): they run only
+    """The strong-decay instances of the fused kernel (kda_fused_kernel<G, 1>): they run only
     for (sequence, head) pairs with a chunk of strong decay, and their per-pair Gram work
-    spills; the usual instances must not."""
-    return "kda_fused_kernel" in name and "Lb1E" in name
+    spills; the usual (mode 0) and segment-map (mode 2) instances must not."""
+    return "kda_fused_kernel" in name and "ELi1EEEv" in name
 
 
 def test_no_scratch_and_no_spills(resources):
@@ -85,9 +86,9 @@ def test_no_scratch_and_no_spills(resources):
 
 def test_fused_kernel_runs_two_waves_per_simd(resources):
     fused = {n: r for n, r in resources.items() if "kda_fused_kernel" in n}
-    # the usual instances: per channel, per head, none, from pre-activations (with q, k
-    # normalised or not); the strong-decay instances of all but "none"
-    assert sum(not _strong_fused(n) for n in fused) == 5 and sum(_strong_fused(n) for n in fused) == 4
+    # the usual and the segment-map instances: per channel, per head, none, from
+    # pre-activations (with q, k normalised or not); the strong-decay instances of all but "none"
+    assert sum(not _strong_fused(n) for n in fused) == 10 and sum(_strong_fused(n) for n in fused) == 4
     for n, r in fused.items():
         assert int(r["Occupancy [waves/SIMD]"]) >= 2, (n, r)
         assert int(r["VGPRs"]) <= 256, (n, r)

@@ -7,16 +7,22 @@ fp32 gates and state (token = one (sequence, position) across all 32 heads).
 One step = one kda_chunk_fwd call over the whole batch, inputs resident in HBM.
 
 Also reported on the same line:
-  roofline      achieved algorithmic HBM bytes/s of the prefill pass vs 8 TB/s
+  roofline      achieved algorithmic HBM bytes/s of the prefill pass vs 8 TB/s, the
+                measured HBM traffic, and (mfma) algorithmic TFLOP/s of the chunk form's
+                products vs the 2.5 PFLOP/s bf16 matrix peak with the matrix cores' busy
+                fraction from the committed counters
   decode        kda_recurrent_step on 256 sequences x 32 heads (fp32 128x128
                 states, 537 MB), tokens/s = 256 / step time, with its own roofline
+  workloads     the other prefill configurations, each with its roofline: prefill
+                (1 x 4096 tokens, H=16), varlen (4 packed sequences, 65,536 tokens,
+                H=32, chunk 128) and tiny (1 x 256 tokens, H=2, d=64, fp32) by default
+  attn_decode   the softmax-attention decode step the pages compare KDA's with
+  backward      kda_chunk_bwd on the batched shape with bf16 I/O (the matrix-core pass),
+                and with fp32 I/O (backward_f32_io: the direct pass)
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded sample
                 of the same prefill workload
 
-With --workloads NAMES, further prefill workloads (the small-batch, varlen and fp32
-ones of kda_synth) are timed the same way and reported under "workloads".
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,varlen,tiny]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,varlen,tiny] [--no-bwd]
 """
 from __future__ import annotations
 
@@ -50,13 +56,13 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
 COMMON_SRC = ["kda_device.hpp", "kda_internal.hpp"]  # included by every kernel source
 PATHS = {
     "fused": dict(kernel="kda_fused_kernel", sources=["kda_fused.hip"] + COMMON_SRC,
-                  traffic="kda_fused_kernel_batched_prefill_traffic.md"),
+                  counters="kda_fused_kernel_batched_prefill_counters.md"),
     "segmented": dict(kernel="kda_fused_kernel (segment maps, then segments) + kda_segment_chain_kernel",
                       sources=["kda_fused.hip", "kda_segment.hip"] + COMMON_SRC,
-                      traffic="kda_segmented_pass_traffic.md"),
+                      counters="kda_segmented_pass_prefill_varlen_counters.md"),
     "split": dict(kernel="kda_prep_kernel + kda_state_kernel",
                   sources=["kda_prep.hip", "kda_state.hip", "kda_solve.hpp"] + COMMON_SRC,
-                  traffic="kda_split_pass_batched_prefill_traffic.md"),
+                  counters="kda_split_pass_tiny_counters.md"),
 }
 
 
@@ -73,7 +79,7 @@ def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16, n_seqs=0):
         return "fused"
     chunks = (T + 63) // 64 + n_seqs if varlen else B * ((T + 63) // 64)
     lc = 4
-    while lc < 1024 and lc * 2 * 512 <= chunks * H:
+    while lc < 1024 and lc * 2 * 256 <= chunks * H:
         lc *= 2
     seg = lc * 64
     longer = T > seg if varlen else (T + seg - 1) // seg > 1
@@ -88,20 +94,26 @@ def sources_digest(names):
     return h.hexdigest()
 
 
-def stored_traffic(path_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    schedule (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or
-    None when there is none or the kernel sources changed since it was taken."""
+def stored_counter(path_key, workload, key):
+    """A figure of the committed rocprofv3 counter summary of this schedule, the line
+    `key[workload]: value`, or None when there is none or the kernel sources changed
+    since the counters were taken (the summary records their SHA-256)."""
     info = PATHS[path_key]
-    fn = os.path.join(ROOT, "profiles", info["traffic"])
+    fn = os.path.join(ROOT, "profiles", info["counters"])
     if not os.path.exists(fn):
         return None
     txt = open(fn).read()
-    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_b = re.search(re.escape(f"{key}[{workload}]:") + r"\s*([0-9.eE+]+)", txt)
     m_h = re.search(r"sources_sha256:\s*([0-9a-f]{64})", txt)
     if not (m_b and m_h) or m_h.group(1) != sources_digest(info["sources"]):
         return None
     return float(m_b.group(1))
+
+
+def stored_traffic(path_key, workload):
+    """HBM bytes per call (FETCH_SIZE + WRITE_SIZE over the call's kernels, each calibrated
+    on a device copy of known size), or None."""
+    return stored_counter(path_key, workload, "traffic_bytes_per_launch")
 
 
 def copy_probe(torch, mib):
@@ -172,6 +184,33 @@ def prefill_algorithmic_bytes(token_heads, dk, dv, io_bytes, n_states_out, n_sta
     return token_heads * per + 4 * dk * dv * (n_states_out + n_states_in)
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def prefill_algorithmic_flops(seqlens, H, dk, dv, C):
+    """Flops of the chunk form's products per call (2 per multiply-add), each dense product
+    counted once at its full size: per chunk of C rows and head, the Gram matrices of the
+    solve and of the output (K K^T and Q K^T, C x C x dk each), W = T Bk (C x C x dk), U~ = T Bv
+    (C x C x dv), the intra-chunk output Aqk U (C x C x dv), and the three state products
+    W S, Q S and R^T U (C x dk x dv each). The triangular solve, the decay factors and the
+    segment maps of the segmented pass are not counted."""
+    macs = 3 * C * C * dk + 2 * C * C * dv + 3 * C * dk * dv
+    chunks = sum((n + C - 1) // C for n in seqlens)
+    return 2 * macs * chunks * H
+
+
+def mfma_roofline(flops, ms, path_key, workload):
+    """Algorithmic TFLOP/s of the call against the bf16 matrix peak, and the matrix cores'
+    busy fraction over the call's kernels from the committed counters (SQ_VALU_MFMA_BUSY_CYCLES
+    over 4 x SQ_BUSY_CU_CYCLES: four matrix units per CU), or None."""
+    t = flops / (ms * 1e-3) / 1e12
+    return {"achieved": round(t, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(t / BF16_MFMA_PEAK_TFLOPS, 4), "alg_flops_per_launch": flops,
+            "busy": stored_counter(path_key, workload, "mfma_busy_frac")}
+
+
+
+
 def bench_prefill(args, kda, torch):
     w = kda_synth.WORKLOADS["batched"]
     B, T, H, dk, dv, C = len(w.seqlens), w.seqlens[0], w.H, w.dk, w.dv, w.chunk
@@ -218,7 +257,8 @@ def bench_prefill(args, kda, torch):
         f"{tokens / (ms * 1e-3):.3e} tokens/s, {achieved:.0f} GB/s algorithmic")
     path = prefill_path(B, T, H, dk, dv, C, False, True)
     res = dict(ms=ms, ev_ms=ev_avg, tokens_per_s=tokens / (ms * 1e-3), alg_bytes=alg,
-               achieved_gbs=achieved, workload=w, x=x, path=path)
+               achieved_gbs=achieved, workload=w, x=x, path=path,
+               mfma=mfma_roofline(prefill_algorithmic_flops(w.seqlens, H, dk, dv, 64), ev_avg, path, "batched"))
     del q, k, v, la, beta, o, hT, ws
     return res
 
@@ -290,8 +330,10 @@ def bench_workload(args, kda, torch, name):
                                     0 if h0 is None else n_seqs * w.H, w.gate)
     achieved = alg / (ms * 1e-3) / 1e9
     path = prefill_path(B, T, w.H, w.dk, w.dv, w.chunk, varlen, w.io == "bf16", len(w.seqlens))
+    mf = mfma_roofline(prefill_algorithmic_flops(w.seqlens, w.H, w.dk, w.dv, w.chunk if path == "split" else 64),
+                       ms, path, name)
     log(f"[bench] workload {name} ({path} pass): {ms:.3f} ms/call, {tokens / (ms * 1e-3):.3e} tokens/s, "
-        f"{achieved:.0f} GB/s algorithmic")
+        f"{achieved:.0f} GB/s algorithmic, {mf['achieved']:.1f} TFLOP/s")
     return {"value": tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 4), "pass": path,
             "kernel": PATHS[path]["kernel"],
             "workload": f"seqlens {list(w.seqlens)}, H={w.H}, d_k=d_v={w.dk}, chunk {w.chunk}, {w.io} q/k/v/o, "
@@ -299,7 +341,8 @@ def bench_workload(args, kda, torch, name):
                            "preact": "gates formed in the kernel from pre-activations",
                            "preact_qk": "gates, and q and k (silu, L2 norm), formed in the kernel"}[w.gate],
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg}}
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg,
+                         "traffic": stored_traffic(path, name), "mfma": mf}}
 
 
 def bench_decode(args, kda, torch):
@@ -405,6 +448,14 @@ def bwd_algorithmic_flops(B, T, H, dk, dv, C=64):
     return 2 * macs * B * ((T + C - 1) // C) * H
 
 
+def bwd_algorithmic_bytes(B, T, H, dk, dv, io_bytes):
+    """Bytes the backward pass must move at least: q, k, v, the output gradient and dq, dk,
+    dv in the io dtype, log_alpha and dlog_alpha (fp32, per key channel), beta and dbeta per
+    token-head, and the fp32 loss gradient of each final state (dhT) read."""
+    per = (2 * dk + 2 * dv) * io_bytes + (2 * dk + dv) * io_bytes + 2 * 4 * dk + 2 * 4
+    return B * T * H * per + B * H * dk * dv * 4
+
+
 def bench_bwd(args, kda, torch, io="f32"):
     """The backward pass (kda_chunk_bwd) on the batched workload's shape: B=8, T=8192, H=32,
     d=128, chunk 64, q, k, v and the output gradient in `io` (fp32 arithmetic either way),
@@ -439,19 +490,32 @@ def bench_bwd(args, kda, torch, io="f32"):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    # bound: the products, in fp32 on the matrix cores (the inputs and gradients themselves are
-    # 9.7 GB, 1.2 ms of HBM time at 8 TB/s)
     flops = bwd_algorithmic_flops(B, T, H, d, d)
-    achieved = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] backward ({io} I/O): {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, {achieved:.1f} "
-        "TFLOP/s algorithmic (fp32 products)")
+    tflops = flops / (ms * 1e-3) / 1e12
+    nbytes = bwd_algorithmic_bytes(B, T, H, d, d, 2 if io == "bf16" else 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    if io == "bf16":
+        # the matrix-core pass (bf16 products): 1.07 TFLOP is 0.43 ms at the bf16 peak, the
+        # 5.9 GB of inputs and gradients 0.74 ms at 8 TB/s, so HBM bounds it
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_call": nbytes,
+                "mfma": {"achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "alg_flops_per_call": flops}}
+        kind = "matrix-core pass, bf16 products"
+    else:
+        # the direct pass (fp32 products): 6.8 ms at the fp32 matrix peak against 1.2 ms of HBM time
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP32_MATRIX_PEAK_TFLOPS, 4), "alg_flops_per_call": flops,
+                "alg_bytes_per_call": nbytes}
+        kind = "direct pass, fp32 products"
+    log(f"[bench] backward ({io} I/O, {kind}): {ms:.2f} ms/call, {B * T / (ms * 1e-3):.3e} tokens/s, "
+        f"{tflops:.1f} TFLOP/s and {gbs:.0f} GB/s algorithmic")
     del q, k, v, dout, la, beta, dhT, ws
     torch.cuda.empty_cache()
     return {"value": B * T / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 3), "steps": n,
-            "workload": f"backward of the batched prefill: B={B} x T={T}, H={H}, d_k=d_v={d}, chunk 64, {io} I/O",
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MATRIX_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / FP32_MATRIX_PEAK_TFLOPS, 4),
-                         "alg_flops_per_call": flops}}
+            "workload": f"backward of the batched prefill: B={B} x T={T}, H={H}, d_k=d_v={d}, chunk 64, {io} I/O "
+                        f"({kind})",
+            "roofline": roof}
 
 
 def cpu_baseline(pre, args):
@@ -478,7 +542,37 @@ def cpu_baseline(pre, args):
                       f"the batched prefill workload; fp64 token-by-token recurrence, {dt:.2f} s"}
 
 
+def trace_summary(csv_path, last):
+    """Markdown table of a rocprofv3 kernel trace (`--kernel-trace --output-format csv`,
+    the *_kernel_trace.csv file): per (kernel, grid, workgroup size), in order of first
+    dispatch, the number of dispatches, the average duration over all of them and over the
+    last `last` (a leg's timed launches are its last --steps dispatches)."""
+    import csv
+    groups = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+            key = (r["Kernel_Name"], grid, wg)
+            groups.setdefault(key, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    print(f"| kernel | workgroups | threads | dispatches | average (us) | average of the last {last} (us) |")
+    print("|---|---|---|---|---|---|")
+    for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: min(t for t, _ in kv[1])):
+        v.sort()
+        d = [(e - b) / 1000.0 for b, e in v]
+        tail = d[-last:]
+        short = name if len(name) <= 90 else name[:87] + "..."
+        print(f"| `{short}` | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.1f} | {sum(tail) / len(tail):.1f} |")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--trace-summary", metavar="CSV", required=True)
+        ap.add_argument("--last", type=int, default=20)
+        a = ap.parse_args()
+        trace_summary(a.trace_summary, a.last)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -498,12 +592,13 @@ def main():
                     help="attention-decode comparator workloads to time (" + ", ".join(kda_synth.ATTN_WORKLOADS) +
                          "; empty for none)")
     ap.add_argument("--attn-steps", type=int, default=50)
-    ap.add_argument("--bwd", action="store_true",
-                    help="also time the backward pass on the batched shape (fp32 and bf16 I/O)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward pass on the batched shape (fp32 and bf16 I/O)")
+    ap.add_argument("--bwd", action="store_true", help=argparse.SUPPRESS)  # the default; kept for old commands
     ap.add_argument("--bwd-steps", type=int, default=3)
-    ap.add_argument("--workloads", default="", metavar="NAMES",
+    ap.add_argument("--workloads", default="prefill,varlen,tiny", metavar="NAMES",
                     help="comma-separated further prefill workloads to time and report (" +
-                         ", ".join(n for n in kda_synth.WORKLOADS if n != "batched") + ")")
+                         ", ".join(n for n in kda_synth.WORKLOADS if n != "batched") + "; empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -523,7 +618,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, kda, torch)
     others = {n: bench_workload(args, kda, torch, n) for n in args.workloads.split(",") if n}
     attn = {n: bench_attn(args, kda, torch, n, dec) for n in args.attn.split(",") if n}
-    bwd = {io: bench_bwd(args, kda, torch, io) for io in ("f32", "bf16")} if args.bwd else None
+    bwd = None if args.no_bwd else {io: bench_bwd(args, kda, torch, io) for io in ("bf16", "f32")}
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
 
     w = pre["workload"]
@@ -546,7 +641,7 @@ def main():
                    "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(pre["achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pre["achieved_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(pre["path"]),
+                     "traffic": stored_traffic(pre["path"], "batched"), "mfma": pre["mfma"],
                      "kernel": PATHS[pre["path"]]["kernel"],
                      "alg_bytes_per_launch": pre["alg_bytes"], "avg_launch_ms": round(pre["ev_ms"], 4)},
         "cpu_baseline": cpu,
@@ -561,8 +656,8 @@ def main():
     if attn:
         line["attn_decode"] = attn
     if bwd is not None:
-        line["backward"] = bwd["f32"]
-        line["backward_bf16_io"] = bwd["bf16"]
+        line["backward"] = bwd["bf16"]
+        line["backward_f32_io"] = bwd["f32"]
     if others:
         line["workloads"] = others
     print(json.dumps(line), flush=True)

@@ -60,9 +60,11 @@ struct FusedPlan {
 };
 
 // Segments of 4 to 1024 chunks of 64 tokens, the longest for which the (segment, head)
-// pairs still number at least 512 (two per compute unit or more: the map and the output
-// launches each run one workgroup per CU, and later ones fill the CUs the short segments
-// at sequence ends free).
+// pairs still number at least 256 (one per compute unit): the maps cost about as much as
+// the segments' own pass, and longer segments leave fewer of them (on 4 packed sequences of
+// 32,768 to 4,096 tokens x 32 heads, 128-chunk segments took 1.37 ms against 1.40 ms at 64
+// and 1.50 ms at 32; on 1 x 4,096 tokens x 16 heads the rule gives 4-chunk segments, 98 us
+// against 112 us at 8 and 149 us at 2).
 FusedPlan fused_plan(int B, int T, int H, bool varlen, int n_seqs) {
     const int64_t pairs = (int64_t)(varlen ? n_seqs : B) * H;
     const int n_seq = varlen ? n_seqs : B;
@@ -71,7 +73,7 @@ FusedPlan fused_plan(int B, int T, int H, bool varlen, int n_seqs) {
     const int64_t chunks = varlen ? ((int64_t)T + 63) / 64 + n_seqs : (int64_t)B * (((int64_t)T + 63) / 64);
     const int64_t work = chunks * H;
     int64_t lc = 4;
-    while (lc < 1024 && lc * 2 * 512 <= work) lc *= 2;
+    while (lc < 1024 && lc * 2 * 256 <= work) lc *= 2;
     const int seg_len = (int)(lc * 64);
     if (!varlen) {
         const int sps = (T + seg_len - 1) / seg_len;
@@ -526,16 +528,49 @@ namespace {
 struct BwdPlan {
     size_t per_bytes, scratch_off, total;
     int n_chunks, n_groups;
+    // the matrix-core pass (bf16, d_k = d_v = 128): offsets of its workspace buffers
+    bool fast;
+    size_t W, U, QO, KtT, Aqk, eg, strong, st, ut, ds, du, discard;
 };
+
+// bf16 I/O with d_k = d_v = 128 takes the matrix-core backward pass (kda_bwd_bf16.hip);
+// everything else the direct one (kda_bwd.hip).
+bool bwd_fast(int d_k, int d_v, int io) { return io == KDA_BF16 && d_k == 128 && d_v == 128; }
 
 int check_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io, BwdPlan *p) {
     if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 1) return KDA_ERR_INVALID_ARG;
     if (chunk != kda::kBwdChunk || !supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
     if (B > 65535 || H > 65535 || (int64_t)B * T * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-    const kda::BwdLayout L{d_k, d_v};
+    *p = BwdPlan{};
     p->n_chunks = (T + chunk - 1) / chunk;
     const int64_t units = (int64_t)B * p->n_chunks * H;
+    p->fast = bwd_fast(d_k, d_v, io);
+    if (p->fast) {
+        // per (chunk, head): the forward's chunk quantities, then S^T, U^T, dS'^T and dU^T (bf16)
+        const size_t u = (size_t)units, C = chunk, e = 2;
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            const size_t at = off;
+            off = round_up(off + bytes, 256);
+            return at;
+        };
+        p->W = take(u * C * d_k * e);
+        p->U = take(u * C * d_v * e);
+        p->QO = take(u * C * d_k * e);
+        p->KtT = take(u * d_k * C * e);
+        p->Aqk = take(u * C * C * e);
+        p->eg = take(u * d_k * 4);
+        p->strong = take(u);
+        p->st = take(u * d_v * d_k * e);
+        p->ut = take(u * d_v * C * e);
+        p->ds = take(u * d_v * d_k * e);
+        p->du = take(u * d_v * C * e);
+        p->discard = take(256);
+        p->total = units > 0 ? off : 0;
+        return KDA_OK;
+    }
+    const kda::BwdLayout L{d_k, d_v};
     p->n_groups = (int)std::min<int64_t>(units, kda::kBwdMaxGroups);
     p->per_bytes = (size_t)L.per_chunk() * sizeof(float);
     p->scratch_off = round_up((size_t)units * p->per_bytes, 256);
@@ -588,6 +623,23 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
             if (overlaps(workspace, p.total, outs[i], out_n[i])) return KDA_ERR_INVALID_ARG;
     }
     if (ntok == 0 && !(dh0 && B > 0)) return KDA_OK;
+    if (p.fast) {
+        unsigned char *w8 = static_cast<unsigned char *>(workspace);
+        kda::BwdFastArgs a{};
+        a.q = q, a.k = k, a.v = v, a.log_alpha = log_alpha, a.beta = beta, a.h0 = h0, a.dout = dout, a.dhT = dhT;
+        a.scale = scale;
+        a.dq = dq, a.dk = dk, a.dv = dv, a.dlog_alpha = dlog_alpha, a.dbeta = dbeta, a.dh0 = dh0;
+        a.H = H;
+        a.map = kda::SeqMap{nullptr, nullptr, nullptr, 0, B, T, kda::kBwdChunk};
+        if (p.total > 0) {
+            a.buf = kda::ChunkBuffers{w8 + p.W, w8 + p.U, w8 + p.QO, w8 + p.KtT, w8 + p.Aqk,
+                                      reinterpret_cast<float *>(w8 + p.eg), w8 + p.strong};
+            a.st = w8 + p.st, a.ut = w8 + p.ut, a.ds = w8 + p.ds, a.du = w8 + p.du, a.discard = w8 + p.discard;
+        }
+        return kda::launch_chunk_bwd_bf16(a, B, B * p.n_chunks, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+                   ? KDA_OK
+                   : KDA_ERR_HIP;
+    }
     float *ws = static_cast<float *>(workspace);
     const kda::BwdArgs a{q,  k,  v,  log_alpha, beta,       h0,    dout, dhT, scale,
                          dq, dk, dv, dlog_alpha, dbeta, dh0, ws,

@@ -406,8 +406,11 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
     constexpr BwdLayout L{DK, DV};
     __shared__ Stage st;
     __shared__ float lg[C * DK], lm[DK], lgam[DK], lbet[C];
-    // row sums for dbeta, column sums for dgamma (dR R and dS' S), by LDS atomics
-    __shared__ float lbacc[C], lgacc[DK], lsacc[DK];
+    // Partial sums, one slot per wave step (64 consecutive elements of a loop) or per thread,
+    // added up in a fixed order at the end: dbeta's three row sums, and dgamma's column sums
+    // of dR R and dS' S. No atomics, so every run gives the same bits.
+    static_assert(C % 64 == 0 && DK % 64 == 0 && DV % 64 == 0 && kBwdThreads % DK == 0, "wave-aligned rows");
+    __shared__ float lb1[C * C / 64], lb2[C * DV / 64], lb3[C * DK / 64], lgp[kBwdThreads], lsp[DK * DV / 64];
     Scr<DK, DV> S(a.scratch + (size_t)blockIdx.x * L.scratch());
     S.G = lg;  // the prefix (later its gradient), gamma, m and beta live in LDS
     S.m = lm;
@@ -421,11 +424,6 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
         const float *cb = a.ws + (size_t)ch * L.per_chunk();
         const float *Tm = cb + L.oT(), *AqkT = cb + L.oAqk(), *W = cb + L.oW(), *Ut = cb + L.oUt();
         const float *Rm = cb + L.oR(), *S0 = cb + L.oS(), *dS1 = cb + L.oDS();
-        for (int i = tid; i < C; i += kBwdThreads) lbacc[i] = 0.f;
-        for (int i = tid; i < DK; i += kBwdThreads) {
-            lgacc[i] = 0.f;
-            lsacc[i] = 0.f;
-        }
         load_chunk<T, DK, DV>(a, b, h, t0, n, S, true);
         __syncthreads();
         chunk_factors<DK, DV>(S);
@@ -464,7 +462,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
             else
                 t = d * S.PN()[idx];
             t = wave_sum(t);
-            if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
+            if ((tid & 63) == 0) lb1[idx >> 6] = t;
         }
         __syncthreads();
         #pragma unroll 2
@@ -473,7 +471,7 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
             const float dbv = S.dBv()[idx];
             if (r < n) static_cast<T *>(a.dv)[row_of(a, b, t0 + r, h) * DV + idx % DV] = from_f32<T>(S.bet[r] * dbv);
             const float t = wave_sum(dbv * S.V()[idx]);
-            if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
+            if ((tid & 63) == 0) lb2[idx >> 6] = t;
         }
         for (int idx = tid; idx < C * C; idx += kBwdThreads) S.dA()[idx] *= S.bet[idx / C];  // diag(beta) dA
         __syncthreads();
@@ -501,18 +499,27 @@ __global__ __launch_bounds__(kBwdThreads) void kda_bwd_chunk_grads_kernel(BwdArg
                 static_cast<T *>(a.dk)[off] = from_f32<T>(bb * dBk * eG + dP * eGm + dN * emG + dR * eR);
             }
             const float t = wave_sum(dBk * kv * eG);
-            if ((tid & 63) == 0) atomicAdd(&lbacc[r], t);
+            if ((tid & 63) == 0) lb3[idx >> 6] = t;
         }
-        atomicAdd(&lgacc[tid % DK], dgr);
+        lgp[tid] = dgr;
         #pragma unroll 2
         for (int idx = tid; idx < DK * DV; idx += kBwdThreads) {  // rowsum(dS' * S), a wave per row
             const float t = wave_sum(dS1[idx] * S0[idx]);
-            if ((tid & 63) == 0) atomicAdd(&lsacc[idx / DV], t);
+            if ((tid & 63) == 0) lsp[idx >> 6] = t;
         }
         __syncthreads();
-        for (int r = tid; r < n; r += kBwdThreads) a.dbeta[row_of(a, b, t0 + r, h)] = lbacc[r];
+        for (int r = tid; r < n; r += kBwdThreads) {
+            float acc = 0.f;
+            for (int j = 0; j < C / 64; ++j) acc += lb1[r * (C / 64) + j];
+            for (int j = 0; j < DV / 64; ++j) acc += lb2[r * (DV / 64) + j];
+            for (int j = 0; j < DK / 64; ++j) acc += lb3[r * (DK / 64) + j];
+            a.dbeta[row_of(a, b, t0 + r, h)] = acc;
+        }
         for (int i = tid; i < DK; i += kBwdThreads) {  // dgamma, then the reverse prefix of dg
-            float acc = fmaf(expf(S.gam[i]), lsacc[i], lgacc[i]);
+            float gs = 0.f, ss = 0.f;
+            for (int j = 0; j < kBwdThreads / DK; ++j) gs += lgp[j * DK + i];
+            for (int j = 0; j < DV / 64; ++j) ss += lsp[i * (DV / 64) + j];
+            float acc = fmaf(expf(S.gam[i]), ss, gs);
             for (int r = C - 1; r >= 0; --r) {
                 acc += S.G[r * DK + i];
                 if (r < n) a.dlog_alpha[row_of(a, b, t0 + r, h) * DK + i] = acc;

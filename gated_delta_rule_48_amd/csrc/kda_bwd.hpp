@@ -50,4 +50,27 @@ struct BwdArgs {
 // hipSuccess or the first launch error.
 hipError_t launch_chunk_bwd(const BwdArgs &a, int dk, int dv, bool bf16, hipStream_t stream);
 
+// The backward pass on the matrix cores (kda_bwd_bf16.hip): bf16 I/O, d_k = d_v = 128,
+// chunk 64. Its workspace holds the forward's chunk quantities (buf, as the split forward
+// pass lays them out) and four bf16 matrices per (chunk, head), fragment-ordered: the
+// state entering the chunk as S^T [d_v][d_k], the corrected writes as U^T [d_v][C], the
+// gradient with respect to the state at the chunk's end as dS'^T [d_v][d_k], and dU^T
+// [d_v][C].
+struct BwdFastArgs {
+    const void *q, *k, *v;  // bf16, as dout and dq, dk, dv
+    const float *log_alpha, *beta, *h0;
+    const void *dout;
+    const float *dhT;
+    float scale;
+    void *dq, *dk, *dv;
+    float *dlog_alpha, *dbeta, *dh0;
+    int H;
+    SeqMap map;
+    ChunkBuffers buf;
+    void *st, *ut, *ds, *du;
+    void *discard;  // 256 bytes
+};
+
+hipError_t launch_chunk_bwd_bf16(const BwdFastArgs &a, int n_seqs, int total_chunks, hipStream_t stream);
+
 }  // namespace kda

@@ -62,12 +62,17 @@ struct PrepArgs {
 struct StateArgs {
     const float *h0;
     float *hT;
-    void *o;
+    void *o;        // null: no outputs (the backward pass runs this kernel for its states only)
     void *discard;  // 64 io-dtype elements of workspace that absorb writes of rows past a sequence end
     int H;
     int xcd_group;  // set by the launcher: map a pair's d_v slices onto one XCD
     SeqMap map;
     ChunkBuffers buf;
+    // Optional (backward pass), per (chunk, head) in the io dtype: the state entering the
+    // chunk as fragment-ordered S^T ([d_v][d_k]: row j = value column j, contraction over key
+    // channels), and the chunk's corrected writes U as fragment-ordered U^T ([d_v][C]).
+    void *st_out;
+    void *ut_out;
 };
 
 struct FusedArgs {

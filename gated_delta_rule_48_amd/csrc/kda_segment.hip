@@ -10,12 +10,17 @@
 // walks each sequence's segments in order, S_in(p + 1) = M(p) S_in(p) + N(p), and the
 // usual instance runs every segment from its S_in in parallel.
 //
-// One workgroup of 4 waves per (sequence, head, 16 value columns): the columns of the
-// state evolve independently. Each step is a 128 x 128 by 128 x 16 product in fp32 on
-// the matrix cores (v_mfma_f32_16x16x4_f32), wave w forming rows 32 w .. 32 w + 31. Each
-// lane reads its share of M(p) straight from memory (the contraction index of operand
-// slot g of product kk is 32 g + kk, so a lane's share of a row is 32 adjacent values),
-// M(p + 1) while step p computes; the 16 columns of S_in stay in LDS between steps. All
+// One workgroup of 8 waves per (sequence, head, 16 value columns): the columns of the
+// state evolve independently. Each step is a 128 x 128 by 128 x 16 product on the matrix
+// cores, wave w forming rows 16 w .. 16 w + 15. M(p) and S_in(p) are fp32; each operand is
+// split as x = hi + lo (hi = x rounded to bf16, lo = the rest rounded to bf16) and the
+// product taken as hi hi' + hi lo' + lo hi' with v_mfma_f32_16x16x32_bf16 (lane l supplies
+// A[l%16][8 (l/16) .. + 7] and B[8 (l/16) .. + 7][l%16]), fp32 accumulation: about 16
+// significant bits per product, at a fifth of the matrix-core time of fp32 instructions.
+// Each lane reads its share of M(p) and N(p) straight from memory, those of step p + 1
+// while step p computes; the 16 columns of S_in stay in LDS (transposed, two buffers used
+// in turn, so one barrier per step). The 8 workgroups of one (sequence, head) run on one
+// XCD (block ids 8 apart), so M(p) is fetched into one L2 and read there 8 times. All
 // buffers hold states in channel order, row-major (row = key channel), like h0 and hT.
 
 #include "kda_internal.hpp"
@@ -24,13 +29,28 @@ namespace kda {
 namespace {
 
 constexpr int kD = 128;
+constexpr int kChainThreads = 512;
+constexpr int kStPitch = kD + 4;  // floats per row of the transposed S_in buffers
 
-__global__ __launch_bounds__(256) void kda_segment_chain_kernel(FusedArgs a) {
-    __shared__ __align__(16) float Sb[kD * 16];
+// hi = bf16(x), lo = bf16(x - hi) for 8 values
+__device__ __forceinline__ void split_hi_lo(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = static_cast<bf16>(x0[e]);
+        lo[e] = static_cast<bf16>(x0[e] - static_cast<float>(hi[e]));
+        hi[e + 4] = static_cast<bf16>(x1[e]);
+        lo[e + 4] = static_cast<bf16>(x1[e] - static_cast<float>(hi[e + 4]));
+    }
+}
+
+__global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedArgs a) {
+    __shared__ __align__(16) float St[2][16 * kStPitch];  // St[b][n * kStPitch + k] = S_in[k][n]
     const int H = a.H;
-    const int pair = blockIdx.x >> 3, cb = blockIdx.x & 7;
+    // blocks are dealt round-robin to the 8 XCDs: block id = xcd + 8 (cb + 8 q), pair = xcd + 8 q
+    const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    const int cb = rest & 7, pair = xcd + 8 * (rest >> 3);
+    if (pair >= a.n_seqs * H) return;
     const int s = pair / H, h = pair % H;
-    if (s >= a.n_seqs) return;
     const int g0 = a.cu_seqlens ? a.seg_off[s] : s * a.segs_per_seq;
     const int P = a.cu_seqlens ? a.seg_off[s + 1] - g0 : a.segs_per_seq;
     if (P <= 1) return;
@@ -43,65 +63,72 @@ __global__ __launch_bounds__(256) void kda_segment_chain_kernel(FusedArgs a) {
     {
         const float *N0 = map_of(0) + DD;
         float *S1 = state_of(1);
-        for (int e = tid; e < kD * 16; e += 256) {
+        for (int e = tid; e < kD * 16; e += kChainThreads) {
             const int r = e >> 4, c = e & 15;
             const float x = N0[r * kD + 16 * cb + c];
-            Sb[e] = x;
+            St[1][c * kStPitch + r] = x;
             S1[r * kD + 16 * cb + c] = x;
         }
     }
-    // this lane's A operands of M(p): rows 32 w + 16 t + n, columns 32 g .. 32 g + 31, in two
-    // sets used in turn (step p computes from one while M(p + 1) arrives in the other)
-    f32x4 amA[2][8], amB[2][8];
-    auto fetch = [&](int p, f32x4 (&dst)[2][8]) {
+    // this lane's A operands of M(p) (row 16 w + n, contraction indices 32 kb + 8 g .. + 7) and
+    // the four entries of N(p) its outputs add, in two sets used in turn
+    f32x4 amA[4][2], amB[4][2];
+    float nA[4], nB[4];
+    auto fetch = [&](int p, f32x4 (&am)[4][2], float (&nd)[4]) {
         const float *M = map_of(p);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                dst[t][j] = *reinterpret_cast<const f32x4 *>(M + (32 * w + 16 * t + n) * kD + 32 * g + 4 * j);
+            for (int j = 0; j < 2; ++j)
+                am[kb][j] = *reinterpret_cast<const f32x4 *>(M + (16 * w + n) * kD + 32 * kb + 8 * g + 4 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nd[i] = M[DD + (16 * w + 4 * g + i) * kD + 16 * cb + n];
     };
-    auto step = [&](int p, const f32x4 (&am)[2][8]) {
-        __syncthreads();  // Sb holds S_in(p)
-        const float *N = map_of(p) + DD;
-        f32x4 acc[2];
+    // S_in(p + 1) = M(p) S_in(p) + N(p); S_in(p) is in buffer p & 1
+    auto step = [&](int p, const f32x4 (&am)[4][2], const float (&nv)[4]) {
+        __syncthreads();  // S_in(p) complete; every wave is done with the other buffer
+        const float *src = St[p & 1];
+        f32x4 hh = {0.f, 0.f, 0.f, 0.f}, hl = hh, lh = hh;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int kk = 4 * j + e;
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[t][j][e], Sb[(32 * g + kk) * 16 + n], acc[t], 0, 0, 0);
-                }
+        for (int kb = 0; kb < 4; ++kb) {
+            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(src + n * kStPitch + 32 * kb + 8 * g);
+            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(src + n * kStPitch + 32 * kb + 8 * g + 4);
+            bf16x8 ah, al, bh, bl;
+            split_hi_lo(am[kb][0], am[kb][1], ah, al);
+            split_hi_lo(b0, b1, bh, bl);
+            hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, hh, 0, 0, 0);
+            hl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, hl, 0, 0, 0);
+            lh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, lh, 0, 0, 0);
         }
-        __syncthreads();  // every wave has read Sb
+        float *dst = St[(p + 1) & 1];
         float *Sn = state_of(p + 1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 32 * w + 16 * t + 4 * g + i;
-                const float x = acc[t][i] + N[r * kD + 16 * cb + n];
-                Sb[r * 16 + n] = x;
-                Sn[r * kD + 16 * cb + n] = x;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * g + i;
+            const float x = hh[i] + (hl[i] + lh[i]) + nv[i];
+            dst[n * kStPitch + r] = x;
+            Sn[r * kD + 16 * cb + n] = x;
+        }
     };
-    if (P > 2) fetch(1, amA);
+    // Every fetch is unconditional (past the last step a set re-reads map P - 1, which lies
+    // inside the workspace and is not used), so that the number of loads in flight is the
+    // same on every path and each step waits for exactly its own operands.
+    if (P <= 2) return;
+    fetch(1, amA, nA);
     for (int p = 1; p + 1 < P; p += 2) {
-        if (p + 2 < P) fetch(p + 1, amB);
-        step(p, amA);
+        fetch(min(p + 1, P - 1), amB, nB);
+        step(p, amA, nA);
         if (p + 2 >= P) break;
-        if (p + 3 < P) fetch(p + 2, amA);
-        step(p + 1, amB);
+        fetch(min(p + 2, P - 1), amA, nA);
+        step(p + 1, amB, nB);
     }
 }
 
 }  // namespace
 
 hipError_t launch_segment_chain(const FusedArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(kda_segment_chain_kernel, dim3(a.n_seqs * a.H * 8), dim3(256), 0, stream, a);
+    const int groups = (a.n_seqs * a.H + 7) / 8;  // of 8 (sequence, head) pairs, one per XCD
+    hipLaunchKernelGGL(kda_segment_chain_kernel, dim3(groups * 64), dim3(kChainThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -54,7 +54,9 @@ __device__ __forceinline__ void frag_store4(T *base, int n, int k0, f32x4 v, int
     }
 }
 
-template <int C, int DK, int DV, int DVS, typename T>
+// kRecord: the backward pass's instance, which also records S^T and U^T of every chunk
+// (StateArgs::st_out, ut_out) and writes no outputs.
+template <int C, int DK, int DV, int DVS, typename T, bool kRecord>
 __global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
     typedef Frag<T> F;
     typedef typename F::Vec V;
@@ -161,10 +163,26 @@ __global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
             op.ut[nt] = *reinterpret_cast<const R4 *>(Ug + acc_tile_off(w, (col0 >> 4) + nt, DV));
     };
 
+    // A fragment-ordered [DVS][K] slice in LDS (rows = this workgroup's value columns) to
+    // rows col0 .. of the [DV][K] matrix of chunk ci in global memory: whole groups of 64
+    // lanes x 16 bytes (EPL values of T).
+    auto copy_slice = [&](const T *src, void *dst_base, int K, int ci) {
+        static_assert(F::EPL * sizeof(T) == 16, "one 16-byte share per lane");
+        const size_t jh = (size_t)(c_begin + ci) * H + h;
+        T *dst = static_cast<T *>(dst_base) + jh * DV * K;
+        const int ngroups = (K / F::KG) * (DVS / 16);
+        for (int gi = w; gi < ngroups; gi += NW) {
+            const int kg = gi / (DVS / 16), rb = gi % (DVS / 16);
+            *reinterpret_cast<uint4 *>(dst + (((size_t)kg * (DV / 16) + (col0 >> 4) + rb) * 64 + l) * F::EPL) =
+                *reinterpret_cast<const uint4 *>(src + ((size_t)gi * 64 + l) * F::EPL);
+        }
+    };
+
     // One chunk: U = U~ - W S, O = QO S + Aqk U, S <- exp(gamma) S + KtT U.
     auto chunk_step = [&](int ci, const Ops &op) {
         const int t0 = tb + ci * C;
         const int L = min(C, te - t0);
+        if constexpr (kRecord) copy_slice(St, a.st_out, DK, ci);  // S^T entering the chunk
         f32x4 accU[NTL], accO[NTL];
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
@@ -180,10 +198,12 @@ __global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
             frag_store4<T>(Ut, 16 * nt + acc_col(), 16 * w + acc_row(0), accU[nt], DVS);
         }
         __syncthreads();  // U^T complete; every wave is done reading S^T
+        if constexpr (kRecord) copy_slice(Ut, a.ut_out, C, ci);
 
         // O += Aqk U (zero above the diagonal; the groups past it are skipped)
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) {
+            if constexpr (kRecord) break;
 #pragma unroll
             for (int kg = 0; kg < NCG; ++kg)
                 if (kg <= kgq) accO[nt] = F::mma(accO[nt], op.af[kg], frag_load<T>(Ut, kg, nt, DVS));
@@ -249,7 +269,13 @@ __global__ __launch_bounds__(4 * C) void kda_state_kernel(StateArgs a) {
 
 template <int C, int DK, int DV, int DVS, typename T>
 hipError_t launch_state_t(const StateArgs &a, int n_seqs, hipStream_t stream) {
-    auto kern = kda_state_kernel<C, DK, DV, DVS, T>;
+    auto kern = kda_state_kernel<C, DK, DV, DVS, T, false>;
+    if (a.st_out) {  // recording instance: built for the backward pass's shape only
+        if constexpr (C == 64 && DK == 128 && DV == 128 && sizeof(T) == 2)
+            kern = kda_state_kernel<C, DK, DV, DVS, T, true>;
+        else
+            return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL(kern, dim3(n_seqs * a.H * (DV / DVS)), dim3(4 * C), 0, stream, a);
     return hipGetLastError();
 }

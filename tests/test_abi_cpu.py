@@ -62,7 +62,7 @@ def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
         if pairs < 256:
             chunks = (T + 63) // 64 + n_seqs if n_seqs else B * ((T + 63) // 64)
             lc = 4
-            while lc < 1024 and lc * 2 * 512 <= chunks * H:
+            while lc < 1024 and lc * 2 * 256 <= chunks * H:
                 lc *= 2
             seg_len = lc * 64
             if n_seqs:

@@ -69,3 +69,29 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_algorithmic_flops_of_the_batched_workload():
+    # per chunk of 64 rows and head at d = 128: 3 C^2 dk + 2 C^2 dv + 3 C dk dv multiply-adds
+    bench = _bench()
+    macs = 3 * 64 * 64 * 128 + 2 * 64 * 64 * 128 + 3 * 64 * 128 * 128
+    assert macs == 5_767_168
+    assert bench.prefill_algorithmic_flops((8192,) * 8, 32, 128, 128, 64) == 2 * macs * 128 * 8 * 32
+    # a ragged sequence counts its last partial chunk whole
+    assert bench.prefill_algorithmic_flops((65, 1), 1, 128, 128, 64) == 2 * macs * 3
+
+
+def test_stored_counters_follow_the_sources(tmp_path):
+    bench = _bench()
+    info = bench.PATHS["segmented"]
+    (tmp_path / "profiles").mkdir()
+    f = tmp_path / "profiles" / info["counters"]
+    digest = bench.sources_digest(info["sources"])
+    f.write_text(f"traffic_bytes_per_launch[varlen]: 123456\nmfma_busy_frac[varlen]: 0.25\n"
+                 f"sources_sha256: {digest}\n")
+    bench.ROOT = str(tmp_path)
+    assert bench.stored_traffic("segmented", "varlen") == 123456
+    assert bench.stored_counter("segmented", "varlen", "mfma_busy_frac") == 0.25
+    assert bench.stored_traffic("segmented", "prefill") is None   # no line for it
+    f.write_text(f"traffic_bytes_per_launch[varlen]: 123456\nsources_sha256: {'0' * 64}\n")
+    assert bench.stored_traffic("segmented", "varlen") is None    # sources changed since

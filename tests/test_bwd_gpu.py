@@ -72,6 +72,20 @@ def test_bwd_shapes(dk, dv, T):
     _check("bwd", 2, T, 2, dk, dv, seed=T + dk + dv)
 
 
+# bf16 I/O with d_k = d_v = 128 runs the matrix-core pass (bf16 products, kda_bwd_bf16.hip):
+# ragged and exact chunk ends, one token, several heads and sequences
+@pytest.mark.parametrize("B,T,H", [(1, 1, 1), (2, 64, 2), (1, 65, 3), (3, 200, 2), (2, 333, 1)])
+def test_bwd_bf16_matrix_core_shapes(B, T, H):
+    _check("bwd-bf16-mc", B, T, H, 128, 128, seed=7 * T + B + H, io="bf16")
+
+
+def test_bwd_bf16_matrix_core_options():
+    _check("bwd-bf16-mc no-h0", 2, 130, 2, 128, 128, seed=11, h0=False, io="bf16")
+    _check("bwd-bf16-mc no-dhT", 2, 130, 2, 128, 128, seed=12, dhT=False, io="bf16")
+    _check("bwd-bf16-mc strong", 2, 130, 2, 128, 128, gates="strong", seed=13, io="bf16")
+    _check("bwd-bf16-mc weak", 1, 190, 2, 128, 128, gates="weak", seed=14, io="bf16")
+
+
 def test_bwd_strong_gates_and_short_sequences():
     _check("strong", 2, 130, 2, 128, 128, gates="strong", seed=3)
     _check("short", 3, 1, 2, 64, 64, seed=4)
@@ -122,3 +136,58 @@ def test_bwd_full_size_sampled():
         say(f"[bwd-full] (b={b}, h={h}) rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
         for n, e in errs.items():
             assert e <= TOL["f32"], (n, e)
+
+
+def test_bwd_full_size_sampled_bf16():
+    """The matrix-core backward at the batched workload's shape (B=8, T=8192, H=32, d=128,
+    bf16 I/O, weak gates, as the bench times it): the whole batch on the GPU, the oracle on
+    two sampled (sequence, head) pairs over their full length."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    w = kda_synth.WORKLOADS["batched"]
+    B, T, H, d = len(w.seqlens), w.seqlens[0], w.H, w.dk
+    say(f"[bwd-full-bf16] B={B} T={T} H={H} d={d} bf16 gates={w.gates}")
+    x = kda_synth.gen_sequences(w.seqlens, H, d, d, "bf16", w.gates, "zero", w.seed)
+    gr = kda_synth.gen_grad_outputs(B, T, H, d, d, w.seed)
+    dout_np = kda_synth.round_bf16(gr["dout"])
+    t = {n: torch.from_numpy(x[n].reshape((B, T) + x[n].shape[1:])).cuda()
+         for n in ("q", "k", "v", "log_alpha", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    dout, dhT = torch.from_numpy(dout_np).cuda().to(torch.bfloat16), torch.from_numpy(gr["dhT"]).cuda()
+    out = kda.chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], dout, scale=d ** -0.5, dhT=dhT)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = lambda a: a[b:b + 1, :, h:h + 1].float().cpu().numpy()  # noqa: E731
+        ref = oracle.kda_backward_reference(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["log_alpha"]),
+                                            sl(t["beta"]), d ** -0.5, dout_np[b:b + 1, :, h:h + 1],
+                                            dhT=gr["dhT"][b:b + 1, h:h + 1])
+        errs = {n: rel_l2(sl(out[i]), ref[n]) for i, n in enumerate(NAMES[:5])}
+        say(f"[bwd-full-bf16] (b={b}, h={h}) rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], (n, e)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_bitwise_deterministic(io):
+    """Every reduction in the backward runs in a fixed order (no atomics), so two calls on
+    the same inputs give the same bits, also when the second call's workspace starts out
+    holding other values."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    B, T, H, d = 2, 333, 4, 128
+    say(f"[bwd-det] B={B} T={T} H={H} d={d} io={io}")
+    x = _inputs(B, T, H, d, d, "main", 41, io=io)
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).cuda() for n, a in x.items()}
+    if io == "bf16":
+        for n in ("q", "k", "v", "dout"):
+            t[n] = t[n].to(torch.bfloat16)
+    need = kda.chunk_bwd_workspace_bytes(B, T, H, d, d, io=kda.KDA_BF16 if io == "bf16" else kda.KDA_F32)
+    runs = []
+    for fill in (0, 0x7F):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        runs.append(kda.chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["dout"], h0=t["h0"],
+                                  dhT=t["dhT"], workspace=ws))
+    torch.cuda.synchronize()
+    for n, a, b in zip(NAMES, *runs):
+        assert torch.equal(a, b), n

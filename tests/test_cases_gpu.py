@@ -11,9 +11,10 @@ bf16 pass (or the example's own tolerance where the page rounds, as "0.9^20 = 0.
 is also held to the usual parity bar against the oracle on the rounded inputs.
 
 Colliding keys: kda_synth.gen_key_repeats, exact repeats among three keys per head and
-near-duplicates (cosine about 0.99), beta = 1, on the fused pass, the split pass (bf16 at
-chunks 64 and 128, fp32) and the decode step, against the oracle with the per-head and
-per-row bounds of kda_testlib.
+near-duplicates (cosine about 0.99), beta = 1, on the fused pass (one workgroup per
+(sequence, head), and with segments), the split pass (bf16 at d = 64, fp32 at d = 128,
+chunks 64 and 128) and the decode step, against the oracle with the per-head and per-row
+bounds of kda_testlib.
 """
 import json
 import os
@@ -144,13 +145,25 @@ def test_colliding_keys_fused(kind):
 
 
 @pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
-def test_colliding_keys_split(kind, io, chunk):
-    x = kda_synth.gen_key_repeats([300, 129, 64], 4, 128, 128, io, kind, seed=302 + chunk)
-    say(f"[keys {kind}] split pass, {io}, C={chunk}, beta=1")
+@pytest.mark.parametrize("io,chunk,d", [("bf16", 64, 64), ("bf16", 128, 64), ("f32", 64, 128), ("f32", 128, 128)])
+def test_colliding_keys_split(kind, io, chunk, d):
+    """The split pass: fp32 at d = 128, and bf16 at d = 64 (bf16 at d = 128 takes the fused pass)."""
+    x = kda_synth.gen_key_repeats([300, 129, 64], 4, d, d, io, kind, seed=302 + chunk)
+    say(f"[keys {kind}] split pass, {io}, d={d}, C={chunk}, beta=1")
     o, hT = run_packed(x, io, chunk)
     o_ref, h_ref, _ = oracle_run(x)
-    assert_parity(o, o_ref, hT, h_ref, io, f"keys {kind} split {io} C{chunk}", cu=x["cu_seqlens"])
+    assert_parity(o, o_ref, hT, h_ref, io, f"keys {kind} split {io} d{d} C{chunk}", cu=x["cu_seqlens"])
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_colliding_keys_segmented(kind):
+    """bf16, d = 128, 12 (sequence, head) pairs: the fused pass with segments (the 300-token
+    sequence is longer than one segment)."""
+    x = kda_synth.gen_key_repeats([300, 129, 64], 4, 128, 128, "bf16", kind, seed=304)
+    say(f"[keys {kind}] fused pass with segments, bf16, beta=1")
+    o, hT = run_packed(x, "bf16", 64)
+    o_ref, h_ref, _ = oracle_run(x)
+    assert_parity(o, o_ref, hT, h_ref, "bf16", f"keys {kind} segmented", cu=x["cu_seqlens"])
 
 
 @pytest.mark.parametrize("kind", KINDS)

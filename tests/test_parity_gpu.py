@@ -280,30 +280,36 @@ def test_decode_workload_1024_steps():
     assert_parity(seq["o"], o_ref, st_got[None], h_ref, "bf16", "decode-1024")
 
 
-# ----------------------------------------------------------------------------- fused pass
-# Uniform batches with at least 256 (sequence, head) pairs and chunk 64 take the
-# fused pass (one workgroup per pair); the cases below have B * H = 256.
+# ----------------------------------------------------------------------------- 256-pair batches
+# Uniform batches of B * H = 256 (sequence, head) pairs: bf16 with d_k = d_v = 128 takes the
+# fused pass (one workgroup per pair), every other dtype and size the split pass.
+
+def _pass(io, dk, dv):
+    return "fused" if io == "bf16" and dk == dv == 128 else "split"
+
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
 @pytest.mark.parametrize("T", [200, 1, 64])
-def test_fused_path(io, dk, dv, T):
+def test_uniform_batch_256_pairs(io, dk, dv, T):
     x = gen([T, T], 128, dk, dv, io, seed=7 * T + dk + dv)
-    _check(x, io, 64, f"fused T={T}", varlen=False, B=2, T=T)
+    _check(x, io, 64, f"{_pass(io, dk, dv)} T={T}", varlen=False, B=2, T=T)
 
 
-@pytest.mark.parametrize("io,path", [("f32", "split"), ("bf16", "split"), ("bf16", "fused")])
+@pytest.mark.parametrize("io,path", [("f32", "split"), ("bf16", "split"), ("bf16", "fused"), ("bf16", "few-pairs")])
 def test_strong_decay(io, path):
     """Fast-forgetting gates ("strong": chunk sums of log alpha near -117 on average and
-    down to about -150, inside the documented >= -170 limit). The in-chunk decay factors
-    then span up to e^(+-75) and the state factors reach e^(-75) per chunk: products of
-    such factors must be formed in an order that stays inside the fp32 range."""
+    down to about -150). The in-chunk decay factors then span up to e^(+-75) and the state
+    factors reach e^(-75) per chunk: products of such factors must be formed in an order
+    that stays inside the fp32 range. Passes: split (fp32 at d = 128, bf16 at d = 64), fused
+    (256 pairs) and fused with few pairs (16, one workgroup each)."""
     if path == "fused":
         x = gen([200, 200], 128, 128, 128, io, gates="strong", seed=91)
         _check(x, io, 64, "strong fused", varlen=False, B=2, T=200)
     else:
-        x = gen([200, 130], 8, 128, 128, io, gates="strong", seed=92)
-        _check(x, io, 64, "strong split")
+        d = 64 if (io == "bf16" and path == "split") else 128
+        x = gen([200, 130], 8, d, d, io, gates="strong", seed=92)
+        _check(x, io, 64, f"strong {path}")
 
 
 def test_fused_path_no_h0():
@@ -313,41 +319,49 @@ def test_fused_path_no_h0():
     assert_parity(o, o_ref, hT, h_ref, "bf16", "fused no h0", cu=x["cu_seqlens"])
 
 
-def test_fused_matches_split():
-    """The same bf16 batch through the fused pass ([B, T, H, d]) and through the
-    split pass (packed with cu_seqlens): two schedules of the same arithmetic,
-    both within tolerance of the oracle and close to each other."""
-    x = gen([300, 300], 128, 128, 128, "bf16", seed=79)
-    of, hf = run_packed(x, "bf16", 64, varlen=False, B=2, T=300)
-    os_, hs = run_packed(x, "bf16", 64, varlen=True)
+def test_fused_matches_segmented():
+    """The same sequence through the fused pass in one workgroup per (sequence, head) (as
+    part of a 256-pair batch) and alone, 128 pairs, where the pass cuts its 600 tokens into
+    segments (maps, their composition, then the segments): two schedules of the same
+    arithmetic, both within tolerance of the oracle and close to each other."""
+    x = gen([600, 600], 128, 128, 128, "bf16", seed=79)
+    of, hf = run_packed(x, "bf16", 64, varlen=False, B=2, T=600)
+    one = dict(x, q=x["q"][:600], k=x["k"][:600], v=x["v"][:600], log_alpha=x["log_alpha"][:600],
+               beta=x["beta"][:600], h0=None if x["h0"] is None else x["h0"][:1],
+               cu_seqlens=np.array([0, 600], np.int32))
+    og, hg = run_packed(one, "bf16", 64, varlen=False, B=1, T=600)
     o_ref, h_ref, _ = oracle_run(x)
-    for o, hT, n in ((of, hf, "fused"), (os_, hs, "split")):
-        assert_parity(o, o_ref, hT, h_ref, "bf16", f"fused vs split: {n}", cu=x["cu_seqlens"])
-    assert rel_l2(of, os_) <= 1e-2 and rel_l2(hf, hs) <= 1e-2
+    assert_parity(of, o_ref, hf, h_ref, "bf16", "fused vs segmented: fused", cu=x["cu_seqlens"])
+    assert_parity(og, o_ref[:600], hg, h_ref[:1], "bf16", "fused vs segmented: segmented", cu=one["cu_seqlens"])
+    assert rel_l2(of[:600], og) <= 1e-2 and rel_l2(hf[:1], hg) <= 1e-2
 
 
 # ----------------------------------------------------------------------------- gate kinds
 
 @pytest.mark.parametrize("gate", ["head", "none"])
 @pytest.mark.parametrize("io,path,chunk", [("f32", "split", 64), ("bf16", "split", 64), ("bf16", "split", 128),
-                                           ("bf16", "fused", 64)])
+                                           ("bf16", "fused", 64), ("bf16", "few-pairs", 128)])
 def test_gate_kinds(gate, io, path, chunk):
     """kda_chunk_fwd_gated with one decay per token and head (Gated DeltaNet) and with
     none (DeltaNet): the oracle runs the same recurrence with that decay on every key
-    channel, or with log alpha = 0."""
+    channel, or with log alpha = 0. Passes: split (fp32 at d = 128, bf16 at d = 64), fused
+    (256 pairs) and fused with few pairs (12)."""
     seed = {"head": 101, "none": 102}[gate] + chunk
     if path == "fused":
         x = with_gate(gen([200, 200], 128, 128, 128, io, seed=seed), gate)
         _check(x, io, chunk, f"{gate} fused", varlen=False, B=2, T=200, gate=gate)
     else:
-        x = with_gate(gen([200, 130, 1], 4, 128, 128, io, seed=seed), gate)
-        _check(x, io, chunk, f"{gate} split", gate=gate)
+        d = 64 if (io == "bf16" and path == "split") else 128
+        x = with_gate(gen([200, 130, 1], 4, d, d, io, seed=seed), gate)
+        _check(x, io, chunk, f"{gate} {path}", gate=gate)
 
 
 @pytest.mark.parametrize("path", ["split", "fused"])
 def test_head_gate_equals_broadcast_channel_gate(path):
-    """A per-head decay and the same decay given for every key channel: one arithmetic."""
-    x = with_gate(gen([150, 150], 128, 128, 128, "bf16", seed=111), "head")
+    """A per-head decay and the same decay given for every key channel: one arithmetic
+    (split pass: bf16 at d = 64; fused pass: d = 128)."""
+    d = 64 if path == "split" else 128
+    x = with_gate(gen([150, 150], 128, d, d, "bf16", seed=111), "head")
     kw = dict(varlen=False, B=2, T=150) if path == "fused" else dict(varlen=True)
     oh, hh = run_packed(x, "bf16", 64, gate="head", **kw)
     oc, hc = run_packed(x, "bf16", 64, gate="channel", **kw)
@@ -374,17 +388,20 @@ def _preact_case(x, io, seed):
 
 @pytest.mark.parametrize("qk_norm", [False, True])
 @pytest.mark.parametrize("io,path,chunk", [("f32", "split", 64), ("bf16", "split", 64), ("bf16", "split", 128),
-                                           ("f32", "split", 128), ("bf16", "fused", 64)])
+                                           ("f32", "split", 128), ("bf16", "fused", 64), ("bf16", "few-pairs", 64)])
 def test_preact_gates(io, path, chunk, qk_norm):
     """kda_chunk_fwd_preact: log alpha = -exp(A_log) softplus(a + dt_bias) and beta =
     sigmoid(b) formed in the kernels, and with qk_norm q, k = silu(.) / ||silu(.)|| per
-    row too; the oracle runs the recurrence on the same gates (and q, k) formed in fp64."""
+    row too; the oracle runs the recurrence on the same gates (and q, k) formed in fp64.
+    Passes: split (fp32 at d = 128, bf16 at d = 64), fused (256 pairs), fused with few
+    pairs (12)."""
     import torch
     import gated_delta_rule_48_amd as kda
     if path == "fused":
         x = gen([200, 200], 128, 128, 128, io, seed=121)
     else:
-        x = gen([200, 130, 1], 4, 128, 128, io, seed=122 + chunk)
+        d = 64 if (io == "bf16" and path == "split") else 128
+        x = gen([200, 130, 1], 4, d, d, io, seed=122 + chunk)
     p, y = _preact_case(x, io, seed=123 + chunk)
     if qk_norm:
         T, H, dk = x["q"].shape

@@ -53,6 +53,12 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ int fresh_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // x, opaque to the compiler: an exponential of it is computed again instead of being kept
 // in a register from an earlier phase.
 __device__ __forceinline__ float fresh(float x) {
@@ -90,22 +96,36 @@ __device__ __forceinline__ void prod(f32x4 (&acc)[NU], const bf16 *A, int RA, in
     }
 }
 
-// A fragment-ordered [R][K] bf16 matrix in global memory, transposed into F(X^T) ([K][R])
-// in LDS: thread slots of 8 values (one row, 8 contraction indices) over the whole matrix.
-template <int R, int K, int NT>
-__device__ __forceinline__ void transpose_into(bf16 *dst, const bf16 *src, bool negate) {
-    constexpr int slots = R * K / 8;
-    const int l = threadIdx.x & 63, hi = l >> 4;
-    for (int u = threadIdx.x; u < slots; u += NT) {
-        const int gi = u >> 6, kg = gi / (R / 16), rb = gi % (R / 16);
-        const int r = 16 * rb + (l & 15);
-        V8 x = *reinterpret_cast<const V8 *>(src + (size_t)u * 8);
+// One thread's share of a fragment-ordered [R][K] bf16 matrix: slots tid, tid + NT, ...
+// (whole 16-byte operand shares), and those shares written transposed into F(X^T) ([K][R])
+// in LDS.
+template <int R, int K, int NT> struct Shares {
+    static constexpr int N = R * K / 8 / NT;
+    V8 x[N];
+    __device__ __forceinline__ void load(const bf16 *src) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float f = static_cast<float>(x[j]);
-            dst[frag_off<bf16>(frag_chan<bf16>(kg, hi, j), r, K)] = static_cast<bf16>(negate ? -f : f);
+        for (int m = 0; m < N; ++m) x[m] = *reinterpret_cast<const V8 *>(src + ((size_t)threadIdx.x + NT * m) * 8);
+    }
+    __device__ __forceinline__ void store_transposed(bf16 *dst, bool negate) const {
+        const int l = threadIdx.x & 63, hi = l >> 4;
+#pragma unroll
+        for (int m = 0; m < N; ++m) {
+            const int gi = (threadIdx.x + NT * m) >> 6, kg = gi / (R / 16), rb = gi % (R / 16);
+            const int r = 16 * rb + (l & 15);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float f = static_cast<float>(x[m][j]);
+                dst[frag_off<bf16>(frag_chan<bf16>(kg, hi, j), r, K)] = static_cast<bf16>(negate ? -f : f);
+            }
         }
     }
+};
+
+template <int R, int K, int NT>
+__device__ __forceinline__ void transpose_into(bf16 *dst, const bf16 *src, bool negate) {
+    Shares<R, K, NT> sh;
+    sh.load(src);
+    sh.store_transposed(dst, negate);
 }
 
 // ------------------------------------------------------------------ (3) reverse recursion
@@ -146,8 +166,39 @@ __global__ __launch_bounds__(256) void kda_bwd_rev_kernel(BwdFastArgs a) {
     const int n_c = (te - tb + kC - 1) / kC;
     const bf16 *dout = static_cast<const bf16 *>(a.dout);
 
-    for (int ci = n_c - 1; ci >= 0; --ci) {
+    // One chunk's operands as loaded (this thread's shares), the next chunk's in flight while
+    // one computes. Every load is unconditional (rows past the sequence's end re-read its last
+    // row and are then zeroed), so that the compiler waits for exactly the set it needs.
+    struct Ops {
+        Shares<kC, kC, 256> aq;
+        Shares<kD, kC, 256> kt;
+        Shares<kC, kD, 256> qo, wm;
+        V8 o[4];
+        f32x4 eg0, eg1;
+    };
+    auto load_ops = [&](int ci, Ops &op) {
         const int t0 = tb + ci * kC, L_rows = min(kC, te - t0);
+        const size_t jh = (size_t)(c_begin + ci) * H + h;
+        op.aq.load(static_cast<const bf16 *>(a.buf.Aqk) + jh * kC * kC);
+        op.kt.load(static_cast<const bf16 *>(a.buf.KtT) + jh * kD * kC);
+        op.qo.load(static_cast<const bf16 *>(a.buf.QO) + jh * kC * kD);
+        op.wm.load(static_cast<const bf16 *>(a.buf.W) + jh * kC * kD);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {  // dO: 8 adjacent value columns of one row per share
+            const int u = threadIdx.x + 256 * m, r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
+            op.o[m] = *reinterpret_cast<const V8 *>(dout + ((size_t)(t0 + min(r, L_rows - 1)) * H + h) * kD + j0);
+            if (r >= L_rows) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) op.o[m][e] = static_cast<bf16>(0.f);
+            }
+        }
+        op.eg0 = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * (2 * w) + 4 * (l >> 4));
+        op.eg1 = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * (2 * w + 1) + 4 * (l >> 4));
+    };
+    Ops op;
+    if (n_c > 0) load_ops(n_c - 1, op);
+
+    for (int ci = n_c - 1; ci >= 0; --ci) {
         const size_t jh = (size_t)(c_begin + ci) * H + h;
         // dS' (the gradient at this chunk's end) into LDS
 #pragma unroll
@@ -155,25 +206,18 @@ __global__ __launch_bounds__(256) void kda_bwd_rev_kernel(BwdFastArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) store_t(L.dSt, 2 * w + sb, nt, acc[sb][nt], kD);
         // this chunk's operands, transposed
-        transpose_into<kC, kC, 256>(L.AqT, static_cast<const bf16 *>(a.buf.Aqk) + jh * kC * kC, false);
-        transpose_into<kD, kC, 256>(L.Rf, static_cast<const bf16 *>(a.buf.KtT) + jh * kD * kC, false);
-        transpose_into<kC, kD, 256>(L.QOt, static_cast<const bf16 *>(a.buf.QO) + jh * kC * kD, false);
-        transpose_into<kC, kD, 256>(L.Wn, static_cast<const bf16 *>(a.buf.W) + jh * kC * kD, true);
-        // dO rows (zero past the sequence's end): 8 adjacent value columns per thread and step
-        for (int u = threadIdx.x; u < kC * kD / 8; u += 256) {
-            const int r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
-            V8 x;
-            if (r < L_rows) {
-                x = *reinterpret_cast<const V8 *>(dout + ((size_t)(t0 + r) * H + h) * kD + j0);
-            } else {
+        op.aq.store_transposed(L.AqT, false);
+        op.kt.store_transposed(L.Rf, false);
+        op.qo.store_transposed(L.QOt, false);
+        op.wm.store_transposed(L.Wn, true);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(0.f);
-            }
+        for (int m = 0; m < 4; ++m) {
+            const int u = threadIdx.x + 256 * m, r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) L.dOt[frag_off<bf16>(j0 + e, r, kD)] = x[e];
+            for (int e = 0; e < 8; ++e) L.dOt[frag_off<bf16>(j0 + e, r, kD)] = op.o[m][e];
         }
-        const f32x4 eg0 = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * (2 * w) + 4 * (l >> 4));
-        const f32x4 eg1 = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * (2 * w + 1) + 4 * (l >> 4));
+        const f32x4 eg0 = op.eg0, eg1 = op.eg1;
+        load_ops(ci > 0 ? ci - 1 : 0, op);  // the next chunk's (the first re-reads itself)
         __syncthreads();
         // record dS'^T of this chunk
         {
@@ -259,7 +303,8 @@ constexpr int gam = bet + 4 * kC;          // fp32 [128]
 constexpr int bpart = gam + 4 * kD;        // fp32 [3 terms][2 halves][C]: dbeta partial sums
 constexpr int gpart = bpart + 4 * 6 * kC;  // fp32 [4 row blocks][128]: colsum(dR R)
 constexpr int spart = gpart + 4 * 4 * kD;  // fp32 [8 value blocks][128]: rowsum(dS' S)
-constexpr int TOTAL = spart + 4 * 8 * kD;
+constexpr int qpart = spart + 4 * 8 * kD;  // fp32 [4 quarters][128]: row-quarter sums of the scans
+constexpr int TOTAL = qpart + 4 * 4 * kD;
 static_assert(As >= Lg + 4 * kC * LgP && FP >= As + 4 * kC * AsP && FN + 16384 <= REGION, "phase 1 layout");
 static_assert(TOTAL <= 160 * 1024, "LDS budget");
 }  // namespace cl
@@ -299,14 +344,22 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk_kernel(BwdFastArgs a) {
         }
         if (tid < kC) ffl(cl::bet)[tid] = tid < L ? a.beta[tok(tid)] : 0.f;
         __syncthreads();
-        if (tid < kD) {
-            float g = 0.f;
-            for (int r = 0; r < kC; ++r) {
-                g += Lg[r * cl::LgP + tid];
-                Lg[r * cl::LgP + tid] = g;
-            }
-            ffl(cl::gam)[tid] = g;
-        }
+        // thread (channel c, quarter qq): the prefix over rows 16 qq .. 16 qq + 15 in registers,
+        // then the quarters' totals through LDS
+        const int ft = fresh_tid(), c = ft & (kD - 1), qq = ft >> 7;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = Lg[(16 * qq + r) * cl::LgP + c];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) x[r] += x[r - 1];
+        ffl(cl::qpart)[qq * kD + c] = x[15];
+        __syncthreads();
+        float off = 0.f;
+#pragma unroll
+        for (int b = 0; b < 3; ++b) off += b < qq ? ffl(cl::qpart)[b * kD + c] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lg[(16 * qq + r) * cl::LgP + c] = x[r] + off;
+        if (qq == 3) ffl(cl::gam)[c] = x[15] + off;
         __syncthreads();
     }
     // this thread's elements of the C x 128 layout: k, g (q is read again where needed); m and
@@ -530,10 +583,12 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk_kernel(BwdFastArgs a) {
         for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(0.f);
         if (r < L) {
             const bf16 *p = v_g + tok(r) * kD + 32 * kg + 4 * hi;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(p), hi2 = *reinterpret_cast<const uint2 *>(p + 16);
+            const bf16 *vl = reinterpret_cast<const bf16 *>(&lo), *vh = reinterpret_cast<const bf16 *>(&hi2);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = static_cast<bf16>(b * static_cast<float>(p[e]));
-                x[e + 4] = static_cast<bf16>(b * static_cast<float>(p[16 + e]));
+                x[e] = static_cast<bf16>(b * static_cast<float>(vl[e]));
+                x[e + 4] = static_cast<bf16>(b * static_cast<float>(vh[e]));
             }
         }
         *reinterpret_cast<V8 *>(fbuf(cl::FBv) + (size_t)u * 8) = x;
@@ -622,9 +677,11 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk_kernel(BwdFastArgs a) {
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                // above the diagonal G = P N^T can overflow (e^(g_r - g_i) with i after r): selected
+                // away, never multiplied by a zero
                 const bool low = (16 * (cbC + u) + n) < row_of(i);
                 const float dA = low ? -t[u][i] : 0.f;
-                rs[i] = fmaf(dA, G[u][i], rs[i]);
+                rs[i] = low ? fmaf(dA, G[u][i], rs[i]) : rs[i];
                 t[u][i] = brow[i] * dA;
             }
             store_n(fbuf(cl::FdAp), rb, cbC + u, t[u], kC);
@@ -715,25 +772,37 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk_kernel(BwdFastArgs a) {
             }
     }
     __syncthreads();
-    if (tid < kD) {
-        const float *gp = ffl(cl::gpart), *sp = ffl(cl::spart), *Lg = ffl(cl::Lg);
+    // dlog alpha: thread (channel c, quarter qq) forms the suffix sums of its 16 rows, then adds
+    // the later quarters' totals and dgamma
+    {
+        const int ft = fresh_tid(), c = ft & (kD - 1), qq = ft >> 7;
+        const float *Lg = ffl(cl::Lg);
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = Lg[(16 * qq + r) * cl::LgP + c];
+#pragma unroll
+        for (int r = 14; r >= 0; --r) x[r] += x[r + 1];
+        ffl(cl::qpart)[qq * kD + c] = x[0];
+        if (tid < kC) {  // dbeta, rows 0 .. C - 1: its six partial sums in a fixed order
+            const float *bp = ffl(cl::bpart);
+            float acc = 0.f;
+#pragma unroll
+            for (int t = 0; t < 6; ++t) acc += bp[t * kC + tid];
+            if (tid < L) a.dbeta[tok(tid)] = acc;
+        }
+        __syncthreads();
+        const float *gp = ffl(cl::gpart), *sp = ffl(cl::spart);
         float cs = 0.f, ss = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) cs += gp[b * kD + tid];
+        for (int b = 0; b < 4; ++b) cs += gp[b * kD + c];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) ss += sp[b * kD + tid];
-        float acc = fmaf(__expf(ffl(cl::gam)[tid]), ss, cs);
-        for (int r = kC - 1; r >= 0; --r) {
-            acc += Lg[r * cl::LgP + tid];
-            if (r < L) a.dlog_alpha[tok(r) * kD + tid] = acc;
-        }
-    } else if (tid >= 256 && tid < 256 + kC) {
-        const int r = tid - 256;
-        const float *bp = ffl(cl::bpart);
-        float acc = 0.f;
+        for (int b = 0; b < 8; ++b) ss += sp[b * kD + c];
+        float off = fmaf(__expf(ffl(cl::gam)[c]), ss, cs);
 #pragma unroll
-        for (int t = 0; t < 6; ++t) acc += bp[t * kC + r];
-        if (r < L) a.dbeta[tok(r)] = acc;
+        for (int b = 1; b < 4; ++b) off += b > qq ? ffl(cl::qpart)[b * kD + c] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (16 * qq + r < L) a.dlog_alpha[tok(16 * qq + r) * kD + c] = x[r] + off;
     }
 }
 #undef KDA_ROW

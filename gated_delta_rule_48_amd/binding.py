@@ -23,8 +23,9 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
            "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_preact", "kda_recurrent_step",
            "kda_recurrent_step_gated", "kda_recurrent_step_preact", "kda_attn_decode_workspace_bytes",
-           "kda_attn_decode", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_noalloc")
-ABI_VERSION = 5
+           "kda_attn_decode", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
+           "kda_chunk_bwd_varlen_workspace_bytes", "kda_chunk_bwd_varlen")
+ABI_VERSION = 6
 NOALLOC_MAX_WORKSPACE = 32 << 20  # KDA_NOALLOC_MAX_WORKSPACE
 
 
@@ -73,6 +74,10 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_bwd_workspace_bytes.restype = Z
     lib.kda_chunk_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.kda_chunk_bwd.restype = I
+    lib.kda_chunk_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.kda_chunk_bwd_varlen_workspace_bytes.restype = Z
+    lib.kda_chunk_bwd_varlen.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, P, P, I, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.kda_chunk_bwd_varlen.restype = I
     lib.kda_chunk_fwd_noalloc.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, F, P, P, I, P, P, P]
     lib.kda_chunk_fwd_noalloc.restype = I
     if lib.kda_abi_version() != ABI_VERSION:
@@ -384,16 +389,26 @@ def chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk=64, io=KDA_F32) -> int:
     return int(load().kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, io))
 
 
+def chunk_bwd_varlen_workspace_bytes(T, H, dk, dv, n_seqs, chunk=64, io=KDA_BF16) -> int:
+    return int(load().kda_chunk_bwd_varlen_workspace_bytes(T, H, dk, dv, chunk, n_seqs, io))
+
+
 def chunk_bwd(q, k, v, log_alpha, beta, dout, scale: Optional[float] = None, h0=None, dhT=None,
-              chunk: int = 64, workspace=None, stream=None):
+              chunk: int = 64, workspace=None, stream=None, cu_seqlens=None):
     """Backward pass of chunk_fwd (kda_chunk_bwd) for equal-length sequences: q, k
     [B, T, H, dk]; v, dout [B, T, H, dv] (fp32 or bf16); log_alpha [B, T, H, dk]; beta
     [B, T, H]; h0, dhT [B, H, dk, dv] or None (fp32). Returns (dq, dk, dv in q's dtype,
-    dlog_alpha, dbeta, dh0 in fp32), dh0 None when h0 is None."""
+    dlog_alpha, dbeta, dh0 in fp32), dh0 None when h0 is None.
+    With cu_seqlens (int32 [n_seqs + 1], on the device), packed sequences
+    (kda_chunk_bwd_varlen, bf16 with dk = dv = 128): q, k [T, H, dk], v, dout [T, H, dv],
+    log_alpha [T, H, dk], beta [T, H], h0 and dhT [n_seqs, H, dk, dv]."""
     import torch
     lib = load()
     dev = q.device
     io = _io_code(q.dtype)
+    if cu_seqlens is not None:
+        return _chunk_bwd_varlen(lib, q, k, v, log_alpha, beta, dout, scale, h0, dhT, chunk, workspace, stream,
+                                 cu_seqlens, io)
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
@@ -424,4 +439,43 @@ def chunk_bwd(q, k, v, log_alpha, beta, dout, scale: Optional[float] = None, h0=
                            _ptr(dlog_alpha), _ptr(dbeta), _ptr(dh0), _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_chunk_bwd")
+    return dq, dk_, dv_, dlog_alpha, dbeta, dh0
+
+
+def _chunk_bwd_varlen(lib, q, k, v, log_alpha, beta, dout, scale, h0, dhT, chunk, workspace, stream, cu_seqlens, io):
+    import torch
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("with cu_seqlens q must be [T, H, dk]")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    f32 = torch.float32
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.numel(),), dev)
+    n = cu_seqlens.numel() - 1
+    _check(q, "q", q.dtype, (T, H, dk), dev)
+    _check(k, "k", q.dtype, (T, H, dk), dev)
+    _check(v, "v", q.dtype, (T, H, dv), dev)
+    _check(log_alpha, "log_alpha", f32, (T, H, dk), dev)
+    _check(beta, "beta", f32, (T, H), dev)
+    _check(dout, "dout", q.dtype, (T, H, dv), dev)
+    for t, nm in ((h0, "h0"), (dhT, "dhT")):
+        if t is not None:
+            _check(t, nm, f32, (n, H, dk, dv), dev)
+    dq, dk_ = (torch.empty((T, H, dk), dtype=q.dtype, device=dev) for _ in range(2))
+    dlog_alpha = torch.empty((T, H, dk), dtype=f32, device=dev)
+    dv_ = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    dbeta = torch.empty((T, H), dtype=f32, device=dev)
+    dh0 = torch.empty((n, H, dk, dv), dtype=f32, device=dev) if h0 is not None else None
+    need = int(lib.kda_chunk_bwd_varlen_workspace_bytes(T, H, dk, dv, chunk, n, io))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dk ** -0.5
+    st = lib.kda_chunk_bwd_varlen(T, H, dk, dv, chunk, io, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  float(scale), _ptr(h0), _ptr(cu_seqlens), n, _ptr(dout), _ptr(dhT), _ptr(dq),
+                                  _ptr(dk_), _ptr(dv_), _ptr(dlog_alpha), _ptr(dbeta), _ptr(dh0), _ptr(workspace),
+                                  ws_bytes, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_bwd_varlen")
     return dq, dk_, dv_, dlog_alpha, dbeta, dh0

@@ -530,8 +530,36 @@ struct BwdPlan {
     int n_chunks, n_groups;
     // the matrix-core pass (bf16, d_k = d_v = 128): offsets of its workspace buffers
     bool fast;
-    size_t W, U, QO, KtT, Aqk, eg, strong, st, ut, ds, du, discard;
+    size_t W, U, QO, KtT, Aqk, eg, strong, st, ut, ds, du, discard, choff;
+    int64_t fast_chunks;  // chunks over all sequences (an upper bound with cu_seqlens)
 };
+
+// The matrix-core pass's workspace: per (chunk, head) the forward's chunk quantities, then
+// S^T, U^T, dS'^T and dU^T (bf16); with packed sequences, the chunk-offset table.
+void bwd_fast_layout(int64_t chunks, int H, int d_k, int d_v, int C, int n_seqs_varlen, BwdPlan *p) {
+    const size_t u = (size_t)chunks * H, e = 2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    p->W = take(u * C * d_k * e);
+    p->U = take(u * C * d_v * e);
+    p->QO = take(u * C * d_k * e);
+    p->KtT = take(u * d_k * C * e);
+    p->Aqk = take(u * C * C * e);
+    p->eg = take(u * d_k * 4);
+    p->strong = take(u);
+    p->st = take(u * d_v * d_k * e);
+    p->ut = take(u * d_v * C * e);
+    p->ds = take(u * d_v * d_k * e);
+    p->du = take(u * d_v * C * e);
+    p->discard = take(256);
+    p->choff = n_seqs_varlen > 0 ? take(((size_t)3 * n_seqs_varlen + 1) * sizeof(int32_t)) : 0;
+    p->fast_chunks = chunks;
+    p->total = u > 0 || n_seqs_varlen > 0 ? off : 0;
+}
 
 // bf16 I/O with d_k = d_v = 128 takes the matrix-core backward pass (kda_bwd_bf16.hip);
 // everything else the direct one (kda_bwd.hip).
@@ -547,27 +575,7 @@ int check_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io, BwdPlan 
     const int64_t units = (int64_t)B * p->n_chunks * H;
     p->fast = bwd_fast(d_k, d_v, io);
     if (p->fast) {
-        // per (chunk, head): the forward's chunk quantities, then S^T, U^T, dS'^T and dU^T (bf16)
-        const size_t u = (size_t)units, C = chunk, e = 2;
-        size_t off = 0;
-        auto take = [&](size_t bytes) {
-            const size_t at = off;
-            off = round_up(off + bytes, 256);
-            return at;
-        };
-        p->W = take(u * C * d_k * e);
-        p->U = take(u * C * d_v * e);
-        p->QO = take(u * C * d_k * e);
-        p->KtT = take(u * d_k * C * e);
-        p->Aqk = take(u * C * C * e);
-        p->eg = take(u * d_k * 4);
-        p->strong = take(u);
-        p->st = take(u * d_v * d_k * e);
-        p->ut = take(u * d_v * C * e);
-        p->ds = take(u * d_v * d_k * e);
-        p->du = take(u * d_v * C * e);
-        p->discard = take(256);
-        p->total = units > 0 ? off : 0;
+        bwd_fast_layout((int64_t)B * p->n_chunks, H, d_k, d_v, chunk, 0, p);
         return KDA_OK;
     }
     const kda::BwdLayout L{d_k, d_v};
@@ -649,4 +657,79 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
     if (kda::launch_chunk_bwd(a, d_k, d_v, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+namespace {
+
+int check_bwd_varlen(int T, int H, int d_k, int d_v, int chunk, int n_seqs, int io, BwdPlan *p) {
+    if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (T < 0 || H < 1 || n_seqs < 1) return KDA_ERR_INVALID_ARG;
+    if (chunk != kda::kBwdChunk || !bwd_fast(d_k, d_v, io)) return KDA_ERR_UNSUPPORTED;
+    if (H > 65535 || n_seqs > 65535 || (int64_t)T * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    *p = BwdPlan{};
+    p->fast = true;
+    bwd_fast_layout(((int64_t)T + chunk - 1) / chunk + n_seqs, H, d_k, d_v, chunk, n_seqs, p);
+    return KDA_OK;
+}
+
+}  // namespace
+
+KDA_EXPORT size_t kda_chunk_bwd_varlen_workspace_bytes(int T, int H, int d_k, int d_v, int chunk, int n_seqs,
+                                                       int io) {
+    BwdPlan p;
+    if (check_bwd_varlen(T, H, d_k, d_v, chunk, n_seqs, io, &p) != KDA_OK) return 0;
+    return p.total;
+}
+
+KDA_EXPORT int kda_chunk_bwd_varlen(int T, int H, int d_k, int d_v, int chunk, int io, const void *q, const void *k,
+                                    const void *v, const float *log_alpha, const float *beta, float scale,
+                                    const float *h0, const int32_t *cu_seqlens, int n_seqs, const void *dout,
+                                    const float *dhT, void *dq, void *dk, void *dv, float *dlog_alpha, float *dbeta,
+                                    float *dh0, void *workspace, size_t workspace_bytes, void *stream) {
+    BwdPlan p;
+    const int st = check_bwd_varlen(T, H, d_k, d_v, chunk, n_seqs, io, &p);
+    if (st != KDA_OK) return st;
+    if (!isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    const size_t ntok = (size_t)T * H, esz = 2;
+    const size_t nk = ntok * d_k * esz, nv = ntok * d_v * esz, nb = ntok * 4, ns = (size_t)n_seqs * H * d_k * d_v * 4;
+    const size_t nla = ntok * d_k * 4;
+    if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+    if (ntok > 0 && (!q || !k || !v || !log_alpha || !beta || !dout || !dq || !dk || !dv || !dlog_alpha || !dbeta))
+        return KDA_ERR_INVALID_ARG;
+    const void *in16[] = {q, k, v, log_alpha, dout, h0, dhT, dq, dk, dv, dlog_alpha, dh0};
+    for (const void *x : in16)
+        if (!aligned(x, 16)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(beta, 4) || !aligned(dbeta, 4)) return KDA_ERR_INVALID_ARG;
+    const size_t ncu = ((size_t)n_seqs + 1) * sizeof(int32_t);
+    const void *ins[] = {q, k, v, log_alpha, beta, h0, dout, dhT, cu_seqlens};
+    const size_t in_n[] = {nk, nk, nv, nla, nb, ns, nv, ns, ncu};
+    const void *outs[] = {dq, dk, dv, dlog_alpha, dbeta, dh0};
+    const size_t out_n[] = {nk, nk, nv, nla, nb, ns};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 9; ++j)
+            if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return KDA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return KDA_ERR_INVALID_ARG;
+    }
+    if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+    for (int j = 0; j < 9; ++j)
+        if (overlaps(workspace, p.total, ins[j], in_n[j])) return KDA_ERR_INVALID_ARG;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(workspace, p.total, outs[i], out_n[i])) return KDA_ERR_INVALID_ARG;
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    unsigned char *w8 = static_cast<unsigned char *>(workspace);
+    int32_t *tab = reinterpret_cast<int32_t *>(w8 + p.choff);
+    if (kda::launch_chunk_offsets(cu_seqlens, n_seqs, T, kda::kBwdChunk, tab, tab + n_seqs + 1, tab + 2 * n_seqs + 1,
+                                  hs) != hipSuccess)
+        return KDA_ERR_HIP;
+    kda::BwdFastArgs a{};
+    a.q = q, a.k = k, a.v = v, a.log_alpha = log_alpha, a.beta = beta, a.h0 = h0, a.dout = dout, a.dhT = dhT;
+    a.scale = scale;
+    a.dq = dq, a.dk = dk, a.dv = dv, a.dlog_alpha = dlog_alpha, a.dbeta = dbeta, a.dh0 = dh0;
+    a.H = H;
+    a.map = kda::SeqMap{tab, tab + n_seqs + 1, tab + 2 * n_seqs + 1, 1, n_seqs, 0, kda::kBwdChunk};
+    a.buf = kda::ChunkBuffers{w8 + p.W, w8 + p.U, w8 + p.QO, w8 + p.KtT, w8 + p.Aqk,
+                              reinterpret_cast<float *>(w8 + p.eg), w8 + p.strong};
+    a.st = w8 + p.st, a.ut = w8 + p.ut, a.ds = w8 + p.ds, a.du = w8 + p.du, a.discard = w8 + p.discard;
+    return kda::launch_chunk_bwd_bf16(a, n_seqs, (int)p.fast_chunks, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
     KDA_OK = 0,
@@ -279,11 +279,18 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  * chunk by chunk: the chunk-local forward quantities, the chunk-start states in
  * order, the state gradients in reverse order, then the chunk-local gradients.
  *
+ * Two implementations: bf16 I/O with d_k = d_v = 128 runs the matrix-core pass (the
+ * forward's chunk preparation and state recursion, recording the state entering every
+ * chunk; the state gradients in reverse; one fused kernel per (chunk, head) for the
+ * chunk-local gradients), whose products take bf16 operands with fp32 accumulation as
+ * the forward's bf16 passes do; every other case runs the direct pass, all arithmetic
+ * fp32. Both add every sum in a fixed order: repeated calls give the same bits.
+ *
  * Arguments
- *   B, T, H, d_k, d_v   equal-length sequences [B, T, H, d] (no cu_seqlens);
- *               d_k, d_v in {64, 128}; B, H <= 65535.
+ *   B, T, H, d_k, d_v   equal-length sequences [B, T, H, d] (packed sequences:
+ *               kda_chunk_bwd_varlen); d_k, d_v in {64, 128}; B, H <= 65535.
  *   chunk       64.   io   dtype of q, k, v, dout and dq, dk, dv (KDA_F32 or KDA_BF16);
- *               all arithmetic is fp32.
+ *               gates, states and their gradients are fp32.
  *   q, k, v, log_alpha, beta, scale, h0   the forward call's inputs (h0 NULL =
  *               zero initial state).
  *   dout        [B, T, H, d_v] dtype io, the gradient with respect to o.
@@ -291,10 +298,10 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  *   dq, dk      [B, T, H, d_k], dv [B, T, H, d_v]: dtype io;  dlog_alpha [B, T, H, d_k]
  *               and dbeta [B, T, H]: fp32. Written, none overlapping any argument.
  *   dh0         [B, H, d_k, d_v] fp32 or NULL (not computed).
- *   workspace   kda_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned
- *               (about 300 KB per (chunk, head) at d = 128, plus a fixed scratch
- *               of at most 1024 x 770 KB): the chunk-local matrices, the
- *               chunk-start states and the state gradients.
+ *   workspace   kda_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned: on the
+ *               matrix-core pass about 170 KB per (chunk, head) (the forward's chunk
+ *               quantities and four bf16 matrices); on the direct pass about 300 KB per
+ *               (chunk, head) at d = 128 plus a fixed scratch of at most 1024 x 770 KB.
  * Gate values as for kda_chunk_fwd. Errors as for the other entry points.
  */
 size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, int io);
@@ -305,6 +312,29 @@ int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io,
                   const float *h0, const void *dout, const float *dhT,
                   void *dq, void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dh0,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_bwd_varlen -- kda_chunk_bwd for packed variable-length sequences, the
+ * layout of kda_chunk_fwd with cu_seqlens: q, k, dq, dk, log_alpha, dlog_alpha
+ * [T, H, d_k]; v, dout, dv [T, H, d_v]; beta, dbeta [T, H]; h0, dhT, dh0
+ * [n_seqs, H, d_k, d_v] (h0, dhT NULL = zero; dh0 NULL = not computed). cu_seqlens is
+ * a device int32 [n_seqs + 1] table with the meaning, and the clamping of malformed
+ * values, of kda_chunk_fwd's; n_seqs >= 1.
+ *
+ * Served by the matrix-core pass: io = KDA_BF16, d_k = d_v = 128, chunk 64; any other
+ * size returns KDA_ERR_UNSUPPORTED. Workspace: kda_chunk_bwd_varlen_workspace_bytes
+ * (sized for up to ceil(T / 64) + n_seqs chunks). Empty sequences give dh0 = dhT.
+ * Everything else as kda_chunk_bwd.
+ */
+size_t kda_chunk_bwd_varlen_workspace_bytes(int T, int H, int d_k, int d_v, int chunk, int n_seqs, int io);
+
+int kda_chunk_bwd_varlen(int T, int H, int d_k, int d_v, int chunk, int io,
+                         const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta, float scale,
+                         const float *h0, const int32_t *cu_seqlens, int n_seqs,
+                         const void *dout, const float *dhT,
+                         void *dq, void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dh0,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Full-attention decode over a KV cache: the comparator of the decode step

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing, misaligned or too small")]:
         assert lib.kda_status_string(code) == text
     assert lib.kda_status_string(99) == b"unknown status"
@@ -348,3 +348,47 @@ def test_chunk_bwd_workspace(lib):
         assert ws(*args, 64, F32) == expect(*args), args
     assert ws(2, 100, 4, 64, 64, 64, BF16) == expect(2, 100, 4, 64, 64)  # fp32 buffers whatever the io dtype
     assert ws(2, 100, 4, 64, 64, 128, F32) == 0
+    # bf16 at d = 128: the matrix-core pass, about 170 KB of bf16 buffers per (chunk, head)
+    assert ws(8, 8192, 32, 128, 128, 64, BF16) == _bwd_fast_expect(8 * 128, 32, 0)
+    assert ws(2, 100, 4, 128, 128, 64, BF16) == _bwd_fast_expect(2 * 2, 4, 0)
+    assert ws(2, 0, 4, 128, 128, 64, BF16) == 0
+
+
+def _bwd_fast_expect(chunks, H, n_seqs_varlen, C=64, d=128):
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    u = chunks * H
+    parts = [u * C * d * 2, u * C * d * 2, u * C * d * 2, u * d * C * 2, u * C * C * 2, u * d * 4, u,
+             u * d * d * 2, u * d * C * 2, u * d * d * 2, u * d * C * 2, 256]
+    if n_seqs_varlen:
+        parts.append((3 * n_seqs_varlen + 1) * 4)
+    return sum(r(x) for x in parts)
+
+
+def bwd_varlen(lib, **kw):
+    a = dict(T=300, H=4, dk=128, dv=128, chunk=64, io=BF16, q=A, k=A, v=A, la=A, beta=A, scale=0.125, h0=None,
+             cu=0x3000000, n=3, dout=A, dhT=None, dq=0x4000000, dk_=0x5000000, dv_=0x6000000, dla=0x7000000,
+             dbeta=0x8000000, dh0=None, ws=0x10000000, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd_varlen(a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["io"], a["q"], a["k"], a["v"],
+                                    a["la"], a["beta"], a["scale"], a["h0"], a["cu"], a["n"], a["dout"], a["dhT"],
+                                    a["dq"], a["dk_"], a["dv_"], a["dla"], a["dbeta"], a["dh0"], a["ws"],
+                                    a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(io=F32), UNSUPPORTED), (dict(dk=64), UNSUPPORTED), (dict(dv=64), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
+    (dict(io=5), UNSUPPORTED), (dict(n=0), INVALID), (dict(T=-1), INVALID), (dict(H=0), INVALID),
+    (dict(cu=None), INVALID), (dict(cu=0x3000000 + 2), INVALID), (dict(q=None), INVALID), (dict(q=A + 8), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(dq=A), INVALID), (dict(dq=0x3000000), INVALID),  # dq on cu_seqlens
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=4096), WORKSPACE), (dict(ws=0x10000000 + 16), WORKSPACE),
+])
+def test_chunk_bwd_varlen_rejects(lib, kw, code):
+    assert bwd_varlen(lib, **kw) == code
+
+
+def test_chunk_bwd_varlen_workspace(lib):
+    ws = lib.kda_chunk_bwd_varlen_workspace_bytes
+    # sized for ceil(T / 64) + n_seqs chunks, plus the chunk-offset table
+    assert ws(300, 4, 128, 128, 64, 3, BF16) == _bwd_fast_expect(5 + 3, 4, 3)
+    assert ws(0, 4, 128, 128, 64, 2, BF16) == _bwd_fast_expect(0 + 2, 4, 2)
+    assert ws(300, 4, 128, 128, 64, 3, F32) == 0 and ws(300, 4, 64, 64, 64, 3, BF16) == 0

@@ -191,3 +191,69 @@ def test_bwd_bitwise_deterministic(io):
     torch.cuda.synchronize()
     for n, a, b in zip(NAMES, *runs):
         assert torch.equal(a, b), n
+
+
+def _varlen_case(seqlens, H, seed, h0=True, dhT=True):
+    """Packed bf16 sequences at d = 128 through kda_chunk_bwd_varlen, and the oracle run on
+    each sequence on its own (sequences are independent)."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    d, n = 128, len(seqlens)
+    x = kda_synth.gen_sequences(seqlens, H, d, d, "bf16", "main", "normal" if h0 else "zero", seed)
+    T = int(sum(seqlens))
+    do = kda_synth.round_bf16(kda_synth.gen_grad_outputs(1, T, H, d, d, seed)["dout"][0])
+    dh = kda_synth.gen_grad_outputs(n, 0, H, d, d, seed + 1)["dhT"] if dhT else None
+    cu = x["cu_seqlens"]
+    t = {m: torch.from_numpy(np.ascontiguousarray(x[m])).cuda() for m in ("q", "k", "v", "log_alpha", "beta")}
+    for m in ("q", "k", "v"):
+        t[m] = t[m].to(torch.bfloat16)
+    got = kda.chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"],
+                        torch.from_numpy(do).cuda().to(torch.bfloat16), scale=d ** -0.5,
+                        h0=None if x["h0"] is None else torch.from_numpy(x["h0"]).cuda(),
+                        dhT=None if dh is None else torch.from_numpy(dh).cuda(),
+                        cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    got = {nm: (None if a is None else a.float().cpu().numpy()) for nm, a in zip(NAMES, got)}
+    refs = []
+    for s in range(n):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda z: z[a:b][None]  # noqa: E731
+        refs.append(oracle.kda_backward_reference(
+            sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]), sl(x["beta"]), d ** -0.5, sl(do),
+            dhT=None if dh is None else dh[s:s + 1], h0=None if x["h0"] is None else x["h0"][s:s + 1]))
+    return got, refs
+
+
+@pytest.mark.parametrize("seqlens,H", [((0, 1, 63, 64, 65, 130, 0, 200), 3), ((300, 5), 2)])
+def test_bwd_varlen_packed_ragged(seqlens, H):
+    say(f"[bwd-varlen] seqlens={seqlens} H={H} bf16 d=128")
+    got, refs = _varlen_case(seqlens, H, seed=51 + H)
+    errs = {}
+    for nm in NAMES[:5]:
+        ref = np.concatenate([r[nm][0] for r in refs], axis=0)
+        assert np.all(np.isfinite(got[nm])), nm
+        errs[nm] = rel_l2(got[nm], ref)
+    errs["dh0"] = rel_l2(got["dh0"], np.concatenate([r["dh0"] for r in refs], axis=0))
+    say(f"[bwd-varlen] rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    for nm, e in errs.items():
+        assert e <= TOL["bf16"], (nm, e)
+
+
+def test_bwd_varlen_equals_batched():
+    """Equal lengths given packed with cu_seqlens and given as [B, T, H, d]: the same chunks,
+    the same kernels, the same bits."""
+    import torch
+    import gated_delta_rule_48_amd as kda
+    B, T, H, d = 2, 150, 3, 128
+    x = _inputs(B, T, H, d, d, "main", 61, io="bf16")
+    t = {n: torch.from_numpy(np.ascontiguousarray(a)).cuda() for n, a in x.items()}
+    for n in ("q", "k", "v", "dout"):
+        t[n] = t[n].to(torch.bfloat16)
+    a = kda.chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["dout"], h0=t["h0"], dhT=t["dhT"])
+    flat = lambda z: z.reshape((B * T,) + tuple(z.shape[2:]))  # noqa: E731
+    cu = torch.tensor([0, T, 2 * T], dtype=torch.int32, device="cuda")
+    b = kda.chunk_bwd(flat(t["q"]), flat(t["k"]), flat(t["v"]), flat(t["log_alpha"]), flat(t["beta"]),
+                      flat(t["dout"]), h0=t["h0"], dhT=t["dhT"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    for n, x1, x2 in zip(NAMES, a, b):
+        assert torch.equal(flat(x1) if n != "dh0" else x1, x2), n

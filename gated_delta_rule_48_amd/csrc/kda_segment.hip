@@ -17,9 +17,10 @@
 // product taken as hi hi' + hi lo' + lo hi' with v_mfma_f32_16x16x32_bf16 (lane l supplies
 // A[l%16][8 (l/16) .. + 7] and B[8 (l/16) .. + 7][l%16]), fp32 accumulation: about 16
 // significant bits per product, at a fifth of the matrix-core time of fp32 instructions.
-// Each lane reads its share of M(p) and N(p) straight from memory, those of step p + 1
-// while step p computes; the 16 columns of S_in stay in LDS (transposed, two buffers used
-// in turn, so one barrier per step). The 8 workgroups of one (sequence, head) run on one
+// Each lane reads its share of M(p) and N(p) straight from memory, those of steps p + 1
+// and p + 2 in flight while step p computes. The 16 columns of S_in stay in LDS, split into
+// hi and lo once, by the lanes that form them (transposed; two sets of buffers used in turn,
+// so one barrier per step). The 8 workgroups of one (sequence, head) run on one
 // XCD (block ids 8 apart), so M(p) is fetched into one L2 and read there 8 times. All
 // buffers hold states in channel order, row-major (row = key channel), like h0 and hT.
 
@@ -30,7 +31,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kChainThreads = 512;
-constexpr int kStPitch = kD + 4;  // floats per row of the transposed S_in buffers
+constexpr int kStPitch = kD + 8;  // bf16 per row of the transposed S_in buffers
 
 // hi = bf16(x), lo = bf16(x - hi) for 8 values
 __device__ __forceinline__ void split_hi_lo(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
@@ -44,7 +45,9 @@ __device__ __forceinline__ void split_hi_lo(const f32x4 &x0, const f32x4 &x1, bf
 }
 
 __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedArgs a) {
-    __shared__ __align__(16) float St[2][16 * kStPitch];  // St[b][n * kStPitch + k] = S_in[k][n]
+    // S_in's 16 columns as the B operand, already split: Sh[b][n * kStPitch + k] = hi of S_in[k][n],
+    // Sl the rest (each value is split once, by the lane that forms it, for all eight waves)
+    __shared__ __align__(16) bf16 Sh[2][16 * kStPitch], Sl[2][16 * kStPitch];
     const int H = a.H;
     // blocks are dealt round-robin to the 8 XCDs: block id = xcd + 8 (cb + 8 q), pair = xcd + 8 q
     const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
@@ -66,61 +69,74 @@ __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedA
         for (int e = tid; e < kD * 16; e += kChainThreads) {
             const int r = e >> 4, c = e & 15;
             const float x = N0[r * kD + 16 * cb + c];
-            St[1][c * kStPitch + r] = x;
+            const bf16 xh = static_cast<bf16>(x);
+            Sh[1][c * kStPitch + r] = xh;
+            Sl[1][c * kStPitch + r] = static_cast<bf16>(x - static_cast<float>(xh));
             S1[r * kD + 16 * cb + c] = x;
         }
     }
     // this lane's A operands of M(p) (row 16 w + n, contraction indices 32 kb + 8 g .. + 7) and
-    // the four entries of N(p) its outputs add, in two sets used in turn
-    f32x4 amA[4][2], amB[4][2];
-    float nA[4], nB[4];
-    auto fetch = [&](int p, f32x4 (&am)[4][2], float (&nd)[4]) {
+    // the four entries of N(p) its outputs add, in three sets used in turn: step p computes
+    // from one while the maps of steps p + 1 and p + 2 are in flight (a step is much shorter
+    // than a load of M from memory)
+    f32x4 amA[4][2], amB[4][2], amC[4][2];
+    float nA[4], nB[4], nC[4];
+    auto fetch = [&](int p, f32x4 (&a4)[4][2], float (&n4)[4]) {
         const float *M = map_of(p);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                am[kb][j] = *reinterpret_cast<const f32x4 *>(M + (16 * w + n) * kD + 32 * kb + 8 * g + 4 * j);
+                a4[kb][j] = *reinterpret_cast<const f32x4 *>(M + (16 * w + n) * kD + 32 * kb + 8 * g + 4 * j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nd[i] = M[DD + (16 * w + 4 * g + i) * kD + 16 * cb + n];
+        for (int i = 0; i < 4; ++i) n4[i] = M[DD + (16 * w + 4 * g + i) * kD + 16 * cb + n];
     };
     // S_in(p + 1) = M(p) S_in(p) + N(p); S_in(p) is in buffer p & 1
-    auto step = [&](int p, const f32x4 (&am)[4][2], const float (&nv)[4]) {
+    auto step = [&](int p, const f32x4 (&a4)[4][2], const float (&nv)[4]) {
+        bf16x8 ah[4], al[4];  // M's split does not wait for S_in
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) split_hi_lo(a4[kb][0], a4[kb][1], ah[kb], al[kb]);
         __syncthreads();  // S_in(p) complete; every wave is done with the other buffer
-        const float *src = St[p & 1];
+        const bf16 *sh = Sh[p & 1], *sl = Sl[p & 1];
         f32x4 hh = {0.f, 0.f, 0.f, 0.f}, hl = hh, lh = hh;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(src + n * kStPitch + 32 * kb + 8 * g);
-            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(src + n * kStPitch + 32 * kb + 8 * g + 4);
-            bf16x8 ah, al, bh, bl;
-            split_hi_lo(am[kb][0], am[kb][1], ah, al);
-            split_hi_lo(b0, b1, bh, bl);
-            hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, hh, 0, 0, 0);
-            hl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, hl, 0, 0, 0);
-            lh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, lh, 0, 0, 0);
+            const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(sh + n * kStPitch + 32 * kb + 8 * g);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(sl + n * kStPitch + 32 * kb + 8 * g);
+            hh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[kb], bh, hh, 0, 0, 0);
+            hl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[kb], bl, hl, 0, 0, 0);
+            lh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[kb], bh, lh, 0, 0, 0);
         }
-        float *dst = St[(p + 1) & 1];
+        bf16 *dh = Sh[(p + 1) & 1], *dl = Sl[(p + 1) & 1];
         float *Sn = state_of(p + 1);
+        bf16 xh[4], xl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * w + 4 * g + i;
             const float x = hh[i] + (hl[i] + lh[i]) + nv[i];
-            dst[n * kStPitch + r] = x;
+            xh[i] = static_cast<bf16>(x);
+            xl[i] = static_cast<bf16>(x - static_cast<float>(xh[i]));
             Sn[r * kD + 16 * cb + n] = x;
         }
+        // rows 16 w + 4 g .. + 3 of column n: four adjacent entries of each buffer's row n
+        *reinterpret_cast<uint2 *>(dh + n * kStPitch + 16 * w + 4 * g) = *reinterpret_cast<const uint2 *>(xh);
+        *reinterpret_cast<uint2 *>(dl + n * kStPitch + 16 * w + 4 * g) = *reinterpret_cast<const uint2 *>(xl);
     };
     // Every fetch is unconditional (past the last step a set re-reads map P - 1, which lies
     // inside the workspace and is not used), so that the number of loads in flight is the
     // same on every path and each step waits for exactly its own operands.
     if (P <= 2) return;
     fetch(1, amA, nA);
-    for (int p = 1; p + 1 < P; p += 2) {
-        fetch(min(p + 1, P - 1), amB, nB);
+    fetch(min(2, P - 1), amB, nB);
+    for (int p = 1; p + 1 < P; p += 3) {
+        fetch(min(p + 2, P - 1), amC, nC);
         step(p, amA, nA);
         if (p + 2 >= P) break;
-        fetch(min(p + 2, P - 1), amA, nA);
+        fetch(min(p + 3, P - 1), amA, nA);
         step(p + 1, amB, nB);
+        if (p + 3 >= P) break;
+        fetch(min(p + 4, P - 1), amB, nB);
+        step(p + 2, amC, nC);
     }
 }
 

@@ -1271,8 +1271,8 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int p = 16 * tm + 4 * hi + i;
                 const float e = ehalf[e_slot(p)];
-                mp[chan_of_pos(p) * kDK + cc] = e * accM[tm][i];
-                mp[kDK * kDK + chan_of_pos(p) * kDV + cc] = e * accS[tm][i];
+                mp[seg_m_index(chan_of_pos(p), cc)] = e * accM[tm][i];
+                mp[kDK * kDK + seg_n_index(chan_of_pos(p), cc)] = e * accS[tm][i];
             }
         }
         return;

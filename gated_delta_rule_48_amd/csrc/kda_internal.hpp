@@ -100,8 +100,20 @@ struct FusedArgs {
     const int32_t *seg_tb;     // then each sequence's clamped begin and end ([n_seqs] each)
     const int32_t *seg_te;
     float *seg_state;          // [n_seg, H, d_k, d_v] fp32: the state entering each segment (p > 0)
-    float *seg_map;            // [n_seg, H, 2, d_k, d_k | d_v] fp32: M and N of each segment (S_out = M S_in + N)
+    float *seg_map;            // [n_seg, H, 2, d_k * d_k] fp32: M and N of each segment (S_out = M S_in + N),
+                               // in the order the composition reads them (seg_m_index, seg_n_index)
 };
+
+// Positions of M[r][c] and N[r][c] (d_k = d_v = 128, channel order) within a segment's map.
+// The composition's wave w, lane n + 16 g reads M[16 w + n][32 kb + 8 g + 4 j .. + 3] with one
+// 16-byte load per (kb, j), and N[16 w + 4 g + i][16 cb + n] with one 4-byte load per i: in
+// these orders every such load instruction reads one contiguous run of 1 KB (M) or 256 B (N).
+__host__ __device__ constexpr int seg_m_index(int r, int c) {
+    return ((((r >> 4) * 4 + (c >> 5)) * 2 + ((c >> 2) & 1)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 4 + (c & 3);
+}
+__host__ __device__ constexpr int seg_n_index(int r, int c) {
+    return (((c >> 4) * 8 + (r >> 4)) * 4 + (r & 3)) * 64 + (c & 15) + 16 * ((r >> 2) & 3);
+}
 
 // The composition of segment maps: per (sequence, head, 16 value columns), in order,
 // S_in(1) = N(0) (segment 0's map starts from h0) and S_in(p + 1) = M(p) S_in(p) + N(p).

@@ -21,8 +21,11 @@
 // and p + 2 in flight while step p computes. The 16 columns of S_in stay in LDS, split into
 // hi and lo once, by the lanes that form them (transposed; two sets of buffers used in turn,
 // so one barrier per step). The 8 workgroups of one (sequence, head) run on one
-// XCD (block ids 8 apart), so M(p) is fetched into one L2 and read there 8 times. All
-// buffers hold states in channel order, row-major (row = key channel), like h0 and hT.
+// XCD (block ids 8 apart), so M(p) is fetched into one L2 and read there 8 times. The maps
+// are stored in the order of these reads (seg_m_index, seg_n_index: one contiguous 1 KB run
+// per load instruction of M, where row-major order would touch 16 cache lines per
+// instruction, half of each); the entering states are row-major (row = key channel), like h0
+// and hT.
 
 #include "kda_internal.hpp"
 
@@ -32,6 +35,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kChainThreads = 512;
 constexpr int kStPitch = kD + 8;  // bf16 per row of the transposed S_in buffers
+constexpr int kBlockSteps = 15;   // steps per straight-line block (a multiple of the three operand sets)
 
 // hi = bf16(x), lo = bf16(x - hi) for 8 values
 __device__ __forceinline__ void split_hi_lo(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
@@ -63,17 +67,13 @@ __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedA
     auto state_of = [&](int p) { return a.seg_state + ((size_t)(g0 + p) * H + h) * DD; };
 
     // S_in(1) = N(0): this workgroup's 16 columns, to LDS and to segment 1's entering state
-    {
-        const float *N0 = map_of(0) + DD;
-        float *S1 = state_of(1);
-        for (int e = tid; e < kD * 16; e += kChainThreads) {
-            const int r = e >> 4, c = e & 15;
-            const float x = N0[r * kD + 16 * cb + c];
-            const bf16 xh = static_cast<bf16>(x);
-            Sh[1][c * kStPitch + r] = xh;
-            Sl[1][c * kStPitch + r] = static_cast<bf16>(x - static_cast<float>(xh));
-            S1[r * kD + 16 * cb + c] = x;
-        }
+    // (its loads are issued first, the first two steps' operands right behind them, so that
+    // the three wait out one memory latency together)
+    float n0[kD * 16 / kChainThreads];
+#pragma unroll
+    for (int k = 0; k < kD * 16 / kChainThreads; ++k) {
+        const int e = tid + k * kChainThreads, r = e >> 4, c = e & 15;
+        n0[k] = map_of(0)[DD + seg_n_index(r, 16 * cb + c)];
     }
     // this lane's A operands of M(p) (row 16 w + n, contraction indices 32 kb + 8 g .. + 7) and
     // the four entries of N(p) its outputs add, in three sets used in turn: step p computes
@@ -87,9 +87,9 @@ __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedA
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                a4[kb][j] = *reinterpret_cast<const f32x4 *>(M + (16 * w + n) * kD + 32 * kb + 8 * g + 4 * j);
+                a4[kb][j] = *reinterpret_cast<const f32x4 *>(M + seg_m_index(16 * w + n, 32 * kb + 8 * g + 4 * j));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) n4[i] = M[DD + (16 * w + 4 * g + i) * kD + 16 * cb + n];
+        for (int i = 0; i < 4; ++i) n4[i] = M[DD + seg_n_index(16 * w + 4 * g + i, 16 * cb + n)];
     };
     // S_in(p + 1) = M(p) S_in(p) + N(p); S_in(p) is in buffer p & 1
     auto step = [&](int p, const f32x4 (&a4)[4][2], const float (&nv)[4]) {
@@ -108,35 +108,58 @@ __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedA
             lh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[kb], bh, lh, 0, 0, 0);
         }
         bf16 *dh = Sh[(p + 1) & 1], *dl = Sl[(p + 1) & 1];
-        float *Sn = state_of(p + 1);
+        float x[4];
         bf16 xh[4], xl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * g + i;
-            const float x = hh[i] + (hl[i] + lh[i]) + nv[i];
-            xh[i] = static_cast<bf16>(x);
-            xl[i] = static_cast<bf16>(x - static_cast<float>(xh[i]));
-            Sn[r * kD + 16 * cb + n] = x;
+            x[i] = hh[i] + (hl[i] + lh[i]) + nv[i];
+            xh[i] = static_cast<bf16>(x[i]);
+            xl[i] = static_cast<bf16>(x[i] - static_cast<float>(xh[i]));
         }
-        // rows 16 w + 4 g .. + 3 of column n: four adjacent entries of each buffer's row n
+        // rows 16 w + 4 g .. + 3 of column n: four adjacent entries of each buffer's row n (the
+        // next step's operand first: the stores to memory below may wait behind loads in flight)
         *reinterpret_cast<uint2 *>(dh + n * kStPitch + 16 * w + 4 * g) = *reinterpret_cast<const uint2 *>(xh);
         *reinterpret_cast<uint2 *>(dl + n * kStPitch + 16 * w + 4 * g) = *reinterpret_cast<const uint2 *>(xl);
+        float *Sn = state_of(p + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sn[(16 * w + 4 * g + i) * kD + 16 * cb + n] = x[i];
     };
     // Every fetch is unconditional (past the last step a set re-reads map P - 1, which lies
     // inside the workspace and is not used), so that the number of loads in flight is the
-    // same on every path and each step waits for exactly its own operands.
+    // same on every path and each step waits for exactly its own operands. The steps run in
+    // straight-line blocks of kBlockSteps: at the header of a loop the compiler's wait for
+    // the loads in flight has to hold for the entry and for the back edge alike, and there
+    // it waits for nearly all of them, so the pipeline drains once per block.
+    if (P > 2) {
+        fetch(1, amA, nA);
+        fetch(min(2, P - 1), amB, nB);
+    }
+    {
+        float *S1 = state_of(1);
+#pragma unroll
+        for (int k = 0; k < kD * 16 / kChainThreads; ++k) {
+            const int e = tid + k * kChainThreads, r = e >> 4, c = e & 15;
+            const bf16 xh = static_cast<bf16>(n0[k]);
+            Sh[1][c * kStPitch + r] = xh;
+            Sl[1][c * kStPitch + r] = static_cast<bf16>(n0[k] - static_cast<float>(xh));
+            S1[r * kD + 16 * cb + c] = n0[k];
+        }
+    }
     if (P <= 2) return;
-    fetch(1, amA, nA);
-    fetch(min(2, P - 1), amB, nB);
-    for (int p = 1; p + 1 < P; p += 3) {
-        fetch(min(p + 2, P - 1), amC, nC);
-        step(p, amA, nA);
-        if (p + 2 >= P) break;
-        fetch(min(p + 3, P - 1), amA, nA);
-        step(p + 1, amB, nB);
-        if (p + 3 >= P) break;
-        fetch(min(p + 4, P - 1), amB, nB);
-        step(p + 2, amC, nC);
+    for (int p0 = 1; p0 + 1 < P; p0 += kBlockSteps) {
+#pragma unroll
+        for (int j = 0; j < kBlockSteps; j += 3) {
+            const int p = p0 + j;
+            if (p + 1 >= P) break;
+            fetch(min(p + 2, P - 1), amC, nC);
+            step(p, amA, nA);
+            if (p + 2 >= P) break;
+            fetch(min(p + 3, P - 1), amA, nA);
+            step(p + 1, amB, nB);
+            if (p + 3 >= P) break;
+            fetch(min(p + 4, P - 1), amB, nB);
+            step(p + 2, amC, nC);
+        }
     }
 }
 

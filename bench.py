@@ -69,21 +69,24 @@ PATHS = {
 def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16, n_seqs=0):
     """Which schedule kda_chunk_fwd runs for these sizes: for bf16 and d_k = d_v = 128 (any
     chunk size asked) the fused pass, one workgroup per (sequence, head) when there are at
-    least 256 pairs, else with segments of long sequences (maps, their composition, then the
-    segments) when a sequence is longer than one segment; otherwise the split prep + state
-    pass. Same rule as the library's dispatch."""
+    least 256 pairs; below that the planned pass, "segmented" when it cuts sequences (segment
+    0 of every sequence and the maps of the middle segments, their composition, then the
+    other segments): for equal lengths when the budget leaves more than one segment per
+    sequence, for packed ones (where the device plans) when the batch has 8 chunks or more;
+    otherwise the split prep + state pass. Same rule as the library's dispatch."""
     if not (bf16 and dk == dv == 128 and T > 0):
         return "split"
     n = n_seqs if varlen else B
     if n * H >= 256:
         return "fused"
-    chunks = (T + 63) // 64 + n_seqs if varlen else B * ((T + 63) // 64)
-    lc = 4
-    while lc < 1024 and lc * 2 * 256 <= chunks * H:
-        lc *= 2
-    seg = lc * 64
-    longer = T > seg if varlen else (T + seg - 1) // seg > 1
-    return "segmented" if longer else "fused"
+    u, c = 256 // H, (T + 63) // 64
+    if c < 8:
+        return "fused"
+    if varlen:
+        return "segmented"
+    units_a = lambda t: max(-(-c // t) - 1, 1) if c > t else 1  # noqa: E731
+    t = next(t for t in range(1, c + 1) if B * units_a(t) <= u)
+    return "segmented" if c > t else "fused"
 
 
 def sources_digest(names):

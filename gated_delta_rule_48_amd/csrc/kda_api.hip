@@ -38,12 +38,14 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // for equal-length and for packed sequences, whatever chunk size is asked (chunking
 // is an exact refactoring of the recurrence: 64 and 128 give the same results up to
 // rounding). When the (sequence, head) pairs alone fill the chip it runs one
-// workgroup per pair. Otherwise it cuts the sequences into segments of seg_len tokens
-// and runs one workgroup per (segment, head): first each segment's map S_out = M S_in
-// + N, then their composition in order, then every segment from its entering state.
-// Other inputs (fp32, d = 64) take the split pass (parallel chunk preparation, then
-// state propagation over d_v slices) at the asked chunk size.
+// workgroup per pair. Otherwise it cuts the sequences into segments and runs one
+// workgroup per (segment, head) in two launches of at most one workgroup per compute
+// unit: segment 0 of every sequence with its outputs and the maps S_out = M S_in + N
+// of the middle segments, then (after the maps' composition) the other segments from
+// their entering states. Other inputs (fp32, d = 64) take the split pass (parallel
+// chunk preparation, then state propagation over d_v slices) at the asked chunk size.
 constexpr int kFusedMinPairs = 256;
+constexpr int kComputeUnits = 256;  // MI355X
 bool use_fused(int B, int T, int H, int dk, int dv, int C, bool varlen, int io, int n_seqs) {
     (void)B;
     (void)H;
@@ -54,34 +56,37 @@ bool use_fused(int B, int T, int H, int dk, int dv, int C, bool varlen, int io, 
 }
 
 struct FusedPlan {
-    int seg_len;       // tokens per segment (0: one workgroup per (sequence, head))
-    int segs_per_seq;  // equal-length sequences: segments of each
-    int n_seg;         // upper bound on the number of segments
+    int u;      // units per head in each of the two launches (0: no segments)
+    int T;      // equal-length sequences: the budget (chunks per unit)
+    int P;      // equal-length sequences: segments of each
+    int slots;  // segment slots per head (entering states and maps): at least launch C's units
 };
 
-// Segments of 4 to 1024 chunks of 64 tokens, the longest for which the (segment, head)
-// pairs still number at least 256 (one per compute unit): the maps cost about as much as
-// the segments' own pass, and longer segments leave fewer of them (on 4 packed sequences of
-// 32,768 to 4,096 tokens x 32 heads, 128-chunk segments took 1.37 ms against 1.40 ms at 64
-// and 1.50 ms at 32; on 1 x 4,096 tokens x 16 heads the rule gives 4-chunk segments, 98 us
-// against 112 us at 8 and 149 us at 2).
+// Below 256 (sequence, head) pairs the pass runs on the plan (kda_internal.hpp): per head u =
+// 256 / H units in each of two launches. For packed sequences the device works out the plan
+// from the offsets (kda_seg_plan_kernel); for B equal sequences of c chunks the host does:
+// the smallest budget T for which B plan_units_a(c, T) <= u. Both launches then take about T
+// chunk-steps (the 4 packed sequences of 32,768 + 16,384 + 12,288 + 4,096 tokens x 32 heads:
+// T = 103 of their 1,024 chunks per head, 8 units in launch A and 7 in launch C; 1 x 4,096
+// tokens x 16 heads: T = 4, 15 units each). Sequences of fewer than kMinSegChunks chunks are
+// not cut (T = the longest: one unit per sequence): below that the composition and the
+// second launch cost about what the segments save. Either way the usual body runs in the
+// same kernel, so equal-length and packed layouts of the same sequences agree bit for bit.
 FusedPlan fused_plan(int B, int T, int H, bool varlen, int n_seqs) {
     const int64_t pairs = (int64_t)(varlen ? n_seqs : B) * H;
-    const int n_seq = varlen ? n_seqs : B;
-    FusedPlan none{0, 1, n_seq};
-    if (pairs >= kFusedMinPairs || T <= 0) return none;
-    const int64_t chunks = varlen ? ((int64_t)T + 63) / 64 + n_seqs : (int64_t)B * (((int64_t)T + 63) / 64);
-    const int64_t work = chunks * H;
-    int64_t lc = 4;
-    while (lc < 1024 && lc * 2 * 256 <= work) lc *= 2;
-    const int seg_len = (int)(lc * 64);
-    if (!varlen) {
-        const int sps = (T + seg_len - 1) / seg_len;
-        if (sps <= 1) return none;
-        return FusedPlan{seg_len, sps, B * sps};
+    if (pairs >= kFusedMinPairs || T <= 0) return FusedPlan{0, 0, 0, 0};
+    const int u = kComputeUnits / H;  // (>= the number of sequences: fewer than 256 pairs)
+    const int64_t c = ((int64_t)T + 63) / 64;  // chunks of one sequence, or at most of a packed one
+    // (launch C's units have a chunk each at least: no more than the chunks of all sequences)
+    if (varlen) return FusedPlan{u, 0, 0, (int)std::min<int64_t>(u, c + n_seqs)};
+    int lo = 1, hi = (int)c;
+    if (c < kda::kMinSegChunks) lo = hi;
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if ((int64_t)B * kda::plan_units_a((int)c, mid) <= u) hi = mid; else lo = mid + 1;
     }
-    if (T <= seg_len) return none;
-    return FusedPlan{seg_len, 0, (T + seg_len - 1) / seg_len + n_seqs};
+    const int P = kda::plan_segments((int)c, lo);
+    return FusedPlan{u, lo, P, B * (P - 1)};
 }
 
 struct WsLayout {
@@ -106,13 +111,13 @@ bool ws_layout(int B, int T, int H, int dk, int dv, int C, int n_seqs, bool varl
         // the discard slot; one byte per (sequence or segment, head): left to the strong-decay
         // instance; with segments, their table, entering states and maps (fp32, 64 KB each)
         const FusedPlan fp = fused_plan(B, T, H, varlen, n_seqs);
-        const size_t units = (size_t)fp.n_seg * H;
+        const size_t slots = (size_t)fp.slots * H;
         L->discard = take(256);
-        L->strong = take(units);
-        if (fp.seg_len > 0) {
-            L->seg_tab = varlen ? take(((size_t)3 * n_seqs + 1) * sizeof(int32_t)) : 0;
-            L->seg_state = take(units * dk * dv * sizeof(float));
-            L->seg_map = take(units * 2 * dk * dv * sizeof(float));
+        L->strong = take(fp.u > 0 ? (size_t)2 * fp.u * H : (size_t)(varlen ? n_seqs : B) * H);
+        if (fp.u > 0) {
+            L->seg_tab = varlen ? take((size_t)kda::PlanTab::ints(n_seqs) * sizeof(int32_t)) : 0;
+            L->seg_state = take(slots * dk * dv * sizeof(float));
+            L->seg_map = take(slots * 2 * dk * dv * sizeof(float));
         }
         L->total = off;
         return true;
@@ -274,23 +279,21 @@ int chunk_fwd_impl(int gate, const kda::PreactArgs &pre, int B, int T, int H, in
         kda::FusedArgs fa{q,  k,     v,  log_alpha, beta, scale, h0, hT,   o, ws + L.discard, H,
                           T,  varlen ? cu_seqlens : nullptr, (int)tokens, gate, pre,
                           reinterpret_cast<uint8_t *>(ws + L.strong)};
-        fa.seg_len = fp.seg_len;
         fa.n_seqs = nseq;
-        fa.segs_per_seq = fp.segs_per_seq;
-        if (fp.seg_len > 0) {
+        fa.plan_u = fp.u;
+        fa.plan_T = fp.T;
+        fa.plan_P = fp.P;
+        if (fp.u > 0) {
             fa.seg_state = reinterpret_cast<float *>(ws + L.seg_state);
             fa.seg_map = reinterpret_cast<float *>(ws + L.seg_map);
             if (varlen) {
                 int32_t *tab = reinterpret_cast<int32_t *>(ws + L.seg_tab);
-                fa.seg_off = tab;
-                fa.seg_tb = tab + n_seqs + 1;
-                fa.seg_te = tab + 2 * n_seqs + 1;
-                if (kda::launch_chunk_offsets(cu_seqlens, n_seqs, (int)tokens, fp.seg_len, tab, tab + n_seqs + 1,
-                                              tab + 2 * n_seqs + 1, hs, 1) != hipSuccess)
+                fa.plan_tab = tab;
+                if (kda::launch_seg_plan(cu_seqlens, n_seqs, (int)tokens, fp.u, tab, hs) != hipSuccess)
                     return KDA_ERR_HIP;
             }
         }
-        return kda::launch_fused(fa, d_k, d_v, bf, nseq, fp.n_seg, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        return kda::launch_fused(fa, d_k, d_v, bf, nseq, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     ChunkBuffers buf{};
     if (L.total > 0) {

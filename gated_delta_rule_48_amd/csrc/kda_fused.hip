@@ -199,22 +199,36 @@ __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb 
     (void)hi;                                                                  \
     (void)r;
 
-// Instances (kMode):
-//   kUsual  the usual pass. Where a chunk's decay sums below -kStrongDecay on some channel
-//           (the midpoint factors would leave the fp32 range), it records the (sequence,
-//           head) in a.redo and stops.
-//   kStrongPass  runs after it, on the recorded pairs only, from the start of the
-//           sequence, with every exponent <= 0: the state-side factors taken from the
+// Bodies (kMode):
+//   kUsual  the usual pass over one run of chunks (a whole sequence, or a segment of one).
+//           Where a chunk's decay sums below -kStrongDecay on some channel (the midpoint
+//           factors would leave the fp32 range), it flags its unit and stops.
+//   kStrongPass  runs after it, on the flagged (sequence, head) pairs only, from the start
+//           of the sequence, with every exponent <= 0: the state-side factors taken from the
 //           chunk's start, the Gram tiles left of the diagonal from the end of their column
 //           block, the diagonal tiles pair by pair.
-//   kMap    for a segment of a long sequence: its map S_out = M S_in + N, with M (d_k x d_k)
-//           carried from I and N from h0 (first segment) or zero through the segment's
-//           chunks as a second state, no outputs. A segment with a chunk of strong decay
-//           stops; its pair is run again by the strong instance.
-constexpr int kUsual = 0, kStrongPass = 1, kMap = 2;
+//   kMap    for a middle segment of a long sequence: its map S_out = M S_in + N, with M
+//           (d_k x d_k) carried from I and N from zero through the segment's chunks as a
+//           second state, no outputs. A chunk of strong decay flags the unit and stops.
+// Kernels (the same template argument): kUsual over the (sequence, head) pairs, kStrongPass
+// over the pairs, and with segments kPlanA (segment 0 of every sequence with the kUsual body,
+// the maps of segments 1 .. P - 2 with the kMap body) and kPlanC (segments 1 .. P - 1 with
+// the kUsual body, each from its entering state).
+constexpr int kUsual = 0, kStrongPass = 1, kMap = 2, kPlanA = 3, kPlanC = 4;
+
+// One workgroup's run of chunks.
+struct Unit {
+    int h;
+    size_t seq0;          // its first token
+    int T_len;            // its tokens
+    const float *h0src;   // the state it starts from ([d_k][d_v] fp32), or null (zero)
+    float *out_state;     // where the state at its end goes ([d_k][d_v] fp32), or null
+    float *map_out;       // kMap: M and N (seg_m_index, seg_n_index)
+    uint8_t *redo;        // its flag: 1 if it left its pair to the strong instance, else 0
+};
 
 template <int G, int kMode>
-__global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
+__device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
     constexpr bool kStrong = kMode == kStrongPass;
     constexpr bool kMapMode = kMode == kMap;
     // G: the kda_gate kinds, kGatePreact, and kGatePreactQK (kGatePreact with q and k
@@ -247,76 +261,14 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     float *saq = reinterpret_cast<float *>(smem + Lds::SAQ);
 
     const int H = a.H;
-    int s = blockIdx.x / H;
-    const int h = blockIdx.x % H;
-    // segments of this sequence: before this workgroup's and in all (1, 1 without segments)
-    int seg_p = 0, seg_n = 1;
-    if (a.seg_len > 0 && !kStrong) {  // (the strong instance runs whole pairs: one workgroup each)
-        // the workgroup runs segment gi (of all sequences): find its sequence
-        const int gi = blockIdx.x / H;
-        if (a.cu_seqlens) {
-            if (gi >= a.seg_off[a.n_seqs]) return;  // past the last segment
-            int lo = 0, hi2 = a.n_seqs - 1;  // last s with seg_off[s] <= gi (empty sequences have one)
-            while (lo < hi2) {
-                const int mid = (lo + hi2 + 1) >> 1;
-                if (a.seg_off[mid] <= gi) lo = mid; else hi2 = mid - 1;
-            }
-            s = lo;
-            seg_p = gi - a.seg_off[s];
-            seg_n = a.seg_off[s + 1] - a.seg_off[s];
-        } else {
-            s = gi / a.segs_per_seq;
-            if (s >= a.n_seqs) return;
-            seg_p = gi - s * a.segs_per_seq;
-            seg_n = a.segs_per_seq;
-        }
-    }
-    if constexpr (kStrong) {
-        // the usual instance finished this pair unless it flagged it (or one of its segments)
-        bool any = false;
-        if (a.seg_len > 0) {
-            const int g0 = a.cu_seqlens ? a.seg_off[s] : s * a.segs_per_seq;
-            const int gn = a.cu_seqlens ? a.seg_off[s + 1] : g0 + a.segs_per_seq;
-            for (int gi = g0; gi < gn; ++gi) any |= a.redo[(size_t)gi * H + h] != 0;
-        } else {
-            any = a.redo[blockIdx.x] != 0;
-        }
-        if (!any) return;
-    }
-    if constexpr (kMapMode) {
-        if (seg_p >= seg_n - 1) return;  // the last segment's map is not needed
-    }
+    const int h = u.h;
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, hi = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rb = w & 3, hf = w >> 2;
     const float scale = a.scale;
-    // this sequence's tokens: seq_len each, or packed at the (clamped) offsets cu_seqlens
-    // (with segments, the segment's part of them)
-    int T_len = a.seq_len;
-    size_t seq0 = (size_t)s * T_len;
-    if (a.seg_len > 0 && !kStrong) {
-        const int tb = a.cu_seqlens ? a.seg_tb[s] : s * a.seq_len;
-        const int te = a.cu_seqlens ? a.seg_te[s] : tb + a.seq_len;
-        const int t_beg = min(tb + seg_p * a.seg_len, te);
-        T_len = min(a.seg_len, te - t_beg);
-        seq0 = T_len > 0 ? (size_t)t_beg : 0;
-    } else if (a.cu_seqlens) {
-        const int b0 = min(max(a.cu_seqlens[s], 0), a.T_total);
-        const int b1 = min(max(a.cu_seqlens[s + 1], b0), a.T_total);
-        T_len = b1 - b0;
-        // an empty sequence runs no chunk; its first chunk's loads (issued before the
-        // loop) then read row 0 of the batch, which exists, and are never used
-        seq0 = T_len > 0 ? (size_t)b0 : 0;
-    }
-    // the state this workgroup starts from: h0 of the sequence (its first segment), or the
-    // state entering the segment; it writes hT only if it runs the sequence's end
-    const float *h0src = nullptr;
-    if (seg_p == 0 || kStrong) {
-        h0src = a.h0 ? a.h0 + ((size_t)s * H + h) * kDK * kDV : nullptr;
-    } else if constexpr (!kMapMode) {
-        h0src = a.seg_state + (size_t)blockIdx.x * kDK * kDV;
-    }
-    const bool writes_hT = a.hT && (kStrong || seg_p == seg_n - 1);
+    const int T_len = u.T_len;
+    const size_t seq0 = u.seq0;
+    const float *h0src = u.h0src;
     const int n_c = (T_len + kC - 1) / kC;
     const int T_ld = max(T_len, 1);  // the rows the loads may touch (row 0 for an empty sequence)
 
@@ -574,10 +526,9 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         __syncthreads();
         if constexpr (!kStrong) {
-            // a chunk of strong decay: the pair is left to the strong instance (a segment's
-            // map is then not needed: the workgroup that runs the segment records it)
+            // a chunk of strong decay: the pair is left to the strong instance
             if (__builtin_amdgcn_readfirstlane(flg[2] | flg[3]) != 0) {
-                if (!kMapMode && tid == 0) a.redo[blockIdx.x] = 1;
+                if (tid == 0) *u.redo = 1;
                 return;
             }
         }
@@ -1263,7 +1214,7 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         __syncthreads();
         if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
         __syncthreads();
-        float *mp = a.seg_map + (size_t)blockIdx.x * 2 * kDK * kDV;
+        float *mp = u.map_out;
         const int cc = chan_of_pos(16 * w + lr);
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) {
@@ -1275,12 +1226,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
                 mp[kDK * kDK + seg_n_index(chan_of_pos(p), cc)] = e * accS[tm][i];
             }
         }
+        if (tid == 0) *u.redo = 0;  // no chunk of strong decay in this segment
         return;
     } else if constexpr (!kStrong) {
-        if (tid == 0) a.redo[blockIdx.x] = 0;  // no chunk of strong decay in this pair
+        if (tid == 0) *u.redo = 0;  // no chunk of strong decay in this run
     } else {
-        if (a.hT) {
-            float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
+        if (u.out_state) {
+            float *hT = u.out_state + chan_of_pos(16 * w + lr);
 #pragma unroll
             for (int tm = 0; tm < 8; ++tm)
 #pragma unroll
@@ -1288,13 +1240,13 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
         }
         return;
     }
-    if (writes_hT) {
+    if (u.out_state) {
         // S = E_last Q: the factor exp(gamma / 2) of the last chunk, once every wave has
         // read that chunk's factors
         __syncthreads();
         if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
         __syncthreads();
-        float *hT = a.hT + ((size_t)s * H + h) * kDK * kDV + chan_of_pos(16 * w + lr);
+        float *hT = u.out_state + chan_of_pos(16 * w + lr);
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) {
             const f32x4 e4 = {ehalf[e_slot(16 * tm + 4 * hi)], ehalf[e_slot(16 * tm + 4 * hi + 1)],
@@ -1305,57 +1257,206 @@ __global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
     }
 }
 
+// Segment p of sequence s under the plan: its token range [*beg, *beg + *len).
+__device__ __forceinline__ void plan_range(int tb, int te, int T, int p, size_t *beg, int *len) {
+    int sc, lc;
+    plan_segment_chunks((te - tb + kC - 1) / kC, T, p, &sc, &lc);
+    const int b = min(tb + sc * kC, te);
+    *beg = (size_t)b;
+    *len = min(tb + (sc + lc) * kC, te) - b;
+}
+
+// The plan's view of sequence s: token range, segments, and its units in launches A
+// and C ([a0, a1), [c0, c1)).
+struct PlanSeq {
+    int tb, te, T, P, a0, a1, c0, c1;
+};
+__device__ __forceinline__ PlanSeq plan_seq(const FusedArgs &a, int s) {
+    PlanSeq q;
+    if (a.plan_tab) {
+        const PlanTab t{a.plan_tab, a.n_seqs};
+        q.tb = t.tb()[s];
+        q.te = t.te()[s];
+        q.T = t.T();
+        q.P = plan_segments((q.te - q.tb + kC - 1) / kC, q.T);
+        q.a0 = t.a_off()[s];
+        q.a1 = t.a_off()[s + 1];
+        q.c0 = t.c_off()[s];
+        q.c1 = t.c_off()[s + 1];
+    } else {
+        q.tb = s * a.seq_len;
+        q.te = q.tb + a.seq_len;
+        q.T = a.plan_T;
+        q.P = a.plan_P;
+        const int ua = max(q.P - 1, 1);
+        q.a0 = s * ua;
+        q.a1 = q.a0 + ua;
+        q.c0 = s * (q.P - 1);
+        q.c1 = q.c0 + q.P - 1;
+    }
+    return q;
+}
+
+// The sequence that unit u of a launch belongs to: the last s with off[s] <= u (sequences
+// without units in that launch have off[s] = off[s + 1] and are passed over).
+__device__ __forceinline__ int plan_find(const int32_t *off, int n, int u) {
+    int lo = 0, hi2 = n - 1;
+    while (lo < hi2) {
+        const int mid = (lo + hi2 + 1) >> 1;
+        if (off[mid] <= u) lo = mid; else hi2 = mid - 1;
+    }
+    return lo;
+}
+
+template <int G, int kMode>
+__global__ __launch_bounds__(kNT) void kda_fused_kernel(FusedArgs a) {
+    const int H = a.H;
+    const size_t DD = (size_t)kDK * kDV;
+    if constexpr (kMode == kUsual) {
+        // one workgroup per (sequence, head): equal lengths, or packed at the (clamped)
+        // offsets cu_seqlens
+        const int s = blockIdx.x / H, h = blockIdx.x % H;
+        Unit u;
+        u.h = h;
+        u.T_len = a.seq_len;
+        u.seq0 = (size_t)s * a.seq_len;
+        if (a.cu_seqlens) {
+            const int b0 = min(max(a.cu_seqlens[s], 0), a.T_total);
+            const int b1 = min(max(a.cu_seqlens[s + 1], b0), a.T_total);
+            u.T_len = b1 - b0;
+            // an empty sequence runs no chunk; its first chunk's loads (issued before the
+            // loop) then read row 0 of the batch, which exists, and are never used
+            u.seq0 = u.T_len > 0 ? (size_t)b0 : 0;
+        }
+        u.h0src = a.h0 ? a.h0 + ((size_t)s * H + h) * DD : nullptr;
+        u.out_state = a.hT ? a.hT + ((size_t)s * H + h) * DD : nullptr;
+        u.map_out = nullptr;
+        u.redo = a.redo + blockIdx.x;
+        fused_body<G, kUsual>(a, u);
+    } else if constexpr (kMode == kStrongPass) {
+        // the whole pair again, from h0, if any of its units flagged it
+        const int s = blockIdx.x / H, h = blockIdx.x % H;
+        Unit u;
+        u.h = h;
+        bool any = false;
+        if (a.plan_u > 0) {
+            const PlanSeq q = plan_seq(a, s);
+            for (int i = q.a0; i < q.a1; ++i) any |= a.redo[(size_t)i * H + h] != 0;
+            for (int i = q.c0; i < q.c1; ++i) any |= a.redo[(size_t)(a.plan_u + i) * H + h] != 0;
+            u.T_len = q.te - q.tb;
+            u.seq0 = u.T_len > 0 ? (size_t)q.tb : 0;
+        } else {
+            any = a.redo[blockIdx.x] != 0;
+            u.T_len = a.seq_len;
+            u.seq0 = (size_t)s * a.seq_len;
+            if (a.cu_seqlens) {
+                const int b0 = min(max(a.cu_seqlens[s], 0), a.T_total);
+                const int b1 = min(max(a.cu_seqlens[s + 1], b0), a.T_total);
+                u.T_len = b1 - b0;
+                u.seq0 = u.T_len > 0 ? (size_t)b0 : 0;
+            }
+        }
+        if (!any) return;
+        u.h0src = a.h0 ? a.h0 + ((size_t)s * H + h) * DD : nullptr;
+        u.out_state = a.hT ? a.hT + ((size_t)s * H + h) * DD : nullptr;
+        u.map_out = nullptr;
+        u.redo = nullptr;
+        fused_body<G, kStrongPass>(a, u);
+    } else {
+        // launch A (segment 0 of every sequence, the maps of its middle segments) or C
+        // (segments 1 .. P - 1): unit ui of head h
+        const int ui = blockIdx.x / H, h = blockIdx.x % H;
+        int s, j;
+        if (a.plan_tab) {
+            const PlanTab t{a.plan_tab, a.n_seqs};
+            const int32_t *off = kMode == kPlanA ? t.a_off() : t.c_off();
+            if (ui >= off[a.n_seqs]) return;
+            s = plan_find(off, a.n_seqs, ui);
+            j = ui - off[s];
+        } else {
+            const int per = kMode == kPlanA ? max(a.plan_P - 1, 1) : a.plan_P - 1;
+            if (per <= 0) return;
+            s = ui / per;
+            j = ui - s * per;
+            if (s >= a.n_seqs) return;
+        }
+        const PlanSeq q = plan_seq(a, s);
+        const int p = kMode == kPlanA ? j : j + 1;  // the segment
+        Unit u;
+        u.h = h;
+        plan_range(q.tb, q.te, q.T, p, &u.seq0, &u.T_len);
+        if (u.T_len <= 0) u.seq0 = 0;  // (an empty sequence: row 0 is read, never used)
+        u.map_out = nullptr;
+        u.redo = a.redo + (size_t)((kMode == kPlanA ? 0 : a.plan_u) + ui) * H + h;
+        // slot of segment p >= 1: the state entering it, and its map
+        auto slot = [&](int pp) { return (size_t)(q.c0 + pp - 1) * H + h; };
+        float *hT_pair = a.hT ? a.hT + ((size_t)s * H + h) * DD : nullptr;
+        if constexpr (kMode == kPlanC) {
+            u.h0src = a.seg_state + slot(p) * DD;
+            u.out_state = p == q.P - 1 ? hT_pair : nullptr;
+            fused_body<G, kUsual>(a, u);
+        } else {
+            // (the condition is uniform and opaque to the compiler: otherwise it kept values
+            // of one body live across the other, in scratch)
+            int first = __builtin_amdgcn_readfirstlane(p == 0 ? 1 : 0);
+            asm volatile("" : "+s"(first));
+            if (first) {
+                u.h0src = a.h0 ? a.h0 + ((size_t)s * H + h) * DD : nullptr;
+                u.out_state = q.P == 1 ? hT_pair : a.seg_state + slot(1) * DD;
+                fused_body<G, kUsual>(a, u);
+            } else {
+                u.h0src = nullptr;
+                u.out_state = nullptr;
+                u.map_out = a.seg_map + slot(p) * 2 * DD;
+                fused_body<G, kMap>(a, u);
+            }
+        }
+    }
+}
+
 }  // namespace
 
-hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, int n_seg_grid,
-                        hipStream_t stream) {
+hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream) {
     // the fused pass is built for bf16 input and d_k = d_v = 128 only
     if (!bf16 || dk != kDK || dv != kDV) return hipErrorInvalidValue;
     constexpr size_t smem = Lds::SIZE;
     // Without segments: the usual instance over the (sequence, head) pairs, then the strong
-    // one over the pairs the first left to it. With segments: the maps of the segments, their
-    // composition, the usual instance over the (segment, head) pairs, then the strong one over
-    // the (sequence, head) pairs any of whose segments was left to it. (Without a decay, no
-    // chunk can leave anything to the strong instance.)
+    // one over the pairs the first left to it. With segments: launch A (segment 0 of every
+    // sequence and the maps of the middle segments), the composition of the maps, launch C
+    // (segments 1 .. P - 1), then the strong instance over the (sequence, head) pairs any of
+    // whose units was left to it. (Without a decay, no chunk can leave anything to it.)
     typedef void (*Kern)(FusedArgs);
-    Kern usual, strong, map;
-    if (a.gate == kGateHead) {
-        usual = kda_fused_kernel<kGateHead, kUsual>;
-        strong = kda_fused_kernel<kGateHead, kStrongPass>;
-        map = kda_fused_kernel<kGateHead, kMap>;
-    } else if (a.gate == kGateNone) {
-        usual = kda_fused_kernel<kGateNone, kUsual>;
-        strong = nullptr;
-        map = kda_fused_kernel<kGateNone, kMap>;
-    } else if (a.gate == kGatePreact && a.pre.qk_norm) {
-        usual = kda_fused_kernel<kGatePreactQK, kUsual>;
-        strong = kda_fused_kernel<kGatePreactQK, kStrongPass>;
-        map = kda_fused_kernel<kGatePreactQK, kMap>;
-    } else if (a.gate == kGatePreact) {
-        usual = kda_fused_kernel<kGatePreact, kUsual>;
-        strong = kda_fused_kernel<kGatePreact, kStrongPass>;
-        map = kda_fused_kernel<kGatePreact, kMap>;
-    } else {
-        usual = kda_fused_kernel<kGateChannel, kUsual>;
-        strong = kda_fused_kernel<kGateChannel, kStrongPass>;
-        map = kda_fused_kernel<kGateChannel, kMap>;
-    }
-    auto go = [&](Kern k, int grid) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+    struct Set { Kern usual, strong, plan_a, plan_c; };
+    auto set_of = [](auto gt) {
+        constexpr int Gk = decltype(gt)::value;
+        Set r{kda_fused_kernel<Gk, kUsual>, nullptr, kda_fused_kernel<Gk, kPlanA>, kda_fused_kernel<Gk, kPlanC>};
+        if constexpr (Gk != kGateNone) r.strong = kda_fused_kernel<Gk, kStrongPass>;
+        return r;
+    };
+    Set k;
+    if (a.gate == kGateHead) k = set_of(IntTag<kGateHead>{});
+    else if (a.gate == kGateNone) k = set_of(IntTag<kGateNone>{});
+    else if (a.gate == kGatePreact && a.pre.qk_norm) k = set_of(IntTag<kGatePreactQK>{});
+    else if (a.gate == kGatePreact) k = set_of(IntTag<kGatePreact>{});
+    else k = set_of(IntTag<kGateChannel>{});
+    auto go = [&](Kern kern, int grid) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(k, dim3(grid), dim3(kNT), smem, stream, a);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kNT), smem, stream, a);
         return hipGetLastError();
     };
     hipError_t err;
-    if (a.seg_len > 0) {
-        if ((err = go(map, n_seg_grid * a.H)) != hipSuccess) return err;
-        if ((err = launch_segment_chain(a, stream)) != hipSuccess) return err;
-        if ((err = go(usual, n_seg_grid * a.H)) != hipSuccess) return err;
+    if (a.plan_u > 0) {
+        if ((err = go(k.plan_a, a.plan_u * a.H)) != hipSuccess) return err;
+        if (a.plan_tab || a.plan_P > 1) {  // (equal lengths in one segment each: nothing more)
+            if ((err = launch_segment_chain(a, stream)) != hipSuccess) return err;
+            if ((err = go(k.plan_c, a.plan_u * a.H)) != hipSuccess) return err;
+        }
     } else {
-        if ((err = go(usual, n_seqs * a.H)) != hipSuccess) return err;
+        if ((err = go(k.usual, n_seqs * a.H)) != hipSuccess) return err;
     }
-    if (strong && (err = go(strong, n_seqs * a.H)) != hipSuccess) return err;
+    if (k.strong && (err = go(k.strong, n_seqs * a.H)) != hipSuccess) return err;
     return hipSuccess;
 }
 

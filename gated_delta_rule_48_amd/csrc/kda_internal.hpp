@@ -89,19 +89,29 @@ struct FusedArgs {
     int T_total;
     int gate;       // as in PrepArgs
     PreactArgs pre;
-    uint8_t *redo;  // [n_seqs * H] (or [n_seg * H] with segments): 1 where the usual instance met
-                    // a chunk of strong decay and left the (sequence, head) to the strong instance
-    // Segments: each sequence cut into runs of seg_len tokens (a multiple of 64), one
-    // workgroup per (segment, head); seg_len = 0: one workgroup per (sequence, head).
-    int seg_len;
+    uint8_t *redo;  // one byte per unit (see below): 1 where the unit met a chunk of strong decay
+                    // and left its (sequence, head) to the strong instance
+    // Segments (plan_u > 0: fewer (sequence, head) pairs than compute units). Each sequence of
+    // c chunks is cut, for a budget of plan_T chunks, into P = max(1, ceil(c / plan_T))
+    // segments: segment 0 of min(c, plan_T) chunks, then P - 1 near-equal ones. Launch A runs,
+    // per head, every sequence's segment 0 (outputs, and the state at its end) and the maps of
+    // segments 1 .. P - 2 (S_out = M S_in + N, from S_in = 0); the composition then forms the
+    // states entering segments 2 .. P - 1; launch C runs segments 1 .. P - 1 from their
+    // entering states. Each launch has at most plan_u units per head (one per compute unit).
+    // The budget is the longest sequence (one segment each: launch A alone does the work) if
+    // that has fewer than kMinSegChunks chunks. plan_u = 0 (256 pairs or more): one workgroup
+    // per (sequence, head), redo [n_seqs * H].
+    int plan_u;
+    int plan_T;               // equal-length sequences: the budget (chunks)
+    int plan_P;               // equal-length sequences: segments of each
+    const int32_t *plan_tab;  // packed sequences: the plan (PlanTab layout), written by kda_seg_plan_kernel
     int n_seqs;
-    int segs_per_seq;          // equal-length sequences: segments of each
-    const int32_t *seg_off;    // packed sequences: [n_seqs + 1] segments before each sequence,
-    const int32_t *seg_tb;     // then each sequence's clamped begin and end ([n_seqs] each)
-    const int32_t *seg_te;
-    float *seg_state;          // [n_seg, H, d_k, d_v] fp32: the state entering each segment (p > 0)
-    float *seg_map;            // [n_seg, H, 2, d_k * d_k] fp32: M and N of each segment (S_out = M S_in + N),
-                               // in the order the composition reads them (seg_m_index, seg_n_index)
+    float *seg_state;  // [slots, H, d_k, d_v] fp32: the state entering segment p >= 1 (slot of the segment)
+    float *seg_map;    // [slots, H, 2, d_k * d_k] fp32: M and N of segment p = 1 .. P - 2 (its slot),
+                       // in the order the composition reads them (seg_m_index, seg_n_index)
+    // With segments, redo holds [2 plan_u, H]: launch A's unit u at u H + h, launch C's at
+    // (plan_u + u) H + h. The slot of segment p >= 1 of sequence s is the index of its unit in
+    // launch C: c_off(s) + p - 1.
 };
 
 // Positions of M[r][c] and N[r][c] (d_k = d_v = 128, channel order) within a segment's map.
@@ -115,9 +125,52 @@ __host__ __device__ constexpr int seg_n_index(int r, int c) {
     return (((c >> 4) * 8 + (r >> 4)) * 4 + (r & 3)) * 64 + (c & 15) + 16 * ((r >> 2) & 3);
 }
 
-// The composition of segment maps: per (sequence, head, 16 value columns), in order,
-// S_in(1) = N(0) (segment 0's map starts from h0) and S_in(p + 1) = M(p) S_in(p) + N(p).
+// The plan table of packed sequences (n = n_seqs): [0] the budget T (chunks); then a_off
+// [n + 1] (launch A's units before each sequence), c_off [n + 1] (launch C's), tb [n] and te
+// [n] (each sequence's token range, clamped to [0, T_total] and made monotone).
+struct PlanTab {
+    static constexpr int ints(int n) { return 4 * n + 3; }
+    const int32_t *t;
+    int n;
+    __host__ __device__ int T() const { return t[0]; }
+    __host__ __device__ const int32_t *a_off() const { return t + 1; }
+    __host__ __device__ const int32_t *c_off() const { return t + n + 2; }
+    __host__ __device__ const int32_t *tb() const { return t + 2 * n + 3; }
+    __host__ __device__ const int32_t *te() const { return t + 3 * n + 3; }
+};
+
+// Sequences are cut into segments only if the longest has this many chunks or more.
+constexpr int kMinSegChunks = 8;
+
+// Segments of a sequence of c chunks under budget T, and its units in launch A (segment 0
+// and the maps of segments 1 .. P - 2; at least one unit, for segment 0).
+__host__ __device__ inline int plan_segments(int c, int T) { return c <= T ? 1 : (c + T - 1) / T; }
+__host__ __device__ inline int plan_units_a(int c, int T) {
+    const int P = plan_segments(c, T);
+    return P > 1 ? P - 1 : 1;
+}
+
+// Chunk range [*sc, *sc + *lc) of segment p of a sequence of c chunks under budget T.
+__host__ __device__ inline void plan_segment_chunks(int c, int T, int p, int *sc, int *lc) {
+    const int f = c < T ? c : T;
+    if (p == 0) {
+        *sc = 0;
+        *lc = f;
+        return;
+    }
+    const int parts = plan_segments(c, T) - 1, R = c - f, q = R / parts, e = R % parts;
+    *sc = f + (p - 1) * q + (p - 1 < e ? p - 1 : e);
+    *lc = q + (p - 1 < e ? 1 : 0);
+}
+
+// The composition of segment maps: per (sequence, head, 16 value columns) with P >= 3
+// segments, in order, S_in(p + 1) = M(p) S_in(p) + N(p) for p = 1 .. P - 2, from S_in(1)
+// (the state at the end of segment 0, written by launch A).
 hipError_t launch_segment_chain(const FusedArgs &a, hipStream_t stream);
+// The plan of packed sequences: clamped token ranges, the smallest budget T for which
+// every head's units in launch A number at most u_max, and the units' offsets.
+hipError_t launch_seg_plan(const int32_t *cu, int n_seqs, int T_total, int u_max, int32_t *tab,
+                           hipStream_t stream);
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -139,9 +192,7 @@ hipError_t launch_prep(const PrepArgs &a, int C, int dk, int dv, bool bf16, int 
                        hipStream_t stream);
 hipError_t launch_state(const StateArgs &a, int C, int dk, int dv, bool bf16, int n_seqs,
                         hipStream_t stream);
-// n_seg_grid: with segments (a.seg_len > 0), an upper bound on the number of segments
-hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, int n_seg_grid,
-                        hipStream_t stream);
+hipError_t launch_fused(const FusedArgs &a, int dk, int dv, bool bf16, int n_seqs, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int dk, int dv, bool bf16, hipStream_t stream);
 
 }  // namespace kda

@@ -121,9 +121,12 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int 
  *               The fused pass (bf16, d_k = d_v = 128) works in chunks of 64
  *               rows for either value; since chunking is exact, only rounding
  *               differs. With fewer than 256 (sequence, head) pairs the fused
- *               pass cuts long sequences into segments: the affine map each
- *               segment applies to its entering state, the maps composed in
- *               order, then every segment again from its own entering state.
+ *               pass cuts long sequences into segments sized so that two
+ *               launches of at most one workgroup per compute unit cover them:
+ *               segment 0 of every sequence together with the affine maps the
+ *               middle segments apply to their entering states, the maps
+ *               composed in order, then the other segments from their own
+ *               entering states.
  *   q, k, v     [B*T, H, d_k|d_k|d_v], dtype io.
  *   log_alpha   [B*T, H, d_k] fp32, log of the per-channel decay (<= 0 normally).
  *   beta        [B*T, H] fp32, write strength.
@@ -176,7 +179,9 @@ int kda_chunk_fwd_gated(int gate, int B, int T, int H, int d_k, int d_v, int chu
  * rejected with KDA_ERR_WORKSPACE before anything is enqueued. The fused pass (bf16,
  * d_k = d_v = 128) with at least 256 (sequence, head) pairs needs 256 bytes plus one per
  * pair, so all such calls fit; with fewer pairs it cuts long sequences into segments and
- * needs 192 KB per (segment, head), which fits up to about 170 of them; split-pass calls
+ * needs 192 KB per (segment, head) after each sequence's first, which fits up to about 170
+ * of them (a sequence of fewer than 512 tokens is never cut, and at most 256 // H
+ * segments per head are used); split-pass calls
  * (fp32 or d = 64) fit up to about 25,000 to 30,000 token-heads at d = 128. The first call
  * on a device looks up the array's device address (KDA_ERR_HIP if that fails).
  *

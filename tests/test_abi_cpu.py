@@ -55,32 +55,25 @@ def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
     pairs = n_seq * H
     if esz == 2 and dk == dv == 128 and T > 0:
         # fused pass (equal-length or packed sequences, any chunk size asked): the 256-byte
-        # discard slot and one byte per (sequence or segment, head) for the strong-decay
-        # instance; below 256 pairs, segments of lc chunks of 64 tokens with their table,
-        # entering states and maps
-        seg_len, n_seg = 0, n_seq
-        if pairs < 256:
-            chunks = (T + 63) // 64 + n_seqs if n_seqs else B * ((T + 63) // 64)
-            lc = 4
-            while lc < 1024 and lc * 2 * 256 <= chunks * H:
-                lc *= 2
-            seg_len = lc * 64
-            if n_seqs:
-                if T <= seg_len:
-                    seg_len = 0
-                else:
-                    n_seg = (T + seg_len - 1) // seg_len + n_seqs
-            else:
-                sps = (T + seg_len - 1) // seg_len
-                if sps <= 1:
-                    seg_len = 0
-                else:
-                    n_seg = B * sps
-        total = 256 + r(n_seg * H)
-        if seg_len:
-            if n_seqs:
-                total += r((3 * n_seqs + 1) * 4)
-            total += r(n_seg * H * dk * dv * 4) + r(n_seg * H * 2 * dk * dv * 4)
+        # discard slot and a flag byte per unit for the strong-decay instance. From 256 pairs
+        # on, one unit per pair. Below, the plan: two launches of at most u = 256 // H units per
+        # head (2 u flag bytes per head), the plan table of packed sequences, and per segment
+        # slot an entering state and a map. Slots per head: packed, min(u, c + n_seqs) (launch
+        # C's units hold a chunk each at least); equal lengths, B (P - 1) for the smallest
+        # budget t with B (ceil(c / t) - 1, at least 1) <= u and P = ceil(c / t) segments (no
+        # cut, P = 1, below 8 chunks).
+        if pairs >= 256:
+            return 256 + r(n_seq * H)
+        u, c = 256 // H, (T + 63) // 64
+        total = 256 + r(2 * u * H)
+        if n_seqs:
+            slots = min(u, c + n_seqs)
+            total += r((4 * n_seqs + 3) * 4)
+        else:
+            ua = lambda t: max(-(-c // t) - 1, 1) if c > t else 1  # noqa: E731
+            t = c if c < 8 else next(t for t in range(1, c + 1) if B * ua(t) <= u)
+            slots = B * (-(-c // t) - 1)
+        total += r(slots * H * dk * dv * 4) + r(slots * H * 2 * dk * dv * 4)
         return total
     per = (T + C - 1) // C
     nch = (per + n_seqs if n_seqs else B * per) * H

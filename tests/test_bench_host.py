@@ -44,7 +44,7 @@ def test_digest_covers_the_compiled_sources():
 def test_pass_rule_matches_the_library():
     # the library's rule, read from its source and its workspace sizes: bf16 and d_k = d_v = 128
     # take the fused pass (any chunk size asked), with segments below 256 (sequence, head)
-    # pairs when a sequence is longer than a segment
+    # pairs when a sequence may have 8 chunks or more
     src = open(os.path.join(CSRC, "kda_api.hip")).read()
     assert "kFusedMinPairs = 256" in src
     bench = _bench()
@@ -55,13 +55,15 @@ def test_pass_rule_matches_the_library():
     assert bench.prefill_path(1, 200, 4, 128, 128, 64, False, True) == "fused"          # one segment: no maps
     assert bench.prefill_path(8, 8192, 32, 128, 128, 64, False, False) == "split"       # fp32
     assert bench.prefill_path(8, 8192, 32, 64, 64, 64, False, True) == "split"          # d = 64
-    # the workspace says the same: 256 bytes of discard slot and one byte per unit on the
-    # fused pass, more than 64 KB per segment with segments, per chunk on the split pass
+    # the workspace says the same: 256 bytes of discard slot and a flag byte per unit on the
+    # fused pass (two launches of 256 // H units per head below 256 pairs), with segments
+    # 192 KB per slot (entering state and map; 15 slots per head for 1 x 4096 tokens x 16
+    # heads), per chunk on the split pass
     import gated_delta_rule_48_amd as kda
     ws = lambda *a: kda.workspace_bytes(*a)  # noqa: E731
     assert ws(8, 8192, 32, 128, 128, 64, 0, kda.KDA_BF16) == 512
-    assert ws(1, 200, 4, 128, 128, 64, 0, kda.KDA_BF16) == 512
-    assert ws(1, 4096, 16, 128, 128, 64, 0, kda.KDA_BF16) > 16 * 16 * 3 * 65536
+    assert ws(1, 200, 4, 128, 128, 64, 0, kda.KDA_BF16) == 256 + 2 * 64 * 4  # planned, no slot
+    assert ws(1, 4096, 16, 128, 128, 64, 0, kda.KDA_BF16) > 15 * 16 * 3 * 65536
 
 
 def test_more_than_one_gpu_is_refused():

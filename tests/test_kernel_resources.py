@@ -57,7 +57,8 @@ def resources():
 
 def test_every_kernel_is_reported(resources):
     names = " ".join(resources)
-    for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_segment_chain_kernel", "kda_decode_kernel",
+    for k in ("kda_fused_kernel", "kda_prep_kernel", "kda_state_kernel", "kda_segment_chain_kernel", "kda_seg_plan_kernel",
+              "kda_decode_kernel",
               "kda_chunk_offsets_kernel", "kda_attn_decode_kernel", "kda_attn_combine_kernel",
               "kda_bwd_chunk_fwd_kernel", "kda_bwd_states_kernel", "kda_bwd_state_grads_kernel",
               "kda_bwd_chunk_grads_kernel", "kda_bwd_rev_kernel", "kda_bwd_chunk_kernel"):
@@ -67,7 +68,8 @@ def test_every_kernel_is_reported(resources):
 def _strong_fused(name):
     """The strong-decay instances of the fused kernel (kda_fused_kernel<G, 1>): they run only
     for (sequence, head) pairs with a chunk of strong decay, and their per-pair Gram work
-    spills; the usual (mode 0) and segment-map (mode 2) instances must not."""
+    spills; the usual instance (mode 0) and the two launches with segments (modes 3 and 4,
+    mode 3 holding the usual and the segment-map bodies) must not."""
     return "kda_fused_kernel" in name and "ELi1EEEv" in name
 
 
@@ -86,9 +88,9 @@ def test_no_scratch_and_no_spills(resources):
 
 def test_fused_kernel_runs_two_waves_per_simd(resources):
     fused = {n: r for n, r in resources.items() if "kda_fused_kernel" in n}
-    # the usual and the segment-map instances: per channel, per head, none, from
+    # the usual instance and the two launches with segments: per channel, per head, none, from
     # pre-activations (with q, k normalised or not); the strong-decay instances of all but "none"
-    assert sum(not _strong_fused(n) for n in fused) == 10 and sum(_strong_fused(n) for n in fused) == 4
+    assert sum(not _strong_fused(n) for n in fused) == 15 and sum(_strong_fused(n) for n in fused) == 4
     for n, r in fused.items():
         assert int(r["Occupancy [waves/SIMD]"]) >= 2, (n, r)
         assert int(r["VGPRs"]) <= 256, (n, r)

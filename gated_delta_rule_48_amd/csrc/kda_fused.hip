@@ -191,6 +191,50 @@ __device__ __forceinline__ bf16x8 fld(const bf16 *base, int kg, int rb, int R, i
 // Lane l's element offset in tile (rb, cb) of an accumulator-ordered [R][NC] matrix.
 __device__ __forceinline__ int ato(int rb, int cb, int NC, int l) { return ((rb * (NC >> 4) + cb) * 64 + l) * 4; }
 
+// States pass to and from memory through LDS (before the first chunk and after the last,
+// when no operand lives there): memory sees whole 16-byte pieces of consecutive rows, while
+// each lane's accumulator share (rows 16 tm + 4 hi + i of one column) is scattered in a row-
+// major state. Staging buffer: [d_k][kSP] fp32 from the start of LDS.
+constexpr int kSP = kDV + 4;
+static_assert(kDK * kSP * 4 <= 123 * 1024, "state staging below the identity operands");
+
+// accS <- the [d_k][d_v] fp32 state at src (row = key channel), in the permuted positions of
+// the accumulators (tile tm, lane (lr, hi) of wave w: rows 16 tm + 4 hi + i of column 16 w + lr).
+__device__ __forceinline__ void load_state(const float *src, f32x4 (&acc)[8], float *stg, int tid, int w, int lr,
+                                           int hi) {
+#pragma unroll
+    for (int k = 0; k < kDK * kDV / 4 / kNT; ++k) {
+        const int piece = tid + kNT * k, row = piece / (kDV / 4), c4 = piece % (kDV / 4);
+        *reinterpret_cast<f32x4 *>(stg + row * kSP + 4 * c4) =
+            *reinterpret_cast<const f32x4 *>(src + (size_t)row * kDV + 4 * c4);
+    }
+    __syncthreads();
+    const int col = chan_of_pos(16 * w + lr);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[tm][i] = stg[chan_of_pos(16 * tm + 4 * hi + i) * kSP + col];
+    __syncthreads();  // the buffer is free again
+}
+
+// The [d_k][d_v] fp32 state at dst <- acc (the layout of load_state). The caller has passed a
+// barrier after the last read of LDS operands.
+__device__ __forceinline__ void store_state(float *dst, const f32x4 (&acc)[8], float *stg, int tid, int w, int lr,
+                                            int hi) {
+    const int col = chan_of_pos(16 * w + lr);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stg[chan_of_pos(16 * tm + 4 * hi + i) * kSP + col] = acc[tm][i];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kDK * kDV / 4 / kNT; ++k) {
+        const int piece = tid + kNT * k, row = piece / (kDV / 4), c4 = piece % (kDV / 4);
+        *reinterpret_cast<f32x4 *>(dst + (size_t)row * kDV + 4 * c4) =
+            *reinterpret_cast<const f32x4 *>(stg + row * kSP + 4 * c4);
+    }
+}
+
 // Declares this lane's index l, its row lr and lane group hi, and its chunk row r
 // (within the wave's row block rb), for the enclosing phase.
 #define KDA_PHASE_LANE                                                         \
@@ -276,11 +320,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
     //      positions) 16 tm + 4 hi + i of column 16 w + lr
     f32x4 accS[8];
     if (h0src) {
-        const float *h0 = h0src + chan_of_pos(16 * w + lr);
-#pragma unroll
-        for (int tm = 0; tm < 8; ++tm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) accS[tm][i] = h0[chan_of_pos(16 * tm + 4 * hi + i) * kDV];
+        load_state(h0src, accS, reinterpret_cast<float *>(smem), tid, w, lr, hi);
     } else {
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) accS[tm] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -528,7 +568,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
         if constexpr (!kStrong) {
             // a chunk of strong decay: the pair is left to the strong instance
             if (__builtin_amdgcn_readfirstlane(flg[2] | flg[3]) != 0) {
-                if (tid == 0) *u.redo = 1;
+                if (tid == 0 && u.redo) *u.redo = 1;
                 return;
             }
         }
@@ -1208,52 +1248,64 @@ __device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
         // reads (from the per-channel factors on), every wave passes its first barrier.
     }
 
-    if constexpr (kMapMode) {
-        // M = E_last Q_M and N = E_last Q_N: the factor exp(gamma / 2) of the last chunk,
-        // once every wave has read that chunk's factors
-        __syncthreads();
-        if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
-        __syncthreads();
-        float *mp = u.map_out;
-        const int cc = chan_of_pos(16 * w + lr);
-#pragma unroll
-        for (int tm = 0; tm < 8; ++tm) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = 16 * tm + 4 * hi + i;
-                const float e = ehalf[e_slot(p)];
-                mp[seg_m_index(chan_of_pos(p), cc)] = e * accM[tm][i];
-                mp[kDK * kDK + seg_n_index(chan_of_pos(p), cc)] = e * accS[tm][i];
-            }
-        }
-        if (tid == 0) *u.redo = 0;  // no chunk of strong decay in this segment
-        return;
-    } else if constexpr (!kStrong) {
-        if (tid == 0) *u.redo = 0;  // no chunk of strong decay in this run
-    } else {
-        if (u.out_state) {
-            float *hT = u.out_state + chan_of_pos(16 * w + lr);
-#pragma unroll
-            for (int tm = 0; tm < 8; ++tm)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hT[chan_of_pos(16 * tm + 4 * hi + i) * kDV] = accS[tm][i];
-        }
-        return;
-    }
-    if (u.out_state) {
-        // S = E_last Q: the factor exp(gamma / 2) of the last chunk, once every wave has
-        // read that chunk's factors
-        __syncthreads();
-        if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
-        __syncthreads();
-        float *hT = u.out_state + chan_of_pos(16 * w + lr);
+    // The last chunk's factor exp(gamma / 2) on the rows of what leaves (S = E_last Q), once
+    // every wave has read that chunk's factors; then the buffer that held them may be reused.
+    auto last_factor = [&](f32x4 (&acc)[8]) {
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) {
             const f32x4 e4 = {ehalf[e_slot(16 * tm + 4 * hi)], ehalf[e_slot(16 * tm + 4 * hi + 1)],
                               ehalf[e_slot(16 * tm + 4 * hi + 2)], ehalf[e_slot(16 * tm + 4 * hi + 3)]};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hT[chan_of_pos(16 * tm + 4 * hi + i) * kDV] = e4[i] * accS[tm][i];
+            acc[tm] = acc[tm] * e4;
         }
+    };
+    float *stg = reinterpret_cast<float *>(smem);
+    if constexpr (kMapMode) {
+        // M = E_last Q_M and N = E_last Q_N, each staged in LDS in the order the composition
+        // reads it (seg_m_index, seg_n_index), then copied out in whole 16-byte pieces
+        __syncthreads();
+        if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
+        __syncthreads();
+        last_factor(accM);
+        last_factor(accS);
+        __syncthreads();
+        const int cc = chan_of_pos(16 * w + lr);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int tm = 0; tm < 8; ++tm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = chan_of_pos(16 * tm + 4 * hi + i);
+                    if (half == 0) stg[seg_m_index(r, cc)] = accM[tm][i];
+                    else stg[seg_n_index(r, cc)] = accS[tm][i];
+                }
+            __syncthreads();
+            float *dst = u.map_out + half * kDK * kDK;
+#pragma unroll
+            for (int k = 0; k < kDK * kDK / 4 / kNT; ++k) {
+                const int piece = tid + kNT * k;
+                *reinterpret_cast<f32x4 *>(dst + 4 * piece) = *reinterpret_cast<const f32x4 *>(stg + 4 * piece);
+            }
+            if (half == 0) __syncthreads();
+        }
+        if (tid == 0) *u.redo = 0;  // no chunk of strong decay in this segment
+        return;
+    } else if constexpr (!kStrong) {
+        if (tid == 0 && u.redo) *u.redo = 0;  // no chunk of strong decay in this run
+    } else {
+        if (u.out_state) {
+            __syncthreads();  // every wave is done with the last chunk's operands
+            store_state(u.out_state, accS, stg, tid, w, lr, hi);
+        }
+        return;
+    }
+    if (u.out_state) {
+        __syncthreads();
+        if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
+        __syncthreads();
+        last_factor(accS);
+        __syncthreads();
+        store_state(u.out_state, accS, stg, tid, w, lr, hi);
     }
 }
 

@@ -85,8 +85,21 @@ def prefill_path(B, T, H, dk, dv, chunk, varlen, bf16, n_seqs=0):
     if varlen:
         return "segmented"
     units_a = lambda t: max(-(-c // t) - 1, 1) if c > t else 1  # noqa: E731
-    t = next(t for t in range(1, c + 1) if B * units_a(t) <= u)
+    t = plan_budget(c, next(t for t in range(1, c + 1) if B * units_a(t) <= u))
     return "segmented" if c > t else "fused"
+
+
+def plan_budget(c_max, t_min):
+    """The library's budget choice: from the smallest budget that fits the compute units, the
+    one minimising 8 T + max(ceil(c_max / T) - 2, 0) (two launches of about T chunk-steps and the
+    composition's dependent steps)."""
+    cost = lambda t: 8 * t + max(-(-c_max // t) - 2, 0)  # noqa: E731
+    best, best_cost, t = t_min, cost(t_min), t_min + 1
+    while t <= c_max and 8 * t <= best_cost:
+        if cost(t) < best_cost:
+            best, best_cost = t, cost(t)
+        t += 1
+    return best
 
 
 def sources_digest(names):

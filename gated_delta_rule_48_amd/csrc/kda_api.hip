@@ -64,14 +64,15 @@ struct FusedPlan {
 
 // Below 256 (sequence, head) pairs the pass runs on the plan (kda_internal.hpp): per head u =
 // 256 / H units in each of two launches. For packed sequences the device works out the plan
-// from the offsets (kda_seg_plan_kernel); for B equal sequences of c chunks the host does:
-// the smallest budget T for which B plan_units_a(c, T) <= u. Both launches then take about T
-// chunk-steps (the 4 packed sequences of 32,768 + 16,384 + 12,288 + 4,096 tokens x 32 heads:
-// T = 103 of their 1,024 chunks per head, 8 units in launch A and 7 in launch C; 1 x 4,096
-// tokens x 16 heads: T = 4, 15 units each). Sequences of fewer than kMinSegChunks chunks are
-// not cut (T = the longest: one unit per sequence): below that the composition and the
-// second launch cost about what the segments save. Either way the usual body runs in the
-// same kernel, so equal-length and packed layouts of the same sequences agree bit for bit.
+// from the offsets (kda_seg_plan_kernel); for B equal sequences of c chunks the host does: from
+// the smallest budget T for which B plan_units_a(c, T) <= u, the budget of plan_budget. Both
+// launches then take about T chunk-steps (the 4 packed sequences of 32,768 + 16,384 + 12,288 +
+// 4,096 tokens x 32 heads: T = 103 of their 1,024 chunks per head, 8 units in launch A and 7 in
+// launch C; 1 x 4,096 tokens x 16 heads: T = 4, 15 units each). Sequences of fewer than
+// kMinSegChunks chunks are not cut (T = the longest: one unit per sequence): below that the
+// composition and the second launch cost about what the segments save. Either way the usual
+// body runs in the same kernel, so equal-length and packed layouts of the same sequences agree
+// bit for bit.
 FusedPlan fused_plan(int B, int T, int H, bool varlen, int n_seqs) {
     const int64_t pairs = (int64_t)(varlen ? n_seqs : B) * H;
     if (pairs >= kFusedMinPairs || T <= 0) return FusedPlan{0, 0, 0, 0};
@@ -85,8 +86,9 @@ FusedPlan fused_plan(int B, int T, int H, bool varlen, int n_seqs) {
         const int mid = (lo + hi) / 2;
         if ((int64_t)B * kda::plan_units_a((int)c, mid) <= u) hi = mid; else lo = mid + 1;
     }
-    const int P = kda::plan_segments((int)c, lo);
-    return FusedPlan{u, lo, P, B * (P - 1)};
+    const int T_b = kda::plan_budget((int)c, lo);
+    const int P = kda::plan_segments((int)c, T_b);
+    return FusedPlan{u, T_b, P, B * (P - 1)};
 }
 
 struct WsLayout {

@@ -150,6 +150,28 @@ __host__ __device__ inline int plan_units_a(int c, int T) {
     return P > 1 ? P - 1 : 1;
 }
 
+// The budget from the smallest that fits the compute units (t_min) and the longest sequence
+// (c_max chunks): both launches take about T chunk-steps (about 5.5 us each) and the composition
+// max(P - 2, 0) dependent steps (about 1.4 us each), so the budget minimises 8 T + max(P - 2, 0).
+// With many units per head (few heads) that is longer than t_min: one sequence of 64 chunks and
+// 64 units per head takes T = 3 (44 against 70 for T = 1, whose composition has 62 steps). The
+// cost only grows with T once 8 T passes the best cost found.
+__host__ __device__ inline int plan_budget(int c_max, int t_min) {
+    auto cost = [&](int T) {
+        const int P = plan_segments(c_max, T);
+        return 8 * T + (P > 2 ? P - 2 : 0);
+    };
+    int best = t_min, best_cost = cost(t_min);
+    for (int T = t_min + 1; T <= c_max && 8 * T <= best_cost; ++T) {
+        const int c = cost(T);
+        if (c < best_cost) {
+            best = T;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
 // Chunk range [*sc, *sc + *lc) of segment p of a sequence of c chunks under budget T.
 __host__ __device__ inline void plan_segment_chunks(int c, int T, int p, int *sc, int *lc) {
     const int f = c < T ? c : T;

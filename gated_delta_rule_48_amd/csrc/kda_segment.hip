@@ -14,9 +14,10 @@
 // lengths): for a budget of T chunks, a sequence of c chunks has P = ceil(c / T) segments, the
 // first of min(c, T) chunks and the others near-equal (at most T each). Per head, launch A
 // holds one unit per sequence with P = 1 and P - 1 units per sequence with P > 1, launch C
-// P - 1 per sequence. T is the smallest budget for which launch A's units fit the compute
-// units (u_max per head); both launches then take about T chunk-steps. If the longest
-// sequence has fewer than kMinSegChunks chunks, T is its length: no sequence is cut.
+// P - 1 per sequence. T starts from the smallest budget for which launch A's units fit the
+// compute units (u_max per head) and grows while that shortens the composition by more than
+// it lengthens the two launches (plan_budget). If the longest sequence has fewer than
+// kMinSegChunks chunks, T is its length: no sequence is cut.
 //
 // Composition: one workgroup of 8 waves per (sequence, head, 16 value columns): the columns of
 // the state evolve independently. Each step is a 128 x 128 by 128 x 16 product on the matrix
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_seg_plan_kernel(const int32_
         const int units = block_sum(t < n ? plan_units_a(c, mid) : 0, red);
         if (units <= u_max) hi = mid; else lo = mid + 1;
     }
-    const int T = lo;
+    const int T = plan_budget(cmax, lo);  // (uniform: every thread works it out)
     // exclusive prefix sums of the units of launches A and C
     const int ua = t < n ? plan_units_a(c, T) : 0, uc = t < n ? plan_segments(c, T) - 1 : 0;
     __syncthreads();
@@ -238,9 +239,7 @@ __global__ __launch_bounds__(kPlanThreads) void kda_seg_plan_kernel(const int32_
         pm[1][t] += yc;
     }
     __syncthreads();
-    const PlanTab pt{tab, n};
-    int32_t *a_off = tab + 1, *c_off = tab + n + 2, *tbo = tab + 2 * n + 3, *teo = tab + 3 * n + 3;
-    (void)pt;
+    int32_t *a_off = tab + 1, *c_off = tab + n + 2, *tbo = tab + 2 * n + 3, *teo = tab + 3 * n + 3;  // (PlanTab)
     if (t == 0) {
         tab[0] = T;
         a_off[0] = 0;

@@ -59,9 +59,9 @@ def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
         # on, one unit per pair. Below, the plan: two launches of at most u = 256 // H units per
         # head (2 u flag bytes per head), the plan table of packed sequences, and per segment
         # slot an entering state and a map. Slots per head: packed, min(u, c + n_seqs) (launch
-        # C's units hold a chunk each at least); equal lengths, B (P - 1) for the smallest
-        # budget t with B (ceil(c / t) - 1, at least 1) <= u and P = ceil(c / t) segments (no
-        # cut, P = 1, below 8 chunks).
+        # C's units hold a chunk each at least); equal lengths, B (P - 1) with P = ceil(c / T)
+        # segments for the budget T: from the smallest t with B max(ceil(c / t) - 1, 1) <= u,
+        # the lowest 8 T + max(P - 2, 0) (no cut, P = 1, below 8 chunks).
         if pairs >= 256:
             return 256 + r(n_seq * H)
         u, c = 256 // H, (T + 63) // 64
@@ -72,7 +72,12 @@ def _ws_expect(B, T, H, dk, dv, C, n_seqs, esz):
         else:
             ua = lambda t: max(-(-c // t) - 1, 1) if c > t else 1  # noqa: E731
             t = c if c < 8 else next(t for t in range(1, c + 1) if B * ua(t) <= u)
-            slots = B * (-(-c // t) - 1)
+            cost = lambda t: 8 * t + max(-(-c // t) - 2, 0)  # noqa: E731
+            tb, t2 = t, t + 1  # the budget: the lowest cost from t on (8 T + composition steps)
+            while t2 <= c and 8 * t2 <= cost(tb):
+                tb = t2 if cost(t2) < cost(tb) else tb
+                t2 += 1
+            slots = B * (-(-c // tb) - 1)
         total += r(slots * H * dk * dv * 4) + r(slots * H * 2 * dk * dv * 4)
         return total
     per = (T + C - 1) // C

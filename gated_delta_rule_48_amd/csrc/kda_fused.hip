@@ -267,7 +267,7 @@ struct Unit {
     int T_len;            // its tokens
     const float *h0src;   // the state it starts from ([d_k][d_v] fp32), or null (zero)
     float *out_state;     // where the state at its end goes ([d_k][d_v] fp32), or null
-    float *map_out;       // kMap: M and N (seg_m_index, seg_n_index)
+    float *map_out;       // kMap: M (bf16 parts) and N (seg_mh_index, seg_n_index)
     uint8_t *redo;        // its flag: 1 if it left its pair to the strong instance, else 0
 };
 
@@ -1261,7 +1261,8 @@ __device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
     float *stg = reinterpret_cast<float *>(smem);
     if constexpr (kMapMode) {
         // M = E_last Q_M and N = E_last Q_N, each staged in LDS in the order the composition
-        // reads it (seg_m_index, seg_n_index), then copied out in whole 16-byte pieces
+        // reads it, then copied out in whole 16-byte pieces: first M as its two bf16 parts
+        // (hi = M rounded, lo = the rest rounded, seg_mh_index), then N in fp32 (seg_n_index)
         __syncthreads();
         if (tid < kDK) ehalf[e_slot(tid)] = exp2_fast(m_prev * kL2E);
         __syncthreads();
@@ -1269,6 +1270,7 @@ __device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
         last_factor(accS);
         __syncthreads();
         const int cc = chan_of_pos(16 * w + lr);
+        bf16 *stg_h = reinterpret_cast<bf16 *>(smem);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -1276,8 +1278,13 @@ __device__ __forceinline__ void fused_body(const FusedArgs &a, const Unit &u) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = chan_of_pos(16 * tm + 4 * hi + i);
-                    if (half == 0) stg[seg_m_index(r, cc)] = accM[tm][i];
-                    else stg[seg_n_index(r, cc)] = accS[tm][i];
+                    if (half == 0) {
+                        const bf16 mh = static_cast<bf16>(accM[tm][i]);
+                        stg_h[seg_mh_index(r, cc)] = mh;
+                        stg_h[kDK * kDK + seg_mh_index(r, cc)] = static_cast<bf16>(accM[tm][i] - static_cast<float>(mh));
+                    } else {
+                        stg[seg_n_index(r, cc)] = accS[tm][i];
+                    }
                 }
             __syncthreads();
             float *dst = u.map_out + half * kDK * kDK;

@@ -107,19 +107,21 @@ struct FusedArgs {
     const int32_t *plan_tab;  // packed sequences: the plan (PlanTab layout), written by kda_seg_plan_kernel
     int n_seqs;
     float *seg_state;  // [slots, H, d_k, d_v] fp32: the state entering segment p >= 1 (slot of the segment)
-    float *seg_map;    // [slots, H, 2, d_k * d_k] fp32: M and N of segment p = 1 .. P - 2 (its slot),
-                       // in the order the composition reads them (seg_m_index, seg_n_index)
+    float *seg_map;    // [slots, H, 128 KB]: M (split into two bf16 parts) and N of segment p = 1 .. P - 2
+                       // (its slot), in the order the composition reads them (seg_mh_index, seg_n_index)
     // With segments, redo holds [2 plan_u, H]: launch A's unit u at u H + h, launch C's at
     // (plan_u + u) H + h. The slot of segment p >= 1 of sequence s is the index of its unit in
     // launch C: c_off(s) + p - 1.
 };
 
-// Positions of M[r][c] and N[r][c] (d_k = d_v = 128, channel order) within a segment's map.
-// The composition's wave w, lane n + 16 g reads M[16 w + n][32 kb + 8 g + 4 j .. + 3] with one
-// 16-byte load per (kb, j), and N[16 w + 4 g + i][16 cb + n] with one 4-byte load per i: in
-// these orders every such load instruction reads one contiguous run of 1 KB (M) or 256 B (N).
-__host__ __device__ constexpr int seg_m_index(int r, int c) {
-    return ((((r >> 4) * 4 + (c >> 5)) * 2 + ((c >> 2) & 1)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 4 + (c & 3);
+// A segment's map (d_k = d_v = 128, channel order), 128 KB: M split as M = Mh + Ml (Mh = M
+// rounded to bf16, Ml = the rest rounded to bf16), Mh then Ml as bf16 [16384] each at
+// seg_mh_index, then N as fp32 [16384] at seg_n_index. The composition's wave w, lane n + 16 g
+// reads Mh and Ml [16 w + n][32 kb + 8 g .. + 7] with one 16-byte load each per kb, and
+// N[16 w + 4 g + i][16 cb + n] with one 4-byte load per i: in these orders every such load
+// instruction reads one contiguous run of 1 KB (Mh, Ml) or 256 B (N).
+__host__ __device__ constexpr int seg_mh_index(int r, int c) {
+    return ((((r >> 4) * 4 + (c >> 5)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 8 + (c & 7));
 }
 __host__ __device__ constexpr int seg_n_index(int r, int c) {
     return (((c >> 4) * 8 + (r >> 4)) * 4 + (r & 3)) * 64 + (c & 15) + 16 * ((r >> 2) & 3);

@@ -26,15 +26,16 @@
 // product taken as hi hi' + hi lo' + lo hi' with v_mfma_f32_16x16x32_bf16 (lane l supplies
 // A[l%16][8 (l/16) .. + 7] and B[8 (l/16) .. + 7][l%16]), fp32 accumulation: about 16
 // significant bits per product, at a fifth of the matrix-core time of fp32 instructions.
-// Each lane reads its share of M(p) and N(p) straight from memory, those of steps p + 1
-// and p + 2 in flight while step p computes. The 16 columns of S_in stay in LDS, split into
-// hi and lo once, by the lanes that form them (transposed; two sets of buffers used in turn,
-// so one barrier per step). The 8 workgroups of one (sequence, head) run on one
-// XCD (block ids 8 apart), so M(p) is fetched into one L2 and read there 8 times. The maps
-// are stored in the order of these reads (seg_m_index, seg_n_index: one contiguous 1 KB run
-// per load instruction of M, where row-major order would touch 16 cache lines per
-// instruction, half of each); the entering states are row-major (row = key channel), like h0
-// and hT.
+// M(p) arrives split: the map instance stores its two bf16 parts (split there once, not in
+// every step of the eight workgroups that read it). Each lane reads its share of M(p) and N(p)
+// straight from memory, those of steps p + 1 and p + 2 in flight while step p computes. The
+// 16 columns of S_in stay in LDS, split into hi and lo once, by the lanes that form them
+// (transposed; two sets of buffers used in turn, so one barrier per step). The 8 workgroups of
+// one (sequence, head) run on one XCD (block ids 8 apart), so M(p) is fetched into one L2 and
+// read there 8 times. The maps are stored in the order of these reads (seg_mh_index,
+// seg_n_index: one contiguous 1 KB run per load instruction of M's parts, where row-major
+// order would touch 16 cache lines per instruction, half of each); the entering states are
+// row-major (row = key channel), like h0 and hT.
 
 #include "kda_internal.hpp"
 
@@ -45,17 +46,6 @@ constexpr int kD = 128;
 constexpr int kChainThreads = 512;
 constexpr int kStPitch = kD + 8;  // bf16 per row of the transposed S_in buffers
 constexpr int kBlockSteps = 15;   // steps per straight-line block (a multiple of the three operand sets)
-
-// hi = bf16(x), lo = bf16(x - hi) for 8 values
-__device__ __forceinline__ void split_hi_lo(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        hi[e] = static_cast<bf16>(x0[e]);
-        lo[e] = static_cast<bf16>(x0[e] - static_cast<float>(hi[e]));
-        hi[e + 4] = static_cast<bf16>(x1[e]);
-        lo[e + 4] = static_cast<bf16>(x1[e] - static_cast<float>(hi[e + 4]));
-    }
-}
 
 __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedArgs a) {
     // S_in's 16 columns as the B operand, already split: Sh[b][n * kStPitch + k] = hi of S_in[k][n],
@@ -96,23 +86,24 @@ __global__ __launch_bounds__(kChainThreads) void kda_segment_chain_kernel(FusedA
     // the four entries of N(p) its outputs add, in three sets used in turn: step p computes
     // from one while the maps of steps p + 1 and p + 2 are in flight (a step is much shorter
     // than a load of M from memory)
-    f32x4 amA[4][2], amB[4][2], amC[4][2];
+    // (M arrives split: the map instance stores its two bf16 parts)
+    bf16x8 amA[2][4], amB[2][4], amC[2][4];
     float nA[4], nB[4], nC[4];
-    auto fetch = [&](int p, f32x4 (&a4)[4][2], float (&n4)[4]) {
+    auto fetch = [&](int p, bf16x8 (&a8)[2][4], float (&n4)[4]) {
         const float *M = map_of(p);
+        const bf16 *Mh = reinterpret_cast<const bf16 *>(M);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int part = 0; part < 2; ++part)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                a4[kb][j] = *reinterpret_cast<const f32x4 *>(M + seg_m_index(16 * w + n, 32 * kb + 8 * g + 4 * j));
+            for (int kb = 0; kb < 4; ++kb)
+                a8[part][kb] = *reinterpret_cast<const bf16x8 *>(Mh + part * kD * kD + seg_mh_index(16 * w + n, 32 * kb + 8 * g));
 #pragma unroll
         for (int i = 0; i < 4; ++i) n4[i] = M[DD + seg_n_index(16 * w + 4 * g + i, 16 * cb + n)];
     };
     // S_in(p + 1) = M(p) S_in(p) + N(p); S_in(p) is in buffer p & 1
-    auto step = [&](int p, const f32x4 (&a4)[4][2], const float (&nv)[4]) {
-        bf16x8 ah[4], al[4];  // M's split does not wait for S_in
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) split_hi_lo(a4[kb][0], a4[kb][1], ah[kb], al[kb]);
+    auto step = [&](int p, const bf16x8 (&a8)[2][4], const float (&nv)[4]) {
+        const bf16x8(&ah)[4] = a8[0];
+        const bf16x8(&al)[4] = a8[1];
         __syncthreads();  // S_in(p) complete; every wave is done with the other buffer
         const bf16 *sh = Sh[p & 1], *sl = Sl[p & 1];
         f32x4 hh = {0.f, 0.f, 0.f, 0.f}, hl = hh, lh = hh;

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_state.hip", "kda_fused.hip", "kda_segment.hip", "kda_decode.hip",
-           "kda_attn.hip", "kda_bwd.hip", "kda_bwd_bf16.hip"]
+           "kda_attn.hip", "kda_bwd.hip", "kda_bwd_bf16.hip", "kda_bwd_tok.hip"]
 HEADERS = ["kda_device.hpp", "kda_internal.hpp", "kda_solve.hpp"]
 
 HIPCC_FLAGS = [

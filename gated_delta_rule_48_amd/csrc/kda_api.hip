@@ -537,11 +537,29 @@ struct BwdPlan {
     bool fast;
     size_t W, U, QO, KtT, Aqk, eg, strong, st, ut, ds, du, discard, choff;
     int64_t fast_chunks;  // chunks over all sequences (an upper bound with cu_seqlens)
+    // the token pass (kda_bwd_tok.hip): its chunk flags (direct pass; the matrix-core pass
+    // reads the chunk preparation's), its workgroups' checkpoints
+    size_t tok_flags, tok_scratch, tok_slot_floats;
+    int tok_slots, tok_nblk;
 };
+
+// The token pass's checkpoints from offset off (one slot per workgroup, as many as the
+// budget holds, at most one per pair); the end of them.
+size_t tok_layout(size_t off, int64_t n_pairs, int64_t n_blk_max, int d_k, int d_v, BwdPlan *p) {
+    p->tok_nblk = (int)n_blk_max;
+    p->tok_slot_floats = (size_t)(n_blk_max + 8) * d_k * d_v;
+    const size_t slot_bytes = p->tok_slot_floats * sizeof(float);
+    int64_t slots = (int64_t)(kda::kTokScratchBudget / slot_bytes);
+    slots = std::max<int64_t>(1, std::min<int64_t>(slots, std::min<int64_t>(n_pairs, 1024)));
+    p->tok_slots = n_pairs > 0 && n_blk_max > 0 ? (int)slots : 0;
+    p->tok_scratch = off;
+    return round_up(off + (size_t)p->tok_slots * slot_bytes, 256);
+}
 
 // The matrix-core pass's workspace: per (chunk, head) the forward's chunk quantities, then
 // S^T, U^T, dS'^T and dU^T (bf16); with packed sequences, the chunk-offset table.
-void bwd_fast_layout(int64_t chunks, int H, int d_k, int d_v, int C, int n_seqs_varlen, BwdPlan *p) {
+void bwd_fast_layout(int64_t chunks, int H, int d_k, int d_v, int C, int n_seqs_varlen, int64_t n_pairs,
+                     int64_t n_blk_max, BwdPlan *p) {
     const size_t u = (size_t)chunks * H, e = 2;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -563,6 +581,7 @@ void bwd_fast_layout(int64_t chunks, int H, int d_k, int d_v, int C, int n_seqs_
     p->discard = take(256);
     p->choff = n_seqs_varlen > 0 ? take(((size_t)3 * n_seqs_varlen + 1) * sizeof(int32_t)) : 0;
     p->fast_chunks = chunks;
+    off = tok_layout(off, n_pairs, n_blk_max, d_k, d_v, p);
     p->total = u > 0 || n_seqs_varlen > 0 ? off : 0;
 }
 
@@ -580,15 +599,36 @@ int check_bwd(int B, int T, int H, int d_k, int d_v, int chunk, int io, BwdPlan 
     const int64_t units = (int64_t)B * p->n_chunks * H;
     p->fast = bwd_fast(d_k, d_v, io);
     if (p->fast) {
-        bwd_fast_layout((int64_t)B * p->n_chunks, H, d_k, d_v, chunk, 0, p);
+        bwd_fast_layout((int64_t)B * p->n_chunks, H, d_k, d_v, chunk, 0, (int64_t)B * H, p->n_chunks, p);
         return KDA_OK;
     }
     const kda::BwdLayout L{d_k, d_v};
     p->n_groups = (int)std::min<int64_t>(units, kda::kBwdMaxGroups);
     p->per_bytes = (size_t)L.per_chunk() * sizeof(float);
     p->scratch_off = round_up((size_t)units * p->per_bytes, 256);
-    p->total = units > 0 ? p->scratch_off + round_up((size_t)p->n_groups * L.scratch() * sizeof(float), 256) : 0;
+    p->tok_flags = p->scratch_off + round_up((size_t)p->n_groups * L.scratch() * sizeof(float), 256);
+    const size_t end = tok_layout(round_up(p->tok_flags + (size_t)units, 256), (int64_t)B * H, p->n_chunks, d_k, d_v, p);
+    p->total = units > 0 ? end : 0;
     return KDA_OK;
+}
+
+// After either backward pass: the token pass over the pairs whose chunks `flags` marks.
+int launch_tok_after(const BwdPlan &p, unsigned char *w8, const uint8_t *flags, const kda::SeqMap &map, int H,
+                     int d_k, int d_v, int io, const void *q, const void *k, const void *v, const float *log_alpha,
+                     const float *beta, float scale, const float *h0, const void *dout, const float *dhT, void *dq,
+                     void *dk, void *dv, float *dlog_alpha, float *dbeta, float *dh0, size_t ntok, hipStream_t hs) {
+    if (p.total == 0 || ntok == 0 || p.tok_slots == 0) return KDA_OK;
+    kda::TokArgs t{};
+    t.q = q, t.k = k, t.v = v, t.dout = dout, t.log_alpha = log_alpha, t.beta = beta, t.h0 = h0, t.dhT = dhT;
+    t.scale = scale;
+    t.dq = dq, t.dk = dk, t.dv = dv, t.dlog_alpha = dlog_alpha, t.dbeta = dbeta, t.dh0 = dh0;
+    t.map = map;
+    t.H = H;
+    t.flags = flags;
+    t.scratch = reinterpret_cast<float *>(w8 + p.tok_scratch);
+    t.slot_floats = p.tok_slot_floats;
+    t.n_blk_max = p.tok_nblk;
+    return kda::launch_bwd_tok(t, d_k, d_v, io == KDA_BF16, p.tok_slots, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -649,9 +689,10 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
                                       reinterpret_cast<float *>(w8 + p.eg), w8 + p.strong};
             a.st = w8 + p.st, a.ut = w8 + p.ut, a.ds = w8 + p.ds, a.du = w8 + p.du, a.discard = w8 + p.discard;
         }
-        return kda::launch_chunk_bwd_bf16(a, B, B * p.n_chunks, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
-                   ? KDA_OK
-                   : KDA_ERR_HIP;
+        const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        if (kda::launch_chunk_bwd_bf16(a, B, B * p.n_chunks, hs) != hipSuccess) return KDA_ERR_HIP;
+        return launch_tok_after(p, w8, w8 + p.strong, a.map, H, d_k, d_v, io, q, k, v, log_alpha, beta, scale, h0,
+                                dout, dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, ntok, hs);
     }
     float *ws = static_cast<float *>(workspace);
     const kda::BwdArgs a{q,  k,  v,  log_alpha, beta,       h0,    dout, dhT, scale,
@@ -659,9 +700,15 @@ KDA_EXPORT int kda_chunk_bwd(int B, int T, int H, int d_k, int d_v, int chunk, i
                          p.total > 0 ? reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + p.scratch_off)
                                      : nullptr,
                          B, T, H, p.n_chunks, p.n_groups};
-    if (kda::launch_chunk_bwd(a, d_k, d_v, io == KDA_BF16, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (kda::launch_chunk_bwd(a, d_k, d_v, io == KDA_BF16, hs) != hipSuccess) return KDA_ERR_HIP;
+    if (p.total == 0 || ntok == 0) return KDA_OK;
+    unsigned char *w8 = static_cast<unsigned char *>(workspace);
+    const kda::SeqMap map{nullptr, nullptr, nullptr, 0, B, T, kda::kBwdChunk};
+    if (kda::launch_bwd_tok_detect(log_alpha, map, H, d_k, B * p.n_chunks, w8 + p.tok_flags, hs) != hipSuccess)
         return KDA_ERR_HIP;
-    return KDA_OK;
+    return launch_tok_after(p, w8, w8 + p.tok_flags, map, H, d_k, d_v, io, q, k, v, log_alpha, beta, scale, h0, dout,
+                            dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, ntok, hs);
 }
 
 namespace {
@@ -673,7 +720,8 @@ int check_bwd_varlen(int T, int H, int d_k, int d_v, int chunk, int n_seqs, int 
     if (H > 65535 || n_seqs > 65535 || (int64_t)T * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     *p = BwdPlan{};
     p->fast = true;
-    bwd_fast_layout(((int64_t)T + chunk - 1) / chunk + n_seqs, H, d_k, d_v, chunk, n_seqs, p);
+    bwd_fast_layout(((int64_t)T + chunk - 1) / chunk + n_seqs, H, d_k, d_v, chunk, n_seqs, (int64_t)n_seqs * H,
+                    ((int64_t)T + chunk - 1) / chunk, p);
     return KDA_OK;
 }
 
@@ -736,5 +784,7 @@ KDA_EXPORT int kda_chunk_bwd_varlen(int T, int H, int d_k, int d_v, int chunk, i
     a.buf = kda::ChunkBuffers{w8 + p.W, w8 + p.U, w8 + p.QO, w8 + p.KtT, w8 + p.Aqk,
                               reinterpret_cast<float *>(w8 + p.eg), w8 + p.strong};
     a.st = w8 + p.st, a.ut = w8 + p.ut, a.ds = w8 + p.ds, a.du = w8 + p.du, a.discard = w8 + p.discard;
-    return kda::launch_chunk_bwd_bf16(a, n_seqs, (int)p.fast_chunks, hs) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (kda::launch_chunk_bwd_bf16(a, n_seqs, (int)p.fast_chunks, hs) != hipSuccess) return KDA_ERR_HIP;
+    return launch_tok_after(p, w8, w8 + p.strong, a.map, H, d_k, d_v, io, q, k, v, log_alpha, beta, scale, h0, dout,
+                            dhT, dq, dk, dv, dlog_alpha, dbeta, dh0, ntok, hs);
 }

@@ -73,4 +73,29 @@ struct BwdFastArgs {
 
 hipError_t launch_chunk_bwd_bf16(const BwdFastArgs &a, int n_seqs, int total_chunks, hipStream_t stream);
 
+// The backward token by token (kda_bwd_tok.hip), run after either pass for the (sequence,
+// head) pairs holding a chunk whose summed log_alpha falls below -kStrongDecay on some key
+// channel (flags, one byte per (chunk, head) in the chunk order of map: such chunks leave
+// the range of the chunked passes' midpoint factors). It overwrites every gradient of those
+// pairs. Each of its workgroups keeps the checkpoints of one pair at a time in scratch.
+constexpr size_t kTokScratchBudget = size_t(512) << 20;  // bytes of checkpoints, at most
+struct TokArgs {
+    const void *q, *k, *v, *dout;  // io dtype
+    const float *log_alpha, *beta, *h0, *dhT;
+    float scale;
+    void *dq, *dk, *dv;  // io dtype
+    float *dlog_alpha, *dbeta, *dh0;
+    SeqMap map;          // chunks of 64 rows from each sequence's start
+    int H;
+    const uint8_t *flags;   // [chunk][head]
+    float *scratch;         // n_slots x slot_floats
+    size_t slot_floats;     // (n_blk_max + 8) d_k d_v: a state per 64-token block, then per 8-token group
+    int n_blk_max;          // 64-token blocks of the longest sequence, at most
+};
+
+// flags[j][h] for every chunk j of map (n_chunks_grid: an upper bound of map's chunk count).
+hipError_t launch_bwd_tok_detect(const float *log_alpha, const SeqMap &map, int H, int dk, int n_chunks_grid,
+                                 uint8_t *flags, hipStream_t stream);
+hipError_t launch_bwd_tok(const TokArgs &a, int dk, int dv, bool io_bf16, int n_slots, hipStream_t stream);
+
 }  // namespace kda

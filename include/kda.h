@@ -44,7 +44,8 @@
  *    near -500 and -2000 for every gate kind. On the fused pass (bf16,
  *    d_k = d_v = 128) such a chunk sends its whole (sequence, head) pair to the
  *    second instance, which runs it again from the start, one workgroup per
- *    pair. kda_chunk_bwd keeps the -170 limit of its midpoint factors.
+ *    pair. kda_chunk_bwd has no limit either: the (sequence, head) pairs holding
+ *    such a chunk are recomputed token by token after its chunked pass.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -291,6 +292,16 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  * the forward's bf16 passes do; every other case runs the direct pass, all arithmetic
  * fp32. Both add every sum in a fixed order: repeated calls give the same bits.
  *
+ * Both factor the decay inside a chunk around the chunk's midpoint, which holds while a
+ * chunk's summed log_alpha is >= -160 on every key channel. After either pass, the
+ * (sequence, head) pairs holding a chunk below that are recomputed token by token (fp32
+ * arithmetic, every decay applied as alpha = exp(log_alpha) <= 1): the exact reverse mode
+ * of the recurrence, with the states recomputed from checkpoints (one per 64 tokens, then
+ * one per 8 tokens of the block being reversed). This pass is sequential over the tokens of
+ * a pair and runs on as many pairs at once as its share of the workspace holds checkpoints
+ * for (at most 512 MiB, at least one pair at a time); calls without such chunks spend only
+ * the check on it.
+ *
  * Arguments
  *   B, T, H, d_k, d_v   equal-length sequences [B, T, H, d] (packed sequences:
  *               kda_chunk_bwd_varlen); d_k, d_v in {64, 128}; B, H <= 65535.
@@ -306,8 +317,11 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  *   workspace   kda_chunk_bwd_workspace_bytes(...) bytes, 256-byte aligned: on the
  *               matrix-core pass about 170 KB per (chunk, head) (the forward's chunk
  *               quantities and four bf16 matrices); on the direct pass about 300 KB per
- *               (chunk, head) at d = 128 plus a fixed scratch of at most 1024 x 770 KB.
- * Gate values as for kda_chunk_fwd. Errors as for the other entry points.
+ *               (chunk, head) at d = 128 plus a fixed scratch of at most 1024 x 770 KB;
+ *               on both, the token pass's checkpoints: (ceil(T / 64) + 8) d_k d_v fp32
+ *               per pair it runs at once, within 512 MiB.
+ * Gate values: any finite log_alpha (<= 0 in the method's use) and beta. Errors as for
+ * the other entry points.
  */
 size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk, int io);
 

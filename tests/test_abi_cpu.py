@@ -340,26 +340,38 @@ def test_chunk_bwd_workspace(lib):
         per = 2 * C * C + 3 * C * dk + C * dv + dk + 2 * dk * dv
         scr = 15 * C * dk + 6 * C * dv + 5 * C * C + C + 2 * dk
         units = B * ((T + C - 1) // C) * H
-        return r(units * per * 4) + r(min(units, 1024) * scr * 4) if units else 0
+        return (r(units * per * 4) + r(min(units, 1024) * scr * 4) + r(units) +
+                _tok_expect(B * H, (T + C - 1) // C, dk, dv)) if units else 0
 
     for args in ((2, 100, 4, 64, 64), (8, 8192, 32, 128, 128), (1, 1, 1, 64, 128), (3, 0, 2, 128, 64)):
         assert ws(*args, 64, F32) == expect(*args), args
     assert ws(2, 100, 4, 64, 64, 64, BF16) == expect(2, 100, 4, 64, 64)  # fp32 buffers whatever the io dtype
     assert ws(2, 100, 4, 64, 64, 128, F32) == 0
     # bf16 at d = 128: the matrix-core pass, about 170 KB of bf16 buffers per (chunk, head)
-    assert ws(8, 8192, 32, 128, 128, 64, BF16) == _bwd_fast_expect(8 * 128, 32, 0)
-    assert ws(2, 100, 4, 128, 128, 64, BF16) == _bwd_fast_expect(2 * 2, 4, 0)
+    assert ws(8, 8192, 32, 128, 128, 64, BF16) == _bwd_fast_expect(8 * 128, 32, 0, 8 * 32, 128)
+    assert ws(2, 100, 4, 128, 128, 64, BF16) == _bwd_fast_expect(2 * 2, 4, 0, 2 * 4, 2)
     assert ws(2, 0, 4, 128, 128, 64, BF16) == 0
 
 
-def _bwd_fast_expect(chunks, H, n_seqs_varlen, C=64, d=128):
+def _tok_expect(n_pairs, n_blk, dk, dv):
+    """The token pass's checkpoints: a state per 64-token block of the longest sequence and
+    per 8-token group, for as many workgroups as 512 MiB holds (at least one, at most one per
+    pair and 1024)."""
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    if n_pairs <= 0 or n_blk <= 0:
+        return 0
+    slot = (n_blk + 8) * dk * dv * 4
+    return r(max(1, min((512 << 20) // slot, n_pairs, 1024)) * slot)
+
+
+def _bwd_fast_expect(chunks, H, n_seqs_varlen, n_pairs, n_blk, C=64, d=128):
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
     u = chunks * H
     parts = [u * C * d * 2, u * C * d * 2, u * C * d * 2, u * d * C * 2, u * C * C * 2, u * d * 4, u,
              u * d * d * 2, u * d * C * 2, u * d * d * 2, u * d * C * 2, 256]
     if n_seqs_varlen:
         parts.append((3 * n_seqs_varlen + 1) * 4)
-    return sum(r(x) for x in parts)
+    return sum(r(x) for x in parts) + _tok_expect(n_pairs, n_blk, d, d)
 
 
 def bwd_varlen(lib, **kw):
@@ -387,6 +399,6 @@ def test_chunk_bwd_varlen_rejects(lib, kw, code):
 def test_chunk_bwd_varlen_workspace(lib):
     ws = lib.kda_chunk_bwd_varlen_workspace_bytes
     # sized for ceil(T / 64) + n_seqs chunks, plus the chunk-offset table
-    assert ws(300, 4, 128, 128, 64, 3, BF16) == _bwd_fast_expect(5 + 3, 4, 3)
-    assert ws(0, 4, 128, 128, 64, 2, BF16) == _bwd_fast_expect(0 + 2, 4, 2)
+    assert ws(300, 4, 128, 128, 64, 3, BF16) == _bwd_fast_expect(5 + 3, 4, 3, 3 * 4, 5)
+    assert ws(0, 4, 128, 128, 64, 2, BF16) == _bwd_fast_expect(0 + 2, 4, 2, 2 * 4, 0)
     assert ws(300, 4, 128, 128, 64, 3, F32) == 0 and ws(300, 4, 64, 64, 64, 3, BF16) == 0

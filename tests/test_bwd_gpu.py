@@ -193,13 +193,16 @@ def test_bwd_bitwise_deterministic(io):
         assert torch.equal(a, b), n
 
 
-def _varlen_case(seqlens, H, seed, h0=True, dhT=True):
+def _varlen_case(seqlens, H, seed, h0=True, dhT=True, mutate=None):
     """Packed bf16 sequences at d = 128 through kda_chunk_bwd_varlen, and the oracle run on
-    each sequence on its own (sequences are independent)."""
+    each sequence on its own (sequences are independent). mutate(x) may change the drawn
+    inputs first."""
     import torch
     import gated_delta_rule_48_amd as kda
     d, n = 128, len(seqlens)
     x = kda_synth.gen_sequences(seqlens, H, d, d, "bf16", "main", "normal" if h0 else "zero", seed)
+    if mutate is not None:
+        mutate(x)
     T = int(sum(seqlens))
     do = kda_synth.round_bf16(kda_synth.gen_grad_outputs(1, T, H, d, d, seed)["dout"][0])
     dh = kda_synth.gen_grad_outputs(n, 0, H, d, d, seed + 1)["dhT"] if dhT else None
@@ -224,19 +227,23 @@ def _varlen_case(seqlens, H, seed, h0=True, dhT=True):
     return got, refs
 
 
-@pytest.mark.parametrize("seqlens,H", [((0, 1, 63, 64, 65, 130, 0, 200), 3), ((300, 5), 2)])
-def test_bwd_varlen_packed_ragged(seqlens, H):
-    say(f"[bwd-varlen] seqlens={seqlens} H={H} bf16 d=128")
-    got, refs = _varlen_case(seqlens, H, seed=51 + H)
+def _check_varlen(name, got, refs):
     errs = {}
     for nm in NAMES[:5]:
         ref = np.concatenate([r[nm][0] for r in refs], axis=0)
         assert np.all(np.isfinite(got[nm])), nm
         errs[nm] = rel_l2(got[nm], ref)
     errs["dh0"] = rel_l2(got["dh0"], np.concatenate([r["dh0"] for r in refs], axis=0))
-    say(f"[bwd-varlen] rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    say(f"[{name}] rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     for nm, e in errs.items():
         assert e <= TOL["bf16"], (nm, e)
+
+
+@pytest.mark.parametrize("seqlens,H", [((0, 1, 63, 64, 65, 130, 0, 200), 3), ((300, 5), 2)])
+def test_bwd_varlen_packed_ragged(seqlens, H):
+    say(f"[bwd-varlen] seqlens={seqlens} H={H} bf16 d=128")
+    got, refs = _varlen_case(seqlens, H, seed=51 + H)
+    _check_varlen("bwd-varlen", got, refs)
 
 
 def test_bwd_varlen_equals_batched():
@@ -257,3 +264,68 @@ def test_bwd_varlen_equals_batched():
     torch.cuda.synchronize()
     for n, x1, x2 in zip(NAMES, a, b):
         assert torch.equal(flat(x1) if n != "dh0" else x1, x2), n
+
+
+# Chunks whose summed log alpha falls below -160 on some key channel leave the range of the
+# chunked passes' midpoint factors: their (sequence, head) pairs are recomputed token by
+# token (kda_bwd_tok.hip) after either pass. Chunk sums near -500 and -2000 per channel on
+# every chunk, and on one chunk of one pair among ordinary ones.
+@pytest.mark.parametrize("gates", ["sum500", "sum2000"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 128)])
+def test_bwd_strong_chunks_direct(gates, dk, dv):
+    _check("bwd-tok " + gates, 2, 150, 2, dk, dv, gates=gates, seed=71 + dk + dv)
+
+
+@pytest.mark.parametrize("gates", ["sum500", "sum2000"])
+def test_bwd_strong_chunks_matrix_core(gates):
+    _check("bwd-tok-mc " + gates, 2, 150, 2, 128, 128, gates=gates, seed=73, io="bf16")
+
+
+def _one_strong_chunk(B, T, H, dk, dv, seed, io):
+    """Ordinary gates, except chunk 1 (rows 64 .. 127) of sequence B - 1, head 0, whose log
+    alpha is -8 on every channel (a chunk sum of -512)."""
+    name = f"bwd-tok one-chunk {io} dk={dk} dv={dv}"
+    say(f"[{name}] B={B} T={T} H={H}")
+    d = _inputs(B, T, H, dk, dv, "main", seed, io=io)
+    d["log_alpha"][B - 1, 64:128, 0, :] = -8.0
+    scale = dk ** -0.5
+    got = _run(d, scale, io)
+    ref = oracle.kda_backward_reference(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], scale, d["dout"],
+                                        dhT=d["dhT"], h0=d["h0"])
+    errs = {}
+    for n in NAMES:
+        assert np.all(np.isfinite(got[n])), n
+        errs[n] = rel_l2(got[n], ref[n])
+        # the recomputed pair on its own, and one pair the chunked pass kept
+        if n == "dbeta":
+            a, b = got[n][B - 1, :, 0], ref[n][B - 1, :, 0]
+            c, e = got[n][0, :, H - 1], ref[n][0, :, H - 1]
+        elif n == "dh0":
+            a, b = got[n][B - 1, 0], ref[n][B - 1, 0]
+            c, e = got[n][0, H - 1], ref[n][0, H - 1]
+        else:
+            a, b = got[n][B - 1, :, 0], ref[n][B - 1, :, 0]
+            c, e = got[n][0, :, H - 1], ref[n][0, :, H - 1]
+        errs[n + "[strong pair]"] = rel_l2(a, b)
+        errs[n + "[other pair]"] = rel_l2(c, e)
+    say(f"[{name}] rel_l2 " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[io], (n, e)
+
+
+@pytest.mark.parametrize("io,dk,dv", [("f32", 64, 64), ("f32", 128, 128), ("bf16", 128, 128), ("bf16", 64, 128)])
+def test_bwd_one_strong_chunk(io, dk, dv):
+    _one_strong_chunk(2, 200, 3, dk, dv, 81 + dk, io)
+
+
+def test_bwd_varlen_strong_sequence():
+    """Packed sequences, the third of which has a chunk of summed log alpha -512 on head 1."""
+    seqlens, H = (70, 0, 200, 1, 129), 2
+
+    def mutate(x):
+        a = int(x["cu_seqlens"][2])
+        x["log_alpha"][a + 64:a + 128, 1, :] = -8.0
+
+    say(f"[bwd-tok varlen] seqlens={seqlens} H={H} bf16 d=128")
+    got, refs = _varlen_case(seqlens, H, seed=91, mutate=mutate)
+    _check_varlen("bwd-tok varlen", got, refs)

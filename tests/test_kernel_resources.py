@@ -19,7 +19,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_48_amd", "csrc")
 SOURCES = ["kda_fused.hip", "kda_prep.hip", "kda_state.hip", "kda_segment.hip", "kda_decode.hip", "kda_attn.hip",
-           "kda_bwd.hip", "kda_bwd_bf16.hip"]
+           "kda_bwd.hip", "kda_bwd_bf16.hip", "kda_bwd_tok.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
@@ -61,7 +61,8 @@ def test_every_kernel_is_reported(resources):
               "kda_decode_kernel",
               "kda_chunk_offsets_kernel", "kda_attn_decode_kernel", "kda_attn_combine_kernel",
               "kda_bwd_chunk_fwd_kernel", "kda_bwd_states_kernel", "kda_bwd_state_grads_kernel",
-              "kda_bwd_chunk_grads_kernel", "kda_bwd_rev_kernel", "kda_bwd_chunk_kernel"):
+              "kda_bwd_chunk_grads_kernel", "kda_bwd_rev_kernel", "kda_bwd_chunk_kernel", "kda_bwd_tok_kernel",
+              "kda_bwd_tok_detect_kernel"):
         assert k in names, k
 
 

@@ -547,7 +547,7 @@ struct BwdPlan {
 // budget holds, at most one per pair); the end of them.
 size_t tok_layout(size_t off, int64_t n_pairs, int64_t n_blk_max, int d_k, int d_v, BwdPlan *p) {
     p->tok_nblk = (int)n_blk_max;
-    p->tok_slot_floats = (size_t)(n_blk_max + 8) * d_k * d_v;
+    p->tok_slot_floats = (size_t)(n_blk_max + 16) * d_k * d_v;
     const size_t slot_bytes = p->tok_slot_floats * sizeof(float);
     int64_t slots = (int64_t)(kda::kTokScratchBudget / slot_bytes);
     slots = std::max<int64_t>(1, std::min<int64_t>(slots, std::min<int64_t>(n_pairs, 1024)));

@@ -89,7 +89,7 @@ struct TokArgs {
     int H;
     const uint8_t *flags;   // [chunk][head]
     float *scratch;         // n_slots x slot_floats
-    size_t slot_floats;     // (n_blk_max + 8) d_k d_v: a state per 64-token block, then per 8-token group
+    size_t slot_floats;     // (n_blk_max + 16) d_k d_v: a state per 64-token block, then per 4-token group
     int n_blk_max;          // 64-token blocks of the longest sequence, at most
 };
 

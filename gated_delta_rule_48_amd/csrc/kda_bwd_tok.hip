@@ -20,7 +20,7 @@
 //     dlog_alpha = rowsum(S~ (.) dS~),  dL/dS_{t-1} = Diag(alpha) dS~
 // The states S_{t-1} are recomputed forward from checkpoints: the state entering every
 // 64-token block (stored by a first pass over the sequence), the state entering every
-// 8-token group of the block being reversed (from the block's), and inside a group from
+// 4-token group of the block being reversed (from the block's), and inside a group from
 // the group's, kept in registers.
 //
 // Work split: one workgroup of four waves per pair, a fixed number of workgroups (the
@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kTokThreads = 256;
 constexpr int kTokBlock = 64;  // tokens between stored checkpoints
-constexpr int kTokGroup = 8;   // tokens between the checkpoints of the block being reversed
+constexpr int kTokGroup = 4;   // tokens between the checkpoints of the block being reversed
 
 template <int CTRL> __device__ __forceinline__ float dppf(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));

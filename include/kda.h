@@ -297,10 +297,10 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  * (sequence, head) pairs holding a chunk below that are recomputed token by token (fp32
  * arithmetic, every decay applied as alpha = exp(log_alpha) <= 1): the exact reverse mode
  * of the recurrence, with the states recomputed from checkpoints (one per 64 tokens, then
- * one per 8 tokens of the block being reversed). This pass is sequential over the tokens of
- * a pair and runs on as many pairs at once as its share of the workspace holds checkpoints
- * for (at most 512 MiB, at least one pair at a time); calls without such chunks spend only
- * the check on it.
+ * one per 4 tokens of the block being reversed). This pass is sequential over the tokens of
+ * a pair (about 8 us per token on one MI355X compute unit) and runs on as many pairs at once
+ * as its share of the workspace holds checkpoints for (at most 512 MiB, at least one pair at
+ * a time); calls without such chunks spend only the check on it.
  *
  * Arguments
  *   B, T, H, d_k, d_v   equal-length sequences [B, T, H, d] (packed sequences:
@@ -318,7 +318,7 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  *               matrix-core pass about 170 KB per (chunk, head) (the forward's chunk
  *               quantities and four bf16 matrices); on the direct pass about 300 KB per
  *               (chunk, head) at d = 128 plus a fixed scratch of at most 1024 x 770 KB;
- *               on both, the token pass's checkpoints: (ceil(T / 64) + 8) d_k d_v fp32
+ *               on both, the token pass's checkpoints: (ceil(T / 64) + 16) d_k d_v fp32
  *               per pair it runs at once, within 512 MiB.
  * Gate values: any finite log_alpha (<= 0 in the method's use) and beta. Errors as for
  * the other entry points.

@@ -355,12 +355,12 @@ def test_chunk_bwd_workspace(lib):
 
 def _tok_expect(n_pairs, n_blk, dk, dv):
     """The token pass's checkpoints: a state per 64-token block of the longest sequence and
-    per 8-token group, for as many workgroups as 512 MiB holds (at least one, at most one per
+    per 4-token group, for as many workgroups as 512 MiB holds (at least one, at most one per
     pair and 1024)."""
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
     if n_pairs <= 0 or n_blk <= 0:
         return 0
-    slot = (n_blk + 8) * dk * dv * 4
+    slot = (n_blk + 16) * dk * dv * 4
     return r(max(1, min((512 << 20) // slot, n_pairs, 1024)) * slot)
 
 

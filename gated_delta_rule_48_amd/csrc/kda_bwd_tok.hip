@@ -55,58 +55,92 @@ __device__ __forceinline__ float row16_allsum(float x) {
 template <typename T, int DK, int DV>
 struct TokPass {
     static constexpr int RB = DK / 16, CB = DV / 16;
-    static constexpr int RED = 16 * CB + 16;  // one wave's column partials and extra values
+    static constexpr int RED = 32 * CB;  // one wave's column partials (two matrices)
 
     const TokArgs &a;
     float *stg_k, *stg_q, *stg_a, *stg_v, *stg_do, *stg_b, *red;
     int tid, w, l, bi, bj, r0, c0, h;
     int rbuf = 0;  // the reduction buffer of the next column sum
 
-    // Column sums over all d_k rows of the per-thread partials p (this thread's CB columns)
-    // and of one extra per-thread value e: in-wave across the four row groups, then across
-    // the waves in LDS. Every thread receives the sums. One barrier; the two buffers
+    // Column sums over all d_k rows of per-thread partials (NV values per thread: this
+    // thread's CB columns of one or two matrices): in-wave across the four row groups, then
+    // across the waves in LDS. Every thread receives the sums. One barrier; the two buffers
     // alternate, so a buffer is written again only after every thread has passed the next
     // barrier, that is, after every thread has read it.
-    __device__ __forceinline__ void col_allsum(float (&p)[CB], float &e) {
+    template <int NV> __device__ __forceinline__ void col_allsum(float (&p)[NV]) {
+        static_assert(16 * NV <= RED, "reduction buffer");
 #pragma unroll
-        for (int c = 0; c < CB; ++c) {
+        for (int c = 0; c < NV; ++c) {
             p[c] += __shfl_xor(p[c], 16);
             p[c] += __shfl_xor(p[c], 32);
         }
-        e += __shfl_xor(e, 16);
-        e += __shfl_xor(e, 32);
         float *rb = red + rbuf * 4 * RED;
         rbuf ^= 1;
         if (l < 16) {
 #pragma unroll
-            for (int c = 0; c < CB; ++c) rb[w * RED + CB * bj + c] = p[c];
-            rb[w * RED + 16 * CB + bj] = e;
+            for (int c = 0; c < NV; ++c) rb[w * RED + NV * bj + c] = p[c];
         }
         __syncthreads();
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
-            p[c] = (rb[CB * bj + c] + rb[RED + CB * bj + c]) + (rb[2 * RED + CB * bj + c] + rb[3 * RED + CB * bj + c]);
-        e = (rb[16 * CB + bj] + rb[RED + 16 * CB + bj]) + (rb[2 * RED + 16 * CB + bj] + rb[3 * RED + 16 * CB + bj]);
+        for (int c = 0; c < NV; ++c)
+            p[c] = (rb[NV * bj + c] + rb[RED + NV * bj + c]) + (rb[2 * RED + NV * bj + c] + rb[3 * RED + NV * bj + c]);
     }
 
-    // Tokens [row0, row0 + n) of the pair (packed row indices) into the staging slots:
-    // k, alpha = exp(log_alpha), v, beta, and with q/do also q and dout (fp32).
-    __device__ void stage(int row0, int n, bool with_q) {
+    // One 4-token group's inputs (this thread's elements, as loaded): requested by fetch()
+    // one group ahead and stored, converted, into the staging slots by put() when the group
+    // is reached, so that the loads overlap the work in between.
+    static constexpr int NEK = (kTokGroup * DK + kTokThreads - 1) / kTokThreads;
+    static constexpr int NEV = (kTokGroup * DV + kTokThreads - 1) / kTokThreads;
+    struct Fetch {
+        T k[NEK], q[NEK], v[NEV], d[NEV];
+        float la[NEK], b;
+    };
+    // Tokens [row0, row0 + n) of the pair (packed row indices): k, log_alpha, v, beta, and with
+    // with_q also q and dout.
+    __device__ __forceinline__ void fetch(Fetch &f, int row0, int n, bool with_q) {
         const int H = a.H;
-        for (int idx = tid; idx < n * DK; idx += kTokThreads) {
-            const int i = idx / DK, c = idx % DK;
-            const size_t g = ((size_t)(row0 + i) * H + h) * DK + c;
-            stg_k[i * DK + c] = to_f32(static_cast<const T *>(a.k)[g]);
-            stg_a[i * DK + c] = expf(a.log_alpha[g]);
-            if (with_q) stg_q[i * DK + c] = to_f32(static_cast<const T *>(a.q)[g]);
+#pragma unroll
+        for (int e = 0; e < NEK; ++e) {
+            const int idx = tid + kTokThreads * e;
+            if (idx < n * DK) {
+                const size_t g = ((size_t)(row0 + idx / DK) * H + h) * DK + idx % DK;
+                f.k[e] = static_cast<const T *>(a.k)[g];
+                f.la[e] = a.log_alpha[g];
+                if (with_q) f.q[e] = static_cast<const T *>(a.q)[g];
+            }
         }
-        for (int idx = tid; idx < n * DV; idx += kTokThreads) {
-            const int i = idx / DV, c = idx % DV;
-            const size_t g = ((size_t)(row0 + i) * H + h) * DV + c;
-            stg_v[i * DV + c] = to_f32(static_cast<const T *>(a.v)[g]);
-            if (with_q) stg_do[i * DV + c] = to_f32(static_cast<const T *>(a.dout)[g]);
+#pragma unroll
+        for (int e = 0; e < NEV; ++e) {
+            const int idx = tid + kTokThreads * e;
+            if (idx < n * DV) {
+                const size_t g = ((size_t)(row0 + idx / DV) * H + h) * DV + idx % DV;
+                f.v[e] = static_cast<const T *>(a.v)[g];
+                if (with_q) f.d[e] = static_cast<const T *>(a.dout)[g];
+            }
         }
-        if (tid < n) stg_b[tid] = a.beta[(size_t)(row0 + tid) * H + h];
+        if (tid < n) f.b = a.beta[(size_t)(row0 + tid) * H + h];
+    }
+    // The fetched group into the staging slots: k, alpha = exp(log_alpha), v, beta (and q,
+    // dout), fp32, slot i at offset i * d.
+    __device__ __forceinline__ void put(const Fetch &f, int n, bool with_q) {
+#pragma unroll
+        for (int e = 0; e < NEK; ++e) {
+            const int idx = tid + kTokThreads * e;
+            if (idx < n * DK) {
+                stg_k[idx] = to_f32(f.k[e]);
+                stg_a[idx] = expf(f.la[e]);
+                if (with_q) stg_q[idx] = to_f32(f.q[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < NEV; ++e) {
+            const int idx = tid + kTokThreads * e;
+            if (idx < n * DV) {
+                stg_v[idx] = to_f32(f.v[e]);
+                if (with_q) stg_do[idx] = to_f32(f.d[e]);
+            }
+        }
+        if (tid < n) stg_b[tid] = f.b;
     }
 
     __device__ __forceinline__ void load_state(const float *src, float (&S)[RB][CB]) {
@@ -146,8 +180,7 @@ struct TokPass {
                 S[r][c] *= ar[r];
                 p[c] = fmaf(S[r][c], kr[r], p[c]);
             }
-        float e = 0.f;
-        col_allsum(p, e);  // p = S~^T k
+        col_allsum(p);  // p = S~^T k
 #pragma unroll
         for (int c = 0; c < CB; ++c) p[c] = stg_v[i * DV + c0 + c] - p[c];  // u
 #pragma unroll
@@ -169,50 +202,46 @@ struct TokPass {
         }
         const float b = stg_b[i];
 #pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            dc[c] = stg_do[i * DV + c0 + c];
-            p[c] = 0.f;
-        }
-        // S~ and u = v - S~^T k
+        for (int c = 0; c < CB; ++c) dc[c] = stg_do[i * DV + c0 + c];
+        // S~; dS' = dS + scale q do^T; one column sum for u = v - S~^T k and du = beta dS'^T k
+        float pp[2 * CB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int c = 0; c < 2 * CB; ++c) pp[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const float sq = scale * qr[r];
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
                 Sp[r][c] *= ar[r];
-                p[c] = fmaf(Sp[r][c], kr[r], p[c]);
+                dS[r][c] = fmaf(sq, dc[c], dS[r][c]);
+                pp[c] = fmaf(Sp[r][c], kr[r], pp[c]);
+                pp[CB + c] = fmaf(dS[r][c], kr[r], pp[CB + c]);
             }
-        float e = 0.f;
-        col_allsum(p, e);
+        }
+        col_allsum(pp);
+        // dbeta = k^T dS' u = (dS'^T k) . u, summed over this thread's columns, then the row
+        float eb = 0.f;
 #pragma unroll
-        for (int c = 0; c < CB; ++c) u[c] = stg_v[i * DV + c0 + c] - p[c];
-        // dS' = dS + scale q do^T; x1 = S_t do (S_t = S~ + beta k u^T); x2 = dS' u
+        for (int c = 0; c < CB; ++c) {
+            u[c] = stg_v[i * DV + c0 + c] - pp[c];
+            eb = fmaf(pp[CB + c], u[c], eb);
+            p[c] = b * pp[CB + c];  // du
+        }
+        eb = row16_allsum(eb);
+        // x1 = S_t do (S_t = S~ + beta k u^T); x2 = dS' u
         float x1[RB], x2[RB];
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const float bk = b * kr[r], sq = scale * qr[r];
+            const float bk = b * kr[r];
             float s1 = 0.f, s2 = 0.f;
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                dS[r][c] = fmaf(sq, dc[c], dS[r][c]);
                 s1 = fmaf(fmaf(bk, u[c], Sp[r][c]), dc[c], s1);
                 s2 = fmaf(dS[r][c], u[c], s2);
             }
             x1[r] = row16_allsum(s1);
             x2[r] = row16_allsum(s2);
         }
-        // du = beta dS'^T k; dbeta = k^T dS' u (the extra value of the column sums)
-        float eb = 0.f;
-#pragma unroll
-        for (int c = 0; c < CB; ++c) p[c] = 0.f;
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-#pragma unroll
-            for (int c = 0; c < CB; ++c) p[c] = fmaf(dS[r][c], kr[r], p[c]);
-            eb = fmaf(kr[r], x2[r], eb);
-        }
-        col_allsum(p, eb);
-#pragma unroll
-        for (int c = 0; c < CB; ++c) p[c] *= b;  // du
         // y1 = S~ du; dS~ = dS' - k du^T; y2 = rowsum(S~ (.) dS~); dS <- Diag(alpha) dS~
         float y1[RB], y2[RB];
 #pragma unroll
@@ -263,16 +292,17 @@ struct TokPass {
 #pragma unroll
                 for (int c = 0; c < CB; ++c) S[r][c] = 0.f;
         }
-        for (int bk = 0; bk < n_blk; ++bk) {
-            store_state(ck + (size_t)bk * DK * DV, S);
-            const int b0 = tb + bk * kTokBlock, b1 = min(b0 + kTokBlock, te);
-            for (int g0 = b0; g0 < b1; g0 += kTokGroup) {
-                const int n = min(kTokGroup, b1 - g0);
-                __syncthreads();  // the previous group's staging is read
-                stage(g0, n, false);
-                __syncthreads();
-                for (int i = 0; i < n; ++i) forward_step(S, i);
-            }
+        Fetch f;
+        const int n_all = (T_len + kTokGroup - 1) / kTokGroup;  // groups (blocks hold whole groups)
+        if (n_all > 0) fetch(f, tb, min(kTokGroup, T_len), false);
+        for (int gi = 0; gi < n_all; ++gi) {
+            const int g0 = tb + gi * kTokGroup, n = min(kTokGroup, te - g0);
+            if ((gi * kTokGroup) % kTokBlock == 0) store_state(ck + (size_t)(gi * kTokGroup / kTokBlock) * DK * DV, S);
+            __syncthreads();  // the previous group's staging is read
+            put(f, n, false);
+            if (gi + 1 < n_all) fetch(f, g0 + kTokGroup, min(kTokGroup, te - g0 - kTokGroup), false);
+            __syncthreads();
+            for (int i = 0; i < n; ++i) forward_step(S, i);
         }
 
         // reverse, block by block
@@ -285,16 +315,26 @@ struct TokPass {
 #pragma unroll
                 for (int c = 0; c < CB; ++c) dS[r][c] = 0.f;
         }
+        // the first group of the last block
+        if (n_blk > 0) {
+            const int b0 = tb + (n_blk - 1) * kTokBlock;
+            fetch(f, b0, min(kTokGroup, te - b0), false);
+        }
         for (int bk = n_blk - 1; bk >= 0; --bk) {
             const int b0 = tb + bk * kTokBlock, b1 = min(b0 + kTokBlock, te);
             const int n_grp = (b1 - b0 + kTokGroup - 1) / kTokGroup;
-            // the state entering every group of the block
+            const int g_last = b0 + (n_grp - 1) * kTokGroup;
+            // the state entering every group of the block (its first group is in flight)
             load_state(ck + (size_t)bk * DK * DV, S);
             for (int gi = 0; gi < n_grp; ++gi) {
                 const int g0 = b0 + gi * kTokGroup, n = min(kTokGroup, b1 - g0);
                 store_state(grp + (size_t)gi * DK * DV, S);
                 __syncthreads();
-                stage(g0, n, false);
+                put(f, n, false);
+                if (gi + 1 < n_grp)
+                    fetch(f, g0 + kTokGroup, min(kTokGroup, b1 - g0 - kTokGroup), false);
+                else
+                    fetch(f, g_last, b1 - g_last, true);  // the reverse's first group
                 __syncthreads();
                 for (int i = 0; i < n; ++i) forward_step(S, i);
             }
@@ -302,7 +342,11 @@ struct TokPass {
             for (int gi = n_grp - 1; gi >= 0; --gi) {
                 const int g0 = b0 + gi * kTokGroup, n = min(kTokGroup, b1 - g0);
                 __syncthreads();
-                stage(g0, n, true);
+                put(f, n, true);
+                if (gi > 0)
+                    fetch(f, g0 - kTokGroup, kTokGroup, true);
+                else if (bk > 0)
+                    fetch(f, b0 - kTokBlock, kTokGroup, false);  // the previous block's first group
                 __syncthreads();
                 float Sg[RB][CB];
                 load_state(grp + (size_t)gi * DK * DV, Sg);

@@ -298,7 +298,7 @@ int kda_recurrent_step_preact(int flags, int N, int H, int d_k, int d_v, int io,
  * arithmetic, every decay applied as alpha = exp(log_alpha) <= 1): the exact reverse mode
  * of the recurrence, with the states recomputed from checkpoints (one per 64 tokens, then
  * one per 4 tokens of the block being reversed). This pass is sequential over the tokens of
- * a pair (about 8 us per token on one MI355X compute unit) and runs on as many pairs at once
+ * a pair (about 7 us per token on one MI355X compute unit) and runs on as many pairs at once
  * as its share of the workspace holds checkpoints for (at most 512 MiB, at least one pair at
  * a time); calls without such chunks spend only the check on it.
  *

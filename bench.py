@@ -534,6 +534,55 @@ def bench_bwd(args, kda, torch, io="f32"):
             "roofline": roof}
 
 
+def bench_bwd_strong(args, kda, torch):
+    """The backward's token pass: kda_chunk_bwd on one sequence of 8,192 tokens, one head, d=128,
+    once with ordinary gates and once with chunk 1 at log alpha = -8 on every channel (a chunk
+    sum of -512, past the chunked passes' range, so the pair is recomputed token by token), in
+    both I/O dtypes; the difference of the two times is the token pass's cost for the pair."""
+    B, T, H, d = 1, 8192, 1, 128
+    dev = torch.device("cuda:0")
+    out = {}
+    for io in ("bf16", "f32"):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1011)
+        rn = lambda *s: torch.randn(s, generator=g, device=dev)  # noqa: E731
+        q = torch.nn.functional.normalize(rn(B, T, H, d), dim=-1)
+        k = torch.nn.functional.normalize(rn(B, T, H, d), dim=-1)
+        v, dout = rn(B, T, H, d), rn(B, T, H, d)
+        if io == "bf16":
+            q, k, v, dout = (x.to(torch.bfloat16) for x in (q, k, v, dout))
+        la = -torch.nn.functional.softplus(rn(B, T, H, d) - 2.0)
+        beta = torch.sigmoid(rn(B, T, H))
+        ws = torch.empty(kda.chunk_bwd_workspace_bytes(B, T, H, d, d, io=kda.KDA_BF16 if io == "bf16" else kda.KDA_F32),
+                         dtype=torch.uint8, device=dev)
+        times = {}
+        for case in ("ordinary", "one strong chunk"):
+            if case != "ordinary":
+                la[:, 64:128] = -8.0
+
+            def step():
+                kda.chunk_bwd(q, k, v, la, beta, dout, workspace=ws)
+
+            step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.bwd_steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            times[case] = e0.elapsed_time(e1) / args.bwd_steps
+        extra = times["one strong chunk"] - times["ordinary"]
+        log(f"[bench] backward token pass ({io} I/O): {times['ordinary']:.3f} ms/call with ordinary gates, "
+            f"{times['one strong chunk']:.3f} ms with one strong chunk: {extra:.2f} ms for the pair's {T} tokens "
+            f"({extra * 1000 / T:.2f} us per token)")
+        out[io] = {"ms_ordinary": round(times["ordinary"], 3), "ms_one_strong_chunk": round(times["one strong chunk"], 3),
+                   "us_per_token": round(extra * 1000 / T, 3)}
+        del q, k, v, dout, la, beta, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(pre, args):
     """The fp64 oracle on the prefill workload's first `--cpu-seqs` sequences (all
     of them by default: all heads, full length), on this host's cores."""
@@ -612,6 +661,9 @@ def main():
                     help="skip the backward pass on the batched shape (fp32 and bf16 I/O)")
     ap.add_argument("--bwd", action="store_true", help=argparse.SUPPRESS)  # the default; kept for old commands
     ap.add_argument("--bwd-steps", type=int, default=3)
+    ap.add_argument("--bwd-strong", action="store_true",
+                    help="also time the backward's token pass (one sequence of 8192 tokens, one head, with and "
+                         "without a chunk of strong decay)")
     ap.add_argument("--workloads", default="prefill,varlen,tiny", metavar="NAMES",
                     help="comma-separated further prefill workloads to time and report (" +
                          ", ".join(n for n in kda_synth.WORKLOADS if n != "batched") + "; empty for none)")
@@ -635,6 +687,7 @@ def main():
     others = {n: bench_workload(args, kda, torch, n) for n in args.workloads.split(",") if n}
     attn = {n: bench_attn(args, kda, torch, n, dec) for n in args.attn.split(",") if n}
     bwd = None if args.no_bwd else {io: bench_bwd(args, kda, torch, io) for io in ("bf16", "f32")}
+    bwd_strong = bench_bwd_strong(args, kda, torch) if args.bwd_strong else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre, args)
 
     w = pre["workload"]
@@ -674,6 +727,8 @@ def main():
     if bwd is not None:
         line["backward"] = bwd["bf16"]
         line["backward_f32_io"] = bwd["f32"]
+    if bwd_strong is not None:
+        line["backward_token_pass"] = bwd_strong
     if others:
         line["workloads"] = others
     print(json.dumps(line), flush=True)

@@ -130,8 +130,9 @@ __device__ __forceinline__ void transpose_into(bf16 *dst, const bf16 *src, bool 
 
 // ------------------------------------------------------------------ (3) reverse recursion
 //
-// One workgroup of 4 waves per (sequence, head); the state gradient dS' (128 x 128 fp32)
-// in matrix-core accumulators, wave w owning key channels 32 w .. 32 w + 31. Per chunk,
+// One workgroup of 8 waves per (sequence, head), two per SIMD so that one wave's loads and
+// LDS waits overlap the other's products; the state gradient dS' (128 x 128 fp32) in
+// matrix-core accumulators, wave w owning key channels 16 w .. 16 w + 15. Per chunk,
 // last first: the chunk's Aqk, KtT, QO and W (fragment-ordered for the forward's uses)
 // are transposed into LDS for the reverse uses, and dO's rows into F(dO^T).
 struct RevLds {
@@ -144,21 +145,19 @@ struct RevLds {
     bf16 dUt[kD * kC];   // F(dU^T)
 };
 
-__global__ __launch_bounds__(256) void kda_bwd_rev_kernel(BwdFastArgs a) {
+__global__ __launch_bounds__(512) void kda_bwd_rev_kernel(BwdFastArgs a) {
     __shared__ __align__(16) RevLds L;
     const int H = a.H, sh = blockIdx.x, h = sh % H, s = sh / H;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    // dS' tiles of this wave: key-channel blocks 2 w + sb, value blocks nt
-    f32x4 acc[2][8];
+    // dS' tiles of this wave: key-channel block w, value blocks nt
+    f32x4 acc[8];
     {
         const float *dhT = a.dhT ? a.dhT + ((size_t)s * H + h) * kD * kD : nullptr;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[sb][nt][i] = dhT ? dhT[(16 * (2 * w + sb) + acc_row(i)) * kD + 16 * nt + acc_col()] : 0.f;
+            for (int i = 0; i < 4; ++i)
+                acc[nt][i] = dhT ? dhT[(16 * w + acc_row(i)) * kD + 16 * nt + acc_col()] : 0.f;
     }
     int tb, te;
     a.map.seq_range(s, tb, te);
@@ -170,11 +169,11 @@ __global__ __launch_bounds__(256) void kda_bwd_rev_kernel(BwdFastArgs a) {
     // one computes. Every load is unconditional (rows past the sequence's end re-read its last
     // row and are then zeroed), so that the compiler waits for exactly the set it needs.
     struct Ops {
-        Shares<kC, kC, 256> aq;
-        Shares<kD, kC, 256> kt;
-        Shares<kC, kD, 256> qo, wm;
-        V8 o[4];
-        f32x4 eg0, eg1;
+        Shares<kC, kC, 512> aq;
+        Shares<kD, kC, 512> kt;
+        Shares<kC, kD, 512> qo, wm;
+        V8 o[2];
+        f32x4 eg;
     };
     auto load_ops = [&](int ci, Ops &op) {
         const int t0 = tb + ci * kC, L_rows = min(kC, te - t0);
@@ -184,16 +183,15 @@ __global__ __launch_bounds__(256) void kda_bwd_rev_kernel(BwdFastArgs a) {
         op.qo.load(static_cast<const bf16 *>(a.buf.QO) + jh * kC * kD);
         op.wm.load(static_cast<const bf16 *>(a.buf.W) + jh * kC * kD);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {  // dO: 8 adjacent value columns of one row per share
-            const int u = threadIdx.x + 256 * m, r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
+        for (int m = 0; m < 2; ++m) {  // dO: 8 adjacent value columns of one row per share
+            const int u = threadIdx.x + 512 * m, r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
             op.o[m] = *reinterpret_cast<const V8 *>(dout + ((size_t)(t0 + min(r, L_rows - 1)) * H + h) * kD + j0);
             if (r >= L_rows) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) op.o[m][e] = static_cast<bf16>(0.f);
             }
         }
-        op.eg0 = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * (2 * w) + 4 * (l >> 4));
-        op.eg1 = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * (2 * w + 1) + 4 * (l >> 4));
+        op.eg = *reinterpret_cast<const f32x4 *>(a.buf.eg + jh * kD + 16 * w + 4 * (l >> 4));
     };
     Ops op;
     if (n_c > 0) load_ops(n_c - 1, op);
@@ -202,68 +200,62 @@ __global__ __launch_bounds__(256) void kda_bwd_rev_kernel(BwdFastArgs a) {
         const size_t jh = (size_t)(c_begin + ci) * H + h;
         // dS' (the gradient at this chunk's end) into LDS
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) store_t(L.dSt, 2 * w + sb, nt, acc[sb][nt], kD);
+        for (int nt = 0; nt < 8; ++nt) store_t(L.dSt, w, nt, acc[nt], kD);
         // this chunk's operands, transposed
         op.aq.store_transposed(L.AqT, false);
         op.kt.store_transposed(L.Rf, false);
         op.qo.store_transposed(L.QOt, false);
         op.wm.store_transposed(L.Wn, true);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int u = threadIdx.x + 256 * m, r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
+        for (int m = 0; m < 2; ++m) {
+            const int u = threadIdx.x + 512 * m, r = u / (kD / 8), j0 = 8 * (u % (kD / 8));
 #pragma unroll
             for (int e = 0; e < 8; ++e) L.dOt[frag_off<bf16>(j0 + e, r, kD)] = op.o[m][e];
         }
-        const f32x4 eg0 = op.eg0, eg1 = op.eg1;
+        const f32x4 eg = op.eg;
         load_ops(ci > 0 ? ci - 1 : 0, op);  // the next chunk's (the first re-reads itself)
         __syncthreads();
         // record dS'^T of this chunk
         {
             bf16 *dst = static_cast<bf16 *>(a.ds) + jh * kD * kD;
-            for (int u = threadIdx.x; u < kD * kD / 8; u += 256)
+            for (int u = threadIdx.x; u < kD * kD / 8; u += 512)
                 *reinterpret_cast<uint4 *>(dst + (size_t)u * 8) = *reinterpret_cast<const uint4 *>(L.dSt + (size_t)u * 8);
         }
-        // dU = Aqk^T dO + R dS': rows 16 w .. of the chunk, all 128 value columns
+        // dU = Aqk^T dO + R dS': rows 16 (w % 4) .. of the chunk, value blocks 4 (w / 4) .. + 3
         {
-            f32x4 du[8];
+            const int rb = w & 3, cb0 = 4 * (w >> 2);
+            f32x4 du[4];
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) du[nt] = zero4();
-            prod<8, kC / 32>(du, L.AqT, kC, w, L.dOt, kD, 0);
-            prod<8, kD / 32>(du, L.Rf, kC, w, L.dSt, kD, 0);
+            for (int nt = 0; nt < 4; ++nt) du[nt] = zero4();
+            prod<4, kC / 32>(du, L.AqT, kC, rb, L.dOt, kD, cb0);
+            prod<4, kD / 32>(du, L.Rf, kC, rb, L.dSt, kD, cb0);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) store_t(L.dUt, w, nt, du[nt], kD);
+            for (int nt = 0; nt < 4; ++nt) store_t(L.dUt, rb, cb0 + nt, du[nt], kD);
         }
         __syncthreads();
         {
             bf16 *dst = static_cast<bf16 *>(a.du) + jh * kD * kC;
-            for (int u = threadIdx.x; u < kD * kC / 8; u += 256)
+            for (int u = threadIdx.x; u < kD * kC / 8; u += 512)
                 *reinterpret_cast<uint4 *>(dst + (size_t)u * 8) = *reinterpret_cast<const uint4 *>(L.dUt + (size_t)u * 8);
         }
         // dS = Diag(e^gamma) dS' + QO^T dO - W^T dU
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const f32x4 eg = sb ? eg1 : eg0;
+        {
             f32x4 t[8];
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) t[nt] = acc[sb][nt] * eg;
-            prod<8, kC / 32>(t, L.QOt, kD, 2 * w + sb, L.dOt, kD, 0);
-            prod<8, kC / 32>(t, L.Wn, kD, 2 * w + sb, L.dUt, kD, 0);
+            for (int nt = 0; nt < 8; ++nt) t[nt] = acc[nt] * eg;
+            prod<8, kC / 32>(t, L.QOt, kD, w, L.dOt, kD, 0);
+            prod<8, kC / 32>(t, L.Wn, kD, w, L.dUt, kD, 0);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[sb][nt] = t[nt];
+            for (int nt = 0; nt < 8; ++nt) acc[nt] = t[nt];
         }
         __syncthreads();  // LDS free for the next chunk
     }
     if (a.dh0) {
         float *dh0 = a.dh0 + ((size_t)s * H + h) * kD * kD;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dh0[(16 * (2 * w + sb) + acc_row(i)) * kD + 16 * nt + acc_col()] = acc[sb][nt][i];
+            for (int i = 0; i < 4; ++i) dh0[(16 * w + acc_row(i)) * kD + 16 * nt + acc_col()] = acc[nt][i];
     }
 }
 
@@ -820,7 +812,7 @@ hipError_t launch_chunk_bwd_bf16(const BwdFastArgs &a, int n_seqs, int total_chu
         if ((err = launch_state(sa, kC, kD, kD, true, n_seqs, stream)) != hipSuccess) return err;
     }
     // (3) the reverse recursion
-    hipLaunchKernelGGL(kda_bwd_rev_kernel, dim3(n_seqs * a.H), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kda_bwd_rev_kernel, dim3(n_seqs * a.H), dim3(512), 0, stream, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // (4) the chunk-local gradients
     if (total_chunks > 0) {

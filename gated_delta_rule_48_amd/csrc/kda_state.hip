@@ -288,6 +288,9 @@ hipError_t launch_state_w(StateArgs a, int n_seqs, hipStream_t stream) {
     const int pairs = n_seqs * a.H;
     a.xcd_group = (pairs % 8) == 0;
     if constexpr (sizeof(T) == 2) {
+        // (the backward's recording instance: two slices of 64 columns per pair, which
+        // keep two workgroups on each compute unit)
+        if (a.st_out) return launch_state_t<C, DK, DV, (DV > 64 ? 64 : DV), T>(a, n_seqs, stream);
         if (pairs >= 256) return launch_state_t<C, DK, DV, DV, T>(a, n_seqs, stream);
     }
     return launch_state_t<C, DK, DV, 32, T>(a, n_seqs, stream);

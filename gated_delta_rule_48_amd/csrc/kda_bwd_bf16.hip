@@ -406,32 +406,34 @@ __global__ __launch_bounds__(512) void kda_bwd_chunk_kernel(BwdFastArgs a) {
             }
     }
     __syncthreads();
-    // forward substitution on four waves: column jc on the four lanes of quad jc, lane qd
-    // holding x_i for i = qd mod 4 and summing those terms; the partial sums meet by two DPP swaps
-    float xs[kC / 4];
-    if (w < 4) {
+    // forward substitution on all eight waves: column jc on the eight lanes jc * 8 .., lane qd
+    // holding x_i for i = qd mod 8 and summing those terms; the partial sums meet by three DPP
+    // swaps (pairs, quads, then the two quads of the half row)
+    float xs[kC / 8];
+    {
         const float *As = ffl(cl::As);
-        const int jc = tid >> 2, qd = tid & 3;
+        const int jc = tid >> 3, qd = tid & 7;
 #pragma unroll
-        for (int mm = 0; mm < kC / 4; ++mm) xs[mm] = 0.f;
+        for (int mm = 0; mm < kC / 8; ++mm) xs[mm] = 0.f;
 #pragma unroll
         for (int r = 0; r < kC; ++r) {
             float part = 0.f;
 #pragma unroll
-            for (int mm = 0; mm < kC / 4; ++mm)
-                if (4 * mm < r) part = fmaf(4 * mm + qd < r ? As[r * cl::AsP + 4 * mm + qd] : 0.f, xs[mm], part);
+            for (int mm = 0; mm < kC / 8; ++mm)
+                if (8 * mm < r) part = fmaf(8 * mm + qd < r ? As[r * cl::AsP + 8 * mm + qd] : 0.f, xs[mm], part);
             part += quad_swap<0xB1>(part);
             part += quad_swap<0x4E>(part);
+            part += quad_swap<0x141>(part);
             const float xr = (r == jc ? 1.f : 0.f) - part;
-            if ((r & 3) == qd) xs[r >> 2] = xr;
+            if ((r & 7) == qd) xs[r >> 3] = xr;
         }
     }
     __syncthreads();  // every read of A done
-    if (w < 4) {
+    {
         float *As = ffl(cl::As);
-        const int jc = tid >> 2, qd = tid & 3;
+        const int jc = tid >> 3, qd = tid & 7;
 #pragma unroll
-        for (int mm = 0; mm < kC / 4; ++mm) As[(4 * mm + qd) * cl::AsP + jc] = xs[mm];
+        for (int mm = 0; mm < kC / 8; ++mm) As[(8 * mm + qd) * cl::AsP + jc] = xs[mm];
     }
     __syncthreads();
     // F(T) (rows r, contraction i) and F(T^T) (rows i, contraction r): one slot of 8 each per thread
